@@ -1,0 +1,1 @@
+"""DF11 CPU oracle -- test infrastructure only (see oracle.py)."""
