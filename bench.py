@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the DF11 decode hot path on one MI355X.
+
+Default workload: one Llama-3-8B-shaped decoder layer of synthetic
+N(0, 0.02) BF16 weights (q, k, v, o, gate, up, down: 218,103,808 elements)
+with one codebook for the layer, compressed and resident in HBM.  One step
+decodes all seven matrices, one after another, into one reused BF16 buffer.
+
+Prints one JSON line:
+  value     decoded BF16 GB/s (2 bytes per element / step time)
+  roofline  the decode kernel's algorithmic HBM bytes per launch / its
+            average launch time (HIP events on the launch stream), against
+            the 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle's bit-serial decode of the same layer, timed
+            on this host (single thread)
+
+    python bench.py [--steps K] [--warmup W] [--workload layer|tensor1024|adversarial|fused]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(enc) -> int:
+    """Bytes a decode must move: the exponent stream, one sign+mantissa byte
+    per element, the per-lane gaps and per-segment records, and the BF16
+    output (2 bytes per element)."""
+    stream = (enc.total_bits + 7) // 8
+    return stream + enc.n + enc.n_segments * 64 + (enc.n_segments + 1) * 16 + 2 * enc.n
+
+
+def build_layer(seed: int = 0):
+    from huffman_decode_df11_amd import api, synth
+    t0 = time.time()
+    mats = synth.llama_layer(seed=seed, layer=0)
+    hist = None
+    for _, m in mats:
+        hist = api.hist_accumulate(m, hist)
+    cb = api.build_codebook(hist)
+    encs = [(name, m, api.encode(m, codebook=cb)) for name, m in mats]
+    log("layer generated and encoded in %.1f s" % (time.time() - t0))
+    return encs
+
+
+def time_decode(dts, outbuf, steps: int, warmup: int):
+    """Time `steps` passes over all tensors; also time every launch."""
+    import torch
+    from huffman_decode_df11_amd import api
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for dt in dts:
+            api.decode(dt, out=outbuf, stream=stream)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in dts]
+          for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(steps):
+        for i, dt in enumerate(dts):
+            ev[s][i][0].record(stream)
+            api.decode(dt, out=outbuf, stream=stream)
+            ev[s][i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    per_launch = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])   # [steps, tensors] ms
+    return total_ms / steps, per_launch
+
+
+def verify(dts, mats, outbuf):
+    import torch
+    from huffman_decode_df11_amd import api
+    for dt, m in zip(dts, mats):
+        api.decode(dt, out=outbuf)
+        torch.cuda.synchronize()
+        got = outbuf.view(torch.int16)[:m.size].cpu().numpy().view(np.uint16)
+        if not np.array_equal(got, m.reshape(-1)):
+            raise SystemExit("parity check failed before timing")
+
+
+def cpu_baseline_layer(mats, budget_s: float = 20.0):
+    """The oracle's serial decode on the host, over the layer's matrices in
+    order until the time budget is used (at least one matrix)."""
+    from oracle import oracle as orc
+    from huffman_decode_df11_amd import api
+    hist = None
+    for m in mats:
+        hist = orc.histogram(m) if hist is None else hist + orc.histogram(m)
+    ln = orc.code_lengths(hist, 32)
+    elems, secs, names = 0, 0.0, 0
+    for m in mats:
+        ref = orc.encode(m, lengths=ln)
+        t0 = time.perf_counter()
+        out = orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln)
+        secs += time.perf_counter() - t0
+        elems += m.size
+        names += 1
+        if not np.array_equal(out, m.reshape(-1)):
+            raise SystemExit("oracle round trip failed")
+        del ref, out
+        if secs >= budget_s:
+            break
+    return {"value": round(2.0 * elems / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "bit-serial oracle decode of the first %d of the layer's 7 matrices "
+                      "(%d elements, %.1f s), one host thread" % (names, elems, secs)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer", choices=["layer"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path has no cross-GPU step; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from huffman_decode_df11_amd import api
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+
+    encs = build_layer(args.seed)
+    mats = [m for _, m, _ in encs]
+    dts = [e.to("cuda") for _, _, e in encs]
+    n_total = sum(e.n for _, _, e in encs)
+    biggest = max(e.n for _, _, e in encs)
+    outbuf = torch.empty(biggest, dtype=torch.bfloat16, device="cuda")
+    verify(dts, mats, outbuf)
+    log("parity verified on all %d matrices" % len(dts))
+
+    ms_per_step, per_launch = time_decode(dts, outbuf, args.steps, args.warmup)
+    alg = [algorithmic_bytes(e) for _, _, e in encs]
+    launch_ms = per_launch.mean(axis=0)                  # average duration per tensor
+    achieved = (sum(alg) / len(alg)) / (launch_ms.mean() * 1e-3) / 1e9
+    compressed = sum(e.compressed_nbytes() for _, _, e in encs)
+    stream_bits = sum(e.total_bits for _, _, e in encs)
+
+    result = {
+        "metric": "decoded BF16 GB/s (df11_decode, Llama-3-8B layer)",
+        "value": round(2.0 * n_total / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3-8b-layer: q,k,v,o,gate,up,down bf16 N(0,0.02), 218,103,808 elements, "
+                        "one codebook, decoded into one reused buffer",
+            "elements": n_total,
+            "launches_per_step": len(dts),
+            "bits_per_weight": round(8.0 * compressed / n_total, 4),
+            "exponent_bits_per_weight": round(stream_bits / n_total, 4),
+            "parallelism": "1 GPU",
+        },
+        "elements_per_s": round(n_total / (ms_per_step * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "decode_kernel",
+            "algorithmic_bytes_per_element": round(sum(alg) / n_total, 4),
+            "launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_layer(mats)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

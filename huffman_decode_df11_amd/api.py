@@ -1,0 +1,220 @@
+"""Thin Python binding over libdf11.so: argument marshalling only.
+
+Every step of the codec runs in the library -- the host encoder in C++ and
+the decode paths in HIP kernels on the GPU.  PyTorch provides device memory
+and streams.  There is no Python or CPU fallback: if the library is missing
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import _lib
+from ._lib import Codebook, Layout, View, check, lib
+
+DEFAULT_MAX_LEN = 32
+DEFAULT_FAST_BITS = _lib.DF11_FAST_BITS_DEFAULT
+
+
+def _u16(bits) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(bits, torch.Tensor):
+            if bits.is_cuda:
+                raise ValueError("the encoder runs on the host: pass a CPU tensor or numpy array")
+            bits = bits.contiguous().view(torch.int16).numpy()
+    except ImportError:
+        pass
+    a = np.asarray(bits)
+    if a.dtype not in (np.uint16, np.int16):
+        raise TypeError("BF16 weights are passed as their 16-bit patterns (uint16/int16), got %s" % a.dtype)
+    return np.ascontiguousarray(a.reshape(-1)).view(np.uint16)
+
+
+def hist_accumulate(bits, hist: Optional[np.ndarray] = None) -> np.ndarray:
+    """Add the exponent counts of `bits` to `hist` (new zeros if None)."""
+    u = _u16(bits)
+    if hist is None:
+        hist = np.zeros(256, np.uint64)
+    assert hist.dtype == np.uint64 and hist.size == 256 and hist.flags.c_contiguous
+    check(lib().df11_hist_accumulate(u.ctypes.data, u.size, hist.ctypes.data), "df11_hist_accumulate")
+    return hist
+
+
+def build_codebook(hist, max_len: int = DEFAULT_MAX_LEN, fast_bits: int = DEFAULT_FAST_BITS) -> Codebook:
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    cb = Codebook()
+    check(lib().df11_codebook_build(h.ctypes.data, max_len, fast_bits, ctypes.byref(cb)), "df11_codebook_build")
+    return cb
+
+
+def codebook_lengths(cb: Codebook) -> np.ndarray:
+    return np.frombuffer(bytes(cb.len), dtype=np.uint8).copy()
+
+
+def codebook_codes(cb: Codebook) -> np.ndarray:
+    return np.ctypeslib.as_array(cb.code).astype(np.uint32).copy()
+
+
+def make_layout(chunk_bytes: int = 16, align_elems: int = 0, rows: int = 0, cols: int = 0,
+                tile_rows: int = 0, tile_cols: int = 0) -> Layout:
+    return Layout(chunk_bytes=chunk_bytes, seg_lanes=64, align_elems=align_elems, rows=rows,
+                  cols=cols, tile_rows=tile_rows, tile_cols=tile_cols)
+
+
+def gemm_layout(rows: int, cols: int) -> Layout:
+    lay = Layout()
+    check(lib().df11_gemm_layout(rows, cols, ctypes.byref(lay)), "df11_gemm_layout")
+    return lay
+
+
+def gemm_tile() -> tuple:
+    L = lib()
+    return int(L.df11_gemm_tile_rows()), int(L.df11_gemm_tile_cols())
+
+
+class Encoded:
+    """A host encoding owned by the library (freed with the object)."""
+
+    def __init__(self, handle: int, codebook: Codebook, shape: tuple):
+        self._handle = ctypes.c_void_p(handle)
+        self.codebook = codebook
+        self.shape = shape
+        self.view = View()
+        check(lib().df11_encoded_view(self._handle, ctypes.byref(self.view)), "df11_encoded_view")
+        self.arrays = {}
+        for name, ct in _lib.VIEW_ARRAYS:
+            count = int(getattr(self.view, "n_" + name))
+            ptr = getattr(self.view, name)
+            nbytes = count * ctypes.sizeof(ct)
+            if nbytes:
+                buf = (ctypes.c_uint8 * nbytes).from_address(ptr)
+                self.arrays[name] = np.frombuffer(buf, dtype=np.uint8)
+            else:
+                self.arrays[name] = np.zeros(0, np.uint8)
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h is not None and h.value:
+            lib().df11_encoded_free(h)
+            self._handle = None
+
+    # typed views of the host arrays
+    @property
+    def exp_words(self): return self.arrays["exp_words"].view(np.uint32)
+    @property
+    def sm(self): return self.arrays["sm"]
+    @property
+    def gaps(self): return self.arrays["gaps"]
+    @property
+    def seg_elem(self): return self.arrays["segs"].view(np.uint64).reshape(-1, 2)[:, 0]
+    @property
+    def seg_nbits(self): return self.arrays["segs"].view(np.uint32).reshape(-1, 4)[:, 2]
+    @property
+    def chain(self): return self.arrays["chain"].view(np.uint16)
+    @property
+    def fast(self): return self.arrays["fast"].view(np.uint32)
+
+    @property
+    def n(self) -> int: return int(self.view.n)
+    @property
+    def total_bits(self) -> int: return int(self.view.total_bits)
+    @property
+    def n_segments(self) -> int: return int(self.view.n_segments)
+
+    def stream_bytes_msb_first(self) -> np.ndarray:
+        """The exponent stream as a byte sequence, first bit in bit 7 of byte 0."""
+        nbytes = (self.total_bits + 7) // 8
+        return self.exp_words.byteswap().view(np.uint8)[:nbytes]
+
+    def compressed_nbytes(self) -> int:
+        """Bytes a decode reads: stream, sign+mantissa, gaps, segment records, tables."""
+        return sum(a.size for a in self.arrays.values())
+
+    def bits_per_weight(self) -> float:
+        return 8.0 * self.compressed_nbytes() / max(self.n, 1)
+
+    def validate(self) -> None:
+        check(lib().df11_validate(ctypes.byref(self.view), ctypes.byref(self.codebook)), "df11_validate")
+
+    def to(self, device="cuda") -> "DF11Tensor":
+        return DF11Tensor(self, device)
+
+
+def encode(bits, codebook: Optional[Codebook] = None, layout: Optional[Layout] = None,
+           max_len: int = DEFAULT_MAX_LEN, fast_bits: int = DEFAULT_FAST_BITS) -> Encoded:
+    """Encode BF16 bit patterns on the host.  Without a codebook one is built
+    from this tensor's own exponent histogram."""
+    shape = tuple(np.shape(bits)) if not hasattr(bits, "shape") else tuple(bits.shape)
+    u = _u16(bits)
+    if codebook is None:
+        codebook = build_codebook(hist_accumulate(u), max_len, fast_bits)
+    h = ctypes.c_void_p()
+    lay = ctypes.byref(layout) if layout is not None else None
+    check(lib().df11_encode(u.ctypes.data, u.size, ctypes.byref(codebook), lay, ctypes.byref(h)), "df11_encode")
+    return Encoded(h.value, codebook, shape)
+
+
+class DF11Tensor:
+    """An encoded tensor resident in device memory, plus its device view."""
+
+    def __init__(self, enc: Encoded, device="cuda"):
+        import torch
+        self.shape = enc.shape
+        self.n = enc.n
+        self.codebook = enc.codebook
+        self.host_view = enc.view
+        self.tensors = {}
+        for name, _ in _lib.VIEW_ARRAYS:
+            a = enc.arrays[name]
+            t = torch.from_numpy(a.copy() if a.size else np.zeros(16, np.uint8)).to(device)
+            self.tensors[name] = t
+        self.view = View()
+        ctypes.memmove(ctypes.byref(self.view), ctypes.byref(enc.view), ctypes.sizeof(View))
+        for name, _ in _lib.VIEW_ARRAYS:
+            setattr(self.view, name, self.tensors[name].data_ptr())
+        self.device = self.tensors["sm"].device
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.tensors.values())
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def decode(t: DF11Tensor, out=None, stream=None):
+    """Decode to BF16 on the GPU (bit-exact).  Returns `out` (a new
+    torch.bfloat16 tensor of t.shape when None)."""
+    import torch
+    if out is None:
+        out = torch.empty(t.shape if t.shape else (t.n,), dtype=torch.bfloat16, device=t.device)
+    assert out.is_cuda and out.is_contiguous() and out.numel() >= t.n and out.element_size() == 2
+    check(lib().df11_decode(ctypes.byref(t.view), out.data_ptr(), _stream_handle(stream)), "df11_decode")
+    return out
+
+
+def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None):
+    """y = x @ W^T with W decoded tile by tile inside the kernel.  x: [B, K]
+    bf16 on the GPU; returns y [B, N] float32."""
+    import torch
+    N, K = int(w.host_view.rows), int(w.host_view.cols)
+    assert x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[1] == K
+    x = x.contiguous()
+    B = x.shape[0]
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    assert out.is_contiguous() and out.dtype == torch.float32 and out.numel() == B * N
+    wd = 0
+    if w_debug is not None:
+        assert w_debug.is_contiguous() and w_debug.numel() == N * K and w_debug.element_size() == 2
+        wd = w_debug.data_ptr()
+    check(lib().df11_decode_gemm(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), wd,
+                                 _stream_handle(stream)), "df11_decode_gemm")
+    return out

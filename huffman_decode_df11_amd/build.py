@@ -1,0 +1,71 @@
+"""Build libdf11.so in-tree: HIP kernels for gfx950 with hipcc, host C++ with g++.
+
+    python -m huffman_decode_df11_amd.build
+
+The library lands in huffman_decode_df11_amd/_build/libdf11.so.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+OUT_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(OUT_DIR, "libdf11.so")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HIP_SOURCES = ["decode.hip", "decode_gemm.hip"]
+CPP_SOURCES = ["host_codebook.cpp", "host_encode.cpp", "host_validate.cpp"]
+
+# Packed FP32 instructions are kept out of every HIP object.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+
+
+def _run_all(cmds):
+    procs = [(c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)) for c in cmds]
+    failed = []
+    for c, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        if p.returncode != 0:
+            failed.append((c, text))
+        elif text.strip():
+            sys.stderr.write(text)
+    if failed:
+        msg = "\n\n".join(" ".join(c) + "\n" + t for c, t in failed)
+        raise RuntimeError("libdf11 build failed:\n" + msg)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    cmds, objs = [], []
+    for src in HIP_SOURCES:
+        path = os.path.join(CSRC, src)
+        if not os.path.exists(path):
+            continue
+        obj = os.path.join(OUT_DIR, src + ".o")
+        cmds.append([HIPCC, *HIP_FLAGS, "-c", path, "-o", obj])
+        objs.append(obj)
+    for src in CPP_SOURCES:
+        obj = os.path.join(OUT_DIR, src + ".o")
+        cmds.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    if verbose:
+        for c in cmds:
+            print(" ".join(c))
+    _run_all(cmds)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run_all([[HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,31 @@
+// Internal declarations shared by the host sources of libdf11.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/df11.h"
+
+namespace df11 {
+
+// Record a failure for df11_last_error() and return `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+void canonical_codes(const uint8_t *len, uint32_t *code);
+uint16_t chain_walk(const uint16_t *chain, uint32_t window);
+int build_tables(df11_codebook *cb);
+
+}  // namespace df11
+
+struct df11_encoded {
+    uint64_t n = 0, total_bits = 0, n_segments = 0;
+    df11_layout layout{};
+    uint32_t min_len = 0, max_len = 0, n_tables = 0, fast_bits = 0;
+    std::vector<uint32_t> exp_words;
+    std::vector<uint8_t> sm;
+    std::vector<uint8_t> gaps;
+    std::vector<df11_segment> segs;
+    std::vector<uint16_t> chain;
+    std::vector<uint32_t> fast;
+};

@@ -1,0 +1,220 @@
+/*
+ * df11.h -- C ABI of libdf11.so, an MI355X (gfx950) implementation of the
+ * DFloat11 (Dynamic-length Float) codec for BF16 weights.
+ *
+ * What the codec computes (sources cited by page title and section):
+ *   [P1] "DFloat11无损压缩技术：基于哈夫曼编码的BFloat16大模型显存优化方案"
+ *        (jsqmd.com) 2.1: a BF16 word is 1 sign bit, 8 exponent bits and
+ *        7 mantissa bits.  2.2 item 1: the exponents' frequencies are counted
+ *        and a Huffman code gives frequent exponents short codes.  2.2 item 2:
+ *        sign and mantissa are kept unchanged next to the variable-length
+ *        exponent code, packed into aligned blocks (about 11 bits per weight).
+ *        2.2 item 3: the compressed weights stay in GPU memory and a GPU
+ *        kernel restores BF16 right before the matmul that uses them.
+ *   [P2] "DFloat11：用于高效 GPU 推理的 LLM 和扩散模型无损压缩"
+ *        (gittoolsai.com), "工作原理": Huffman-coded BF16 exponents, decoded
+ *        on the GPU before each matrix product, output bit-for-bit identical.
+ *   [P3] "DFloat11重新定义LLM无损压缩的技术边界" (ocdem.com) 2.2: compact
+ *        hierarchical lookup tables, a locate phase and a reconstruct phase,
+ *        and a parallel prefix sum for output positions; 4.2: each thread
+ *        takes a fixed run of encoded bytes; 5.2: 256-byte aligned data.
+ *
+ * Conventions
+ *   - Every function returns DF11_OK (0) or a negative DF11_E_* status, and
+ *     never throws.  df11_last_error() gives the calling thread's detail text
+ *     for the most recent failure.
+ *   - BF16 tensors are passed as their uint16 bit patterns.
+ *   - "host" pointers are CPU memory; "device" pointers are GPU memory of the
+ *     current HIP device.  Device work is asynchronous on `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream).  The library
+ *     allocates no device memory in any call and keeps no per-call state.
+ *
+ * Stream format (what df11_encode writes and the kernels read)
+ *   exp_words  The exponent codes of all elements in stream order, each code
+ *              most significant bit first, laid end to end.  Stream bit j is
+ *              bit (31 - j % 32) of 32-bit word j / 32.  Zero bits pad the
+ *              stream; when layout.align_elems > 0 zero bits also pad each
+ *              block of align_elems elements up to a segment boundary.
+ *   sm         One byte per element: sign in bit 7, mantissa in bits 6..0.
+ *   segments   The stream is cut into segments of seg_lanes * chunk_bytes
+ *              bytes; a segment is decoded by one 64-lane wavefront, each lane
+ *              taking one chunk of chunk_bytes bytes.
+ *   gaps       One byte per chunk: the distance in bits from the chunk start
+ *              to the first code that starts at or after it (0..31), or 0 for
+ *              a chunk at or past its segment's last code.
+ *   segs       n_segments + 1 records: elem_off = number of codes that start
+ *              before the segment (the last record's elem_off = n); nbits =
+ *              bits from the segment start to the end of the last code that
+ *              starts in it, at most the segment size.
+ *   chain      The hierarchical lookup tables: n_tables tables of 256 uint16
+ *              entries.  Table 0 is indexed by the next 8 stream bits, each
+ *              later table by the 8 bits after its parent's.  Entry bit 15
+ *              clear: a code ends here -- exponent in bits 0..7, total code
+ *              length in bits 8..13.  Bit 15 set: bits 0..14 name the next
+ *              table.
+ *   fast       2^fast_bits pairs of uint32 {syms, meta} indexed by the next
+ *              fast_bits stream bits: the up to 4 whole codes that fit, first
+ *              code in the lowest byte, each byte the exponent rotated right
+ *              by one bit; meta = (count << 16) - bits consumed, modulo 2^32;
+ *              meta = 0 when the first code is longer than fast_bits.
+ *   Element order is row-major, or, when tile_rows > 0, tile order: the
+ *   [rows, cols] matrix is cut into tile_rows x tile_cols tiles taken row
+ *   block by row block, row-major inside each tile.
+ */
+#ifndef DF11_H
+#define DF11_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DF11_OK 0
+#define DF11_E_ARG (-1)       /* null/misaligned pointer, size or layout out of range */
+#define DF11_E_UNCODED (-2)   /* an input exponent has no code in the codebook */
+#define DF11_E_CODE_LEN (-3)  /* max_len outside 1..32, or more than DF11_MAX_TABLES tables */
+#define DF11_E_FORMAT (-4)    /* df11_validate found an inconsistent stream or codebook */
+#define DF11_E_DEVICE (-5)    /* a HIP call failed; detail in df11_last_error() */
+#define DF11_E_ALLOC (-6)     /* host allocation failed */
+#define DF11_E_UNSUPPORTED (-7) /* a valid request this build does not handle */
+
+#define DF11_MAX_LEN 32
+#define DF11_MAX_TABLES 64
+#define DF11_FAST_BITS_MIN 8
+#define DF11_FAST_BITS_MAX 12
+#define DF11_FAST_BITS_DEFAULT 11
+#define DF11_SEG_LANES 64
+
+/* A codebook: code lengths, canonical codes and the lookup tables derived
+ * from them.  Plain data; the caller owns the struct. */
+typedef struct df11_codebook {
+    uint32_t max_len;     /* longest code length (0 when no symbol occurs) */
+    uint32_t min_len;     /* shortest code length */
+    uint32_t n_symbols;   /* exponents with a code */
+    uint32_t n_tables;    /* hierarchical 256-entry tables used in chain[] */
+    uint32_t fast_bits;   /* index width of fast[] */
+    uint32_t reserved[3];
+    uint8_t len[256];     /* code length per exponent, 0 = no code */
+    uint32_t code[256];   /* canonical code per exponent, right-aligned */
+    uint16_t chain[DF11_MAX_TABLES * 256];
+    uint32_t fast[2u << DF11_FAST_BITS_MAX];
+} df11_codebook;
+
+/* How the stream is laid out.  Zero-initialise and set what you need:
+ * chunk_bytes 0 means 16; seg_lanes 0 means 64. */
+typedef struct df11_layout {
+    uint32_t chunk_bytes;   /* stream bytes per lane: multiple of 4 in 4..32 */
+    uint32_t seg_lanes;     /* lanes per segment: must be 64 */
+    uint64_t align_elems;   /* 0, or begin a new segment every align_elems elements */
+    uint64_t rows, cols;    /* matrix shape; cols = 0 means a flat tensor of rows = n */
+    uint32_t tile_rows, tile_cols;  /* 0, 0: row-major; else tile order (see above) */
+} df11_layout;
+
+typedef struct df11_segment {
+    uint64_t elem_off;
+    uint32_t nbits;
+    uint32_t reserved;
+} df11_segment;
+
+/* Pointers and sizes of one encoded tensor.  The pointers are all host or all
+ * device memory; the caller fills a device view by copying every array of a
+ * host view to the GPU and keeping the scalars. */
+typedef struct df11_view {
+    uint64_t n;             /* elements */
+    uint64_t total_bits;    /* end of the last code in the stream */
+    uint64_t n_segments;
+    uint32_t chunk_bytes, seg_lanes;
+    uint64_t rows, cols;
+    uint32_t tile_rows, tile_cols;
+    uint64_t align_elems;
+    uint32_t min_len, max_len, n_tables, fast_bits;
+    const uint32_t *exp_words;  uint64_t n_exp_words;  /* n_segments*seg_words + 2 */
+    const uint8_t *sm;          uint64_t n_sm;         /* n rounded up to 16 */
+    const uint8_t *gaps;        uint64_t n_gaps;       /* n_segments * seg_lanes */
+    const df11_segment *segs;   uint64_t n_segs;       /* n_segments + 1 */
+    const uint16_t *chain;      uint64_t n_chain;      /* n_tables * 256 */
+    const uint32_t *fast;       uint64_t n_fast;       /* 2 << fast_bits */
+} df11_view;
+
+typedef struct df11_encoded df11_encoded;   /* opaque, library-owned host arrays */
+
+/* ---------------------------------------------------------------- host side */
+
+/* hist[e] += number of elements of bf16_bits[0..n) whose exponent is e
+ * ([P1] 2.2 item 1).  Accumulates, so several tensors can share one codebook.
+ * bf16_bits and hist are host pointers; n = 0 is a no-op.  Errors: E_ARG for
+ * a null pointer with n > 0. */
+int df11_hist_accumulate(const uint16_t *bf16_bits, uint64_t n, uint64_t hist[256]);
+
+/* Build a codebook from an exponent histogram ([P1] 2.2 item 1; [P2]
+ * "工作原理"): Huffman code lengths, replaced by the optimal code limited to
+ * max_len bits (package-merge) when Huffman is longer; canonical codes in
+ * (length, exponent) order; the hierarchical tables ([P3] 2.2) and the
+ * fast_bits-wide multi-code table.  max_len in 1..32, fast_bits in 8..12.
+ * Errors: E_ARG (null), E_CODE_LEN (max_len out of range or too small for
+ * the number of symbols, or more than DF11_MAX_TABLES tables). */
+int df11_codebook_build(const uint64_t hist[256], uint32_t max_len, uint32_t fast_bits,
+                        df11_codebook *cb);
+
+/* Encode n BF16 words (host) with codebook cb into a new library-owned
+ * encoding ([P1] 2.2 item 2; [P3] 4.2): exponent stream, sign+mantissa
+ * bytes, per-lane gaps and per-segment records, laid out by `layout` (NULL
+ * = defaults).  *out receives the encoding; free it with df11_encoded_free.
+ * Errors: E_ARG (null pointers, layout out of range, rows*cols != n, tile
+ * shape not dividing the matrix or tile_cols not a multiple of 16),
+ * E_UNCODED (an exponent without a code), E_ALLOC. */
+int df11_encode(const uint16_t *bf16_bits, uint64_t n, const df11_codebook *cb,
+                const df11_layout *layout, df11_encoded **out);
+
+void df11_encoded_free(df11_encoded *enc);
+
+/* Fill *v with host pointers into enc (valid until df11_encoded_free). */
+int df11_encoded_view(const df11_encoded *enc, df11_view *v);
+
+/* The layout df11_decode_gemm needs for an [rows, cols] weight: tile order
+ * with tiles of df11_gemm_tile_rows() x df11_gemm_tile_cols() elements, each
+ * tile beginning a segment.  Errors: E_ARG when the shape does not divide. */
+int df11_gemm_layout(uint64_t rows, uint64_t cols, df11_layout *layout);
+uint32_t df11_gemm_tile_rows(void);
+uint32_t df11_gemm_tile_cols(void);
+
+/* O(n) CPU check of a host view against its codebook: array sizes, table
+ * consistency, gaps and segment records recomputed by walking the stream.
+ * Returns DF11_OK or E_FORMAT / E_ARG with the first problem in
+ * df11_last_error().  Detection path for corrupt data; the kernels do not
+ * check streams. */
+int df11_validate(const df11_view *host_view, const df11_codebook *cb);
+
+/* -------------------------------------------------------------- device side */
+
+/* Decode a device view into out[0..n) BF16 bits in row-major order
+ * ([P1] 2.2 item 3; [P3] 2.2 locate/reconstruct with a prefix sum).
+ * out: device, 16-byte aligned, n elements.  Bit-exact: every input pattern,
+ * including zeros, subnormals, Inf and NaN payloads, comes back unchanged.
+ * Writes stay inside out[0..n) even for a corrupt stream (then the values are
+ * unspecified).  n = 0 is a no-op.  Errors: E_ARG (null, misaligned, view
+ * inconsistent), E_UNSUPPORTED (tables too large for the kernel), E_DEVICE. */
+int df11_decode(const df11_view *device_view, uint16_t *out, void *stream);
+
+/* Fused decode + matrix product ([P1] 2.2 item 3: decoded weights feed the
+ * matmul and are discarded): y[b][j] = sum_k x[b][k] * W[j][k] for W the
+ * [rows = N, cols = K] weight of `w` (encoded with df11_gemm_layout), x a
+ * device [B, K] BF16 row-major matrix, y a device [B, N] float32 matrix.
+ * Products of BF16 values are exact in float32 and accumulate in float32.
+ * w_debug: NULL, or a device [N, K] buffer that also receives the decoded
+ * BF16 weights.  B in 1..256.  Errors: E_ARG (null, misaligned, layout not
+ * from df11_gemm_layout, B out of range), E_UNSUPPORTED, E_DEVICE. */
+int df11_decode_gemm(const df11_view *device_view, const uint16_t *x, uint32_t B,
+                     float *y, uint16_t *w_debug, void *stream);
+
+/* ---------------------------------------------------------------- utilities */
+const char *df11_status_string(int status);
+const char *df11_last_error(void);
+const char *df11_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DF11_H */

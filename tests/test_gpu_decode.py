@@ -1,0 +1,180 @@
+"""GPU parity of df11_decode against the oracle (bit-exact), through the C ABI.
+
+The oracle's decode of its own encoding is the input itself (pinned by the
+round-trip tests), so the expected output of every case is the oracle's
+decode; for large inputs it is the input bits, which the oracle reproduces
+exactly, checked on sampled segments."""
+import sys
+
+import numpy as np
+import pytest
+
+from huffman_decode_df11_amd import api, synth
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+SENTINELS = (0x5555, 0xAAAA)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _to_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+
+
+def _decode_checked(dt, n, margin=64):
+    """Decode twice into buffers pre-filled with two different sentinels and
+    a guard margin: every element must be written (both runs agree) and no
+    element past n may change."""
+    outs = []
+    for s in SENTINELS:
+        buf = torch.full((n + margin,), s - 65536 if s >= 32768 else s, dtype=torch.int16, device="cuda")
+        api.decode(dt, out=buf.view(torch.bfloat16))
+        torch.cuda.synchronize()
+        b = _to_bits(buf)
+        assert (b[n:] == s).all(), "decode wrote past the end of the output"
+        outs.append(b[:n])
+    assert np.array_equal(outs[0], outs[1]), "some outputs were not written"
+    return outs[0]
+
+
+def _check(u, layout=None, fast_bits=11, max_len=32, oracle=True, tag=""):
+    u = np.ascontiguousarray(u).reshape(-1)
+    _say("case", tag, "n=%d fast_bits=%d" % (u.size, fast_bits))
+    enc = api.encode(u, layout=layout, fast_bits=fast_bits, max_len=max_len)
+    dt = enc.to("cuda")
+    got = _decode_checked(dt, u.size)
+    if oracle:
+        ln = api.codebook_lengths(enc.codebook)
+        ref = orc.encode(u, lengths=ln, chunk_bytes=16, align_elems=layout.align_elems if layout else 0)
+        want = orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln,
+                          seg_bits=16 * 8 * 64, align_elems=layout.align_elems if layout else 0)
+    else:
+        want = u
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "%d mismatches, first at %s: got %04x want %04x" % (
+        bad.size, bad[:5], got[bad[0]], want[bad[0]])
+    return enc
+
+
+@pytest.mark.parametrize("fast_bits", [8, 9, 10, 11, 12])
+def test_tensor_1024x1024(fast_bits):
+    _check(synth.tensor_1024(seed=0), fast_bits=fast_bits, tag="1024x1024")
+
+
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 255, 1000, 4097, 65537, 1_000_003])
+def test_ragged_sizes(n):
+    _check(synth.normal_bf16(n, 0.02, seed=n), tag="ragged")
+
+
+def test_exhaustive_all_patterns():
+    _check(synth.exhaustive_bf16(), tag="exhaustive")
+
+
+def test_adversarial_small():
+    _check(synth.adversarial_bf16(1 << 20, seed=1), tag="adversarial-1M")
+
+
+def test_adversarial_full_16m():
+    u = synth.adversarial_bf16(1 << 24, seed=0)
+    enc = _check(u, oracle=False, tag="adversarial-16M")
+    _oracle_sampled(enc, u)
+
+
+def test_fibonacci_32bit_codes():
+    u = synth.fibonacci_bf16()
+    enc = _check(u, oracle=False, tag="fibonacci")
+    assert enc.codebook.max_len == 32     # the 32-bit limit binds (Huffman would need 33)
+
+
+@pytest.mark.parametrize("lmax", [12, 16])
+def test_length_limited(lmax):
+    _check(synth.adversarial_bf16(1 << 20, seed=2), max_len=lmax, tag="lmax%d" % lmax)
+
+
+def test_one_and_two_symbols():
+    one = (np.full(100_003, 0x3F80, np.uint16) | (np.arange(100_003) % 256).astype(np.uint16)).astype(np.uint16)
+    _check(one, tag="one-symbol")
+    two = np.where(np.arange(77_777) % 5 == 0, 0xBF80, 0x4000).astype(np.uint16)
+    _check(two, tag="two-symbols")
+
+
+def test_aligned_layout():
+    _check(synth.normal_bf16(500_000, 0.02, seed=3), layout=api.make_layout(align_elems=4096), tag="aligned")
+
+
+def test_tile_order_decodes_row_major():
+    rows, cols = 128, 2048
+    u = synth.normal_bf16(rows * cols, 0.02, seed=4).reshape(rows, cols)
+    lay = api.make_layout(rows=rows, cols=cols, tile_rows=32, tile_cols=512, align_elems=32 * 512)
+    _say("case tile order")
+    enc = api.encode(u, layout=lay)
+    got = _decode_checked(enc.to("cuda"), u.size)
+    assert np.array_equal(got, u.reshape(-1))
+
+
+def test_empty():
+    enc = api.encode(np.zeros(0, np.uint16))
+    dt = enc.to("cuda")
+    out = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
+    api.decode(dt, out=out)
+    torch.cuda.synchronize()
+    assert (_to_bits(out) == 0).all()
+
+
+def _oracle_sampled(enc, u, nseg=24, seed=0):
+    """The oracle decodes sampled segments of the library's stream on its own
+    (bit-serial) and must reproduce the same elements."""
+    ln = api.codebook_lengths(enc.codebook)
+    stream = enc.stream_bytes_msb_first()
+    rng = np.random.default_rng(seed)
+    segs = rng.choice(enc.n_segments, size=min(nseg, enc.n_segments), replace=False)
+    seg_bits = 16 * 8 * 64
+    for s in segs:
+        g0, g1 = int(enc.seg_elem[s]), int(enc.seg_elem[s + 1])
+        if g1 == g0:
+            continue
+        # first code of segment s starts at s*seg_bits + gap of its first lane
+        start = int(s) * seg_bits + int(enc.gaps[int(s) * 64])
+        # the segment's codes, re-aligned so the first one starts at bit 0
+        sub = np.zeros(seg_bits // 8 + 16, np.uint8)
+        b0 = start // 8
+        chunk = stream[b0:b0 + seg_bits // 8 + 8]
+        sub[:chunk.size] = chunk
+        bits = np.unpackbits(sub)[start - 8 * b0:]
+        packed = np.packbits(bits)
+        out = orc.decode(packed, bits.size, enc.sm[g0:g1], g1 - g0, ln)
+        assert np.array_equal(out, u[g0:g1]), "segment %d" % s
+
+
+def test_llama_layer_full_size_reused_buffer():
+    """The seven Llama-3-8B-shaped matrices of one layer, one codebook for the
+    layer, each decoded into one reused BF16 buffer."""
+    mats = synth.llama_layer(seed=0, layer=0)
+    hist = None
+    for _, m in mats:
+        hist = api.hist_accumulate(m, hist)
+    cb = api.build_codebook(hist)
+    biggest = max(m.size for _, m in mats)
+    buf = torch.empty(biggest + 64, dtype=torch.int16, device="cuda")
+    for name, m in mats:
+        _say("case llama", name, m.shape)
+        enc = api.encode(m, codebook=cb)
+        dt = enc.to("cuda")
+        buf.fill_(0x5555)
+        api.decode(dt, out=buf.view(torch.bfloat16))
+        torch.cuda.synchronize()
+        got = _to_bits(buf)
+        assert np.array_equal(got[:m.size], m.reshape(-1)), name
+        assert (got[m.size:] == 0x5555).all()
+        if name in ("up_proj", "k_proj"):
+            _oracle_sampled(enc, m.reshape(-1), nseg=8)
+        del dt, enc

@@ -1,0 +1,260 @@
+"""CPU tests of libdf11's host half against the oracle: exported symbols, code
+optimality, canonical codes, stream, sign+mantissa bytes, gaps, segment
+records, both lookup tables, the validator and the error paths."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from huffman_decode_df11_amd import _lib, api, synth
+from oracle import oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _cost(hist, lengths):
+    return int(sum(int(h) * int(l) for h, l in zip(hist, lengths)))
+
+
+def _kraft_units(lengths):
+    return sum(1 << (32 - int(l)) for l in lengths if l)
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "df11.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"\b(df11_[a-z_0-9]+)\s*\(", text))
+    assert declared, "no declarations found"
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [s for s in sorted(declared) if not hasattr(L, s)]
+    assert not missing, missing
+    assert set(_lib.EXPORTS) == declared
+
+
+WORKLOADS = {
+    "normal": lambda: synth.normal_bf16(300_000, 0.02, seed=11),
+    "adversarial": lambda: synth.adversarial_bf16(300_000, seed=12),
+    "exhaustive": synth.exhaustive_bf16,
+    "fibonacci": lambda: synth.fibonacci_bf16(),
+    "one_symbol": lambda: np.full(5000, 0x3F80, np.uint16) | np.arange(5000, dtype=np.uint16) % 128,
+    "two_symbols": lambda: np.where(np.arange(7001) % 3 == 0, 0x3F80, 0x4000).astype(np.uint16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_codebook_is_optimal_and_canonical(name):
+    u = WORKLOADS[name]()
+    h = api.hist_accumulate(u)
+    assert np.array_equal(h, orc.histogram(u))
+    cb = api.build_codebook(h, 32)
+    ln = api.codebook_lengths(cb)
+    want = orc.code_lengths(h, 32)
+    assert _cost(h, ln) == _cost(h, want)            # optimal (lengths themselves may differ)
+    assert ln.max() <= 32
+    assert all((ln[s] > 0) == (h[s] > 0) for s in range(256))
+    if (h > 0).sum() >= 2:
+        assert _kraft_units(ln) == 1 << 32
+    assert np.array_equal(api.codebook_codes(cb), orc.canonical_codes(ln))
+    assert cb.max_len == ln.max() and cb.min_len == ln[ln > 0].min()
+
+
+@pytest.mark.parametrize("lmax", [10, 12, 16, 20])
+def test_codebook_length_limit_matches_package_merge(lmax):
+    u = synth.adversarial_bf16(200_000, seed=13)
+    h = api.hist_accumulate(u)
+    cb = api.build_codebook(h, lmax)
+    ln = api.codebook_lengths(cb)
+    assert ln.max() <= lmax
+    assert _cost(h, ln) == _cost(h, orc.code_lengths(h, lmax))
+
+
+def _chain_walk(chain, window):
+    t = 0
+    for level in range(4):
+        e = int(chain[t * 256 + ((window >> (24 - 8 * level)) & 0xFF)])
+        if not e & 0x8000:
+            return e & 0xFF, (e >> 8) & 0x3F
+        t = e & 0x7FFF
+    return None
+
+
+@pytest.mark.parametrize("name", ["normal", "adversarial", "fibonacci", "exhaustive"])
+def test_lookup_tables_against_oracle_codes(name):
+    u = WORKLOADS[name]()
+    enc = api.encode(u)
+    ln = api.codebook_lengths(enc.codebook)
+    codes = orc.canonical_codes(ln)
+    chain = enc.chain
+    rng = np.random.default_rng(5)
+    # every code, with random suffixes, walks to its own exponent and length
+    for s in range(256):
+        if not ln[s]:
+            continue
+        L = int(ln[s])
+        for suf in rng.integers(0, 1 << 32, size=4, dtype=np.uint64):
+            win = ((int(codes[s]) << (32 - L)) | (int(suf) >> L)) & 0xFFFFFFFF
+            assert _chain_walk(chain, win) == (s, L)
+    # the multi-code table: greedy decode of the window with the oracle's codes
+    K = enc.codebook.fast_bits
+    byprefix = {(int(codes[s]), int(ln[s])): s for s in range(256) if ln[s]}
+    fast = enc.fast.reshape(-1, 2)
+    for idx in range(1 << K):
+        bits = format(idx, "0%db" % K)
+        pos, syms = 0, []
+        while len(syms) < 4:
+            hit = None
+            for L in range(1, K - pos + 1):
+                key = (int(bits[pos:pos + L], 2), L)
+                if key in byprefix:
+                    hit = (byprefix[key], L)
+                    break
+            if hit is None:
+                break
+            syms.append(hit[0])
+            pos += hit[1]
+        want_meta = ((len(syms) << 16) - pos) & 0xFFFFFFFF if syms else 0
+        want_syms = 0
+        for i, e in enumerate(syms):
+            want_syms |= (((e >> 1) | (e << 7)) & 0xFF) << (8 * i)
+        assert int(fast[idx, 1]) == want_meta, idx
+        assert int(fast[idx, 0]) == want_syms, idx
+
+
+LAYOUTS = {
+    "default": dict(),
+    "chunk8": dict(chunk_bytes=8),
+    "chunk32": dict(chunk_bytes=32),
+    "aligned": dict(align_elems=4096),
+}
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+@pytest.mark.parametrize("name", ["normal", "adversarial", "fibonacci", "two_symbols", "one_symbol"])
+def test_encoder_matches_oracle(name, layout):
+    u = WORKLOADS[name]()
+    kw = LAYOUTS[layout]
+    enc = api.encode(u, layout=api.make_layout(**kw))
+    ln = api.codebook_lengths(enc.codebook)
+    ref = orc.encode(u, lengths=ln, chunk_bytes=kw.get("chunk_bytes", 16), seg_lanes=64,
+                     align_elems=kw.get("align_elems", 0))
+    assert enc.total_bits == ref.total_bits
+    assert np.array_equal(enc.stream_bytes_msb_first(), ref.E)
+    assert np.array_equal(enc.sm[:enc.n], ref.sm) and not enc.sm[enc.n:].any()
+    assert enc.n_segments == ref.n_segments
+    assert np.array_equal(enc.gaps, ref.gaps)
+    assert np.array_equal(enc.seg_elem, ref.seg_elem)
+    assert np.array_equal(enc.seg_nbits[:-1], ref.seg_nbits)
+    enc.validate()
+    # the oracle's bit-serial decoder reads the library's stream back
+    out = orc.decode(enc.stream_bytes_msb_first(), enc.total_bits, enc.sm[:enc.n], enc.n, ln,
+                     seg_bits=8 * 64 * kw.get("chunk_bytes", 16), align_elems=kw.get("align_elems", 0))
+    assert np.array_equal(out, u)
+
+
+def test_encoder_tile_order_matches_oracle_permutation():
+    rows, cols, tr, tc = 64, 1024, 32, 512
+    u = synth.normal_bf16(rows * cols, 0.02, seed=14).reshape(rows, cols)
+    lay = api.make_layout(rows=rows, cols=cols, tile_rows=tr, tile_cols=tc, align_elems=tr * tc)
+    enc = api.encode(u, layout=lay)
+    ln = api.codebook_lengths(enc.codebook)
+    perm = orc.tile_order(u, rows, cols, tr, tc)
+    ref = orc.encode(perm, lengths=ln, align_elems=tr * tc)
+    assert np.array_equal(enc.stream_bytes_msb_first(), ref.E)
+    assert np.array_equal(enc.sm[:enc.n], ref.sm)
+    assert np.array_equal(enc.gaps, ref.gaps)
+    assert np.array_equal(enc.seg_elem, ref.seg_elem)
+    enc.validate()
+
+
+def test_gemm_layout_shape_rules():
+    tr, tc = api.gemm_tile()
+    lay = api.gemm_layout(14336, 4096)
+    assert lay.tile_rows == tr and lay.tile_cols == tc and lay.align_elems == tr * tc
+    with pytest.raises(_lib.DF11Error):
+        api.gemm_layout(14336 + 1, 4096)
+
+
+def test_empty_tensor_encodes():
+    enc = api.encode(np.zeros(0, np.uint16))
+    assert enc.n == 0 and enc.n_segments == 0 and enc.total_bits == 0
+    enc.validate()
+
+
+# --------------------------------------------------------------- error paths
+
+def test_uncoded_exponent_rejected():
+    u = synth.normal_bf16(1000, 0.02, seed=15)
+    cb = api.build_codebook(api.hist_accumulate(u))
+    v = u.copy()
+    v[7] = 0x7F80   # Inf: exponent 255 never occurred
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.encode(v, codebook=cb)
+    assert ei.value.status == -2
+
+
+@pytest.mark.parametrize("max_len", [0, 33])
+def test_bad_max_len_rejected(max_len):
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.build_codebook(np.ones(256, np.uint64), max_len)
+    assert ei.value.status == -3
+
+
+def test_too_many_tables_rejected():
+    # 9-bit limit over ~256 exponents: every 8-bit prefix would need its own table
+    h = api.hist_accumulate(synth.adversarial_bf16(200_000, seed=13))
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.build_codebook(h, 9)
+    assert ei.value.status == -3
+
+
+def test_max_len_too_small_rejected():
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.build_codebook(np.ones(256, np.uint64), 7)    # 256 symbols need 8 bits
+    assert ei.value.status == -3
+
+
+@pytest.mark.parametrize("kw", [dict(chunk_bytes=6), dict(chunk_bytes=64), dict(align_elems=10),
+                                dict(rows=3, cols=5), dict(rows=100, cols=100, tile_rows=3, tile_cols=16)])
+def test_bad_layout_rejected(kw):
+    u = synth.normal_bf16(10_000, 0.02, seed=16)
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.encode(u, layout=api.make_layout(**kw))
+    assert ei.value.status == -1
+
+
+def _corrupt_and_validate(enc, mutate):
+    mutate(enc)
+    with pytest.raises(_lib.DF11Error) as ei:
+        enc.validate()
+    assert ei.value.status in (-4, -1)
+
+
+@pytest.mark.parametrize("what", ["stream_bit", "gap", "seg_elem", "seg_nbits", "chain", "fast",
+                                  "codebook_len", "n_segments"])
+def test_validator_catches_corruption(what):
+    u = synth.normal_bf16(200_000, 0.02, seed=17)
+    enc = api.encode(u)
+    enc.validate()
+
+    def mutate(e):
+        if what == "stream_bit":
+            w = e.exp_words
+            w[w.size // 3] ^= 0x00400000
+        elif what == "gap":
+            g = e.gaps
+            g[100] = (int(g[100]) + 3) % 32
+        elif what == "seg_elem":
+            e.seg_elem[5] += 1
+        elif what == "seg_nbits":
+            e.seg_nbits[e.n_segments - 1] -= 1
+        elif what == "chain":
+            e.chain[3] ^= 1
+        elif what == "fast":
+            e.fast[10] ^= 1
+        elif what == "codebook_len":
+            e.codebook.len[121] += 1
+        elif what == "n_segments":
+            e.view.n_segments -= 1
+    _corrupt_and_validate(enc, mutate)
