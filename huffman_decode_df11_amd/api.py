@@ -99,7 +99,10 @@ class Encoded:
     def __del__(self):
         h = getattr(self, "_handle", None)
         if h is not None and h.value:
-            lib().df11_encoded_free(h)
+            try:
+                lib().df11_encoded_free(h)
+            except Exception:   # interpreter shutdown: the module may be gone
+                pass
             self._handle = None
 
     # typed views of the host arrays

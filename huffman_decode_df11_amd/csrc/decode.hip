@@ -1,5 +1,5 @@
-// df11_decode / df11_decode_batch: restore BF16 weights from the DFloat11
-// stream on the GPU, right before the matmul that consumes them.
+// df11_decode: restore BF16 weights from the DFloat11 stream on the GPU,
+// right before the matmul that consumes them.
 //
 // [P1] "DFloat11无损压缩技术：基于哈夫曼编码的BFloat16大模型显存优化方案" 2.2
 //      item 3: compressed weights stay in GPU memory; a kernel reads, decodes
@@ -10,9 +10,13 @@
 //
 // Mapping to gfx950: one 64-lane wavefront per segment, so the prefix sum is
 // a wavefront scan and no workgroup barrier sits on the decode path.  A
-// workgroup of WAVES waves stages the tables in LDS once and then loops over
-// segments.  Exponents are staged in LDS and merged with the sign+mantissa
-// bytes in 16-element groups: 16-byte loads of sm, 32-byte BF16 stores.
+// workgroup of WAVES waves stages the tables in LDS once; each wave then
+// walks its segments with the next segment's stream words and this
+// segment's sign+mantissa bytes already in flight, so global-memory latency
+// overlaps the LDS-bound decode.  Exponents are staged in LDS and merged
+// with the sign+mantissa bytes in 16-element groups: 16-byte loads, 32-byte
+// BF16 stores; the at most 30 elements of a segment's two ragged groups are
+// written one per lane.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -25,6 +29,12 @@ using namespace df11dev;
 
 namespace {
 
+constexpr uint32_t kChunkBytes = 16;
+constexpr uint32_t kChunkBits = 8 * kChunkBytes;
+constexpr uint32_t kSegWords = 64 * kChunkBytes / 4;
+constexpr uint32_t kSlotBytes = 4 * kSlotWords;
+constexpr int kPrefetchRounds = 4;
+
 struct ViewArgs {
     const uint32_t *words;
     const uint8_t *sm;
@@ -33,7 +43,6 @@ struct ViewArgs {
     uint16_t *out;
     uint64_t n;
     uint64_t n_segments;
-    uint64_t seg_begin;       // first global segment id of this view (batch launches)
     // tile order (tr == 0: row-major)
     uint32_t tr, tc, tiles_per_row, pad;
     uint64_t cols;
@@ -56,104 +65,125 @@ __device__ __forceinline__ uint64_t out_index(const ViewArgs &v, uint64_t g)
     return (rb * v.tr + r) * v.cols + cb * v.tc + c;
 }
 
-// Decode segment `s` of view v with one wavefront.  stg: LDS byte offset of
-// this wave's exponent staging; ereg: LDS byte offset of its word region.
-template <int CB, int K>
-__device__ __forceinline__ void decode_segment(const ViewArgs &v, uint64_t s, uint8_t *lds,
-                                               uint32_t stg, uint32_t ereg, uint32_t stg_bytes,
-                                               const uint2 *fast, const uint16_t *chain)
+// Everything a wave needs from global memory to start a segment.
+struct SegLoad {
+    uint4 own;          // this lane's 4 stream words
+    uint32_t next;      // the following word (look-ahead)
+    uint32_t gap;
+    uint64_t g0, g1;
+    uint32_t nbits;
+};
+
+__device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, uint32_t lane)
 {
-    constexpr uint32_t kChunkBits = 8 * CB;
-    const uint32_t lane = lane_id();
-    const uint64_t g0 = v.segs[s].elem_off;
-    const uint64_t g1 = v.segs[s + 1].elem_off;
-    const uint32_t nbits = v.segs[s].nbits;
-    if (g1 > v.n || g1 < g0) return;                                   // corrupt records
-    const uint32_t head = (uint32_t)(g0 & 15);
-    if ((uint64_t)head + (g1 - g0) + 32 > stg_bytes) return;           // cannot be a valid segment
-
-    const uint32_t rbase = stage_segment<CB>(lds, ereg, v.words, s);
-    const uint32_t gap = v.gaps[s * 64 + lane];
-    wave_lds_sync();
-
-    const SegWindow win{lds, rbase};
-    const uint32_t c0 = lane * kChunkBits;
-    const uint32_t p0 = c0 + gap;
-    const uint32_t end = min(c0 + kChunkBits, nbits);
-    const uint32_t cnt = p0 < end ? count_codes<K>(win, fast, chain, p0, end) : 0u;
-    uint32_t total;
-    const uint32_t excl = wave_exclusive_scan(cnt, &total);
-    if (total != (uint32_t)(g1 - g0)) return;                          // stream and records disagree
-
-    emit_codes<K>(win, fast, chain, lds, p0, stg + head + excl, cnt);
-    wave_lds_sync();
-
-    // merge: 16-element groups aligned to the stream index
-    const uint64_t gbase = g0 & ~15ull;
-    const uint32_t ngroups = (uint32_t)((((g1 + 15) & ~15ull) - gbase) >> 4);
-    const uint8_t *sm = v.sm;
-    for (uint32_t gi = lane; gi < ngroups; gi += 64) {
-        const uint64_t gs = gbase + 16ull * gi;
-        const uint4 smv = *reinterpret_cast<const uint4 *>(sm + gs);
-        const uint4 rx = *reinterpret_cast<const uint4 *>(lds + stg + 16 * gi);
-        const uint64_t o = out_index(v, gs);
-        if (gs >= g0 && gs + 16 <= g1) {
-            const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
-            const uint2 c = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
-            uint4 *dst = reinterpret_cast<uint4 *>(v.out + o);
-            dst[0] = make_uint4(a.x, a.y, b.x, b.y);
-            dst[1] = make_uint4(c.x, c.y, d.x, d.y);
-        } else {
-            const uint32_t smw[4] = {smv.x, smv.y, smv.z, smv.w};
-            const uint32_t rxw[4] = {rx.x, rx.y, rx.z, rx.w};
-#pragma unroll
-            for (uint32_t j = 0; j < 16; j++) {
-                const uint64_t g = gs + j;
-                if (g >= g0 && g < g1)
-                    v.out[o + j] = assemble1(smw[j >> 2] >> (8 * (j & 3)), rxw[j >> 2] >> (8 * (j & 3)));
-            }
-        }
-    }
-    wave_lds_sync();   // staging is reused by this wave's next segment
+    SegLoad L;
+    const uint32_t *w = v.words + s * kSegWords + lane * 4;
+    L.own = *reinterpret_cast<const uint4 *>(w);
+    L.next = w[4];
+    L.gap = v.gaps[s * 64 + lane];
+    L.g0 = v.segs[s].elem_off;
+    L.g1 = v.segs[s + 1].elem_off;
+    L.nbits = v.segs[s].nbits;
+    return L;
 }
 
-template <int CB>
-constexpr uint32_t ereg_bytes() { return (64 * (CB / 4) + 8) * 4; }
-
-// Stage both tables into LDS once per workgroup.
-template <int K>
-__device__ __forceinline__ void stage_tables(uint8_t *lds, uint32_t fast_off, uint32_t chain_off,
-                                             const TableArgs &t)
-{
-    uint32_t *fl = reinterpret_cast<uint32_t *>(lds + fast_off);
-    for (uint32_t i = threadIdx.x; i < (2u << K); i += blockDim.x) fl[i] = t.fast[i];
-    uint16_t *cl = reinterpret_cast<uint16_t *>(lds + chain_off);
-    for (uint32_t i = threadIdx.x; i < t.n_chain; i += blockDim.x) cl[i] = t.chain[i];
-    __syncthreads();
-}
-
-template <int CB, int K, int WAVES>
+template <int K, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_kernel(ViewArgs v, TableArgs t)
 {
-    extern __shared__ __align__(16) uint8_t lds[];
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t stg = 16 + wave * t.stg_bytes;
-    const uint32_t ereg_off = 16 + WAVES * t.stg_bytes;
-    const uint32_t ereg = ereg_off + wave * ereg_bytes<CB>();
-    const uint32_t fast_off = ereg_off + WAVES * ereg_bytes<CB>();
-    const uint32_t chain_off = fast_off + (8u << K);
-    stage_tables<K>(lds, fast_off, chain_off, t);
-    const uint2 *fast = reinterpret_cast<const uint2 *>(lds + fast_off);
-    const uint16_t *chain = reinterpret_cast<const uint16_t *>(lds + chain_off);
-    for (uint64_t s = (uint64_t)blockIdx.x * WAVES + wave; s < v.n_segments; s += (uint64_t)gridDim.x * WAVES)
-        decode_segment<CB, K>(v, s, lds, stg, ereg, t.stg_bytes, fast, chain);
+    const uint32_t lane = lane_id();
+    const uint32_t stg = lds0 + 16 + wave * t.stg_bytes;
+    const uint32_t slots = lds0 + 16 + WAVES * t.stg_bytes;
+    const uint32_t slot = slots + (wave * 64 + lane) * kSlotBytes;
+    const uint32_t fast = (slots + WAVES * 64 * kSlotBytes + 15) & ~15u;
+    const uint32_t chain = fast + (8u << K);
+
+    // tables into LDS, once per workgroup
+    for (uint32_t i = threadIdx.x; i < (2u << K); i += blockDim.x) st32(fast + 4 * i, t.fast[i]);
+    for (uint32_t i = threadIdx.x; i < t.n_chain; i += blockDim.x)
+        *(lds_u16 *)(size_t)(chain + 2 * i) = t.chain[i];
+    __syncthreads();
+
+    uint64_t s = (uint64_t)blockIdx.x * WAVES + wave;
+    const uint64_t stride = (uint64_t)gridDim.x * WAVES;
+    if (s >= v.n_segments) return;
+    SegLoad nx = load_segment(v, s, lane);
+    for (;;) {
+        const SegLoad cur = nx;
+        const uint32_t rbase = stage_chunk(slot, cur.own, cur.next);
+        const uint64_t g0 = cur.g0, g1 = cur.g1;
+        const uint64_t gbase = g0 & ~15ull;
+        const uint32_t head = (uint32_t)(g0 & 15);
+        const bool valid = g1 <= v.n && g1 >= g0 && (uint64_t)head + (g1 - g0) + 32 <= t.stg_bytes;
+        const uint32_t ngroups = valid ? (uint32_t)((((g1 + 15) & ~15ull) - gbase) >> 4) : 0u;
+
+        // this segment's sign+mantissa bytes, first rounds
+        uint4 smp[kPrefetchRounds];
+#pragma unroll
+        for (int r = 0; r < kPrefetchRounds; r++) {
+            const uint32_t gi = lane + 64u * r;
+            smp[r] = gi < ngroups ? *reinterpret_cast<const uint4 *>(v.sm + gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
+        }
+        // the next segment's stream words and records
+        const uint64_t s_next = s + stride;
+        const bool more = s_next < v.n_segments;
+        if (more) nx = load_segment(v, s_next, lane);
+        wave_lds_sync();
+
+        if (valid) {
+            const uint32_t c0 = lane * kChunkBits;
+            const uint32_t end = cur.nbits > c0 ? min(kChunkBits, cur.nbits - c0) : 0u;
+            const uint32_t p0 = cur.gap;
+            const uint32_t cnt = p0 < end ? count_codes<K>(rbase, fast, chain, p0, end) : 0u;
+            uint32_t total;
+            const uint32_t excl = wave_exclusive_scan(cnt, &total);
+            if (total == (uint32_t)(g1 - g0)) {
+                emit_codes<K>(rbase, fast, chain, p0, stg + head + excl, cnt);
+                wave_lds_sync();
+
+                // whole 16-element groups
+                for (uint32_t r = 0; 64u * r < ngroups; r++) {
+                    const uint32_t gi = lane + 64u * r;
+                    uint4 smv;
+                    if (r < kPrefetchRounds) {
+                        smv = r == 0 ? smp[0] : r == 1 ? smp[1] : r == 2 ? smp[2] : smp[3];
+                    } else {
+                        smv = gi < ngroups ? *reinterpret_cast<const uint4 *>(v.sm + gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
+                    }
+                    const uint64_t gs = gbase + 16ull * gi;
+                    if (gi < ngroups && gs >= g0 && gs + 16 <= g1) {
+                        const uint4 rx = ld128(stg + 16 * gi);
+                        const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
+                        const uint2 c = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
+                        uint4 *dst = reinterpret_cast<uint4 *>(v.out + out_index(v, gs));
+                        dst[0] = make_uint4(a.x, a.y, b.x, b.y);
+                        dst[1] = make_uint4(c.x, c.y, d.x, d.y);
+                    }
+                }
+                // ragged ends: lanes 0..15 the head group, lanes 16..31 the tail group
+                const uint64_t hend = min((g0 + 15) & ~15ull, g1);
+                const uint64_t tstart = max(g1 & ~15ull, hend);
+                const uint64_t g = lane < 16 ? g0 + lane : tstart + (lane - 16);
+                const bool act = lane < 16 ? g < hend : (lane < 32 && g < g1);
+                if (act) {
+                    const uint32_t rx = *(const lds_u8 *)(size_t)(stg + (uint32_t)(g - gbase));
+                    v.out[out_index(v, g)] = assemble1(v.sm[g], rx);
+                }
+            }
+        }
+        wave_lds_sync();   // slots and staging are reused by the next segment
+        if (!more) break;
+        s = s_next;
+    }
 }
 
-int check_view(const df11_view *v, uint64_t out_elems)
+int check_view(const df11_view *v)
 {
     if (!v) return df11::fail(DF11_E_ARG, "null view");
-    if (v->seg_lanes != 64 || v->chunk_bytes != 16)
+    if (v->seg_lanes != 64 || v->chunk_bytes != kChunkBytes)
         return df11::fail(DF11_E_UNSUPPORTED, "decode kernels are built for 16-byte chunks and 64-lane segments (got %u, %u)",
                           v->chunk_bytes, v->seg_lanes);
     if (v->fast_bits < DF11_FAST_BITS_MIN || v->fast_bits > DF11_FAST_BITS_MAX)
@@ -161,9 +191,8 @@ int check_view(const df11_view *v, uint64_t out_elems)
     if (v->n_tables < 1 || v->n_tables > DF11_MAX_TABLES || v->n_chain != (uint64_t)v->n_tables * 256 ||
         v->n_fast != (2ull << v->fast_bits))
         return df11::fail(DF11_E_ARG, "table sizes inconsistent");
-    const uint64_t seg_words = 64ull * v->chunk_bytes / 4;
     if (v->n_segs != v->n_segments + 1 || v->n_gaps != v->n_segments * 64 ||
-        v->n_exp_words < v->n_segments * seg_words + 2 || v->n_sm < (v->n + 15) / 16 * 16)
+        v->n_exp_words < v->n_segments * kSegWords + 2 || v->n_sm < (v->n + 15) / 16 * 16)
         return df11::fail(DF11_E_ARG, "view array sizes inconsistent with n / n_segments");
     if (v->n && (!v->exp_words || !v->sm || !v->gaps || !v->segs || !v->chain || !v->fast))
         return df11::fail(DF11_E_ARG, "null array in view");
@@ -175,13 +204,14 @@ int check_view(const df11_view *v, uint64_t out_elems)
             (uint64_t)v->tile_rows * v->tile_cols > 0xFFFFFFFFull)
             return df11::fail(DF11_E_ARG, "bad tile order in view");
     }
-    (void)out_elems;
     return DF11_OK;
 }
 
+// Exponent staging per wave: room for the most codes a segment can hold
+// (segment bits / shortest code), a 16-element head offset and a tail group.
 uint32_t staging_bytes(const df11_view *v)
 {
-    const uint32_t seg_bits = 64u * 8u * v->chunk_bytes;
+    const uint32_t seg_bits = 64u * kChunkBits;
     const uint32_t minlen = std::max(1u, v->min_len);
     const uint32_t tmax = seg_bits / minlen + 1;
     return (16 + tmax + 32 + 15) & ~15u;
@@ -192,13 +222,14 @@ struct LaunchShape {
     uint32_t lds;
 };
 
-// Pick waves per workgroup so that exponent staging stays under 64 KB (the
-// emit loop keeps LDS addresses in 16 bits) and the total fits 160 KB.
+// Waves per workgroup: exponent staging must stay in the first 64 KB of LDS
+// (the emit loop keeps byte addresses in 16 bits) and everything in 160 KB.
 int pick_shape(uint32_t stg, uint32_t fast_bits, uint32_t n_tables, LaunchShape *sh)
 {
-    const uint32_t tables = (8u << fast_bits) + ((n_tables * 512u + 15) & ~15u);
+    const uint32_t tables = (8u << fast_bits) + n_tables * 512u;
     for (int w : {8, 4, 2, 1}) {
-        const uint32_t total = 16 + w * stg + w * ereg_bytes<16>() + tables;
+        const uint32_t slots = ((uint32_t)w * 64 * kSlotBytes + 15) & ~15u;
+        const uint32_t total = 16 + w * stg + slots + tables;
         if (16 + (uint32_t)w * stg <= 65520 && total <= 160 * 1024) {
             sh->waves = w;
             sh->lds = total;
@@ -221,7 +252,7 @@ int device_cu_count()
     return cus;
 }
 
-ViewArgs make_args(const df11_view *v, uint16_t *out, uint64_t seg_begin)
+ViewArgs make_args(const df11_view *v, uint16_t *out)
 {
     ViewArgs a{};
     a.words = v->exp_words;
@@ -231,7 +262,6 @@ ViewArgs make_args(const df11_view *v, uint16_t *out, uint64_t seg_begin)
     a.out = out;
     a.n = v->n;
     a.n_segments = v->n_segments;
-    a.seg_begin = seg_begin;
     a.tr = v->tile_rows;
     a.tc = v->tile_cols;
     a.tiles_per_row = v->tile_rows ? (uint32_t)(v->cols / v->tile_cols) : 0;
@@ -247,10 +277,10 @@ int launch_one(const ViewArgs &a, const TableArgs &t, const LaunchShape &sh, uin
     const uint64_t groups = std::min<uint64_t>(groups_needed, (uint64_t)device_cu_count() * per_cu);
     if (!groups) return DF11_OK;
     switch (sh.waves) {
-    case 8: hipLaunchKernelGGL((decode_kernel<16, K, 8>), dim3((uint32_t)groups), dim3(512), sh.lds, st, a, t); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<16, K, 4>), dim3((uint32_t)groups), dim3(256), sh.lds, st, a, t); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<16, K, 2>), dim3((uint32_t)groups), dim3(128), sh.lds, st, a, t); break;
-    default: hipLaunchKernelGGL((decode_kernel<16, K, 1>), dim3((uint32_t)groups), dim3(64), sh.lds, st, a, t); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<K, 8>), dim3((uint32_t)groups), dim3(512), sh.lds, st, a, t); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<K, 4>), dim3((uint32_t)groups), dim3(256), sh.lds, st, a, t); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<K, 2>), dim3((uint32_t)groups), dim3(128), sh.lds, st, a, t); break;
+    default: hipLaunchKernelGGL((decode_kernel<K, 1>), dim3((uint32_t)groups), dim3(64), sh.lds, st, a, t); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode launch: %s", hipGetErrorString(e));
@@ -261,7 +291,7 @@ int launch_one(const ViewArgs &a, const TableArgs &t, const LaunchShape &sh, uin
 
 extern "C" int df11_decode(const df11_view *v, uint16_t *out, void *stream)
 {
-    int rc = check_view(v, v ? v->n : 0);
+    int rc = check_view(v);
     if (rc) return rc;
     if (!v->n) return DF11_OK;
     if (!out || ((uintptr_t)out & 15)) return df11::fail(DF11_E_ARG, "out must be a 16-byte aligned device pointer");
@@ -269,7 +299,7 @@ extern "C" int df11_decode(const df11_view *v, uint16_t *out, void *stream)
     LaunchShape sh;
     if ((rc = pick_shape(stg, v->fast_bits, v->n_tables, &sh))) return rc;
     TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, stg};
-    const ViewArgs a = make_args(v, out, 0);
+    const ViewArgs a = make_args(v, out);
     hipStream_t st = (hipStream_t)stream;
     switch (v->fast_bits) {
     case 8: return launch_one<8>(a, t, sh, v->n_segments, st);

@@ -1,7 +1,8 @@
 // Device building blocks shared by the decode and fused decode+GEMM kernels.
 //
 // One 64-lane wavefront decodes one segment of the exponent stream:
-//   stage   the segment's words go to LDS in reversed word order;
+//   stage   every lane copies its chunk of stream words (plus one look-ahead
+//           word) into a private, padded LDS slot;
 //   locate  every lane counts the codes that start in its chunk ([P3]
 //           "DFloat11重新定义LLM无损压缩的技术边界" 2.2 Phase 1), reading the
 //           multi-code table and, for long codes, the hierarchical tables;
@@ -14,13 +15,13 @@
 // bytes ([P1] "DFloat11无损压缩技术：基于哈夫曼编码的BFloat16大模型显存优化方案"
 // 2.2 item 2) into BF16.
 //
-// Bit cursor.  A lane keeps one 32-bit state word: bits 0..15 hold
-// kM0 - p for stream position p (bits from the segment start) and bits
-// 16..31 hold a count or an LDS byte address.  A multi-code table entry's
-// meta = (codes << 16) - bits, so `state += meta` advances both halves.
-// With the segment's words stored reversed in LDS, the 32-bit window at p is
-// alignbit(word[(p-1)>>5], word[((p-1)>>5)+1], -p), whose two words are
-// adjacent in LDS at an address linear in (state >> 5) & 0x7FF.
+// Bit cursor.  A lane keeps one 32-bit state word: bits 0..15 hold kM0 - p
+// for the bit position p inside its chunk and bits 16..31 hold a count or an
+// LDS byte address.  A multi-code table entry's meta = (codes << 16) - bits,
+// so `state += meta` advances both halves at once.  The lane's words are
+// stored in reversed order, so the 32-bit window at p,
+// alignbit(word[(p-1)>>5], word[((p-1)>>5)+1], -p), reads two adjacent LDS
+// words at an address linear in (state >> 5) & 0x7FF.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,81 +29,98 @@
 
 namespace df11dev {
 
-constexpr uint32_t kM0 = 65504;          // multiple of 32, above any segment size
+constexpr uint32_t kM0 = 65504;          // multiple of 32, above any chunk size
 constexpr uint32_t kQ = kM0 / 32;
+constexpr uint32_t kSlotWords = 7;       // per-lane stream slot: 6 words used, odd stride
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v2u32 lds_u2;
+typedef __attribute__((address_space(3))) v4u32 lds_u4;
+
+// LDS accesses by 32-bit byte address
+__device__ __forceinline__ uint32_t ld32(uint32_t a) { return *(const lds_u32 *)(size_t)a; }
+__device__ __forceinline__ uint16_t ld16(uint32_t a) { return *(const lds_u16 *)(size_t)a; }
+__device__ __forceinline__ uint2 ld64(uint32_t a)
+{
+    const v2u32 v = *(const lds_u2 *)(size_t)a;
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 ld128(uint32_t a)
+{
+    const v4u32 v = *(const lds_u4 *)(size_t)a;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st8(uint32_t a, uint32_t v) { *(lds_u8 *)(size_t)a = (uint8_t)v; }
+__device__ __forceinline__ void st32(uint32_t a, uint32_t v) { *(lds_u32 *)(size_t)a = v; }
+
+// a * (1 << sh) + b as one v_lshl_add_u32 (kept out of the compiler's reach:
+// it would otherwise rewrite the bitfield extract as shift + and + add)
+template <int SH>
+__device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "i"(SH), "v"(b));
+    return r;
+}
+
+// the same with a wave-uniform b held in a scalar register
+template <int SH>
+__device__ __forceinline__ uint32_t lshl_add_s(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "i"(SH), "s"(b));
+    return r;
+}
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
-// LDS byte pointer helpers (generic pointers into __shared__ memory)
-__device__ __forceinline__ uint32_t lds_u32(const uint8_t *lds, uint32_t byte_addr)
+// The 32-bit window of a lane's chunk at the position held in `st`.
+__device__ __forceinline__ uint32_t window(uint32_t rbase, uint32_t st)
 {
-    return *reinterpret_cast<const uint32_t *>(lds + byte_addr);
+    const uint32_t a = lshl_add<2>(__builtin_amdgcn_ubfe(st, 5, 11), rbase);
+    const uint32_t w_next = ld32(a);        // word[a'+1]
+    const uint32_t w_cur = ld32(a + 4);     // word[a']
+    return __builtin_amdgcn_alignbit(w_cur, w_next, st);
 }
 
-struct SegWindow {
-    const uint8_t *lds;    // base of dynamic LDS
-    uint32_t rbase;        // byte address such that word[(p-1)>>5] sits at rbase + 4*((state>>5)&0x7FF) + 4
-    __device__ __forceinline__ uint32_t operator()(uint32_t st) const
-    {
-        const uint32_t d = __builtin_amdgcn_ubfe(st, 5, 11);
-        const uint32_t a = rbase + 4u * d;
-        const uint32_t w_next = lds_u32(lds, a);        // word[a'+1]
-        const uint32_t w_cur = lds_u32(lds, a + 4);     // word[a']
-        return __builtin_amdgcn_alignbit(w_cur, w_next, st);
-    }
-};
-
-// First code of a window through the hierarchical tables in LDS.  Returns
-// exponent | length << 8; a malformed walk yields length 32.
-__device__ __forceinline__ uint32_t chain_decode(const uint16_t *chain, uint32_t win)
+// First code of a window through the hierarchical tables at LDS byte
+// address `chain`.  Returns exponent | length << 8; a malformed walk yields
+// length 32 so that every step advances.
+__device__ __forceinline__ uint32_t chain_decode(uint32_t chain, uint32_t win)
 {
-    uint32_t e = chain[win >> 24];
+    uint32_t e = ld16(lshl_add_s<1>(win >> 24, chain));
     if (e & 0x8000u) {
-        e = chain[(e & 0x7FFFu) * 256u + ((win >> 16) & 0xFFu)];
+        e = ld16(chain + 2u * ((e & 0x7FFFu) * 256u + ((win >> 16) & 0xFFu)));
         if (e & 0x8000u) {
-            e = chain[(e & 0x7FFFu) * 256u + ((win >> 8) & 0xFFu)];
+            e = ld16(chain + 2u * ((e & 0x7FFFu) * 256u + ((win >> 8) & 0xFFu)));
             if (e & 0x8000u) {
-                e = chain[(e & 0x7FFFu) * 256u + (win & 0xFFu)];
+                e = ld16(chain + 2u * ((e & 0x7FFFu) * 256u + (win & 0xFFu)));
                 if (e & 0x8000u) e = 32u << 8;
             }
         }
     }
-    if (!(e & 0x3F00u)) e = 32u << 8;   // never advance by zero bits
+    if (!(e & 0x3F00u)) e = 32u << 8;
     return e;
 }
 
 __device__ __forceinline__ uint32_t rot_exp(uint32_t e) { return ((e >> 1) | (e << 7)) & 0xFFu; }
 
-// Stage one segment's words into LDS in reversed order.  region: LDS byte
-// offset of a (seg_words + 8)-word, 16-byte aligned region.  Word i of the
-// segment lands at word index K0 - i with K0 = region/4 + 3 + seg_words;
-// word seg_words (the next segment's first word, read as look-ahead) at
-// region/4 + 3 and the guard word[-1] at K0 + 1.  Returns rbase.
-template <int CB>
-__device__ __forceinline__ uint32_t stage_segment(uint8_t *lds, uint32_t region,
-                                                  const uint32_t *__restrict__ words,
-                                                  uint64_t seg)
+// Per-lane stream slot: words -1..4 of the lane's chunk (4 own words, the
+// next chunk's first word as look-ahead, word -1 a never-used guard) stored
+// reversed at slot + 4*(5 - i).  Returns the lane's rbase.
+__device__ __forceinline__ uint32_t stage_chunk(uint32_t slot, uint4 own, uint32_t next)
 {
-    constexpr uint32_t kWordsPerLane = CB / 4;
-    constexpr uint32_t kSegWords = 64 * kWordsPerLane;
-    const uint32_t lane = lane_id();
-    const uint32_t *src = words + seg * kSegWords + lane * kWordsPerLane;
-    const uint32_t k0 = region / 4 + 3 + kSegWords;
-    uint32_t *ldsw = reinterpret_cast<uint32_t *>(lds);
-    if constexpr (kWordsPerLane == 4) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(src);
-        // words 4l..4l+3 go to k0-4l-3 .. k0-4l, i.e. reversed inside the uint4
-        *reinterpret_cast<uint4 *>(ldsw + (k0 - 4 * lane - 3)) = make_uint4(v.w, v.z, v.y, v.x);
-    } else {
-#pragma unroll
-        for (uint32_t i = 0; i < kWordsPerLane; i++) ldsw[k0 - kWordsPerLane * lane - i] = src[i];
-    }
-    if (lane == 0) {
-        ldsw[k0 - kSegWords] = words[(seg + 1) * kSegWords];
-        ldsw[k0 + 1] = 0;
-    }
-    // word[a'] for state st is at k0 - (kQ - 1 - d); the pair read starts one word lower
-    return 4u * (k0 - kQ);
+    st32(slot + 4, next);        // word 4
+    st32(slot + 8, own.w);       // word 3
+    st32(slot + 12, own.z);
+    st32(slot + 16, own.y);
+    st32(slot + 20, own.x);      // word 0
+    // word[a'+1] for a' = kQ - 1 - d sits at slot + 4*(5 - a' - 1)
+    return slot + 20u - 4u * kQ;
 }
 
 // Wavefront-scope ordering of LDS traffic between lanes of one wave.
@@ -113,17 +131,17 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Locate: number of codes starting in [p0, end).
+// Locate: number of codes starting in [p0, end) of the lane's chunk.
 template <int K>
-__device__ __forceinline__ uint32_t count_codes(const SegWindow &win, const uint2 *fast,
-                                                const uint16_t *chain, uint32_t p0, uint32_t end)
+__device__ __forceinline__ uint32_t count_codes(uint32_t rbase, uint32_t fast, uint32_t chain,
+                                                uint32_t p0, uint32_t end)
 {
     uint32_t st = kM0 - p0;
     const uint32_t lim = kM0 - end;            // p < end  <=>  (st & 0xFFFF) > lim
     uint32_t meta = 0;
     while ((st & 0xFFFFu) > lim) {
-        const uint32_t w = win(st);
-        meta = fast[w >> (32 - K)].y;
+        const uint32_t w = window(rbase, st);
+        meta = ld32(lshl_add_s<3>(w >> (32 - K), fast) + 4);
         if (meta == 0) meta = (1u << 16) - ((chain_decode(chain, w) >> 8) & 0x3Fu);
         st += meta;
     }
@@ -131,7 +149,7 @@ __device__ __forceinline__ uint32_t count_codes(const SegWindow &win, const uint
     // step back and redo it one code at a time
     st -= meta;
     while ((st & 0xFFFFu) > lim) {
-        const uint32_t w = win(st);
+        const uint32_t w = window(rbase, st);
         st += (1u << 16) - ((chain_decode(chain, w) >> 8) & 0x3Fu);
     }
     return st >> 16;
@@ -140,32 +158,31 @@ __device__ __forceinline__ uint32_t count_codes(const SegWindow &win, const uint
 // Emit: decode `cnt` codes from p0 and write their rotated exponents to LDS
 // bytes [wpos, wpos + cnt).  wpos + cnt must be below 65536.
 template <int K>
-__device__ __forceinline__ void emit_codes(const SegWindow &win, const uint2 *fast,
-                                           const uint16_t *chain, uint8_t *lds, uint32_t p0,
-                                           uint32_t wpos, uint32_t cnt)
+__device__ __forceinline__ void emit_codes(uint32_t rbase, uint32_t fast, uint32_t chain,
+                                           uint32_t p0, uint32_t wpos, uint32_t cnt)
 {
     uint32_t st = (kM0 - p0) | (wpos << 16);
     const uint32_t bound = (wpos + cnt - 3u) << 16;   // st < bound <=> at least 4 codes left
     while (st < bound) {
-        const uint32_t w = win(st);
-        const uint2 f = fast[w >> (32 - K)];
+        const uint32_t w = window(rbase, st);
+        const uint2 f = ld64(lshl_add_s<3>(w >> (32 - K), fast));
         uint32_t syms = f.x, meta = f.y;
         if (meta == 0) {
             const uint32_t e = chain_decode(chain, w);
             syms = rot_exp(e & 0xFFu);
             meta = (1u << 16) - ((e >> 8) & 0x3Fu);
         }
-        uint8_t *dst = lds + (st >> 16);
-        dst[0] = (uint8_t)syms;
-        dst[1] = (uint8_t)(syms >> 8);
-        dst[2] = (uint8_t)(syms >> 16);
-        dst[3] = (uint8_t)(syms >> 24);
+        const uint32_t a = st >> 16;
+        st8(a, syms);
+        st8(a + 1, syms >> 8);
+        st8(a + 2, syms >> 16);
+        st8(a + 3, syms >> 24);
         st += meta;
     }
     const uint32_t lend = wpos + cnt;
     while ((st >> 16) < lend) {
-        const uint32_t e = chain_decode(chain, win(st));
-        lds[st >> 16] = (uint8_t)rot_exp(e & 0xFFu);
+        const uint32_t e = chain_decode(chain, window(rbase, st));
+        st8(st >> 16, rot_exp(e & 0xFFu));
         st += (1u << 16) - ((e >> 8) & 0x3Fu);
     }
 }
