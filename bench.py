@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--workload", default="layer", choices=["layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path has no cross-GPU step; "
@@ -192,6 +194,13 @@ def main():
             "launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
         },
     }
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 256 << 20
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_layer(mats)
     print(json.dumps(result), flush=True)

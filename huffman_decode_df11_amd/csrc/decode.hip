@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 
 #include "df11_device.h"
@@ -217,28 +218,6 @@ uint32_t staging_bytes(const df11_view *v)
     return (16 + tmax + 32 + 15) & ~15u;
 }
 
-struct LaunchShape {
-    int waves;
-    uint32_t lds;
-};
-
-// Waves per workgroup: exponent staging must stay in the first 64 KB of LDS
-// (the emit loop keeps byte addresses in 16 bits) and everything in 160 KB.
-int pick_shape(uint32_t stg, uint32_t fast_bits, uint32_t n_tables, LaunchShape *sh)
-{
-    const uint32_t tables = (8u << fast_bits) + n_tables * 512u;
-    for (int w : {8, 4, 2, 1}) {
-        const uint32_t slots = ((uint32_t)w * 64 * kSlotBytes + 15) & ~15u;
-        const uint32_t total = 16 + w * stg + slots + tables;
-        if (16 + (uint32_t)w * stg <= 65520 && total <= 160 * 1024) {
-            sh->waves = w;
-            sh->lds = total;
-            return DF11_OK;
-        }
-    }
-    return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
-}
-
 int device_cu_count()
 {
     static int cus = 0;
@@ -269,19 +248,63 @@ ViewArgs make_args(const df11_view *v, uint16_t *out)
     return a;
 }
 
-template <int K>
-int launch_one(const ViewArgs &a, const TableArgs &t, const LaunchShape &sh, uint64_t nseg, hipStream_t st)
+// LDS bytes of a workgroup of `waves` waves: staging, stream slots, tables.
+uint32_t lds_bytes(int waves, uint32_t stg, uint32_t fast_bits, uint32_t n_tables)
 {
-    const uint64_t groups_needed = (nseg + sh.waves - 1) / sh.waves;
-    const uint64_t per_cu = std::max<uint64_t>(1, std::min<uint64_t>((160u * 1024u) / sh.lds, 32 / sh.waves));
-    const uint64_t groups = std::min<uint64_t>(groups_needed, (uint64_t)device_cu_count() * per_cu);
-    if (!groups) return DF11_OK;
-    switch (sh.waves) {
-    case 8: hipLaunchKernelGGL((decode_kernel<K, 8>), dim3((uint32_t)groups), dim3(512), sh.lds, st, a, t); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<K, 4>), dim3((uint32_t)groups), dim3(256), sh.lds, st, a, t); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<K, 2>), dim3((uint32_t)groups), dim3(128), sh.lds, st, a, t); break;
-    default: hipLaunchKernelGGL((decode_kernel<K, 1>), dim3((uint32_t)groups), dim3(64), sh.lds, st, a, t); break;
+    const uint32_t slots = ((uint32_t)waves * 64 * kSlotBytes + 15) & ~15u;
+    return 16 + (uint32_t)waves * stg + slots + (8u << fast_bits) + n_tables * 512u;
+}
+
+template <int K, int W>
+int try_launch(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
+               hipStream_t st, int *resident)
+{
+    if (waves != W) return 1;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<K, W>, W * 64, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    *resident = per_cu * W;
+    if (!a.words) return 0;   // query only
+    const uint64_t groups = std::min<uint64_t>((nseg + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
+    if (groups) hipLaunchKernelGGL((decode_kernel<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
+    return 0;
+}
+
+constexpr int kWaveChoices[] = {4, 6, 8, 10, 12};
+
+template <int K>
+int run_shape(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
+              hipStream_t st, int *resident)
+{
+    return try_launch<K, 4>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 6>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 8>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 10>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 12>(waves, a, t, lds, nseg, st, resident);
+}
+
+// Waves per workgroup: the choice with the most resident waves per CU
+// (LDS and registers both count) among those whose exponent staging stays
+// in the first 64 KB of LDS (the emit loop keeps byte addresses in 16 bits).
+// DF11_DECODE_WAVES overrides the choice for tuning.
+template <int K>
+int launch_decode(const ViewArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
+{
+    int best = 0, best_res = -1;
+    const char *env = getenv("DF11_DECODE_WAVES");
+    const int forced = env ? atoi(env) : 0;
+    ViewArgs probe{};
+    for (int w : kWaveChoices) {
+        const uint32_t lds = lds_bytes(w, t.stg_bytes, v->fast_bits, v->n_tables);
+        if (16 + (uint32_t)w * t.stg_bytes > 65520 || lds > 160u * 1024u) continue;
+        int res = 0;
+        run_shape<K>(w, probe, t, lds, 0, st, &res);
+        if (forced == w || (!forced && res > best_res)) { best = w; best_res = res; }
+        if (forced == w) break;
     }
+    if (!best) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
+    int res = 0;
+    run_shape<K>(best, a, t, lds_bytes(best, t.stg_bytes, v->fast_bits, v->n_tables), v->n_segments, st, &res);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode launch: %s", hipGetErrorString(e));
     return DF11_OK;
@@ -296,16 +319,14 @@ extern "C" int df11_decode(const df11_view *v, uint16_t *out, void *stream)
     if (!v->n) return DF11_OK;
     if (!out || ((uintptr_t)out & 15)) return df11::fail(DF11_E_ARG, "out must be a 16-byte aligned device pointer");
     const uint32_t stg = staging_bytes(v);
-    LaunchShape sh;
-    if ((rc = pick_shape(stg, v->fast_bits, v->n_tables, &sh))) return rc;
     TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, stg};
     const ViewArgs a = make_args(v, out);
     hipStream_t st = (hipStream_t)stream;
     switch (v->fast_bits) {
-    case 8: return launch_one<8>(a, t, sh, v->n_segments, st);
-    case 9: return launch_one<9>(a, t, sh, v->n_segments, st);
-    case 10: return launch_one<10>(a, t, sh, v->n_segments, st);
-    case 11: return launch_one<11>(a, t, sh, v->n_segments, st);
-    default: return launch_one<12>(a, t, sh, v->n_segments, st);
+    case 8: return launch_decode<8>(a, t, v, st);
+    case 9: return launch_decode<9>(a, t, v, st);
+    case 10: return launch_decode<10>(a, t, v, st);
+    case 11: return launch_decode<11>(a, t, v, st);
+    default: return launch_decode<12>(a, t, v, st);
     }
 }
