@@ -45,6 +45,35 @@ def algorithmic_bytes(enc) -> int:
     return stream + enc.n + enc.n_segments * 64 + (enc.n_segments + 1) * 16 + 2 * enc.n
 
 
+def measured_traffic(profile: str, sources) -> float | None:
+    """HBM bytes per decode launch from the committed rocprofv3 summary
+    (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or None
+    when the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("|", "#", "(", "`")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+DECODE_SOURCES = ("huffman_decode_df11_amd/csrc/decode.hip", "huffman_decode_df11_amd/csrc/df11_device.h")
+
+
 def build_layer(seed: int = 0):
     from huffman_decode_df11_amd import api, synth
     t0 = time.time()
@@ -188,7 +217,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode_kernel_llama3_8b_layer.md", DECODE_SOURCES),
             "kernel": "decode_kernel",
             "algorithmic_bytes_per_element": round(sum(alg) / n_total, 4),
             "launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
