@@ -51,6 +51,7 @@ class View(ctypes.Structure):
         ("segs", ctypes.c_void_p), ("n_segs", u64),
         ("chain", ctypes.c_void_p), ("n_chain", u64),
         ("fast", ctypes.c_void_p), ("n_fast", u64),
+        ("block_seg", ctypes.c_void_p), ("n_block_seg", u64),
     ]
 
 
@@ -62,6 +63,7 @@ VIEW_ARRAYS = (
     ("segs", Segment),
     ("chain", ctypes.c_uint16),
     ("fast", ctypes.c_uint32),
+    ("block_seg", ctypes.c_uint64),
 )
 
 EXPORTS = (

@@ -120,6 +120,8 @@ class Encoded:
     def chain(self): return self.arrays["chain"].view(np.uint16)
     @property
     def fast(self): return self.arrays["fast"].view(np.uint32)
+    @property
+    def block_seg(self): return self.arrays["block_seg"].view(np.uint64)
 
     @property
     def n(self) -> int: return int(self.view.n)
@@ -135,7 +137,7 @@ class Encoded:
 
     def compressed_nbytes(self) -> int:
         """Bytes a decode reads: stream, sign+mantissa, gaps, segment records, tables."""
-        return sum(a.size for a in self.arrays.values())
+        return sum(a.size for k, a in self.arrays.items() if k != "block_seg")
 
     def bits_per_weight(self) -> float:
         return 8.0 * self.compressed_nbytes() / max(self.n, 1)

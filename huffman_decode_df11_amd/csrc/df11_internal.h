@@ -28,4 +28,5 @@ struct df11_encoded {
     std::vector<df11_segment> segs;
     std::vector<uint16_t> chain;
     std::vector<uint32_t> fast;
+    std::vector<uint64_t> block_seg;
 };

@@ -149,6 +149,7 @@ extern "C" int df11_encode(const uint16_t *bits, uint64_t n, const df11_codebook
         enc->segs.assign(nseg + 1, df11_segment{0, 0, 0});
         enc->chain.assign(cb->chain, cb->chain + (size_t)cb->n_tables * 256);
         enc->fast.assign(cb->fast, cb->fast + (2u << cb->fast_bits));
+        if (L.align_elems) enc->block_seg.assign((n + L.align_elems - 1) / L.align_elems + 1, nseg);
     } catch (...) {
         delete enc;
         return fail(DF11_E_ALLOC, "out of host memory for %llu elements", (unsigned long long)n);
@@ -182,6 +183,7 @@ extern "C" int df11_encode(const uint16_t *bits, uint64_t n, const df11_codebook
     pos = 0;
     for (uint64_t g = 0; g < n; g++) {
         if (L.align_elems && g && g % L.align_elems == 0) pos = (pos + seg_bits - 1) / seg_bits * seg_bits;
+        if (L.align_elems && g % L.align_elems == 0) enc->block_seg[g / L.align_elems] = pos / seg_bits;
         const uint64_t s = pos / seg_bits;
         while (cs < s) {
             close_segment(cs);
@@ -247,6 +249,7 @@ extern "C" int df11_encoded_view(const df11_encoded *enc, df11_view *v)
     v->segs = enc->segs.data();            v->n_segs = enc->segs.size();
     v->chain = enc->chain.data();          v->n_chain = enc->chain.size();
     v->fast = enc->fast.data();            v->n_fast = enc->fast.size();
+    v->block_seg = enc->block_seg.data();  v->n_block_seg = enc->block_seg.size();
     return DF11_OK;
 }
 

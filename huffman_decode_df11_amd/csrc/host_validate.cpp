@@ -60,6 +60,21 @@ extern "C" int df11_validate(const df11_view *v, const df11_codebook *cb)
     if (v->segs[0].elem_off != 0 || v->segs[v->n_segments].elem_off != v->n)
         return fail(DF11_E_FORMAT, "first/last segment record must be 0 / n");
 
+    // aligned blocks: each block's first element opens its first segment
+    if (v->align_elems) {
+        const uint64_t nb = (v->n + v->align_elems - 1) / v->align_elems;
+        if (v->n_block_seg != nb + 1 || !v->block_seg) return fail(DF11_E_FORMAT, "block_seg size");
+        if (v->block_seg[nb] != v->n_segments) return fail(DF11_E_FORMAT, "block_seg must end with n_segments");
+        for (uint64_t b = 0; b < nb; b++) {
+            const uint64_t s = v->block_seg[b];
+            if (s > v->block_seg[b + 1] || s >= v->n_segments || v->segs[s].elem_off != b * v->align_elems ||
+                v->gaps[s * lanes] != 0)
+                return fail(DF11_E_FORMAT, "block %llu does not open segment %llu", (unsigned long long)b,
+                            (unsigned long long)s);
+        }
+    } else if (v->n_block_seg) {
+        return fail(DF11_E_FORMAT, "block_seg given without align_elems");
+    }
     // walk every segment
     std::vector<uint32_t> count(lanes);
     for (uint64_t s = 0; s < v->n_segments; s++) {

@@ -57,6 +57,9 @@
  *              code in the lowest byte, each byte the exponent rotated right
  *              by one bit; meta = (count << 16) - bits consumed, modulo 2^32;
  *              meta = 0 when the first code is longer than fast_bits.
+ *   block_seg  When align_elems > 0: for every block of align_elems elements the
+ *              index of the segment its first code starts in, followed by
+ *              n_segments (ceil(n / align_elems) + 1 entries); else empty.
  *   Element order is row-major, or, when tile_rows > 0, tile order: the
  *   [rows, cols] matrix is cut into tile_rows x tile_cols tiles taken row
  *   block by row block, row-major inside each tile.
@@ -136,6 +139,8 @@ typedef struct df11_view {
     const df11_segment *segs;   uint64_t n_segs;       /* n_segments + 1 */
     const uint16_t *chain;      uint64_t n_chain;      /* n_tables * 256 */
     const uint32_t *fast;       uint64_t n_fast;       /* 2 << fast_bits */
+    const uint64_t *block_seg;  uint64_t n_block_seg;  /* align_elems > 0: first segment of
+                                                          every aligned block, then n_segments */
 } df11_view;
 
 typedef struct df11_encoded df11_encoded;   /* opaque, library-owned host arrays */

@@ -1,0 +1,116 @@
+"""GPU parity of df11_decode_gemm (fused decode + bf16 matrix cores) through
+the C ABI: the decoded weights are bit-exact against the input (w_debug), and
+y matches the oracle's float32 product within 2e-3 relative Frobenius error
+(float32 accumulation differs only in summation order; BF16 products are
+exact)."""
+import sys
+
+import numpy as np
+import pytest
+
+from huffman_decode_df11_amd import api, synth
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+TOL = 2e-3
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _x_to_gpu(X):
+    return torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _run(W, X, with_debug=True):
+    N, K = W.shape
+    enc = api.encode(W, layout=api.gemm_layout(N, K))
+    enc.validate()
+    dt = enc.to("cuda")
+    x = _x_to_gpu(X)
+    wdbg = torch.full((N, K), 0x5555, dtype=torch.int16, device="cuda") if with_debug else None
+    y = torch.full((X.shape[0], N), float("nan"), dtype=torch.float32, device="cuda")
+    api.decode_gemm(dt, x, out=y, w_debug=wdbg.view(torch.bfloat16) if with_debug else None)
+    torch.cuda.synchronize()
+    wd = wdbg.cpu().numpy().view(np.uint16) if with_debug else None
+    return y.cpu().numpy(), wd
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a.astype(np.float64) - b) / max(np.linalg.norm(b), 1e-30))
+
+
+@pytest.mark.parametrize("B", [1, 3, 8, 31, 32, 33, 64, 100, 128, 200, 256])
+def test_small_weight_all_batch_shapes(B):
+    N, K = 96, 1536
+    _say("case gemm small B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=20).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=21)
+    y, wd = _run(W, X)
+    assert np.array_equal(wd, W), "decoded weights differ"
+    ref = orc.gemm_f64(X, W)
+    assert np.isfinite(y).all()
+    assert _rel(y, ref) < TOL
+    assert _rel(y, orc.gemm_f32(X, W).astype(np.float64)) < TOL
+
+
+def test_identity_x_recovers_weights_exactly():
+    # x = I: y[b, n] = W[n, b] exactly (one nonzero product per output)
+    N, K, B = 64, 512, 256
+    _say("case gemm identity")
+    W = synth.normal_bf16(N * K, 0.02, seed=22).reshape(N, K)
+    X = np.zeros((B, K), np.uint16)
+    X[np.arange(B), np.arange(B)] = 0x3F80
+    y, _ = _run(W, X, with_debug=False)
+    Wf = (W.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(y, Wf[:, :B].T)
+
+
+def test_adversarial_weights_decode_exactly():
+    # all exponents incl. Inf/NaN: w_debug must be bit-exact (y is not checked)
+    N, K = 64, 1024
+    _say("case gemm adversarial")
+    W = synth.adversarial_bf16(N * K, seed=23).reshape(N, K)
+    _, wd = _run(W, synth.activations_bf16(4, K, seed=24))
+    assert np.array_equal(wd, W)
+
+
+@pytest.mark.parametrize("B", [1, 8, 64, 256])
+def test_up_proj_full_size(B):
+    """Wup 14336 x 4096, the fused workload: decoded weights compared in full
+    on the GPU, y against the oracle on 48 sampled output features."""
+    N, K = 14336, 4096
+    _say("case gemm up_proj B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=1)
+    enc = api.encode(W, layout=api.gemm_layout(N, K))
+    dt = enc.to("cuda")
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg)
+    torch.cuda.synchronize()
+    wt = torch.from_numpy(W.view(np.int16)).cuda()
+    assert torch.equal(wdbg.view(torch.int16), wt), "decoded weights differ"
+    cols = np.random.default_rng(B).choice(N, size=48, replace=False)
+    ref = orc.gemm_f64(X, W[cols])
+    got = y.cpu().numpy()[:, cols]
+    assert _rel(got, ref) < TOL
+    # and the whole product against torch's float32 matmul of the same BF16 values
+    yt = (_x_to_gpu(X).float() @ wt.view(torch.bfloat16).float().T)
+    rel = float((y - yt).norm() / yt.norm())
+    assert rel < TOL
+
+
+def test_rejects_row_major_layout():
+    from huffman_decode_df11_amd import _lib
+    W = synth.normal_bf16(64 * 512, 0.02, seed=25).reshape(64, 512)
+    dt = api.encode(W, layout=api.make_layout(rows=64, cols=512)).to("cuda")
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.decode_gemm(dt, _x_to_gpu(synth.activations_bf16(2, 512)))
+    assert ei.value.status == -1
