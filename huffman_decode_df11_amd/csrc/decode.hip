@@ -13,7 +13,7 @@
 // workgroup of WAVES waves stages the tables in LDS once; each wave then
 // walks its segments with the next segment's stream words and this
 // segment's sign+mantissa bytes already in flight, so global-memory latency
-// overlaps the LDS-bound decode.  Exponents are staged in LDS and merged
+// overlaps the decode.  A lane's stream words stay in registers.  Exponents are staged in LDS and merged
 // with the sign+mantissa bytes in 16-element groups: 16-byte loads, 32-byte
 // BF16 stores; the at most 30 elements of a segment's two ragged groups are
 // written one per lane.
@@ -33,7 +33,6 @@ namespace {
 constexpr uint32_t kChunkBytes = 16;
 constexpr uint32_t kChunkBits = 8 * kChunkBytes;
 constexpr uint32_t kSegWords = 64 * kChunkBytes / 4;
-constexpr uint32_t kSlotBytes = 4 * kSlotWords;
 constexpr int kPrefetchRounds = 4;
 
 struct ViewArgs {
@@ -97,9 +96,7 @@ decode_kernel(ViewArgs v, TableArgs t)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = lane_id();
     const uint32_t stg = lds0 + 16 + wave * t.stg_bytes;
-    const uint32_t slots = lds0 + 16 + WAVES * t.stg_bytes;
-    const uint32_t slot = slots + (wave * 64 + lane) * kSlotBytes;
-    const uint32_t fast = (slots + WAVES * 64 * kSlotBytes + 15) & ~15u;
+    const uint32_t fast = lds0 + 16 + WAVES * t.stg_bytes;
     const uint32_t chain = fast + (8u << K);
 
     // tables into LDS, once per workgroup
@@ -114,7 +111,6 @@ decode_kernel(ViewArgs v, TableArgs t)
     SegLoad nx = load_segment(v, s, lane);
     for (;;) {
         const SegLoad cur = nx;
-        const uint32_t rbase = stage_chunk(slot, cur.own, cur.next);
         const uint64_t g0 = cur.g0, g1 = cur.g1;
         const uint64_t gbase = g0 & ~15ull;
         const uint32_t head = (uint32_t)(g0 & 15);
@@ -132,17 +128,17 @@ decode_kernel(ViewArgs v, TableArgs t)
         const uint64_t s_next = s + stride;
         const bool more = s_next < v.n_segments;
         if (more) nx = load_segment(v, s_next, lane);
-        wave_lds_sync();
 
         if (valid) {
             const uint32_t c0 = lane * kChunkBits;
             const uint32_t end = cur.nbits > c0 ? min(kChunkBits, cur.nbits - c0) : 0u;
             const uint32_t p0 = cur.gap;
-            const uint32_t cnt = p0 < end ? count_codes<K>(rbase, fast, chain, p0, end) : 0u;
+            const Window win = make_window(cur.own, cur.next, p0);
+            const uint32_t cnt = p0 < end ? count_codes<K>(win, fast, chain, p0, end) : 0u;
             uint32_t total;
             const uint32_t excl = wave_exclusive_scan(cnt, &total);
             if (total == (uint32_t)(g1 - g0)) {
-                emit_codes<K>(rbase, fast, chain, p0, stg + head + excl, cnt);
+                emit_codes<K>(win, fast, chain, stg + head + excl, cnt);
                 wave_lds_sync();
 
                 // whole 16-element groups
@@ -175,7 +171,7 @@ decode_kernel(ViewArgs v, TableArgs t)
                 }
             }
         }
-        wave_lds_sync();   // slots and staging are reused by the next segment
+        wave_lds_sync();   // the staging is reused by the next segment
         if (!more) break;
         s = s_next;
     }
@@ -248,11 +244,10 @@ ViewArgs make_args(const df11_view *v, uint16_t *out)
     return a;
 }
 
-// LDS bytes of a workgroup of `waves` waves: staging, stream slots, tables.
+// LDS bytes of a workgroup of `waves` waves: exponent staging and tables.
 uint32_t lds_bytes(int waves, uint32_t stg, uint32_t fast_bits, uint32_t n_tables)
 {
-    const uint32_t slots = ((uint32_t)waves * 64 * kSlotBytes + 15) & ~15u;
-    return 16 + (uint32_t)waves * stg + slots + (8u << fast_bits) + n_tables * 512u;
+    return 16 + (uint32_t)waves * stg + (8u << fast_bits) + n_tables * 512u;
 }
 
 template <int K, int W>
@@ -270,7 +265,7 @@ int try_launch(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, u
     return 0;
 }
 
-constexpr int kWaveChoices[] = {4, 6, 8, 10, 12};
+constexpr int kWaveChoices[] = {4, 6, 8, 10, 12, 14};
 
 template <int K>
 int run_shape(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
@@ -280,7 +275,8 @@ int run_shape(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, ui
            try_launch<K, 6>(waves, a, t, lds, nseg, st, resident) &&
            try_launch<K, 8>(waves, a, t, lds, nseg, st, resident) &&
            try_launch<K, 10>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 12>(waves, a, t, lds, nseg, st, resident);
+           try_launch<K, 12>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 14>(waves, a, t, lds, nseg, st, resident);
 }
 
 // Waves per workgroup: the choice with the most resident waves per CU

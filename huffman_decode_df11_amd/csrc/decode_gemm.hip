@@ -39,7 +39,6 @@ namespace {
 constexpr uint32_t kTR = 32, kTC = 512, kTile = kTR * kTC;
 constexpr uint32_t kChunkBits = 128;
 constexpr uint32_t kSegWords = 256;
-constexpr uint32_t kSlotBytes = 4 * kSlotWords;
 constexpr uint32_t kPlaneBytes = kTile + 16;       // exponent plane (+ spare)
 constexpr uint32_t kBfBytes = kTile * 2;           // BF16 tile
 
@@ -67,8 +66,8 @@ struct GemmArgs {
 // Decode one segment of tile-aligned stream into the exponent plane.
 template <int K>
 __device__ __forceinline__ void decode_segment_to_plane(const GemmArgs &g, uint64_t s, uint64_t tile_start,
-                                                        uint32_t slot, uint32_t plane, uint32_t fast,
-                                                        uint32_t chain, uint32_t lane)
+                                                        uint32_t plane, uint32_t fast, uint32_t chain,
+                                                        uint32_t lane)
 {
     const uint32_t *w = g.words + s * kSegWords + lane * 4;
     const uint4 own = *reinterpret_cast<const uint4 *>(w);
@@ -76,18 +75,16 @@ __device__ __forceinline__ void decode_segment_to_plane(const GemmArgs &g, uint6
     const uint32_t gap = g.gaps[s * 64 + lane];
     const uint64_t g0 = g.segs[s].elem_off, g1 = g.segs[s + 1].elem_off;
     const uint32_t nbits = g.segs[s].nbits;
-    const uint32_t rbase = stage_chunk(slot, own, next);
-    wave_lds_sync();
     if (g0 >= tile_start && g1 >= g0 && g1 <= tile_start + kTile) {
         const uint32_t c0 = lane * kChunkBits;
         const uint32_t end = nbits > c0 ? min(kChunkBits, nbits - c0) : 0u;
-        const uint32_t cnt = gap < end ? count_codes<K>(rbase, fast, chain, gap, end) : 0u;
+        const Window win = make_window(own, next, gap);
+        const uint32_t cnt = gap < end ? count_codes<K>(win, fast, chain, gap, end) : 0u;
         uint32_t total;
         const uint32_t excl = wave_exclusive_scan(cnt, &total);
         if (total == (uint32_t)(g1 - g0))
-            emit_codes<K>(rbase, fast, chain, gap, plane + (uint32_t)(g0 - tile_start) + excl, cnt);
+            emit_codes<K>(win, fast, chain, plane + (uint32_t)(g0 - tile_start) + excl, cnt);
     }
-    wave_lds_sync();
 }
 
 // BF16 tile address of the 16-byte chunk `c` (8 columns) of tile row r.
@@ -111,9 +108,7 @@ decode_gemm_kernel(GemmArgs g)
     const uint32_t lane = lane_id();
     const uint32_t plane = lds0 + 16;
     const uint32_t bf = lds0 + 16 + kPlaneBytes;
-    const uint32_t slots = bf + kBfBytes;
-    const uint32_t slot = slots + (wave * 64 + lane) * kSlotBytes;
-    const uint32_t fast = (slots + WAVES * 64 * kSlotBytes + 15) & ~15u;
+    const uint32_t fast = bf + kBfBytes;
     const uint32_t chain = fast + (8u << K);
 
     for (uint32_t i = threadIdx.x; i < (2u << K); i += blockDim.x) st32(fast + 4 * i, g.fast[i]);
@@ -136,7 +131,7 @@ decode_gemm_kernel(GemmArgs g)
             // decode the tile's segments (one wave per segment)
             const uint64_t s0 = g.block_seg[t], s1 = min(g.block_seg[t + 1], g.n_segments);
             for (uint64_t s = s0 + wave; s < s1; s += WAVES)
-                decode_segment_to_plane<K>(g, s, tile_start, slot, plane, fast, chain, lane);
+                decode_segment_to_plane<K>(g, s, tile_start, plane, fast, chain, lane);
             __syncthreads();
 
             // merge exponents and sign+mantissa bytes into the swizzled BF16 tile
@@ -201,10 +196,9 @@ decode_gemm_kernel(GemmArgs g)
     }
 }
 
-uint32_t gemm_lds_bytes(int waves, uint32_t fast_bits, uint32_t n_tables)
+uint32_t gemm_lds_bytes(uint32_t fast_bits, uint32_t n_tables)
 {
-    const uint32_t slots = (uint32_t)waves * 64 * kSlotBytes;
-    return ((16 + kPlaneBytes + kBfBytes + slots + 15) & ~15u) + (8u << fast_bits) + n_tables * 512u;
+    return 16 + kPlaneBytes + kBfBytes + (8u << fast_bits) + n_tables * 512u;
 }
 
 int cu_count()
@@ -237,7 +231,7 @@ template <int K>
 int launch_mt(const GemmArgs &a, uint32_t n_tables, hipStream_t st)
 {
     constexpr int W = 8;
-    const uint32_t lds = gemm_lds_bytes(W, K, n_tables);
+    const uint32_t lds = gemm_lds_bytes(K, n_tables);
     if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm tables do not fit in LDS");
     const uint32_t mt = (a.B + 31) / 32;
     if (mt <= 1) return launch<K, 1, W>(a, lds, st);

@@ -1,8 +1,8 @@
 // Device building blocks shared by the decode and fused decode+GEMM kernels.
 //
 // One 64-lane wavefront decodes one segment of the exponent stream:
-//   stage   every lane copies its chunk of stream words (plus one look-ahead
-//           word) into a private, padded LDS slot;
+//   load    every lane holds its chunk of four stream words plus the next
+//           chunk's first word (160 bits) in registers;
 //   locate  every lane counts the codes that start in its chunk ([P3]
 //           "DFloat11重新定义LLM无损压缩的技术边界" 2.2 Phase 1), reading the
 //           multi-code table and, for long codes, the hierarchical tables;
@@ -15,13 +15,13 @@
 // bytes ([P1] "DFloat11无损压缩技术：基于哈夫曼编码的BFloat16大模型显存优化方案"
 // 2.2 item 2) into BF16.
 //
-// Bit cursor.  A lane keeps one 32-bit state word: bits 0..15 hold kM0 - p
-// for the bit position p inside its chunk and bits 16..31 hold a count or an
-// LDS byte address.  A multi-code table entry's meta = (codes << 16) - bits,
-// so `state += meta` advances both halves at once.  The lane's words are
-// stored in reversed order, so the 32-bit window at p,
-// alignbit(word[(p-1)>>5], word[((p-1)>>5)+1], -p), reads two adjacent LDS
-// words at an address linear in (state >> 5) & 0x7FF.
+// Bit window.  The 160 bits live in five registers, most significant first;
+// consuming b bits shifts all five left with v_alignbit_b32 by (32 - b) mod 32,
+// which is exactly the low five bits of the table word meta = (codes << 16) - b,
+// so a lookup costs one LDS read and no address arithmetic on the stream.
+// Cursor.  A lane keeps one 32-bit state word: bits 0..15 hold kM0 - p for
+// the bit position p in its chunk, bits 16..31 a count or an LDS byte
+// address; `state += meta` advances both halves at once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,7 +31,6 @@ namespace df11dev {
 
 constexpr uint32_t kM0 = 65504;          // multiple of 32, above any chunk size
 constexpr uint32_t kQ = kM0 / 32;
-constexpr uint32_t kSlotWords = 7;       // per-lane stream slot: 6 words used, odd stride
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -78,13 +77,25 @@ __device__ __forceinline__ uint32_t lshl_add_s(uint32_t a, uint32_t b)
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
-// The 32-bit window of a lane's chunk at the position held in `st`.
-__device__ __forceinline__ uint32_t window(uint32_t rbase, uint32_t st)
+// A lane's 160-bit stream window, first stream bit in bit 31 of w0.
+struct Window {
+    uint32_t w0, w1, w2, w3, w4;
+    // consume b bits (1 <= b <= 32) where sh holds (32 - b) mod 32 in its low five bits
+    __device__ __forceinline__ void consume(uint32_t sh)
+    {
+        w0 = __builtin_amdgcn_alignbit(w0, w1, sh);
+        w1 = __builtin_amdgcn_alignbit(w1, w2, sh);
+        w2 = __builtin_amdgcn_alignbit(w2, w3, sh);
+        w3 = __builtin_amdgcn_alignbit(w3, w4, sh);
+        w4 = __builtin_amdgcn_alignbit(w4, 0u, sh);
+    }
+};
+
+__device__ __forceinline__ Window make_window(uint4 own, uint32_t next, uint32_t gap)
 {
-    const uint32_t a = lshl_add<2>(__builtin_amdgcn_ubfe(st, 5, 11), rbase);
-    const uint32_t w_next = ld32(a);        // word[a'+1]
-    const uint32_t w_cur = ld32(a + 4);     // word[a']
-    return __builtin_amdgcn_alignbit(w_cur, w_next, st);
+    Window w{own.x, own.y, own.z, own.w, next};
+    if (gap) w.consume(0u - gap);
+    return w;
 }
 
 // First code of a window through the hierarchical tables at LDS byte
@@ -109,20 +120,6 @@ __device__ __forceinline__ uint32_t chain_decode(uint32_t chain, uint32_t win)
 
 __device__ __forceinline__ uint32_t rot_exp(uint32_t e) { return ((e >> 1) | (e << 7)) & 0xFFu; }
 
-// Per-lane stream slot: words -1..4 of the lane's chunk (4 own words, the
-// next chunk's first word as look-ahead, word -1 a never-used guard) stored
-// reversed at slot + 4*(5 - i).  Returns the lane's rbase.
-__device__ __forceinline__ uint32_t stage_chunk(uint32_t slot, uint4 own, uint32_t next)
-{
-    st32(slot + 4, next);        // word 4
-    st32(slot + 8, own.w);       // word 3
-    st32(slot + 12, own.z);
-    st32(slot + 16, own.y);
-    st32(slot + 20, own.x);      // word 0
-    // word[a'+1] for a' = kQ - 1 - d sits at slot + 4*(5 - a' - 1)
-    return slot + 20u - 4u * kQ;
-}
-
 // Wavefront-scope ordering of LDS traffic between lanes of one wave.
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -131,44 +128,46 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Locate: number of codes starting in [p0, end) of the lane's chunk.
+// Locate: number of codes starting in [p0, end) of the lane's chunk; w is
+// the window at p0.
 template <int K>
-__device__ __forceinline__ uint32_t count_codes(uint32_t rbase, uint32_t fast, uint32_t chain,
-                                                uint32_t p0, uint32_t end)
+__device__ __forceinline__ uint32_t count_codes(Window w, uint32_t fast, uint32_t chain, uint32_t p0,
+                                                uint32_t end)
 {
     uint32_t st = kM0 - p0;
     const uint32_t lim = kM0 - end;            // p < end  <=>  (st & 0xFFFF) > lim
-    uint32_t meta = 0;
+    uint32_t meta = 0, prev = w.w0;
     while ((st & 0xFFFFu) > lim) {
-        const uint32_t w = window(rbase, st);
-        meta = ld32(lshl_add_s<3>(w >> (32 - K), fast) + 4);
-        if (meta == 0) meta = (1u << 16) - ((chain_decode(chain, w) >> 8) & 0x3Fu);
+        prev = w.w0;
+        meta = ld32(lshl_add_s<3>(w.w0 >> (32 - K), fast) + 4);
+        if (meta == 0) meta = (1u << 16) - ((chain_decode(chain, w.w0) >> 8) & 0x3Fu);
+        w.consume(meta);
         st += meta;
     }
     // the last lookup may have counted codes that start at or past `end`:
-    // step back and redo it one code at a time
+    // step back and redo it one code at a time (its codes lie in `prev`)
     st -= meta;
     while ((st & 0xFFFFu) > lim) {
-        const uint32_t w = window(rbase, st);
-        st += (1u << 16) - ((chain_decode(chain, w) >> 8) & 0x3Fu);
+        const uint32_t step = (1u << 16) - ((chain_decode(chain, prev) >> 8) & 0x3Fu);
+        prev = __builtin_amdgcn_alignbit(prev, 0u, step);
+        st += step;
     }
     return st >> 16;
 }
 
-// Emit: decode `cnt` codes from p0 and write their rotated exponents to LDS
-// bytes [wpos, wpos + cnt).  wpos + cnt must be below 65536.
+// Emit: decode `cnt` codes from the window w and write their rotated
+// exponents to LDS bytes [wpos, wpos + cnt).  wpos + cnt must be below 65536.
 template <int K>
-__device__ __forceinline__ void emit_codes(uint32_t rbase, uint32_t fast, uint32_t chain,
-                                           uint32_t p0, uint32_t wpos, uint32_t cnt)
+__device__ __forceinline__ void emit_codes(Window w, uint32_t fast, uint32_t chain, uint32_t wpos,
+                                           uint32_t cnt)
 {
-    uint32_t st = (kM0 - p0) | (wpos << 16);
+    uint32_t st = (wpos << 16) | kM0;   // the low half only has to keep borrowing
     const uint32_t bound = (wpos + cnt - 3u) << 16;   // st < bound <=> at least 4 codes left
     while (st < bound) {
-        const uint32_t w = window(rbase, st);
-        const uint2 f = ld64(lshl_add_s<3>(w >> (32 - K), fast));
+        const uint2 f = ld64(lshl_add_s<3>(w.w0 >> (32 - K), fast));
         uint32_t syms = f.x, meta = f.y;
         if (meta == 0) {
-            const uint32_t e = chain_decode(chain, w);
+            const uint32_t e = chain_decode(chain, w.w0);
             syms = rot_exp(e & 0xFFu);
             meta = (1u << 16) - ((e >> 8) & 0x3Fu);
         }
@@ -177,13 +176,16 @@ __device__ __forceinline__ void emit_codes(uint32_t rbase, uint32_t fast, uint32
         st8(a + 1, syms >> 8);
         st8(a + 2, syms >> 16);
         st8(a + 3, syms >> 24);
+        w.consume(meta);
         st += meta;
     }
     const uint32_t lend = wpos + cnt;
     while ((st >> 16) < lend) {
-        const uint32_t e = chain_decode(chain, window(rbase, st));
+        const uint32_t e = chain_decode(chain, w.w0);
+        const uint32_t step = (1u << 16) - ((e >> 8) & 0x3Fu);
         st8(st >> 16, rot_exp(e & 0xFFu));
-        st += (1u << 16) - ((e >> 8) & 0x3Fu);
+        w.consume(step);
+        st += step;
     }
 }
 
