@@ -33,7 +33,7 @@ namespace {
 constexpr uint32_t kChunkBytes = 16;
 constexpr uint32_t kChunkBits = 8 * kChunkBytes;
 constexpr uint32_t kSegWords = 64 * kChunkBytes / 4;
-constexpr int kPrefetchRounds = 4;
+constexpr int kPrefetchRounds = 3;
 
 struct ViewArgs {
     const uint32_t *words;
@@ -88,7 +88,7 @@ __device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, u
 }
 
 template <int K, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64)
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
 decode_kernel(ViewArgs v, TableArgs t)
 {
     extern __shared__ __align__(16) uint8_t lds_raw[];
@@ -146,7 +146,7 @@ decode_kernel(ViewArgs v, TableArgs t)
                     const uint32_t gi = lane + 64u * r;
                     uint4 smv;
                     if (r < kPrefetchRounds) {
-                        smv = r == 0 ? smp[0] : r == 1 ? smp[1] : r == 2 ? smp[2] : smp[3];
+                        smv = r == 0 ? smp[0] : r == 1 ? smp[1] : smp[2];
                     } else {
                         smv = gi < ngroups ? *reinterpret_cast<const uint4 *>(v.sm + gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
                     }
@@ -204,13 +204,14 @@ int check_view(const df11_view *v)
     return DF11_OK;
 }
 
-// Exponent staging per wave: room for the most codes a segment can hold
-// (segment bits / shortest code), a 16-element head offset and a tail group.
+// Exponent staging per wave: room for the most codes any segment of this
+// tensor holds (recorded by the encoder, at most segment bits / shortest
+// code), a 16-element head offset and a tail group.
 uint32_t staging_bytes(const df11_view *v)
 {
     const uint32_t seg_bits = 64u * kChunkBits;
     const uint32_t minlen = std::max(1u, v->min_len);
-    const uint32_t tmax = seg_bits / minlen + 1;
+    const uint32_t tmax = std::min(seg_bits / minlen + 1, std::max(1u, v->max_seg_elems));
     return (16 + tmax + 32 + 15) & ~15u;
 }
 
@@ -260,12 +261,14 @@ int try_launch(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, u
         per_cu = 1;
     *resident = per_cu * W;
     if (!a.words) return 0;   // query only
+    // every resident slot busy: the decode is latency-bound per wave, so
+    // more waves in flight beat an evenly split last round
     const uint64_t groups = std::min<uint64_t>((nseg + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
     if (groups) hipLaunchKernelGGL((decode_kernel<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
     return 0;
 }
 
-constexpr int kWaveChoices[] = {4, 6, 8, 10, 12, 14};
+constexpr int kWaveChoices[] = {4, 6, 8, 10, 12, 14, 16};
 
 template <int K>
 int run_shape(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
@@ -276,7 +279,8 @@ int run_shape(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, ui
            try_launch<K, 8>(waves, a, t, lds, nseg, st, resident) &&
            try_launch<K, 10>(waves, a, t, lds, nseg, st, resident) &&
            try_launch<K, 12>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 14>(waves, a, t, lds, nseg, st, resident);
+           try_launch<K, 14>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 16>(waves, a, t, lds, nseg, st, resident);
 }
 
 // Waves per workgroup: the choice with the most resident waves per CU

@@ -189,16 +189,18 @@ __device__ __forceinline__ void emit_codes(Window w, uint32_t fast, uint32_t cha
     }
 }
 
-// Exclusive prefix sum over the wavefront; *total receives the sum.
+// Exclusive prefix sum over the wavefront; *total receives the sum.  DPP
+// row shifts scan each row of 16 lanes, then the row totals are broadcast
+// to the rows above them (gfx9 row_bcast:15 and row_bcast:31).
 __device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t x, uint32_t *total)
 {
-    const uint32_t lane = lane_id();
     uint32_t v = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(v, d, 64);
-        if (lane >= (uint32_t)d) v += y;
-    }
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
     *total = __builtin_amdgcn_readlane(v, 63);
     return v - x;
 }

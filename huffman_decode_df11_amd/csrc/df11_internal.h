@@ -21,7 +21,7 @@ int build_tables(df11_codebook *cb);
 struct df11_encoded {
     uint64_t n = 0, total_bits = 0, n_segments = 0;
     df11_layout layout{};
-    uint32_t min_len = 0, max_len = 0, n_tables = 0, fast_bits = 0;
+    uint32_t min_len = 0, max_len = 0, n_tables = 0, fast_bits = 0, max_seg_elems = 0;
     std::vector<uint32_t> exp_words;
     std::vector<uint8_t> sm;
     std::vector<uint8_t> gaps;

@@ -219,6 +219,10 @@ extern "C" int df11_encode(const uint16_t *bits, uint64_t n, const df11_codebook
         }
     }
     segs[nseg].elem_off = n;
+    for (uint64_t s = 0; s < nseg; s++) {
+        const uint64_t c = segs[s + 1].elem_off - segs[s].elem_off;
+        if (c > enc->max_seg_elems) enc->max_seg_elems = (uint32_t)c;
+    }
     *out = enc;
     return DF11_OK;
 }
@@ -243,6 +247,7 @@ extern "C" int df11_encoded_view(const df11_encoded *enc, df11_view *v)
     v->max_len = enc->max_len;
     v->n_tables = enc->n_tables;
     v->fast_bits = enc->fast_bits;
+    v->max_seg_elems = enc->max_seg_elems;
     v->exp_words = enc->exp_words.data();  v->n_exp_words = enc->exp_words.size();
     v->sm = enc->sm.data();                v->n_sm = enc->sm.size();
     v->gaps = enc->gaps.data();            v->n_gaps = enc->gaps.size();

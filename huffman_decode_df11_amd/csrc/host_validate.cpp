@@ -110,6 +110,8 @@ extern "C" int df11_validate(const df11_view *v, const df11_codebook *cb)
             if (c1 >= vend && sg.nbits < seg_bits && p != vend)
                 return fail(DF11_E_FORMAT, "segment %llu: last code does not end at nbits", (unsigned long long)s);
         }
+        if (want > v->max_seg_elems)
+            return fail(DF11_E_FORMAT, "segment %llu holds more codes than max_seg_elems", (unsigned long long)s);
         if (got != want)
             return fail(DF11_E_FORMAT, "segment %llu holds %llu codes but its records say %llu",
                         (unsigned long long)s, (unsigned long long)got, (unsigned long long)want);

@@ -133,6 +133,8 @@ typedef struct df11_view {
     uint32_t tile_rows, tile_cols;
     uint64_t align_elems;
     uint32_t min_len, max_len, n_tables, fast_bits;
+    uint32_t max_seg_elems;     /* most codes starting in any one segment */
+    uint32_t reserved;
     const uint32_t *exp_words;  uint64_t n_exp_words;  /* n_segments*seg_words + 2 */
     const uint8_t *sm;          uint64_t n_sm;         /* n rounded up to 16 */
     const uint8_t *gaps;        uint64_t n_gaps;       /* n_segments * seg_lanes */
