@@ -163,6 +163,25 @@ def encode(bits, codebook: Optional[Codebook] = None, layout: Optional[Layout] =
     return Encoded(h.value, codebook, shape)
 
 
+_TABLE_ARRAYS = ("chain", "fast")
+
+
+def _device_tables(enc: Encoded, device):
+    """The codebook's tables on `device`, uploaded once per codebook and
+    device, so that tensors sharing a codebook share device tables (which a
+    batched decode requires)."""
+    import torch
+    cb = enc.codebook
+    cache = getattr(cb, "_device_tables", None)
+    if cache is None:
+        cache = {}
+        cb._device_tables = cache
+    key = str(torch.device(device))
+    if key not in cache:
+        cache[key] = {name: torch.from_numpy(enc.arrays[name].copy()).to(device) for name in _TABLE_ARRAYS}
+    return cache[key]
+
+
 class DF11Tensor:
     """An encoded tensor resident in device memory, plus its device view."""
 
@@ -173,7 +192,11 @@ class DF11Tensor:
         self.codebook = enc.codebook
         self.host_view = enc.view
         self.tensors = {}
+        shared = _device_tables(enc, device)
         for name, _ in _lib.VIEW_ARRAYS:
+            if name in shared:
+                self.tensors[name] = shared[name]
+                continue
             a = enc.arrays[name]
             t = torch.from_numpy(a.copy() if a.size else np.zeros(16, np.uint8)).to(device)
             self.tensors[name] = t
@@ -203,6 +226,25 @@ def decode(t: DF11Tensor, out=None, stream=None):
     assert out.is_cuda and out.is_contiguous() and out.numel() >= t.n and out.element_size() == 2
     check(lib().df11_decode(ctypes.byref(t.view), out.data_ptr(), _stream_handle(stream)), "df11_decode")
     return out
+
+
+def decode_batch(tensors: Sequence[DF11Tensor], outs=None, stream=None):
+    """Decode several tensors that share a codebook in one launch.  Returns
+    the list of outputs (new torch.bfloat16 tensors where outs is None)."""
+    import torch
+    tensors = list(tensors)
+    if outs is None:
+        outs = [torch.empty(t.shape if t.shape else (t.n,), dtype=torch.bfloat16, device=t.device)
+                for t in tensors]
+    assert len(outs) == len(tensors)
+    views = (View * max(len(tensors), 1))()
+    ptrs = (ctypes.c_void_p * max(len(tensors), 1))()
+    for i, (t, o) in enumerate(zip(tensors, outs)):
+        assert o.is_cuda and o.is_contiguous() and o.numel() >= t.n and o.element_size() == 2
+        ctypes.memmove(ctypes.byref(views, i * ctypes.sizeof(View)), ctypes.byref(t.view), ctypes.sizeof(View))
+        ptrs[i] = o.data_ptr()
+    check(lib().df11_decode_batch(views, ptrs, len(tensors), _stream_handle(stream)), "df11_decode_batch")
+    return outs
 
 
 def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None):

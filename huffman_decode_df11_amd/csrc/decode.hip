@@ -48,6 +48,22 @@ struct ViewArgs {
     uint64_t cols;
 };
 
+// Up to kMaxBatch views per launch, passed by value; segments of all views
+// form one flat index space (view i owns [seg_begin[i], seg_begin[i + 1])).
+constexpr uint32_t kMaxBatch = 16;
+struct BatchArgs {
+    ViewArgs v[kMaxBatch];
+    uint64_t seg_begin[kMaxBatch + 1];
+    uint32_t count;
+};
+
+__device__ __forceinline__ uint32_t view_of(const BatchArgs &b, uint64_t s)
+{
+    uint32_t i = 0;
+    while (i + 1 < b.count && b.seg_begin[i + 1] <= s) i++;
+    return i;
+}
+
 struct TableArgs {
     const uint16_t *chain;
     const uint32_t *fast;
@@ -89,7 +105,7 @@ __device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, u
 
 template <int K, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
-decode_kernel(ViewArgs v, TableArgs t)
+decode_kernel(BatchArgs b, TableArgs t)
 {
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
@@ -105,12 +121,15 @@ decode_kernel(ViewArgs v, TableArgs t)
         *(lds_u16 *)(size_t)(chain + 2 * i) = t.chain[i];
     __syncthreads();
 
+    const uint64_t n_total = b.seg_begin[b.count];
     uint64_t s = (uint64_t)blockIdx.x * WAVES + wave;
     const uint64_t stride = (uint64_t)gridDim.x * WAVES;
-    if (s >= v.n_segments) return;
-    SegLoad nx = load_segment(v, s, lane);
+    if (s >= n_total) return;
+    uint32_t vi = view_of(b, s);
+    SegLoad nx = load_segment(b.v[vi], s - b.seg_begin[vi], lane);
     for (;;) {
         const SegLoad cur = nx;
+        const ViewArgs &v = b.v[vi];
         const uint64_t g0 = cur.g0, g1 = cur.g1;
         const uint64_t gbase = g0 & ~15ull;
         const uint32_t head = (uint32_t)(g0 & 15);
@@ -126,8 +145,9 @@ decode_kernel(ViewArgs v, TableArgs t)
         }
         // the next segment's stream words and records
         const uint64_t s_next = s + stride;
-        const bool more = s_next < v.n_segments;
-        if (more) nx = load_segment(v, s_next, lane);
+        const bool more = s_next < n_total;
+        const uint32_t vi_next = more ? view_of(b, s_next) : vi;
+        if (more) nx = load_segment(b.v[vi_next], s_next - b.seg_begin[vi_next], lane);
 
         if (valid) {
             const uint32_t c0 = lane * kChunkBits;
@@ -174,6 +194,7 @@ decode_kernel(ViewArgs v, TableArgs t)
         wave_lds_sync();   // the staging is reused by the next segment
         if (!more) break;
         s = s_next;
+        vi = vi_next;
     }
 }
 
@@ -252,7 +273,7 @@ uint32_t lds_bytes(int waves, uint32_t stg, uint32_t fast_bits, uint32_t n_table
 }
 
 template <int K, int W>
-int try_launch(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
+int try_launch(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
                hipStream_t st, int *resident)
 {
     if (waves != W) return 1;
@@ -260,7 +281,7 @@ int try_launch(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, u
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<K, W>, W * 64, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
     *resident = per_cu * W;
-    if (!a.words) return 0;   // query only
+    if (!nseg) return 0;   // query only
     // every resident slot busy: the decode is latency-bound per wave, so
     // more waves in flight beat an evenly split last round
     const uint64_t groups = std::min<uint64_t>((nseg + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
@@ -271,7 +292,7 @@ int try_launch(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, u
 constexpr int kWaveChoices[] = {4, 6, 8, 10, 12, 14, 16};
 
 template <int K>
-int run_shape(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
+int run_shape(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
               hipStream_t st, int *resident)
 {
     return try_launch<K, 4>(waves, a, t, lds, nseg, st, resident) &&
@@ -288,12 +309,12 @@ int run_shape(int waves, const ViewArgs &a, const TableArgs &t, uint32_t lds, ui
 // in the first 64 KB of LDS (the emit loop keeps byte addresses in 16 bits).
 // DF11_DECODE_WAVES overrides the choice for tuning.
 template <int K>
-int launch_decode(const ViewArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
+int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
 {
     int best = 0, best_res = -1;
     const char *env = getenv("DF11_DECODE_WAVES");
     const int forced = env ? atoi(env) : 0;
-    ViewArgs probe{};
+    BatchArgs probe{};
     for (int w : kWaveChoices) {
         const uint32_t lds = lds_bytes(w, t.stg_bytes, v->fast_bits, v->n_tables);
         if (16 + (uint32_t)w * t.stg_bytes > 65520 || lds > 160u * 1024u) continue;
@@ -304,10 +325,46 @@ int launch_decode(const ViewArgs &a, const TableArgs &t, const df11_view *v, hip
     }
     if (!best) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
     int res = 0;
-    run_shape<K>(best, a, t, lds_bytes(best, t.stg_bytes, v->fast_bits, v->n_tables), v->n_segments, st, &res);
+    run_shape<K>(best, a, t, lds_bytes(best, t.stg_bytes, v->fast_bits, v->n_tables), a.seg_begin[a.count], st,
+                 &res);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode launch: %s", hipGetErrorString(e));
     return DF11_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// One launch over up to kMaxBatch views that share their tables.
+int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, hipStream_t st)
+{
+    BatchArgs b{};
+    uint32_t stg = 0;
+    const df11_view *v0 = nullptr;
+    for (uint32_t i = 0; i < count; i++) {
+        const df11_view *v = &views[i];
+        if (!v->n) continue;
+        if (!outs[i] || ((uintptr_t)outs[i] & 15))
+            return df11::fail(DF11_E_ARG, "output %u must be a 16-byte aligned device pointer", i);
+        if (v0 && (v->fast != v0->fast || v->chain != v0->chain || v->fast_bits != v0->fast_bits ||
+                   v->n_tables != v0->n_tables))
+            return df11::fail(DF11_E_ARG, "views of one batch must share their device tables (view %u differs)", i);
+        if (!v0) v0 = v;
+        b.v[b.count] = make_args(v, outs[i]);
+        b.seg_begin[b.count + 1] = b.seg_begin[b.count] + v->n_segments;
+        b.count++;
+        stg = std::max(stg, staging_bytes(v));
+    }
+    if (!b.count || !b.seg_begin[b.count]) return DF11_OK;
+    TableArgs t{v0->chain, v0->fast, (uint32_t)v0->n_chain, stg};
+    switch (v0->fast_bits) {
+    case 8: return launch_decode<8>(b, t, v0, st);
+    case 9: return launch_decode<9>(b, t, v0, st);
+    case 10: return launch_decode<10>(b, t, v0, st);
+    case 11: return launch_decode<11>(b, t, v0, st);
+    default: return launch_decode<12>(b, t, v0, st);
+    }
 }
 
 }  // namespace
@@ -318,15 +375,20 @@ extern "C" int df11_decode(const df11_view *v, uint16_t *out, void *stream)
     if (rc) return rc;
     if (!v->n) return DF11_OK;
     if (!out || ((uintptr_t)out & 15)) return df11::fail(DF11_E_ARG, "out must be a 16-byte aligned device pointer");
-    const uint32_t stg = staging_bytes(v);
-    TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, stg};
-    const ViewArgs a = make_args(v, out);
-    hipStream_t st = (hipStream_t)stream;
-    switch (v->fast_bits) {
-    case 8: return launch_decode<8>(a, t, v, st);
-    case 9: return launch_decode<9>(a, t, v, st);
-    case 10: return launch_decode<10>(a, t, v, st);
-    case 11: return launch_decode<11>(a, t, v, st);
-    default: return launch_decode<12>(a, t, v, st);
+    uint16_t *outs[1] = {out};
+    return decode_views(v, outs, 1, (hipStream_t)stream);
+}
+
+extern "C" int df11_decode_batch(const df11_view *views, uint16_t *const *outs, uint32_t count, void *stream)
+{
+    if (count && (!views || !outs)) return df11::fail(DF11_E_ARG, "df11_decode_batch: null pointer");
+    for (uint32_t i = 0; i < count; i++) {
+        int rc = check_view(&views[i]);
+        if (rc) return rc;
     }
+    for (uint32_t i = 0; i < count; i += kMaxBatch) {
+        int rc = decode_views(views + i, outs + i, std::min(kMaxBatch, count - i), (hipStream_t)stream);
+        if (rc) return rc;
+    }
+    return DF11_OK;
 }

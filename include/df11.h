@@ -205,6 +205,16 @@ int df11_validate(const df11_view *host_view, const df11_codebook *cb);
  * inconsistent), E_UNSUPPORTED (tables too large for the kernel), E_DEVICE. */
 int df11_decode(const df11_view *device_view, uint16_t *out, void *stream);
 
+/* Decode several device views in one launch: view i into outs[i] (device,
+ * 16-byte aligned, views[i].n elements), for example the seven matrices of a
+ * decoder layer.  views is a host array of `count` device views that share
+ * their device tables (the same chain and fast pointers, i.e. one codebook
+ * uploaded once).  Same guarantees and errors as df11_decode, plus E_ARG when
+ * the views do not share their tables.  More than 16 views are decoded in
+ * launches of 16. */
+int df11_decode_batch(const df11_view *device_views, uint16_t *const *outs, uint32_t count,
+                      void *stream);
+
 /* Fused decode + matrix product ([P1] 2.2 item 3: decoded weights feed the
  * matmul and are discarded): y[b][j] = sum_k x[b][k] * W[j][k] for W the
  * [rows = N, cols = K] weight of `w` (encoded with df11_gemm_layout), x a

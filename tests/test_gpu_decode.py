@@ -178,3 +178,50 @@ def test_llama_layer_full_size_reused_buffer():
         if name in ("up_proj", "k_proj"):
             _oracle_sampled(enc, m.reshape(-1), nseg=8)
         del dt, enc
+
+
+def test_batch_llama_layer_one_launch():
+    """All seven matrices of a layer in one launch, each into its own output."""
+    mats = synth.llama_layer(seed=0, layer=1)
+    hist = None
+    for _, m in mats:
+        hist = api.hist_accumulate(m, hist)
+    cb = api.build_codebook(hist)
+    dts = [api.encode(m, codebook=cb).to("cuda") for _, m in mats]
+    _say("case batch llama layer")
+    outs = [torch.full((m.size + 32,), 0x5555, dtype=torch.int16, device="cuda") for _, m in mats]
+    api.decode_batch(dts, outs=[o.view(torch.bfloat16) for o in outs])
+    torch.cuda.synchronize()
+    for (name, m), o in zip(mats, outs):
+        got = _to_bits(o)
+        assert np.array_equal(got[:m.size], m.reshape(-1)), name
+        assert (got[m.size:] == 0x5555).all(), name
+
+
+def test_batch_many_small_and_empty():
+    """More views than one launch takes (16), ragged sizes and an empty one."""
+    rng = np.random.default_rng(7)
+    sizes = [0, 1, 17, 4096, 100_000] + [int(x) for x in rng.integers(1, 300_000, size=17)]
+    tensors = [synth.normal_bf16(n, 0.02, seed=100 + i) for i, n in enumerate(sizes)]
+    hist = None
+    for t in tensors:
+        hist = api.hist_accumulate(t, hist)
+    cb = api.build_codebook(hist)
+    dts = [api.encode(t, codebook=cb).to("cuda") for t in tensors]
+    _say("case batch small", len(dts))
+    outs = [torch.full((max(t.size, 1) + 16,), 0x5555, dtype=torch.int16, device="cuda") for t in tensors]
+    api.decode_batch(dts, outs=[o.view(torch.bfloat16) for o in outs])
+    torch.cuda.synchronize()
+    for t, o in zip(tensors, outs):
+        got = _to_bits(o)
+        assert np.array_equal(got[:t.size], t)
+        assert (got[t.size:] == 0x5555).all()
+
+
+def test_batch_rejects_different_codebooks():
+    from huffman_decode_df11_amd import _lib
+    a = api.encode(synth.normal_bf16(5000, 0.02, seed=1)).to("cuda")
+    b = api.encode(synth.normal_bf16(5000, 0.03, seed=2)).to("cuda")
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.decode_batch([a, b])
+    assert ei.value.status == -1
