@@ -113,6 +113,114 @@ def time_decode(dts, outbuf, steps: int, warmup: int):
     return total_ms / steps, per_launch
 
 
+def time_batched(dts, steps: int, warmup: int):
+    """One df11_decode_batch launch per step over all tensors, each into its
+    own slice of one reused layer-sized buffer."""
+    import torch
+    from huffman_decode_df11_amd import api
+    total = sum(((dt.n + 7) // 8) * 8 for dt in dts)
+    buf = torch.empty(total, dtype=torch.bfloat16, device="cuda")
+    outs, off = [], 0
+    for dt in dts:
+        outs.append(buf[off:off + dt.n])
+        off += ((dt.n + 7) // 8) * 8
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        api.decode_batch(dts, outs=outs, stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        api.decode_batch(dts, outs=outs, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps, outs
+
+
+def time_graph(dts, outbuf, steps: int, warmup: int):
+    """The per-matrix launches captured once in a HIP graph and replayed."""
+    import torch
+    from huffman_decode_df11_amd import api
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for dt in dts:
+            api.decode(dt, out=outbuf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for dt in dts:
+            api.decode(dt, out=outbuf)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def fused_up_proj(steps: int, warmup: int, seed: int = 0):
+    """df11_decode_gemm on the up_proj weight (14336 x 4096) for B in
+    {1, 8, 64, 256}, next to torch.matmul on the decoded BF16 weight."""
+    import torch
+    from huffman_decode_df11_amd import api, synth
+    N, K = 14336, 4096
+    W = synth.normal_bf16(N * K, 0.02, seed=seed, index=5, count=7).reshape(N, K)
+    enc = api.encode(W, layout=api.gemm_layout(N, K))
+    dt = enc.to("cuda")
+    wt = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
+    w_bytes = enc.compressed_nbytes()
+
+    def timeit(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    rows = {}
+    for B in (1, 8, 64, 256):
+        X = synth.activations_bf16(B, K, seed=1)
+        x = torch.from_numpy(X.view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.empty(B, N, dtype=torch.float32, device="cuda")
+        api.decode_gemm(dt, x, out=y)
+        yt = x.float() @ wt.float().T
+        torch.cuda.synchronize()
+        rel = float((y - yt).norm() / yt.norm())
+        if not rel < 2e-3:
+            raise SystemExit("fused decode+GEMM parity failed at B=%d (rel %.3g)" % (B, rel))
+        t_fused = timeit(lambda: api.decode_gemm(dt, x, out=y))
+        t_plain = timeit(lambda: torch.matmul(x, wt.T))
+        flops = 2.0 * B * N * K
+        alg = w_bytes + B * K * 2 + B * N * 4
+        mfma_bound = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > alg / (HBM_PEAK_GBS * 1e9)
+        rows[str(B)] = {
+            "fused_ms": round(t_fused, 4),
+            "fused_tflops": round(flops / t_fused / 1e9, 2),
+            "plain_bf16_matmul_ms": round(t_plain, 4),
+            "fused_over_plain": round(t_fused / t_plain, 3),
+            "rel_err_vs_fp32": rel,
+            "roofline": ({"bound": "mfma", "achieved": round(flops / t_fused / 1e9, 2),
+                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(flops / t_fused / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4)}
+                         if mfma_bound else
+                         {"bound": "hbm", "achieved": round(alg / t_fused / 1e6, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(alg / t_fused / 1e6 / HBM_PEAK_GBS, 4)}),
+        }
+    return {"workload": "up_proj 14336x4096 bf16 N(0,0.02), x[B,4096] N(0,1), y float32",
+            "compressed_weight_bytes": w_bytes, "by_batch": rows}
+
+
 def verify(dts, mats, outbuf):
     import torch
     from huffman_decode_df11_amd import api
@@ -158,6 +266,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer", choices=["layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM counters)")
@@ -223,6 +332,24 @@ def main():
             "launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
         },
     }
+    t_batch, outs = time_batched(dts, args.steps, args.warmup)
+    for o, m in zip(outs, mats):
+        if not np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), m.reshape(-1)):
+            raise SystemExit("batched parity check failed")
+    result["batched_layer"] = {
+        "launches_per_step": 1, "ms_per_step": round(t_batch, 4),
+        "decoded_gbs": round(2.0 * n_total / (t_batch * 1e-3) / 1e9, 2),
+        "hbm_frac": round(sum(alg) / (t_batch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "buffer": "one reused layer-sized buffer, each matrix in its own slice",
+    }
+    t_graph = time_graph(dts, outbuf, args.steps, args.warmup)
+    result["graph_layer"] = {
+        "launches_per_step": len(dts), "ms_per_step": round(t_graph, 4),
+        "decoded_gbs": round(2.0 * n_total / (t_graph * 1e-3) / 1e9, 2),
+        "note": "the seven per-matrix launches captured in one HIP graph",
+    }
+    if not args.no_fused:
+        result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
