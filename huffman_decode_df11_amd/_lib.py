@@ -30,6 +30,7 @@ class Layout(ctypes.Structure):
     _fields_ = [
         ("chunk_bytes", u32), ("seg_lanes", u32), ("align_elems", u64),
         ("rows", u64), ("cols", u64), ("tile_rows", u32), ("tile_cols", u32),
+        ("tile_kchunk", u32), ("reserved", u32),
     ]
 
 
@@ -43,6 +44,7 @@ class View(ctypes.Structure):
         ("chunk_bytes", u32), ("seg_lanes", u32),
         ("rows", u64), ("cols", u64),
         ("tile_rows", u32), ("tile_cols", u32),
+        ("tile_kchunk", u32), ("reserved0", u32),
         ("align_elems", u64),
         ("min_len", u32), ("max_len", u32), ("n_tables", u32), ("fast_bits", u32),
         ("max_seg_elems", u32), ("reserved", u32),

@@ -60,9 +60,9 @@ def codebook_codes(cb: Codebook) -> np.ndarray:
 
 
 def make_layout(chunk_bytes: int = 16, align_elems: int = 0, rows: int = 0, cols: int = 0,
-                tile_rows: int = 0, tile_cols: int = 0) -> Layout:
+                tile_rows: int = 0, tile_cols: int = 0, tile_kchunk: int = 0) -> Layout:
     return Layout(chunk_bytes=chunk_bytes, seg_lanes=64, align_elems=align_elems, rows=rows,
-                  cols=cols, tile_rows=tile_rows, tile_cols=tile_cols)
+                  cols=cols, tile_rows=tile_rows, tile_cols=tile_cols, tile_kchunk=tile_kchunk)
 
 
 def gemm_layout(rows: int, cols: int) -> Layout:

@@ -43,8 +43,8 @@ struct ViewArgs {
     uint16_t *out;
     uint64_t n;
     uint64_t n_segments;
-    // tile order (tr == 0: row-major)
-    uint32_t tr, tc, tiles_per_row, pad;
+    // tile order (tr == 0: row-major); kc > 0: column groups inside a tile
+    uint32_t tr, tc, tiles_per_row, kc;
     uint64_t cols;
 };
 
@@ -75,8 +75,17 @@ __device__ __forceinline__ uint64_t out_index(const ViewArgs &v, uint64_t g)
 {
     if (!v.tr) return g;
     const uint64_t tile = (uint64_t)v.tr * v.tc;
-    const uint64_t t = g / tile, w = g - t * tile;
-    const uint32_t r = (uint32_t)(w / v.tc), c = (uint32_t)(w - (uint64_t)r * v.tc);
+    const uint64_t t = g / tile;
+    const uint32_t w = (uint32_t)(g - t * tile);
+    uint32_t r, c;
+    if (v.kc) {
+        const uint32_t grp = w / (v.tr * v.kc), in = w - grp * (v.tr * v.kc);
+        r = in / v.kc;
+        c = grp * v.kc + (in - r * v.kc);
+    } else {
+        r = w / v.tc;
+        c = w - r * v.tc;
+    }
     const uint64_t rb = t / v.tiles_per_row, cb = t - rb * v.tiles_per_row;
     return (rb * v.tr + r) * v.cols + cb * v.tc + c;
 }
@@ -175,9 +184,11 @@ decode_kernel(BatchArgs b, TableArgs t)
                         const uint4 rx = ld128(stg + 16 * gi);
                         const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
                         const uint2 c = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
-                        uint4 *dst = reinterpret_cast<uint4 *>(v.out + out_index(v, gs));
-                        dst[0] = make_uint4(a.x, a.y, b.x, b.y);
-                        dst[1] = make_uint4(c.x, c.y, d.x, d.y);
+                        // row-major, or two 8-element runs of different rows for column groups
+                        uint4 *dst0 = reinterpret_cast<uint4 *>(v.out + out_index(v, gs));
+                        uint4 *dst1 = v.kc ? reinterpret_cast<uint4 *>(v.out + out_index(v, gs + 8)) : dst0 + 1;
+                        dst0[0] = make_uint4(a.x, a.y, b.x, b.y);
+                        dst1[0] = make_uint4(c.x, c.y, d.x, d.y);
                     }
                 }
                 // ragged ends: lanes 0..15 the head group, lanes 16..31 the tail group
@@ -219,7 +230,8 @@ int check_view(const df11_view *v)
         return df11::fail(DF11_E_ARG, "view arrays must be 16-byte aligned (sm, exp_words)");
     if (v->tile_rows) {
         if (!v->tile_cols || v->tile_cols % 16 || !v->cols || v->cols % v->tile_cols ||
-            (uint64_t)v->tile_rows * v->tile_cols > 0xFFFFFFFFull)
+            (uint64_t)v->tile_rows * v->tile_cols > 0xFFFFFFFFull ||
+            (v->tile_kchunk && (v->tile_kchunk % 8 || v->tile_cols % v->tile_kchunk || v->tile_rows % 2)))
             return df11::fail(DF11_E_ARG, "bad tile order in view");
     }
     return DF11_OK;
@@ -262,6 +274,7 @@ ViewArgs make_args(const df11_view *v, uint16_t *out)
     a.tr = v->tile_rows;
     a.tc = v->tile_cols;
     a.tiles_per_row = v->tile_rows ? (uint32_t)(v->cols / v->tile_cols) : 0;
+    a.kc = v->tile_rows ? v->tile_kchunk : 0;
     a.cols = v->cols;
     return a;
 }

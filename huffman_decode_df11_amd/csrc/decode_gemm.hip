@@ -9,20 +9,22 @@
 // [P3] "DFloat11重新定义LLM无损压缩的技术边界" 2.2 (locate, prefix sum,
 //      reconstruct), 5.2 (a batch of 32 or more hides the decode cost).
 //
-// Layout: W [N, K] is encoded in tile order with 32 x 512 tiles, each tile
-// starting a new segment (df11_gemm_layout), so the segments of one tile are
-// block_seg[t] .. block_seg[t+1].  A workgroup owns a block of 32 weight rows
-// (32 output features) and walks its K / 512 tiles:
-//   decode  the waves take the tile's segments, each decoded by one wavefront
-//           exactly as in df11_decode, writing rotated exponents into a
-//           16 KiB LDS plane at the element's offset in the tile;
-//   merge   all threads join exponents with the sign+mantissa bytes into a
-//           32 KiB BF16 tile in LDS, 16-byte chunks XOR-swizzled by row so
-//           that the matrix-core operand reads are bank-conflict free;
-//   mfma    v_mfma_f32_32x32x16_bf16 with A = x rows (the batch, from
-//           global memory / L2) and B = the decoded tile, float32 accumulate.
-// The next tile's decode overlaps other waves' matrix work; the barrier after
-// each decode also separates one tile's matrix reads from the next merge.
+// Layout (df11_gemm_layout): W [N, K] in 32 x 512 tiles, tiles row block by
+// row block, each tile starting a new segment (block_seg[t] is its first
+// segment), and inside a tile 8-column groups: group c holds rows 0..31, 8
+// columns each.  That is the order of the B operand of
+// v_mfma_f32_32x32x16_bf16: lane l reads row l % 32, columns 8 * (2 * step +
+// l / 32) .. + 7, i.e. 8 consecutive stream elements, so operand reads are
+// contiguous across lanes.
+//
+// A workgroup owns a block of 32 weight rows (32 output features) and walks
+// its K / 512 tiles with two LDS buffers, each an exponent plane (filled by
+// the wavefront decode, one wave per segment) and a sign+mantissa plane
+// (copied from HBM).  While the waves run the matrix cores on tile t from
+// one buffer, tile t + 1's sign+mantissa bytes and stream words are already
+// in flight and its segments are decoded into the other buffer.  B operands
+// are assembled in registers (two bit-selects and two byte permutes per four
+// weights) from the two planes; A operands (x, the batch) come from L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -36,12 +38,11 @@ using namespace df11dev;
 
 namespace {
 
-constexpr uint32_t kTR = 32, kTC = 512, kTile = kTR * kTC;
+constexpr uint32_t kTR = 32, kTC = 512, kKC = 8, kTile = kTR * kTC;
 constexpr uint32_t kChunkBits = 128;
 constexpr uint32_t kSegWords = 256;
-constexpr uint32_t kPlaneBytes = kTile + 16;       // exponent plane (+ spare)
-constexpr uint32_t kBfBytes = kTile * 2;           // BF16 tile
 
+typedef __attribute__((address_space(3))) float lds_f32;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -63,98 +64,126 @@ struct GemmArgs {
     uint64_t n_segments;
 };
 
-// Decode one segment of tile-aligned stream into the exponent plane.
-template <int K>
-__device__ __forceinline__ void decode_segment_to_plane(const GemmArgs &g, uint64_t s, uint64_t tile_start,
-                                                        uint32_t plane, uint32_t fast, uint32_t chain,
-                                                        uint32_t lane)
+struct SegLoad {
+    uint4 own;
+    uint32_t next, gap, nbits;
+    uint64_t g0, g1;
+};
+
+__device__ __forceinline__ SegLoad load_segment(const GemmArgs &g, uint64_t s, uint32_t lane)
 {
+    SegLoad L;
     const uint32_t *w = g.words + s * kSegWords + lane * 4;
-    const uint4 own = *reinterpret_cast<const uint4 *>(w);
-    const uint32_t next = w[4];
-    const uint32_t gap = g.gaps[s * 64 + lane];
-    const uint64_t g0 = g.segs[s].elem_off, g1 = g.segs[s + 1].elem_off;
-    const uint32_t nbits = g.segs[s].nbits;
-    if (g0 >= tile_start && g1 >= g0 && g1 <= tile_start + kTile) {
+    L.own = *reinterpret_cast<const uint4 *>(w);
+    L.next = w[4];
+    L.gap = g.gaps[s * 64 + lane];
+    L.g0 = g.segs[s].elem_off;
+    L.g1 = g.segs[s + 1].elem_off;
+    L.nbits = g.segs[s].nbits;
+    return L;
+}
+
+// Decode one tile-aligned segment into the exponent plane of its tile.
+template <int K>
+__device__ __forceinline__ void decode_into_plane(const SegLoad &L, uint64_t tile_start, uint32_t plane,
+                                                  uint32_t fast, uint32_t chain, uint32_t lane)
+{
+    if (L.g0 >= tile_start && L.g1 >= L.g0 && L.g1 <= tile_start + kTile) {
         const uint32_t c0 = lane * kChunkBits;
-        const uint32_t end = nbits > c0 ? min(kChunkBits, nbits - c0) : 0u;
-        const Window win = make_window(own, next, gap);
-        const uint32_t cnt = gap < end ? count_codes<K>(win, fast, chain, gap, end) : 0u;
+        const uint32_t end = L.nbits > c0 ? min(kChunkBits, L.nbits - c0) : 0u;
+        const Window win = make_window(L.own, L.next, L.gap);
+        const uint32_t cnt = L.gap < end ? count_codes<K>(win, fast, chain, L.gap, end) : 0u;
         uint32_t total;
         const uint32_t excl = wave_exclusive_scan(cnt, &total);
-        if (total == (uint32_t)(g1 - g0))
-            emit_codes<K>(win, fast, chain, plane + (uint32_t)(g0 - tile_start) + excl, cnt);
+        if (total == (uint32_t)(L.g1 - L.g0))
+            emit_codes<K>(win, fast, chain, plane + (uint32_t)(L.g0 - tile_start) + excl, cnt);
     }
 }
 
-// BF16 tile address of the 16-byte chunk `c` (8 columns) of tile row r.
-__device__ __forceinline__ uint32_t bf_chunk(uint32_t bf, uint32_t r, uint32_t c)
-{
-    return bf + r * (kTC * 2) + ((c ^ r) << 4);
-}
-
-// MT: 32-row tiles of the batch (B <= 32 * MT).  WAVES: waves per workgroup.
-// Wave w works on batch tiles m = w % MT (+ WAVES, ... when MT > WAVES) and on
-// k-steps ks = w / MT (mod WAVES / MT) of every tile.
+// MT: 32-row tiles of the batch (B <= 32 * MT).  Wave w works on batch tiles
+// m = w % MT (and + WAVES, ... when MT > WAVES) and on the k-steps
+// ks = w / MT (mod WAVES / MT) of every weight tile.
 template <int K, int MT, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64)
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 decode_gemm_kernel(GemmArgs g)
 {
     constexpr int kMPerWave = MT > WAVES ? MT / WAVES : 1;
     constexpr int kKSlices = MT >= WAVES ? 1 : WAVES / MT;
+    constexpr uint32_t kThreads = WAVES * 64;
+    constexpr uint32_t kSmPerThread = kTile / 16 / kThreads;     // uint4 of sign+mantissa per thread
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = lane_id();
-    const uint32_t plane = lds0 + 16;
-    const uint32_t bf = lds0 + 16 + kPlaneBytes;
-    const uint32_t fast = bf + kBfBytes;
+    // [guard][exponent plane 0][exponent plane 1][sm plane 0][sm plane 1][tables]
+    const uint32_t eplane0 = lds0 + 16;
+    const uint32_t smplane0 = eplane0 + 2 * kTile;
+    const uint32_t fast = smplane0 + 2 * kTile;
     const uint32_t chain = fast + (8u << K);
 
-    for (uint32_t i = threadIdx.x; i < (2u << K); i += blockDim.x) st32(fast + 4 * i, g.fast[i]);
-    for (uint32_t i = threadIdx.x; i < g.n_chain; i += blockDim.x)
-        *(lds_u16 *)(size_t)(chain + 2 * i) = g.chain[i];
+    for (uint32_t i = threadIdx.x; i < (2u << K); i += kThreads) st32(fast + 4 * i, g.fast[i]);
+    for (uint32_t i = threadIdx.x; i < g.n_chain; i += kThreads) *(lds_u16 *)(size_t)(chain + 2 * i) = g.chain[i];
     __syncthreads();
 
     const uint32_t kslice = kKSlices > 1 ? wave / MT : 0;
     const uint32_t m_first = kKSlices > 1 ? wave % MT : wave;
+    const uint32_t n_l = lane & 31, khalf = lane >> 5;
+    const bool writes_w = g.w_debug && m_first == 0;
 
     for (uint32_t rb = blockIdx.x; rb < g.n_rowblocks; rb += gridDim.x) {
         f32x16 acc[kMPerWave];
 #pragma unroll
         for (int m = 0; m < kMPerWave; m++)
+#pragma unroll
             for (int j = 0; j < 16; j++) acc[m][j] = 0.0f;
 
-        for (uint32_t kt = 0; kt < g.tiles_per_row; kt++) {
-            const uint64_t t = (uint64_t)rb * g.tiles_per_row + kt;
-            const uint64_t tile_start = t * kTile;
-            // decode the tile's segments (one wave per segment)
-            const uint64_t s0 = g.block_seg[t], s1 = min(g.block_seg[t + 1], g.n_segments);
-            for (uint64_t s = s0 + wave; s < s1; s += WAVES)
-                decode_segment_to_plane<K>(g, s, tile_start, plane, fast, chain, lane);
-            __syncthreads();
-
-            // merge exponents and sign+mantissa bytes into the swizzled BF16 tile
-            for (uint32_t q = threadIdx.x; q < kTile / 16; q += WAVES * 64) {
-                const uint32_t r = q >> 5, c = (q & 31) * 2;
-                const uint4 smv = *reinterpret_cast<const uint4 *>(g.sm + tile_start + 16ull * q);
-                const uint4 rx = ld128(plane + 16 * q);
-                const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
-                const uint2 cc = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
-                *(lds_u4 *)(size_t)bf_chunk(bf, r, c) = v4u32{a.x, a.y, b.x, b.y};
-                *(lds_u4 *)(size_t)bf_chunk(bf, r, c + 1) = v4u32{cc.x, cc.y, d.x, d.y};
-                if (g.w_debug) {
-                    uint4 *dst = reinterpret_cast<uint4 *>(g.w_debug + (uint64_t)(rb * kTR + r) * g.K + kt * kTC + c * 8);
-                    dst[0] = make_uint4(a.x, a.y, b.x, b.y);
-                    dst[1] = make_uint4(cc.x, cc.y, d.x, d.y);
-                }
+        // tile 0: copy its sign+mantissa bytes and decode its segments
+        {
+            const uint64_t t0 = (uint64_t)rb * g.tiles_per_row;
+            const uint64_t ts = t0 * kTile;
+#pragma unroll
+            for (uint32_t i = 0; i < kSmPerThread; i++) {
+                const uint32_t q = threadIdx.x + i * kThreads;
+                const uint4 v = *reinterpret_cast<const uint4 *>(g.sm + ts + 16ull * q);
+                *(lds_u4 *)(size_t)(smplane0 + 16 * q) = v4u32{v.x, v.y, v.z, v.w};
             }
+            const uint64_t s1 = min(g.block_seg[t0 + 1], g.n_segments);
+            for (uint64_t s = g.block_seg[t0] + wave; s < s1; s += WAVES)
+                decode_into_plane<K>(load_segment(g, s, lane), ts, eplane0, fast, chain, lane);
             __syncthreads();
+        }
 
-            // matrix cores: acc[m] += x[m-tile, k-step] * tile^T
-            const uint32_t n_l = lane & 31, khalf = lane >> 5;
-            for (uint32_t ks = kslice; ks < kTC / 16; ks += kKSlices) {
-                const v4u32 wb = *(const lds_u4 *)(size_t)bf_chunk(bf, n_l, 2 * ks + khalf);
+        for (uint32_t kt = 0; kt < g.tiles_per_row; kt++) {
+            const uint32_t cur = kt & 1;
+            const bool has_next = kt + 1 < g.tiles_per_row;
+            const uint64_t t = (uint64_t)rb * g.tiles_per_row + kt;
+            const uint64_t nts = (t + 1) * kTile;
+            // next tile's data in flight before the matrix work
+            uint4 smn[kSmPerThread];
+            SegLoad nseg{};
+            uint64_t ns0 = 0, ns1 = 0;
+            if (has_next) {
+#pragma unroll
+                for (uint32_t i = 0; i < kSmPerThread; i++)
+                    smn[i] = *reinterpret_cast<const uint4 *>(g.sm + nts + 16ull * (threadIdx.x + i * kThreads));
+                ns0 = g.block_seg[t + 1] + wave;
+                ns1 = min(g.block_seg[t + 2], g.n_segments);
+                if (ns0 < ns1) nseg = load_segment(g, ns0, lane);
+            }
+
+            // matrix cores on tile t
+            const uint32_t ep = eplane0 + cur * kTile, sp = smplane0 + cur * kTile;
+#pragma unroll 4
+            for (uint32_t i = 0; i < kTC / 16 / kKSlices; i++) {
+                const uint32_t ks = kslice + i * kKSlices;
+                const uint32_t c = 2 * ks + khalf;
+                const uint32_t off = c * (kTR * kKC) + n_l * kKC;
+                const uint2 rx = ld64(ep + off), sv = ld64(sp + off);
+                const uint2 lo = assemble4(sv.x, rx.x), hi = assemble4(sv.y, rx.y);
+                const v4u32 wb{lo.x, lo.y, hi.x, hi.y};
+                if (writes_w)
+                    *reinterpret_cast<uint4 *>(g.w_debug + (uint64_t)(rb * kTR + n_l) * g.K + kt * kTC + c * kKC) =
+                        make_uint4(lo.x, lo.y, hi.x, hi.y);
                 const bf16x8 bop = __builtin_bit_cast(bf16x8, wb);
 #pragma unroll
                 for (int m = 0; m < kMPerWave; m++) {
@@ -162,21 +191,37 @@ decode_gemm_kernel(GemmArgs g)
                     uint4 xa = make_uint4(0, 0, 0, 0);
                     if (brow < g.B)
                         xa = *reinterpret_cast<const uint4 *>(g.x + (uint64_t)brow * g.K + kt * kTC + ks * 16 + khalf * 8);
-                    const bf16x8 aop = __builtin_bit_cast(bf16x8, xa);
-                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, acc[m], 0, 0, 0);
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa), bop, acc[m], 0, 0, 0);
                 }
             }
-        }
-        // reduce the k-slices through LDS (the BF16 tile is free after this barrier)
-        if (kKSlices > 1) {
+
+            // next tile into the other buffer
+            if (has_next) {
+                const uint32_t nx = cur ^ 1;
+#pragma unroll
+                for (uint32_t i = 0; i < kSmPerThread; i++)
+                    *(lds_u4 *)(size_t)(smplane0 + nx * kTile + 16 * (threadIdx.x + i * kThreads)) =
+                        v4u32{smn[i].x, smn[i].y, smn[i].z, smn[i].w};
+                const uint32_t np = eplane0 + nx * kTile;
+                for (uint64_t s = ns0; s < ns1; s += WAVES)
+                    decode_into_plane<K>(s == ns0 ? nseg : load_segment(g, s, lane), nts, np, fast, chain, lane);
+            }
             __syncthreads();
-            float *red = (float *)lds_raw + (bf - lds0) / 4;
+        }
+
+        // reduce the k-slices through LDS (the planes are free after the last barrier)
+        if (kKSlices > 1) {
+            lds_f32 *red = (lds_f32 *)(size_t)eplane0;
             if (kslice > 0)
+#pragma unroll
                 for (int j = 0; j < 16; j++) red[((kslice - 1) * MT + m_first) * 1024 + j * 64 + lane] = acc[0][j];
             __syncthreads();
-            if (kslice == 0)
+            if (kslice == 0) {
+#pragma unroll 1
                 for (uint32_t ksl = 1; ksl < (uint32_t)kKSlices; ksl++)
+#pragma unroll
                     for (int j = 0; j < 16; j++) acc[0][j] += red[((ksl - 1) * MT + m_first) * 1024 + j * 64 + lane];
+            }
         }
         // y[b, n]: lane holds n = rb*32 + lane%32, b = m*32 + 8*blk + 4*(lane/32) + e
         if (kslice == 0) {
@@ -187,8 +232,8 @@ decode_gemm_kernel(GemmArgs g)
                 for (int blk = 0; blk < 4; blk++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const uint32_t b = mt * 32 + 8 * blk + 4 * (lane >> 5) + e;
-                        if (b < g.B) g.y[(uint64_t)b * g.N + rb * kTR + (lane & 31)] = acc[m][4 * blk + e];
+                        const uint32_t b = mt * 32 + 8 * blk + 4 * khalf + e;
+                        if (b < g.B) g.y[(uint64_t)b * g.N + rb * kTR + n_l] = acc[m][4 * blk + e];
                     }
             }
         }
@@ -198,7 +243,7 @@ decode_gemm_kernel(GemmArgs g)
 
 uint32_t gemm_lds_bytes(uint32_t fast_bits, uint32_t n_tables)
 {
-    return 16 + kPlaneBytes + kBfBytes + (8u << fast_bits) + n_tables * 512u;
+    return 16 + 4 * kTile + (8u << fast_bits) + n_tables * 512u;
 }
 
 int cu_count()
@@ -247,9 +292,9 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
 {
     if (!w || !x || !y) return df11::fail(DF11_E_ARG, "df11_decode_gemm: null pointer");
     if (B < 1 || B > 256) return df11::fail(DF11_E_ARG, "B = %u outside 1..256", B);
-    if (w->tile_rows != kTR || w->tile_cols != kTC || w->align_elems != kTile || w->chunk_bytes != 16 ||
-        w->seg_lanes != 64 || !w->rows || !w->cols || w->rows % kTR || w->cols % kTC ||
-        w->rows * w->cols != w->n)
+    if (w->tile_rows != kTR || w->tile_cols != kTC || w->tile_kchunk != kKC || w->align_elems != kTile ||
+        w->chunk_bytes != 16 || w->seg_lanes != 64 || !w->rows || !w->cols || w->rows % kTR ||
+        w->cols % kTC || w->rows * w->cols != w->n)
         return df11::fail(DF11_E_ARG, "weight was not encoded with df11_gemm_layout");
     if (w->rows > 0xFFFFFFFFull || w->cols > 0xFFFFFFFFull)
         return df11::fail(DF11_E_ARG, "weight too large");

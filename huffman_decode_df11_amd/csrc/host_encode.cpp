@@ -37,6 +37,7 @@ using namespace df11;
 // Gemm tiles: 32 weight rows by 512 columns, one tile per segment run.
 static const uint32_t kGemmTileRows = 32;
 static const uint32_t kGemmTileCols = 512;
+static const uint32_t kGemmKChunk = 8;
 
 extern "C" uint32_t df11_gemm_tile_rows(void) { return kGemmTileRows; }
 extern "C" uint32_t df11_gemm_tile_cols(void) { return kGemmTileCols; }
@@ -54,6 +55,7 @@ extern "C" int df11_gemm_layout(uint64_t rows, uint64_t cols, df11_layout *layou
     layout->cols = cols;
     layout->tile_rows = kGemmTileRows;
     layout->tile_cols = kGemmTileCols;
+    layout->tile_kchunk = kGemmKChunk;
     layout->align_elems = (uint64_t)kGemmTileRows * kGemmTileCols;
     return DF11_OK;
 }
@@ -77,21 +79,25 @@ int check_layout(const df11_layout &L, uint64_t n)
         if (L.rows % L.tile_rows || L.cols % L.tile_cols || L.tile_cols % 16)
             return fail(DF11_E_ARG, "tile %ux%u does not divide [%llu, %llu] or tile_cols %% 16 != 0",
                         L.tile_rows, L.tile_cols, (unsigned long long)L.rows, (unsigned long long)L.cols);
+        if (L.tile_kchunk && (L.tile_kchunk % 8 || L.tile_cols % L.tile_kchunk || L.tile_rows % 2))
+            return fail(DF11_E_ARG, "tile_kchunk %u: need a multiple of 8 dividing tile_cols, even tile_rows",
+                        L.tile_kchunk);
     } else if (L.cols && L.rows * L.cols != n) {
         return fail(DF11_E_ARG, "rows*cols != n");
     }
+    if (L.tile_kchunk && !L.tile_rows) return fail(DF11_E_ARG, "tile_kchunk needs tile order");
     return DF11_OK;
 }
 
 // Row-major index of stream element g.
 struct Order {
     bool tiled = false;
-    uint64_t cols = 0, tr = 0, tc = 0, tile = 0, tiles_per_row = 0;
+    uint64_t cols = 0, tr = 0, tc = 0, kc = 0, tile = 0, tiles_per_row = 0;
     explicit Order(const df11_layout &L)
     {
         if (L.tile_rows) {
             tiled = true;
-            cols = L.cols; tr = L.tile_rows; tc = L.tile_cols;
+            cols = L.cols; tr = L.tile_rows; tc = L.tile_cols; kc = L.tile_kchunk;
             tile = tr * tc;
             tiles_per_row = cols / tc;
         }
@@ -100,7 +106,15 @@ struct Order {
     {
         if (!tiled) return g;
         uint64_t t = g / tile, w = g - t * tile;
-        uint64_t r = w / tc, c = w - r * tc;
+        uint64_t r, c;
+        if (kc) {
+            const uint64_t grp = w / (tr * kc), in = w - grp * (tr * kc);
+            r = in / kc;
+            c = grp * kc + (in - r * kc);
+        } else {
+            r = w / tc;
+            c = w - r * tc;
+        }
         uint64_t rb = t / tiles_per_row, cb = t - rb * tiles_per_row;
         return (rb * tr + r) * cols + cb * tc + c;
     }
@@ -242,6 +256,7 @@ extern "C" int df11_encoded_view(const df11_encoded *enc, df11_view *v)
     v->cols = enc->layout.cols;
     v->tile_rows = enc->layout.tile_rows;
     v->tile_cols = enc->layout.tile_cols;
+    v->tile_kchunk = enc->layout.tile_kchunk;
     v->align_elems = enc->layout.align_elems;
     v->min_len = enc->min_len;
     v->max_len = enc->max_len;

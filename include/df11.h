@@ -62,7 +62,9 @@
  *              n_segments (ceil(n / align_elems) + 1 entries); else empty.
  *   Element order is row-major, or, when tile_rows > 0, tile order: the
  *   [rows, cols] matrix is cut into tile_rows x tile_cols tiles taken row
- *   block by row block, row-major inside each tile.
+ *   block by row block, row-major inside each tile, or, when tile_kchunk > 0,
+ *   in column groups of tile_kchunk columns: group after group, each group
+ *   row after row (the order matrix-core operands read).
  */
 #ifndef DF11_H
 #define DF11_H
@@ -113,6 +115,8 @@ typedef struct df11_layout {
     uint64_t align_elems;   /* 0, or begin a new segment every align_elems elements */
     uint64_t rows, cols;    /* matrix shape; cols = 0 means a flat tensor of rows = n */
     uint32_t tile_rows, tile_cols;  /* 0, 0: row-major; else tile order (see above) */
+    uint32_t tile_kchunk;           /* 0: row-major inside a tile; else column groups (see above) */
+    uint32_t reserved;
 } df11_layout;
 
 typedef struct df11_segment {
@@ -131,6 +135,7 @@ typedef struct df11_view {
     uint32_t chunk_bytes, seg_lanes;
     uint64_t rows, cols;
     uint32_t tile_rows, tile_cols;
+    uint32_t tile_kchunk, reserved0;
     uint64_t align_elems;
     uint32_t min_len, max_len, n_tables, fast_bits;
     uint32_t max_seg_elems;     /* most codes starting in any one segment */
@@ -181,8 +186,9 @@ void df11_encoded_free(df11_encoded *enc);
 int df11_encoded_view(const df11_encoded *enc, df11_view *v);
 
 /* The layout df11_decode_gemm needs for an [rows, cols] weight: tile order
- * with tiles of df11_gemm_tile_rows() x df11_gemm_tile_cols() elements, each
- * tile beginning a segment.  Errors: E_ARG when the shape does not divide. */
+ * with tiles of df11_gemm_tile_rows() x df11_gemm_tile_cols() elements in
+ * 8-column groups, each tile beginning a segment.  Errors: E_ARG when the
+ * shape does not divide. */
 int df11_gemm_layout(uint64_t rows, uint64_t cols, df11_layout *layout);
 uint32_t df11_gemm_tile_rows(void);
 uint32_t df11_gemm_tile_cols(void);

@@ -337,15 +337,24 @@ void orc_gemm_f64(const uint16_t *X, const uint16_t *W, uint64_t B, uint64_t N,
 }
 
 /* ---- element order for tiled streams: a [rows, cols] matrix cut into
- * tile_rows x tile_cols tiles, tiles taken row-block by row-block, and
- * elements row-major inside each tile. */
+ * tile_rows x tile_cols tiles, tiles taken row-block by row-block.  Inside a
+ * tile the elements go row-major (kc = 0), or, with kc > 0, in column groups
+ * of kc: group by group, each group row by row, kc elements per row. */
 void orc_tile_order(const uint16_t *u, uint64_t rows, uint64_t cols,
-                    uint64_t tr, uint64_t tc, uint16_t *out)
+                    uint64_t tr, uint64_t tc, uint64_t kc, uint16_t *out)
 {
     uint64_t k = 0;
     for (uint64_t rb = 0; rb < rows / tr; rb++)
-        for (uint64_t cb = 0; cb < cols / tc; cb++)
-            for (uint64_t r = 0; r < tr; r++)
-                for (uint64_t c = 0; c < tc; c++)
-                    out[k++] = u[(rb * tr + r) * cols + cb * tc + c];
+        for (uint64_t cb = 0; cb < cols / tc; cb++) {
+            if (!kc) {
+                for (uint64_t r = 0; r < tr; r++)
+                    for (uint64_t c = 0; c < tc; c++)
+                        out[k++] = u[(rb * tr + r) * cols + cb * tc + c];
+            } else {
+                for (uint64_t g = 0; g < tc / kc; g++)
+                    for (uint64_t r = 0; r < tr; r++)
+                        for (uint64_t c = 0; c < kc; c++)
+                            out[k++] = u[(rb * tr + r) * cols + cb * tc + g * kc + c];
+            }
+        }
 }

@@ -64,7 +64,7 @@ def lib():
                                    _u8p, _u64p, _u32p]
         L.orc_gemm_f32.argtypes = [_u16p, _u16p, _u64, _u64, _u64, _f32p]
         L.orc_gemm_f64.argtypes = [_u16p, _u16p, _u64, _u64, _u64, _f64p]
-        L.orc_tile_order.argtypes = [_u16p, _u64, _u64, _u64, _u64, _u16p]
+        L.orc_tile_order.argtypes = [_u16p, _u64, _u64, _u64, _u64, _u64, _u16p]
         _lib = L
     return _lib
 
@@ -192,10 +192,10 @@ def gemm_f64(X, W) -> np.ndarray:
     return Y
 
 
-def tile_order(u, rows: int, cols: int, tile_rows: int, tile_cols: int) -> np.ndarray:
+def tile_order(u, rows: int, cols: int, tile_rows: int, tile_cols: int, kchunk: int = 0) -> np.ndarray:
     u = _u16(u)
     out = np.zeros(u.size, np.uint16)
-    lib().orc_tile_order(u, rows, cols, tile_rows, tile_cols, out)
+    lib().orc_tile_order(u, rows, cols, tile_rows, tile_cols, kchunk, out)
     return out
 
 

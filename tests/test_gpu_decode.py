@@ -111,12 +111,30 @@ def test_aligned_layout():
     _check(synth.normal_bf16(500_000, 0.02, seed=3), layout=api.make_layout(align_elems=4096), tag="aligned")
 
 
-def test_tile_order_decodes_row_major():
+@pytest.mark.parametrize("kc", [0, 8, 16])
+def test_tile_order_decodes_row_major(kc):
+    """Tile order with and without column groups: the decode writes row-major
+    BF16, which must be the input (the oracle's encode/decode round trip is
+    the identity); the stream itself equals the oracle's encoding of the
+    oracle's permutation."""
     rows, cols = 128, 2048
     u = synth.normal_bf16(rows * cols, 0.02, seed=4).reshape(rows, cols)
-    lay = api.make_layout(rows=rows, cols=cols, tile_rows=32, tile_cols=512, align_elems=32 * 512)
-    _say("case tile order")
+    lay = api.make_layout(rows=rows, cols=cols, tile_rows=32, tile_cols=512, align_elems=32 * 512,
+                          tile_kchunk=kc)
+    _say("case tile order kc=%d" % kc)
     enc = api.encode(u, layout=lay)
+    ref = orc.encode(orc.tile_order(u, rows, cols, 32, 512, kc), lengths=api.codebook_lengths(enc.codebook),
+                     align_elems=32 * 512)
+    assert np.array_equal(enc.stream_bytes_msb_first(), ref.E)
+    got = _decode_checked(enc.to("cuda"), u.size)
+    assert np.array_equal(got, u.reshape(-1))
+
+
+def test_gemm_layout_decodes_row_major():
+    rows, cols = 96, 1536
+    u = synth.adversarial_bf16(rows * cols, seed=5).reshape(rows, cols)
+    _say("case gemm layout plain decode")
+    enc = api.encode(u, layout=api.gemm_layout(rows, cols))
     got = _decode_checked(enc.to("cuda"), u.size)
     assert np.array_equal(got, u.reshape(-1))
 

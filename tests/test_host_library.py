@@ -153,13 +153,15 @@ def test_encoder_matches_oracle(name, layout):
     assert np.array_equal(out, u)
 
 
-def test_encoder_tile_order_matches_oracle_permutation():
-    rows, cols, tr, tc = 64, 1024, 32, 512
+@pytest.mark.parametrize("kc", [0, 8, 16, 24])
+def test_encoder_tile_order_matches_oracle_permutation(kc):
+    rows, cols, tr, tc = 64, 1536 if kc == 24 else 1024, 32, 768 if kc == 24 else 512
     u = synth.normal_bf16(rows * cols, 0.02, seed=14).reshape(rows, cols)
-    lay = api.make_layout(rows=rows, cols=cols, tile_rows=tr, tile_cols=tc, align_elems=tr * tc)
+    lay = api.make_layout(rows=rows, cols=cols, tile_rows=tr, tile_cols=tc, align_elems=tr * tc,
+                          tile_kchunk=kc)
     enc = api.encode(u, layout=lay)
     ln = api.codebook_lengths(enc.codebook)
-    perm = orc.tile_order(u, rows, cols, tr, tc)
+    perm = orc.tile_order(u, rows, cols, tr, tc, kc)
     ref = orc.encode(perm, lengths=ln, align_elems=tr * tc)
     assert np.array_equal(enc.stream_bytes_msb_first(), ref.E)
     assert np.array_equal(enc.sm[:enc.n], ref.sm)
@@ -172,6 +174,7 @@ def test_gemm_layout_shape_rules():
     tr, tc = api.gemm_tile()
     lay = api.gemm_layout(14336, 4096)
     assert lay.tile_rows == tr and lay.tile_cols == tc and lay.align_elems == tr * tc
+    assert lay.tile_kchunk == 8
     with pytest.raises(_lib.DF11Error):
         api.gemm_layout(14336 + 1, 4096)
 
@@ -216,9 +219,15 @@ def test_max_len_too_small_rejected():
 
 
 @pytest.mark.parametrize("kw", [dict(chunk_bytes=6), dict(chunk_bytes=64), dict(align_elems=10),
-                                dict(rows=3, cols=5), dict(rows=100, cols=100, tile_rows=3, tile_cols=16)])
+                                dict(rows=3, cols=5), dict(rows=100, cols=100, tile_rows=3, tile_cols=16),
+                                dict(tile_kchunk=8),
+                                dict(rows=64, cols=160, tile_rows=32, tile_cols=32, tile_kchunk=12),
+                                dict(rows=64, cols=160, tile_rows=32, tile_cols=32, tile_kchunk=24),
+                                dict(rows=63, cols=160, tile_rows=7, tile_cols=32, tile_kchunk=8)])
 def test_bad_layout_rejected(kw):
-    u = synth.normal_bf16(10_000, 0.02, seed=16)
+    # the column-group cases have matching sizes, so only tile_kchunk is wrong
+    n = kw["rows"] * kw["cols"] if "tile_kchunk" in kw and "rows" in kw else 10_000
+    u = synth.normal_bf16(n, 0.02, seed=16)
     with pytest.raises(_lib.DF11Error) as ei:
         api.encode(u, layout=api.make_layout(**kw))
     assert ei.value.status == -1

@@ -360,3 +360,11 @@ def test_tile_order_hand_example():
     t = orc.tile_order(u, 4, 6, 2, 3)
     assert t.tolist() == [0, 1, 2, 6, 7, 8, 3, 4, 5, 9, 10, 11,
                           12, 13, 14, 18, 19, 20, 15, 16, 17, 21, 22, 23]
+
+
+def test_tile_order_column_groups_hand_example():
+    # [2, 8] matrix, one 2x8 tile, column groups of 4: row 0 cols 0-3, row 1
+    # cols 0-3, row 0 cols 4-7, row 1 cols 4-7
+    u = np.arange(16, dtype=np.uint16)
+    t = orc.tile_order(u, 2, 8, 2, 8, 4)
+    assert t.tolist() == [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
