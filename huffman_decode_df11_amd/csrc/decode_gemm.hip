@@ -61,6 +61,8 @@ struct GemmArgs {
     uint32_t N, K, B;
     uint32_t tiles_per_row;  // K / 512
     uint32_t n_rowblocks;    // N / 32
+    uint32_t split;          // K ranges per row block; > 1: y accumulated atomically
+    uint32_t tiles_per_split;
     uint64_t n_segments;
 };
 
@@ -100,9 +102,10 @@ __device__ __forceinline__ void decode_into_plane(const SegLoad &L, uint64_t til
     }
 }
 
-// MT: 32-row tiles of the batch (B <= 32 * MT).  Wave w works on batch tiles
-// m = w % MT (and + WAVES, ... when MT > WAVES) and on the k-steps
-// ks = w / MT (mod WAVES / MT) of every weight tile.
+// One workgroup of WAVES wavefronts takes a unit = (32-row block, range of
+// K tiles).  MT: 32-row tiles of the batch (B <= 32 * MT).  Wave w works on
+// batch tiles m = w % MT (and + WAVES, ... when MT > WAVES) and on the
+// k-steps ks = w / MT (mod WAVES / MT) of every weight tile.
 template <int K, int MT, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 decode_gemm_kernel(GemmArgs g)
@@ -110,15 +113,13 @@ decode_gemm_kernel(GemmArgs g)
     constexpr int kMPerWave = MT > WAVES ? MT / WAVES : 1;
     constexpr int kKSlices = MT >= WAVES ? 1 : WAVES / MT;
     constexpr uint32_t kThreads = WAVES * 64;
-    constexpr uint32_t kSmPerThread = kTile / 16 / kThreads;     // uint4 of sign+mantissa per thread
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = lane_id();
-    // [guard][exponent plane 0][exponent plane 1][sm plane 0][sm plane 1][tables]
+    // [guard][exponent plane 0][exponent plane 1][tables]
     const uint32_t eplane0 = lds0 + 16;
-    const uint32_t smplane0 = eplane0 + 2 * kTile;
-    const uint32_t fast = smplane0 + 2 * kTile;
+    const uint32_t fast = eplane0 + 2 * kTile;
     const uint32_t chain = fast + (8u << K);
 
     for (uint32_t i = threadIdx.x; i < (2u << K); i += kThreads) st32(fast + 4 * i, g.fast[i]);
@@ -129,56 +130,49 @@ decode_gemm_kernel(GemmArgs g)
     const uint32_t m_first = kKSlices > 1 ? wave % MT : wave;
     const uint32_t n_l = lane & 31, khalf = lane >> 5;
     const bool writes_w = g.w_debug && m_first == 0;
+    const uint32_t n_units = g.n_rowblocks * g.split;
 
-    for (uint32_t rb = blockIdx.x; rb < g.n_rowblocks; rb += gridDim.x) {
+    for (uint32_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+        const uint32_t rb = unit / g.split, sp = unit - rb * g.split;
+        const uint32_t kt0 = sp * g.tiles_per_split;
+        const uint32_t kt1 = min(kt0 + g.tiles_per_split, g.tiles_per_row);
         f32x16 acc[kMPerWave];
 #pragma unroll
         for (int m = 0; m < kMPerWave; m++)
 #pragma unroll
             for (int j = 0; j < 16; j++) acc[m][j] = 0.0f;
 
-        // tile 0: copy its sign+mantissa bytes and decode its segments
-        {
-            const uint64_t t0 = (uint64_t)rb * g.tiles_per_row;
-            const uint64_t ts = t0 * kTile;
-#pragma unroll
-            for (uint32_t i = 0; i < kSmPerThread; i++) {
-                const uint32_t q = threadIdx.x + i * kThreads;
-                const uint4 v = *reinterpret_cast<const uint4 *>(g.sm + ts + 16ull * q);
-                *(lds_u4 *)(size_t)(smplane0 + 16 * q) = v4u32{v.x, v.y, v.z, v.w};
-            }
+        {   // first tile of the range
+            const uint64_t t0 = (uint64_t)rb * g.tiles_per_row + kt0;
             const uint64_t s1 = min(g.block_seg[t0 + 1], g.n_segments);
             for (uint64_t s = g.block_seg[t0] + wave; s < s1; s += WAVES)
-                decode_into_plane<K>(load_segment(g, s, lane), ts, eplane0, fast, chain, lane);
+                decode_into_plane<K>(load_segment(g, s, lane), t0 * kTile, eplane0, fast, chain, lane);
             __syncthreads();
         }
 
-        for (uint32_t kt = 0; kt < g.tiles_per_row; kt++) {
-            const uint32_t cur = kt & 1;
-            const bool has_next = kt + 1 < g.tiles_per_row;
+        for (uint32_t kt = kt0; kt < kt1; kt++) {
+            const uint32_t cur = (kt - kt0) & 1;
+            const bool has_next = kt + 1 < kt1;
             const uint64_t t = (uint64_t)rb * g.tiles_per_row + kt;
-            const uint64_t nts = (t + 1) * kTile;
-            // next tile's data in flight before the matrix work
-            uint4 smn[kSmPerThread];
+            // next tile's first segment in flight during the matrix work
             SegLoad nseg{};
             uint64_t ns0 = 0, ns1 = 0;
             if (has_next) {
-#pragma unroll
-                for (uint32_t i = 0; i < kSmPerThread; i++)
-                    smn[i] = *reinterpret_cast<const uint4 *>(g.sm + nts + 16ull * (threadIdx.x + i * kThreads));
                 ns0 = g.block_seg[t + 1] + wave;
                 ns1 = min(g.block_seg[t + 2], g.n_segments);
                 if (ns0 < ns1) nseg = load_segment(g, ns0, lane);
             }
 
-            // matrix cores on tile t
-            const uint32_t ep = eplane0 + cur * kTile, sp = smplane0 + cur * kTile;
+            // matrix cores on tile t: B operand = 8 weights of row n_l, group c
+            const uint32_t ep = eplane0 + cur * kTile;
+            const uint8_t *smt = g.sm + t * kTile;
 #pragma unroll 4
             for (uint32_t i = 0; i < kTC / 16 / kKSlices; i++) {
                 const uint32_t ks = kslice + i * kKSlices;
                 const uint32_t c = 2 * ks + khalf;
                 const uint32_t off = c * (kTR * kKC) + n_l * kKC;
-                const uint2 rx = ld64(ep + off), sv = ld64(sp + off);
+                const uint2 sv = *reinterpret_cast<const uint2 *>(smt + off);
+                const uint2 rx = ld64(ep + off);
                 const uint2 lo = assemble4(sv.x, rx.x), hi = assemble4(sv.y, rx.y);
                 const v4u32 wb{lo.x, lo.y, hi.x, hi.y};
                 if (writes_w)
@@ -195,16 +189,12 @@ decode_gemm_kernel(GemmArgs g)
                 }
             }
 
-            // next tile into the other buffer
+            // next tile into the other plane
             if (has_next) {
-                const uint32_t nx = cur ^ 1;
-#pragma unroll
-                for (uint32_t i = 0; i < kSmPerThread; i++)
-                    *(lds_u4 *)(size_t)(smplane0 + nx * kTile + 16 * (threadIdx.x + i * kThreads)) =
-                        v4u32{smn[i].x, smn[i].y, smn[i].z, smn[i].w};
-                const uint32_t np = eplane0 + nx * kTile;
+                const uint32_t np = eplane0 + (cur ^ 1) * kTile;
                 for (uint64_t s = ns0; s < ns1; s += WAVES)
-                    decode_into_plane<K>(s == ns0 ? nseg : load_segment(g, s, lane), nts, np, fast, chain, lane);
+                    decode_into_plane<K>(s == ns0 ? nseg : load_segment(g, s, lane), (t + 1) * kTile, np, fast, chain,
+                                         lane);
             }
             __syncthreads();
         }
@@ -233,17 +223,35 @@ decode_gemm_kernel(GemmArgs g)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const uint32_t b = mt * 32 + 8 * blk + 4 * khalf + e;
-                        if (b < g.B) g.y[(uint64_t)b * g.N + rb * kTR + n_l] = acc[m][4 * blk + e];
+                        if (b < g.B) {
+                            float *dst = g.y + (uint64_t)b * g.N + rb * kTR + n_l;
+                            if (g.split > 1)
+                                unsafeAtomicAdd(dst, acc[m][4 * blk + e]);
+                            else
+                                *dst = acc[m][4 * blk + e];
+                        }
                     }
             }
         }
-        __syncthreads();   // the reduction buffer and planes are reused by the next row block
+        __syncthreads();   // the reduction buffer and planes are reused by the next unit
     }
+}
+
+__global__ void zero_kernel(float4 *p, uint64_t n4)
+{
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n4; i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__global__ void zero_tail_kernel(float *p, uint64_t n)
+{
+    const uint64_t i = threadIdx.x;
+    if (i < n) p[i] = 0.f;
 }
 
 uint32_t gemm_lds_bytes(uint32_t fast_bits, uint32_t n_tables)
 {
-    return 16 + 4 * kTile + (8u << fast_bits) + n_tables * 512u;
+    return 16 + 2 * kTile + (8u << fast_bits) + n_tables * 512u;
 }
 
 int cu_count()
@@ -259,13 +267,28 @@ int cu_count()
 }
 
 template <int K, int MT, int W>
-int launch(const GemmArgs &a, uint32_t lds, hipStream_t st)
+int launch(GemmArgs a, uint32_t lds, hipStream_t st)
 {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gemm_kernel<K, MT, W>, W * 64, lds) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
-    const uint32_t groups = std::min<uint32_t>(a.n_rowblocks, (uint32_t)(cu_count() * per_cu));
+    const uint32_t slots = (uint32_t)(cu_count() * per_cu);
+    // split K when there are too few row blocks to fill every slot
+    uint32_t split = 1;
+    if (const char *e = getenv("DF11_GEMM_SPLIT")) split = (uint32_t)atoi(e);
+    else if (2 * a.n_rowblocks <= slots) split = (slots + a.n_rowblocks - 1) / a.n_rowblocks;
+    split = std::max(1u, std::min(split, a.tiles_per_row));
+    a.tiles_per_split = (a.tiles_per_row + split - 1) / split;
+    a.split = (a.tiles_per_row + a.tiles_per_split - 1) / a.tiles_per_split;
+    if (a.split > 1) {
+        const uint64_t n = (uint64_t)a.B * a.N, n4 = n / 4;
+        if (n4) hipLaunchKernelGGL(zero_kernel, dim3((uint32_t)std::min<uint64_t>((n4 + 255) / 256, 4096)), dim3(256), 0, st,
+                                   reinterpret_cast<float4 *>(a.y), n4);
+        if (n & 3) hipLaunchKernelGGL(zero_tail_kernel, dim3(1), dim3(64), 0, st, a.y + n4 * 4, n & 3);
+    }
+    const uint32_t units = a.n_rowblocks * a.split;
+    const uint32_t groups = std::min<uint32_t>(units, slots);
     hipLaunchKernelGGL((decode_gemm_kernel<K, MT, W>), dim3(groups), dim3(W * 64), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
@@ -305,9 +328,9 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
     if (w->fast_bits < DF11_FAST_BITS_MIN || w->fast_bits > DF11_FAST_BITS_MAX || w->n_tables < 1 ||
         w->n_tables > DF11_MAX_TABLES || w->n_chain != (uint64_t)w->n_tables * 256 || w->n_fast != (2ull << w->fast_bits))
         return df11::fail(DF11_E_ARG, "table sizes inconsistent");
-    if (((uintptr_t)x & 15) || ((uintptr_t)y & 3) || ((uintptr_t)w_debug & 15) || ((uintptr_t)w->sm & 15) ||
+    if (((uintptr_t)x & 15) || ((uintptr_t)y & 15) || ((uintptr_t)w_debug & 15) || ((uintptr_t)w->sm & 15) ||
         ((uintptr_t)w->exp_words & 15))
-        return df11::fail(DF11_E_ARG, "x, w_debug and the view arrays must be 16-byte aligned");
+        return df11::fail(DF11_E_ARG, "x, y, w_debug and the view arrays must be 16-byte aligned");
     GemmArgs a{};
     a.words = w->exp_words;
     a.sm = w->sm;

@@ -227,8 +227,13 @@ int df11_decode_batch(const df11_view *device_views, uint16_t *const *outs, uint
  * device [B, K] BF16 row-major matrix, y a device [B, N] float32 matrix.
  * Products of BF16 values are exact in float32 and accumulate in float32.
  * w_debug: NULL, or a device [N, K] buffer that also receives the decoded
- * BF16 weights.  B in 1..256.  Errors: E_ARG (null, misaligned, layout not
- * from df11_gemm_layout, B out of range), E_UNSUPPORTED, E_DEVICE. */
+ * BF16 weights.  B in 1..256.  x, y and w_debug 16-byte aligned.  y is
+ * overwritten.  When the weight has fewer 32-row blocks than the device has
+ * workgroup slots, the K range is split and the partial sums are added into
+ * y (cleared first, on the same stream) with float atomics, so the order of
+ * those few additions, and with it the last bits of y, can differ from run
+ * to run.  Errors: E_ARG (null, misaligned, layout not from
+ * df11_gemm_layout, B out of range), E_UNSUPPORTED, E_DEVICE. */
 int df11_decode_gemm(const df11_view *device_view, const uint16_t *x, uint32_t B,
                      float *y, uint16_t *w_debug, void *stream);
 

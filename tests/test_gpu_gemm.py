@@ -61,6 +61,19 @@ def test_small_weight_all_batch_shapes(B):
     assert _rel(y, orc.gemm_f32(X, W).astype(np.float64)) < TOL
 
 
+@pytest.mark.parametrize("N,K,B", [(256, 14336, 5), (128, 4096, 40), (32, 512, 256)])
+def test_k_split_shapes(N, K, B):
+    """Few 32-row blocks: the K range is split across workgroups and the
+    partial sums meet in y (28 tiles per row in 7 ranges of 4; 8 tiles in 8
+    ranges; a single tile)."""
+    _say("case gemm split N=%d K=%d B=%d" % (N, K, B))
+    W = synth.normal_bf16(N * K, 0.02, seed=26).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=27)
+    y, wd = _run(W, X)
+    assert np.array_equal(wd, W), "decoded weights differ"
+    assert _rel(y, orc.gemm_f64(X, W)) < TOL
+
+
 def test_identity_x_recovers_weights_exactly():
     # x = I: y[b, n] = W[n, b] exactly (one nonzero product per output)
     N, K, B = 64, 512, 256
