@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "df11_device.h"
 #include "df11_internal.h"
@@ -124,18 +125,19 @@ decode_kernel(BatchArgs b, TableArgs t)
     const uint32_t fast = lds0 + 16 + WAVES * t.stg_bytes;
     const uint32_t chain = fast + (8u << K);
 
-    // tables into LDS, once per workgroup
-    for (uint32_t i = threadIdx.x; i < (2u << K); i += blockDim.x) st32(fast + 4 * i, t.fast[i]);
-    for (uint32_t i = threadIdx.x; i < t.n_chain; i += blockDim.x)
-        *(lds_u16 *)(size_t)(chain + 2 * i) = t.chain[i];
-    __syncthreads();
-
+    // the first segment's words in flight while the tables go into LDS
     const uint64_t n_total = b.seg_begin[b.count];
     uint64_t s = (uint64_t)blockIdx.x * WAVES + wave;
     const uint64_t stride = (uint64_t)gridDim.x * WAVES;
+    uint32_t vi = 0;
+    SegLoad nx{};
+    if (s < n_total) {
+        vi = view_of(b, s);
+        nx = load_segment(b.v[vi], s - b.seg_begin[vi], lane);
+    }
+    stage_tables<K, WAVES * 64>(fast, chain, t.fast, t.chain, t.n_chain);
+    __syncthreads();
     if (s >= n_total) return;
-    uint32_t vi = view_of(b, s);
-    SegLoad nx = load_segment(b.v[vi], s - b.seg_begin[vi], lane);
     for (;;) {
         const SegLoad cur = nx;
         const ViewArgs &v = b.v[vi];
@@ -225,9 +227,9 @@ int check_view(const df11_view *v)
         return df11::fail(DF11_E_ARG, "view array sizes inconsistent with n / n_segments");
     if (v->n && (!v->exp_words || !v->sm || !v->gaps || !v->segs || !v->chain || !v->fast))
         return df11::fail(DF11_E_ARG, "null array in view");
-    if (((uintptr_t)v->sm & 15) || ((uintptr_t)v->exp_words & 15) || ((uintptr_t)v->fast & 7) ||
-        ((uintptr_t)v->segs & 7))
-        return df11::fail(DF11_E_ARG, "view arrays must be 16-byte aligned (sm, exp_words)");
+    if (((uintptr_t)v->sm & 15) || ((uintptr_t)v->exp_words & 15) || ((uintptr_t)v->fast & 15) ||
+        ((uintptr_t)v->chain & 15) || ((uintptr_t)v->segs & 7))
+        return df11::fail(DF11_E_ARG, "view arrays must be 16-byte aligned (sm, exp_words, fast, chain)");
     if (v->tile_rows) {
         if (!v->tile_cols || v->tile_cols % 16 || !v->cols || v->cols % v->tile_cols ||
             (uint64_t)v->tile_rows * v->tile_cols > 0xFFFFFFFFull ||
@@ -290,8 +292,10 @@ int try_launch(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, 
                hipStream_t st, int *resident)
 {
     if (waves != W) return 1;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<K, W>, W * 64, lds) != hipSuccess || per_cu < 1)
+    // *resident > 0: the resident waves per CU are already known
+    int per_cu = *resident > 0 ? *resident / W : 0;
+    if (per_cu < 1 &&
+        (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<K, W>, W * 64, lds) != hipSuccess || per_cu < 1))
         per_cu = 1;
     *resident = per_cu * W;
     if (!nseg) return 0;   // query only
@@ -317,29 +321,95 @@ int run_shape(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, u
            try_launch<K, 16>(waves, a, t, lds, nseg, st, resident);
 }
 
-// Waves per workgroup: the choice with the most resident waves per CU
-// (LDS and registers both count) among those whose exponent staging stays
-// in the first 64 KB of LDS (the emit loop keeps byte addresses in 16 bits).
-// DF11_DECODE_WAVES overrides the choice for tuning.
+// Waves per workgroup.  Occupancy (LDS and registers) gives, for every
+// choice whose exponent staging stays in the first 64 KB of LDS (the emit
+// loop keeps byte addresses in 16 bits), the waves that can be resident per
+// CU.  A tensor with more segments than all CUs can hold at once takes the
+// choice with the most resident waves; a smaller one takes the choice that
+// puts the fewest waves on the busiest CU (ties: larger workgroups, fewer
+// table copies), since each wave's segment is then latency-bound.
+// DF11_DECODE_WAVES overrides the choice for tuning.  Occupancy answers
+// depend only on (device, K, staging bytes, table count) and the last few
+// are kept so that a sequence of launches does not repeat the queries.
+constexpr int kNumChoices = sizeof(kWaveChoices) / sizeof(kWaveChoices[0]);
+struct ShapeKey {
+    int dev, k;
+    uint32_t stg, n_tables;
+    bool operator==(const ShapeKey &o) const
+    {
+        return dev == o.dev && k == o.k && stg == o.stg && n_tables == o.n_tables;
+    }
+};
+std::mutex g_shape_mu;
+ShapeKey g_shape_key[8];
+int g_shape_res[8][kNumChoices];
+uint32_t g_shape_n = 0;
+
+// res[i]: resident waves per CU with kWaveChoices[i] waves per workgroup (0: does not fit)
+template <int K>
+void resident_waves(const TableArgs &t, const df11_view *v, hipStream_t st, int res[kNumChoices])
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const ShapeKey key{dev, K, t.stg_bytes, v->n_tables};
+    {
+        std::lock_guard<std::mutex> g(g_shape_mu);
+        for (uint32_t i = 0; i < std::min(g_shape_n, 8u); i++)
+            if (g_shape_key[i] == key) {
+                std::memcpy(res, g_shape_res[i], sizeof(int) * kNumChoices);
+                return;
+            }
+    }
+    BatchArgs probe{};
+    for (int i = 0; i < kNumChoices; i++) {
+        const int w = kWaveChoices[i];
+        const uint32_t lds = lds_bytes(w, t.stg_bytes, v->fast_bits, v->n_tables);
+        res[i] = 0;
+        if (16 + (uint32_t)w * t.stg_bytes > 65520 || lds > 160u * 1024u) continue;
+        run_shape<K>(w, probe, t, lds, 0, st, &res[i]);
+    }
+    std::lock_guard<std::mutex> g(g_shape_mu);
+    g_shape_key[g_shape_n % 8] = key;
+    std::memcpy(g_shape_res[g_shape_n % 8], res, sizeof(int) * kNumChoices);
+    g_shape_n++;
+}
+
+// The choice index for nseg segments, or -1 when nothing fits.
+int pick_waves(const int res[kNumChoices], uint64_t nseg, uint64_t cus)
+{
+    const char *env = getenv("DF11_DECODE_WAVES");
+    const int forced = env ? atoi(env) : 0;
+    int best = -1;
+    for (int i = 0; i < kNumChoices; i++) {
+        if (!res[i]) continue;
+        if (forced) {
+            if (kWaveChoices[i] == forced) return i;
+            continue;
+        }
+        if (best < 0 || res[i] > res[best]) best = i;
+    }
+    if (forced || best < 0 || nseg >= cus * (uint64_t)res[best]) return best;
+    uint64_t best_load = ~0ull;
+    for (int i = 0; i < kNumChoices; i++) {
+        if (!res[i]) continue;
+        const uint64_t w = kWaveChoices[i], groups = (nseg + w - 1) / w;
+        if (groups > cus * (uint64_t)(res[i] / w)) continue;   // would not be resident at once
+        const uint64_t load = (groups + cus - 1) / cus * w;    // waves on the busiest CU
+        if (load <= best_load) { best_load = load; best = i; }
+    }
+    return best;
+}
+
 template <int K>
 int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
 {
-    int best = 0, best_res = -1;
-    const char *env = getenv("DF11_DECODE_WAVES");
-    const int forced = env ? atoi(env) : 0;
-    BatchArgs probe{};
-    for (int w : kWaveChoices) {
-        const uint32_t lds = lds_bytes(w, t.stg_bytes, v->fast_bits, v->n_tables);
-        if (16 + (uint32_t)w * t.stg_bytes > 65520 || lds > 160u * 1024u) continue;
-        int res = 0;
-        run_shape<K>(w, probe, t, lds, 0, st, &res);
-        if (forced == w || (!forced && res > best_res)) { best = w; best_res = res; }
-        if (forced == w) break;
-    }
-    if (!best) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
-    int res = 0;
-    run_shape<K>(best, a, t, lds_bytes(best, t.stg_bytes, v->fast_bits, v->n_tables), a.seg_begin[a.count], st,
-                 &res);
+    int res[kNumChoices];
+    resident_waves<K>(t, v, st, res);
+    const int i = pick_waves(res, a.seg_begin[a.count], (uint64_t)device_cu_count());
+    if (i < 0) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
+    int r = res[i];
+    run_shape<K>(kWaveChoices[i], a, t, lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables),
+                 a.seg_begin[a.count], st, &r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode launch: %s", hipGetErrorString(e));
     return DF11_OK;

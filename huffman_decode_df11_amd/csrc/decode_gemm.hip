@@ -30,6 +30,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "df11_device.h"
 #include "df11_internal.h"
@@ -122,8 +123,7 @@ decode_gemm_kernel(GemmArgs g)
     const uint32_t fast = eplane0 + 2 * kTile;
     const uint32_t chain = fast + (8u << K);
 
-    for (uint32_t i = threadIdx.x; i < (2u << K); i += kThreads) st32(fast + 4 * i, g.fast[i]);
-    for (uint32_t i = threadIdx.x; i < g.n_chain; i += kThreads) *(lds_u16 *)(size_t)(chain + 2 * i) = g.chain[i];
+    stage_tables<K, kThreads>(fast, chain, g.fast, g.chain, g.n_chain);
     __syncthreads();
 
     const uint32_t kslice = kKSlices > 1 ? wave / MT : 0;
@@ -269,10 +269,25 @@ int cu_count()
 template <int K, int MT, int W>
 int launch(GemmArgs a, uint32_t lds, hipStream_t st)
 {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gemm_kernel<K, MT, W>, W * 64, lds) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
+    // resident workgroups per CU, queried once per (device, LDS size)
+    static std::mutex mu;
+    static int q_dev = -1, q_per_cu = 0;
+    static uint32_t q_lds = 0;
+    int dev = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        if (q_dev == dev && q_lds == lds) per_cu = q_per_cu;
+    }
+    if (!per_cu) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gemm_kernel<K, MT, W>, W * 64, lds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        std::lock_guard<std::mutex> lk(mu);
+        q_dev = dev;
+        q_lds = lds;
+        q_per_cu = per_cu;
+    }
     const uint32_t slots = (uint32_t)(cu_count() * per_cu);
     // split K when there are too few row blocks to fill every slot
     uint32_t split = 1;
@@ -329,7 +344,7 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
         w->n_tables > DF11_MAX_TABLES || w->n_chain != (uint64_t)w->n_tables * 256 || w->n_fast != (2ull << w->fast_bits))
         return df11::fail(DF11_E_ARG, "table sizes inconsistent");
     if (((uintptr_t)x & 15) || ((uintptr_t)y & 15) || ((uintptr_t)w_debug & 15) || ((uintptr_t)w->sm & 15) ||
-        ((uintptr_t)w->exp_words & 15))
+        ((uintptr_t)w->exp_words & 15) || ((uintptr_t)w->fast & 15) || ((uintptr_t)w->chain & 15))
         return df11::fail(DF11_E_ARG, "x, y, w_debug and the view arrays must be 16-byte aligned");
     GemmArgs a{};
     a.words = w->exp_words;

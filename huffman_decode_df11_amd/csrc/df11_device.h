@@ -205,6 +205,39 @@ __device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t x, uint32_t *to
     return v - x;
 }
 
+// Copy the multi-code table (8 << K bytes) and the hierarchical tables
+// (n_chain uint16 entries) from global memory into LDS at fast_lds and
+// chain_lds, with 16-byte accesses; every load of the first pass is issued
+// before the first LDS store.  Both global arrays are 16-byte aligned and
+// n_chain is a multiple of 8 (256 entries per table).
+template <int K, uint32_t THREADS>
+__device__ __forceinline__ void stage_tables(uint32_t fast_lds, uint32_t chain_lds, const uint32_t *fast,
+                                             const uint16_t *chain, uint32_t n_chain)
+{
+    constexpr uint32_t kFast4 = (8u << K) / 16;
+    constexpr uint32_t kPer = (kFast4 + THREADS - 1) / THREADS;
+    const uint4 *f4 = reinterpret_cast<const uint4 *>(fast);
+    const uint4 *c4 = reinterpret_cast<const uint4 *>(chain);
+    const uint32_t nc4 = n_chain / 8, tid = threadIdx.x;
+    uint4 v[kPer];
+#pragma unroll
+    for (uint32_t i = 0; i < kPer; i++) {
+        const uint32_t idx = tid + i * THREADS;
+        v[i] = idx < kFast4 ? f4[idx] : make_uint4(0, 0, 0, 0);
+    }
+    const uint4 c = tid < nc4 ? c4[tid] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (uint32_t i = 0; i < kPer; i++) {
+        const uint32_t idx = tid + i * THREADS;
+        if (idx < kFast4) *(lds_u4 *)(size_t)(fast_lds + 16 * idx) = v4u32{v[i].x, v[i].y, v[i].z, v[i].w};
+    }
+    if (tid < nc4) *(lds_u4 *)(size_t)(chain_lds + 16 * tid) = v4u32{c.x, c.y, c.z, c.w};
+    for (uint32_t idx = tid + THREADS; idx < nc4; idx += THREADS) {
+        const uint4 w = c4[idx];
+        *(lds_u4 *)(size_t)(chain_lds + 16 * idx) = v4u32{w.x, w.y, w.z, w.w};
+    }
+}
+
 // Merge 4 sign+mantissa bytes with 4 rotated exponents into 4 BF16 words.
 __device__ __forceinline__ uint2 assemble4(uint32_t sm, uint32_t rx)
 {
