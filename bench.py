@@ -4,7 +4,12 @@
 Default workload: one Llama-3-8B-shaped decoder layer of synthetic
 N(0, 0.02) BF16 weights (q, k, v, o, gate, up, down: 218,103,808 elements)
 with one codebook for the layer, compressed and resident in HBM.  One step
-decodes all seven matrices, one after another, into one reused BF16 buffer.
+decodes all seven matrices, one after another, into one reused BF16 buffer;
+the seven launches are captured once as a HIP graph and replayed.
+
+Also reported: the same launches issued eagerly, one batched launch per
+layer, the whole 8B-parameter model (226 matrices) per pass, and the fused
+decode+GEMM on up_proj at B in {1, 8, 64, 256}.
 
 Prints one JSON line:
   value     decoded BF16 GB/s (2 bytes per element / step time)
@@ -14,7 +19,7 @@ Prints one JSON line:
   cpu_baseline  the CPU oracle's bit-serial decode of the same layer, timed
             on this host (single thread)
 
-    python bench.py [--steps K] [--warmup W] [--workload layer|tensor1024|adversarial|fused]
+    python bench.py [--steps K] [--warmup W] [--no-model] [--no-fused] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -87,8 +92,20 @@ def build_layer(seed: int = 0):
     return encs
 
 
+def _hold_queue(ms: float):
+    """Put a bounded spin kernel at the head of the stream, so that the host
+    enqueues the timed launches while the GPU is busy and the events then
+    see kernel durations, not host launch gaps."""
+    import torch
+    sleep = getattr(torch.cuda, "_sleep", None)
+    if sleep is not None:
+        sleep(int(ms * 1e-3 * 2.4e9))
+
+
 def time_decode(dts, outbuf, steps: int, warmup: int):
-    """Time `steps` passes over all tensors; also time every launch."""
+    """`steps` passes of per-matrix launches, an event before and after every
+    launch, on the launch stream.  Returns (ms per pass, [steps, tensors]
+    per-launch ms, ms per pass without the queue hold)."""
     import torch
     from huffman_decode_df11_amd import api
     stream = torch.cuda.current_stream()
@@ -96,21 +113,27 @@ def time_decode(dts, outbuf, steps: int, warmup: int):
         for dt in dts:
             api.decode(dt, out=outbuf, stream=stream)
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in dts]
-          for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(dts) + 1)] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    _hold_queue(2.0 + 0.05 * steps * len(dts))
     start.record(stream)
     for s in range(steps):
+        ev[s][0].record(stream)
         for i, dt in enumerate(dts):
-            ev[s][i][0].record(stream)
             api.decode(dt, out=outbuf, stream=stream)
-            ev[s][i][1].record(stream)
+            ev[s][i + 1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    per_launch = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])   # [steps, tensors] ms
-    return total_ms / steps, per_launch
+    per_launch = np.array([[row[i].elapsed_time(row[i + 1]) for i in range(len(dts))] for row in ev])
+    held_ms = start.elapsed_time(stop) / steps
+    # the same loop as a host-driven sequence with no hold: what an eager caller sees
+    start.record(stream)
+    for s in range(steps):
+        for dt in dts:
+            api.decode(dt, out=outbuf, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return held_ms, per_launch, start.elapsed_time(stop) / steps
 
 
 def time_batched(dts, steps: int, warmup: int):
@@ -162,6 +185,58 @@ def time_graph(dts, outbuf, steps: int, warmup: int):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def model_pass(steps: int, warmup: int, seed: int = 0):
+    """The 8B-parameter model (32 layers, embedding, LM head; 226 matrices,
+    8,029,995,008 elements, one codebook per layer): every matrix decoded
+    into one reused buffer, as eager launches, as one HIP graph, and as one
+    batched launch per layer."""
+    import torch
+    from huffman_decode_df11_amd import model as mdl
+    t0 = time.time()
+    m = mdl.synthetic_llama3_8b(seed=seed, device="cuda")
+    t_build = time.time() - t0
+    checked = mdl.verify_pass(m, seed)
+    log("8B model built in %.1f s; all %d elements decoded and verified" % (t_build, checked))
+    alg = sum((t.total_bits + 7) // 8 + t.n + t.n_segments * 80 + 16 + 2 * t.n for _, _, t in m.matrices)
+
+    def timeit(f, n):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    n = max(3, steps // 4)
+    t_eager = timeit(m.decode_pass, n)
+    t_graph = timeit(m.capture(), n)
+    t_batched = timeit(m.decode_pass_batched, n)
+    out = {
+        "workload": "llama3-8b model: embedding, 32 layers, LM head, bf16 N(0,0.02), "
+                    "%d elements in %d matrices, one codebook per layer, one reused buffer" % (
+                        m.n_elements, len(m.matrices)),
+        "elements": m.n_elements,
+        "compressed_bytes": m.compressed_nbytes(),
+        "bf16_bytes": 2 * m.n_elements,
+        "bits_per_weight": round(8.0 * m.compressed_nbytes() / m.n_elements, 4),
+        "build_s": round(t_build, 1),
+        "verified_elements": checked,
+        "passes_timed": n,
+    }
+    for name, t, launches in (("graph", t_graph, len(m.matrices)), ("eager", t_eager, len(m.matrices)),
+                              ("batched_per_layer", t_batched, len(m.groups))):
+        out[name] = {"ms_per_pass": round(t, 3), "launches": launches,
+                     "decoded_gbs": round(2.0 * m.n_elements / (t * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(alg / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del m
+    torch.cuda.empty_cache()
+    return out
 
 
 def fused_up_proj(steps: int, warmup: int, seed: int = 0):
@@ -267,6 +342,7 @@ def main():
     ap.add_argument("--workload", default="layer", choices=["layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-model", action="store_true", help="skip the 8B-parameter model pass")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM counters)")
@@ -290,7 +366,12 @@ def main():
     verify(dts, mats, outbuf)
     log("parity verified on all %d matrices" % len(dts))
 
-    ms_per_step, per_launch = time_decode(dts, outbuf, args.steps, args.warmup)
+    held_ms, per_launch, eager_ms = time_decode(dts, outbuf, args.steps, args.warmup)
+    ms_per_step = time_graph(dts, outbuf, args.steps, args.warmup)
+    # after the replays the buffer holds the last matrix of the layer
+    last = outbuf.view(torch.int16)[:mats[-1].size].cpu().numpy().view(np.uint16)
+    if not np.array_equal(last, mats[-1].reshape(-1)):
+        raise SystemExit("graph replay parity check failed")
     alg = [algorithmic_bytes(e) for _, _, e in encs]
     launch_ms = per_launch.mean(axis=0)                  # average duration per tensor
     achieved = (sum(alg) / len(alg)) / (launch_ms.mean() * 1e-3) / 1e9
@@ -312,7 +393,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "llama3-8b-layer: q,k,v,o,gate,up,down bf16 N(0,0.02), 218,103,808 elements, "
-                        "one codebook, decoded into one reused buffer",
+                        "one codebook, each matrix decoded in its own launch into one reused buffer, "
+                        "the seven launches replayed as one HIP graph",
             "elements": n_total,
             "launches_per_step": len(dts),
             "bits_per_weight": round(8.0 * compressed / n_total, 4),
@@ -330,6 +412,13 @@ def main():
             "kernel": "decode_kernel",
             "algorithmic_bytes_per_element": round(sum(alg) / n_total, 4),
             "launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
+            "timing": "events between consecutive launches on the launch stream, queue held busy "
+                      "so the host runs ahead",
+        },
+        "eager_layer": {
+            "launches_per_step": len(dts), "ms_per_step": round(eager_ms, 4),
+            "decoded_gbs": round(2.0 * n_total / (eager_ms * 1e-3) / 1e9, 2),
+            "note": "the same seven launches issued from Python one by one",
         },
     }
     t_batch, outs = time_batched(dts, args.steps, args.warmup)
@@ -342,12 +431,9 @@ def main():
         "hbm_frac": round(sum(alg) / (t_batch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "buffer": "one reused layer-sized buffer, each matrix in its own slice",
     }
-    t_graph = time_graph(dts, outbuf, args.steps, args.warmup)
-    result["graph_layer"] = {
-        "launches_per_step": len(dts), "ms_per_step": round(t_graph, 4),
-        "decoded_gbs": round(2.0 * n_total / (t_graph * 1e-3) / 1e9, 2),
-        "note": "the seven per-matrix launches captured in one HIP graph",
-    }
+    del outs
+    if not args.no_model:
+        result["model_pass"] = model_pass(args.steps, args.warmup, args.seed)
     if not args.no_fused:
         result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
     if args.calibrate_copy:

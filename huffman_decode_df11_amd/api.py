@@ -205,6 +205,13 @@ class DF11Tensor:
         for name, _ in _lib.VIEW_ARRAYS:
             setattr(self.view, name, self.tensors[name].data_ptr())
         self.device = self.tensors["sm"].device
+        self.total_bits = int(enc.view.total_bits)
+        self.n_segments = int(enc.view.n_segments)
+        self._compressed = enc.compressed_nbytes()
+
+    def compressed_nbytes(self) -> int:
+        """Bytes of the encoding a decode reads (same count as Encoded's)."""
+        return self._compressed
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.tensors.values())

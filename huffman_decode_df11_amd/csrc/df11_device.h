@@ -129,27 +129,25 @@ __device__ __forceinline__ void wave_lds_sync()
 }
 
 // Locate: number of codes starting in [p0, end) of the lane's chunk; w is
-// the window at p0.
+// the window at p0.  Multi-code lookups run while a whole table window
+// (K bits) lies before `end`, so every code they count starts inside the
+// chunk; the last bits are then walked one code at a time.
 template <int K>
 __device__ __forceinline__ uint32_t count_codes(Window w, uint32_t fast, uint32_t chain, uint32_t p0,
                                                 uint32_t end)
 {
     uint32_t st = kM0 - p0;
-    const uint32_t lim = kM0 - end;            // p < end  <=>  (st & 0xFFFF) > lim
-    uint32_t meta = 0, prev = w.w0;
-    while ((st & 0xFFFFu) > lim) {
-        prev = w.w0;
-        meta = ld32(lshl_add_s<3>(w.w0 >> (32 - K), fast) + 4);
+    const uint32_t lim = kM0 - end;            // p < end      <=>  (st & 0xFFFF) > lim
+    const uint32_t limk = lim + K;             // p + K <= end <=>  (st & 0xFFFF) >= limk
+    while ((st & 0xFFFFu) >= limk) {
+        uint32_t meta = ld32(lshl_add_s<3>(w.w0 >> (32 - K), fast) + 4);
         if (meta == 0) meta = (1u << 16) - ((chain_decode(chain, w.w0) >> 8) & 0x3Fu);
         w.consume(meta);
         st += meta;
     }
-    // the last lookup may have counted codes that start at or past `end`:
-    // step back and redo it one code at a time (its codes lie in `prev`)
-    st -= meta;
     while ((st & 0xFFFFu) > lim) {
-        const uint32_t step = (1u << 16) - ((chain_decode(chain, prev) >> 8) & 0x3Fu);
-        prev = __builtin_amdgcn_alignbit(prev, 0u, step);
+        const uint32_t step = (1u << 16) - ((chain_decode(chain, w.w0) >> 8) & 0x3Fu);
+        w.consume(step);
         st += step;
     }
     return st >> 16;
@@ -171,11 +169,15 @@ __device__ __forceinline__ void emit_codes(Window w, uint32_t fast, uint32_t cha
             syms = rot_exp(e & 0xFFu);
             meta = (1u << 16) - ((e >> 8) & 0x3Fu);
         }
+        // bytes 0 and 2 of syms and of syms >> 8 (stores of a high half
+        // need no shift)
         const uint32_t a = st >> 16;
+        uint32_t t = syms >> 8;
+        asm("" : "+v"(t));   // keeps t >> 16 from being folded into syms >> 24
         st8(a, syms);
-        st8(a + 1, syms >> 8);
+        st8(a + 1, t);
         st8(a + 2, syms >> 16);
-        st8(a + 3, syms >> 24);
+        st8(a + 3, t >> 16);
         w.consume(meta);
         st += meta;
     }

@@ -19,6 +19,12 @@ Recipe (the pages publish no weights, so every workload is synthetic):
 
 Every tensor draws from its own stream: ``SeedSequence(seed).spawn(k)[i]``
 for the i-th of k tensors of a workload.
+
+The 8B-parameter model (32 layers, embedding, head: 8.03e9 elements) is
+drawn on the device with torch's Philox generator instead, seeded with
+``model_stream_seed(seed, tensor_index)``, so that it can be generated, and
+regenerated for checking, in seconds: same N(0, 0.02) float32 values
+rounded to BF16 with round-to-nearest-even.
 """
 from __future__ import annotations
 
@@ -119,3 +125,31 @@ def exhaustive_bf16() -> np.ndarray:
 def activations_bf16(batch: int, k: int = 4096, seed: int = 1) -> np.ndarray:
     """X[batch, k] ~ N(0, 1) as BF16 bits."""
     return normal_bf16(batch * k, 1.0, seed).reshape(batch, k)
+
+
+# ---------------------------------------------------------------- 8B model
+
+def llama3_8b_tensors(layers: int = LLAMA3_8B_LAYERS):
+    """(group, name, rows, cols) of every weight matrix of the model in
+    decode order: the embedding, the decoder layers, the LM head.  One
+    group shares one codebook."""
+    out = [("embed", "embed_tokens", LLAMA3_8B_VOCAB, LLAMA3_8B_HIDDEN)]
+    for i in range(layers):
+        out += [("layer%d" % i, name, r, c) for name, r, c in LLAMA3_8B_LAYER]
+    out.append(("head", "lm_head", LLAMA3_8B_VOCAB, LLAMA3_8B_HIDDEN))
+    return out
+
+
+def model_stream_seed(seed: int, index: int) -> int:
+    return (seed * 1000003 + index * 7919 + 17) & 0x7FFFFFFFFFFFFFFF
+
+
+def normal_bf16_torch(rows: int, cols: int, seed: int, index: int, device, sigma: float = 0.02):
+    """A [rows, cols] torch.bfloat16 tensor of N(0, sigma) drawn on `device`
+    from the Philox stream model_stream_seed(seed, index)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(model_stream_seed(seed, index))
+    x = torch.randn(rows, cols, generator=g, device=device, dtype=torch.float32)
+    x.mul_(sigma)
+    return x.to(torch.bfloat16)
