@@ -72,7 +72,8 @@ VIEW_ARRAYS = (
 EXPORTS = (
     "df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_free",
     "df11_encoded_view", "df11_gemm_layout", "df11_gemm_tile_rows", "df11_gemm_tile_cols",
-    "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_gemm", "df11_status_string",
+    "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_rows", "df11_decode_gemm",
+    "df11_status_string",
     "df11_last_error", "df11_version",
 )
 
@@ -111,6 +112,7 @@ def lib():
     L.df11_validate.argtypes = [ctypes.POINTER(View), ctypes.POINTER(Codebook)]
     L.df11_decode.argtypes = [ctypes.POINTER(View), vp, vp]
     L.df11_decode_batch.argtypes = [ctypes.POINTER(View), ctypes.POINTER(vp), u32, vp]
+    L.df11_decode_rows.argtypes = [ctypes.POINTER(View), vp, u64, vp, vp]
     L.df11_decode_gemm.argtypes = [ctypes.POINTER(View), vp, u32, vp, vp, vp]
     L.df11_status_string.argtypes = [ctypes.c_int]
     L.df11_status_string.restype = ctypes.c_char_p
@@ -118,7 +120,7 @@ def lib():
     L.df11_version.restype = ctypes.c_char_p
     for name in ("df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_view",
                  "df11_gemm_layout", "df11_validate", "df11_decode", "df11_decode_batch",
-                 "df11_decode_gemm"):
+                 "df11_decode_rows", "df11_decode_gemm"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

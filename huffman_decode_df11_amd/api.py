@@ -254,6 +254,22 @@ def decode_batch(tensors: Sequence[DF11Tensor], outs=None, stream=None):
     return outs
 
 
+def decode_rows(t: DF11Tensor, rows, out=None, stream=None):
+    """Decode only the rows `rows` (a device int64 tensor of row ids) of a
+    row-major [R, C] tensor into out [len(rows), C] (new when None)."""
+    import torch
+    C = int(t.host_view.cols)
+    rows = rows.reshape(-1)
+    assert rows.is_cuda and rows.dtype == torch.int64
+    rows = rows.contiguous()
+    if out is None:
+        out = torch.empty((rows.numel(), C), dtype=torch.bfloat16, device=rows.device)
+    assert out.is_contiguous() and out.numel() >= rows.numel() * C and out.element_size() == 2
+    check(lib().df11_decode_rows(ctypes.byref(t.view), rows.data_ptr(), rows.numel(), out.data_ptr(),
+                                 _stream_handle(stream)), "df11_decode_rows")
+    return out
+
+
 def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None):
     """y = x @ W^T with W decoded tile by tile inside the kernel.  x: [B, K]
     bf16 on the GPU; returns y [B, N] float32."""

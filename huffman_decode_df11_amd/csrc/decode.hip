@@ -113,6 +113,111 @@ __device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, u
     return L;
 }
 
+// ------------------------------------------------------------ one segment
+struct SegPlan {
+    uint64_t g0, g1, gbase;   // elements [g0, g1); 16-element groups from gbase
+    uint32_t head, ngroups;
+    bool valid;               // records consistent and the segment fits the staging
+};
+
+__device__ __forceinline__ SegPlan plan_segment(const SegLoad &cur, uint64_t n, uint32_t stg_bytes)
+{
+    SegPlan p;
+    p.g0 = cur.g0;
+    p.g1 = cur.g1;
+    p.gbase = p.g0 & ~15ull;
+    p.head = (uint32_t)(p.g0 & 15);
+    p.valid = p.g1 <= n && p.g1 >= p.g0 && (uint64_t)p.head + (p.g1 - p.g0) + 32 <= stg_bytes;
+    p.ngroups = p.valid ? (uint32_t)((((p.g1 + 15) & ~15ull) - p.gbase) >> 4) : 0u;
+    return p;
+}
+
+// the segment's sign+mantissa bytes for the first kPrefetchRounds rounds of groups
+__device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm, uint32_t lane,
+                                            uint4 (&smp)[kPrefetchRounds])
+{
+#pragma unroll
+    for (int r = 0; r < kPrefetchRounds; r++) {
+        const uint32_t gi = lane + 64u * r;
+        smp[r] = gi < p.ngroups ? *reinterpret_cast<const uint4 *>(sm + p.gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Locate, scan and emit one segment into the wave's staging (exponent of
+// element g at stg + g - gbase).  False when the stream disagrees with the
+// segment's records (then nothing is staged).
+template <int K>
+__device__ __forceinline__ bool stage_segment(const SegLoad &cur, const SegPlan &p, uint32_t stg, uint32_t fast,
+                                              uint32_t chain, uint32_t lane)
+{
+    const uint32_t c0 = lane * kChunkBits;
+    const uint32_t end = cur.nbits > c0 ? min(kChunkBits, cur.nbits - c0) : 0u;
+    const uint32_t p0 = cur.gap;
+    const Window win = make_window(cur.own, cur.next, p0);
+    const uint32_t cnt = p0 < end ? count_codes<K>(win, fast, chain, p0, end) : 0u;
+    uint32_t total;
+    const uint32_t excl = wave_exclusive_scan(cnt, &total);
+    if (total != (uint32_t)(p.g1 - p.g0)) return false;
+    emit_codes<K>(win, fast, chain, stg + p.head + excl, cnt);
+    wave_lds_sync();
+    return true;
+}
+
+// Output placement of decoded element g of a view (row-major, tile order or
+// column-group tiles).
+struct ViewOut {
+    const ViewArgs &v;
+    __device__ __forceinline__ uint16_t *at(uint64_t g) const { return v.out + out_index(v, g); }
+    __device__ __forceinline__ bool split8() const { return v.kc != 0; }
+};
+
+// Output placement of element g of row r into row i of a gather: out_row + (g - r * cols).
+struct RowOut {
+    uint16_t *out_row;
+    uint64_t row_start;
+    __device__ __forceinline__ uint16_t *at(uint64_t g) const { return out_row + (g - row_start); }
+    __device__ __forceinline__ bool split8() const { return false; }
+};
+
+// Merge the staged exponents of elements [lo, hi) (inside the segment) with
+// their sign+mantissa bytes and store BF16: whole 16-element groups with
+// 16-byte accesses, the ragged ends one element per lane (lanes 0..15 the
+// head group, lanes 16..31 the tail group).
+template <class Out>
+__device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint64_t hi, const uint4 (&smp)[kPrefetchRounds],
+                                            const uint8_t *sm, const Out &out, uint32_t stg, uint32_t lane)
+{
+    for (uint32_t r = 0; 64u * r < p.ngroups; r++) {
+        const uint32_t gi = lane + 64u * r;
+        uint4 smv;
+        if (r < kPrefetchRounds) {
+            smv = r == 0 ? smp[0] : r == 1 ? smp[1] : smp[2];
+        } else {
+            smv = gi < p.ngroups ? *reinterpret_cast<const uint4 *>(sm + p.gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
+        }
+        const uint64_t gs = p.gbase + 16ull * gi;
+        if (gi < p.ngroups && gs >= lo && gs + 16 <= hi) {
+            const uint4 rx = ld128(stg + 16 * gi);
+            const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
+            const uint2 c = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
+            // contiguous, or two 8-element runs of different rows for column groups
+            uint4 *dst0 = reinterpret_cast<uint4 *>(out.at(gs));
+            uint4 *dst1 = out.split8() ? reinterpret_cast<uint4 *>(out.at(gs + 8)) : dst0 + 1;
+            dst0[0] = make_uint4(a.x, a.y, b.x, b.y);
+            dst1[0] = make_uint4(c.x, c.y, d.x, d.y);
+        }
+    }
+    const uint64_t hend = min((lo + 15) & ~15ull, hi);
+    const uint64_t tstart = max(hi & ~15ull, hend);
+    const uint64_t g = lane < 16 ? lo + lane : tstart + (lane - 16);
+    const bool act = lane < 16 ? g < hend : (lane < 32 && g < hi);
+    if (act) {
+        const uint32_t rx = *(const lds_u8 *)(size_t)(stg + (uint32_t)(g - p.gbase));
+        *out.at(g) = assemble1(sm[g], rx);
+    }
+}
+
+// ------------------------------------------------------------ kernels
 template <int K, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
 decode_kernel(BatchArgs b, TableArgs t)
@@ -141,73 +246,70 @@ decode_kernel(BatchArgs b, TableArgs t)
     for (;;) {
         const SegLoad cur = nx;
         const ViewArgs &v = b.v[vi];
-        const uint64_t g0 = cur.g0, g1 = cur.g1;
-        const uint64_t gbase = g0 & ~15ull;
-        const uint32_t head = (uint32_t)(g0 & 15);
-        const bool valid = g1 <= v.n && g1 >= g0 && (uint64_t)head + (g1 - g0) + 32 <= t.stg_bytes;
-        const uint32_t ngroups = valid ? (uint32_t)((((g1 + 15) & ~15ull) - gbase) >> 4) : 0u;
-
-        // this segment's sign+mantissa bytes, first rounds
+        const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
         uint4 smp[kPrefetchRounds];
-#pragma unroll
-        for (int r = 0; r < kPrefetchRounds; r++) {
-            const uint32_t gi = lane + 64u * r;
-            smp[r] = gi < ngroups ? *reinterpret_cast<const uint4 *>(v.sm + gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
-        }
+        prefetch_sm(p, v.sm, lane, smp);
         // the next segment's stream words and records
         const uint64_t s_next = s + stride;
         const bool more = s_next < n_total;
         const uint32_t vi_next = more ? view_of(b, s_next) : vi;
         if (more) nx = load_segment(b.v[vi_next], s_next - b.seg_begin[vi_next], lane);
 
-        if (valid) {
-            const uint32_t c0 = lane * kChunkBits;
-            const uint32_t end = cur.nbits > c0 ? min(kChunkBits, cur.nbits - c0) : 0u;
-            const uint32_t p0 = cur.gap;
-            const Window win = make_window(cur.own, cur.next, p0);
-            const uint32_t cnt = p0 < end ? count_codes<K>(win, fast, chain, p0, end) : 0u;
-            uint32_t total;
-            const uint32_t excl = wave_exclusive_scan(cnt, &total);
-            if (total == (uint32_t)(g1 - g0)) {
-                emit_codes<K>(win, fast, chain, stg + head + excl, cnt);
-                wave_lds_sync();
-
-                // whole 16-element groups
-                for (uint32_t r = 0; 64u * r < ngroups; r++) {
-                    const uint32_t gi = lane + 64u * r;
-                    uint4 smv;
-                    if (r < kPrefetchRounds) {
-                        smv = r == 0 ? smp[0] : r == 1 ? smp[1] : smp[2];
-                    } else {
-                        smv = gi < ngroups ? *reinterpret_cast<const uint4 *>(v.sm + gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
-                    }
-                    const uint64_t gs = gbase + 16ull * gi;
-                    if (gi < ngroups && gs >= g0 && gs + 16 <= g1) {
-                        const uint4 rx = ld128(stg + 16 * gi);
-                        const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
-                        const uint2 c = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
-                        // row-major, or two 8-element runs of different rows for column groups
-                        uint4 *dst0 = reinterpret_cast<uint4 *>(v.out + out_index(v, gs));
-                        uint4 *dst1 = v.kc ? reinterpret_cast<uint4 *>(v.out + out_index(v, gs + 8)) : dst0 + 1;
-                        dst0[0] = make_uint4(a.x, a.y, b.x, b.y);
-                        dst1[0] = make_uint4(c.x, c.y, d.x, d.y);
-                    }
-                }
-                // ragged ends: lanes 0..15 the head group, lanes 16..31 the tail group
-                const uint64_t hend = min((g0 + 15) & ~15ull, g1);
-                const uint64_t tstart = max(g1 & ~15ull, hend);
-                const uint64_t g = lane < 16 ? g0 + lane : tstart + (lane - 16);
-                const bool act = lane < 16 ? g < hend : (lane < 32 && g < g1);
-                if (act) {
-                    const uint32_t rx = *(const lds_u8 *)(size_t)(stg + (uint32_t)(g - gbase));
-                    v.out[out_index(v, g)] = assemble1(v.sm[g], rx);
-                }
-            }
-        }
+        if (p.valid && stage_segment<K>(cur, p, stg, fast, chain, lane))
+            merge_range(p, p.g0, p.g1, smp, v.sm, ViewOut{v}, stg, lane);
         wave_lds_sync();   // the staging is reused by the next segment
         if (!more) break;
         s = s_next;
         vi = vi_next;
+    }
+}
+
+// Row gather: one wave per requested row; the segments that overlap the row
+// are found by binary search on the segment records, decoded whole into the
+// staging, and only the row's elements are written.
+struct RowArgs {
+    ViewArgs v;               // row-major view (out unused)
+    const int64_t *rows;      // requested row ids
+    uint16_t *out;            // [n_rows, cols]
+    uint64_t n_rows, n_view_rows;
+};
+
+template <int K, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
+decode_rows_kernel(RowArgs a, TableArgs t)
+{
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = lane_id();
+    const uint32_t stg = lds0 + 16 + wave * t.stg_bytes;
+    const uint32_t fast = lds0 + 16 + WAVES * t.stg_bytes;
+    const uint32_t chain = fast + (8u << K);
+    stage_tables<K, WAVES * 64>(fast, chain, t.fast, t.chain, t.n_chain);
+    __syncthreads();
+
+    const ViewArgs &v = a.v;
+    for (uint64_t i = (uint64_t)blockIdx.x * WAVES + wave; i < a.n_rows; i += (uint64_t)gridDim.x * WAVES) {
+        const int64_t r = a.rows[i];
+        if (r < 0 || (uint64_t)r >= a.n_view_rows) continue;   // out-of-range id: row left as it is
+        const uint64_t lo = (uint64_t)r * v.cols, hi = lo + v.cols;
+        // last segment whose first element is <= lo
+        uint64_t s0 = 0, s1 = v.n_segments;   // invariant: elem_off[s0] <= lo < elem_off[s1] (or s1 = end)
+        while (s1 - s0 > 1) {
+            const uint64_t mid = (s0 + s1) >> 1;
+            if (v.segs[mid].elem_off <= lo) s0 = mid; else s1 = mid;
+        }
+        const RowOut out{a.out + i * v.cols, lo};
+        for (uint64_t s = s0; s < v.n_segments; s++) {
+            const SegLoad cur = load_segment(v, s, lane);
+            if (cur.g0 >= hi) break;
+            const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
+            uint4 smp[kPrefetchRounds];
+            prefetch_sm(p, v.sm, lane, smp);
+            if (p.valid && cur.g1 > lo && stage_segment<K>(cur, p, stg, fast, chain, lane))
+                merge_range(p, max(lo, p.g0), min(hi, p.g1), smp, v.sm, out, stg, lane);
+            wave_lds_sync();
+        }
     }
 }
 
@@ -450,7 +552,65 @@ int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, 
     }
 }
 
+template <int K, int W>
+int launch_rows_w(const RowArgs &a, const TableArgs &t, uint32_t lds, int resident, hipStream_t st)
+{
+    const uint64_t per_cu = std::max(1, resident / W);
+    const uint64_t groups = std::min<uint64_t>((a.n_rows + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
+    hipLaunchKernelGGL((decode_rows_kernel<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
+    return DF11_OK;
+}
+
+template <int K>
+int launch_rows(const RowArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
+{
+    int res[kNumChoices];
+    resident_waves<K>(t, v, st, res);
+    const int i = pick_waves(res, a.n_rows, (uint64_t)device_cu_count());
+    if (i < 0) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
+    const uint32_t lds = lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables);
+    switch (kWaveChoices[i]) {
+    case 4: launch_rows_w<K, 4>(a, t, lds, res[i], st); break;
+    case 6: launch_rows_w<K, 6>(a, t, lds, res[i], st); break;
+    case 8: launch_rows_w<K, 8>(a, t, lds, res[i], st); break;
+    case 10: launch_rows_w<K, 10>(a, t, lds, res[i], st); break;
+    case 12: launch_rows_w<K, 12>(a, t, lds, res[i], st); break;
+    case 14: launch_rows_w<K, 14>(a, t, lds, res[i], st); break;
+    default: launch_rows_w<K, 16>(a, t, lds, res[i], st); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_rows launch: %s", hipGetErrorString(e));
+    return DF11_OK;
+}
+
 }  // namespace
+
+extern "C" int df11_decode_rows(const df11_view *v, const int64_t *rows, uint64_t n_rows, uint16_t *out,
+                                void *stream)
+{
+    int rc = check_view(v);
+    if (rc) return rc;
+    if (!n_rows) return DF11_OK;
+    if (!rows || !out || ((uintptr_t)out & 15) || ((uintptr_t)rows & 7))
+        return df11::fail(DF11_E_ARG, "df11_decode_rows: rows (8-byte aligned) and out (16-byte aligned) are device pointers");
+    if (v->tile_rows || !v->cols || !v->rows || v->rows * v->cols != v->n || v->cols % 8)
+        return df11::fail(DF11_E_ARG, "df11_decode_rows needs a row-major [rows, cols] view with cols a multiple of 8");
+    RowArgs a{};
+    a.v = make_args(v, nullptr);
+    a.rows = rows;
+    a.out = out;
+    a.n_rows = n_rows;
+    a.n_view_rows = v->rows;
+    TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, staging_bytes(v)};
+    hipStream_t st = (hipStream_t)stream;
+    switch (v->fast_bits) {
+    case 8: return launch_rows<8>(a, t, v, st);
+    case 9: return launch_rows<9>(a, t, v, st);
+    case 10: return launch_rows<10>(a, t, v, st);
+    case 11: return launch_rows<11>(a, t, v, st);
+    default: return launch_rows<12>(a, t, v, st);
+    }
+}
 
 extern "C" int df11_decode(const df11_view *v, uint16_t *out, void *stream)
 {

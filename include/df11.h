@@ -221,6 +221,18 @@ int df11_decode(const df11_view *device_view, uint16_t *out, void *stream);
 int df11_decode_batch(const df11_view *device_views, uint16_t *const *outs, uint32_t count,
                       void *stream);
 
+/* Row gather: decode rows rows[0..n_rows) of a row-major [rows, cols] view
+ * into out[i][0..cols) (device, 16-byte aligned, n_rows x cols BF16), for
+ * an embedding lookup that restores only the rows a batch uses ([P1] 2.2
+ * item 3: weights are restored right before use).  rows: device int64 ids,
+ * 8-byte aligned.  The segments that overlap each requested row are found
+ * by binary search on the segment records and decoded whole; only the row's
+ * elements are written.  An id outside [0, rows) leaves its output row
+ * unwritten.  Bit-exact like df11_decode.  Errors: E_ARG (null, misaligned,
+ * tile-ordered view, cols not a multiple of 8), E_UNSUPPORTED, E_DEVICE. */
+int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t n_rows, uint16_t *out,
+                     void *stream);
+
 /* Fused decode + matrix product ([P1] 2.2 item 3: decoded weights feed the
  * matmul and are discarded): y[b][j] = sum_k x[b][k] * W[j][k] for W the
  * [rows = N, cols = K] weight of `w` (encoded with df11_gemm_layout), x a

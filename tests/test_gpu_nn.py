@@ -1,0 +1,117 @@
+"""GPU checks of df11_decode_rows and of the DF11Linear / DF11Embedding
+modules.  Expected values: the input weights themselves (the oracle's
+encode/decode round trip is the identity), torch's own products of the same
+BF16 values, and the oracle's float64 product."""
+import sys
+
+import numpy as np
+import pytest
+
+from huffman_decode_df11_amd import api, synth
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from huffman_decode_df11_amd import nn as dnn   # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _i16(u):
+    return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).cuda()
+
+
+@pytest.mark.parametrize("rows,cols", [(1000, 4096), (333, 24), (64, 40000)])
+def test_decode_rows_matches_input(rows, cols):
+    """Random ids with repeats, the first and last rows; rows spanning one,
+    several and a fraction of a segment."""
+    _say("case decode_rows %dx%d" % (rows, cols))
+    W = synth.normal_bf16(rows * cols, 0.02, seed=30).reshape(rows, cols)
+    dt = api.encode(W, layout=api.make_layout(rows=rows, cols=cols)).to("cuda")
+    ids = np.concatenate([[0, rows - 1, rows - 1], np.random.default_rng(31).integers(0, rows, 200)])
+    out = api.decode_rows(dt, torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), _i16(W[ids]))
+
+
+def test_decode_rows_adversarial_and_bad_ids():
+    rows, cols = 512, 1024
+    _say("case decode_rows adversarial")
+    W = synth.adversarial_bf16(rows * cols, seed=32).reshape(rows, cols)
+    dt = api.encode(W, layout=api.make_layout(rows=rows, cols=cols)).to("cuda")
+    ids = torch.tensor([5, -1, rows, 7, 10 ** 12], dtype=torch.int64, device="cuda")
+    out = torch.full((5, cols), 0x5555, dtype=torch.int16, device="cuda")
+    api.decode_rows(dt, ids, out=out.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(o[0], W[5]) and np.array_equal(o[3], W[7])
+    for k in (1, 2, 4):   # out-of-range ids: rows left as they were
+        assert (o[k] == 0x5555).all()
+
+
+def test_decode_rows_rejects_tile_order():
+    from huffman_decode_df11_amd import _lib
+    W = synth.normal_bf16(64 * 512, 0.02, seed=33).reshape(64, 512)
+    dt = api.encode(W, layout=api.gemm_layout(64, 512)).to("cuda")
+    with pytest.raises(_lib.DF11Error):
+        api.decode_rows(dt, torch.zeros(3, dtype=torch.int64, device="cuda"))
+
+
+@pytest.mark.parametrize("B", [1, 7, 64, 300])
+def test_linear_fused_and_decode_modes(B):
+    N, K = 256, 1024
+    _say("case DF11Linear B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=34).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=35)
+    bias = torch.from_numpy(synth.normal_bf16(N, 0.1, seed=36).view(np.int16)).cuda().view(torch.bfloat16)
+    x = _i16(X).view(torch.bfloat16).reshape(B, K)
+    w = _i16(W).view(torch.bfloat16)
+    ref = (x.float() @ w.float().t() + bias.float())
+    for mode in ("fused", "decode"):
+        lin = dnn.DF11Linear(W, bias=bias, mode=mode)
+        y = lin(x)
+        torch.cuda.synchronize()
+        assert y.dtype == torch.bfloat16 and y.shape == (B, N)
+        rel = float((y.float() - ref).norm() / ref.norm())
+        assert rel < 8e-3, (mode, rel)          # BF16 output rounding dominates
+        assert torch.equal(lin.decoded_weight().view(torch.int16), w.view(torch.int16))
+    # without bias, against the oracle's float64 product (float32 output before rounding)
+    lin = dnn.DF11Linear(W, mode="fused")
+    if B <= 256:
+        y32 = api.decode_gemm(lin.weight_df11, x)
+        r64 = orc.gemm_f64(X.reshape(B, K), W)
+        assert float(np.linalg.norm(y32.cpu().numpy() - r64) / np.linalg.norm(r64)) < 2e-3
+
+
+def test_linear_from_torch_and_3d_input():
+    lin_t = torch.nn.Linear(512, 96, bias=True).to(torch.bfloat16).cuda()
+    lin = dnn.DF11Linear.from_linear(lin_t)
+    assert lin.mode == "fused"
+    x = torch.randn(2, 5, 512, device="cuda").to(torch.bfloat16)
+    y = lin(x)
+    yt = lin_t(x)
+    assert y.shape == (2, 5, 96)
+    assert float((y.float() - yt.float()).norm() / yt.float().norm()) < 8e-3
+    odd = dnn.DF11Linear(lin_t.weight[:, :300].contiguous(), mode="auto")   # 300 % 512 != 0
+    assert odd.mode == "decode"
+    assert torch.equal(odd(x[..., :300]).float(), (x[..., :300] @ lin_t.weight[:, :300].t()).float())
+
+
+def test_embedding_lookup():
+    V, D = 5000, 4096
+    _say("case DF11Embedding")
+    W = synth.normal_bf16(V * D, 0.02, seed=37).reshape(V, D)
+    emb = dnn.DF11Embedding(W)
+    ids = torch.from_numpy(np.random.default_rng(38).integers(0, V, (4, 33))).cuda()
+    out = emb(ids)
+    torch.cuda.synchronize()
+    assert out.shape == (4, 33, D) and out.dtype == torch.bfloat16
+    ref = torch.nn.functional.embedding(ids, _i16(W).view(torch.bfloat16))
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
