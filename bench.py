@@ -240,6 +240,63 @@ def model_pass(steps: int, warmup: int, seed: int = 0):
     return out
 
 
+def offload_pass(steps: int, warmup: int, seed: int = 0, layers: int = 4):
+    """Compressed CPU offload: `layers` decoder layers of the 8B model held in
+    pinned host memory, each streamed to the GPU one layer ahead of its
+    decode; next to a plain host-to-device copy of the same layers in BF16."""
+    import torch
+    from huffman_decode_df11_amd import model as mdl
+    from huffman_decode_df11_amd.offload import OffloadedModel
+    groups = mdl.encode_llama3_8b(seed=seed, device="cuda", layers=layers, embed_and_head=False)
+    off = OffloadedModel(groups)
+    out = torch.empty(off.max_elements, dtype=torch.bfloat16, device="cuda")
+    got = []
+    off.decode_pass(out, on_matrix=lambda g, name, o: got.append(o.view(torch.int16)[:16].clone()))
+    torch.cuda.synchronize()
+    specs = [sp for sp in __import__("huffman_decode_df11_amd.synth", fromlist=["x"]).llama3_8b_tensors(layers)
+             if sp[0] not in ("embed", "head")]
+    # spot check: the first 16 elements of every matrix against the generator
+    from huffman_decode_df11_amd import synth
+    for k, ((g, name, r, c), o) in enumerate(zip(specs, got)):
+        want = synth.normal_bf16_torch(r, c, seed, k + 1, "cuda").view(torch.int16).reshape(-1)[:16]
+        if not torch.equal(o, want):
+            raise SystemExit("offload parity check failed at %s %s" % (g, name))
+
+    def timeit(f, n):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    n = max(2, steps // 5)
+    t_off = timeit(lambda: off.decode_pass(out), n)
+    host = off.host_nbytes()
+    bf16_bytes = 2 * off.n_elements
+    src = torch.empty(bf16_bytes // 2, dtype=torch.int16, pin_memory=True)
+    dst = torch.empty(bf16_bytes // 2, dtype=torch.int16, device="cuda")
+    t_bf16 = timeit(lambda: dst.copy_(src, non_blocking=True), n)
+    res = {
+        "workload": "%d llama3-8b layers (%d elements) compressed in pinned host memory, "
+                    "streamed layer by layer through two device slots" % (layers, off.n_elements),
+        "host_bytes_per_pass": host,
+        "ms_per_pass": round(t_off, 3),
+        "pcie_gbs": round(host / (t_off * 1e-3) / 1e9, 2),
+        "decoded_gbs": round(bf16_bytes / (t_off * 1e-3) / 1e9, 2),
+        "bf16_copy_ms": round(t_bf16, 3),
+        "bf16_copy_gbs": round(bf16_bytes / (t_bf16 * 1e-3) / 1e9, 2),
+        "bytes_saved_vs_bf16": round(1 - host / bf16_bytes, 4),
+    }
+    del off, out, src, dst, groups
+    torch.cuda.empty_cache()
+    return res
+
+
 def fused_up_proj(steps: int, warmup: int, seed: int = 0):
     """df11_decode_gemm on the up_proj weight (14336 x 4096) for B in
     {1, 8, 64, 256}, next to torch.matmul on the decoded BF16 weight."""
@@ -435,6 +492,7 @@ def main():
     del outs
     if not args.no_model:
         result["model_pass"] = model_pass(args.steps, args.warmup, args.seed)
+        result["offload_pass"] = offload_pass(args.steps, args.warmup, args.seed)
     if not args.no_fused:
         result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
     if args.calibrate_copy:

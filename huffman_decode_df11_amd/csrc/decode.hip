@@ -132,15 +132,18 @@ __device__ __forceinline__ SegPlan plan_segment(const SegLoad &cur, uint64_t n, 
     return p;
 }
 
-// the segment's sign+mantissa bytes for the first kPrefetchRounds rounds of groups
+// the segment's sign+mantissa bytes for the first kPrefetchRounds rounds of
+// groups.  Lanes past the last group load the last group again (an address
+// that is always inside the array), so no value has to be selected and the
+// loads stay in flight during the decode.
 __device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm, uint32_t lane,
                                             uint4 (&smp)[kPrefetchRounds])
 {
+    const uint32_t last = p.ngroups ? p.ngroups - 1 : 0u;
+    const uint64_t base = p.ngroups ? p.gbase : 0ull;
 #pragma unroll
-    for (int r = 0; r < kPrefetchRounds; r++) {
-        const uint32_t gi = lane + 64u * r;
-        smp[r] = gi < p.ngroups ? *reinterpret_cast<const uint4 *>(sm + p.gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < kPrefetchRounds; r++)
+        smp[r] = *reinterpret_cast<const uint4 *>(sm + base + 16ull * min(lane + 64u * r, last));
 }
 
 // Locate, scan and emit one segment into the wave's staging (exponent of
@@ -179,33 +182,40 @@ struct RowOut {
     __device__ __forceinline__ bool split8() const { return false; }
 };
 
+// One 16-element group gi of the segment: staged exponents + sign+mantissa
+// bytes smv -> BF16, stored when the group lies inside [lo, hi).
+template <class Out>
+__device__ __forceinline__ void merge_group(const SegPlan &p, uint64_t lo, uint64_t hi, uint32_t gi, uint4 smv,
+                                            const Out &out, uint32_t stg)
+{
+    const uint64_t gs = p.gbase + 16ull * gi;
+    if (gi < p.ngroups && gs >= lo && gs + 16 <= hi) {
+        const uint4 rx = ld128(stg + 16 * gi);
+        const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
+        const uint2 c = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
+        // contiguous, or two 8-element runs of different rows for column groups
+        uint4 *dst0 = reinterpret_cast<uint4 *>(out.at(gs));
+        uint4 *dst1 = out.split8() ? reinterpret_cast<uint4 *>(out.at(gs + 8)) : dst0 + 1;
+        dst0[0] = make_uint4(a.x, a.y, b.x, b.y);
+        dst1[0] = make_uint4(c.x, c.y, d.x, d.y);
+    }
+}
+
 // Merge the staged exponents of elements [lo, hi) (inside the segment) with
 // their sign+mantissa bytes and store BF16: whole 16-element groups with
-// 16-byte accesses, the ragged ends one element per lane (lanes 0..15 the
-// head group, lanes 16..31 the tail group).
+// 16-byte accesses (the first rounds from the prefetched bytes), the ragged
+// ends one element per lane (lanes 0..15 the head group, lanes 16..31 the
+// tail group).
 template <class Out>
 __device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint64_t hi, const uint4 (&smp)[kPrefetchRounds],
                                             const uint8_t *sm, const Out &out, uint32_t stg, uint32_t lane)
 {
-    for (uint32_t r = 0; 64u * r < p.ngroups; r++) {
+#pragma unroll
+    for (int r = 0; r < kPrefetchRounds; r++) merge_group(p, lo, hi, lane + 64u * r, smp[r], out, stg);
+    for (uint32_t r = kPrefetchRounds; 64u * r < p.ngroups; r++) {
         const uint32_t gi = lane + 64u * r;
-        uint4 smv;
-        if (r < kPrefetchRounds) {
-            smv = r == 0 ? smp[0] : r == 1 ? smp[1] : smp[2];
-        } else {
-            smv = gi < p.ngroups ? *reinterpret_cast<const uint4 *>(sm + p.gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
-        }
-        const uint64_t gs = p.gbase + 16ull * gi;
-        if (gi < p.ngroups && gs >= lo && gs + 16 <= hi) {
-            const uint4 rx = ld128(stg + 16 * gi);
-            const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
-            const uint2 c = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
-            // contiguous, or two 8-element runs of different rows for column groups
-            uint4 *dst0 = reinterpret_cast<uint4 *>(out.at(gs));
-            uint4 *dst1 = out.split8() ? reinterpret_cast<uint4 *>(out.at(gs + 8)) : dst0 + 1;
-            dst0[0] = make_uint4(a.x, a.y, b.x, b.y);
-            dst1[0] = make_uint4(c.x, c.y, d.x, d.y);
-        }
+        const uint4 smv = gi < p.ngroups ? *reinterpret_cast<const uint4 *>(sm + p.gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
+        merge_group(p, lo, hi, gi, smv, out, stg);
     }
     const uint64_t hend = min((lo + 15) & ~15ull, hi);
     const uint64_t tstart = max(hi & ~15ull, hend);

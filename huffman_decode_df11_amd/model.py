@@ -97,15 +97,19 @@ def _round8(n: int) -> int:
     return (n + 7) // 8 * 8
 
 
-def synthetic_llama3_8b(seed: int = 0, device="cuda", layers: int = synth.LLAMA3_8B_LAYERS,
-                        threads: int = 0, log=None) -> CompressedModel:
-    """Generate the 8B-parameter model's matrices on `device` (torch Philox,
-    N(0, 0.02) rounded to BF16), encode each group on host threads with the
-    group's own codebook, and keep only the compressed tensors on `device`."""
+def encode_llama3_8b(seed: int = 0, device="cuda", layers: int = synth.LLAMA3_8B_LAYERS, threads: int = 0,
+                     embed_and_head: bool = True, on_group=None):
+    """Generate the model's matrices on `device` (torch Philox, N(0, 0.02)
+    rounded to BF16) and encode each group (a decoder layer, the embedding,
+    the head) on host threads with the group's own codebook.  on_group(g,
+    [(name, Encoded)]) is called as each group is done (in completion
+    order); returns the groups in model order when on_group is None."""
     import torch
     specs = synth.llama3_8b_tensors(layers)
     by_group = {}
     for idx, (g, name, r, c) in enumerate(specs):
+        if not embed_and_head and g in ("embed", "head"):
+            continue
         by_group.setdefault(g, []).append((idx, name, r, c))
     order = list(by_group)
     threads = threads or min(16, os.cpu_count() or 4)
@@ -128,11 +132,28 @@ def synthetic_llama3_8b(seed: int = 0, device="cuda", layers: int = synth.LLAMA3
     with cf.ThreadPoolExecutor(threads) as ex:
         for fut in cf.as_completed([ex.submit(encode_group, g) for g in order]):
             g, encs = fut.result()
-            done[g] = [(name, e.to(device)) for name, e in encs]
-            del encs
-            if log:
-                log("encoded %s (%d/%d groups)" % (g, len(done), len(order)))
-    return CompressedModel([(g, done[g]) for g in order], device=device)
+            if on_group is not None:
+                on_group(g, encs)
+            else:
+                done[g] = encs
+    return None if on_group is not None else [(g, done[g]) for g in order]
+
+
+def synthetic_llama3_8b(seed: int = 0, device="cuda", layers: int = synth.LLAMA3_8B_LAYERS,
+                        threads: int = 0, log=None) -> CompressedModel:
+    """The 8B-parameter model encoded group by group (encode_llama3_8b), with
+    only the compressed tensors kept, on `device`."""
+    order = [g for g, _, _, _ in synth.llama3_8b_tensors(layers)]
+    order = list(dict.fromkeys(order))
+    resident = {}
+
+    def upload(g, encs):
+        resident[g] = [(name, e.to(device)) for name, e in encs]
+        if log:
+            log("encoded %s (%d/%d groups)" % (g, len(resident), len(order)))
+
+    encode_llama3_8b(seed, device, layers, threads, on_group=upload)
+    return CompressedModel([(g, resident[g]) for g in order], device=device)
 
 
 def verify_pass(model: CompressedModel, seed: int, stream=None) -> int:

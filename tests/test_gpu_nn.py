@@ -90,6 +90,7 @@ def test_linear_fused_and_decode_modes(B):
         assert float(np.linalg.norm(y32.cpu().numpy() - r64) / np.linalg.norm(r64)) < 2e-3
 
 
+@torch.no_grad()
 def test_linear_from_torch_and_3d_input():
     lin_t = torch.nn.Linear(512, 96, bias=True).to(torch.bfloat16).cuda()
     lin = dnn.DF11Linear.from_linear(lin_t)
