@@ -297,6 +297,31 @@ def offload_pass(steps: int, warmup: int, seed: int = 0, layers: int = 4):
     return res
 
 
+def encode_rate(seed: int = 0):
+    """Encoding up_proj (14336 x 4096) on the GPU (histogram, codebook on the
+    host, df11_encode_device) next to the host encoder on one thread."""
+    import torch
+    from huffman_decode_df11_amd import api, synth
+    N, K = 14336, 4096
+    w = synth.normal_bf16_torch(N, K, seed, 99, "cuda")
+    api.encode_device(w)      # warm-up (library load, kernels)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 5
+    for _ in range(reps):
+        d = api.encode_device(w)
+    torch.cuda.synchronize()
+    t_dev = (time.perf_counter() - t0) / reps
+    u = w.view(torch.int16).cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    h = api.encode(u)
+    t_host = time.perf_counter() - t0
+    same = all(np.array_equal(h.arrays[k], d.to_host().arrays[k]) for k in ("exp_words", "sm", "gaps", "segs"))
+    return {"workload": "encode up_proj 14336x4096 bf16 N(0,0.02), codebook from its own histogram",
+            "device_ms": round(t_dev * 1e3, 2), "device_bf16_gbs": round(2 * N * K / t_dev / 1e9, 1),
+            "host_one_thread_ms": round(t_host * 1e3, 1), "identical_to_host_encoder": bool(same)}
+
+
 def fused_up_proj(steps: int, warmup: int, seed: int = 0):
     """df11_decode_gemm on the up_proj weight (14336 x 4096) for B in
     {1, 8, 64, 256}, next to torch.matmul on the decoded BF16 weight."""
@@ -493,6 +518,7 @@ def main():
     if not args.no_model:
         result["model_pass"] = model_pass(args.steps, args.warmup, args.seed)
         result["offload_pass"] = offload_pass(args.steps, args.warmup, args.seed)
+        result["encode"] = encode_rate(args.seed)
     if not args.no_fused:
         result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
     if args.calibrate_copy:

@@ -73,8 +73,9 @@ EXPORTS = (
     "df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_free",
     "df11_encoded_view", "df11_gemm_layout", "df11_gemm_tile_rows", "df11_gemm_tile_cols",
     "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_rows", "df11_decode_gemm",
-    "df11_status_string",
-    "df11_last_error", "df11_version",
+    "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
+    "df11_device_encoded_to_host",
+    "df11_status_string", "df11_last_error", "df11_version",
 )
 
 _lib = None
@@ -114,13 +115,21 @@ def lib():
     L.df11_decode_batch.argtypes = [ctypes.POINTER(View), ctypes.POINTER(vp), u32, vp]
     L.df11_decode_rows.argtypes = [ctypes.POINTER(View), vp, u64, vp, vp]
     L.df11_decode_gemm.argtypes = [ctypes.POINTER(View), vp, u32, vp, vp, vp]
+    L.df11_hist_device.argtypes = [vp, u64, vp, vp]
+    L.df11_encode_device.argtypes = [vp, u64, ctypes.POINTER(Codebook), ctypes.POINTER(Layout), vp,
+                                     ctypes.POINTER(vp)]
+    L.df11_device_encoded_free.argtypes = [vp]
+    L.df11_device_encoded_free.restype = None
+    L.df11_device_encoded_view.argtypes = [vp, ctypes.POINTER(View)]
+    L.df11_device_encoded_to_host.argtypes = [vp, ctypes.POINTER(vp)]
     L.df11_status_string.argtypes = [ctypes.c_int]
     L.df11_status_string.restype = ctypes.c_char_p
     L.df11_last_error.restype = ctypes.c_char_p
     L.df11_version.restype = ctypes.c_char_p
     for name in ("df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_view",
                  "df11_gemm_layout", "df11_validate", "df11_decode", "df11_decode_batch",
-                 "df11_decode_rows", "df11_decode_gemm"):
+                 "df11_decode_rows", "df11_decode_gemm", "df11_hist_device", "df11_encode_device",
+                 "df11_device_encoded_view", "df11_device_encoded_to_host"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

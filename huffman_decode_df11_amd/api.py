@@ -92,6 +92,7 @@ class Encoded:
             nbytes = count * ctypes.sizeof(ct)
             if nbytes:
                 buf = (ctypes.c_uint8 * nbytes).from_address(ptr)
+                buf._owner = self   # the arrays keep the library-owned encoding alive
                 self.arrays[name] = np.frombuffer(buf, dtype=np.uint8)
             else:
                 self.arrays[name] = np.zeros(0, np.uint8)
@@ -163,23 +164,102 @@ def encode(bits, codebook: Optional[Codebook] = None, layout: Optional[Layout] =
     return Encoded(h.value, codebook, shape)
 
 
+def hist_device(bits, hist: Optional[np.ndarray] = None, stream=None) -> np.ndarray:
+    """Exponent counts of a device BF16 tensor (computed on the GPU), added
+    into `hist` (new zeros if None)."""
+    if hist is None:
+        hist = np.zeros(256, np.uint64)
+    assert hist.dtype == np.uint64 and hist.size == 256 and hist.flags.c_contiguous
+    t = bits.contiguous()
+    assert t.is_cuda and t.element_size() == 2
+    check(lib().df11_hist_device(t.data_ptr(), t.numel(), hist.ctypes.data, _stream_handle(stream)),
+          "df11_hist_device")
+    return hist
+
+
+class DeviceEncoded:
+    """An encoding made on the GPU (df11_encode_device); every array lives in
+    device memory owned by the library.  Usable wherever a DF11Tensor is
+    (decode, decode_rows, decode_gemm)."""
+
+    def __init__(self, handle: int, codebook: Codebook, shape: tuple, device):
+        self._handle = ctypes.c_void_p(handle)
+        self.codebook = codebook
+        self.shape = shape
+        self.device = device
+        self.view = View()
+        check(lib().df11_device_encoded_view(self._handle, ctypes.byref(self.view)), "df11_device_encoded_view")
+        self.host_view = self.view      # only its scalar fields are read on the host
+        # decode through the codebook's shared device tables (the library's
+        # own copy stays allocated), so that tensors of one codebook can be
+        # decoded in one batched launch
+        shared = _codebook_tables(codebook, device)
+        self.view.chain = shared["chain"].data_ptr()
+        self.view.fast = shared["fast"].data_ptr()
+        self._tables = shared
+        self.n = int(self.view.n)
+        self.total_bits = int(self.view.total_bits)
+        self.n_segments = int(self.view.n_segments)
+
+    def compressed_nbytes(self) -> int:
+        return sum(int(getattr(self.view, "n_" + name)) * ctypes.sizeof(ct)
+                   for name, ct in _lib.VIEW_ARRAYS if name != "block_seg")
+
+    def to_host(self) -> Encoded:
+        h = ctypes.c_void_p()
+        check(lib().df11_device_encoded_to_host(self._handle, ctypes.byref(h)), "df11_device_encoded_to_host")
+        return Encoded(h.value, self.codebook, self.shape)
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h is not None and h.value:
+            try:
+                lib().df11_device_encoded_free(h)
+            except Exception:   # interpreter shutdown: the module may be gone
+                pass
+            self._handle = None
+
+
+def encode_device(bits, codebook: Optional[Codebook] = None, layout: Optional[Layout] = None,
+                  max_len: int = DEFAULT_MAX_LEN, fast_bits: int = DEFAULT_FAST_BITS, stream=None) -> DeviceEncoded:
+    """Encode a device BF16 tensor on the GPU.  Without a codebook one is
+    built (on the host, 256 symbols) from the tensor's device histogram."""
+    t = bits.contiguous()
+    assert t.is_cuda and t.element_size() == 2
+    if codebook is None:
+        codebook = build_codebook(hist_device(t, stream=stream), max_len, fast_bits)
+    h = ctypes.c_void_p()
+    lay = ctypes.byref(layout) if layout is not None else None
+    check(lib().df11_encode_device(t.data_ptr(), t.numel(), ctypes.byref(codebook), lay, _stream_handle(stream),
+                                   ctypes.byref(h)), "df11_encode_device")
+    return DeviceEncoded(h.value, codebook, tuple(t.shape), t.device)
+
+
 _TABLE_ARRAYS = ("chain", "fast")
 
 
-def _device_tables(enc: Encoded, device):
-    """The codebook's tables on `device`, uploaded once per codebook and
-    device, so that tensors sharing a codebook share device tables (which a
-    batched decode requires)."""
+def _codebook_tables(cb: Codebook, device):
+    """The codebook's chain and fast tables on `device`, uploaded once per
+    codebook and device (the same cache the host encodings use)."""
     import torch
-    cb = enc.codebook
     cache = getattr(cb, "_device_tables", None)
     if cache is None:
         cache = {}
         cb._device_tables = cache
     key = str(torch.device(device))
     if key not in cache:
-        cache[key] = {name: torch.from_numpy(enc.arrays[name].copy()).to(device) for name in _TABLE_ARRAYS}
+        chain = np.ctypeslib.as_array(cb.chain)[:cb.n_tables * 256].astype(np.uint16).view(np.uint8)
+        fast = np.ctypeslib.as_array(cb.fast)[:2 << cb.fast_bits].astype(np.uint32).view(np.uint8)
+        cache[key] = {"chain": torch.from_numpy(chain.copy()).to(device),
+                      "fast": torch.from_numpy(fast.copy()).to(device)}
     return cache[key]
+
+
+def _device_tables(enc: Encoded, device):
+    """The codebook's tables on `device`, uploaded once per codebook and
+    device, so that tensors sharing a codebook share device tables (which a
+    batched decode requires)."""
+    return _codebook_tables(enc.codebook, device)
 
 
 class DF11Tensor:

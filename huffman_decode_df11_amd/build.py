@@ -18,7 +18,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["decode.hip", "decode_gemm.hip"]
+HIP_SOURCES = ["decode.hip", "decode_gemm.hip", "encode.hip"]
 CPP_SOURCES = ["host_codebook.cpp", "host_encode.cpp", "host_validate.cpp"]
 
 # Packed FP32 instructions are kept out of every HIP object.

@@ -16,6 +16,11 @@ void canonical_codes(const uint8_t *len, uint32_t *code);
 uint16_t chain_walk(const uint16_t *chain, uint32_t window);
 int build_tables(df11_codebook *cb);
 
+// Layout checks shared by the host and device encoders: defaults filled in
+// (chunk_bytes 16, seg_lanes 64), then the layout checked against n.
+df11_layout complete_layout(const df11_layout *in);
+int check_layout(const df11_layout &L, uint64_t n);
+
 }  // namespace df11
 
 struct df11_encoded {

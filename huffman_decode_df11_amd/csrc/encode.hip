@@ -1,0 +1,482 @@
+// The DFloat11 encoder on the GPU: exponent histogram, code placement and
+// segment metadata for a BF16 tensor already in device memory.  It writes
+// the same bytes as df11_encode on the host for the same codebook and
+// layout.
+//
+// [P1] "DFloat11无损压缩技术：基于哈夫曼编码的BFloat16大模型显存优化方案" 2.2
+//      items 1-2: count exponent frequencies, build the Huffman code, store
+//      the coded exponents and the verbatim sign+mantissa bytes.
+// [P3] "DFloat11重新定义LLM无损压缩的技术边界" 4.1: the offline compression of
+//      a large model takes hours on the CPU; here every step but the
+//      256-symbol code construction runs on the device.
+//
+// Steps: (1) hist_kernel counts exponents (LDS sub-histograms per wave);
+// the host builds the codebook from the counts.  (2) bits_kernel sums the
+// code lengths of fixed blocks of E elements in stream order.  (3) The host
+// turns the block sums into block start bits (adding the padding that
+// starts an aligned block on a segment boundary), which fixes the stream
+// length, the segment count and every output size.  (4) emit_kernel: per
+// block, a workgroup scan of the code lengths gives each element's first
+// bit; the code is OR-ed into the zeroed stream words with 32-bit atomics
+// (a code touches at most two words, shared with neighbours), the
+// sign+mantissa byte is stored, and the elements at segment and chunk
+// boundaries write the gaps and segment records.  (5) seg_max_kernel finds
+// the largest segment.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "df11_internal.h"
+
+struct df11_device_encoded {
+    uint64_t n = 0, total_bits = 0, n_segments = 0;
+    df11_layout layout{};
+    uint32_t min_len = 0, max_len = 0, n_tables = 0, fast_bits = 0, max_seg_elems = 0;
+    uint32_t *exp_words = nullptr;
+    uint8_t *sm = nullptr;
+    uint8_t *gaps = nullptr;
+    df11_segment *segs = nullptr;
+    uint16_t *chain = nullptr;
+    uint32_t *fast = nullptr;
+    uint64_t *block_seg = nullptr;
+    uint64_t n_exp_words = 0, n_sm = 0, n_gaps = 0, n_segs = 0, n_chain = 0, n_fast = 0, n_block_seg = 0;
+};
+
+namespace {
+
+constexpr uint32_t kThreads = 256;
+constexpr uint32_t kMaxBlock = 4096;   // elements per scan block
+
+// Stream position g -> index of the source element (row-major, tile order,
+// column groups inside tiles), as the layout defines it.
+struct DevOrder {
+    uint64_t cols, tr, tc, kc, tile, tiles_per_row;
+    __device__ __forceinline__ uint64_t operator()(uint64_t g) const
+    {
+        if (!tr) return g;
+        const uint64_t t = g / tile, w = g - t * tile;
+        uint64_t r, c;
+        if (kc) {
+            const uint64_t grp = w / (tr * kc), in = w - grp * (tr * kc);
+            r = in / kc;
+            c = grp * kc + (in - r * kc);
+        } else {
+            r = w / tc;
+            c = w - r * tc;
+        }
+        const uint64_t rb = t / tiles_per_row, cb = t - rb * tiles_per_row;
+        return (rb * tr + r) * cols + cb * tc + c;
+    }
+};
+
+DevOrder make_order(const df11_layout &L)
+{
+    DevOrder o{};
+    if (L.tile_rows) {
+        o.cols = L.cols;
+        o.tr = L.tile_rows;
+        o.tc = L.tile_cols;
+        o.kc = L.tile_kchunk;
+        o.tile = o.tr * o.tc;
+        o.tiles_per_row = L.cols / L.tile_cols;
+    }
+    return o;
+}
+
+struct CodeTable {
+    uint8_t len[256];
+    uint32_t code[256];
+};
+
+__global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *bits, uint64_t n, unsigned long long *hist)
+{
+    __shared__ uint32_t h[kThreads / 64][256];
+    const uint32_t wave = threadIdx.x >> 6;
+    for (uint32_t i = threadIdx.x; i < 256 * (kThreads / 64); i += kThreads) h[i / 256][i % 256] = 0;
+    __syncthreads();
+    for (uint64_t i = blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n; i += (uint64_t)gridDim.x * kThreads)
+        atomicAdd(&h[wave][(bits[i] >> 7) & 0xFF], 1u);
+    __syncthreads();
+    for (uint32_t e = threadIdx.x; e < 256; e += kThreads) {
+        uint64_t c = 0;
+        for (uint32_t w = 0; w < kThreads / 64; w++) c += h[w][e];
+        if (c) atomicAdd(&hist[e], (unsigned long long)c);
+    }
+}
+
+// Sum of the code lengths of each block of E elements (stream order); an
+// exponent without a code sets *uncoded.
+__global__ void __launch_bounds__(kThreads) bits_kernel(const uint16_t *bits, uint64_t n, uint32_t E, DevOrder order,
+                                                        CodeTable ct, uint32_t *block_bits, uint32_t *uncoded)
+{
+    __shared__ uint8_t len[256];
+    __shared__ uint32_t part[kThreads / 64];
+    for (uint32_t i = threadIdx.x; i < 256; i += kThreads) len[i] = ct.len[i];
+    __syncthreads();
+    const uint64_t g0 = (uint64_t)blockIdx.x * E;
+    uint32_t sum = 0, bad = 0;
+    for (uint32_t i = threadIdx.x; i < E && g0 + i < n; i += kThreads) {
+        const uint32_t L = len[(bits[order(g0 + i)] >> 7) & 0xFF];
+        bad |= L == 0;
+        sum += L;
+    }
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
+    if (bad) atomicOr(uncoded, 1u);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (uint32_t w = 0; w < kThreads / 64; w++) t += part[w];
+        block_bits[blockIdx.x] = t;
+    }
+}
+
+struct EmitArgs {
+    const uint16_t *bits;
+    uint64_t n, nseg, seg_bits, chunk_bits;
+    uint32_t E;
+    DevOrder order;
+    const uint64_t *base;   // [nblocks + 1]: first bit of each block; base[nblocks] = ~0
+    const uint64_t *end;    // [nblocks]: bit after each block's last code
+    uint32_t *words;
+    uint8_t *sm;
+    uint8_t *gaps;
+    df11_segment *segs;
+};
+
+__global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct)
+{
+    __shared__ uint8_t len[256];
+    __shared__ uint32_t code[256];
+    __shared__ uint32_t scan[kThreads];
+    for (uint32_t i = threadIdx.x; i < 256; i += kThreads) {
+        len[i] = ct.len[i];
+        code[i] = ct.code[i];
+    }
+    const uint64_t b = blockIdx.x;
+    const uint64_t g0 = b * a.E;
+    const uint32_t cnt = (uint32_t)min<uint64_t>(a.E, a.n - g0);
+    const uint32_t per = (cnt + kThreads - 1) / kThreads;       // consecutive elements per thread
+    const uint32_t i0 = min(cnt, threadIdx.x * per), i1 = min(cnt, i0 + per);
+    __syncthreads();
+    uint32_t mine = 0;
+    for (uint32_t i = i0; i < i1; i++) mine += len[(a.bits[a.order(g0 + i)] >> 7) & 0xFF];
+    scan[threadIdx.x] = mine;
+    __syncthreads();
+    for (uint32_t off = 1; off < kThreads; off <<= 1) {   // inclusive Hillis-Steele scan
+        const uint32_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0u;
+        __syncthreads();
+        scan[threadIdx.x] += v;
+        __syncthreads();
+    }
+    uint64_t pos = a.base[b] + (scan[threadIdx.x] - mine);
+    // start of the element before i0
+    uint64_t prev;
+    bool has_prev = g0 + i0 > 0;
+    if (!has_prev) {
+        prev = 0;
+    } else {
+        const uint32_t lp = len[(a.bits[a.order(g0 + i0 - 1)] >> 7) & 0xFF];
+        prev = (i0 == 0 ? a.end[b - 1] : pos) - lp;
+    }
+    const uint64_t SB = a.seg_bits, CB = a.chunk_bits;
+    for (uint32_t i = i0; i < i1; i++) {
+        const uint64_t g = g0 + i;
+        const uint16_t u = a.bits[a.order(g)];
+        const uint32_t e = (u >> 7) & 0xFF;
+        const uint32_t L = len[e];
+        // the code, first bit at bit (31 - pos % 32) of word pos / 32
+        const uint64_t w = pos >> 5, off = pos & 31;
+        const uint64_t wide = (uint64_t)code[e] << (64 - off - L);
+        const uint32_t hi = (uint32_t)(wide >> 32), lo = (uint32_t)wide;
+        if (hi) atomicOr(&a.words[w], hi);
+        if (lo) atomicOr(&a.words[w + 1], lo);
+        a.sm[g] = (uint8_t)(((u >> 8) & 0x80) | (u & 0x7F));
+        const uint64_t s = pos / SB;
+        // gap of the chunk holding this code's first bit, when no earlier code starts in it
+        const uint64_t c0 = pos - pos % CB;
+        if (!has_prev || prev < c0) a.gaps[c0 / CB] = (uint8_t)(pos - c0);
+        // this element opens segments (previous segment, s]
+        const uint64_t sp = has_prev ? prev / SB : ~0ull;
+        for (uint64_t t = sp + 1; t <= s; t++) a.segs[t].elem_off = g;
+        // last code of its segment: segment length in bits and the gap of a chunk it runs into
+        const uint64_t vend = pos + L;
+        const uint64_t next = i + 1 < cnt ? vend : a.base[b + 1];
+        if (next == ~0ull || next / SB > s) {
+            a.segs[s].nbits = (uint32_t)min<uint64_t>(SB, vend - s * SB);
+            const uint64_t c1 = c0 + CB;
+            if (c1 < vend && c1 < (s + 1) * SB) a.gaps[c1 / CB] = (uint8_t)(vend - c1);
+        }
+        if (g + 1 == a.n)   // trailing segments without a code start, and the closing record
+            for (uint64_t t = s + 1; t <= a.nseg; t++) a.segs[t].elem_off = a.n;
+        prev = pos;
+        has_prev = true;
+        pos = vend;
+    }
+}
+
+__global__ void seg_max_kernel(const df11_segment *segs, uint64_t nseg, uint32_t *out)
+{
+    uint32_t m = 0;
+    for (uint64_t s = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; s < nseg; s += (uint64_t)gridDim.x * blockDim.x)
+        m = max(m, (uint32_t)(segs[s + 1].elem_off - segs[s].elem_off));
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return df11::fail(e == hipErrorOutOfMemory ? DF11_E_ALLOC : DF11_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call, what)                          \
+    do {                                             \
+        hipError_t e_ = (call);                      \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+uint32_t grid_for(uint64_t items, uint32_t per_group)
+{
+    return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((items + per_group - 1) / per_group, 65535ull * 16));
+}
+
+void free_device(df11_device_encoded *d)
+{
+    if (!d) return;
+    void *ps[] = {d->exp_words, d->sm, d->gaps, d->segs, d->chain, d->fast, d->block_seg};
+    for (void *p : ps)
+        if (p) (void)hipFree(p);
+    delete d;
+}
+
+// Device scratch freed on every return path.
+struct Scratch {
+    std::vector<void *> ptrs;
+    ~Scratch()
+    {
+        for (void *p : ptrs) (void)hipFree(p);
+    }
+    template <class T>
+    hipError_t alloc(T **p, uint64_t count)
+    {
+        *p = nullptr;
+        hipError_t e = hipMalloc((void **)p, std::max<uint64_t>(count, 1) * sizeof(T));
+        if (e == hipSuccess) ptrs.push_back(*p);
+        return e;
+    }
+};
+
+}  // namespace
+
+extern "C" int df11_hist_device(const uint16_t *bits, uint64_t n, uint64_t hist[256], void *stream)
+{
+    if (!hist || (n && !bits)) return df11::fail(DF11_E_ARG, "df11_hist_device: null pointer");
+    if (!n) return DF11_OK;
+    hipStream_t st = (hipStream_t)stream;
+    Scratch s;
+    unsigned long long *dh;
+    HIP_TRY(s.alloc(&dh, 256), "hist buffer");
+    HIP_TRY(hipMemsetAsync(dh, 0, 256 * sizeof(unsigned long long), st), "hist clear");
+    hipLaunchKernelGGL(hist_kernel, dim3(grid_for(n, kThreads * 64)), dim3(kThreads), 0, st, bits, n, dh);
+    HIP_TRY(hipGetLastError(), "hist launch");
+    unsigned long long h[256];
+    HIP_TRY(hipMemcpyAsync(h, dh, sizeof h, hipMemcpyDeviceToHost, st), "hist copy");
+    HIP_TRY(hipStreamSynchronize(st), "hist sync");
+    for (int i = 0; i < 256; i++) hist[i] += h[i];
+    return DF11_OK;
+}
+
+extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_codebook *cb,
+                                  const df11_layout *layout_in, void *stream, df11_device_encoded **out)
+{
+    if (!out || !cb || (n && !bits)) return df11::fail(DF11_E_ARG, "df11_encode_device: null pointer");
+    *out = nullptr;
+    const df11_layout L = df11::complete_layout(layout_in);
+    int rc = df11::check_layout(L, n);
+    if (rc) return rc;
+    if (cb->fast_bits < DF11_FAST_BITS_MIN || cb->fast_bits > DF11_FAST_BITS_MAX || cb->n_tables < 1 ||
+        cb->n_tables > DF11_MAX_TABLES || cb->max_len > DF11_MAX_LEN)
+        return df11::fail(DF11_E_ARG, "codebook not built by df11_codebook_build");
+    hipStream_t st = (hipStream_t)stream;
+    const uint64_t chunk_bits = 8ull * L.chunk_bytes, seg_bits = chunk_bits * L.seg_lanes, seg_words = seg_bits / 32;
+    // scan blocks nest in aligned blocks, so padding only falls between scan blocks
+    const uint32_t E = L.align_elems ? (uint32_t)std::gcd<uint64_t>(L.align_elems, kMaxBlock) : kMaxBlock;
+    const uint64_t nb = (n + E - 1) / E;
+    const DevOrder order = make_order(L);
+    CodeTable ct;
+    for (int i = 0; i < 256; i++) {
+        ct.len[i] = (uint8_t)cb->len[i];
+        ct.code[i] = cb->code[i];
+    }
+
+    Scratch s;
+    std::vector<uint64_t> base(nb + 1), end(nb);
+    uint64_t total = 0;
+    if (n) {
+        uint32_t *dbits, *dflag;
+        HIP_TRY(s.alloc(&dbits, nb), "block sums");
+        HIP_TRY(s.alloc(&dflag, 1), "flag");
+        HIP_TRY(hipMemsetAsync(dflag, 0, sizeof(uint32_t), st), "flag clear");
+        hipLaunchKernelGGL(bits_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, st, bits, n, E, order, ct, dbits, dflag);
+        HIP_TRY(hipGetLastError(), "block sum launch");
+        std::vector<uint32_t> bb(nb);
+        uint32_t flag = 0;
+        HIP_TRY(hipMemcpyAsync(bb.data(), dbits, nb * sizeof(uint32_t), hipMemcpyDeviceToHost, st), "block sum copy");
+        HIP_TRY(hipMemcpyAsync(&flag, dflag, sizeof flag, hipMemcpyDeviceToHost, st), "flag copy");
+        HIP_TRY(hipStreamSynchronize(st), "block sum sync");
+        if (flag) return df11::fail(DF11_E_UNCODED, "an exponent of the tensor has no code");
+        for (uint64_t b = 0; b < nb; b++) {
+            const uint64_t g = b * E;
+            if (L.align_elems && g && g % L.align_elems == 0) total = (total + seg_bits - 1) / seg_bits * seg_bits;
+            base[b] = total;
+            total += bb[b];
+            end[b] = total;
+        }
+    }
+    base[nb] = ~0ull;
+    const uint64_t nseg = (total + seg_bits - 1) / seg_bits;
+
+    df11_device_encoded *d = new (std::nothrow) df11_device_encoded();
+    if (!d) return df11::fail(DF11_E_ALLOC, "out of host memory");
+    struct Guard {
+        df11_device_encoded *&d;
+        ~Guard() { free_device(d); }
+    } guard{d};
+    d->n = n;
+    d->total_bits = total;
+    d->n_segments = nseg;
+    d->layout = L;
+    d->min_len = cb->min_len;
+    d->max_len = cb->max_len;
+    d->n_tables = cb->n_tables;
+    d->fast_bits = cb->fast_bits;
+    d->n_exp_words = nseg * seg_words + 2;
+    d->n_sm = (n + 15) / 16 * 16;
+    d->n_gaps = nseg * L.seg_lanes;
+    d->n_segs = nseg + 1;
+    d->n_chain = (uint64_t)cb->n_tables * 256;
+    d->n_fast = 2ull << cb->fast_bits;
+    d->n_block_seg = L.align_elems ? (n + L.align_elems - 1) / L.align_elems + 1 : 0;
+    HIP_TRY(hipMalloc((void **)&d->exp_words, d->n_exp_words * 4), "stream words");
+    HIP_TRY(hipMalloc((void **)&d->sm, std::max<uint64_t>(d->n_sm, 16)), "sign+mantissa");
+    HIP_TRY(hipMalloc((void **)&d->gaps, std::max<uint64_t>(d->n_gaps, 16)), "gaps");
+    HIP_TRY(hipMalloc((void **)&d->segs, d->n_segs * sizeof(df11_segment)), "segment records");
+    HIP_TRY(hipMalloc((void **)&d->chain, d->n_chain * 2), "tables");
+    HIP_TRY(hipMalloc((void **)&d->fast, d->n_fast * 4), "tables");
+    if (d->n_block_seg) HIP_TRY(hipMalloc((void **)&d->block_seg, d->n_block_seg * 8), "block index");
+    HIP_TRY(hipMemsetAsync(d->exp_words, 0, d->n_exp_words * 4, st), "clear");
+    HIP_TRY(hipMemsetAsync(d->sm, 0, std::max<uint64_t>(d->n_sm, 16), st), "clear");
+    HIP_TRY(hipMemsetAsync(d->gaps, 0, std::max<uint64_t>(d->n_gaps, 16), st), "clear");
+    HIP_TRY(hipMemsetAsync(d->segs, 0, d->n_segs * sizeof(df11_segment), st), "clear");
+    HIP_TRY(hipMemcpyAsync(d->chain, cb->chain, d->n_chain * 2, hipMemcpyHostToDevice, st), "tables");
+    HIP_TRY(hipMemcpyAsync(d->fast, cb->fast, d->n_fast * 4, hipMemcpyHostToDevice, st), "tables");
+    std::vector<uint64_t> bseg(d->n_block_seg);
+    for (uint64_t a = 0; a + 1 < d->n_block_seg; a++) bseg[a] = base[a * L.align_elems / E] / seg_bits;
+    if (d->n_block_seg) {
+        bseg[d->n_block_seg - 1] = nseg;
+        HIP_TRY(hipMemcpyAsync(d->block_seg, bseg.data(), d->n_block_seg * 8, hipMemcpyHostToDevice, st), "block index");
+    }
+    if (n) {
+        uint64_t *dbase, *dend;
+        uint32_t *dmax;
+        HIP_TRY(s.alloc(&dbase, nb + 1), "block starts");
+        HIP_TRY(s.alloc(&dend, nb), "block ends");
+        HIP_TRY(s.alloc(&dmax, 1), "max");
+        HIP_TRY(hipMemcpyAsync(dbase, base.data(), (nb + 1) * 8, hipMemcpyHostToDevice, st), "block starts");
+        HIP_TRY(hipMemcpyAsync(dend, end.data(), nb * 8, hipMemcpyHostToDevice, st), "block ends");
+        HIP_TRY(hipMemsetAsync(dmax, 0, 4, st), "clear");
+        EmitArgs a{bits, n, nseg, seg_bits, chunk_bits, E, order, dbase, dend, d->exp_words, d->sm, d->gaps, d->segs};
+        hipLaunchKernelGGL(emit_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, st, a, ct);
+        HIP_TRY(hipGetLastError(), "emit launch");
+        hipLaunchKernelGGL(seg_max_kernel, dim3(grid_for(nseg, 256)), dim3(256), 0, st, d->segs, nseg, dmax);
+        HIP_TRY(hipGetLastError(), "segment max launch");
+        HIP_TRY(hipMemcpyAsync(&d->max_seg_elems, dmax, 4, hipMemcpyDeviceToHost, st), "max copy");
+        HIP_TRY(hipStreamSynchronize(st), "encode sync");
+    } else {
+        HIP_TRY(hipStreamSynchronize(st), "encode sync");
+    }
+    *out = d;
+    d = nullptr;   // ownership passes to the caller
+    return DF11_OK;
+}
+
+extern "C" void df11_device_encoded_free(df11_device_encoded *enc) { free_device(enc); }
+
+extern "C" int df11_device_encoded_view(const df11_device_encoded *d, df11_view *v)
+{
+    if (!d || !v) return df11::fail(DF11_E_ARG, "df11_device_encoded_view: null pointer");
+    std::memset(v, 0, sizeof(*v));
+    v->n = d->n;
+    v->total_bits = d->total_bits;
+    v->n_segments = d->n_segments;
+    v->chunk_bytes = d->layout.chunk_bytes;
+    v->seg_lanes = d->layout.seg_lanes;
+    v->rows = d->layout.rows;
+    v->cols = d->layout.cols;
+    v->tile_rows = d->layout.tile_rows;
+    v->tile_cols = d->layout.tile_cols;
+    v->tile_kchunk = d->layout.tile_kchunk;
+    v->align_elems = d->layout.align_elems;
+    v->min_len = d->min_len;
+    v->max_len = d->max_len;
+    v->n_tables = d->n_tables;
+    v->fast_bits = d->fast_bits;
+    v->max_seg_elems = d->max_seg_elems;
+    v->exp_words = d->exp_words;  v->n_exp_words = d->n_exp_words;
+    v->sm = d->sm;                v->n_sm = d->n_sm;
+    v->gaps = d->gaps;            v->n_gaps = d->n_gaps;
+    v->segs = d->segs;            v->n_segs = d->n_segs;
+    v->chain = d->chain;          v->n_chain = d->n_chain;
+    v->fast = d->fast;            v->n_fast = d->n_fast;
+    v->block_seg = d->block_seg;  v->n_block_seg = d->n_block_seg;
+    return DF11_OK;
+}
+
+extern "C" int df11_device_encoded_to_host(const df11_device_encoded *d, df11_encoded **out)
+{
+    if (!d || !out) return df11::fail(DF11_E_ARG, "df11_device_encoded_to_host: null pointer");
+    *out = nullptr;
+    df11_encoded *h = new (std::nothrow) df11_encoded();
+    if (!h) return df11::fail(DF11_E_ALLOC, "out of host memory");
+    try {
+        h->exp_words.resize(d->n_exp_words);
+        h->sm.resize(d->n_sm);
+        h->gaps.resize(d->n_gaps);
+        h->segs.resize(d->n_segs);
+        h->chain.resize(d->n_chain);
+        h->fast.resize(d->n_fast);
+        h->block_seg.resize(d->n_block_seg);
+    } catch (...) {
+        delete h;
+        return df11::fail(DF11_E_ALLOC, "out of host memory");
+    }
+    h->n = d->n;
+    h->total_bits = d->total_bits;
+    h->n_segments = d->n_segments;
+    h->layout = d->layout;
+    h->min_len = d->min_len;
+    h->max_len = d->max_len;
+    h->n_tables = d->n_tables;
+    h->fast_bits = d->fast_bits;
+    h->max_seg_elems = d->max_seg_elems;
+    struct { void *dst; const void *src; uint64_t bytes; } parts[] = {
+        {h->exp_words.data(), d->exp_words, d->n_exp_words * 4}, {h->sm.data(), d->sm, d->n_sm},
+        {h->gaps.data(), d->gaps, d->n_gaps}, {h->segs.data(), d->segs, d->n_segs * sizeof(df11_segment)},
+        {h->chain.data(), d->chain, d->n_chain * 2}, {h->fast.data(), d->fast, d->n_fast * 4},
+        {h->block_seg.data(), d->block_seg, d->n_block_seg * 8}};
+    for (auto &p : parts) {
+        if (!p.bytes) continue;
+        hipError_t e = hipMemcpy(p.dst, p.src, p.bytes, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) {
+            delete h;
+            return hip_fail(e, "device to host copy");
+        }
+    }
+    *out = h;
+    return DF11_OK;
+}
+

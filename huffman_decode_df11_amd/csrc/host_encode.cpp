@@ -60,7 +60,7 @@ extern "C" int df11_gemm_layout(uint64_t rows, uint64_t cols, df11_layout *layou
     return DF11_OK;
 }
 
-namespace {
+namespace df11 {
 
 int check_layout(const df11_layout &L, uint64_t n)
 {
@@ -88,6 +88,19 @@ int check_layout(const df11_layout &L, uint64_t n)
     if (L.tile_kchunk && !L.tile_rows) return fail(DF11_E_ARG, "tile_kchunk needs tile order");
     return DF11_OK;
 }
+
+df11_layout complete_layout(const df11_layout *in)
+{
+    df11_layout L{};
+    if (in) L = *in;
+    if (!L.chunk_bytes) L.chunk_bytes = 16;
+    if (!L.seg_lanes) L.seg_lanes = DF11_SEG_LANES;
+    return L;
+}
+
+}  // namespace df11
+
+namespace {
 
 // Row-major index of stream element g.
 struct Order {
@@ -127,10 +140,7 @@ extern "C" int df11_encode(const uint16_t *bits, uint64_t n, const df11_codebook
 {
     if (!out || !cb || (n && !bits)) return fail(DF11_E_ARG, "df11_encode: null pointer");
     *out = nullptr;
-    df11_layout L{};
-    if (layout_in) L = *layout_in;
-    if (!L.chunk_bytes) L.chunk_bytes = 16;
-    if (!L.seg_lanes) L.seg_lanes = DF11_SEG_LANES;
+    const df11_layout L = complete_layout(layout_in);
     int rc = check_layout(L, n);
     if (rc) return rc;
     if (cb->fast_bits < DF11_FAST_BITS_MIN || cb->fast_bits > DF11_FAST_BITS_MAX || cb->n_tables < 1 ||

@@ -140,11 +140,15 @@ def encode_llama3_8b(seed: int = 0, device="cuda", layers: int = synth.LLAMA3_8B
 
 
 def synthetic_llama3_8b(seed: int = 0, device="cuda", layers: int = synth.LLAMA3_8B_LAYERS,
-                        threads: int = 0, log=None) -> CompressedModel:
-    """The 8B-parameter model encoded group by group (encode_llama3_8b), with
-    only the compressed tensors kept, on `device`."""
+                        threads: int = 0, log=None, encoder: str = "device") -> CompressedModel:
+    """The 8B-parameter model, only the compressed tensors kept on `device`.
+    encoder "device": each group generated, counted and encoded on the GPU
+    (df11_hist_device, df11_encode_device; the 256-symbol codebook is built
+    on the host); "host": encode_llama3_8b on host threads."""
     order = [g for g, _, _, _ in synth.llama3_8b_tensors(layers)]
     order = list(dict.fromkeys(order))
+    if encoder == "device":
+        return CompressedModel(_encode_on_device(seed, device, layers, log), device=device)
     resident = {}
 
     def upload(g, encs):
@@ -154,6 +158,27 @@ def synthetic_llama3_8b(seed: int = 0, device="cuda", layers: int = synth.LLAMA3
 
     encode_llama3_8b(seed, device, layers, threads, on_group=upload)
     return CompressedModel([(g, resident[g]) for g in order], device=device)
+
+
+def _encode_on_device(seed: int, device, layers: int, log=None):
+    specs = synth.llama3_8b_tensors(layers)
+    by_group = {}
+    for idx, (g, name, r, c) in enumerate(specs):
+        by_group.setdefault(g, []).append((idx, name, r, c))
+    groups = []
+    for g, mats in by_group.items():
+        hist = None
+        for idx, name, r, c in mats:
+            hist = api.hist_device(synth.normal_bf16_torch(r, c, seed, idx, device), hist)
+        cb = api.build_codebook(hist)
+        encs = []
+        for idx, name, r, c in mats:
+            # generated again rather than kept: one matrix at a time in device memory
+            encs.append((name, api.encode_device(synth.normal_bf16_torch(r, c, seed, idx, device), codebook=cb)))
+        groups.append((g, encs))
+        if log:
+            log("encoded %s on the device (%d/%d groups)" % (g, len(groups), len(by_group)))
+    return groups
 
 
 def verify_pass(model: CompressedModel, seed: int, stream=None) -> int:

@@ -200,6 +200,38 @@ uint32_t df11_gemm_tile_cols(void);
  * check streams. */
 int df11_validate(const df11_view *host_view, const df11_codebook *cb);
 
+/* ---------------------------------------------------------- device encoder */
+
+/* A tensor encoded on the GPU: every array in device memory owned by the
+ * library (including a copy of the codebook's tables). */
+typedef struct df11_device_encoded df11_device_encoded;
+
+/* Exponent histogram of n BF16 words in device memory, added into hist
+ * (host) ([P1] 2.2 item 1).  Synchronises `stream`.  Errors: E_ARG (null),
+ * E_DEVICE. */
+int df11_hist_device(const uint16_t *device_bits, uint64_t n, uint64_t hist[256], void *stream);
+
+/* Encode n BF16 words in device memory on the GPU ([P1] 2.2 items 1-2;
+ * [P3] 4.1 on the cost of offline compression): the same stream, sign and
+ * mantissa bytes, gaps, segment records and block index, byte for byte, as
+ * df11_encode with the same codebook and layout.  The library allocates the
+ * device arrays; free them with df11_device_encoded_free.  Synchronises
+ * `stream` (twice: the stream length decides the output sizes).  Errors:
+ * E_ARG (null, layout), E_UNCODED (an exponent without a code), E_ALLOC,
+ * E_DEVICE. */
+int df11_encode_device(const uint16_t *device_bits, uint64_t n, const df11_codebook *cb,
+                       const df11_layout *layout, void *stream, df11_device_encoded **out);
+void df11_device_encoded_free(df11_device_encoded *enc);
+
+/* Fill *v with the device pointers of enc (valid until
+ * df11_device_encoded_free): a device view for df11_decode and friends. */
+int df11_device_encoded_view(const df11_device_encoded *enc, df11_view *v);
+
+/* Copy a device encoding into a new host encoding (free with
+ * df11_encoded_free), e.g. to store it or to check it with df11_validate.
+ * Errors: E_ARG, E_ALLOC, E_DEVICE. */
+int df11_device_encoded_to_host(const df11_device_encoded *enc, df11_encoded **out);
+
 /* -------------------------------------------------------------- device side */
 
 /* Decode a device view into out[0..n) BF16 bits in row-major order

@@ -24,11 +24,13 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def test_model_pass_two_layers_full_shapes():
-    """Embedding, two full-size decoder layers and the head: every matrix of
-    the pass decoded into the reused buffer and compared in full."""
-    _say("case model pass 2 layers")
-    m = model.synthetic_llama3_8b(seed=3, device="cuda", layers=2, threads=4)
+@pytest.mark.parametrize("encoder", ["device", "host"])
+def test_model_pass_two_layers_full_shapes(encoder):
+    """Embedding, two full-size decoder layers and the head, encoded on the
+    GPU or on host threads: every matrix of the pass decoded into the reused
+    buffer and compared in full."""
+    _say("case model pass 2 layers, %s encoder" % encoder)
+    m = model.synthetic_llama3_8b(seed=3, device="cuda", layers=2, threads=4, encoder=encoder)
     assert len(m.matrices) == 2 * 7 + 2
     assert m.n_elements == 2 * 218103808 + 2 * 128256 * 4096
     assert model.verify_pass(m, seed=3) == m.n_elements

@@ -267,3 +267,15 @@ def test_validator_catches_corruption(what):
         elif what == "n_segments":
             e.view.n_segments -= 1
     _corrupt_and_validate(enc, mutate)
+
+
+def test_arrays_keep_their_encoding_alive():
+    """A typed array taken from a temporary encoding stays valid: the array
+    holds a reference to the library-owned memory's owner."""
+    import gc
+    u = synth.normal_bf16(50_000, 0.02, seed=60)
+    ref = api.encode(u).arrays["exp_words"].copy()
+    arr = api.encode(u).arrays["exp_words"]      # the Encoded object is a temporary
+    gc.collect()
+    _ = [api.encode(synth.normal_bf16(50_000, 0.02, seed=61)) for _ in range(3)]   # reuse freed memory
+    assert np.array_equal(arr, ref)
