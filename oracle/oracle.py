@@ -62,6 +62,7 @@ def lib():
         L.orc_decode.restype = ctypes.c_int
         L.orc_metadata.argtypes = [_u64p, _u16p, _u64, _u8p, _u64, _u64, _u64,
                                    _u8p, _u64p, _u32p]
+        L.orc_chunk_counts.argtypes = [_u64p, _u64, _u64, _u64, _u8p]
         L.orc_gemm_f32.argtypes = [_u16p, _u16p, _u64, _u64, _u64, _f32p]
         L.orc_gemm_f64.argtypes = [_u16p, _u16p, _u64, _u64, _u64, _f64p]
         L.orc_tile_order.argtypes = [_u16p, _u64, _u64, _u64, _u64, _u64, _u16p]
@@ -148,9 +149,12 @@ def encode(u, lengths=None, lmax: int = 32, chunk_bytes: int = 16, seg_lanes: in
     seg_elem = np.zeros(nseg + 1, np.uint64)
     seg_nbits = np.zeros(max(nseg, 1), np.uint32)
     lib().orc_metadata(start, u, n, ln, chunk_bits, seg_bits, nseg, gaps, seg_elem, seg_nbits)
+    counts = np.zeros(max(nseg * seg_lanes, 1), np.uint8)
+    lib().orc_chunk_counts(start, n, chunk_bits, nseg * seg_lanes, counts)
     return Encoded(n=n, lengths=ln, codes=codes, starts=start[:n], total_bits=total,
                    E=E[:(total + 7) // 8], sm=sm, n_segments=nseg,
-                   gaps=gaps[:nseg * seg_lanes], seg_elem=seg_elem, seg_nbits=seg_nbits[:nseg],
+                   gaps=gaps[:nseg * seg_lanes], counts=counts[:nseg * seg_lanes],
+                   seg_elem=seg_elem, seg_nbits=seg_nbits[:nseg],
                    chunk_bytes=chunk_bytes, seg_lanes=seg_lanes, align_elems=align_elems)
 
 

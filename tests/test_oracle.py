@@ -219,6 +219,8 @@ def test_tiny_stream_hand_worked():
     assert enc.total_bits == int(g["total_bits"][0])
     assert enc.E.tolist() == [int(x, 16) for x in g["stream"]]
     assert enc.sm.tolist() == [int(x, 16) for x in g["sign_mantissa"]]
+    # all six codes (11 bits) start in the first 128-bit chunk
+    assert enc.counts.tolist() == [6] + [0] * 63
 
 
 def test_uniform_code_stream_is_raw_exponents():
@@ -254,6 +256,13 @@ def test_metadata_closed_form_fixed_length(L, chunk_bytes, seg_lanes):
             c0 = s * sb + l * cb
             want = (-c0) % L if c0 < n * L else 0
             assert int(enc.gaps[s * seg_lanes + l]) == want
+            # code starts in [c0, c0 + cb) below n*L: multiples of L
+            hi = min(c0 + cb, n * L)
+            starts_in = max(0, -(-hi // L) - (-(-c0 // L))) if c0 < n * L else 0
+            assert int(enc.counts[s * seg_lanes + l]) == starts_in
+        # a segment's chunk counts add up to its elements
+        assert int(enc.counts[s * seg_lanes:(s + 1) * seg_lanes].sum()) == \
+            int(enc.seg_elem[s + 1]) - int(enc.seg_elem[s])
     assert int(enc.seg_elem[-1]) == n
 
 
@@ -268,9 +277,25 @@ def test_aligned_layout_pads_to_segments():
     assert enc.total_bits == 120
     assert enc.seg_elem.tolist() == [0, 2, 3, 5, 6, 8, 9, 11, 12]
     assert enc.seg_nbits.tolist() == [16, 8, 16, 8, 16, 8, 16, 8]
+    # one 8-bit code per 8-bit chunk, none in the padding chunks
+    assert enc.counts.tolist() == [1, 1, 1, 0] * 4
 
 
 # --------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("name", ["normal", "adversarial", "fibonacci"])
+def test_chunk_counts_add_up_per_segment(name):
+    """Variable-length codes: a segment's chunk counts sum to its element
+    count, and a chunk's count equals its code starts found by brute force."""
+    u = {"normal": lambda: synth.normal_bf16(200_000, 0.02, seed=70),
+         "adversarial": lambda: synth.adversarial_bf16(200_000, seed=71),
+         "fibonacci": lambda: synth.fibonacci_bf16(seed=72)[:300_000]}[name]()
+    enc = orc.encode(u)
+    cnt = enc.counts.astype(np.int64).reshape(enc.n_segments, 64)
+    assert (cnt.sum(axis=1) == np.diff(enc.seg_elem.astype(np.int64))).all()
+    brute = np.bincount((enc.starts // 128).astype(np.int64), minlength=enc.n_segments * 64)
+    assert np.array_equal(brute, enc.counts.astype(np.int64))
+
 
 @pytest.mark.parametrize("name", ["normal", "adversarial", "exhaustive", "fibonacci", "tiny"])
 def test_round_trip_identity(name):
