@@ -44,10 +44,10 @@ def log(*a):
 
 def algorithmic_bytes(enc) -> int:
     """Bytes a decode must move: the exponent stream, one sign+mantissa byte
-    per element, the per-lane gaps and per-segment records, and the BF16
-    output (2 bytes per element)."""
+    per element, the per-lane gaps and code counts, the per-segment records,
+    and the BF16 output (2 bytes per element)."""
     stream = (enc.total_bits + 7) // 8
-    return stream + enc.n + enc.n_segments * 64 + (enc.n_segments + 1) * 16 + 2 * enc.n
+    return stream + enc.n + enc.n_segments * 128 + (enc.n_segments + 1) * 16 + 2 * enc.n
 
 
 def measured_traffic(profile: str, sources) -> float | None:
@@ -200,7 +200,7 @@ def model_pass(steps: int, warmup: int, seed: int = 0):
     t_build = time.time() - t0
     checked = mdl.verify_pass(m, seed)
     log("8B model built in %.1f s; all %d elements decoded and verified" % (t_build, checked))
-    alg = sum((t.total_bits + 7) // 8 + t.n + t.n_segments * 80 + 16 + 2 * t.n for _, _, t in m.matrices)
+    alg = sum((t.total_bits + 7) // 8 + t.n + t.n_segments * 144 + 16 + 2 * t.n for _, _, t in m.matrices)
 
     def timeit(f, n):
         for _ in range(warmup):

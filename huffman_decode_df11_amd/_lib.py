@@ -55,6 +55,7 @@ class View(ctypes.Structure):
         ("chain", ctypes.c_void_p), ("n_chain", u64),
         ("fast", ctypes.c_void_p), ("n_fast", u64),
         ("block_seg", ctypes.c_void_p), ("n_block_seg", u64),
+        ("counts", ctypes.c_void_p), ("n_counts", u64),
     ]
 
 
@@ -67,6 +68,7 @@ VIEW_ARRAYS = (
     ("chain", ctypes.c_uint16),
     ("fast", ctypes.c_uint32),
     ("block_seg", ctypes.c_uint64),
+    ("counts", ctypes.c_uint8),
 )
 
 EXPORTS = (

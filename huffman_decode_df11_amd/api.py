@@ -114,6 +114,8 @@ class Encoded:
     @property
     def gaps(self): return self.arrays["gaps"]
     @property
+    def counts(self): return self.arrays["counts"]
+    @property
     def seg_elem(self): return self.arrays["segs"].view(np.uint64).reshape(-1, 2)[:, 0]
     @property
     def seg_nbits(self): return self.arrays["segs"].view(np.uint32).reshape(-1, 4)[:, 2]

@@ -40,6 +40,7 @@ struct ViewArgs {
     const uint32_t *words;
     const uint8_t *sm;
     const uint8_t *gaps;
+    const uint8_t *counts;
     const df11_segment *segs;
     uint16_t *out;
     uint64_t n;
@@ -96,8 +97,9 @@ struct SegLoad {
     uint4 own;          // this lane's 4 stream words
     uint32_t next;      // the following word (look-ahead)
     uint32_t gap;
-    uint64_t g0, g1;
+    uint32_t count;     // codes that start in this lane's chunk, when the view stores counts
     uint32_t nbits;
+    uint64_t g0, g1;
 };
 
 __device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, uint32_t lane)
@@ -107,6 +109,7 @@ __device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, u
     L.own = *reinterpret_cast<const uint4 *>(w);
     L.next = w[4];
     L.gap = v.gaps[s * 64 + lane];
+    L.count = v.counts ? v.counts[s * 64 + lane] : 0u;
     L.g0 = v.segs[s].elem_off;
     L.g1 = v.segs[s + 1].elem_off;
     L.nbits = v.segs[s].nbits;
@@ -147,17 +150,21 @@ __device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm,
 }
 
 // Locate, scan and emit one segment into the wave's staging (exponent of
-// element g at stg + g - gbase).  False when the stream disagrees with the
-// segment's records (then nothing is staged).
+// element g at stg + g - gbase).  The lane's code count is the stored one
+// when the view carries counts, else the locate pass walks the chunk.
+// False when the counts disagree with the segment's records (then nothing
+// is staged).
 template <int K>
-__device__ __forceinline__ bool stage_segment(const SegLoad &cur, const SegPlan &p, uint32_t stg, uint32_t fast,
-                                              uint32_t chain, uint32_t lane)
+__device__ __forceinline__ bool stage_segment(const SegLoad &cur, const SegPlan &p, bool stored, uint32_t stg,
+                                              uint32_t fast, uint32_t chain, uint32_t lane)
 {
-    const uint32_t c0 = lane * kChunkBits;
-    const uint32_t end = cur.nbits > c0 ? min(kChunkBits, cur.nbits - c0) : 0u;
-    const uint32_t p0 = cur.gap;
-    const Window win = make_window(cur.own, cur.next, p0);
-    const uint32_t cnt = p0 < end ? count_codes<K>(win, fast, chain, p0, end) : 0u;
+    const Window win = make_window(cur.own, cur.next, cur.gap);
+    uint32_t cnt = cur.count;
+    if (!stored) {
+        const uint32_t c0 = lane * kChunkBits;
+        const uint32_t end = cur.nbits > c0 ? min(kChunkBits, cur.nbits - c0) : 0u;
+        cnt = cur.gap < end ? count_codes<K>(win, fast, chain, cur.gap, end) : 0u;
+    }
     uint32_t total;
     const uint32_t excl = wave_exclusive_scan(cnt, &total);
     if (total != (uint32_t)(p.g1 - p.g0)) return false;
@@ -265,7 +272,7 @@ decode_kernel(BatchArgs b, TableArgs t)
         const uint32_t vi_next = more ? view_of(b, s_next) : vi;
         if (more) nx = load_segment(b.v[vi_next], s_next - b.seg_begin[vi_next], lane);
 
-        if (p.valid && stage_segment<K>(cur, p, stg, fast, chain, lane))
+        if (p.valid && stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane))
             merge_range(p, p.g0, p.g1, smp, v.sm, ViewOut{v}, stg, lane);
         wave_lds_sync();   // the staging is reused by the next segment
         if (!more) break;
@@ -316,7 +323,7 @@ decode_rows_kernel(RowArgs a, TableArgs t)
             const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
             uint4 smp[kPrefetchRounds];
             prefetch_sm(p, v.sm, lane, smp);
-            if (p.valid && cur.g1 > lo && stage_segment<K>(cur, p, stg, fast, chain, lane))
+            if (p.valid && cur.g1 > lo && stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane))
                 merge_range(p, max(lo, p.g0), min(hi, p.g1), smp, v.sm, out, stg, lane);
             wave_lds_sync();
         }
@@ -335,6 +342,7 @@ int check_view(const df11_view *v)
         v->n_fast != (2ull << v->fast_bits))
         return df11::fail(DF11_E_ARG, "table sizes inconsistent");
     if (v->n_segs != v->n_segments + 1 || v->n_gaps != v->n_segments * 64 ||
+        (v->n_counts && (v->n_counts != v->n_segments * 64 || !v->counts)) ||
         v->n_exp_words < v->n_segments * kSegWords + 2 || v->n_sm < (v->n + 15) / 16 * 16)
         return df11::fail(DF11_E_ARG, "view array sizes inconsistent with n / n_segments");
     if (v->n && (!v->exp_words || !v->sm || !v->gaps || !v->segs || !v->chain || !v->fast))
@@ -381,6 +389,7 @@ ViewArgs make_args(const df11_view *v, uint16_t *out)
     a.words = v->exp_words;
     a.sm = v->sm;
     a.gaps = v->gaps;
+    a.counts = v->n_counts ? v->counts : nullptr;   // no counts: the decode runs the locate pass
     a.segs = v->segs;
     a.out = out;
     a.n = v->n;

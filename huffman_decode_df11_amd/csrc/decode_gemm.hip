@@ -51,6 +51,7 @@ struct GemmArgs {
     const uint32_t *words;
     const uint8_t *sm;
     const uint8_t *gaps;
+    const uint8_t *counts;
     const df11_segment *segs;
     const uint64_t *block_seg;
     const uint16_t *chain;
@@ -69,7 +70,7 @@ struct GemmArgs {
 
 struct SegLoad {
     uint4 own;
-    uint32_t next, gap, nbits;
+    uint32_t next, gap, count, nbits;
     uint64_t g0, g1;
 };
 
@@ -80,6 +81,7 @@ __device__ __forceinline__ SegLoad load_segment(const GemmArgs &g, uint64_t s, u
     L.own = *reinterpret_cast<const uint4 *>(w);
     L.next = w[4];
     L.gap = g.gaps[s * 64 + lane];
+    L.count = g.counts ? g.counts[s * 64 + lane] : 0u;
     L.g0 = g.segs[s].elem_off;
     L.g1 = g.segs[s + 1].elem_off;
     L.nbits = g.segs[s].nbits;
@@ -88,14 +90,17 @@ __device__ __forceinline__ SegLoad load_segment(const GemmArgs &g, uint64_t s, u
 
 // Decode one tile-aligned segment into the exponent plane of its tile.
 template <int K>
-__device__ __forceinline__ void decode_into_plane(const SegLoad &L, uint64_t tile_start, uint32_t plane,
+__device__ __forceinline__ void decode_into_plane(const SegLoad &L, uint64_t tile_start, uint32_t plane, bool stored,
                                                   uint32_t fast, uint32_t chain, uint32_t lane)
 {
     if (L.g0 >= tile_start && L.g1 >= L.g0 && L.g1 <= tile_start + kTile) {
-        const uint32_t c0 = lane * kChunkBits;
-        const uint32_t end = L.nbits > c0 ? min(kChunkBits, L.nbits - c0) : 0u;
         const Window win = make_window(L.own, L.next, L.gap);
-        const uint32_t cnt = L.gap < end ? count_codes<K>(win, fast, chain, L.gap, end) : 0u;
+        uint32_t cnt = L.count;
+        if (!stored) {   // no stored counts: the locate pass walks the chunk
+            const uint32_t c0 = lane * kChunkBits;
+            const uint32_t end = L.nbits > c0 ? min(kChunkBits, L.nbits - c0) : 0u;
+            cnt = L.gap < end ? count_codes<K>(win, fast, chain, L.gap, end) : 0u;
+        }
         uint32_t total;
         const uint32_t excl = wave_exclusive_scan(cnt, &total);
         if (total == (uint32_t)(L.g1 - L.g0))
@@ -146,7 +151,7 @@ decode_gemm_kernel(GemmArgs g)
             const uint64_t t0 = (uint64_t)rb * g.tiles_per_row + kt0;
             const uint64_t s1 = min(g.block_seg[t0 + 1], g.n_segments);
             for (uint64_t s = g.block_seg[t0] + wave; s < s1; s += WAVES)
-                decode_into_plane<K>(load_segment(g, s, lane), t0 * kTile, eplane0, fast, chain, lane);
+                decode_into_plane<K>(load_segment(g, s, lane), t0 * kTile, eplane0, g.counts != nullptr, fast, chain, lane);
             __syncthreads();
         }
 
@@ -193,8 +198,8 @@ decode_gemm_kernel(GemmArgs g)
             if (has_next) {
                 const uint32_t np = eplane0 + (cur ^ 1) * kTile;
                 for (uint64_t s = ns0; s < ns1; s += WAVES)
-                    decode_into_plane<K>(s == ns0 ? nseg : load_segment(g, s, lane), (t + 1) * kTile, np, fast, chain,
-                                         lane);
+                    decode_into_plane<K>(s == ns0 ? nseg : load_segment(g, s, lane), (t + 1) * kTile, np,
+                                         g.counts != nullptr, fast, chain, lane);
             }
             __syncthreads();
         }
@@ -338,7 +343,7 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
         return df11::fail(DF11_E_ARG, "weight too large");
     const uint64_t nb = w->n / kTile;
     if (w->n_block_seg != nb + 1 || !w->block_seg || w->n_segs != w->n_segments + 1 ||
-        w->n_gaps != w->n_segments * 64 || w->n_exp_words < w->n_segments * kSegWords + 2 || w->n_sm < w->n)
+        w->n_gaps != w->n_segments * 64 || (w->n_counts && (w->n_counts != w->n_segments * 64 || !w->counts)) || w->n_exp_words < w->n_segments * kSegWords + 2 || w->n_sm < w->n)
         return df11::fail(DF11_E_ARG, "view array sizes inconsistent");
     if (w->fast_bits < DF11_FAST_BITS_MIN || w->fast_bits > DF11_FAST_BITS_MAX || w->n_tables < 1 ||
         w->n_tables > DF11_MAX_TABLES || w->n_chain != (uint64_t)w->n_tables * 256 || w->n_fast != (2ull << w->fast_bits))
@@ -350,6 +355,7 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
     a.words = w->exp_words;
     a.sm = w->sm;
     a.gaps = w->gaps;
+    a.counts = w->n_counts ? w->counts : nullptr;   // no counts: the decode runs the locate pass
     a.segs = w->segs;
     a.block_seg = w->block_seg;
     a.chain = w->chain;

@@ -20,6 +20,8 @@ int build_tables(df11_codebook *cb);
 // (chunk_bytes 16, seg_lanes 64), then the layout checked against n.
 df11_layout complete_layout(const df11_layout *in);
 int check_layout(const df11_layout &L, uint64_t n);
+// A chunk's code count is stored in a byte: chunk bits / shortest code <= 255.
+int check_counts_fit(const df11_layout &L, const df11_codebook *cb);
 
 }  // namespace df11
 
@@ -34,4 +36,5 @@ struct df11_encoded {
     std::vector<uint16_t> chain;
     std::vector<uint32_t> fast;
     std::vector<uint64_t> block_seg;
+    std::vector<uint8_t> counts;
 };

@@ -43,7 +43,8 @@ struct df11_device_encoded {
     uint16_t *chain = nullptr;
     uint32_t *fast = nullptr;
     uint64_t *block_seg = nullptr;
-    uint64_t n_exp_words = 0, n_sm = 0, n_gaps = 0, n_segs = 0, n_chain = 0, n_fast = 0, n_block_seg = 0;
+    uint8_t *counts = nullptr;
+    uint64_t n_exp_words = 0, n_sm = 0, n_gaps = 0, n_segs = 0, n_chain = 0, n_fast = 0, n_block_seg = 0, n_counts = 0;
 };
 
 namespace {
@@ -146,6 +147,7 @@ struct EmitArgs {
     uint8_t *sm;
     uint8_t *gaps;
     df11_segment *segs;
+    uint32_t *counts32;     // codes starting in each chunk (accumulated)
 };
 
 __global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct)
@@ -184,6 +186,8 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct
         prev = (i0 == 0 ? a.end[b - 1] : pos) - lp;
     }
     const uint64_t SB = a.seg_bits, CB = a.chunk_bits;
+    uint64_t run_chunk = ~0ull;   // chunk of the codes counted in run_n, not yet added
+    uint32_t run_n = 0;
     for (uint32_t i = i0; i < i1; i++) {
         const uint64_t g = g0 + i;
         const uint16_t u = a.bits[a.order(g)];
@@ -196,6 +200,12 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct
         if (hi) atomicOr(&a.words[w], hi);
         if (lo) atomicOr(&a.words[w + 1], lo);
         a.sm[g] = (uint8_t)(((u >> 8) & 0x80) | (u & 0x7F));
+        if (pos / CB != run_chunk) {
+            if (run_n) atomicAdd(&a.counts32[run_chunk], run_n);
+            run_chunk = pos / CB;
+            run_n = 0;
+        }
+        run_n++;
         const uint64_t s = pos / SB;
         // gap of the chunk holding this code's first bit, when no earlier code starts in it
         const uint64_t c0 = pos - pos % CB;
@@ -217,6 +227,13 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct
         has_prev = true;
         pos = vend;
     }
+    if (run_n) atomicAdd(&a.counts32[run_chunk], run_n);
+}
+
+__global__ void narrow_counts_kernel(const uint32_t *c32, uint8_t *c8, uint64_t n)
+{
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+        c8[i] = (uint8_t)c32[i];
 }
 
 __global__ void seg_max_kernel(const df11_segment *segs, uint64_t nseg, uint32_t *out)
@@ -247,7 +264,7 @@ uint32_t grid_for(uint64_t items, uint32_t per_group)
 void free_device(df11_device_encoded *d)
 {
     if (!d) return;
-    void *ps[] = {d->exp_words, d->sm, d->gaps, d->segs, d->chain, d->fast, d->block_seg};
+    void *ps[] = {d->exp_words, d->sm, d->gaps, d->segs, d->chain, d->fast, d->block_seg, d->counts};
     for (void *p : ps)
         if (p) (void)hipFree(p);
     delete d;
@@ -301,6 +318,8 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
     if (cb->fast_bits < DF11_FAST_BITS_MIN || cb->fast_bits > DF11_FAST_BITS_MAX || cb->n_tables < 1 ||
         cb->n_tables > DF11_MAX_TABLES || cb->max_len > DF11_MAX_LEN)
         return df11::fail(DF11_E_ARG, "codebook not built by df11_codebook_build");
+    rc = df11::check_counts_fit(L, cb);
+    if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     const uint64_t chunk_bits = 8ull * L.chunk_bytes, seg_bits = chunk_bits * L.seg_lanes, seg_words = seg_bits / 32;
     // scan blocks nest in aligned blocks, so padding only falls between scan blocks
@@ -357,6 +376,7 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
     d->n_exp_words = nseg * seg_words + 2;
     d->n_sm = (n + 15) / 16 * 16;
     d->n_gaps = nseg * L.seg_lanes;
+    d->n_counts = d->n_gaps;
     d->n_segs = nseg + 1;
     d->n_chain = (uint64_t)cb->n_tables * 256;
     d->n_fast = 2ull << cb->fast_bits;
@@ -364,6 +384,7 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
     HIP_TRY(hipMalloc((void **)&d->exp_words, d->n_exp_words * 4), "stream words");
     HIP_TRY(hipMalloc((void **)&d->sm, std::max<uint64_t>(d->n_sm, 16)), "sign+mantissa");
     HIP_TRY(hipMalloc((void **)&d->gaps, std::max<uint64_t>(d->n_gaps, 16)), "gaps");
+    HIP_TRY(hipMalloc((void **)&d->counts, std::max<uint64_t>(d->n_counts, 16)), "counts");
     HIP_TRY(hipMalloc((void **)&d->segs, d->n_segs * sizeof(df11_segment)), "segment records");
     HIP_TRY(hipMalloc((void **)&d->chain, d->n_chain * 2), "tables");
     HIP_TRY(hipMalloc((void **)&d->fast, d->n_fast * 4), "tables");
@@ -371,6 +392,7 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
     HIP_TRY(hipMemsetAsync(d->exp_words, 0, d->n_exp_words * 4, st), "clear");
     HIP_TRY(hipMemsetAsync(d->sm, 0, std::max<uint64_t>(d->n_sm, 16), st), "clear");
     HIP_TRY(hipMemsetAsync(d->gaps, 0, std::max<uint64_t>(d->n_gaps, 16), st), "clear");
+    HIP_TRY(hipMemsetAsync(d->counts, 0, std::max<uint64_t>(d->n_counts, 16), st), "clear");
     HIP_TRY(hipMemsetAsync(d->segs, 0, d->n_segs * sizeof(df11_segment), st), "clear");
     HIP_TRY(hipMemcpyAsync(d->chain, cb->chain, d->n_chain * 2, hipMemcpyHostToDevice, st), "tables");
     HIP_TRY(hipMemcpyAsync(d->fast, cb->fast, d->n_fast * 4, hipMemcpyHostToDevice, st), "tables");
@@ -389,9 +411,16 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
         HIP_TRY(hipMemcpyAsync(dbase, base.data(), (nb + 1) * 8, hipMemcpyHostToDevice, st), "block starts");
         HIP_TRY(hipMemcpyAsync(dend, end.data(), nb * 8, hipMemcpyHostToDevice, st), "block ends");
         HIP_TRY(hipMemsetAsync(dmax, 0, 4, st), "clear");
-        EmitArgs a{bits, n, nseg, seg_bits, chunk_bits, E, order, dbase, dend, d->exp_words, d->sm, d->gaps, d->segs};
+        uint32_t *dcnt;
+        HIP_TRY(s.alloc(&dcnt, d->n_counts), "chunk counts");
+        HIP_TRY(hipMemsetAsync(dcnt, 0, std::max<uint64_t>(d->n_counts, 1) * 4, st), "clear");
+        EmitArgs a{bits, n, nseg, seg_bits, chunk_bits, E, order, dbase, dend, d->exp_words, d->sm, d->gaps, d->segs, dcnt};
         hipLaunchKernelGGL(emit_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, st, a, ct);
         HIP_TRY(hipGetLastError(), "emit launch");
+        if (d->n_counts)
+            hipLaunchKernelGGL(narrow_counts_kernel, dim3(grid_for(d->n_counts, 1024)), dim3(256), 0, st, dcnt, d->counts,
+                               d->n_counts);
+        HIP_TRY(hipGetLastError(), "counts launch");
         hipLaunchKernelGGL(seg_max_kernel, dim3(grid_for(nseg, 256)), dim3(256), 0, st, d->segs, nseg, dmax);
         HIP_TRY(hipGetLastError(), "segment max launch");
         HIP_TRY(hipMemcpyAsync(&d->max_seg_elems, dmax, 4, hipMemcpyDeviceToHost, st), "max copy");
@@ -433,6 +462,7 @@ extern "C" int df11_device_encoded_view(const df11_device_encoded *d, df11_view 
     v->chain = d->chain;          v->n_chain = d->n_chain;
     v->fast = d->fast;            v->n_fast = d->n_fast;
     v->block_seg = d->block_seg;  v->n_block_seg = d->n_block_seg;
+    v->counts = d->counts;        v->n_counts = d->n_counts;
     return DF11_OK;
 }
 
@@ -450,6 +480,7 @@ extern "C" int df11_device_encoded_to_host(const df11_device_encoded *d, df11_en
         h->chain.resize(d->n_chain);
         h->fast.resize(d->n_fast);
         h->block_seg.resize(d->n_block_seg);
+        h->counts.resize(d->n_counts);
     } catch (...) {
         delete h;
         return df11::fail(DF11_E_ALLOC, "out of host memory");
@@ -467,7 +498,7 @@ extern "C" int df11_device_encoded_to_host(const df11_device_encoded *d, df11_en
         {h->exp_words.data(), d->exp_words, d->n_exp_words * 4}, {h->sm.data(), d->sm, d->n_sm},
         {h->gaps.data(), d->gaps, d->n_gaps}, {h->segs.data(), d->segs, d->n_segs * sizeof(df11_segment)},
         {h->chain.data(), d->chain, d->n_chain * 2}, {h->fast.data(), d->fast, d->n_fast * 4},
-        {h->block_seg.data(), d->block_seg, d->n_block_seg * 8}};
+        {h->block_seg.data(), d->block_seg, d->n_block_seg * 8}, {h->counts.data(), d->counts, d->n_counts}};
     for (auto &p : parts) {
         if (!p.bytes) continue;
         hipError_t e = hipMemcpy(p.dst, p.src, p.bytes, hipMemcpyDeviceToHost);

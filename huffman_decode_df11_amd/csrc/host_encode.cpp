@@ -7,6 +7,7 @@
 //      fixed run of encoded bytes; 5.2: data aligned to 256 bytes.
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -89,6 +90,14 @@ int check_layout(const df11_layout &L, uint64_t n)
     return DF11_OK;
 }
 
+int check_counts_fit(const df11_layout &L, const df11_codebook *cb)
+{
+    if (8ull * L.chunk_bytes / std::max(1u, cb->min_len) > 255)
+        return fail(DF11_E_ARG, "chunk_bytes %u with %u-bit codes: a chunk's code count would not fit a byte",
+                    L.chunk_bytes, cb->min_len);
+    return DF11_OK;
+}
+
 df11_layout complete_layout(const df11_layout *in)
 {
     df11_layout L{};
@@ -146,6 +155,8 @@ extern "C" int df11_encode(const uint16_t *bits, uint64_t n, const df11_codebook
     if (cb->fast_bits < DF11_FAST_BITS_MIN || cb->fast_bits > DF11_FAST_BITS_MAX || cb->n_tables < 1 ||
         cb->n_tables > DF11_MAX_TABLES || cb->max_len > DF11_MAX_LEN)
         return fail(DF11_E_ARG, "codebook not built by df11_codebook_build");
+    rc = check_counts_fit(L, cb);
+    if (rc) return rc;
 
     const Order order(L);
     const uint64_t chunk_bits = 8ull * L.chunk_bytes;
@@ -170,6 +181,7 @@ extern "C" int df11_encode(const uint16_t *bits, uint64_t n, const df11_codebook
         enc->exp_words.assign(nseg * seg_words + 2, 0u);
         enc->sm.assign((n + 15) / 16 * 16, 0);
         enc->gaps.assign(nseg * lanes, 0);
+        enc->counts.assign(nseg * lanes, 0);
         enc->segs.assign(nseg + 1, df11_segment{0, 0, 0});
         enc->chain.assign(cb->chain, cb->chain + (size_t)cb->n_tables * 256);
         enc->fast.assign(cb->fast, cb->fast + (2u << cb->fast_bits));
@@ -230,6 +242,7 @@ extern "C" int df11_encode(const uint16_t *bits, uint64_t n, const df11_codebook
         W[w] |= (uint32_t)(wide >> 32);
         W[w + 1] |= (uint32_t)wide;
         enc->sm[g] = (uint8_t)(((u >> 8) & 0x80) | (u & 0x7F));
+        enc->counts[pos / chunk_bits]++;
         vend = pos + len;
         pos += len;
     }
@@ -280,6 +293,7 @@ extern "C" int df11_encoded_view(const df11_encoded *enc, df11_view *v)
     v->chain = enc->chain.data();          v->n_chain = enc->chain.size();
     v->fast = enc->fast.data();            v->n_fast = enc->fast.size();
     v->block_seg = enc->block_seg.data();  v->n_block_seg = enc->block_seg.size();
+    v->counts = enc->counts.data();        v->n_counts = enc->counts.size();
     return DF11_OK;
 }
 

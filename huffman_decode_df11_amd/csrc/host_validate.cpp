@@ -23,7 +23,7 @@ inline uint32_t window_at(const uint32_t *w, uint64_t nwords, uint64_t pos)
 extern "C" int df11_validate(const df11_view *v, const df11_codebook *cb)
 {
     if (!v || !cb) return fail(DF11_E_ARG, "df11_validate: null pointer");
-    if (v->n && (!v->exp_words || !v->sm || !v->gaps || !v->segs || !v->chain || !v->fast))
+    if (v->n && (!v->exp_words || !v->sm || !v->gaps || (v->n_counts && !v->counts) || !v->segs || !v->chain || !v->fast))
         return fail(DF11_E_ARG, "df11_validate: null array in view");
     // codebook: lengths, Kraft sum, canonical codes and tables
     uint64_t kraft = 0;   // in units of 2^-32
@@ -55,7 +55,8 @@ extern "C" int df11_validate(const df11_view *v, const df11_codebook *cb)
     if (v->n_segments != (v->total_bits + seg_bits - 1) / seg_bits)
         return fail(DF11_E_FORMAT, "n_segments %llu does not match total_bits", (unsigned long long)v->n_segments);
     if (v->n_exp_words < v->n_segments * seg_words + 2 || v->n_sm < (v->n + 15) / 16 * 16 ||
-        v->n_gaps != v->n_segments * lanes || v->n_segs != v->n_segments + 1)
+        v->n_gaps != v->n_segments * lanes || (v->n_counts && v->n_counts != v->n_segments * lanes) ||
+        v->n_segs != v->n_segments + 1)
         return fail(DF11_E_FORMAT, "array sizes do not match n and n_segments");
     if (v->segs[0].elem_off != 0 || v->segs[v->n_segments].elem_off != v->n)
         return fail(DF11_E_FORMAT, "first/last segment record must be 0 / n");
@@ -91,12 +92,15 @@ extern "C" int df11_validate(const df11_view *v, const df11_codebook *cb)
             const uint32_t gap = v->gaps[s * lanes + l];
             if (c0 >= vend) {
                 if (gap) return fail(DF11_E_FORMAT, "segment %llu lane %llu: gap past the segment's codes", (unsigned long long)s, (unsigned long long)l);
+                if (v->n_counts && v->counts[s * lanes + l])
+                    return fail(DF11_E_FORMAT, "segment %llu lane %llu: count past the segment's codes", (unsigned long long)s, (unsigned long long)l);
                 continue;
             }
             if (gap >= 32) return fail(DF11_E_FORMAT, "segment %llu lane %llu: gap %u >= 32", (unsigned long long)s, (unsigned long long)l, gap);
             // the previous lane's last code must end exactly where this lane starts
             uint64_t p = c0 + gap;
             const uint64_t end = c1 < vend ? c1 : vend;
+            const uint64_t got0 = got;
             while (p < end) {
                 uint16_t e = chain_walk(v->chain, window_at(v->exp_words, v->n_exp_words, p));
                 uint32_t L = (e >> 8) & 0x3F;
@@ -105,6 +109,10 @@ extern "C" int df11_validate(const df11_view *v, const df11_codebook *cb)
                 p += L;
                 got++;
             }
+            if (v->n_counts && got - got0 != v->counts[s * lanes + l])
+                return fail(DF11_E_FORMAT, "segment %llu lane %llu: %llu codes start in the chunk, count says %u",
+                            (unsigned long long)s, (unsigned long long)l, (unsigned long long)(got - got0),
+                            v->counts[s * lanes + l]);
             if (l + 1 < lanes && c1 < vend && p != c1 + v->gaps[s * lanes + l + 1])
                 return fail(DF11_E_FORMAT, "segment %llu lane %llu: codes do not meet the next lane's gap", (unsigned long long)s, (unsigned long long)l);
             if (c1 >= vend && sg.nbits < seg_bits && p != vend)

@@ -8,7 +8,8 @@ block being computed is on the GPU.  Moving compressed blocks instead of
 BF16 ones moves ~30% fewer bytes over PCIe.
 
 Per group (a decoder layer): its streamed arrays (exponent words,
-sign+mantissa bytes, gaps, segment records) are one pinned host blob; a
+sign+mantissa bytes, gaps, chunk counts, segment records) are one pinned
+host blob; a
 copy stream moves the blob into one of two device slots while the compute
 stream decodes the previous group from the other slot; events order slot
 reuse.  The code tables (a few KB per codebook) stay resident on the GPU.
@@ -23,7 +24,7 @@ import numpy as np
 from . import api
 from ._lib import VIEW_ARRAYS, View
 
-_STREAMED = ("exp_words", "sm", "gaps", "segs", "block_seg")
+_STREAMED = ("exp_words", "sm", "gaps", "counts", "segs", "block_seg")
 _ALIGN = 256
 
 

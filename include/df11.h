@@ -42,6 +42,13 @@
  *   gaps       One byte per chunk: the distance in bits from the chunk start
  *              to the first code that starts at or after it (0..31), or 0 for
  *              a chunk at or past its segment's last code.
+ *   counts     One byte per chunk: the number of codes whose first bit lies
+ *              in the chunk (0 for chunks past the segment's last code).  The
+ *              decoder's output positions are a prefix sum of these counts.
+ *              Optional in a view (n_counts = 0): the decoder then finds each
+ *              lane's count itself by walking its chunk (the locate pass).
+ *              Encoders always write them; a layout whose chunk could hold
+ *              more than 255 codes (chunk bits / shortest code) is refused.
  *   segs       n_segments + 1 records: elem_off = number of codes that start
  *              before the segment (the last record's elem_off = n); nbits =
  *              bits from the segment start to the end of the last code that
@@ -148,6 +155,7 @@ typedef struct df11_view {
     const uint32_t *fast;       uint64_t n_fast;       /* 2 << fast_bits */
     const uint64_t *block_seg;  uint64_t n_block_seg;  /* align_elems > 0: first segment of
                                                           every aligned block, then n_segments */
+    const uint8_t *counts;      uint64_t n_counts;     /* n_segments * seg_lanes, or 0 */
 } df11_view;
 
 typedef struct df11_encoded df11_encoded;   /* opaque, library-owned host arrays */

@@ -243,3 +243,18 @@ def test_batch_rejects_different_codebooks():
     with pytest.raises(_lib.DF11Error) as ei:
         api.decode_batch([a, b])
     assert ei.value.status == -1
+
+
+@pytest.mark.parametrize("name", ["normal", "adversarial", "fibonacci"])
+def test_locate_pass_without_stored_counts(name):
+    """A view without chunk counts: the kernel finds each lane's codes with
+    the locate pass; the output is the same bit-exact result."""
+    u = {"normal": lambda: synth.normal_bf16(2_000_003, 0.02, seed=63),
+         "adversarial": lambda: synth.adversarial_bf16(1_000_000, seed=64),
+         "fibonacci": lambda: synth.fibonacci_bf16(seed=65)}[name]()
+    _say("case locate pass", name)
+    dt = api.encode(u).to("cuda")
+    dt.view.counts = None
+    dt.view.n_counts = 0
+    got = _decode_checked(dt, u.size)
+    assert np.array_equal(got, u)

@@ -127,3 +127,17 @@ def test_rejects_row_major_layout():
     with pytest.raises(_lib.DF11Error) as ei:
         api.decode_gemm(dt, _x_to_gpu(synth.activations_bf16(2, 512)))
     assert ei.value.status == -1
+
+
+def test_fused_locate_pass_without_stored_counts():
+    N, K, B = 96, 1536, 17
+    _say("case gemm locate pass")
+    W = synth.adversarial_bf16(N * K, seed=66).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=67)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    dt.view.counts = None
+    dt.view.n_counts = 0
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg)
+    torch.cuda.synchronize()
+    assert np.array_equal(wdbg.view(torch.int16).cpu().numpy().view(np.uint16), W)

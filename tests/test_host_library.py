@@ -135,7 +135,14 @@ LAYOUTS = {
 def test_encoder_matches_oracle(name, layout):
     u = WORKLOADS[name]()
     kw = LAYOUTS[layout]
-    enc = api.encode(u, layout=api.make_layout(**kw))
+    cb = api.build_codebook(api.hist_accumulate(u))
+    if 8 * kw.get("chunk_bytes", 16) // max(1, cb.min_len) > 255:
+        # a chunk could hold more codes than a count byte records
+        with pytest.raises(_lib.DF11Error) as ei:
+            api.encode(u, codebook=cb, layout=api.make_layout(**kw))
+        assert ei.value.status == -1
+        return
+    enc = api.encode(u, codebook=cb, layout=api.make_layout(**kw))
     ln = api.codebook_lengths(enc.codebook)
     ref = orc.encode(u, lengths=ln, chunk_bytes=kw.get("chunk_bytes", 16), seg_lanes=64,
                      align_elems=kw.get("align_elems", 0))
@@ -144,6 +151,7 @@ def test_encoder_matches_oracle(name, layout):
     assert np.array_equal(enc.sm[:enc.n], ref.sm) and not enc.sm[enc.n:].any()
     assert enc.n_segments == ref.n_segments
     assert np.array_equal(enc.gaps, ref.gaps)
+    assert np.array_equal(enc.counts, ref.counts)
     assert np.array_equal(enc.seg_elem, ref.seg_elem)
     assert np.array_equal(enc.seg_nbits[:-1], ref.seg_nbits)
     enc.validate()
@@ -240,7 +248,7 @@ def _corrupt_and_validate(enc, mutate):
     assert ei.value.status in (-4, -1)
 
 
-@pytest.mark.parametrize("what", ["stream_bit", "gap", "seg_elem", "seg_nbits", "chain", "fast",
+@pytest.mark.parametrize("what", ["stream_bit", "gap", "count", "seg_elem", "seg_nbits", "chain", "fast",
                                   "codebook_len", "n_segments"])
 def test_validator_catches_corruption(what):
     u = synth.normal_bf16(200_000, 0.02, seed=17)
@@ -254,6 +262,9 @@ def test_validator_catches_corruption(what):
         elif what == "gap":
             g = e.gaps
             g[100] = (int(g[100]) + 3) % 32
+        elif what == "count":
+            c = e.counts
+            c[70] += 1
         elif what == "seg_elem":
             e.seg_elem[5] += 1
         elif what == "seg_nbits":
@@ -279,3 +290,12 @@ def test_arrays_keep_their_encoding_alive():
     gc.collect()
     _ = [api.encode(synth.normal_bf16(50_000, 0.02, seed=61)) for _ in range(3)]   # reuse freed memory
     assert np.array_equal(arr, ref)
+
+
+def test_validator_accepts_a_view_without_counts():
+    """Counts are optional in a view: without them the decoder (and the
+    validator) find each lane's codes by walking the chunk."""
+    enc = api.encode(synth.normal_bf16(100_000, 0.02, seed=62))
+    enc.view.counts = None
+    enc.view.n_counts = 0
+    enc.validate()
