@@ -168,38 +168,74 @@ decode_gemm_kernel(GemmArgs g)
                 if (ns0 < ns1) nseg = load_segment(g, ns0, lane);
             }
 
-            // matrix cores on tile t: B operand = 8 weights of row n_l, group c
             const uint32_t ep = eplane0 + cur * kTile;
             const uint8_t *smt = g.sm + t * kTile;
-#pragma unroll 4
-            for (uint32_t i = 0; i < kTC / 16 / kKSlices; i++) {
-                const uint32_t ks = kslice + i * kKSlices;
-                const uint32_t c = 2 * ks + khalf;
-                const uint32_t off = c * (kTR * kKC) + n_l * kKC;
-                const uint2 sv = *reinterpret_cast<const uint2 *>(smt + off);
-                const uint2 rx = ld64(ep + off);
-                const uint2 lo = assemble4(sv.x, rx.x), hi = assemble4(sv.y, rx.y);
-                const v4u32 wb{lo.x, lo.y, hi.x, hi.y};
-                if (writes_w)
-                    *reinterpret_cast<uint4 *>(g.w_debug + (uint64_t)(rb * kTR + n_l) * g.K + kt * kTC + c * kKC) =
-                        make_uint4(lo.x, lo.y, hi.x, hi.y);
-                const bf16x8 bop = __builtin_bit_cast(bf16x8, wb);
+            if constexpr (MT == 1) {
+                // one batch tile: this tile's sign+mantissa bytes and x loads
+                // go out first and land while the next tile decodes
+                constexpr uint32_t kS = kTC / 16 / kKSlices;
+                uint2 svs[kS];
 #pragma unroll
-                for (int m = 0; m < kMPerWave; m++) {
-                    const uint32_t brow = (m_first + m * WAVES) * 32 + n_l;
-                    uint4 xa = make_uint4(0, 0, 0, 0);
-                    if (brow < g.B)
-                        xa = *reinterpret_cast<const uint4 *>(g.x + (uint64_t)brow * g.K + kt * kTC + ks * 16 + khalf * 8);
-                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa), bop, acc[m], 0, 0, 0);
+                for (uint32_t i = 0; i < kS; i++) {
+                    const uint32_t ks = kslice + i * kKSlices;
+                    const uint32_t off = (2 * ks + khalf) * (kTR * kKC) + n_l * kKC;
+                    svs[i] = *reinterpret_cast<const uint2 *>(smt + off);
                 }
-            }
+                if (has_next) {
+                    const uint32_t np = eplane0 + (cur ^ 1) * kTile;
+                    for (uint64_t s = ns0; s < ns1; s += WAVES)
+                        decode_into_plane<K>(s == ns0 ? nseg : load_segment(g, s, lane), (t + 1) * kTile, np,
+                                             g.counts != nullptr, fast, chain, lane);
+                }
+#pragma unroll
+                for (uint32_t i = 0; i < kS; i++) {
+                    const uint32_t ks = kslice + i * kKSlices;
+                    const uint32_t c = 2 * ks + khalf;
+                    const uint32_t off = c * (kTR * kKC) + n_l * kKC;
+                    const uint2 rx = ld64(ep + off);
+                    const uint2 lo = assemble4(svs[i].x, rx.x), hi = assemble4(svs[i].y, rx.y);
+                    if (writes_w)
+                        *reinterpret_cast<uint4 *>(g.w_debug + (uint64_t)(rb * kTR + n_l) * g.K + kt * kTC + c * kKC) =
+                            make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    uint4 xa = make_uint4(0, 0, 0, 0);
+                    if (n_l < g.B)
+                        xa = *reinterpret_cast<const uint4 *>(g.x + (uint64_t)n_l * g.K + kt * kTC + ks * 16 + khalf * 8);
+                    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, xa), __builtin_bit_cast(bf16x8, v4u32{lo.x, lo.y, hi.x, hi.y}),
+                        acc[0], 0, 0, 0);
+                }
+            } else {
+                // matrix cores on tile t: B operand = 8 weights of row n_l, group c
+    #pragma unroll 4
+                for (uint32_t i = 0; i < kTC / 16 / kKSlices; i++) {
+                    const uint32_t ks = kslice + i * kKSlices;
+                    const uint32_t c = 2 * ks + khalf;
+                    const uint32_t off = c * (kTR * kKC) + n_l * kKC;
+                    const uint2 sv = *reinterpret_cast<const uint2 *>(smt + off);
+                    const uint2 rx = ld64(ep + off);
+                    const uint2 lo = assemble4(sv.x, rx.x), hi = assemble4(sv.y, rx.y);
+                    const v4u32 wb{lo.x, lo.y, hi.x, hi.y};
+                    if (writes_w)
+                        *reinterpret_cast<uint4 *>(g.w_debug + (uint64_t)(rb * kTR + n_l) * g.K + kt * kTC + c * kKC) =
+                            make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, wb);
+#pragma unroll
+                    for (int m = 0; m < kMPerWave; m++) {
+                        const uint32_t brow = (m_first + m * WAVES) * 32 + n_l;
+                        uint4 xa = make_uint4(0, 0, 0, 0);
+                        if (brow < g.B)
+                            xa = *reinterpret_cast<const uint4 *>(g.x + (uint64_t)brow * g.K + kt * kTC + ks * 16 + khalf * 8);
+                        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa), bop, acc[m], 0, 0, 0);
+                    }
+                }
 
-            // next tile into the other plane
-            if (has_next) {
-                const uint32_t np = eplane0 + (cur ^ 1) * kTile;
-                for (uint64_t s = ns0; s < ns1; s += WAVES)
-                    decode_into_plane<K>(s == ns0 ? nseg : load_segment(g, s, lane), (t + 1) * kTile, np,
-                                         g.counts != nullptr, fast, chain, lane);
+                // next tile into the other plane
+                if (has_next) {
+                    const uint32_t np = eplane0 + (cur ^ 1) * kTile;
+                    for (uint64_t s = ns0; s < ns1; s += WAVES)
+                        decode_into_plane<K>(s == ns0 ? nseg : load_segment(g, s, lane), (t + 1) * kTile, np,
+                                             g.counts != nullptr, fast, chain, lane);
+                }
             }
             __syncthreads();
         }
