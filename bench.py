@@ -4,18 +4,19 @@
 Default workload: one Llama-3-8B-shaped decoder layer of synthetic
 N(0, 0.02) BF16 weights (q, k, v, o, gate, up, down: 218,103,808 elements)
 with one codebook for the layer, compressed and resident in HBM.  One step
-decodes all seven matrices, one after another, into one reused BF16 buffer;
-the seven launches are captured once as a HIP graph and replayed.
+decodes all seven matrices in one launch (df11_decode_batch), each into its
+slice of one reused layer-sized BF16 buffer.
 
-Also reported: the same launches issued eagerly, one batched launch per
-layer, the whole 8B-parameter model (226 matrices) per pass, and the fused
-decode+GEMM on up_proj at B in {1, 8, 64, 256}.
+Also reported: the seven matrices one launch each into one reused
+matrix-sized buffer (eager, and replayed as one HIP graph), the whole
+8B-parameter model (226 matrices) per pass, compressed CPU offload, the GPU
+encoder, and the fused decode+GEMM on up_proj at B in {1, 8, 64, 256}.
 
 Prints one JSON line:
   value     decoded BF16 GB/s (2 bytes per element / step time)
   roofline  the decode kernel's algorithmic HBM bytes per launch / its
-            average launch time (HIP events on the launch stream), against
-            the 8 TB/s HBM peak
+            average launch time (HIP events on the launch stream; one launch
+            per step), against the 8 TB/s HBM peak
   cpu_baseline  the CPU oracle's bit-serial decode of the same layer, timed
             on this host (single thread)
 
@@ -449,16 +450,18 @@ def main():
     verify(dts, mats, outbuf)
     log("parity verified on all %d matrices" % len(dts))
 
-    launch_ms, eager_ms = time_decode(dts, outbuf, args.steps, args.warmup)
-    ms_per_step = time_graph(dts, outbuf, args.steps, args.warmup)
-    # after the replays the buffer holds the last matrix of the layer
-    last = outbuf.view(torch.int16)[:mats[-1].size].cpu().numpy().view(np.uint16)
-    if not np.array_equal(last, mats[-1].reshape(-1)):
-        raise SystemExit("graph replay parity check failed")
     alg = [algorithmic_bytes(e) for _, _, e in encs]
-    achieved = (sum(alg) / len(alg)) / (launch_ms.mean() * 1e-3) / 1e9
     compressed = sum(e.compressed_nbytes() for _, _, e in encs)
     stream_bits = sum(e.total_bits for _, _, e in encs)
+
+    # the step: the layer's seven matrices in one launch, each into its own
+    # slice of one reused layer-sized buffer
+    ms_per_step, outs = time_batched(dts, args.steps, args.warmup)
+    for o, m in zip(outs, mats):
+        if not np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), m.reshape(-1)):
+            raise SystemExit("batched parity check failed")
+    del outs
+    achieved = sum(alg) / (ms_per_step * 1e-3) / 1e9
 
     result = {
         "metric": "decoded BF16 GB/s (df11_decode, Llama-3-8B layer)",
@@ -475,10 +478,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "llama3-8b-layer: q,k,v,o,gate,up,down bf16 N(0,0.02), 218,103,808 elements, "
-                        "one codebook, each matrix decoded in its own launch into one reused buffer, "
-                        "the seven launches replayed as one HIP graph",
+                        "one codebook, the seven matrices decoded in one launch (df11_decode_batch), each "
+                        "into its slice of one reused layer-sized buffer",
             "elements": n_total,
-            "launches_per_step": len(dts),
+            "launches_per_step": 1,
             "bits_per_weight": round(8.0 * compressed / n_total, 4),
             "exponent_bits_per_weight": round(stream_bits / n_total, 4),
             "parallelism": "1 GPU",
@@ -492,29 +495,31 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("decode_kernel_llama3_8b_layer.md", DECODE_SOURCES),
             "kernel": "decode_kernel",
+            "algorithmic_bytes_per_launch": int(sum(alg)),
             "algorithmic_bytes_per_element": round(sum(alg) / n_total, 4),
-            "launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
-            "timing": "per matrix, back-to-back launches between two events on the launch stream "
-                      "(queue held busy so the host runs ahead); achieved = mean algorithmic bytes per "
-                      "launch / mean launch duration over the seven matrices",
-        },
-        "eager_layer": {
-            "launches_per_step": len(dts), "ms_per_step": round(eager_ms, 4),
-            "decoded_gbs": round(2.0 * n_total / (eager_ms * 1e-3) / 1e9, 2),
-            "note": "the same seven launches issued from Python one by one",
+            "timing": "events around the timed back-to-back launches on the launch stream; one launch "
+                      "per step, so the average launch duration is the step time",
         },
     }
-    t_batch, outs = time_batched(dts, args.steps, args.warmup)
-    for o, m in zip(outs, mats):
-        if not np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), m.reshape(-1)):
-            raise SystemExit("batched parity check failed")
-    result["batched_layer"] = {
-        "launches_per_step": 1, "ms_per_step": round(t_batch, 4),
-        "decoded_gbs": round(2.0 * n_total / (t_batch * 1e-3) / 1e9, 2),
-        "hbm_frac": round(sum(alg) / (t_batch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "buffer": "one reused layer-sized buffer, each matrix in its own slice",
+    # the same matrices one launch each into one matrix-sized reused buffer
+    launch_ms, eager_ms = time_decode(dts, outbuf, args.steps, args.warmup)
+    graph_ms = time_graph(dts, outbuf, args.steps, args.warmup)
+    # after the replays the buffer holds the last matrix of the layer
+    last = outbuf.view(torch.int16)[:mats[-1].size].cpu().numpy().view(np.uint16)
+    if not np.array_equal(last, mats[-1].reshape(-1)):
+        raise SystemExit("graph replay parity check failed")
+    result["per_matrix_layer"] = {
+        "buffer": "one reused buffer of the largest matrix",
+        "graph": {"launches_per_step": len(dts), "ms_per_step": round(graph_ms, 4),
+                  "decoded_gbs": round(2.0 * n_total / (graph_ms * 1e-3) / 1e9, 2),
+                  "hbm_frac": round(sum(alg) / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "eager": {"launches_per_step": len(dts), "ms_per_step": round(eager_ms, 4),
+                  "decoded_gbs": round(2.0 * n_total / (eager_ms * 1e-3) / 1e9, 2)},
+        "repeated_launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
+        "repeated_launch_note": "each matrix decoded again and again into the same buffer; its 100-200 MB "
+                                "of traffic partly stays in the 256 MB Infinity Cache, so these are warm-cache "
+                                "kernel times",
     }
-    del outs
     if not args.no_model:
         result["model_pass"] = model_pass(args.steps, args.warmup, args.seed)
         result["offload_pass"] = offload_pass(args.steps, args.warmup, args.seed)
