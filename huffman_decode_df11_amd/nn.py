@@ -46,9 +46,14 @@ def _bits(weight) -> np.ndarray:
 class DF11Linear(torch.nn.Module):
     """A linear layer y = x W^T + b with W [out_features, in_features] held
     compressed.  mode "fused" (needs out % 32 == 0 and in % 512 == 0) runs
-    df11_decode_gemm for batches of 1..256 rows and decode + matmul above;
-    mode "decode" always decodes into the shared buffer and calls
-    torch.matmul.  "auto" picks "fused" when the shape allows it."""
+    df11_decode_gemm for up to fused_max_rows rows of x (default 96: at
+    larger batches decoding W once and running the library GEMM is faster on
+    MI355X, since the fused kernel re-reads x for every 32-row block of W)
+    and decode + matmul above; mode "decode" always decodes into the shared
+    buffer and calls torch.matmul.  "auto" picks "fused" when the shape
+    allows it."""
+
+    fused_max_rows = 96
 
     def __init__(self, weight, bias: Optional[torch.Tensor] = None, mode: str = "auto", device="cuda",
                  codebook=None):
@@ -87,7 +92,7 @@ class DF11Linear(torch.nn.Module):
         shape = x.shape
         x2 = x.reshape(-1, self.in_features).to(torch.bfloat16).contiguous()
         B = x2.shape[0]
-        if self.mode == "fused" and 1 <= B <= 256:
+        if self.mode == "fused" and 1 <= B <= min(256, self.fused_max_rows):
             y = api.decode_gemm(self.weight_df11, x2)
             if self.bias is not None:
                 y = y + self.bias.float()
