@@ -11,12 +11,13 @@
 // Mapping to gfx950: one 64-lane wavefront per segment, so the prefix sum is
 // a wavefront scan and no workgroup barrier sits on the decode path.  A
 // workgroup of WAVES waves stages the tables in LDS once; each wave then
-// walks its segments with the next segment's stream words and this
-// segment's sign+mantissa bytes already in flight, so global-memory latency
-// overlaps the decode.  A lane's stream words stay in registers.  Exponents are staged in LDS and merged
-// with the sign+mantissa bytes in 16-element groups: 16-byte loads, 32-byte
-// BF16 stores; the at most 30 elements of a segment's two ragged groups are
-// written one per lane.
+// walks its segments with the next segment's stream words, gaps and code
+// counts and this segment's sign+mantissa bytes already in flight, so
+// global-memory latency overlaps the decode.  A lane's stream words stay in
+// registers.  Exponents are staged in LDS and merged with the sign+mantissa
+// bytes in 16-element groups: 16-byte loads, 32-byte BF16 stores; the at
+// most 30 elements of a segment's two ragged groups are written one per
+// lane.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -446,13 +447,15 @@ int run_shape(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, u
 // choice whose exponent staging stays in the first 64 KB of LDS (the emit
 // loop keeps byte addresses in 16 bits), the waves that can be resident per
 // CU.  A tensor with more segments than all CUs can hold at once takes the
-// choice with the most resident waves; a smaller one takes the choice that
+// choice whose resident waves per CU are closest above 24 (or the most, if
+// none reaches 24); a smaller one takes the choice that
 // puts the fewest waves on the busiest CU (ties: larger workgroups, fewer
 // table copies), since each wave's segment is then latency-bound.
 // DF11_DECODE_WAVES overrides the choice for tuning.  Occupancy answers
 // depend only on (device, K, staging bytes, table count) and the last few
 // are kept so that a sequence of launches does not repeat the queries.
 constexpr int kNumChoices = sizeof(kWaveChoices) / sizeof(kWaveChoices[0]);
+constexpr int kSaturatedWaves = 24;
 struct ShapeKey {
     int dev, k;
     uint32_t stg, n_tables;
@@ -509,7 +512,17 @@ int pick_waves(const int res[kNumChoices], uint64_t nseg, uint64_t cus)
         }
         if (best < 0 || res[i] > res[best]) best = i;
     }
-    if (forced || best < 0 || nseg >= cus * (uint64_t)res[best]) return best;
+    if (forced || best < 0) return best;
+    if (nseg >= cus * (uint64_t)res[best]) {
+        // several rounds: 24 resident waves per CU already keep HBM busy
+        // (more waves measured slower on a whole layer in one launch, with
+        // more requests contending); take the shape closest above that,
+        // larger workgroups (fewer table copies) on ties
+        int pick = -1;
+        for (int i = 0; i < kNumChoices; i++)
+            if (res[i] >= kSaturatedWaves && (pick < 0 || res[i] <= res[pick])) pick = i;
+        return pick >= 0 ? pick : best;
+    }
     uint64_t best_load = ~0ull;
     for (int i = 0; i < kNumChoices; i++) {
         if (!res[i]) continue;

@@ -3,9 +3,11 @@
 // One 64-lane wavefront decodes one segment of the exponent stream:
 //   load    every lane holds its chunk of four stream words plus the next
 //           chunk's first word (160 bits) in registers;
-//   locate  every lane counts the codes that start in its chunk ([P3]
-//           "DFloat11重新定义LLM无损压缩的技术边界" 2.2 Phase 1), reading the
-//           multi-code table and, for long codes, the hierarchical tables;
+//   locate  every lane learns how many codes start in its chunk ([P3]
+//           "DFloat11重新定义LLM无损压缩的技术边界" 2.2 Phase 1): the count
+//           stored with the chunk's gap, or, for an encoding without
+//           counts, by walking the chunk through the multi-code table and,
+//           for long codes, the hierarchical tables (count_codes);
 //   scan    a wavefront prefix sum turns counts into output positions
 //           ([P3] 2.2 prefix sum);
 //   emit    every lane decodes its chunk again and writes each exponent
