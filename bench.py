@@ -323,26 +323,34 @@ def encode_rate(seed: int = 0):
             "host_one_thread_ms": round(t_host * 1e3, 1), "identical_to_host_encoder": bool(same)}
 
 
-def fused_up_proj(steps: int, warmup: int, seed: int = 0):
+def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8):
     """df11_decode_gemm on the up_proj weight (14336 x 4096) for B in
-    {1, 8, 64, 256}, next to torch.matmul on the decoded BF16 weight."""
+    {1, 8, 64, 256}, next to torch.matmul on the BF16 weight and to the
+    unfused path (df11_decode of a row-major encoding, then torch.matmul).
+    Every variant cycles through `copies` copies of its weight (> 512 MB in
+    all), so weights come from HBM and not from the 256 MB Infinity Cache;
+    x and y stay small and warm, as activations do."""
     import torch
     from huffman_decode_df11_amd import api, synth
     N, K = 14336, 4096
     W = synth.normal_bf16(N * K, 0.02, seed=seed, index=5, count=7).reshape(N, K)
     enc = api.encode(W, layout=api.gemm_layout(N, K))
-    dt = enc.to("cuda")
-    wt = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
+    enc_rm = api.encode(W, codebook=enc.codebook)
+    dts = [enc.to("cuda") for _ in range(copies)]
+    dts_rm = [enc_rm.to("cuda") for _ in range(copies)]
+    w0 = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
+    wts = [w0] + [w0.clone() for _ in range(copies - 1)]
+    wbuf = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
     w_bytes = enc.compressed_nbytes()
 
     def timeit(f):
-        for _ in range(warmup):
-            f()
+        for i in range(warmup):
+            f(i % copies)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(steps):
-            f()
+        for i in range(steps):
+            f(i % copies)
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
@@ -352,14 +360,15 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0):
         X = synth.activations_bf16(B, K, seed=1)
         x = torch.from_numpy(X.view(np.int16)).cuda().view(torch.bfloat16)
         y = torch.empty(B, N, dtype=torch.float32, device="cuda")
-        api.decode_gemm(dt, x, out=y)
-        yt = x.float() @ wt.float().T
+        api.decode_gemm(dts[0], x, out=y)
+        yt = x.float() @ w0.float().T
         torch.cuda.synchronize()
         rel = float((y - yt).norm() / yt.norm())
         if not rel < 2e-3:
             raise SystemExit("fused decode+GEMM parity failed at B=%d (rel %.3g)" % (B, rel))
-        t_fused = timeit(lambda: api.decode_gemm(dt, x, out=y))
-        t_plain = timeit(lambda: torch.matmul(x, wt.T))
+        t_fused = timeit(lambda i: api.decode_gemm(dts[i], x, out=y))
+        t_plain = timeit(lambda i: torch.matmul(x, wts[i].T))
+        t_unfused = timeit(lambda i: torch.matmul(x, api.decode(dts_rm[i], out=wbuf).T))
         flops = 2.0 * B * N * K
         alg = w_bytes + B * K * 2 + B * N * 4
         mfma_bound = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > alg / (HBM_PEAK_GBS * 1e9)
@@ -367,6 +376,7 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0):
             "fused_ms": round(t_fused, 4),
             "fused_tflops": round(flops / t_fused / 1e9, 2),
             "plain_bf16_matmul_ms": round(t_plain, 4),
+            "decode_then_matmul_ms": round(t_unfused, 4),
             "fused_over_plain": round(t_fused / t_plain, 3),
             "rel_err_vs_fp32": rel,
             "roofline": ({"bound": "mfma", "achieved": round(flops / t_fused / 1e9, 2),
@@ -376,8 +386,28 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0):
                          {"bound": "hbm", "achieved": round(alg / t_fused / 1e6, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(alg / t_fused / 1e6 / HBM_PEAK_GBS, 4)}),
         }
-    return {"workload": "up_proj 14336x4096 bf16 N(0,0.02), x[B,4096] N(0,1), y float32",
+    return {"workload": "up_proj 14336x4096 bf16 N(0,0.02), x[B,4096] N(0,1), y float32; each variant cycles "
+                        "through %d copies of its weight" % copies,
             "compressed_weight_bytes": w_bytes, "by_batch": rows}
+
+
+def copy_peak(nbytes: int = 512 << 20, reps: int = 10):
+    """Device-to-device copy rate (read + write bytes per second) of a
+    buffer larger than the Infinity Cache: the practical HBM ceiling."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
 def verify(dts, mats, outbuf):
@@ -395,27 +425,43 @@ def cpu_baseline_layer(mats, budget_s: float = 20.0):
     """The oracle's serial decode on the host, over the layer's matrices in
     order until the time budget is used (at least one matrix)."""
     from oracle import oracle as orc
-    from huffman_decode_df11_amd import api
     hist = None
     for m in mats:
         hist = orc.histogram(m) if hist is None else hist + orc.histogram(m)
     ln = orc.code_lengths(hist, 32)
-    elems, secs, names = 0, 0.0, 0
-    for m in mats:
-        ref = orc.encode(m, lengths=ln)
-        t0 = time.perf_counter()
-        out = orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln)
-        secs += time.perf_counter() - t0
-        elems += m.size
-        names += 1
-        if not np.array_equal(out, m.reshape(-1)):
-            raise SystemExit("oracle round trip failed")
-        del ref, out
-        if secs >= budget_s:
-            break
+    refs = [orc.encode(m, lengths=ln) for m in mats]
+    # one core: pin the decode loop to the first CPU this process may use
+    allowed = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
+    if allowed:
+        os.sched_setaffinity(0, {allowed[0]})
+    elems, secs, passes = 0, 0.0, 0
+    try:
+        while passes == 0 or secs < budget_s:
+            for m, ref in zip(mats, refs):
+                t0 = time.perf_counter()
+                out = orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln)
+                secs += time.perf_counter() - t0
+                elems += m.size
+                if passes == 0 and not np.array_equal(out, m.reshape(-1)):
+                    raise SystemExit("oracle round trip failed")
+                del out
+            passes += 1
+    finally:
+        if allowed:
+            os.sched_setaffinity(0, set(allowed))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(2.0 * elems / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "bit-serial oracle decode of the first %d of the layer's 7 matrices "
-                      "(%d elements, %.1f s), one host thread" % (names, elems, secs)}
+            "sample": "bit-serial oracle decode of the layer's 7 matrices, %d passes (%d elements, %.1f s), "
+                      "one host thread pinned to CPU %s of %d allowed (%s)" % (
+                          passes, elems, secs, allowed[0] if allowed else "?", len(allowed), cpu)}
 
 
 def main():
@@ -501,6 +547,9 @@ def main():
                       "per step, so the average launch duration is the step time",
         },
     }
+    copy_gbs = copy_peak()
+    result["roofline"]["copy_peak_gbs"] = round(copy_gbs, 1)
+    result["roofline"]["frac_of_copy_peak"] = round(achieved / copy_gbs, 4)
     # the same matrices one launch each into one matrix-sized reused buffer
     launch_ms, eager_ms = time_decode(dts, outbuf, args.steps, args.warmup)
     graph_ms = time_graph(dts, outbuf, args.steps, args.warmup)
