@@ -14,10 +14,16 @@
 // walks its segments with the next segment's stream words, gaps and code
 // counts and this segment's sign+mantissa bytes already in flight, so
 // global-memory latency overlaps the decode.  A lane's stream words stay in
-// registers.  Exponents are staged in LDS and merged with the sign+mantissa
-// bytes in 16-element groups: 16-byte loads, 32-byte BF16 stores; the at
-// most 30 elements of a segment's two ragged groups are written one per
-// lane.
+// registers; segment records come through scalar loads.  Exponents are
+// staged in LDS and merged with the sign+mantissa bytes in 8-element units,
+// lane l of a round taking unit l, so each wave-wide store writes one
+// contiguous kilobyte of BF16; the at most 14 elements of a segment's two
+// ragged units are written one per lane.  The whole layer decode is bound by
+// HBM traffic (the decode itself hides behind it), so the loop is ordered
+// for the memory system: loads that the next step needs are issued before
+// stores that it need not wait for (loads and stores share one completion
+// counter), and launches whose output overflows the last-level cache
+// stream it.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -35,7 +41,7 @@ namespace {
 constexpr uint32_t kChunkBytes = 16;
 constexpr uint32_t kChunkBits = 8 * kChunkBytes;
 constexpr uint32_t kSegWords = 64 * kChunkBytes / 4;
-constexpr int kPrefetchRounds = 3;
+constexpr int kPrefetchRounds = 5;   // 8-element units per lane prefetched before the decode
 
 struct ViewArgs {
     const uint32_t *words;
@@ -58,11 +64,41 @@ struct BatchArgs {
     ViewArgs v[kMaxBatch];
     uint64_t seg_begin[kMaxBatch + 1];
     uint32_t count;
+    uint32_t stream;          // nonzero: streaming (nontemporal) sign+mantissa loads and BF16 stores
 };
 
-__device__ __forceinline__ uint32_t view_of(const BatchArgs &b, uint64_t s)
+// A launch whose BF16 output is larger than the last-level cache (the
+// 256 MB Infinity Cache) cannot leave it there for the matmul that follows,
+// so it streams: sign+mantissa bytes are read and BF16 written with
+// nontemporal accesses, which keeps the write-allocate and eviction of data
+// used once out of the cache.  Smaller outputs are written normally and are
+// still cache-resident when the consumer reads them.
+constexpr uint64_t kStreamOutBytes = 256ull << 20;
+
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u32g __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 load_sm8(const uint8_t *p, bool stream)
 {
-    uint32_t i = 0;
+    if (stream) {
+        const v2u32 t = __builtin_nontemporal_load(reinterpret_cast<const v2u32 *>(p));
+        return make_uint2(t.x, t.y);
+    }
+    return *reinterpret_cast<const uint2 *>(p);
+}
+
+__device__ __forceinline__ void store_bf16x8(uint16_t *p, uint4 v, bool stream)
+{
+    if (stream) {
+        const v4u32g t = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<v4u32g *>(p));
+    } else {
+        *reinterpret_cast<uint4 *>(p) = v;
+    }
+}
+
+__device__ __forceinline__ uint32_t view_of(const BatchArgs &b, uint64_t s, uint32_t i = 0)
+{
     while (i + 1 < b.count && b.seg_begin[i + 1] <= s) i++;
     return i;
 }
@@ -93,12 +129,24 @@ __device__ __forceinline__ uint64_t out_index(const ViewArgs &v, uint64_t g)
     return (rb * v.tr + r) * v.cols + cb * v.tc + c;
 }
 
-// Everything a wave needs from global memory to start a segment.
+// Segment records are read-only for the whole launch: reading them through
+// the constant address space lets the wave fetch them with scalar loads,
+// which are tracked apart from the vector loads and stores.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T *as_const(const T *p)
+{
+    return (const __attribute__((address_space(4))) T *)p;
+}
+
+// Everything a wave needs from global memory to start a segment.  The
+// vector part (stream words, gap, stored count) is always loaded from valid
+// addresses, so the loads carry no condition and are first waited for where
+// the decode uses them.
 struct SegLoad {
     uint4 own;          // this lane's 4 stream words
     uint32_t next;      // the following word (look-ahead)
     uint32_t gap;
-    uint32_t count;     // codes that start in this lane's chunk, when the view stores counts
+    uint32_t count;     // codes that start in this lane's chunk (meaningful when the view stores counts)
     uint32_t nbits;
     uint64_t g0, g1;
 };
@@ -110,17 +158,19 @@ __device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, u
     L.own = *reinterpret_cast<const uint4 *>(w);
     L.next = w[4];
     L.gap = v.gaps[s * 64 + lane];
-    L.count = v.counts ? v.counts[s * 64 + lane] : 0u;
-    L.g0 = v.segs[s].elem_off;
-    L.g1 = v.segs[s + 1].elem_off;
-    L.nbits = v.segs[s].nbits;
+    const uint8_t *cp = v.counts ? v.counts : v.gaps;
+    L.count = cp[s * 64 + lane];
+    const auto *rec = as_const(v.segs + s);
+    L.g0 = rec[0].elem_off;
+    L.g1 = rec[1].elem_off;
+    L.nbits = rec[0].nbits;
     return L;
 }
 
 // ------------------------------------------------------------ one segment
 struct SegPlan {
-    uint64_t g0, g1, gbase;   // elements [g0, g1); 16-element groups from gbase
-    uint32_t head, ngroups;
+    uint64_t g0, g1, gbase;   // elements [g0, g1); 8-element units from gbase
+    uint32_t head, nunits;
     bool valid;               // records consistent and the segment fits the staging
 };
 
@@ -129,25 +179,25 @@ __device__ __forceinline__ SegPlan plan_segment(const SegLoad &cur, uint64_t n, 
     SegPlan p;
     p.g0 = cur.g0;
     p.g1 = cur.g1;
-    p.gbase = p.g0 & ~15ull;
-    p.head = (uint32_t)(p.g0 & 15);
+    p.gbase = p.g0 & ~7ull;
+    p.head = (uint32_t)(p.g0 & 7);
     p.valid = p.g1 <= n && p.g1 >= p.g0 && (uint64_t)p.head + (p.g1 - p.g0) + 32 <= stg_bytes;
-    p.ngroups = p.valid ? (uint32_t)((((p.g1 + 15) & ~15ull) - p.gbase) >> 4) : 0u;
+    p.nunits = p.valid ? (uint32_t)((((p.g1 + 7) & ~7ull) - p.gbase) >> 3) : 0u;
     return p;
 }
 
 // the segment's sign+mantissa bytes for the first kPrefetchRounds rounds of
-// groups.  Lanes past the last group load the last group again (an address
+// units.  Lanes past the last unit load the last unit again (an address
 // that is always inside the array), so no value has to be selected and the
 // loads stay in flight during the decode.
-__device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm, uint32_t lane,
-                                            uint4 (&smp)[kPrefetchRounds])
+__device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm, uint32_t lane, bool stream,
+                                            uint2 (&smp)[kPrefetchRounds])
 {
-    const uint32_t last = p.ngroups ? p.ngroups - 1 : 0u;
-    const uint64_t base = p.ngroups ? p.gbase : 0ull;
+    const uint32_t last = p.nunits ? p.nunits - 1 : 0u;
+    const uint64_t base = p.nunits ? p.gbase : 0ull;
 #pragma unroll
     for (int r = 0; r < kPrefetchRounds; r++)
-        smp[r] = *reinterpret_cast<const uint4 *>(sm + base + 16ull * min(lane + 64u * r, last));
+        smp[r] = load_sm8(sm + base + 8ull * min(lane + 64u * r, last), stream);
 }
 
 // Locate, scan and emit one segment into the wave's staging (exponent of
@@ -179,7 +229,6 @@ __device__ __forceinline__ bool stage_segment(const SegLoad &cur, const SegPlan 
 struct ViewOut {
     const ViewArgs &v;
     __device__ __forceinline__ uint16_t *at(uint64_t g) const { return v.out + out_index(v, g); }
-    __device__ __forceinline__ bool split8() const { return v.kc != 0; }
 };
 
 // Output placement of element g of row r into row i of a gather: out_row + (g - r * cols).
@@ -187,51 +236,66 @@ struct RowOut {
     uint16_t *out_row;
     uint64_t row_start;
     __device__ __forceinline__ uint16_t *at(uint64_t g) const { return out_row + (g - row_start); }
-    __device__ __forceinline__ bool split8() const { return false; }
 };
 
-// One 16-element group gi of the segment: staged exponents + sign+mantissa
-// bytes smv -> BF16, stored when the group lies inside [lo, hi).
+// One 8-element unit ui of the segment: staged exponents + sign+mantissa
+// bytes smv -> BF16, one 16-byte store when the unit lies inside [lo, hi).
+// Lane l of a round takes unit 64r + l, so every store instruction of the
+// wave writes one contiguous kilobyte (an 8-element unit never crosses a
+// row of any output order: tile and column-group widths are multiples of 8).
 template <class Out>
-__device__ __forceinline__ void merge_group(const SegPlan &p, uint64_t lo, uint64_t hi, uint32_t gi, uint4 smv,
-                                            const Out &out, uint32_t stg)
+__device__ __forceinline__ void merge_unit(const SegPlan &p, uint64_t lo, uint64_t hi, uint32_t ui, uint2 smv,
+                                           const Out &out, uint32_t stg, bool stream)
 {
-    const uint64_t gs = p.gbase + 16ull * gi;
-    if (gi < p.ngroups && gs >= lo && gs + 16 <= hi) {
-        const uint4 rx = ld128(stg + 16 * gi);
+    const uint64_t gs = p.gbase + 8ull * ui;
+    if (ui < p.nunits && gs >= lo && gs + 8 <= hi) {
+        const uint2 rx = ld64(stg + 8 * ui);
         const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
-        const uint2 c = assemble4(smv.z, rx.z), d = assemble4(smv.w, rx.w);
-        // contiguous, or two 8-element runs of different rows for column groups
-        uint4 *dst0 = reinterpret_cast<uint4 *>(out.at(gs));
-        uint4 *dst1 = out.split8() ? reinterpret_cast<uint4 *>(out.at(gs + 8)) : dst0 + 1;
-        dst0[0] = make_uint4(a.x, a.y, b.x, b.y);
-        dst1[0] = make_uint4(c.x, c.y, d.x, d.y);
+        store_bf16x8(out.at(gs), make_uint4(a.x, a.y, b.x, b.y), stream);
     }
 }
 
-// Merge the staged exponents of elements [lo, hi) (inside the segment) with
-// their sign+mantissa bytes and store BF16: whole 16-element groups with
-// 16-byte accesses (the first rounds from the prefetched bytes), the ragged
-// ends one element per lane (lanes 0..15 the head group, lanes 16..31 the
-// tail group).
-template <class Out>
-__device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint64_t hi, const uint4 (&smp)[kPrefetchRounds],
-                                            const uint8_t *sm, const Out &out, uint32_t stg, uint32_t lane)
+// The ragged ends of [lo, hi): the elements before the first and after the
+// last whole 8-element unit, one per lane (lanes 0..7 the head, lanes
+// 8..15 the tail).
+struct RaggedLane {
+    uint64_t g;
+    bool act;
+};
+
+__device__ __forceinline__ RaggedLane ragged_lane(uint64_t lo, uint64_t hi, uint32_t lane)
 {
-#pragma unroll
-    for (int r = 0; r < kPrefetchRounds; r++) merge_group(p, lo, hi, lane + 64u * r, smp[r], out, stg);
-    for (uint32_t r = kPrefetchRounds; 64u * r < p.ngroups; r++) {
-        const uint32_t gi = lane + 64u * r;
-        const uint4 smv = gi < p.ngroups ? *reinterpret_cast<const uint4 *>(sm + p.gbase + 16ull * gi) : make_uint4(0, 0, 0, 0);
-        merge_group(p, lo, hi, gi, smv, out, stg);
+    const uint64_t hend = min((lo + 7) & ~7ull, hi);
+    const uint64_t tstart = max(hi & ~7ull, hend);
+    RaggedLane r;
+    r.g = lane < 8 ? lo + lane : tstart + (lane - 8);
+    r.act = lane < 8 ? r.g < hend : (lane < 16 && r.g < hi);
+    return r;
+}
+
+// Merge the staged exponents of elements [lo, hi) (inside the segment) with
+// their sign+mantissa bytes and store BF16: whole 8-element units with
+// 16-byte stores (the first rounds from the prefetched bytes), the ragged
+// ends one element per lane from rag_sm, the lane's ragged element's
+// sign+mantissa byte (loaded by the caller).
+template <class Out>
+__device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint64_t hi, const uint2 (&smp)[kPrefetchRounds],
+                                            uint32_t rag_sm, const uint8_t *sm, const Out &out, uint32_t stg, uint32_t lane,
+                                            bool stream)
+{
+    // the ragged ends first: their store then waits only for loads issued
+    // before the decode, not for the unit stores below
+    const RaggedLane rg = ragged_lane(lo, hi, lane);
+    if (rg.act) {
+        const uint32_t rx = *(const lds_u8 *)(size_t)(stg + (uint32_t)(rg.g - p.gbase));
+        *out.at(rg.g) = assemble1(rag_sm, rx);
     }
-    const uint64_t hend = min((lo + 15) & ~15ull, hi);
-    const uint64_t tstart = max(hi & ~15ull, hend);
-    const uint64_t g = lane < 16 ? lo + lane : tstart + (lane - 16);
-    const bool act = lane < 16 ? g < hend : (lane < 32 && g < hi);
-    if (act) {
-        const uint32_t rx = *(const lds_u8 *)(size_t)(stg + (uint32_t)(g - p.gbase));
-        *out.at(g) = assemble1(sm[g], rx);
+#pragma unroll
+    for (int r = 0; r < kPrefetchRounds; r++) merge_unit(p, lo, hi, lane + 64u * r, smp[r], out, stg, stream);
+    for (uint32_t r = kPrefetchRounds; 64u * r < p.nunits; r++) {
+        const uint32_t ui = lane + 64u * r;
+        const uint2 smv = ui < p.nunits ? load_sm8(sm + p.gbase + 8ull * ui, stream) : make_uint2(0, 0);
+        merge_unit(p, lo, hi, ui, smv, out, stg, stream);
     }
 }
 
@@ -252,6 +316,7 @@ decode_kernel(BatchArgs b, TableArgs t)
     const uint64_t n_total = b.seg_begin[b.count];
     uint64_t s = (uint64_t)blockIdx.x * WAVES + wave;
     const uint64_t stride = (uint64_t)gridDim.x * WAVES;
+    const bool stream = b.stream != 0;
     uint32_t vi = 0;
     SegLoad nx{};
     if (s < n_total) {
@@ -265,16 +330,21 @@ decode_kernel(BatchArgs b, TableArgs t)
         const SegLoad cur = nx;
         const ViewArgs &v = b.v[vi];
         const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
-        uint4 smp[kPrefetchRounds];
-        prefetch_sm(p, v.sm, lane, smp);
-        // the next segment's stream words and records
+        // The next segment's words and records first (the last segment
+        // loads itself again), then this segment's sign+mantissa bytes:
+        // the merge waits for the latter, which leaves the former complete
+        // before the next decode, without waiting on this merge's stores.
         const uint64_t s_next = s + stride;
         const bool more = s_next < n_total;
-        const uint32_t vi_next = more ? view_of(b, s_next) : vi;
-        if (more) nx = load_segment(b.v[vi_next], s_next - b.seg_begin[vi_next], lane);
+        const uint32_t vi_next = more ? view_of(b, s_next, vi) : vi;
+        nx = load_segment(b.v[vi_next], (more ? s_next : s) - b.seg_begin[vi_next], lane);
+        uint2 smp[kPrefetchRounds];
+        prefetch_sm(p, v.sm, lane, stream, smp);
+        const RaggedLane rg = ragged_lane(p.g0, p.g1, lane);
+        const uint32_t rag_sm = v.sm[p.valid && rg.act ? rg.g : 0];
 
         if (p.valid && stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane))
-            merge_range(p, p.g0, p.g1, smp, v.sm, ViewOut{v}, stg, lane);
+            merge_range(p, p.g0, p.g1, smp, rag_sm, v.sm, ViewOut{v}, stg, lane, stream);
         wave_lds_sync();   // the staging is reused by the next segment
         if (!more) break;
         s = s_next;
@@ -322,10 +392,13 @@ decode_rows_kernel(RowArgs a, TableArgs t)
             const SegLoad cur = load_segment(v, s, lane);
             if (cur.g0 >= hi) break;
             const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
-            uint4 smp[kPrefetchRounds];
-            prefetch_sm(p, v.sm, lane, smp);
+            uint2 smp[kPrefetchRounds];
+            prefetch_sm(p, v.sm, lane, false, smp);
+            const uint64_t mlo = max(lo, p.g0), mhi = min(hi, p.g1);
+            const RaggedLane rg = ragged_lane(mlo, mhi, lane);
+            const uint32_t rag_sm = v.sm[p.valid && mlo < mhi && rg.act ? rg.g : 0];
             if (p.valid && cur.g1 > lo && stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane))
-                merge_range(p, max(lo, p.g0), min(hi, p.g1), smp, v.sm, out, stg, lane);
+                merge_range(p, mlo, mhi, smp, rag_sm, v.sm, out, stg, lane, false);
             wave_lds_sync();
         }
     }
@@ -558,6 +631,7 @@ int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, 
 {
     BatchArgs b{};
     uint32_t stg = 0;
+    uint64_t out_bytes = 0;
     const df11_view *v0 = nullptr;
     for (uint32_t i = 0; i < count; i++) {
         const df11_view *v = &views[i];
@@ -571,9 +645,11 @@ int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, 
         b.v[b.count] = make_args(v, outs[i]);
         b.seg_begin[b.count + 1] = b.seg_begin[b.count] + v->n_segments;
         b.count++;
+        out_bytes += 2 * v->n;
         stg = std::max(stg, staging_bytes(v));
     }
     if (!b.count || !b.seg_begin[b.count]) return DF11_OK;
+    b.stream = out_bytes > kStreamOutBytes;
     TableArgs t{v0->chain, v0->fast, (uint32_t)v0->n_chain, stg};
     switch (v0->fast_bits) {
     case 8: return launch_decode<8>(b, t, v0, st);

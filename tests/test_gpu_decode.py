@@ -216,6 +216,28 @@ def test_batch_llama_layer_one_launch():
         assert (got[m.size:] == 0x5555).all(), name
 
 
+def test_batch_streaming_launch_with_ragged_views():
+    """A launch whose output exceeds the last-level cache takes the streaming
+    (nontemporal) loads and stores: a 135M-element tensor and ragged small
+    ones in one batch, each bit-exact with its neighbours untouched."""
+    sizes = [1, 135_000_001, 17, 1_000_003]
+    tensors = [synth.normal_bf16(n, 0.02, seed=300 + i) for i, n in enumerate(sizes)]
+    hist = None
+    for t in tensors:
+        hist = api.hist_accumulate(t, hist)
+    cb = api.build_codebook(hist)
+    dts = [api.encode(t, codebook=cb).to("cuda") for t in tensors]
+    assert 2 * sum(sizes) > 256 << 20
+    _say("case batch streaming", sizes)
+    outs = [torch.full((t.size + 16,), 0x5555, dtype=torch.int16, device="cuda") for t in tensors]
+    api.decode_batch(dts, outs=[o.view(torch.bfloat16) for o in outs])
+    torch.cuda.synchronize()
+    for t, o in zip(tensors, outs):
+        got = _to_bits(o)
+        assert np.array_equal(got[:t.size], t)
+        assert (got[t.size:] == 0x5555).all()
+
+
 def test_batch_many_small_and_empty():
     """More views than one launch takes (16), ragged sizes and an empty one."""
     rng = np.random.default_rng(7)
