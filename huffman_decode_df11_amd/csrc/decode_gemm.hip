@@ -65,6 +65,8 @@ struct GemmArgs {
     uint32_t n_rowblocks;    // N / 32
     uint32_t split;          // K ranges per row block; > 1: y accumulated atomically
     uint32_t tiles_per_split;
+    uint32_t parts;          // segment-parallel form: segment ranges per row block (> 1: y accumulated atomically)
+    uint32_t stg_bytes;      // segment-parallel form: exponent staging per wave
     uint64_t n_segments;
 };
 
@@ -74,6 +76,18 @@ struct SegLoad {
     uint64_t g0, g1;
 };
 
+// Segment records and tile starts are read-only for the launch: read through
+// the constant address space they become scalar loads, tracked apart from
+// the vector loads.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T *as_const(const T *p)
+{
+    return (const __attribute__((address_space(4))) T *)p;
+}
+
+// The vector part is loaded unconditionally (the count from the gaps array
+// when the view stores no counts), so no load carries a condition and each
+// is first waited for where the decode uses it.
 __device__ __forceinline__ SegLoad load_segment(const GemmArgs &g, uint64_t s, uint32_t lane)
 {
     SegLoad L;
@@ -81,10 +95,12 @@ __device__ __forceinline__ SegLoad load_segment(const GemmArgs &g, uint64_t s, u
     L.own = *reinterpret_cast<const uint4 *>(w);
     L.next = w[4];
     L.gap = g.gaps[s * 64 + lane];
-    L.count = g.counts ? g.counts[s * 64 + lane] : 0u;
-    L.g0 = g.segs[s].elem_off;
-    L.g1 = g.segs[s + 1].elem_off;
-    L.nbits = g.segs[s].nbits;
+    const uint8_t *cp = g.counts ? g.counts : g.gaps;
+    L.count = cp[s * 64 + lane];
+    const auto *rec = as_const(g.segs + s);
+    L.g0 = rec[0].elem_off;
+    L.g1 = rec[1].elem_off;
+    L.nbits = rec[0].nbits;
     return L;
 }
 
@@ -278,6 +294,174 @@ decode_gemm_kernel(GemmArgs g)
     }
 }
 
+
+// ---------------------------------------------------------------- B <= 32
+// Segment-parallel form for one batch tile.  The tile-synchronous kernel
+// above decodes a weight tile (~6 segments) per step with a barrier between
+// steps, so a workgroup waits for one segment's decode latency per 16K
+// weights.  Here every wave walks its own run of segments of one row block,
+// like the plain decode: the next segment's words and this segment's
+// sign+mantissa bytes and x operands are in flight during the decode, and
+// nothing waits on a barrier until the row block's partial sums are
+// reduced.  A segment's elements are taken in rounds of 64 units of 8
+// (aligned to 512 elements of the tile, i.e. to one 16-column k-step): in
+// the 8-column-group tile order, unit u of a tile is row u % 32, columns
+// 8 * (u / 32) .. + 7, so a round is exactly the B operand of one
+// v_mfma_f32_32x32x16_bf16 (lanes 0..31 the even column group, 32..63 the
+// odd one).  Elements of the round outside the segment are masked to zero,
+// so the neighbouring segments that share a round add their own parts.
+constexpr int kSegRounds = 4;   // rounds whose operands are loaded before the decode
+
+// byte mask of elements [first, last) of an 8-element unit
+__device__ __forceinline__ uint2 unit_mask(int first, int last)
+{
+    first = max(first, 0);
+    last = min(last, 8);
+    if (first >= last) return make_uint2(0u, 0u);
+    const uint64_t m = (~0ull << (8 * first)) & (~0ull >> (64 - 8 * last));
+    return make_uint2((uint32_t)m, (uint32_t)(m >> 32));
+}
+
+template <int K>
+__device__ __forceinline__ bool stage_seg(const SegLoad &L, bool stored, uint32_t dst, uint32_t fast,
+                                          uint32_t chain, uint32_t lane)
+{
+    const Window win = make_window(L.own, L.next, L.gap);
+    uint32_t cnt = L.count;
+    if (!stored) {
+        const uint32_t c0 = lane * kChunkBits;
+        const uint32_t end = L.nbits > c0 ? min(kChunkBits, L.nbits - c0) : 0u;
+        cnt = L.gap < end ? count_codes<K>(win, fast, chain, L.gap, end) : 0u;
+    }
+    uint32_t total;
+    const uint32_t excl = wave_exclusive_scan(cnt, &total);
+    if (total != (uint32_t)(L.g1 - L.g0)) return false;
+    emit_codes<K>(win, fast, chain, dst + excl, cnt);
+    wave_lds_sync();
+    return true;
+}
+
+template <int K, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+decode_gemm_seg_kernel(GemmArgs g)
+{
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = lane_id();
+    // [guard][staging: WAVES x stg_bytes, also the reduction buffer][tables]
+    const uint32_t area = lds0 + 16;
+    const uint32_t stg = area + wave * g.stg_bytes;
+    const uint32_t fast = area + WAVES * g.stg_bytes;
+    const uint32_t chain = fast + (8u << K);
+    stage_tables<K, WAVES * 64>(fast, chain, g.fast, g.chain, g.n_chain);
+    __syncthreads();
+
+    const uint32_t n_l = lane & 31, khalf = lane >> 5;
+    const bool x_row = n_l < g.B;
+    const bool stored = g.counts != nullptr;
+    const uint64_t n_elems = (uint64_t)g.N * g.K;
+    const uint32_t n_units = g.n_rowblocks * g.parts;
+    for (uint32_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+        const uint32_t rb = unit / g.parts, part = unit - rb * g.parts;
+        const auto *bs = as_const(g.block_seg);
+        const uint64_t S0 = min(bs[(uint64_t)rb * g.tiles_per_row], g.n_segments);
+        const uint64_t S1 = min(bs[(uint64_t)(rb + 1) * g.tiles_per_row], g.n_segments);
+        const uint64_t len = S1 > S0 ? (S1 - S0 + g.parts - 1) / g.parts : 0;
+        const uint64_t s_begin = S0 + part * len, s_end = min(S1, s_begin + len);
+
+        f32x16 acc;
+#pragma unroll
+        for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+
+        uint64_t s = s_begin + wave;
+        SegLoad nx{};
+        if (s < s_end) nx = load_segment(g, s, lane);
+        while (s < s_end) {
+            const SegLoad cur = nx;
+            const uint64_t s_next = s + WAVES;
+            const bool more = s_next < s_end;
+            nx = load_segment(g, more ? s_next : s, lane);
+
+            // the segment inside its tile: elements [lo, hi), rounds from unit u0
+            const uint64_t t = cur.g0 >> 14;
+            bool valid = cur.g0 < n_elems && cur.g1 >= cur.g0 && cur.g1 <= min((t + 1) << 14, n_elems) &&
+                         t / g.tiles_per_row == rb;
+            const uint64_t tile_start = valid ? t << 14 : 0ull;
+            const uint32_t lo = valid ? (uint32_t)(cur.g0 - tile_start) : 0u;
+            const uint32_t hi = valid ? (uint32_t)(cur.g1 - tile_start) : 0u;
+            const uint32_t u0 = (lo >> 9) << 6, head = lo & 511u;
+            valid = valid && head + (hi - lo) + 512 <= g.stg_bytes;
+            const uint32_t nrounds = valid ? (hi - u0 * 8 + 511) >> 9 : 0u;
+            const uint32_t kt = valid ? (uint32_t)(t - (uint64_t)rb * g.tiles_per_row) : 0u;
+            const uint8_t *smt = g.sm + tile_start;
+            const uint16_t *xr = g.x + (uint64_t)n_l * g.K + kt * kTC + khalf * 8;
+
+            // operands of the first rounds (rounds past the segment reload its last round)
+            uint2 smp[kSegRounds];
+            uint4 xp[kSegRounds];
+            const uint32_t last_round = nrounds ? nrounds - 1 : 0u;
+#pragma unroll
+            for (int r = 0; r < kSegRounds; r++) {
+                const uint32_t rr = min((uint32_t)r, last_round);
+                smp[r] = *reinterpret_cast<const uint2 *>(smt + 8 * (u0 + 64 * rr + lane));
+                xp[r] = x_row ? *reinterpret_cast<const uint4 *>(xr + (u0 / 64 + rr) * 16) : make_uint4(0, 0, 0, 0);
+            }
+
+            if (valid && stage_seg<K>(cur, stored, stg + head, fast, chain, lane)) {
+                auto round = [&](uint32_t r, uint2 sv, uint4 xa) {
+                    const uint32_t u = u0 + 64 * r + lane;
+                    const uint2 m = unit_mask((int)lo - (int)(8 * u), (int)hi - (int)(8 * u));
+                    const uint2 rx = ld64(stg + 8 * (64 * r + lane));
+                    const uint2 a = assemble4(sv.x & m.x, rx.x & m.x), b = assemble4(sv.y & m.y, rx.y & m.y);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                                 __builtin_bit_cast(bf16x8, v4u32{a.x, a.y, b.x, b.y}),
+                                                                 acc, 0, 0, 0);
+                };
+#pragma unroll
+                for (int r = 0; r < kSegRounds; r++)
+                    if ((uint32_t)r < nrounds) round(r, smp[r], xp[r]);
+                for (uint32_t r = kSegRounds; r < nrounds; r++) {
+                    const uint2 sv = *reinterpret_cast<const uint2 *>(smt + 8 * (u0 + 64 * r + lane));
+                    const uint4 xa = x_row ? *reinterpret_cast<const uint4 *>(xr + (u0 / 64 + r) * 16) : make_uint4(0, 0, 0, 0);
+                    round(r, sv, xa);
+                }
+            }
+            wave_lds_sync();   // the staging is reused by the next segment
+            s = s_next;
+        }
+
+        // reduce the waves' partial sums through LDS (the staging is free after the barrier)
+        __syncthreads();
+        lds_f32 *red = (lds_f32 *)(size_t)area;
+        if (wave > 0)
+#pragma unroll
+            for (int j = 0; j < 16; j++) red[(wave - 1) * 1024 + j * 64 + lane] = acc[j];
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll 1
+            for (uint32_t w = 1; w < (uint32_t)WAVES; w++)
+#pragma unroll
+                for (int j = 0; j < 16; j++) acc[j] += red[(w - 1) * 1024 + j * 64 + lane];
+            // y[b, n]: lane holds n = rb*32 + lane%32, b = 8*blk + 4*(lane/32) + e
+#pragma unroll
+            for (int blk = 0; blk < 4; blk++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t b = 8 * blk + 4 * khalf + e;
+                    if (b < g.B) {
+                        float *dst = g.y + (uint64_t)b * g.N + rb * kTR + n_l;
+                        if (g.parts > 1)
+                            unsafeAtomicAdd(dst, acc[4 * blk + e]);
+                        else
+                            *dst = acc[4 * blk + e];
+                    }
+                }
+        }
+        __syncthreads();   // the staging is reused by the next unit
+    }
+}
+
 __global__ void zero_kernel(float4 *p, uint64_t n4)
 {
     for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n4; i += (uint64_t)gridDim.x * blockDim.x)
@@ -351,9 +535,62 @@ int launch(GemmArgs a, uint32_t lds, hipStream_t st)
     return DF11_OK;
 }
 
-template <int K>
-int launch_mt(const GemmArgs &a, uint32_t n_tables, hipStream_t st)
+// Segment-parallel launch (B <= 32): row blocks split into `parts` segment
+// ranges so that every resident workgroup slot has work.
+template <int K, int W>
+int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_t st)
 {
+    a.stg_bytes = std::max(4096u, (max_seg_elems + 1024u + 16u + 15u) & ~15u);
+    const uint32_t lds = 16 + W * a.stg_bytes + (8u << K) + n_tables * 512u;
+    if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm staging and tables do not fit in LDS");
+    static std::mutex mu;
+    static int q_dev = -1, q_per_cu = 0;
+    static uint32_t q_lds = 0;
+    int dev = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        if (q_dev == dev && q_lds == lds) per_cu = q_per_cu;
+    }
+    if (!per_cu) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gemm_seg_kernel<K, W>, W * 64, lds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        std::lock_guard<std::mutex> lk(mu);
+        q_dev = dev;
+        q_lds = lds;
+        q_per_cu = per_cu;
+    }
+    const uint32_t slots = (uint32_t)(cu_count() * per_cu);
+    const uint64_t segs_per_rb = (a.n_segments + a.n_rowblocks - 1) / a.n_rowblocks;
+    // as many parts as fit whole into the resident slots (a second partial
+    // wave of workgroups costs more than idle slots: up_proj, 448 row blocks
+    // on 512 slots, 44 us in one part, 47 us in two)
+    uint32_t parts = 1;
+    if (const char *e = getenv("DF11_GEMM_PARTS")) parts = (uint32_t)atoi(e);
+    else parts = std::max(1u, slots / a.n_rowblocks);
+    // at least one segment per wave
+    parts = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(parts, segs_per_rb / W));
+    a.parts = parts;
+    if (parts > 1) {
+        const uint64_t n = (uint64_t)a.B * a.N, n4 = n / 4;
+        if (n4) hipLaunchKernelGGL(zero_kernel, dim3((uint32_t)std::min<uint64_t>((n4 + 255) / 256, 4096)), dim3(256), 0, st,
+                                   reinterpret_cast<float4 *>(a.y), n4);
+        if (n & 3) hipLaunchKernelGGL(zero_tail_kernel, dim3(1), dim3(64), 0, st, a.y + n4 * 4, n & 3);
+    }
+    const uint64_t units = (uint64_t)a.n_rowblocks * parts;
+    const uint32_t groups = (uint32_t)std::min<uint64_t>(units, 1u << 20);
+    hipLaunchKernelGGL((decode_gemm_seg_kernel<K, W>), dim3(groups), dim3(W * 64), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
+    return DF11_OK;
+}
+
+template <int K>
+int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_t st)
+{
+    // the tile-synchronous kernel also serves the w_debug output
+    if (a.B <= 32 && !a.w_debug && !getenv("DF11_GEMM_TILED")) return launch_seg<K, 8>(a, n_tables, max_seg_elems, st);
     constexpr int W = 8;
     const uint32_t lds = gemm_lds_bytes(K, n_tables);
     if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm tables do not fit in LDS");
@@ -408,10 +645,10 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
     a.n_segments = w->n_segments;
     hipStream_t st = (hipStream_t)stream;
     switch (w->fast_bits) {
-    case 8: return launch_mt<8>(a, w->n_tables, st);
-    case 9: return launch_mt<9>(a, w->n_tables, st);
-    case 10: return launch_mt<10>(a, w->n_tables, st);
-    case 11: return launch_mt<11>(a, w->n_tables, st);
-    default: return launch_mt<12>(a, w->n_tables, st);
+    case 8: return launch_mt<8>(a, w->n_tables, w->max_seg_elems, st);
+    case 9: return launch_mt<9>(a, w->n_tables, w->max_seg_elems, st);
+    case 10: return launch_mt<10>(a, w->n_tables, w->max_seg_elems, st);
+    case 11: return launch_mt<11>(a, w->n_tables, w->max_seg_elems, st);
+    default: return launch_mt<12>(a, w->n_tables, w->max_seg_elems, st);
     }
 }

@@ -2,7 +2,10 @@
 the C ABI: the decoded weights are bit-exact against the input (w_debug), and
 y matches the oracle's float32 product within 2e-3 relative Frobenius error
 (float32 accumulation differs only in summation order; BF16 products are
-exact)."""
+exact).  Up to 32 rows of x take the segment-parallel kernel, which has no
+w_debug output: its decode is checked bit-exactly through y with x = rows
+of the identity, and every case checks y of the call without w_debug (the
+product path) as well as of the call with it (the tile-synchronous kernel)."""
 import sys
 
 import numpy as np
@@ -30,17 +33,49 @@ def _x_to_gpu(X):
 
 
 def _run(W, X, with_debug=True):
+    """y of the product call (no w_debug); with_debug: also the decoded
+    weights and y of a second call that writes them.  Returns (y, wd, y_dbg)."""
     N, K = W.shape
     enc = api.encode(W, layout=api.gemm_layout(N, K))
     enc.validate()
     dt = enc.to("cuda")
     x = _x_to_gpu(X)
-    wdbg = torch.full((N, K), 0x5555, dtype=torch.int16, device="cuda") if with_debug else None
     y = torch.full((X.shape[0], N), float("nan"), dtype=torch.float32, device="cuda")
-    api.decode_gemm(dt, x, out=y, w_debug=wdbg.view(torch.bfloat16) if with_debug else None)
+    api.decode_gemm(dt, x, out=y)
+    wd = y_dbg = None
+    if with_debug:
+        wdbg = torch.full((N, K), 0x5555, dtype=torch.int16, device="cuda")
+        yd = torch.full((X.shape[0], N), float("nan"), dtype=torch.float32, device="cuda")
+        api.decode_gemm(dt, x, out=yd, w_debug=wdbg.view(torch.bfloat16))
+        torch.cuda.synchronize()
+        wd = wdbg.cpu().numpy().view(np.uint16)
+        y_dbg = yd.cpu().numpy()
     torch.cuda.synchronize()
-    wd = wdbg.cpu().numpy().view(np.uint16) if with_debug else None
-    return y.cpu().numpy(), wd
+    return y.cpu().numpy(), wd, y_dbg
+
+
+def _recover_by_identity(W, rows=32, counts=True):
+    """W through y alone: x = rows of the identity placed at columns k0 ..
+    k0 + rows - 1, for every k0, gives y[b, n] = W[n, k0 + b] exactly (one
+    nonzero product per output).  counts=False drops the stored code counts
+    (the kernel then runs the locate pass).  Returns the recovered float32 W."""
+    N, K = W.shape
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    if not counts:
+        dt.view.counts = None
+        dt.view.n_counts = 0
+    got = np.empty((N, K), np.float32)
+    for k0 in range(0, K, rows):
+        b = min(rows, K - k0)
+        X = np.zeros((b, K), np.uint16)
+        X[np.arange(b), k0 + np.arange(b)] = 0x3F80
+        y = api.decode_gemm(dt, _x_to_gpu(X))
+        got[:, k0:k0 + b] = y.cpu().numpy().T
+    return got
+
+
+def _as_f32(W):
+    return (W.astype(np.uint32) << 16).view(np.float32)
 
 
 def _rel(a, b):
@@ -53,12 +88,13 @@ def test_small_weight_all_batch_shapes(B):
     _say("case gemm small B=%d" % B)
     W = synth.normal_bf16(N * K, 0.02, seed=20).reshape(N, K)
     X = synth.activations_bf16(B, K, seed=21)
-    y, wd = _run(W, X)
+    y, wd, yd = _run(W, X)
     assert np.array_equal(wd, W), "decoded weights differ"
     ref = orc.gemm_f64(X, W)
-    assert np.isfinite(y).all()
-    assert _rel(y, ref) < TOL
-    assert _rel(y, orc.gemm_f32(X, W).astype(np.float64)) < TOL
+    for got in (y, yd):
+        assert np.isfinite(got).all()
+        assert _rel(got, ref) < TOL
+        assert _rel(got, orc.gemm_f32(X, W).astype(np.float64)) < TOL
 
 
 @pytest.mark.parametrize("N,K,B", [(256, 14336, 5), (128, 4096, 40), (32, 512, 256)])
@@ -69,9 +105,10 @@ def test_k_split_shapes(N, K, B):
     _say("case gemm split N=%d K=%d B=%d" % (N, K, B))
     W = synth.normal_bf16(N * K, 0.02, seed=26).reshape(N, K)
     X = synth.activations_bf16(B, K, seed=27)
-    y, wd = _run(W, X)
+    y, wd, yd = _run(W, X)
     assert np.array_equal(wd, W), "decoded weights differ"
     assert _rel(y, orc.gemm_f64(X, W)) < TOL
+    assert _rel(yd, orc.gemm_f64(X, W)) < TOL
 
 
 def test_identity_x_recovers_weights_exactly():
@@ -81,9 +118,29 @@ def test_identity_x_recovers_weights_exactly():
     W = synth.normal_bf16(N * K, 0.02, seed=22).reshape(N, K)
     X = np.zeros((B, K), np.uint16)
     X[np.arange(B), np.arange(B)] = 0x3F80
-    y, _ = _run(W, X, with_debug=False)
-    Wf = (W.astype(np.uint32) << 16).view(np.float32)
-    assert np.array_equal(y, Wf[:, :B].T)
+    y, _, _ = _run(W, X, with_debug=False)
+    assert np.array_equal(y, _as_f32(W)[:, :B].T)
+
+
+@pytest.mark.parametrize("N,K,seed", [(96, 1536, 28), (256, 4096, 29)])
+def test_identity_x_recovers_weights_segment_parallel(N, K, seed):
+    """Every weight through the segment-parallel kernel (32 rows of x),
+    compared exactly: masks at segment edges, rounds and the row block
+    reduction (and the K split of y for the 8-row-block weight)."""
+    _say("case gemm identity segment-parallel N=%d K=%d" % (N, K))
+    W = synth.normal_bf16(N * K, 0.02, seed=seed).reshape(N, K)
+    assert np.array_equal(_recover_by_identity(W), _as_f32(W))
+
+
+def test_identity_x_recovers_long_code_weights():
+    """Adversarial exponent mix (long codes, short segments) without the
+    non-finite exponent 255, so that 0 * w stays 0: recovered exactly
+    through y of the segment-parallel kernel."""
+    N, K = 64, 1024
+    _say("case gemm identity adversarial")
+    W = synth.adversarial_bf16(N * K, seed=30).reshape(N, K)
+    W = np.where((W >> 7) & 0xFF == 0xFF, W & 0x807F, W).astype(np.uint16)
+    assert np.array_equal(_recover_by_identity(W), _as_f32(W))
 
 
 def test_adversarial_weights_decode_exactly():
@@ -91,7 +148,7 @@ def test_adversarial_weights_decode_exactly():
     N, K = 64, 1024
     _say("case gemm adversarial")
     W = synth.adversarial_bf16(N * K, seed=23).reshape(N, K)
-    _, wd = _run(W, synth.activations_bf16(4, K, seed=24))
+    _, wd, _ = _run(W, synth.activations_bf16(4, K, seed=24))
     assert np.array_equal(wd, W)
 
 
@@ -106,18 +163,19 @@ def test_up_proj_full_size(B):
     enc = api.encode(W, layout=api.gemm_layout(N, K))
     dt = enc.to("cuda")
     wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
-    y = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg)
+    y = api.decode_gemm(dt, _x_to_gpu(X))
+    yd = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg)
     torch.cuda.synchronize()
     wt = torch.from_numpy(W.view(np.int16)).cuda()
     assert torch.equal(wdbg.view(torch.int16), wt), "decoded weights differ"
     cols = np.random.default_rng(B).choice(N, size=48, replace=False)
     ref = orc.gemm_f64(X, W[cols])
-    got = y.cpu().numpy()[:, cols]
-    assert _rel(got, ref) < TOL
     # and the whole product against torch's float32 matmul of the same BF16 values
     yt = (_x_to_gpu(X).float() @ wt.view(torch.bfloat16).float().T)
-    rel = float((y - yt).norm() / yt.norm())
-    assert rel < TOL
+    for out in (y, yd):
+        assert _rel(out.cpu().numpy()[:, cols], ref) < TOL
+        rel = float((out - yt).norm() / yt.norm())
+        assert rel < TOL
 
 
 def test_rejects_row_major_layout():
@@ -139,5 +197,10 @@ def test_fused_locate_pass_without_stored_counts():
     dt.view.n_counts = 0
     wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg)
+    y = api.decode_gemm(dt, _x_to_gpu(X))
     torch.cuda.synchronize()
     assert np.array_equal(wdbg.view(torch.int16).cpu().numpy().view(np.uint16), W)
+    # the segment-parallel kernel's locate pass, exactly through y with x =
+    # identity rows (no non-finite weights, so that 0 * w stays 0)
+    Wf = np.where((W >> 7) & 0xFF == 0xFF, W & 0x807F, W).astype(np.uint16)
+    assert np.array_equal(_recover_by_identity(Wf, counts=False), _as_f32(Wf))
