@@ -590,10 +590,11 @@ int pick_waves(const int res[kNumChoices], uint64_t nseg, uint64_t cus)
         // several rounds: 24 resident waves per CU already keep HBM busy
         // (more waves measured slower on a whole layer in one launch, with
         // more requests contending); take the shape closest above that,
-        // larger workgroups (fewer table copies) on ties
+        // smaller workgroups on ties (a whole layer: 6- and 8-wave groups
+        // 141 us, 12-wave groups 150 us, all at 24 waves per CU)
         int pick = -1;
         for (int i = 0; i < kNumChoices; i++)
-            if (res[i] >= kSaturatedWaves && (pick < 0 || res[i] <= res[pick])) pick = i;
+            if (res[i] >= kSaturatedWaves && (pick < 0 || res[i] < res[pick])) pick = i;
         return pick >= 0 ? pick : best;
     }
     uint64_t best_load = ~0ull;
