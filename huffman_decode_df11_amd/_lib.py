@@ -11,6 +11,8 @@ DF11_OK = 0
 DF11_MAX_TABLES = 64
 DF11_FAST_BITS_MAX = 12
 DF11_FAST_BITS_DEFAULT = 11
+DF11_Y_F32 = 0
+DF11_Y_BF16 = 1
 
 u32, u64 = ctypes.c_uint32, ctypes.c_uint64
 
@@ -75,7 +77,7 @@ EXPORTS = (
     "df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_free",
     "df11_encoded_view", "df11_gemm_layout", "df11_gemm_tile_rows", "df11_gemm_tile_cols",
     "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_rows", "df11_decode_gemm",
-    "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
+    "df11_decode_gemm_out", "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
     "df11_device_encoded_to_host",
     "df11_status_string", "df11_last_error", "df11_version",
 )
@@ -117,6 +119,7 @@ def lib():
     L.df11_decode_batch.argtypes = [ctypes.POINTER(View), ctypes.POINTER(vp), u32, vp]
     L.df11_decode_rows.argtypes = [ctypes.POINTER(View), vp, u64, vp, vp]
     L.df11_decode_gemm.argtypes = [ctypes.POINTER(View), vp, u32, vp, vp, vp]
+    L.df11_decode_gemm_out.argtypes = [ctypes.POINTER(View), vp, u32, vp, ctypes.c_int, vp, vp]
     L.df11_hist_device.argtypes = [vp, u64, vp, vp]
     L.df11_encode_device.argtypes = [vp, u64, ctypes.POINTER(Codebook), ctypes.POINTER(Layout), vp,
                                      ctypes.POINTER(vp)]
@@ -130,7 +133,7 @@ def lib():
     L.df11_version.restype = ctypes.c_char_p
     for name in ("df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_view",
                  "df11_gemm_layout", "df11_validate", "df11_decode", "df11_decode_batch",
-                 "df11_decode_rows", "df11_decode_gemm", "df11_hist_device", "df11_encode_device",
+                 "df11_decode_rows", "df11_decode_gemm", "df11_decode_gemm_out", "df11_hist_device", "df11_encode_device",
                  "df11_device_encoded_view", "df11_device_encoded_to_host"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L

@@ -13,7 +13,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _lib
-from ._lib import Codebook, Layout, View, check, lib
+from ._lib import DF11_Y_BF16, DF11_Y_F32, Codebook, Layout, View, check, lib
 
 DEFAULT_MAX_LEN = 32
 DEFAULT_FAST_BITS = _lib.DF11_FAST_BITS_DEFAULT
@@ -352,21 +352,27 @@ def decode_rows(t: DF11Tensor, rows, out=None, stream=None):
     return out
 
 
-def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None):
+def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None, out_dtype=None):
     """y = x @ W^T with W decoded tile by tile inside the kernel.  x: [B, K]
-    bf16 on the GPU; returns y [B, N] float32."""
+    bf16 on the GPU; returns y [B, N], float32 (default) or bfloat16
+    (out_dtype=torch.bfloat16, or an `out` of that type: the float32 sum
+    rounded once, ties to even)."""
     import torch
     N, K = int(w.host_view.rows), int(w.host_view.cols)
     assert x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[1] == K
     x = x.contiguous()
     B = x.shape[0]
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    assert out_dtype in (torch.float32, torch.bfloat16)
     if out is None:
-        out = torch.empty((B, N), dtype=torch.float32, device=x.device)
-    assert out.is_contiguous() and out.dtype == torch.float32 and out.numel() == B * N
+        out = torch.empty((B, N), dtype=out_dtype, device=x.device)
+    assert out.is_contiguous() and out.dtype == out_dtype and out.numel() == B * N
     wd = 0
     if w_debug is not None:
         assert w_debug.is_contiguous() and w_debug.numel() == N * K and w_debug.element_size() == 2
         wd = w_debug.data_ptr()
-    check(lib().df11_decode_gemm(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), wd,
-                                 _stream_handle(stream)), "df11_decode_gemm")
+    y_dtype = DF11_Y_BF16 if out_dtype == torch.bfloat16 else DF11_Y_F32
+    check(lib().df11_decode_gemm_out(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), y_dtype, wd,
+                                     _stream_handle(stream)), "df11_decode_gemm_out")
     return out

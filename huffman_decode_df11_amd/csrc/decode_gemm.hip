@@ -57,7 +57,8 @@ struct GemmArgs {
     const uint16_t *chain;
     const uint32_t *fast;
     const uint16_t *x;       // [B, K] bf16
-    float *y;                // [B, N]
+    void *y;                 // [B, N] float32, or BF16 when y_bf16
+    uint32_t y_bf16;
     uint16_t *w_debug;       // [N, K] or null
     uint32_t n_chain;
     uint32_t N, K, B;
@@ -102,6 +103,27 @@ __device__ __forceinline__ SegLoad load_segment(const GemmArgs &g, uint64_t s, u
     L.g1 = rec[1].elem_off;
     L.nbits = rec[0].nbits;
     return L;
+}
+
+// float32 -> BF16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// y[b, n] = v: stored as float32 (added atomically when partial sums from
+// several workgroups meet) or rounded once to BF16 (one writer per element).
+__device__ __forceinline__ void store_y(const GemmArgs &g, uint32_t b, uint32_t n, float v, bool add)
+{
+    const uint64_t i = (uint64_t)b * g.N + n;
+    if (g.y_bf16)
+        reinterpret_cast<uint16_t *>(g.y)[i] = bf16_rne(v);
+    else if (add)
+        unsafeAtomicAdd(reinterpret_cast<float *>(g.y) + i, v);
+    else
+        reinterpret_cast<float *>(g.y)[i] = v;
 }
 
 // Decode one tile-aligned segment into the exponent plane of its tile.
@@ -280,13 +302,7 @@ decode_gemm_kernel(GemmArgs g)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const uint32_t b = mt * 32 + 8 * blk + 4 * khalf + e;
-                        if (b < g.B) {
-                            float *dst = g.y + (uint64_t)b * g.N + rb * kTR + n_l;
-                            if (g.split > 1)
-                                unsafeAtomicAdd(dst, acc[m][4 * blk + e]);
-                            else
-                                *dst = acc[m][4 * blk + e];
-                        }
+                        if (b < g.B) store_y(g, b, rb * kTR + n_l, acc[m][4 * blk + e], g.split > 1);
                     }
             }
         }
@@ -449,13 +465,7 @@ decode_gemm_seg_kernel(GemmArgs g)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const uint32_t b = 8 * blk + 4 * khalf + e;
-                    if (b < g.B) {
-                        float *dst = g.y + (uint64_t)b * g.N + rb * kTR + n_l;
-                        if (g.parts > 1)
-                            unsafeAtomicAdd(dst, acc[4 * blk + e]);
-                        else
-                            *dst = acc[4 * blk + e];
-                    }
+                    if (b < g.B) store_y(g, b, rb * kTR + n_l, acc[4 * blk + e], g.parts > 1);
                 }
         }
         __syncthreads();   // the staging is reused by the next unit
@@ -472,6 +482,17 @@ __global__ void zero_tail_kernel(float *p, uint64_t n)
 {
     const uint64_t i = threadIdx.x;
     if (i < n) p[i] = 0.f;
+}
+
+// y = 0 (float32) before partial sums are added into it; a fill kernel, not a
+// memset, so that the call can be captured in a graph.
+void clear_y(const GemmArgs &a, hipStream_t st)
+{
+    float *y = reinterpret_cast<float *>(a.y);
+    const uint64_t n = (uint64_t)a.B * a.N, n4 = n / 4;
+    if (n4) hipLaunchKernelGGL(zero_kernel, dim3((uint32_t)std::min<uint64_t>((n4 + 255) / 256, 4096)), dim3(256), 0, st,
+                               reinterpret_cast<float4 *>(y), n4);
+    if (n & 3) hipLaunchKernelGGL(zero_tail_kernel, dim3(1), dim3(64), 0, st, y + n4 * 4, n & 3);
 }
 
 uint32_t gemm_lds_bytes(uint32_t fast_bits, uint32_t n_tables)
@@ -519,14 +540,10 @@ int launch(GemmArgs a, uint32_t lds, hipStream_t st)
     if (const char *e = getenv("DF11_GEMM_SPLIT")) split = (uint32_t)atoi(e);
     else if (2 * a.n_rowblocks <= slots) split = (slots + a.n_rowblocks - 1) / a.n_rowblocks;
     split = std::max(1u, std::min(split, a.tiles_per_row));
+    if (a.y_bf16) split = 1;   // one writer per BF16 element
     a.tiles_per_split = (a.tiles_per_row + split - 1) / split;
     a.split = (a.tiles_per_row + a.tiles_per_split - 1) / a.tiles_per_split;
-    if (a.split > 1) {
-        const uint64_t n = (uint64_t)a.B * a.N, n4 = n / 4;
-        if (n4) hipLaunchKernelGGL(zero_kernel, dim3((uint32_t)std::min<uint64_t>((n4 + 255) / 256, 4096)), dim3(256), 0, st,
-                                   reinterpret_cast<float4 *>(a.y), n4);
-        if (n & 3) hipLaunchKernelGGL(zero_tail_kernel, dim3(1), dim3(64), 0, st, a.y + n4 * 4, n & 3);
-    }
+    if (a.split > 1) clear_y(a, st);
     const uint32_t units = a.n_rowblocks * a.split;
     const uint32_t groups = std::min<uint32_t>(units, slots);
     hipLaunchKernelGGL((decode_gemm_kernel<K, MT, W>), dim3(groups), dim3(W * 64), lds, st, a);
@@ -571,13 +588,9 @@ int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_
     else parts = std::max(1u, slots / a.n_rowblocks);
     // at least one segment per wave
     parts = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(parts, segs_per_rb / W));
+    if (a.y_bf16) parts = 1;   // one writer per BF16 element
     a.parts = parts;
-    if (parts > 1) {
-        const uint64_t n = (uint64_t)a.B * a.N, n4 = n / 4;
-        if (n4) hipLaunchKernelGGL(zero_kernel, dim3((uint32_t)std::min<uint64_t>((n4 + 255) / 256, 4096)), dim3(256), 0, st,
-                                   reinterpret_cast<float4 *>(a.y), n4);
-        if (n & 3) hipLaunchKernelGGL(zero_tail_kernel, dim3(1), dim3(64), 0, st, a.y + n4 * 4, n & 3);
-    }
+    if (parts > 1) clear_y(a, st);
     const uint64_t units = (uint64_t)a.n_rowblocks * parts;
     const uint32_t groups = (uint32_t)std::min<uint64_t>(units, 1u << 20);
     hipLaunchKernelGGL((decode_gemm_seg_kernel<K, W>), dim3(groups), dim3(W * 64), lds, st, a);
@@ -606,6 +619,14 @@ int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, hipS
 extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t B, float *y,
                                 uint16_t *w_debug, void *stream)
 {
+    return df11_decode_gemm_out(w, x, B, y, DF11_Y_F32, w_debug, stream);
+}
+
+extern "C" int df11_decode_gemm_out(const df11_view *w, const uint16_t *x, uint32_t B, void *y, int y_dtype,
+                                    uint16_t *w_debug, void *stream)
+{
+    if (y_dtype != DF11_Y_F32 && y_dtype != DF11_Y_BF16)
+        return df11::fail(DF11_E_ARG, "df11_decode_gemm_out: unknown y_dtype %d", y_dtype);
     if (!w || !x || !y) return df11::fail(DF11_E_ARG, "df11_decode_gemm: null pointer");
     if (B < 1 || B > 256) return df11::fail(DF11_E_ARG, "B = %u outside 1..256", B);
     if (w->tile_rows != kTR || w->tile_cols != kTC || w->tile_kchunk != kKC || w->align_elems != kTile ||
@@ -635,6 +656,7 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
     a.fast = w->fast;
     a.x = x;
     a.y = y;
+    a.y_bf16 = y_dtype == DF11_Y_BF16;
     a.w_debug = w_debug;
     a.n_chain = (uint32_t)w->n_chain;
     a.N = (uint32_t)w->rows;

@@ -289,6 +289,19 @@ int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t
 int df11_decode_gemm(const df11_view *device_view, const uint16_t *x, uint32_t B,
                      float *y, uint16_t *w_debug, void *stream);
 
+/* Output types of df11_decode_gemm_out. */
+#define DF11_Y_F32 0
+#define DF11_Y_BF16 1
+
+/* df11_decode_gemm with the type of y chosen by y_dtype: DF11_Y_F32 is
+ * df11_decode_gemm itself; DF11_Y_BF16 makes y a device [B, N] BF16 matrix,
+ * each element the float32 sum rounded once to the nearest BF16 (ties to
+ * even; NaN stays NaN).  A BF16 y is written by exactly one workgroup per
+ * element (the K range is not split), so it is the same on every run.
+ * Errors: as df11_decode_gemm, and E_ARG for an unknown y_dtype. */
+int df11_decode_gemm_out(const df11_view *device_view, const uint16_t *x, uint32_t B,
+                         void *y, int y_dtype, uint16_t *w_debug, void *stream);
+
 /* ---------------------------------------------------------------- utilities */
 const char *df11_status_string(int status);
 const char *df11_last_error(void);

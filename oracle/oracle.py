@@ -196,6 +196,36 @@ def gemm_f64(X, W) -> np.ndarray:
     return Y
 
 
+def round_bf16(x) -> np.ndarray:
+    """BF16 bit patterns of float32 values x, each the nearer of its two
+    neighbouring BF16 values, ties to the one whose last mantissa bit is 0
+    (IEEE 754 round-to-nearest-even; BF16 is binary32 with the low 16
+    mantissa bits dropped: 1 sign, 8 exponent, 7 mantissa bits, as the
+    pages give the format).  A value at or past the midpoint between the
+    largest finite BF16 and 2^128 becomes infinity; NaN becomes a quiet NaN
+    (the quiet bit set on the truncated pattern).
+
+    Written from that definition with exact float64 distances, not with the
+    integer rounding trick."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    lo = (bits >> 16).astype(np.int64)               # toward zero, same sign
+    e = (lo >> 7) & 0xFF
+    sign = np.where(lo & 0x8000, -1.0, 1.0)
+    with np.errstate(invalid="ignore"):              # NaN and Inf are settled below
+        vlo = ((lo.astype(np.uint32) << 16)).view(np.float32).astype(np.float64)
+        ulp = np.ldexp(1.0, np.maximum(e, 1) - 127 - 7)  # BF16 spacing at this exponent
+        vhi = vlo + sign * ulp                       # next BF16 away from zero (2^128 past the top)
+        xv = x.astype(np.float64)
+        dlo = np.abs(xv - vlo)
+        dhi = np.abs(vhi - xv)
+        up = (dhi < dlo) | ((dhi == dlo) & ((lo & 1) == 1))
+    out = np.where(up, lo + 1, lo)
+    out = np.where(np.isinf(x), lo, out)
+    out = np.where(np.isnan(x), lo | 0x40, out)
+    return out.astype(np.uint16)
+
+
 def tile_order(u, rows: int, cols: int, tile_rows: int, tile_cols: int, kchunk: int = 0) -> np.ndarray:
     u = _u16(u)
     out = np.zeros(u.size, np.uint16)

@@ -6,6 +6,7 @@ exact).  Up to 32 rows of x take the segment-parallel kernel, which has no
 w_debug output: its decode is checked bit-exactly through y with x = rows
 of the identity, and every case checks y of the call without w_debug (the
 product path) as well as of the call with it (the tile-synchronous kernel)."""
+import ctypes
 import sys
 
 import numpy as np
@@ -76,6 +77,14 @@ def _recover_by_identity(W, rows=32, counts=True):
 
 def _as_f32(W):
     return (W.astype(np.uint32) << 16).view(np.float32)
+
+
+def _bf16_steps(a, b):
+    """Distance in BF16 steps between two arrays of finite BF16 patterns."""
+    def key(u):
+        u = u.astype(np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(key(a) - key(b))
 
 
 def _rel(a, b):
@@ -176,6 +185,45 @@ def test_up_proj_full_size(B):
         assert _rel(out.cpu().numpy()[:, cols], ref) < TOL
         rel = float((out - yt).norm() / yt.norm())
         assert rel < TOL
+    # BF16 y: the same float32 sums (448 row blocks fill the device, so both
+    # calls write every element from one workgroup) rounded once
+    y16 = api.decode_gemm(dt, _x_to_gpu(X), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    got16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got16, orc.round_bf16(y.cpu().numpy()))
+
+
+@pytest.mark.parametrize("B", [1, 8, 32, 64, 256])
+def test_bf16_output_within_one_step_of_oracle(B):
+    """y as BF16 (one rounding of the float32 sum) against the oracle's
+    float64 product rounded to BF16: at most one BF16 step apart (the sums
+    differ only in order, which can move a value across a rounding
+    midpoint), on both kernels."""
+    N, K = 96, 1536
+    _say("case gemm bf16 out B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=31).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=32)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    ref = orc.round_bf16(orc.gemm_f64(X, W).astype(np.float32))
+    y16 = api.decode_gemm(dt, _x_to_gpu(X), out_dtype=torch.bfloat16)
+    wd = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y16d = api.decode_gemm(dt, _x_to_gpu(X), out_dtype=torch.bfloat16, w_debug=wd)
+    torch.cuda.synchronize()
+    for out in (y16, y16d):
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert _bf16_steps(got, ref).max() <= 1
+
+
+def test_rejects_unknown_output_type():
+    from huffman_decode_df11_amd import _lib
+    N, K = 64, 512
+    W = synth.normal_bf16(N * K, 0.02, seed=33).reshape(N, K)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    x = _x_to_gpu(synth.activations_bf16(2, K))
+    y = torch.empty((2, N), dtype=torch.float32, device="cuda")
+    rc = _lib.lib().df11_decode_gemm_out(ctypes.byref(dt.view), x.data_ptr(), 2, y.data_ptr(), 7, None,
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == -1
 
 
 def test_rejects_row_major_layout():

@@ -393,3 +393,35 @@ def test_tile_order_column_groups_hand_example():
     u = np.arange(16, dtype=np.uint16)
     t = orc.tile_order(u, 2, 8, 2, 8, 4)
     assert t.tolist() == [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+
+
+# --------------------------------------------------------------- BF16 rounding
+def test_round_bf16_worked_values():
+    """Round to nearest BF16, ties to even, on values whose answer follows
+    from the format by hand: 1 + 2^-8 lies halfway between 1.0 (0x3F80, even)
+    and 1 + 2^-7 (0x3F81), so it goes down; 1 + 3*2^-8 lies halfway between
+    0x3F81 (odd) and 0x3F82, so it goes up; anything past a midpoint goes to
+    the far side; the sign is kept; the largest float32 is past the midpoint
+    above the largest finite BF16 (0x7F7F) and becomes infinity."""
+    v = np.array([1.0, 1 + 2**-8, 1 + 3 * 2**-8, 1 + 2**-8 + 2**-20, -(1 + 3 * 2**-8), 0.0, -0.0,
+                  np.float32(3.4028235e38), np.float32(3.3895314e38), np.inf, -np.inf, 2.0**-133, 0.75 * 2.0**-133],
+                 np.float32)
+    want = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xBF82, 0x0000, 0x8000, 0x7F80, 0x7F7F, 0x7F80, 0xFF80, 0x0001, 0x0001]
+    assert orc.round_bf16(v).tolist() == want
+    nan = orc.round_bf16(np.array([np.nan], np.float32))[0]
+    assert (nan >> 7) & 0xFF == 0xFF and nan & 0x7F
+
+
+def test_round_bf16_matches_library_conversion():
+    """Against torch's float32 -> bfloat16 conversion (round to nearest even)
+    on random magnitudes and on random bit patterns (NaNs compared as NaN)."""
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(5)
+    a = (r.standard_normal(200_000) * np.exp(r.uniform(-85, 85, 200_000))).astype(np.float32)
+    b = r.integers(0, 2**32, 200_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    for x in (a, b):
+        got = orc.round_bf16(x)
+        ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        fin = ~np.isnan(x)
+        assert np.array_equal(got[fin], ref[fin])
+        assert (((got[~fin] >> 7) & 0xFF) == 0xFF).all() and ((got[~fin] & 0x7F) != 0).all()
