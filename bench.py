@@ -18,9 +18,9 @@ Prints one JSON line:
             average launch time (HIP events on the launch stream; one launch
             per step), against the 8 TB/s HBM peak
   cpu_baseline  the CPU oracle's bit-serial decode of the same layer, timed
-            on this host (single thread)
+            on this host's allowed cores (one thread each; also on one core)
 
-    python bench.py [--steps K] [--warmup W] [--no-model] [--no-fused] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-model] [--no-fused] [--no-shard] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -327,17 +327,18 @@ def encode_rate(seed: int = 0):
             "host_one_thread_ms": round(t_host * 1e3, 1), "identical_to_host_encoder": bool(same)}
 
 
-def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8):
-    """df11_decode_gemm on the up_proj weight (14336 x 4096) for B in
-    {1, 8, 64, 256}, next to torch.matmul on the BF16 weight and to the
-    unfused path (df11_decode of a row-major encoding, then torch.matmul).
-    Every variant cycles through `copies` copies of its weight (> 512 MB in
-    all), so weights come from HBM and not from the 256 MB Infinity Cache;
-    x and y stay small and warm, as activations do."""
+def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8, rows: int = 14336):
+    """df11_decode_gemm on the up_proj weight (14336 x 4096; or its first
+    `rows` rows, one GPU's share of a row split) for B in {1, 8, 64, 256},
+    next to torch.matmul on the BF16 weight and to the unfused path
+    (df11_decode of a row-major encoding, then torch.matmul).  Every variant
+    cycles through `copies` copies of its weight (> 256 MB in all), so
+    weights come from HBM and not from the 256 MB Infinity Cache; x and y
+    stay small and warm, as activations do."""
     import torch
     from huffman_decode_df11_amd import api, synth
-    N, K = 14336, 4096
-    W = synth.normal_bf16(N * K, 0.02, seed=seed, index=5, count=7).reshape(N, K)
+    N, K = rows, 4096
+    W = synth.normal_bf16(14336 * K, 0.02, seed=seed, index=5, count=7).reshape(14336, K)[:N].copy()
     enc = api.encode(W, layout=api.gemm_layout(N, K))
     enc_rm = api.encode(W, codebook=enc.codebook)
     dts = [enc.to("cuda") for _ in range(copies)]
@@ -348,7 +349,7 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8):
     w_bytes = enc.compressed_nbytes()
 
     def timeit(f):
-        for i in range(warmup):
+        for i in range(max(warmup, copies)):   # every copy touched before timing
             f(i % copies)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -359,7 +360,7 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
-    rows = {}
+    by_b = {}
     for B in (1, 8, 64, 256):
         X = synth.activations_bf16(B, K, seed=1)
         x = torch.from_numpy(X.view(np.int16)).cuda().view(torch.bfloat16)
@@ -376,7 +377,7 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8):
         flops = 2.0 * B * N * K
         alg = w_bytes + B * K * 2 + B * N * 4
         mfma_bound = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > alg / (HBM_PEAK_GBS * 1e9)
-        rows[str(B)] = {
+        by_b[str(B)] = {
             "fused_ms": round(t_fused, 4),
             "fused_tflops": round(flops / t_fused / 1e9, 2),
             "plain_bf16_matmul_ms": round(t_plain, 4),
@@ -390,9 +391,50 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8):
                          {"bound": "hbm", "achieved": round(alg / t_fused / 1e6, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(alg / t_fused / 1e6 / HBM_PEAK_GBS, 4)}),
         }
-    return {"workload": "up_proj 14336x4096 bf16 N(0,0.02), x[B,4096] N(0,1), y float32; each variant cycles "
+    what = "up_proj 14336x4096" if N == 14336 else "rows 0..%d of up_proj 14336x4096 (one GPU's share of an %d-way row split)" % (N - 1, 14336 // N)
+    return {"workload": what + " bf16 N(0,0.02), x[B,4096] N(0,1), y float32; each variant cycles "
                         "through %d copies of its weight" % copies,
-            "compressed_weight_bytes": w_bytes, "by_batch": rows}
+            "compressed_weight_bytes": w_bytes, "by_batch": by_b}
+
+
+def shard_layer_decode(steps: int, warmup: int, ways: int = 8, copies: int = 4, seed: int = 0):
+    """One GPU's share of the layer under an `ways`-way row split: the first
+    1/ways of the rows of each of the seven matrices, one codebook, decoded
+    in one df11_decode_batch launch per step; the step cycles through
+    `copies` copies of the encodings so the compressed data (> 256 MB in
+    all) comes from HBM."""
+    import torch
+    from huffman_decode_df11_amd import api, synth
+    mats = [(name, m[: m.shape[0] // ways].copy()) for name, m in synth.llama_layer(seed=seed, layer=0)]
+    hist = None
+    for _, m in mats:
+        hist = api.hist_accumulate(m, hist)
+    cb = api.build_codebook(hist)
+    encs = [api.encode(m, codebook=cb) for _, m in mats]
+    sets = [[e.to("cuda") for e in encs] for _ in range(copies)]
+    n = sum(m.size for _, m in mats)
+    outs = [torch.empty(m.size, dtype=torch.bfloat16, device="cuda") for _, m in mats]
+    api.decode_batch(sets[0], outs=outs)
+    torch.cuda.synchronize()
+    for (_, m), o in zip(mats, outs):
+        if not np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), m.reshape(-1)):
+            raise SystemExit("shard decode parity failed")
+    for i in range(max(warmup, copies)):
+        api.decode_batch(sets[i % copies], outs=outs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _hold_queue(2.0 + 0.05 * steps)
+    a.record()
+    for i in range(steps):
+        api.decode_batch(sets[i % copies], outs=outs)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    alg = sum(algorithmic_bytes(dt) for dt in sets[0])
+    return {"workload": "rows 0..R/%d-1 of each of the seven llama3-8b layer matrices (%d elements), one launch"
+                        % (ways, n), "elements": n, "ms_per_step": round(ms, 4),
+            "decoded_gbs": round(2.0 * n / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def copy_peak(nbytes: int = 512 << 20, reps: int = 10):
@@ -425,22 +467,41 @@ def verify(dts, mats, outbuf):
             raise SystemExit("parity check failed before timing")
 
 
-def cpu_baseline_layer(mats, budget_s: float = 20.0):
-    """The oracle's serial decode on the host, over the layer's matrices in
-    order until the time budget is used (at least one matrix)."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_layer(mats, one_core_s: float = 12.0, all_cores_s: float = 10.0):
+    """The oracle's serial decode on the host over the layer's matrices:
+    first on one core (the loop pinned to the first CPU this process may
+    use), then on every allowed core, one thread per core, each thread
+    decoding whole matrices in turn (independent tensors; the oracle's C
+    decode runs without the interpreter lock).  Returns (all cores, one
+    core) baseline records."""
+    from concurrent.futures import ThreadPoolExecutor
+    import itertools
     from oracle import oracle as orc
     hist = None
     for m in mats:
         hist = orc.histogram(m) if hist is None else hist + orc.histogram(m)
     ln = orc.code_lengths(hist, 32)
     refs = [orc.encode(m, lengths=ln) for m in mats]
-    # one core: pin the decode loop to the first CPU this process may use
     allowed = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
+    cpu = _cpu_model()
+
+    # one core
     if allowed:
         os.sched_setaffinity(0, {allowed[0]})
     elems, secs, passes = 0, 0.0, 0
     try:
-        while passes == 0 or secs < budget_s:
+        while passes == 0 or secs < one_core_s:
             for m, ref in zip(mats, refs):
                 t0 = time.perf_counter()
                 out = orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln)
@@ -453,19 +514,33 @@ def cpu_baseline_layer(mats, budget_s: float = 20.0):
     finally:
         if allowed:
             os.sched_setaffinity(0, set(allowed))
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(2.0 * elems / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "bit-serial oracle decode of the layer's 7 matrices, %d passes (%d elements, %.1f s), "
-                      "one host thread pinned to CPU %s of %d allowed (%s)" % (
-                          passes, elems, secs, allowed[0] if allowed else "?", len(allowed), cpu)}
+    one = {"value": round(2.0 * elems / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "bit-serial oracle decode of the layer's 7 matrices, %d passes (%d elements, %.1f s), "
+                     "one host thread pinned to CPU %s of %d allowed (%s)" % (
+                         passes, elems, secs, allowed[0] if allowed else "?", len(allowed), cpu)}
+
+    # every allowed core: threads take matrices in turn until the budget is used
+    threads = max(1, len(allowed))
+    order = itertools.count()
+    t_start = time.perf_counter()
+    deadline = t_start + all_cores_s
+
+    def worker(_):
+        done = 0
+        while True:
+            i = next(order)
+            if i >= threads and time.perf_counter() >= deadline:
+                return done
+            ref = refs[i % len(refs)]
+            orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln)
+            done += ref.n
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        total = sum(ex.map(worker, range(threads)))
+    wall = time.perf_counter() - t_start
+    allc = {"value": round(2.0 * total / wall / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "bit-serial oracle decode of the layer's 7 matrices (whole matrices, in turn) on %d host "
+                      "threads, one per allowed CPU, %.1f s wall, %d elements (%s)" % (threads, wall, total, cpu)}
+    return allc, one
 
 
 def main():
@@ -476,6 +551,7 @@ def main():
     ap.add_argument("--workload", default="layer", choices=["layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-shard", action="store_true")
     ap.add_argument("--no-model", action="store_true", help="skip the 8B-parameter model pass")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -580,6 +656,12 @@ def main():
         result["encode"] = encode_rate(args.seed)
     if not args.no_fused:
         result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
+    if not args.no_shard:
+        # what one GPU does under an 8-way row split of each matrix (no collective)
+        result["shard_8way"] = {
+            "layer_decode": shard_layer_decode(args.steps, args.warmup, ways=8, seed=args.seed),
+            "fused_up_proj": fused_up_proj(args.steps, args.warmup, args.seed, copies=32, rows=14336 // 8),
+        }
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -588,7 +670,7 @@ def main():
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 256 << 20
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_layer(mats)
+        result["cpu_baseline"], result["cpu_baseline_one_core"] = cpu_baseline_layer(mats)
     print(json.dumps(result), flush=True)
 
 
