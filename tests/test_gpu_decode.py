@@ -238,6 +238,23 @@ def test_batch_streaming_launch_with_ragged_views():
         assert (got[t.size:] == 0x5555).all()
 
 
+def test_streaming_launch_tile_order_output():
+    """A weight in the fused kernel's tile order (8-column groups) whose BF16
+    output exceeds the last-level cache, decoded to row-major by
+    df11_decode: the streaming stores go through the tile-order placement."""
+    rows, cols = 8224, 16384
+    assert 2 * rows * cols > 256 << 20
+    u = synth.normal_bf16(rows * cols, 0.02, seed=320).reshape(rows, cols)
+    _say("case streaming tile order", rows, cols)
+    dt = api.encode(u, layout=api.gemm_layout(rows, cols)).to("cuda")
+    out = torch.full((rows * cols + 16,), 0x5555, dtype=torch.int16, device="cuda")
+    api.decode(dt, out=out.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    want = torch.from_numpy(u.reshape(-1).view(np.int16)).cuda()
+    assert torch.equal(out[:rows * cols], want)
+    assert (out[rows * cols:] == 0x5555).all()
+
+
 def test_batch_many_small_and_empty():
     """More views than one launch takes (16), ragged sizes and an empty one."""
     rng = np.random.default_rng(7)
