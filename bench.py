@@ -397,6 +397,45 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8, rows:
             "compressed_weight_bytes": w_bytes, "by_batch": by_b}
 
 
+def other_configs(steps: int, warmup: int, seed: int = 0):
+    """The two other decode workloads, one df11_decode launch per step: a
+    1024 x 1024 N(0, 0.02) tensor (launch-bound; the same tensor again and
+    again) and 16,777,216 elements of 99% Student-t(3) x 0.02 plus 1% random
+    16-bit patterns (every exponent, the longest codes; 12 copies cycled so
+    the compressed data comes from HBM).  Parity is checked in full first."""
+    import torch
+    from huffman_decode_df11_amd import api, synth
+    out = {}
+    for name, u, copies in (("tensor_1024x1024", synth.tensor_1024(seed=seed).reshape(-1), 1),
+                            ("adversarial_16m", synth.adversarial_bf16(1 << 24, seed=seed), 12)):
+        enc = api.encode(u)
+        dts = [enc.to("cuda") for _ in range(copies)]
+        buf = torch.empty(u.size, dtype=torch.bfloat16, device="cuda")
+        api.decode(dts[0], out=buf)
+        torch.cuda.synchronize()
+        if not np.array_equal(buf.view(torch.int16).cpu().numpy().view(np.uint16), u):
+            raise SystemExit("parity failed on " + name)
+        for i in range(max(warmup, copies)):
+            api.decode(dts[i % copies], out=buf)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_launch = max(steps, 50)
+        _hold_queue(2.0 + 0.05 * n_launch)
+        a.record()
+        for i in range(n_launch):
+            api.decode(dts[i % copies], out=buf)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n_launch
+        alg = algorithmic_bytes(dts[0])
+        out[name] = {"elements": int(u.size), "us_per_launch": round(ms * 1e3, 2),
+                     "decoded_gbs": round(2.0 * u.size / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bits_per_weight": round(enc.compressed_nbytes() * 8.0 / u.size, 3),
+                     "copies_cycled": copies}
+    return out
+
+
 def shard_layer_decode(steps: int, warmup: int, ways: int = 8, copies: int = 4, seed: int = 0):
     """One GPU's share of the layer under an `ways`-way row split: the first
     1/ways of the rows of each of the seven matrices, one codebook, decoded
@@ -656,6 +695,8 @@ def main():
         result["encode"] = encode_rate(args.seed)
     if not args.no_fused:
         result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
+    if not args.no_model:
+        result["other_configs"] = other_configs(args.steps, args.warmup, args.seed)
     if not args.no_shard:
         # what one GPU does under an 8-way row split of each matrix (no collective)
         result["shard_8way"] = {
