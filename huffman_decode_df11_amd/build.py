@@ -2,7 +2,8 @@
 
     python -m huffman_decode_df11_amd.build
 
-The library lands in huffman_decode_df11_amd/_build/libdf11.so.
+The library lands in huffman_decode_df11_amd/_build/libdf11.so, next to
+df11_c_api_check, a host program that uses the C ABI alone (no Python).
 """
 from __future__ import annotations
 
@@ -14,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libdf11.so")
+C_API_CHECK = os.path.join(OUT_DIR, "df11_c_api_check")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -64,6 +66,12 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     _run_all([[HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]])
     os.replace(tmp, LIB)
+    # the C ABI example/check program, linked against the library beside it
+    tmp = C_API_CHECK + ".tmp%d" % os.getpid()
+    _run_all([[HIPCC, "-O2", "-std=c++17", "--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "-I", INCLUDE, os.path.join(CSRC, "examples", "c_api_check.cpp"),
+               "-L", OUT_DIR, "-ldf11", "-Wl,-rpath,$ORIGIN", "-o", tmp]])
+    os.replace(tmp, C_API_CHECK)
     return LIB
 
 

@@ -299,3 +299,16 @@ def test_validator_accepts_a_view_without_counts():
     enc.view.counts = None
     enc.view.n_counts = 0
     enc.validate()
+
+
+def test_c_api_program_host_half():
+    """The C ABI without Python: the example program built beside the library
+    builds a codebook, encodes (row-major and tile order) and validates,
+    and rejects a null input with a status (its device half runs in the GPU
+    tests)."""
+    import subprocess
+    from huffman_decode_df11_amd import build as b
+    assert os.path.exists(b.C_API_CHECK), "build the library first"
+    r = subprocess.run([b.C_API_CHECK, "--host-only"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("c-api ok (host only)")
