@@ -435,7 +435,7 @@ int check_view(const df11_view *v)
 
 // Exponent staging per wave: room for the most codes any segment of this
 // tensor holds (recorded by the encoder, at most segment bits / shortest
-// code), a 16-element head offset and a tail group.
+// code), an 8-element head offset and a tail unit.
 uint32_t staging_bytes(const df11_view *v)
 {
     const uint32_t seg_bits = 64u * kChunkBits;

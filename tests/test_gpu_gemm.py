@@ -252,3 +252,45 @@ def test_fused_locate_pass_without_stored_counts():
     # identity rows (no non-finite weights, so that 0 * w stays 0)
     Wf = np.where((W >> 7) & 0xFF == 0xFF, W & 0x807F, W).astype(np.uint16)
     assert np.array_equal(_recover_by_identity(Wf, counts=False), _as_f32(Wf))
+
+
+def test_graph_replays_match_eager():
+    """The fused product captured in a HIP graph (float32 y with the row
+    blocks split into several runs, so the capture holds the fill kernel and
+    the atomic adds; and BF16 y), replayed five times with the program's own
+    eager work and synchronisations between replays; every replay equals the
+    eager call."""
+    N, K, B = 256, 4096, 8
+    _say("case gemm graph replay")
+    W = synth.normal_bf16(N * K, 0.02, seed=34).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=35)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    x = _x_to_gpu(X)
+    y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((B, N), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        api.decode_gemm(dt, x, out=y)
+        api.decode_gemm(dt, x, out=y16)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref32, ref16 = y.clone(), y16.clone()
+    ref = orc.gemm_f64(X, W)
+    assert _rel(ref32.cpu().numpy(), ref) < TOL
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.decode_gemm(dt, x, out=y)
+        api.decode_gemm(dt, x, out=y16)
+    for i in range(5):
+        y.fill_(float("nan"))
+        y16.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        # float32 partial sums meet in y through atomics: their order may vary
+        assert _rel(y.cpu().numpy(), ref) < TOL, i
+        assert torch.allclose(y, ref32, rtol=1e-5, atol=1e-6), i
+        assert torch.equal(y16.view(torch.int16), ref16.view(torch.int16)), i
+        del junk
