@@ -116,3 +116,38 @@ def test_embedding_lookup():
     assert out.shape == (4, 33, D) and out.dtype == torch.bfloat16
     ref = torch.nn.functional.embedding(ids, _i16(W).view(torch.bfloat16))
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_llama_mlp_block_decode_mode_is_bit_identical():
+    """A Llama-shaped MLP block, down(silu(gate(x)) * up(x)), with the three
+    weights held compressed (DF11Linear, decode mode) gives exactly the
+    output of the same block on the BF16 weights: the decode is lossless and
+    the same matmuls run on the restored weights.  The fused mode (48 rows of
+    x are above its default row limit, so forced here with fused_max_rows)
+    stays within the float32-accumulation tolerance."""
+    torch.manual_seed(0)
+    d, f = 1024, 3584
+    gate = torch.nn.Linear(d, f, bias=False).cuda().to(torch.bfloat16)
+    up = torch.nn.Linear(d, f, bias=False).cuda().to(torch.bfloat16)
+    down = torch.nn.Linear(f, d, bias=False).cuda().to(torch.bfloat16)
+    for lin in (gate, up, down):
+        with torch.no_grad():
+            lin.weight.normal_(0, 0.02)
+    x = torch.randn(3, 16, d, device="cuda").to(torch.bfloat16)
+    _say("case mlp block")
+
+    def block(g, u, dn, x):
+        return dn(torch.nn.functional.silu(g(x)) * u(x))
+
+    with torch.no_grad():
+        ref = block(gate, up, down, x)
+        dec = [dnn.DF11Linear.from_linear(l, mode="decode") for l in (gate, up, down)]
+        got = block(*dec, x)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+        fused = [dnn.DF11Linear.from_linear(l, mode="fused") for l in (gate, up, down)]
+        for m in fused:
+            m.fused_max_rows = 64
+        got_f = block(*fused, x)
+        rel = float((got_f.float() - ref.float()).norm() / ref.float().norm())
+        assert rel < 1e-2, rel
