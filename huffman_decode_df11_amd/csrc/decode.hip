@@ -55,6 +55,11 @@ struct ViewArgs {
     // tile order (tr == 0: row-major); kc > 0: column groups inside a tile
     uint32_t tr, tc, tiles_per_row, kc;
     uint64_t cols;
+    // bit 31 set: tr, tc and kc (when > 0) are powers of two with these
+    // shifts in bits 0-4, 5-9 and 10-14 (the fused kernel's layout is), so
+    // the placement takes shifts and one 32-bit division
+    uint32_t pow2;
+    uint32_t reserved;
 };
 
 // Up to kMaxBatch views per launch, passed by value; segments of all views
@@ -113,6 +118,22 @@ struct TableArgs {
 __device__ __forceinline__ uint64_t out_index(const ViewArgs &v, uint64_t g)
 {
     if (!v.tr) return g;
+    if (v.pow2) {
+        const uint32_t trs = v.pow2 & 31u, tcs = (v.pow2 >> 5) & 31u, kcs = (v.pow2 >> 10) & 31u;
+        const uint32_t ts = trs + tcs;
+        const uint32_t t = (uint32_t)(g >> ts), w = (uint32_t)g & ((1u << ts) - 1u);
+        uint32_t r, c;
+        if (v.kc) {
+            const uint32_t gs = trs + kcs, in = w & ((1u << gs) - 1u);
+            r = in >> kcs;
+            c = ((w >> gs) << kcs) | (in & ((1u << kcs) - 1u));
+        } else {
+            r = w >> tcs;
+            c = w & ((1u << tcs) - 1u);
+        }
+        const uint32_t rb = t / v.tiles_per_row, cb = t - rb * v.tiles_per_row;
+        return (uint64_t)((rb << trs) + r) * v.cols + (cb << tcs) + c;
+    }
     const uint64_t tile = (uint64_t)v.tr * v.tc;
     const uint64_t t = g / tile;
     const uint32_t w = (uint32_t)(g - t * tile);
@@ -299,10 +320,81 @@ __device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint6
     }
 }
 
+// A segment inside one tile of the fused kernel's order (32-row tiles,
+// 8-column groups: unit u of a tile is row u % 32, columns 8 * (u / 32) ..
+// + 7), written to row-major BF16.  Taking the units in stream order would
+// give every lane of a wave-wide store a different row; here lane l takes
+// row 8k + l / 8 of group g + l % 8, so each store instruction writes 8 rows
+// x 128 contiguous bytes and each sign+mantissa load reads 8 runs of 64
+// contiguous bytes (loaded after the decode: registers held across it cost
+// more occupancy than the wait costs).  Ragged ends as in merge_range.
+struct TileSeg {
+    const uint8_t *smt;        // sign+mantissa bytes of the tile
+    uint16_t *obase;           // output of the tile's first element
+    uint32_t lo, hi;           // the segment's elements within the tile
+    uint32_t grp_a, grp_b;     // first and last column group touched
+    uint32_t stg_t;            // staging byte of tile element 0 (modulo 2^32)
+};
+
+__device__ __forceinline__ TileSeg tile_seg(const SegPlan &p, const ViewArgs &v, uint32_t stg)
+{
+    const uint32_t tcs = (v.pow2 >> 5) & 31u, ts = 5 + tcs;
+    const uint64_t tile = p.g0 >> ts, tile_start = tile << ts;
+    TileSeg q;
+    q.lo = (uint32_t)(p.g0 - tile_start);
+    q.hi = (uint32_t)(p.g1 - tile_start);
+    q.grp_a = q.lo >> 8;
+    q.grp_b = (q.hi - 1) >> 8;
+    const uint32_t t32 = (uint32_t)tile, rb = t32 / v.tiles_per_row, cb = t32 - rb * v.tiles_per_row;
+    q.obase = v.out + ((uint64_t)rb << 5) * v.cols + ((uint64_t)cb << tcs);
+    q.smt = v.sm + tile_start;
+    q.stg_t = stg + (uint32_t)(tile_start - p.gbase);
+    return q;
+}
+
+// element offset (in the tile) of lane's unit in pass k of group batch gb
+__device__ __forceinline__ uint32_t tile_unit(uint32_t gb, uint32_t k, uint32_t lane)
+{
+    return ((gb + (lane & 7u)) << 8) + ((8u * k + (lane >> 3)) << 3);
+}
+
+__device__ __forceinline__ bool tile_unit_in(const TileSeg &q, uint32_t gb, uint32_t e0, uint32_t lane)
+{
+    return gb + (lane & 7u) <= q.grp_b && e0 >= q.lo && e0 + 8 <= q.hi;
+}
+
+__device__ __forceinline__ void merge_tile_groups8(const SegPlan &p, const ViewArgs &v, const TileSeg &q,
+                                                   uint32_t rag_sm, uint32_t stg, uint32_t lane, bool stream)
+{
+    const RaggedLane rg = ragged_lane(p.g0, p.g1, lane);
+    if (rg.act) {
+        const uint32_t rx = *(const lds_u8 *)(size_t)(stg + (uint32_t)(rg.g - p.gbase));
+        *(v.out + out_index(v, rg.g)) = assemble1(rag_sm, rx);
+    }
+    auto unit = [&](uint32_t gb, uint32_t k, uint2 sv) {
+        const uint32_t e0 = tile_unit(gb, k, lane);
+        if (tile_unit_in(q, gb, e0, lane)) {
+            const uint2 rx = ld64(q.stg_t + e0);
+            const uint2 a = assemble4(sv.x, rx.x), b = assemble4(sv.y, rx.y);
+            const uint32_t r = 8u * k + (lane >> 3), grp = gb + (lane & 7u);
+            store_bf16x8(q.obase + (uint64_t)r * v.cols + (grp << 3), make_uint4(a.x, a.y, b.x, b.y), stream);
+        }
+    };
+    for (uint32_t gb = q.grp_a; gb <= q.grp_b; gb += 8) {
+        uint2 sv[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t e0 = tile_unit(gb, k, lane);
+            sv[k] = load_sm8(q.smt + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)), stream);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) unit(gb, k, sv[k]);
+    }
+}
+
 // ------------------------------------------------------------ kernels
-template <int K, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
-decode_kernel(BatchArgs b, TableArgs t)
+template <int K, int WAVES, bool TILE8>
+__device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs &t)
 {
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
@@ -339,17 +431,45 @@ decode_kernel(BatchArgs b, TableArgs t)
         const uint32_t vi_next = more ? view_of(b, s_next, vi) : vi;
         nx = load_segment(b.v[vi_next], (more ? s_next : s) - b.seg_begin[vi_next], lane);
         uint2 smp[kPrefetchRounds];
-        prefetch_sm(p, v.sm, lane, stream, smp);
+        bool tiled = false;
+        if constexpr (TILE8) {   // launches holding a view in the fused kernel's tile order
+            const uint32_t ts = 5 + ((v.pow2 >> 5) & 31u);
+            tiled = p.valid && v.kc == 8 && v.pow2 && v.tr == 32 && p.g1 > p.g0 && (p.g0 >> ts) == ((p.g1 - 1) >> ts);
+        }
+        if (!tiled) prefetch_sm(p, v.sm, lane, stream, smp);
         const RaggedLane rg = ragged_lane(p.g0, p.g1, lane);
         const uint32_t rag_sm = v.sm[p.valid && rg.act ? rg.g : 0];
 
-        if (p.valid && stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane))
-            merge_range(p, p.g0, p.g1, smp, rag_sm, v.sm, ViewOut{v}, stg, lane, stream);
+        if (p.valid && stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane)) {
+            if (tiled)
+                merge_tile_groups8(p, v, tile_seg(p, v, stg), rag_sm, stg, lane, stream);
+            else
+                merge_range(p, p.g0, p.g1, smp, rag_sm, v.sm, ViewOut{v}, stg, lane, stream);
+        }
         wave_lds_sync();   // the staging is reused by the next segment
         if (!more) break;
         s = s_next;
         vi = vi_next;
     }
+}
+
+// Two kernels from one body, both at 8 waves per SIMD (64 VGPRs): the
+// row-major one, and one with the tile-order merge for launches that hold
+// such a view (its extra bookkeeping spills a few registers, which costs
+// less than fewer waves: 66 us against 74 us at 6 waves per SIMD on
+// up_proj), so that the row-major kernel stays free of spills.
+template <int K, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
+decode_kernel(BatchArgs b, TableArgs t)
+{
+    decode_body<K, WAVES, false>(b, t);
+}
+
+template <int K, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
+decode_kernel_t8(BatchArgs b, TableArgs t)
+{
+    decode_body<K, WAVES, true>(b, t);
 }
 
 // Row gather: one wave per requested row; the segments that overlap the row
@@ -473,6 +593,18 @@ ViewArgs make_args(const df11_view *v, uint16_t *out)
     a.tiles_per_row = v->tile_rows ? (uint32_t)(v->cols / v->tile_cols) : 0;
     a.kc = v->tile_rows ? v->tile_kchunk : 0;
     a.cols = v->cols;
+    auto log2_exact = [](uint64_t x) -> int {
+        if (!x || (x & (x - 1))) return -1;
+        int k = 0;
+        while ((1ull << k) != x) k++;
+        return k;
+    };
+    if (a.tr) {
+        const int trs = log2_exact(a.tr), tcs = log2_exact(a.tc), kcs = a.kc ? log2_exact(a.kc) : 0;
+        if (trs >= 0 && tcs >= 0 && kcs >= 0 && trs + tcs < 31 && (v->n >> (trs + tcs)) < (1ull << 32) &&
+            ((uint64_t)v->rows >> trs) < (1ull << 32))
+            a.pow2 = (1u << 31) | (uint32_t)trs | ((uint32_t)tcs << 5) | ((uint32_t)kcs << 10);
+    }
     return a;
 }
 
@@ -482,7 +614,7 @@ uint32_t lds_bytes(int waves, uint32_t stg, uint32_t fast_bits, uint32_t n_table
     return 16 + (uint32_t)waves * stg + (8u << fast_bits) + n_tables * 512u;
 }
 
-template <int K, int W>
+template <int K, int W, bool T8>
 int try_launch(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
                hipStream_t st, int *resident)
 {
@@ -490,30 +622,36 @@ int try_launch(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, 
     // *resident > 0: the resident waves per CU are already known
     int per_cu = *resident > 0 ? *resident / W : 0;
     if (per_cu < 1 &&
-        (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<K, W>, W * 64, lds) != hipSuccess || per_cu < 1))
+        (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, T8 ? decode_kernel_t8<K, W> : decode_kernel<K, W>, W * 64, lds) !=
+             hipSuccess || per_cu < 1))
         per_cu = 1;
     *resident = per_cu * W;
     if (!nseg) return 0;   // query only
     // every resident slot busy: the decode is latency-bound per wave, so
     // more waves in flight beat an evenly split last round
     const uint64_t groups = std::min<uint64_t>((nseg + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
-    if (groups) hipLaunchKernelGGL((decode_kernel<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
+    if (groups) {
+        if constexpr (T8)
+            hipLaunchKernelGGL((decode_kernel_t8<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
+        else
+            hipLaunchKernelGGL((decode_kernel<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
+    }
     return 0;
 }
 
 constexpr int kWaveChoices[] = {4, 6, 8, 10, 12, 14, 16};
 
-template <int K>
+template <int K, bool T8>
 int run_shape(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
               hipStream_t st, int *resident)
 {
-    return try_launch<K, 4>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 6>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 8>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 10>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 12>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 14>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 16>(waves, a, t, lds, nseg, st, resident);
+    return try_launch<K, 4, T8>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 6, T8>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 8, T8>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 10, T8>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 12, T8>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 14, T8>(waves, a, t, lds, nseg, st, resident) &&
+           try_launch<K, 16, T8>(waves, a, t, lds, nseg, st, resident);
 }
 
 // Waves per workgroup.  Occupancy (LDS and registers) gives, for every
@@ -532,9 +670,10 @@ constexpr int kSaturatedWaves = 24;
 struct ShapeKey {
     int dev, k;
     uint32_t stg, n_tables;
+    bool t8;
     bool operator==(const ShapeKey &o) const
     {
-        return dev == o.dev && k == o.k && stg == o.stg && n_tables == o.n_tables;
+        return dev == o.dev && k == o.k && stg == o.stg && n_tables == o.n_tables && t8 == o.t8;
     }
 };
 std::mutex g_shape_mu;
@@ -543,12 +682,12 @@ int g_shape_res[8][kNumChoices];
 uint32_t g_shape_n = 0;
 
 // res[i]: resident waves per CU with kWaveChoices[i] waves per workgroup (0: does not fit)
-template <int K>
+template <int K, bool T8>
 void resident_waves(const TableArgs &t, const df11_view *v, hipStream_t st, int res[kNumChoices])
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-    const ShapeKey key{dev, K, t.stg_bytes, v->n_tables};
+    const ShapeKey key{dev, K, t.stg_bytes, v->n_tables, T8};
     {
         std::lock_guard<std::mutex> g(g_shape_mu);
         for (uint32_t i = 0; i < std::min(g_shape_n, 8u); i++)
@@ -563,7 +702,7 @@ void resident_waves(const TableArgs &t, const df11_view *v, hipStream_t st, int 
         const uint32_t lds = lds_bytes(w, t.stg_bytes, v->fast_bits, v->n_tables);
         res[i] = 0;
         if (16 + (uint32_t)w * t.stg_bytes > 65520 || lds > 160u * 1024u) continue;
-        run_shape<K>(w, probe, t, lds, 0, st, &res[i]);
+        run_shape<K, T8>(w, probe, t, lds, 0, st, &res[i]);
     }
     std::lock_guard<std::mutex> g(g_shape_mu);
     g_shape_key[g_shape_n % 8] = key;
@@ -608,19 +747,31 @@ int pick_waves(const int res[kNumChoices], uint64_t nseg, uint64_t cus)
     return best;
 }
 
-template <int K>
-int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
+template <int K, bool T8>
+int launch_decode_t(const BatchArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
 {
     int res[kNumChoices];
-    resident_waves<K>(t, v, st, res);
+    resident_waves<K, T8>(t, v, st, res);
     const int i = pick_waves(res, a.seg_begin[a.count], (uint64_t)device_cu_count());
     if (i < 0) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
     int r = res[i];
-    run_shape<K>(kWaveChoices[i], a, t, lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables),
-                 a.seg_begin[a.count], st, &r);
+    run_shape<K, T8>(kWaveChoices[i], a, t, lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables),
+                     a.seg_begin[a.count], st, &r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode launch: %s", hipGetErrorString(e));
     return DF11_OK;
+}
+
+
+// Views in 8-column-group tile order take a kernel with the row-wise merge
+// for them (merge_tile_groups8); all other launches a kernel without it.
+template <int K>
+int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
+{
+    bool t8 = false;
+    for (uint32_t i = 0; i < a.count; i++)
+        t8 = t8 || (a.v[i].kc == 8 && a.v[i].pow2 && a.v[i].tr == 32);
+    return t8 ? launch_decode_t<K, true>(a, t, v, st) : launch_decode_t<K, false>(a, t, v, st);
 }
 
 }  // namespace
@@ -674,7 +825,7 @@ template <int K>
 int launch_rows(const RowArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
 {
     int res[kNumChoices];
-    resident_waves<K>(t, v, st, res);
+    resident_waves<K, false>(t, v, st, res);
     const int i = pick_waves(res, a.n_rows, (uint64_t)device_cu_count());
     if (i < 0) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
     const uint32_t lds = lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables);
