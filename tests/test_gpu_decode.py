@@ -319,3 +319,31 @@ def test_concurrent_streams():
         assert np.array_equal(_to_bits(o), a)
     for o in outs_b:
         assert np.array_equal(_to_bits(o), b)
+
+
+def test_batch_mixed_layouts():
+    """One launch over a weight in the fused kernel's tile order, a
+    row-major tensor with a ragged size and a tile order with 16-column
+    groups, sharing a codebook: the launch takes the kernel with the
+    row-wise tile merge, which must still merge the other views in stream
+    order; every output bit-exact, guards untouched."""
+    gemm = synth.normal_bf16(256 * 2048, 0.02, seed=340).reshape(256, 2048)
+    flat = synth.normal_bf16(1_000_003, 0.02, seed=341)
+    kc16 = synth.normal_bf16(128 * 1024, 0.02, seed=342).reshape(128, 1024)
+    hist = None
+    for t in (gemm, flat, kc16):
+        hist = api.hist_accumulate(t, hist)
+    cb = api.build_codebook(hist)
+    lay16 = api.make_layout(rows=128, cols=1024, tile_rows=32, tile_cols=512, align_elems=32 * 512, tile_kchunk=16)
+    dts = [api.encode(gemm, codebook=cb, layout=api.gemm_layout(256, 2048)).to("cuda"),
+           api.encode(flat, codebook=cb).to("cuda"),
+           api.encode(kc16, codebook=cb, layout=lay16).to("cuda")]
+    _say("case batch mixed layouts")
+    srcs = (gemm, flat, kc16)
+    outs = [torch.full((t.size + 16,), 0x5555, dtype=torch.int16, device="cuda") for t in srcs]
+    api.decode_batch(dts, outs=[o.view(torch.bfloat16) for o in outs])
+    torch.cuda.synchronize()
+    for t, o in zip(srcs, outs):
+        got = _to_bits(o)
+        assert np.array_equal(got[:t.size], t.reshape(-1))
+        assert (got[t.size:] == 0x5555).all()
