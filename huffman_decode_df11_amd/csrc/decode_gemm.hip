@@ -113,17 +113,22 @@ __device__ __forceinline__ uint16_t bf16_rne(float f)
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// y[b, n] = v: stored as float32 (added atomically when partial sums from
-// several workgroups meet) or rounded once to BF16 (one writer per element).
-__device__ __forceinline__ void store_y(const GemmArgs &g, uint32_t b, uint32_t n, float v, bool add)
+// y[i] = v for i = b * N + n: stored as float32 (added atomically when
+// partial sums from several workgroups meet) or rounded once to BF16 (one
+// writer per element).
+__device__ __forceinline__ void store_y_at(const GemmArgs &g, uint64_t i, float v, bool add)
 {
-    const uint64_t i = (uint64_t)b * g.N + n;
     if (g.y_bf16)
         reinterpret_cast<uint16_t *>(g.y)[i] = bf16_rne(v);
     else if (add)
         unsafeAtomicAdd(reinterpret_cast<float *>(g.y) + i, v);
     else
         reinterpret_cast<float *>(g.y)[i] = v;
+}
+
+__device__ __forceinline__ void store_y(const GemmArgs &g, uint32_t b, uint32_t n, float v, bool add)
+{
+    store_y_at(g, (uint64_t)b * g.N + n, v, add);
 }
 
 // Decode one tile-aligned segment into the exponent plane of its tile.
@@ -311,8 +316,8 @@ decode_gemm_kernel(GemmArgs g)
 }
 
 
-// ---------------------------------------------------------------- B <= 32
-// Segment-parallel form for one batch tile.  The tile-synchronous kernel
+// ---------------------------------------------------------------- B <= 64
+// Segment-parallel form for one or two batch tiles.  The tile-synchronous kernel
 // above decodes a weight tile (~6 segments) per step with a barrier between
 // steps, so a workgroup waits for one segment's decode latency per 16K
 // weights.  Here every wave walks its own run of segments of one row block,
@@ -324,7 +329,8 @@ decode_gemm_kernel(GemmArgs g)
 // the 8-column-group tile order, unit u of a tile is row u % 32, columns
 // 8 * (u / 32) .. + 7, so a round is exactly the B operand of one
 // v_mfma_f32_32x32x16_bf16 (lanes 0..31 the even column group, 32..63 the
-// odd one).  Elements of the round outside the segment are masked to zero,
+// odd one), issued once per batch tile.  Elements of the round outside the
+// segment are masked to zero,
 // so the neighbouring segments that share a round add their own parts.
 constexpr int kSegRounds = 4;   // rounds whose operands are loaded before the decode
 
@@ -357,10 +363,15 @@ __device__ __forceinline__ bool stage_seg(const SegLoad &L, bool stored, uint32_
     return true;
 }
 
-template <int K, int WAVES>
+template <int K, int WAVES, int MT>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 decode_gemm_seg_kernel(GemmArgs g)
 {
+    // MT batch tiles of 32 rows share each round's B operand.  With one tile
+    // its x operands are loaded with the sign+mantissa bytes before the
+    // decode; with two, the registers go to the second accumulator and x
+    // is loaded in the round (from L2).
+    static_assert(MT == 1 || MT == 2, "one or two batch tiles");
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -374,7 +385,6 @@ decode_gemm_seg_kernel(GemmArgs g)
     __syncthreads();
 
     const uint32_t n_l = lane & 31, khalf = lane >> 5;
-    const bool x_row = n_l < g.B;
     const bool stored = g.counts != nullptr;
     const uint64_t n_elems = (uint64_t)g.N * g.K;
     const uint32_t n_units = g.n_rowblocks * g.parts;
@@ -386,9 +396,11 @@ decode_gemm_seg_kernel(GemmArgs g)
         const uint64_t len = S1 > S0 ? (S1 - S0 + g.parts - 1) / g.parts : 0;
         const uint64_t s_begin = S0 + part * len, s_end = min(S1, s_begin + len);
 
-        f32x16 acc;
+        f32x16 acc[MT];
 #pragma unroll
-        for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+        for (int m = 0; m < MT; m++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc[m][j] = 0.0f;
 
         uint64_t s = s_begin + wave;
         SegLoad nx{};
@@ -412,34 +424,47 @@ decode_gemm_seg_kernel(GemmArgs g)
             const uint32_t kt = valid ? (uint32_t)(t - (uint64_t)rb * g.tiles_per_row) : 0u;
             const uint8_t *smt = g.sm + tile_start;
             const uint16_t *xr = g.x + (uint64_t)n_l * g.K + kt * kTC + khalf * 8;
+            // x operand of batch tile m in round r (rows past B are zero)
+            auto x_op = [&](int m, uint32_t r) {
+                return n_l + 32u * m < g.B
+                           ? *reinterpret_cast<const uint4 *>(xr + (uint64_t)(32u * m) * g.K + (u0 / 64 + r) * 16)
+                           : make_uint4(0, 0, 0, 0);
+            };
 
             // operands of the first rounds (rounds past the segment reload its last round)
             uint2 smp[kSegRounds];
-            uint4 xp[kSegRounds];
+            uint4 xp[MT == 1 ? kSegRounds : 1];
             const uint32_t last_round = nrounds ? nrounds - 1 : 0u;
 #pragma unroll
             for (int r = 0; r < kSegRounds; r++) {
                 const uint32_t rr = min((uint32_t)r, last_round);
                 smp[r] = *reinterpret_cast<const uint2 *>(smt + 8 * (u0 + 64 * rr + lane));
-                xp[r] = x_row ? *reinterpret_cast<const uint4 *>(xr + (u0 / 64 + rr) * 16) : make_uint4(0, 0, 0, 0);
+                if constexpr (MT == 1) xp[r] = x_op(0, rr);
             }
 
             if (valid && stage_seg<K>(cur, stored, stg + head, fast, chain, lane)) {
-                auto round = [&](uint32_t r, uint2 sv, uint4 xa) {
+                auto round = [&](uint32_t r, uint2 sv, const uint4 *xa) {
+                    uint4 xl[MT];
+                    if constexpr (MT > 1)
+#pragma unroll
+                        for (int m = 0; m < MT; m++) xl[m] = x_op(m, r);
                     const uint32_t u = u0 + 64 * r + lane;
-                    const uint2 m = unit_mask((int)lo - (int)(8 * u), (int)hi - (int)(8 * u));
+                    const uint2 mk = unit_mask((int)lo - (int)(8 * u), (int)hi - (int)(8 * u));
                     const uint2 rx = ld64(stg + 8 * (64 * r + lane));
-                    const uint2 a = assemble4(sv.x & m.x, rx.x & m.x), b = assemble4(sv.y & m.y, rx.y & m.y);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa),
-                                                                 __builtin_bit_cast(bf16x8, v4u32{a.x, a.y, b.x, b.y}),
-                                                                 acc, 0, 0, 0);
+                    const uint2 a = assemble4(sv.x & mk.x, rx.x & mk.x), b = assemble4(sv.y & mk.y, rx.y & mk.y);
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, v4u32{a.x, a.y, b.x, b.y});
+#pragma unroll
+                    for (int m = 0; m < MT; m++)
+                        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, MT == 1 ? *xa : xl[m]), bop, acc[m], 0, 0, 0);
                 };
 #pragma unroll
                 for (int r = 0; r < kSegRounds; r++)
-                    if ((uint32_t)r < nrounds) round(r, smp[r], xp[r]);
+                    if ((uint32_t)r < nrounds) round(r, smp[r], &xp[MT == 1 ? r : 0]);
                 for (uint32_t r = kSegRounds; r < nrounds; r++) {
                     const uint2 sv = *reinterpret_cast<const uint2 *>(smt + 8 * (u0 + 64 * r + lane));
-                    const uint4 xa = x_row ? *reinterpret_cast<const uint4 *>(xr + (u0 / 64 + r) * 16) : make_uint4(0, 0, 0, 0);
+                    uint4 xa[1];
+                    if constexpr (MT == 1) xa[0] = x_op(0, r);
                     round(r, sv, xa);
                 }
             }
@@ -447,26 +472,36 @@ decode_gemm_seg_kernel(GemmArgs g)
             s = s_next;
         }
 
-        // reduce the waves' partial sums through LDS (the staging is free after the barrier)
-        __syncthreads();
+        // reduce the waves' partial sums through LDS, one batch tile at a
+        // time (the staging is free after the barrier and holds WAVES - 1
+        // tiles of 32 x 32 floats)
         lds_f32 *red = (lds_f32 *)(size_t)area;
-        if (wave > 0)
 #pragma unroll
-            for (int j = 0; j < 16; j++) red[(wave - 1) * 1024 + j * 64 + lane] = acc[j];
-        __syncthreads();
-        if (wave == 0) {
+        for (int m = 0; m < MT; m++) {
+            __syncthreads();
+            if (wave > 0)
+#pragma unroll
+                for (int j = 0; j < 16; j++) red[(wave - 1) * 1024 + j * 64 + lane] = acc[m][j];
+            __syncthreads();
+            if (wave == 0) {
 #pragma unroll 1
-            for (uint32_t w = 1; w < (uint32_t)WAVES; w++)
+                for (uint32_t w = 1; w < (uint32_t)WAVES; w++)
 #pragma unroll
-                for (int j = 0; j < 16; j++) acc[j] += red[(w - 1) * 1024 + j * 64 + lane];
-            // y[b, n]: lane holds n = rb*32 + lane%32, b = 8*blk + 4*(lane/32) + e
+                    for (int j = 0; j < 16; j++) acc[m][j] += red[(w - 1) * 1024 + j * 64 + lane];
+                // y[b, n]: lane holds n = rb*32 + lane%32, b = 32*m + 8*blk + 4*(lane/32) + e.
+                // B and N pass through an empty asm so that the sixteen
+                // addresses and masks are formed here, not kept in registers
+                // across the unit loop.
+                uint32_t nB = g.B, nN = g.N;
+                asm volatile("" : "+s"(nB), "+s"(nN));
 #pragma unroll
-            for (int blk = 0; blk < 4; blk++)
+                for (int blk = 0; blk < 4; blk++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const uint32_t b = 8 * blk + 4 * khalf + e;
-                    if (b < g.B) store_y(g, b, rb * kTR + n_l, acc[4 * blk + e], g.parts > 1);
-                }
+                    for (int e = 0; e < 4; e++) {
+                        const uint32_t b = 32 * m + 8 * blk + 4 * khalf + e;
+                        if (b < nB) store_y_at(g, (uint64_t)b * nN + rb * kTR + n_l, acc[m][4 * blk + e], g.parts > 1);
+                    }
+            }
         }
         __syncthreads();   // the staging is reused by the next unit
     }
@@ -552,9 +587,9 @@ int launch(GemmArgs a, uint32_t lds, hipStream_t st)
     return DF11_OK;
 }
 
-// Segment-parallel launch (B <= 32): row blocks split into `parts` segment
-// ranges so that every resident workgroup slot has work.
-template <int K, int W>
+// Segment-parallel launch (B <= 32 * MT): row blocks split into `parts`
+// segment ranges so that every resident workgroup slot has work.
+template <int K, int W, int MT>
 int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_t st)
 {
     a.stg_bytes = std::max(4096u, (max_seg_elems + 1024u + 16u + 15u) & ~15u);
@@ -570,7 +605,7 @@ int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_
         if (q_dev == dev && q_lds == lds) per_cu = q_per_cu;
     }
     if (!per_cu) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gemm_seg_kernel<K, W>, W * 64, lds) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gemm_seg_kernel<K, W, MT>, W * 64, lds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         std::lock_guard<std::mutex> lk(mu);
@@ -593,7 +628,7 @@ int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_
     if (parts > 1) clear_y(a, st);
     const uint64_t units = (uint64_t)a.n_rowblocks * parts;
     const uint32_t groups = (uint32_t)std::min<uint64_t>(units, 1u << 20);
-    hipLaunchKernelGGL((decode_gemm_seg_kernel<K, W>), dim3(groups), dim3(W * 64), lds, st, a);
+    hipLaunchKernelGGL((decode_gemm_seg_kernel<K, W, MT>), dim3(groups), dim3(W * 64), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
     return DF11_OK;
@@ -603,7 +638,10 @@ template <int K>
 int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_t st)
 {
     // the tile-synchronous kernel also serves the w_debug output
-    if (a.B <= 32 && !a.w_debug && !getenv("DF11_GEMM_TILED")) return launch_seg<K, 8>(a, n_tables, max_seg_elems, st);
+    if (a.B <= 64 && !a.w_debug && !getenv("DF11_GEMM_TILED")) {
+        if (a.B <= 32) return launch_seg<K, 8, 1>(a, n_tables, max_seg_elems, st);
+        return launch_seg<K, 8, 2>(a, n_tables, max_seg_elems, st);
+    }
     constexpr int W = 8;
     const uint32_t lds = gemm_lds_bytes(K, n_tables);
     if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm tables do not fit in LDS");

@@ -2,10 +2,11 @@
 the C ABI: the decoded weights are bit-exact against the input (w_debug), and
 y matches the oracle's float32 product within 2e-3 relative Frobenius error
 (float32 accumulation differs only in summation order; BF16 products are
-exact).  Up to 32 rows of x take the segment-parallel kernel, which has no
-w_debug output: its decode is checked bit-exactly through y with x = rows
-of the identity, and every case checks y of the call without w_debug (the
-product path) as well as of the call with it (the tile-synchronous kernel)."""
+exact).  Up to 64 rows of x take the segment-parallel kernel (one batch
+tile of 32 rows up to 32, two above), which has no w_debug output: its
+decode is checked bit-exactly through y with x = rows of the identity, and
+every case checks y of the call without w_debug (the product path) as well
+as of the call with it (the tile-synchronous kernel)."""
 import ctypes
 import sys
 
@@ -131,14 +132,17 @@ def test_identity_x_recovers_weights_exactly():
     assert np.array_equal(y, _as_f32(W)[:, :B].T)
 
 
+@pytest.mark.parametrize("rows", [32, 48, 64])
 @pytest.mark.parametrize("N,K,seed", [(96, 1536, 28), (256, 4096, 29)])
-def test_identity_x_recovers_weights_segment_parallel(N, K, seed):
-    """Every weight through the segment-parallel kernel (32 rows of x),
-    compared exactly: masks at segment edges, rounds and the row block
-    reduction (and the K split of y for the 8-row-block weight)."""
-    _say("case gemm identity segment-parallel N=%d K=%d" % (N, K))
+def test_identity_x_recovers_weights_segment_parallel(N, K, seed, rows):
+    """Every weight through the segment-parallel kernel (32, 48 or 64 rows
+    of x: one batch tile, then two with the second full or half empty),
+    compared exactly: masks at segment edges, rounds, the row block
+    reduction per batch tile (and the K split of y for the 8-row-block
+    weight)."""
+    _say("case gemm identity segment-parallel N=%d K=%d rows=%d" % (N, K, rows))
     W = synth.normal_bf16(N * K, 0.02, seed=seed).reshape(N, K)
-    assert np.array_equal(_recover_by_identity(W), _as_f32(W))
+    assert np.array_equal(_recover_by_identity(W, rows=rows), _as_f32(W))
 
 
 def test_identity_x_recovers_long_code_weights():
@@ -150,6 +154,7 @@ def test_identity_x_recovers_long_code_weights():
     W = synth.adversarial_bf16(N * K, seed=30).reshape(N, K)
     W = np.where((W >> 7) & 0xFF == 0xFF, W & 0x807F, W).astype(np.uint16)
     assert np.array_equal(_recover_by_identity(W), _as_f32(W))
+    assert np.array_equal(_recover_by_identity(W, rows=64), _as_f32(W))
 
 
 def test_adversarial_weights_decode_exactly():
