@@ -326,8 +326,10 @@ __device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint6
 // give every lane of a wave-wide store a different row; here lane l takes
 // row 8k + l / 8 of group g + l % 8, so each store instruction writes 8 rows
 // x 128 contiguous bytes and each sign+mantissa load reads 8 runs of 64
-// contiguous bytes (loaded after the decode: registers held across it cost
-// more occupancy than the wait costs).  Ragged ends as in merge_range.
+// contiguous bytes.  The loads of the first two 8-group batches (the whole
+// segment at up to ~4K elements) go out before the decode, like the
+// row-major prefetch; later batches load after it.  Ragged ends as in
+// merge_range.
 struct TileSeg {
     const uint8_t *smt;        // sign+mantissa bytes of the tile
     uint16_t *obase;           // output of the tile's first element
@@ -363,8 +365,23 @@ __device__ __forceinline__ bool tile_unit_in(const TileSeg &q, uint32_t gb, uint
     return gb + (lane & 7u) <= q.grp_b && e0 >= q.lo && e0 + 8 <= q.hi;
 }
 
+// sign+mantissa bytes of the lane's units in the first two group batches,
+// loaded before the decode (units outside the segment reload its first unit)
+__device__ __forceinline__ void prefetch_tile8(const TileSeg &q, uint32_t lane, bool stream, uint2 (&tsv)[8])
+{
+#pragma unroll
+    for (int bb = 0; bb < 2; bb++)
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t gb = q.grp_a + 8u * bb;
+            const uint32_t e0 = tile_unit(gb, k, lane);
+            tsv[4 * bb + k] = load_sm8(q.smt + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)), stream);
+        }
+}
+
 __device__ __forceinline__ void merge_tile_groups8(const SegPlan &p, const ViewArgs &v, const TileSeg &q,
-                                                   uint32_t rag_sm, uint32_t stg, uint32_t lane, bool stream)
+                                                   const uint2 (&tsv)[8], uint32_t rag_sm, uint32_t stg,
+                                                   uint32_t lane, bool stream)
 {
     const RaggedLane rg = ragged_lane(p.g0, p.g1, lane);
     if (rg.act) {
@@ -380,7 +397,12 @@ __device__ __forceinline__ void merge_tile_groups8(const SegPlan &p, const ViewA
             store_bf16x8(q.obase + (uint64_t)r * v.cols + (grp << 3), make_uint4(a.x, a.y, b.x, b.y), stream);
         }
     };
-    for (uint32_t gb = q.grp_a; gb <= q.grp_b; gb += 8) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) unit(q.grp_a, k, tsv[k]);
+    if (q.grp_a + 8 <= q.grp_b)
+#pragma unroll
+        for (int k = 0; k < 4; k++) unit(q.grp_a + 8, k, tsv[4 + k]);
+    for (uint32_t gb = q.grp_a + 16; gb <= q.grp_b; gb += 8) {
         uint2 sv[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
@@ -399,7 +421,7 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t lane = lane_id();
+    const uint32_t lane0 = lane_id();
     const uint32_t stg = lds0 + 16 + wave * t.stg_bytes;
     const uint32_t fast = lds0 + 16 + WAVES * t.stg_bytes;
     const uint32_t chain = fast + (8u << K);
@@ -413,12 +435,18 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
     SegLoad nx{};
     if (s < n_total) {
         vi = view_of(b, s);
-        nx = load_segment(b.v[vi], s - b.seg_begin[vi], lane);
+        nx = load_segment(b.v[vi], s - b.seg_begin[vi], lane0);
     }
     stage_tables<K, WAVES * 64>(fast, chain, t.fast, t.chain, t.n_chain);
     __syncthreads();
     if (s >= n_total) return;
     for (;;) {
+        // In the tile-order kernel the lane index passes through an empty
+        // asm statement, so that its lane-derived offsets are formed per
+        // segment: held across the loop they spill (27 VGPRs with the
+        // prefetch below).  The row-major kernel is faster as it is.
+        uint32_t lane = lane0;
+        if constexpr (TILE8) asm volatile("" : "+v"(lane));
         const SegLoad cur = nx;
         const ViewArgs &v = b.v[vi];
         const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
@@ -431,20 +459,29 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
         const uint32_t vi_next = more ? view_of(b, s_next, vi) : vi;
         nx = load_segment(b.v[vi_next], (more ? s_next : s) - b.seg_begin[vi_next], lane);
         uint2 smp[kPrefetchRounds];
+        uint2 tsv[TILE8 ? 8 : 1];
+        TileSeg q{};
         bool tiled = false;
         if constexpr (TILE8) {   // launches holding a view in the fused kernel's tile order
             const uint32_t ts = 5 + ((v.pow2 >> 5) & 31u);
             tiled = p.valid && v.kc == 8 && v.pow2 && v.tr == 32 && p.g1 > p.g0 && (p.g0 >> ts) == ((p.g1 - 1) >> ts);
+            if (tiled) {
+                q = tile_seg(p, v, stg);
+                prefetch_tile8(q, lane, stream, tsv);
+            }
         }
         if (!tiled) prefetch_sm(p, v.sm, lane, stream, smp);
         const RaggedLane rg = ragged_lane(p.g0, p.g1, lane);
         const uint32_t rag_sm = v.sm[p.valid && rg.act ? rg.g : 0];
 
         if (p.valid && stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane)) {
-            if (tiled)
-                merge_tile_groups8(p, v, tile_seg(p, v, stg), rag_sm, stg, lane, stream);
-            else
-                merge_range(p, p.g0, p.g1, smp, rag_sm, v.sm, ViewOut{v}, stg, lane, stream);
+            bool merged = false;
+            if constexpr (TILE8)
+                if (tiled) {
+                    merge_tile_groups8(p, v, q, tsv, rag_sm, stg, lane, stream);
+                    merged = true;
+                }
+            if (!merged) merge_range(p, p.g0, p.g1, smp, rag_sm, v.sm, ViewOut{v}, stg, lane, stream);
         }
         wave_lds_sync();   // the staging is reused by the next segment
         if (!more) break;
@@ -455,8 +492,8 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
 
 // Two kernels from one body, both at 8 waves per SIMD (64 VGPRs): the
 // row-major one, and one with the tile-order merge for launches that hold
-// such a view (its extra bookkeeping spills a few registers, which costs
-// less than fewer waves: 66 us against 74 us at 6 waves per SIMD on
+// such a view (its prefetch and bookkeeping spill a few registers, which
+// costs less than fewer waves: 55 us against 61 us at 7 waves per SIMD on
 // up_proj), so that the row-major kernel stays free of spills.
 template <int K, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))

@@ -48,11 +48,11 @@ class DF11Linear(torch.nn.Module):
     compressed.  mode "fused" (needs out % 32 == 0 and in % 512 == 0) runs
     df11_decode_gemm for up to fused_max_rows rows of x and decode + matmul
     above (default 64: on an up_proj-shaped weight, 14336 x 4096, the fused
-    call measured 77 us at 64 rows against 90 us for decoding the
-    tile-ordered weight and calling torch.matmul, and 122 us against 92 us
-    at 96 rows, since the fused kernel re-reads x for every 32-row block of
-    W); mode "decode" always decodes into the shared buffer and calls
-    torch.matmul.  "auto" picks "fused" when the shape allows it."""
+    call measured 66 us at 48 rows and 77 us at 64 rows against 78-79 us
+    for decoding the tile-ordered weight and calling torch.matmul, and
+    123 us against 80 us at 96 rows, since the fused kernel re-reads x for
+    every 32-row block of W); mode "decode" always decodes into the shared
+    buffer and calls torch.matmul.  "auto" picks "fused" when the shape allows it."""
 
     fused_max_rows = 64
 
