@@ -436,6 +436,54 @@ def other_configs(steps: int, warmup: int, seed: int = 0):
     return out
 
 
+def embedding_lookup(steps: int, warmup: int, seed: int = 0, vocab: int = 128256, dim: int = 4096):
+    """df11_decode_rows (the DF11Embedding lookup) on a vocabulary-sized table,
+    128256 x 4096 bf16 N(0, 0.02) in the row-major layout: B random token ids
+    per call (B = 1, 32, 2048), every returned row checked bit-exactly, timed
+    against torch's embedding gather on the BF16 table.  Algorithmic bytes
+    per row: the row's compressed bytes (exponent bits at the table's mean
+    code length plus one sign+mantissa byte per element) and its BF16 output."""
+    import torch
+    from huffman_decode_df11_amd import api, synth
+    W = synth.normal_bf16_torch(vocab, dim, seed=seed, index=900, device="cuda")
+    dt = api.encode_device(W, layout=api.make_layout(rows=vocab, cols=dim))
+    row_alg = dim * (dt.total_bits / dt.n / 8.0 + 1.0) + 2.0 * dim
+    rng = np.random.default_rng(seed + 77)
+
+    def timeit(f, n):
+        for _ in range(max(warmup, 3)):
+            f()
+        torch.cuda.synchronize()
+        _hold_queue(2.0 + 0.05 * n)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    out = {"workload": "embedding table %dx%d bf16 N(0,0.02), row-major layout, B random token ids per call"
+                       % (vocab, dim),
+           "bits_per_weight": round(dt.compressed_nbytes() * 8.0 / dt.n, 4), "by_tokens": {}}
+    for B in (1, 32, 2048):
+        ids = torch.from_numpy(rng.integers(0, vocab, B)).cuda()
+        buf = torch.empty(B, dim, dtype=torch.bfloat16, device="cuda")
+        api.decode_rows(dt, ids, out=buf)
+        torch.cuda.synchronize()
+        if not torch.equal(buf.view(torch.int16), W[ids].view(torch.int16)):
+            raise SystemExit("embedding lookup parity failed at B=%d" % B)
+        n = max(steps, 50)
+        us = timeit(lambda: api.decode_rows(dt, ids, out=buf), n)
+        us_t = timeit(lambda: torch.nn.functional.embedding(ids, W), n)
+        out["by_tokens"][str(B)] = {"us_per_call": round(us, 2), "torch_bf16_gather_us": round(us_t, 2),
+                                    "rows_per_s": round(B / (us * 1e-6), 1),
+                                    "hbm_frac": round(B * row_alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del W, dt
+    torch.cuda.empty_cache()
+    return out
+
+
 def shard_layer_decode(steps: int, warmup: int, ways: int = 8, copies: int = 4, seed: int = 0):
     """One GPU's share of the layer under an `ways`-way row split: the first
     1/ways of the rows of each of the seven matrices, one codebook, decoded
@@ -697,6 +745,7 @@ def main():
         result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
     if not args.no_model:
         result["other_configs"] = other_configs(args.steps, args.warmup, args.seed)
+        result["embedding_lookup"] = embedding_lookup(args.steps, args.warmup, args.seed)
     if not args.no_shard:
         # what one GPU does under an 8-way row split of each matrix (no collective)
         result["shard_8way"] = {

@@ -509,15 +509,40 @@ decode_kernel_t8(BatchArgs b, TableArgs t)
     decode_body<K, WAVES, true>(b, t);
 }
 
-// Row gather: one wave per requested row; the segments that overlap the row
-// are found by binary search on the segment records, decoded whole into the
-// staging, and only the row's elements are written.
+// Row gather: up to four waves per requested row (about as many as the
+// segments a row overlaps); the row's first segment is found by a 64-way
+// search on the segment records, wave j of the row decodes the overlapping
+// segments j, j + split, ... whole into its staging, and only the row's
+// elements are written.
 struct RowArgs {
     ViewArgs v;               // row-major view (out unused)
     const int64_t *rows;      // requested row ids
     uint16_t *out;            // [n_rows, cols]
     uint64_t n_rows, n_view_rows;
+    uint32_t split;           // waves per row: wave j of a row takes its overlapping segments j, j + split, ...
 };
+
+// The last segment whose first element is <= e (segment records sorted by
+// element offset): a 64-way search, every lane probing one of 64 evenly
+// spaced records of the open range per step, so a range of n segments
+// takes about log_65(n) dependent loads (3 for 170K segments) instead of
+// log_2(n).  Lane l probes p_l = s0 + (l + 1) * span / 65, non-decreasing
+// in l and inside [s0, s1); "record p <= e" holds for a prefix of the
+// lanes, whose length k gives the new range [p_(k-1), p_k).
+__device__ __forceinline__ uint64_t segment_of(const ViewArgs &v, uint64_t e, uint32_t lane)
+{
+    uint64_t s0 = 0, s1 = v.n_segments;   // invariant: elem_off[s0] <= e, and s1 = end or elem_off[s1] > e
+    while (s1 - s0 > 1) {
+        const uint64_t span = s1 - s0;
+        const uint64_t p = s0 + ((uint64_t)(lane + 1) * span) / 65u;
+        const bool le = (p <= s0) | (v.segs[p].elem_off <= e);
+        const uint32_t k = (uint32_t)__popcll(__ballot(le));
+        const uint64_t lo_p = s0 + ((uint64_t)k * span) / 65u;
+        if (k < 64) s1 = s0 + ((uint64_t)(k + 1) * span) / 65u;
+        s0 = lo_p;
+    }
+    return s0;
+}
 
 template <int K, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
@@ -534,18 +559,16 @@ decode_rows_kernel(RowArgs a, TableArgs t)
     __syncthreads();
 
     const ViewArgs &v = a.v;
-    for (uint64_t i = (uint64_t)blockIdx.x * WAVES + wave; i < a.n_rows; i += (uint64_t)gridDim.x * WAVES) {
+    const uint64_t items = a.n_rows * a.split;
+    for (uint64_t w = (uint64_t)blockIdx.x * WAVES + wave; w < items; w += (uint64_t)gridDim.x * WAVES) {
+        const uint64_t i = w / a.split;
+        const uint32_t j = (uint32_t)(w - i * a.split);
         const int64_t r = a.rows[i];
         if (r < 0 || (uint64_t)r >= a.n_view_rows) continue;   // out-of-range id: row left as it is
         const uint64_t lo = (uint64_t)r * v.cols, hi = lo + v.cols;
-        // last segment whose first element is <= lo
-        uint64_t s0 = 0, s1 = v.n_segments;   // invariant: elem_off[s0] <= lo < elem_off[s1] (or s1 = end)
-        while (s1 - s0 > 1) {
-            const uint64_t mid = (s0 + s1) >> 1;
-            if (v.segs[mid].elem_off <= lo) s0 = mid; else s1 = mid;
-        }
+        const uint64_t s0 = segment_of(v, lo, lane);
         const RowOut out{a.out + i * v.cols, lo};
-        for (uint64_t s = s0; s < v.n_segments; s++) {
+        for (uint64_t s = s0 + j; s < v.n_segments; s += a.split) {
             const SegLoad cur = load_segment(v, s, lane);
             if (cur.g0 >= hi) break;
             const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
@@ -853,7 +876,7 @@ template <int K, int W>
 int launch_rows_w(const RowArgs &a, const TableArgs &t, uint32_t lds, int resident, hipStream_t st)
 {
     const uint64_t per_cu = std::max(1, resident / W);
-    const uint64_t groups = std::min<uint64_t>((a.n_rows + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
+    const uint64_t groups = std::min<uint64_t>((a.n_rows * a.split + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
     hipLaunchKernelGGL((decode_rows_kernel<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
     return DF11_OK;
 }
@@ -863,7 +886,7 @@ int launch_rows(const RowArgs &a, const TableArgs &t, const df11_view *v, hipStr
 {
     int res[kNumChoices];
     resident_waves<K, false>(t, v, st, res);
-    const int i = pick_waves(res, a.n_rows, (uint64_t)device_cu_count());
+    const int i = pick_waves(res, a.n_rows * a.split, (uint64_t)device_cu_count());
     if (i < 0) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
     const uint32_t lds = lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables);
     switch (kWaveChoices[i]) {
@@ -898,6 +921,14 @@ extern "C" int df11_decode_rows(const df11_view *v, const int64_t *rows, uint64_
     a.out = out;
     a.n_rows = n_rows;
     a.n_view_rows = v->rows;
+    // a row spans about cols / (elements per segment) + 1 segments: that
+    // many waves per row (at most 4) decode them side by side
+    a.split = 1;
+    if (v->n_segments) {
+        const uint64_t per_seg = std::max<uint64_t>(1, v->n / v->n_segments);
+        a.split = (uint32_t)std::min<uint64_t>(4, v->cols / per_seg + 1);
+    }
+    if (n_rows > (UINT64_MAX >> 3)) return df11::fail(DF11_E_ARG, "df11_decode_rows: too many rows");
     TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, staging_bytes(v)};
     hipStream_t st = (hipStream_t)stream;
     switch (v->fast_bits) {

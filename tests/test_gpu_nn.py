@@ -28,10 +28,12 @@ def _i16(u):
     return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).cuda()
 
 
-@pytest.mark.parametrize("rows,cols", [(1000, 4096), (333, 24), (64, 40000)])
+@pytest.mark.parametrize("rows,cols", [(1000, 4096), (333, 24), (64, 40000), (4096, 4096)])
 def test_decode_rows_matches_input(rows, cols):
     """Random ids with repeats, the first and last rows; rows spanning one,
-    several and a fraction of a segment."""
+    several and a fraction of a segment (one, two and four waves per row),
+    and a table of ~5300 segments (three steps of the 64-way segment
+    search)."""
     _say("case decode_rows %dx%d" % (rows, cols))
     W = synth.normal_bf16(rows * cols, 0.02, seed=30).reshape(rows, cols)
     dt = api.encode(W, layout=api.make_layout(rows=rows, cols=cols)).to("cuda")
