@@ -510,8 +510,8 @@ decode_kernel_t8(BatchArgs b, TableArgs t)
 }
 
 // Row gather: up to four waves per requested row (about as many as the
-// segments a row overlaps); the row's first segment is found by a 64-way
-// search on the segment records, wave j of the row decodes the overlapping
+// segments a row overlaps); the row's first segment is found by segment_of,
+// wave j of the row decodes the overlapping
 // segments j, j + split, ... whole into its staging, and only the row's
 // elements are written.
 struct RowArgs {
@@ -523,7 +523,9 @@ struct RowArgs {
 };
 
 // The last segment whose first element is <= e (segment records sorted by
-// element offset): a 64-way search, every lane probing one of 64 evenly
+// element offset): one probe of the 64 records around the interpolated
+// position, then, if the answer lies outside them, a 64-way search, every
+// lane probing one of 64 evenly
 // spaced records of the open range per step, so a range of n segments
 // takes about log_65(n) dependent loads (3 for 170K segments) instead of
 // log_2(n).  Lane l probes p_l = s0 + (l + 1) * span / 65, non-decreasing
@@ -532,6 +534,18 @@ struct RowArgs {
 __device__ __forceinline__ uint64_t segment_of(const ViewArgs &v, uint64_t e, uint32_t lane)
 {
     uint64_t s0 = 0, s1 = v.n_segments;   // invariant: elem_off[s0] <= e, and s1 = end or elem_off[s1] > e
+    if (s1 > 64) {
+        // Segments hold nearly equal numbers of elements, so e / n * segments
+        // lands within a few records of the answer: the 64 records around it
+        // usually bracket it, and one load settles the search.
+        const uint64_t g = (uint64_t)((float)e * ((float)s1 / (float)v.n));
+        const uint64_t base = min(g > 32 ? g - 32 : 0, s1 - 64);
+        const bool le = v.segs[base + lane].elem_off <= e;
+        const uint32_t k = (uint32_t)__popcll(__ballot(le));
+        if (k > 0 && k < 64) return base + k - 1;
+        if (k == 0) s1 = base;
+        else s0 = base + 63;
+    }
     while (s1 - s0 > 1) {
         const uint64_t span = s1 - s0;
         const uint64_t p = s0 + ((uint64_t)(lane + 1) * span) / 65u;
@@ -544,8 +558,10 @@ __device__ __forceinline__ uint64_t segment_of(const ViewArgs &v, uint64_t e, ui
     return s0;
 }
 
+// (6 waves per SIMD by registers: the staging in LDS allows no more for
+// the usual tables, and at 8 the segment search spills)
 template <int K, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(6, 8)))
 decode_rows_kernel(RowArgs a, TableArgs t)
 {
     extern __shared__ __align__(16) uint8_t lds_raw[];

@@ -266,8 +266,9 @@ int df11_decode_batch(const df11_view *device_views, uint16_t *const *outs, uint
  * an embedding lookup that restores only the rows a batch uses ([P1] 2.2
  * item 3: weights are restored right before use).  rows: device int64 ids,
  * 8-byte aligned.  The segments that overlap each requested row are found
- * by a 64-way search on the segment records and decoded whole (up to four
- * waves per row, one segment each); only the row's elements are written.  An id outside [0, rows) leaves its output row
+ * from an interpolated guess, checked against the 64 segment records around
+ * it, else by a 64-way search, and decoded whole (up to four waves per row,
+ * one segment each); only the row's elements are written.  An id outside [0, rows) leaves its output row
  * unwritten.  Bit-exact like df11_decode.  Errors: E_ARG (null, misaligned,
  * tile-ordered view, cols not a multiple of 8), E_UNSUPPORTED, E_DEVICE. */
 int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t n_rows, uint16_t *out,

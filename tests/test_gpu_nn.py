@@ -43,6 +43,25 @@ def test_decode_rows_matches_input(rows, cols):
     assert torch.equal(out.view(torch.int16), _i16(W[ids]))
 
 
+@pytest.mark.parametrize("zeros_first", [True, False])
+def test_decode_rows_uneven_segments(zeros_first):
+    """Half the table all-zero rows (1-bit codes, ~8K elements per segment)
+    and half random 16-bit patterns (long codes, ~1K per segment): the
+    interpolated segment guess misses by hundreds of segments, below the
+    probed window in one order and above it in the other, so the lookup
+    falls back to the 64-way search.  Every row is looked up."""
+    rows, cols = 2048, 4096
+    _say("case decode_rows uneven zeros_first=%s" % zeros_first)
+    rnd = synth.adversarial_bf16(rows // 2 * cols, seed=39).reshape(rows // 2, cols)
+    zer = np.zeros_like(rnd)
+    W = np.ascontiguousarray(np.concatenate([zer, rnd] if zeros_first else [rnd, zer]))
+    dt = api.encode(W, layout=api.make_layout(rows=rows, cols=cols)).to("cuda")
+    ids = np.concatenate([np.arange(rows), np.random.default_rng(40).integers(0, rows, 300)])
+    out = api.decode_rows(dt, torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), _i16(W[ids]))
+
+
 def test_decode_rows_adversarial_and_bad_ids():
     rows, cols = 512, 1024
     _say("case decode_rows adversarial")
