@@ -316,7 +316,7 @@ decode_gemm_kernel(GemmArgs g)
 }
 
 
-// ---------------------------------------------------------------- B <= 64
+// ---------------------------------------------------------------- B <= 40
 // Segment-parallel form for one or two batch tiles.  The tile-synchronous kernel
 // above decodes a weight tile (~6 segments) per step with a barrier between
 // steps, so a workgroup waits for one segment's decode latency per 16K
@@ -507,6 +507,172 @@ decode_gemm_seg_kernel(GemmArgs g)
     }
 }
 
+// ---------------------------------------------------------------- B > 40
+// Wide batches.  In the tile-synchronous kernel every wave builds the B
+// operand of every k-step (exponent plane + sign+mantissa bytes, two
+// bit-selects and two byte permutes per four weights) for its own batch
+// tile, so a weight is assembled and its byte loaded once per batch tile.
+// Here the decoded tile is merged once per workgroup into a BF16 plane in
+// LDS, laid out in the tile order, which is the operand order of
+// v_mfma_f32_32x32x16_bf16: the B operand of k-step s for lane l is the 16
+// bytes of unit (2s + l/32) * 32 + l%32, a conflict-free 16-byte LDS read
+// shared by all batch tiles.  Per weight tile:
+//   1. the next tile's sign+mantissa bytes (4 units per thread) and this
+//      wave's first x operands are loaded, and the next tile's segments are
+//      decoded into the exponent plane (one wave per segment);
+//   2. matrix cores on the current tile from the BF16 plane;
+//   3. barrier; the next tile is merged into the BF16 plane; barrier.
+// LDS: one 16 KB exponent plane, one 32 KB BF16 plane and the tables.
+constexpr int kWideXAhead = 8;   // k-steps whose x operands are loaded before the decode
+
+template <int K, int MT, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+decode_gemm_wide_kernel(GemmArgs g)
+{
+    constexpr int kMPerWave = MT > WAVES ? MT / WAVES : 1;
+    constexpr int kKSlices = MT >= WAVES ? 1 : WAVES / MT;
+    constexpr int kSteps = (int)(kTC / 16) / kKSlices;             // k-steps per wave and tile
+    constexpr int kAhead = kSteps < kWideXAhead ? kSteps : kWideXAhead;
+    constexpr uint32_t kThreads = WAVES * 64;
+    constexpr uint32_t kPerThread = kTile / 8 / kThreads;           // merge units per thread
+    static_assert(kMPerWave == 1, "one batch tile per wave");
+    static_assert(kTile / 8 % kThreads == 0, "whole merge units per thread");
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = lane_id();
+    // [guard][exponent plane][BF16 plane][tables]
+    const uint32_t eplane = lds0 + 16;
+    const uint32_t wplane = eplane + kTile;
+    const uint32_t fast = wplane + 2 * kTile;
+    const uint32_t chain = fast + (8u << K);
+
+    stage_tables<K, kThreads>(fast, chain, g.fast, g.chain, g.n_chain);
+    __syncthreads();
+
+    const uint32_t kslice = kKSlices > 1 ? wave / MT : 0;
+    const uint32_t m = kKSlices > 1 ? wave % MT : wave;   // this wave's batch tile
+    const bool stored = g.counts != nullptr;
+    const uint32_t n_units = g.n_rowblocks * g.split;
+
+    // (tid: the thread index, passed through an empty asm statement per tile
+    // step so that the thread-derived addresses are formed where they are
+    // used instead of being kept in registers across the loops)
+    auto load_sm = [&](uint32_t tid, uint64_t t, uint2 (&sv)[kPerThread]) {
+#pragma unroll
+        for (uint32_t j = 0; j < kPerThread; j++)
+            sv[j] = *reinterpret_cast<const uint2 *>(g.sm + t * kTile + 8u * (tid + j * kThreads));
+    };
+    auto decode_tile = [&](uint64_t t) {
+        const uint64_t s1 = min(g.block_seg[t + 1], g.n_segments);
+        for (uint64_t s = g.block_seg[t] + wave; s < s1; s += WAVES)
+            decode_into_plane<K>(load_segment(g, s, lane), t * kTile, eplane, stored, fast, chain, lane);
+    };
+    // units u = thread + j * threads of the tile: exponent plane + bytes -> BF16 plane (and w_debug)
+    auto merge = [&](uint32_t tid, const uint2 (&sv)[kPerThread], uint32_t rb, uint32_t kt) {
+#pragma unroll
+        for (uint32_t j = 0; j < kPerThread; j++) {
+            const uint32_t u = tid + j * kThreads;
+            const uint2 rx = ld64(eplane + 8u * u);
+            const uint2 a = assemble4(sv[j].x, rx.x), b = assemble4(sv[j].y, rx.y);
+            *(lds_u4 *)(size_t)(wplane + 16u * u) = v4u32{a.x, a.y, b.x, b.y};
+            if (g.w_debug)
+                *reinterpret_cast<uint4 *>(g.w_debug + (uint64_t)(rb * kTR + (u & 31u)) * g.K + kt * kTC + (u >> 5) * kKC) =
+                    make_uint4(a.x, a.y, b.x, b.y);
+        }
+    };
+    auto x_op = [&](uint32_t tid, uint32_t kt, uint32_t ks) {
+        const uint32_t brow = m * 32 + (tid & 31u), khalf = (tid >> 5) & 1u;
+        return brow < g.B ? *reinterpret_cast<const uint4 *>(g.x + (uint64_t)brow * g.K + kt * kTC + ks * 16 + khalf * 8)
+                          : make_uint4(0, 0, 0, 0);
+    };
+
+    for (uint32_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+        const uint32_t rb = unit / g.split, sp = unit - rb * g.split;
+        const uint32_t kt0 = sp * g.tiles_per_split;
+        const uint32_t kt1 = min(kt0 + g.tiles_per_split, g.tiles_per_row);
+        const uint64_t trow = (uint64_t)rb * g.tiles_per_row;
+        f32x16 acc;
+#pragma unroll
+        for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+
+        {   // the first tile of the range
+            uint32_t tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            uint2 sv[kPerThread];
+            load_sm(tid, trow + kt0, sv);
+            decode_tile(trow + kt0);
+            __syncthreads();
+            merge(tid, sv, rb, kt0);
+            __syncthreads();
+        }
+        for (uint32_t kt = kt0; kt < kt1; kt++) {
+            uint32_t tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            const uint32_t n_l = tid & 31u, khalf = (tid >> 5) & 1u;
+            const bool has_next = kt + 1 < kt1;
+            uint2 sv[kPerThread];
+            uint4 xa[kAhead];
+#pragma unroll
+            for (int i = 0; i < kAhead; i++) xa[i] = x_op(tid, kt, kslice + i * kKSlices);
+            if (has_next) {
+                load_sm(tid, trow + kt + 1, sv);
+                decode_tile(trow + kt + 1);
+            }
+            // matrix cores on tile kt from the BF16 plane
+#pragma unroll
+            for (int i = 0; i < kAhead; i++) {
+                const uint32_t ks = kslice + i * kKSlices;
+                const v4u32 wb = *(const lds_u4 *)(size_t)(wplane + 16u * ((2 * ks + khalf) * kTR + n_l));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[i]),
+                                                             __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
+            }
+#pragma unroll 4
+            for (int i = kAhead; i < kSteps; i++) {
+                const uint32_t ks = kslice + i * kKSlices;
+                const uint4 xb = x_op(tid, kt, ks);
+                const v4u32 wb = *(const lds_u4 *)(size_t)(wplane + 16u * ((2 * ks + khalf) * kTR + n_l));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xb),
+                                                             __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
+            }
+            __syncthreads();   // the BF16 plane is read, the next tile's exponents are staged
+            if (has_next) {
+                merge(tid, sv, rb, kt + 1);
+                __syncthreads();
+            }
+        }
+
+        // reduce the k-slices through LDS (the BF16 plane is free after the last barrier)
+        lds_f32 *red = (lds_f32 *)(size_t)wplane;
+        if (kKSlices > 1) {
+            if (kslice > 0)
+#pragma unroll
+                for (int j = 0; j < 16; j++) red[((kslice - 1) * MT + m) * 1024 + j * 64 + lane] = acc[j];
+            __syncthreads();
+            if (kslice == 0) {
+#pragma unroll 1
+                for (uint32_t ksl = 1; ksl < (uint32_t)kKSlices; ksl++)
+#pragma unroll
+                    for (int j = 0; j < 16; j++) acc[j] += red[((ksl - 1) * MT + m) * 1024 + j * 64 + lane];
+            }
+        }
+        // y[b, n]: lane holds n = rb*32 + lane%32, b = 32*m + 8*blk + 4*(lane/32) + e
+        if (kslice == 0) {
+            const uint32_t n_l = lane & 31u, khalf = lane >> 5;
+            uint32_t nB = g.B, nN = g.N;
+            asm volatile("" : "+s"(nB), "+s"(nN));   // addresses formed here, not kept across the unit loop
+#pragma unroll
+            for (int blk = 0; blk < 4; blk++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t b = m * 32 + 8 * blk + 4 * khalf + e;
+                    if (b < nB) store_y_at(g, (uint64_t)b * nN + rb * kTR + n_l, acc[4 * blk + e], g.split > 1);
+                }
+        }
+        __syncthreads();   // the planes are reused by the next unit
+    }
+}
+
 __global__ void zero_kernel(float4 *p, uint64_t n4)
 {
     for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n4; i += (uint64_t)gridDim.x * blockDim.x)
@@ -547,9 +713,12 @@ int cu_count()
     return cus;
 }
 
-template <int K, int MT, int W>
+template <int K, int MT, int W, bool WIDE>
 int launch(GemmArgs a, uint32_t lds, hipStream_t st)
 {
+    void (*kern)(GemmArgs) = nullptr;
+    if constexpr (WIDE) kern = decode_gemm_wide_kernel<K, MT, W>;
+    else kern = decode_gemm_kernel<K, MT, W>;
     // resident workgroups per CU, queried once per (device, LDS size)
     static std::mutex mu;
     static int q_dev = -1, q_per_cu = 0;
@@ -561,7 +730,7 @@ int launch(GemmArgs a, uint32_t lds, hipStream_t st)
         if (q_dev == dev && q_lds == lds) per_cu = q_per_cu;
     }
     if (!per_cu) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gemm_kernel<K, MT, W>, W * 64, lds) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, W * 64, lds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         std::lock_guard<std::mutex> lk(mu);
@@ -581,7 +750,7 @@ int launch(GemmArgs a, uint32_t lds, hipStream_t st)
     if (a.split > 1) clear_y(a, st);
     const uint32_t units = a.n_rowblocks * a.split;
     const uint32_t groups = std::min<uint32_t>(units, slots);
-    hipLaunchKernelGGL((decode_gemm_kernel<K, MT, W>), dim3(groups), dim3(W * 64), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3(groups), dim3(W * 64), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
     return DF11_OK;
@@ -638,7 +807,10 @@ template <int K>
 int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_t st)
 {
     // the tile-synchronous kernel also serves the w_debug output
-    if (a.B <= 64 && !a.w_debug && !getenv("DF11_GEMM_TILED")) {
+    // segment-parallel up to 40 rows of x (one batch tile to 32, two above);
+    // from 41 rows the wide kernel is faster (up_proj: 58.5 against 60.7 us
+    // at 33 rows, 66.8 against 64.9 at 48, 76.4 against 67.7 at 64)
+    if (a.B <= 40 && !a.w_debug && !getenv("DF11_GEMM_TILED")) {
         if (a.B <= 32) return launch_seg<K, 8, 1>(a, n_tables, max_seg_elems, st);
         return launch_seg<K, 8, 2>(a, n_tables, max_seg_elems, st);
     }
@@ -646,10 +818,15 @@ int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, hipS
     const uint32_t lds = gemm_lds_bytes(K, n_tables);
     if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm tables do not fit in LDS");
     const uint32_t mt = (a.B + 31) / 32;
-    if (mt <= 1) return launch<K, 1, W>(a, lds, st);
-    if (mt <= 2) return launch<K, 2, W>(a, lds, st);
-    if (mt <= 4) return launch<K, 4, W>(a, lds, st);
-    return launch<K, 8, W>(a, lds, st);
+    if (mt <= 1) return launch<K, 1, W, false>(a, lds, st);
+    // two or more batch tiles: the kernel with the shared BF16 plane (which
+    // takes the place of the second exponent plane and 16 KB more);
+    // DF11_GEMM_NARROW selects the tile-synchronous kernel instead
+    const uint32_t lds_wide = lds + kTile;
+    const bool wide = lds_wide <= 160u * 1024u && !getenv("DF11_GEMM_NARROW");
+    if (mt <= 2) return wide ? launch<K, 2, W, true>(a, lds_wide, st) : launch<K, 2, W, false>(a, lds, st);
+    if (mt <= 4) return wide ? launch<K, 4, W, true>(a, lds_wide, st) : launch<K, 4, W, false>(a, lds, st);
+    return wide ? launch<K, 8, W, true>(a, lds_wide, st) : launch<K, 8, W, false>(a, lds, st);
 }
 
 }  // namespace

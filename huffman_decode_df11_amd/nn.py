@@ -47,14 +47,14 @@ class DF11Linear(torch.nn.Module):
     """A linear layer y = x W^T + b with W [out_features, in_features] held
     compressed.  mode "fused" (needs out % 32 == 0 and in % 512 == 0) runs
     df11_decode_gemm for up to fused_max_rows rows of x and decode + matmul
-    above (default 64: on an up_proj-shaped weight, 14336 x 4096, the fused
-    call measured 66 us at 48 rows and 77 us at 64 rows against 78-79 us
-    for decoding the tile-ordered weight and calling torch.matmul, and
-    123 us against 80 us at 96 rows, since the fused kernel re-reads x for
-    every 32-row block of W); mode "decode" always decodes into the shared
-    buffer and calls torch.matmul.  "auto" picks "fused" when the shape allows it."""
+    above (default 88: on an up_proj-shaped weight, 14336 x 4096, the fused
+    call measured 72 us at 64 rows and 78 us at 88 rows against 80 us for
+    decoding the tile-ordered weight and calling torch.matmul, and 82 us
+    against 79 us at 96 rows, since the fused kernel re-reads x for every
+    32-row block of W); mode "decode" always decodes into the shared buffer
+    and calls torch.matmul.  "auto" picks "fused" when the shape allows it."""
 
-    fused_max_rows = 64
+    fused_max_rows = 88
 
     def __init__(self, weight, bias: Optional[torch.Tensor] = None, mode: str = "auto", device="cuda",
                  codebook=None):

@@ -2,11 +2,13 @@
 the C ABI: the decoded weights are bit-exact against the input (w_debug), and
 y matches the oracle's float32 product within 2e-3 relative Frobenius error
 (float32 accumulation differs only in summation order; BF16 products are
-exact).  Up to 64 rows of x take the segment-parallel kernel (one batch
+exact).  Up to 40 rows of x take the segment-parallel kernel (one batch
 tile of 32 rows up to 32, two above), which has no w_debug output: its
-decode is checked bit-exactly through y with x = rows of the identity, and
-every case checks y of the call without w_debug (the product path) as well
-as of the call with it (the tile-synchronous kernel)."""
+decode is checked bit-exactly through y with x = rows of the identity.
+Above 40 rows (and for w_debug calls above 32) the wide kernel merges each
+tile once into a BF16 plane in LDS; up to 32 rows w_debug calls take the
+tile-synchronous kernel.  Every case checks y of the call without w_debug
+(the product path) as well as of the call with it."""
 import ctypes
 import sys
 
@@ -132,14 +134,15 @@ def test_identity_x_recovers_weights_exactly():
     assert np.array_equal(y, _as_f32(W)[:, :B].T)
 
 
-@pytest.mark.parametrize("rows", [32, 48, 64])
+@pytest.mark.parametrize("rows", [32, 40, 48, 64])
 @pytest.mark.parametrize("N,K,seed", [(96, 1536, 28), (256, 4096, 29)])
 def test_identity_x_recovers_weights_segment_parallel(N, K, seed, rows):
-    """Every weight through the segment-parallel kernel (32, 48 or 64 rows
-    of x: one batch tile, then two with the second full or half empty),
-    compared exactly: masks at segment edges, rounds, the row block
-    reduction per batch tile (and the K split of y for the 8-row-block
-    weight)."""
+    """Every weight through y alone, compared exactly: the segment-parallel
+    kernel at 32 and 40 rows of x (one batch tile, then two with the second
+    a quarter full: masks at segment edges, rounds, the row block reduction
+    per batch tile, the K split of y for the 8-row-block weight) and the
+    wide kernel at 48 and 64 rows (the merged BF16 plane, k-slice
+    reduction)."""
     _say("case gemm identity segment-parallel N=%d K=%d rows=%d" % (N, K, rows))
     W = synth.normal_bf16(N * K, 0.02, seed=seed).reshape(N, K)
     assert np.array_equal(_recover_by_identity(W, rows=rows), _as_f32(W))
