@@ -109,11 +109,14 @@ def test_small_weight_all_batch_shapes(B):
         assert _rel(got, orc.gemm_f32(X, W).astype(np.float64)) < TOL
 
 
-@pytest.mark.parametrize("N,K,B", [(256, 14336, 5), (128, 4096, 40), (32, 512, 256)])
+@pytest.mark.parametrize("N,K,B", [(256, 14336, 5), (128, 4096, 40), (32, 512, 256), (128, 4096, 72),
+                                   (64, 2048, 48)])
 def test_k_split_shapes(N, K, B):
     """Few 32-row blocks: the K range is split across workgroups and the
     partial sums meet in y (28 tiles per row in 7 ranges of 4; 8 tiles in 8
-    ranges; a single tile)."""
+    ranges; a single tile), through the segment-parallel kernel (5 and 40
+    rows of x) and the wide one with 8, 4 and 2 batch tiles (256, 72 and 48
+    rows)."""
     _say("case gemm split N=%d K=%d B=%d" % (N, K, B))
     W = synth.normal_bf16(N * K, 0.02, seed=26).reshape(N, K)
     X = synth.activations_bf16(B, K, seed=27)
