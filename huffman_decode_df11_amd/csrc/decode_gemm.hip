@@ -525,60 +525,85 @@ decode_gemm_seg_kernel(GemmArgs g)
 // LDS: one 16 KB exponent plane, one 32 KB BF16 plane and the tables.
 constexpr int kWideXAhead = 8;   // k-steps whose x operands are loaded before the decode
 
-template <int K, int MT, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+// RB row blocks per unit (8 * RB waves): each x operand feeds RB matrix
+// core products, so x is read from L2 once per RB row blocks.
+template <int K, int MT, int RB>
+__global__ void __launch_bounds__(8 * RB * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 decode_gemm_wide_kernel(GemmArgs g)
 {
-    constexpr int kMPerWave = MT > WAVES ? MT / WAVES : 1;
-    constexpr int kKSlices = MT >= WAVES ? 1 : WAVES / MT;
+    constexpr int WAVES = 8 * RB;
+    constexpr int kKSlices = WAVES / MT;
     constexpr int kSteps = (int)(kTC / 16) / kKSlices;             // k-steps per wave and tile
     constexpr int kAhead = kSteps < kWideXAhead ? kSteps : kWideXAhead;
     constexpr uint32_t kThreads = WAVES * 64;
-    constexpr uint32_t kPerThread = kTile / 8 / kThreads;           // merge units per thread
-    static_assert(kMPerWave == 1, "one batch tile per wave");
-    static_assert(kTile / 8 % kThreads == 0, "whole merge units per thread");
+    constexpr uint32_t kTileUnits = kTile / 8;
+    constexpr uint32_t kPerThread = RB * kTileUnits / kThreads;     // merge units per thread
+    static_assert(WAVES % MT == 0 && kPerThread * kThreads == RB * kTileUnits, "shape");
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = lane_id();
-    // [guard][exponent plane][BF16 plane][tables]
+    // [guard][RB exponent planes][RB BF16 planes][tables]
     const uint32_t eplane = lds0 + 16;
-    const uint32_t wplane = eplane + kTile;
-    const uint32_t fast = wplane + 2 * kTile;
+    const uint32_t wplane = eplane + RB * kTile;
+    const uint32_t fast = wplane + RB * 2 * kTile;
     const uint32_t chain = fast + (8u << K);
 
     stage_tables<K, kThreads>(fast, chain, g.fast, g.chain, g.n_chain);
     __syncthreads();
 
-    const uint32_t kslice = kKSlices > 1 ? wave / MT : 0;
-    const uint32_t m = kKSlices > 1 ? wave % MT : wave;   // this wave's batch tile
+    const uint32_t kslice = wave / MT;
+    const uint32_t m = wave % MT;   // this wave's batch tile
     const bool stored = g.counts != nullptr;
-    const uint32_t n_units = g.n_rowblocks * g.split;
+    const uint32_t n_groups = (g.n_rowblocks + RB - 1) / RB;
+    const uint32_t n_units = n_groups * g.split;
 
     // (tid: the thread index, passed through an empty asm statement per tile
     // step so that the thread-derived addresses are formed where they are
     // used instead of being kept in registers across the loops)
-    auto load_sm = [&](uint32_t tid, uint64_t t, uint2 (&sv)[kPerThread]) {
-#pragma unroll
-        for (uint32_t j = 0; j < kPerThread; j++)
-            sv[j] = *reinterpret_cast<const uint2 *>(g.sm + t * kTile + 8u * (tid + j * kThreads));
-    };
-    auto decode_tile = [&](uint64_t t) {
-        const uint64_t s1 = min(g.block_seg[t + 1], g.n_segments);
-        for (uint64_t s = g.block_seg[t] + wave; s < s1; s += WAVES)
-            decode_into_plane<K>(load_segment(g, s, lane), t * kTile, eplane, stored, fast, chain, lane);
-    };
-    // units u = thread + j * threads of the tile: exponent plane + bytes -> BF16 plane (and w_debug)
-    auto merge = [&](uint32_t tid, const uint2 (&sv)[kPerThread], uint32_t rb, uint32_t kt) {
+    auto load_sm = [&](uint32_t tid, uint32_t rb0, uint32_t nrb, uint32_t kt, uint2 (&sv)[kPerThread]) {
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; j++) {
-            const uint32_t u = tid + j * kThreads;
-            const uint2 rx = ld64(eplane + 8u * u);
-            const uint2 a = assemble4(sv[j].x, rx.x), b = assemble4(sv[j].y, rx.y);
-            *(lds_u4 *)(size_t)(wplane + 16u * u) = v4u32{a.x, a.y, b.x, b.y};
-            if (g.w_debug)
-                *reinterpret_cast<uint4 *>(g.w_debug + (uint64_t)(rb * kTR + (u & 31u)) * g.K + kt * kTC + (u >> 5) * kKC) =
-                    make_uint4(a.x, a.y, b.x, b.y);
+            const uint32_t u = tid + j * kThreads, r = u / kTileUnits, uu = u % kTileUnits;
+            const uint64_t t = (uint64_t)(rb0 + (r < nrb ? r : 0)) * g.tiles_per_row + kt;
+            sv[j] = *reinterpret_cast<const uint2 *>(g.sm + t * kTile + 8u * uu);
+        }
+    };
+    auto decode_tiles = [&](uint32_t rb0, uint32_t nrb, uint32_t kt) {
+        const auto *bs = as_const(g.block_seg);
+        uint64_t first[RB], count[RB], total = 0;
+#pragma unroll
+        for (int r = 0; r < RB; r++) {
+            const uint64_t t = (uint64_t)(rb0 + r) * g.tiles_per_row + kt;
+            first[r] = (uint32_t)r < nrb ? min(bs[t], g.n_segments) : 0;
+            const uint64_t end = (uint32_t)r < nrb ? min(bs[t + 1], g.n_segments) : 0;
+            count[r] = end > first[r] ? end - first[r] : 0;
+            total += count[r];
+        }
+        for (uint64_t j = wave; j < total; j += WAVES) {
+            uint64_t jj = j;
+            int r = 0;
+#pragma unroll
+            for (int q = 0; q + 1 < RB; q++)
+                if (r == q && jj >= count[q]) { jj -= count[q]; r = q + 1; }
+            const uint64_t t = (uint64_t)(rb0 + r) * g.tiles_per_row + kt;
+            decode_into_plane<K>(load_segment(g, first[r] + jj, lane), t * kTile, eplane + r * kTile, stored, fast,
+                                 chain, lane);
+        }
+    };
+    // exponent planes + bytes -> BF16 planes (and w_debug), units u = tid + j * threads
+    auto merge = [&](uint32_t tid, const uint2 (&sv)[kPerThread], uint32_t rb0, uint32_t nrb, uint32_t kt) {
+#pragma unroll
+        for (uint32_t j = 0; j < kPerThread; j++) {
+            const uint32_t u = tid + j * kThreads, r = u / kTileUnits, uu = u % kTileUnits;
+            if (r < nrb) {
+                const uint2 rx = ld64(eplane + r * kTile + 8u * uu);
+                const uint2 a = assemble4(sv[j].x, rx.x), b = assemble4(sv[j].y, rx.y);
+                *(lds_u4 *)(size_t)(wplane + r * 2 * kTile + 16u * uu) = v4u32{a.x, a.y, b.x, b.y};
+                if (g.w_debug)
+                    *reinterpret_cast<uint4 *>(g.w_debug + (uint64_t)((rb0 + r) * kTR + (uu & 31u)) * g.K + kt * kTC +
+                                               (uu >> 5) * kKC) = make_uint4(a.x, a.y, b.x, b.y);
+            }
         }
     };
     auto x_op = [&](uint32_t tid, uint32_t kt, uint32_t ks) {
@@ -588,22 +613,24 @@ decode_gemm_wide_kernel(GemmArgs g)
     };
 
     for (uint32_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
-        const uint32_t rb = unit / g.split, sp = unit - rb * g.split;
+        const uint32_t grp = unit / g.split, sp = unit - grp * g.split;
+        const uint32_t rb0 = grp * RB, nrb = min((uint32_t)RB, g.n_rowblocks - rb0);
         const uint32_t kt0 = sp * g.tiles_per_split;
         const uint32_t kt1 = min(kt0 + g.tiles_per_split, g.tiles_per_row);
-        const uint64_t trow = (uint64_t)rb * g.tiles_per_row;
-        f32x16 acc;
+        f32x16 acc[RB];
 #pragma unroll
-        for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+        for (int r = 0; r < RB; r++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc[r][j] = 0.0f;
 
-        {   // the first tile of the range
+        {   // the first tiles of the range
             uint32_t tid = threadIdx.x;
             asm volatile("" : "+v"(tid));
             uint2 sv[kPerThread];
-            load_sm(tid, trow + kt0, sv);
-            decode_tile(trow + kt0);
+            load_sm(tid, rb0, nrb, kt0, sv);
+            decode_tiles(rb0, nrb, kt0);
             __syncthreads();
-            merge(tid, sv, rb, kt0);
+            merge(tid, sv, rb0, nrb, kt0);
             __syncthreads();
         }
         for (uint32_t kt = kt0; kt < kt1; kt++) {
@@ -616,58 +643,66 @@ decode_gemm_wide_kernel(GemmArgs g)
 #pragma unroll
             for (int i = 0; i < kAhead; i++) xa[i] = x_op(tid, kt, kslice + i * kKSlices);
             if (has_next) {
-                load_sm(tid, trow + kt + 1, sv);
-                decode_tile(trow + kt + 1);
+                load_sm(tid, rb0, nrb, kt + 1, sv);
+                decode_tiles(rb0, nrb, kt + 1);
             }
-            // matrix cores on tile kt from the BF16 plane
+            // matrix cores on tile kt of every row block from the BF16 planes
+            auto mma = [&](uint32_t ks, uint4 xv) {
 #pragma unroll
-            for (int i = 0; i < kAhead; i++) {
-                const uint32_t ks = kslice + i * kKSlices;
-                const v4u32 wb = *(const lds_u4 *)(size_t)(wplane + 16u * ((2 * ks + khalf) * kTR + n_l));
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[i]),
-                                                             __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
-            }
+                for (int r = 0; r < RB; r++)
+                    if (RB == 1 || (uint32_t)r < nrb) {
+                        const v4u32 wb =
+                            *(const lds_u4 *)(size_t)(wplane + r * 2 * kTile + 16u * ((2 * ks + khalf) * kTR + n_l));
+                        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv),
+                                                                        __builtin_bit_cast(bf16x8, wb), acc[r], 0, 0, 0);
+                    }
+            };
+#pragma unroll
+            for (int i = 0; i < kAhead; i++) mma(kslice + i * kKSlices, xa[i]);
 #pragma unroll 4
             for (int i = kAhead; i < kSteps; i++) {
                 const uint32_t ks = kslice + i * kKSlices;
-                const uint4 xb = x_op(tid, kt, ks);
-                const v4u32 wb = *(const lds_u4 *)(size_t)(wplane + 16u * ((2 * ks + khalf) * kTR + n_l));
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xb),
-                                                             __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
+                mma(ks, x_op(tid, kt, ks));
             }
-            __syncthreads();   // the BF16 plane is read, the next tile's exponents are staged
+            __syncthreads();   // the BF16 planes are read, the next tiles' exponents are staged
             if (has_next) {
-                merge(tid, sv, rb, kt + 1);
+                merge(tid, sv, rb0, nrb, kt + 1);
                 __syncthreads();
             }
         }
 
-        // reduce the k-slices through LDS (the BF16 plane is free after the last barrier)
-        lds_f32 *red = (lds_f32 *)(size_t)wplane;
-        if (kKSlices > 1) {
-            if (kslice > 0)
+        // per row block: reduce the k-slices through LDS (the planes are free
+        // after the last barrier) and store y[b, n]: lane holds
+        // n = rb*32 + lane%32, b = 32*m + 8*blk + 4*(lane/32) + e
+        lds_f32 *red = (lds_f32 *)(size_t)eplane;
 #pragma unroll
-                for (int j = 0; j < 16; j++) red[((kslice - 1) * MT + m) * 1024 + j * 64 + lane] = acc[j];
-            __syncthreads();
-            if (kslice == 0) {
+        for (int r = 0; r < RB; r++) {
+            if (kKSlices > 1) {
+                if (r > 0) __syncthreads();
+                if (kslice > 0)
+#pragma unroll
+                    for (int j = 0; j < 16; j++) red[((kslice - 1) * MT + m) * 1024 + j * 64 + lane] = acc[r][j];
+                __syncthreads();
+                if (kslice == 0) {
 #pragma unroll 1
-                for (uint32_t ksl = 1; ksl < (uint32_t)kKSlices; ksl++)
+                    for (uint32_t ksl = 1; ksl < (uint32_t)kKSlices; ksl++)
 #pragma unroll
-                    for (int j = 0; j < 16; j++) acc[j] += red[((ksl - 1) * MT + m) * 1024 + j * 64 + lane];
-            }
-        }
-        // y[b, n]: lane holds n = rb*32 + lane%32, b = 32*m + 8*blk + 4*(lane/32) + e
-        if (kslice == 0) {
-            const uint32_t n_l = lane & 31u, khalf = lane >> 5;
-            uint32_t nB = g.B, nN = g.N;
-            asm volatile("" : "+s"(nB), "+s"(nN));   // addresses formed here, not kept across the unit loop
-#pragma unroll
-            for (int blk = 0; blk < 4; blk++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const uint32_t b = m * 32 + 8 * blk + 4 * khalf + e;
-                    if (b < nB) store_y_at(g, (uint64_t)b * nN + rb * kTR + n_l, acc[4 * blk + e], g.split > 1);
+                        for (int j = 0; j < 16; j++) acc[r][j] += red[((ksl - 1) * MT + m) * 1024 + j * 64 + lane];
                 }
+            }
+            if (kslice == 0 && (uint32_t)r < nrb) {
+                const uint32_t n_l = lane & 31u, khalf = lane >> 5;
+                uint32_t nB = g.B, nN = g.N;
+                asm volatile("" : "+s"(nB), "+s"(nN));   // addresses formed here, not kept across the unit loop
+#pragma unroll
+                for (int blk = 0; blk < 4; blk++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const uint32_t b = m * 32 + 8 * blk + 4 * khalf + e;
+                        if (b < nB)
+                            store_y_at(g, (uint64_t)b * nN + (rb0 + r) * kTR + n_l, acc[r][4 * blk + e], g.split > 1);
+                    }
+            }
         }
         __syncthreads();   // the planes are reused by the next unit
     }
@@ -713,12 +748,15 @@ int cu_count()
     return cus;
 }
 
-template <int K, int MT, int W, bool WIDE>
+// Row blocks per unit of work: RB (the wide kernel's row-block group) > 1
+// divides the unit count.
+template <int K, int MT, int W, bool WIDE, int RB = 1>
 int launch(GemmArgs a, uint32_t lds, hipStream_t st)
 {
     void (*kern)(GemmArgs) = nullptr;
-    if constexpr (WIDE) kern = decode_gemm_wide_kernel<K, MT, W>;
+    if constexpr (WIDE) kern = decode_gemm_wide_kernel<K, MT, RB>;
     else kern = decode_gemm_kernel<K, MT, W>;
+    const uint32_t n_groups = (a.n_rowblocks + RB - 1) / RB;
     // resident workgroups per CU, queried once per (device, LDS size)
     static std::mutex mu;
     static int q_dev = -1, q_per_cu = 0;
@@ -742,13 +780,13 @@ int launch(GemmArgs a, uint32_t lds, hipStream_t st)
     // split K when there are too few row blocks to fill every slot
     uint32_t split = 1;
     if (const char *e = getenv("DF11_GEMM_SPLIT")) split = (uint32_t)atoi(e);
-    else if (2 * a.n_rowblocks <= slots) split = (slots + a.n_rowblocks - 1) / a.n_rowblocks;
+    else if (2 * n_groups <= slots) split = (slots + n_groups - 1) / n_groups;
     split = std::max(1u, std::min(split, a.tiles_per_row));
     if (a.y_bf16) split = 1;   // one writer per BF16 element
     a.tiles_per_split = (a.tiles_per_row + split - 1) / split;
     a.split = (a.tiles_per_row + a.tiles_per_split - 1) / a.tiles_per_split;
     if (a.split > 1) clear_y(a, st);
-    const uint32_t units = a.n_rowblocks * a.split;
+    const uint32_t units = n_groups * a.split;
     const uint32_t groups = std::min<uint32_t>(units, slots);
     hipLaunchKernelGGL(kern, dim3(groups), dim3(W * 64), lds, st, a);
     hipError_t e = hipGetLastError();
@@ -824,9 +862,19 @@ int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, hipS
     // DF11_GEMM_NARROW selects the tile-synchronous kernel instead
     const uint32_t lds_wide = lds + kTile;
     const bool wide = lds_wide <= 160u * 1024u && !getenv("DF11_GEMM_NARROW");
-    if (mt <= 2) return wide ? launch<K, 2, W, true>(a, lds_wide, st) : launch<K, 2, W, false>(a, lds, st);
-    if (mt <= 4) return wide ? launch<K, 4, W, true>(a, lds_wide, st) : launch<K, 4, W, false>(a, lds, st);
-    return wide ? launch<K, 8, W, true>(a, lds_wide, st) : launch<K, 8, W, false>(a, lds, st);
+    // above 112 rows of x two row blocks share each x operand (a second
+    // exponent plane and BF16 plane; up_proj at 128 / 192 / 256 rows: 88.1 /
+    // 95.5 / 104.5 us against 92.6 / 113.7 / 141.0 with one, even at 96);
+    // DF11_GEMM_RB = 1 or 2 overrides
+    const uint32_t lds_wide2 = lds_wide + 3 * kTile;
+    const char *rbe = getenv("DF11_GEMM_RB");
+    const bool two = wide && lds_wide2 <= 160u * 1024u && (rbe ? atoi(rbe) == 2 : a.B > 112);
+    if (mt <= 2) return two ? launch<K, 2, 16, true, 2>(a, lds_wide2, st)
+                            : wide ? launch<K, 2, W, true>(a, lds_wide, st) : launch<K, 2, W, false>(a, lds, st);
+    if (mt <= 4) return two ? launch<K, 4, 16, true, 2>(a, lds_wide2, st)
+                            : wide ? launch<K, 4, W, true>(a, lds_wide, st) : launch<K, 4, W, false>(a, lds, st);
+    return two ? launch<K, 8, 16, true, 2>(a, lds_wide2, st)
+               : wide ? launch<K, 8, W, true>(a, lds_wide, st) : launch<K, 8, W, false>(a, lds, st);
 }
 
 }  // namespace

@@ -6,8 +6,9 @@ exact).  Up to 40 rows of x take the segment-parallel kernel (one batch
 tile of 32 rows up to 32, two above), which has no w_debug output: its
 decode is checked bit-exactly through y with x = rows of the identity.
 Above 40 rows (and for w_debug calls above 32) the wide kernel merges each
-tile once into a BF16 plane in LDS; up to 32 rows w_debug calls take the
-tile-synchronous kernel.  Every case checks y of the call without w_debug
+tile once into a BF16 plane in LDS, one row block per unit up to 112 rows
+and two above (DF11_GEMM_RB forces either); up to 32 rows w_debug calls
+take the tile-synchronous kernel.  Every case checks y of the call without w_debug
 (the product path) as well as of the call with it."""
 import ctypes
 import sys
