@@ -127,6 +127,24 @@ def test_k_split_shapes(N, K, B):
     assert _rel(yd, orc.gemm_f64(X, W)) < TOL
 
 
+@pytest.mark.parametrize("rb", ["1", "2"])
+@pytest.mark.parametrize("B", [64, 100, 256])
+def test_wide_kernel_row_block_modes(B, rb, monkeypatch):
+    """The wide kernel with one and with two row blocks per unit, each
+    forced (DF11_GEMM_RB) on a weight of three row blocks (so the last pair
+    has one) and a weight split along K: decoded weights bit-exact, y
+    within tolerance."""
+    monkeypatch.setenv("DF11_GEMM_RB", rb)
+    for N, K, seed in ((96, 1536, 41), (64, 4096, 42)):
+        _say("case gemm wide rb=%s B=%d N=%d K=%d" % (rb, B, N, K))
+        W = synth.normal_bf16(N * K, 0.02, seed=seed).reshape(N, K)
+        X = synth.activations_bf16(B, K, seed=seed + 1)
+        y, wd, yd = _run(W, X)
+        assert np.array_equal(wd, W), "decoded weights differ"
+        ref = orc.gemm_f64(X, W)
+        assert _rel(y, ref) < TOL and _rel(yd, ref) < TOL
+
+
 def test_identity_x_recovers_weights_exactly():
     # x = I: y[b, n] = W[n, b] exactly (one nonzero product per output)
     N, K, B = 64, 512, 256
