@@ -281,11 +281,18 @@ int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t
  * Products of BF16 values are exact in float32 and accumulate in float32.
  * w_debug: NULL, or a device [N, K] buffer that also receives the decoded
  * BF16 weights.  B in 1..256.  x, y and w_debug 16-byte aligned.  y is
- * overwritten.  When the weight has fewer 32-row blocks than the device has
- * workgroup slots, the K range is split and the partial sums are added into
- * y (cleared first, on the same stream) with float atomics, so the order of
- * those few additions, and with it the last bits of y, can differ from run
- * to run.  Errors: E_ARG (null, misaligned, layout not from
+ * overwritten.  When the weight has too few 32-row blocks to fill the
+ * device, a row block's work is split across workgroups (along K, or into
+ * runs of its segments) and the partial sums are added into y (cleared
+ * first, on the same stream) with float atomics, so the order of those few
+ * additions, and with it the last bits of y, can differ from run to run.
+ * The kernel is chosen by B: up to 40 rows a segment-parallel kernel, above
+ * that one that merges each decoded tile once into a BF16 tile in LDS shared
+ * by all batch tiles (two row blocks per workgroup above 112 rows); w_debug
+ * calls up to 32 rows take a tile-synchronous kernel.  The environment
+ * variables DF11_GEMM_TILED, DF11_GEMM_NARROW, DF11_GEMM_RB (1 or 2),
+ * DF11_GEMM_PARTS and DF11_GEMM_SPLIT override these choices for
+ * measurements.  Errors: E_ARG (null, misaligned, layout not from
  * df11_gemm_layout, B out of range), E_UNSUPPORTED, E_DEVICE. */
 int df11_decode_gemm(const df11_view *device_view, const uint16_t *x, uint32_t B,
                      float *y, uint16_t *w_debug, void *stream);
