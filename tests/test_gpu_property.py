@@ -1,0 +1,61 @@
+"""GPU property tests (derandomized): the decode kernels restore random
+small tensors bit for bit, through df11_decode for every value mix and
+aligned-block layout, and through df11_decode_rows for random row shapes
+and ids.  The value mixes are those of the host property test; expected
+values are the inputs themselves (decode(encode(u)) is the identity)."""
+import sys
+
+import numpy as np
+import pytest
+
+from huffman_decode_df11_amd import api
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+hypothesis = pytest.importorskip("hypothesis")
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+from test_property_encode import _values  # noqa: E402
+
+SETTINGS = settings(max_examples=40, deadline=None, derandomize=True,
+                    suppress_health_check=[HealthCheck.too_slow])
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@SETTINGS
+@given(kind=st.sampled_from(["normal", "specials", "few", "one", "uniform"]),
+       n=st.integers(1, 200000), seed=st.integers(0, 2 ** 31 - 1), align=st.sampled_from([0, 512, 16384]))
+def test_decode_random_tensors(kind, n, seed, align):
+    print("case decode", kind, n, seed, align, flush=True)
+    sys.stdout.flush()
+    u = _values(kind, n, seed)
+    dt = api.encode(u, layout=api.make_layout(align_elems=align)).to("cuda")
+    out = torch.full((n + 8,), 0x5555, dtype=torch.int16, device="cuda")
+    api.decode(dt, out=out.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    got = _bits(out)
+    assert np.array_equal(got[:n], u)
+    assert (got[n:] == 0x5555).all()
+
+
+@SETTINGS
+@given(kind=st.sampled_from(["normal", "specials", "few", "uniform"]),
+       rows=st.integers(1, 300), cols8=st.integers(1, 1200), seed=st.integers(0, 2 ** 31 - 1))
+def test_decode_rows_random_shapes(kind, rows, cols8, seed):
+    cols = 8 * cols8
+    print("case rows", kind, rows, cols, seed, flush=True)
+    sys.stdout.flush()
+    u = _values(kind, rows * cols, seed).reshape(rows, cols)
+    dt = api.encode(u, layout=api.make_layout(rows=rows, cols=cols)).to("cuda")
+    ids = np.random.default_rng(seed).integers(0, rows, 50)
+    ids[0], ids[-1] = 0, rows - 1
+    out = api.decode_rows(dt, torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out).reshape(ids.size, cols), u[ids])

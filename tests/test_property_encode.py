@@ -1,0 +1,82 @@
+"""Property tests of the host encoder against the oracle (CPU): for random
+small tensors (value mixes with special values and few-symbol alphabets,
+sizes from 1 element), layouts (chunk bytes, aligned blocks) and code-length
+limits, the library's stream, sign+mantissa bytes, gaps, code counts and
+segment records equal the oracle's step-by-step encoding, the validator
+accepts them, and the oracle's bit-serial decoder restores the input.
+Examples are derandomized, so every run checks the same cases."""
+import math
+
+import numpy as np
+import pytest
+
+from huffman_decode_df11_amd import _lib, api
+from oracle import oracle as orc
+
+hypothesis = pytest.importorskip("hypothesis")
+from hypothesis import HealthCheck, assume, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+
+def _values(kind: str, n: int, seed: int) -> np.ndarray:
+    """BF16 bit patterns of one of several value mixes."""
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        f = rng.normal(0.0, 10.0 ** rng.uniform(-4, 1), n).astype(np.float32)
+        return (f.view(np.uint32) >> 16).astype(np.uint16)
+    if kind == "specials":   # zeros, subnormals, infinities, NaNs mixed into normals
+        f = rng.normal(0.0, 0.02, n).astype(np.float32)
+        u = (f.view(np.uint32) >> 16).astype(np.uint16)
+        pool = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC0, 0xFFFF, 0x7F81], np.uint16)
+        pick = rng.random(n) < 0.2
+        u[pick] = pool[rng.integers(0, pool.size, int(pick.sum()))]
+        return u
+    if kind == "few":        # two to five distinct exponents, random signs and mantissas
+        exps = rng.choice(256, size=int(rng.integers(2, 6)), replace=False)
+        e = exps[rng.integers(0, exps.size, n)]
+        return ((rng.integers(0, 2, n) << 15) | (e << 7) | rng.integers(0, 128, n)).astype(np.uint16)
+    if kind == "one":        # a single exponent
+        e = int(rng.integers(0, 256))
+        return ((rng.integers(0, 2, n) << 15) | (e << 7) | rng.integers(0, 128, n)).astype(np.uint16)
+    return rng.integers(0, 65536, n).astype(np.uint16)   # "uniform": every exponent
+
+
+@settings(max_examples=300, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.filter_too_much])
+@given(kind=st.sampled_from(["normal", "specials", "few", "one", "uniform"]),
+       n=st.integers(1, 3000),
+       seed=st.integers(0, 2 ** 31 - 1),
+       chunk_bytes=st.sampled_from([8, 16, 32]),
+       align=st.sampled_from([0, 0, 512, 4096]),
+       lmax_slack=st.integers(0, 24))
+def test_encoder_matches_oracle_on_random_tensors(kind, n, seed, chunk_bytes, align, lmax_slack):
+    u = _values(kind, n, seed)
+    hist = api.hist_accumulate(u)
+    distinct = int((hist > 0).sum())
+    lmax = min(32, max(1, math.ceil(math.log2(max(distinct, 2)))) + lmax_slack)
+    try:
+        cb = api.build_codebook(hist, max_len=lmax)
+    except _lib.DF11Error:
+        assume(False)   # this length limit needs more lookup tables than a codebook may hold
+    ln = api.codebook_lengths(cb)
+    assert int(ln.max()) <= lmax
+    lay = api.make_layout(chunk_bytes=chunk_bytes, align_elems=align)
+    if 8 * chunk_bytes // max(1, cb.min_len) > 255:
+        # a chunk could hold more codes than its count byte records: refused
+        with pytest.raises(_lib.DF11Error):
+            api.encode(u, codebook=cb, layout=lay)
+        return
+    enc = api.encode(u, codebook=cb, layout=lay)
+    ref = orc.encode(u, lengths=ln, chunk_bytes=chunk_bytes, seg_lanes=64, align_elems=align)
+    assert enc.total_bits == ref.total_bits
+    assert np.array_equal(enc.stream_bytes_msb_first(), ref.E)
+    assert np.array_equal(enc.sm[:enc.n], ref.sm)
+    assert enc.n_segments == ref.n_segments
+    assert np.array_equal(enc.gaps, ref.gaps)
+    assert np.array_equal(enc.counts, ref.counts)
+    assert np.array_equal(enc.seg_elem, ref.seg_elem)
+    assert np.array_equal(enc.seg_nbits[:-1], ref.seg_nbits)
+    enc.validate()
+    out = orc.decode(enc.stream_bytes_msb_first(), enc.total_bits, enc.sm[:enc.n], enc.n, ln,
+                     seg_bits=8 * 64 * chunk_bytes, align_elems=align)
+    assert np.array_equal(out, u)
