@@ -26,6 +26,8 @@
 // stream it.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
@@ -640,18 +642,7 @@ uint32_t staging_bytes(const df11_view *v)
     return (16 + tmax + 32 + 15) & ~15u;
 }
 
-int device_cu_count()
-{
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return 256;
-        hipDeviceProp_t p;
-        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return 256;
-        cus = p.multiProcessorCount;
-    }
-    return cus;
-}
+int device_cu_count() { return df11::cu_count(); }
 
 ViewArgs make_args(const df11_view *v, uint16_t *out)
 {
@@ -979,3 +970,23 @@ extern "C" int df11_decode_batch(const df11_view *views, uint16_t *const *outs, 
     }
     return DF11_OK;
 }
+
+namespace df11 {
+
+int cu_count()
+{
+    constexpr int kDevices = 64;
+    static std::atomic<int> cached[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 256;
+    if (dev >= 0 && dev < kDevices) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+}  // namespace df11

@@ -736,17 +736,7 @@ uint32_t gemm_lds_bytes(uint32_t fast_bits, uint32_t n_tables)
     return 16 + 2 * kTile + (8u << fast_bits) + n_tables * 512u;
 }
 
-int cu_count()
-{
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        hipDeviceProp_t p;
-        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess) return 256;
-        cus = p.multiProcessorCount;
-    }
-    return cus;
-}
+int cu_count() { return df11::cu_count(); }
 
 // Row blocks per unit of work: RB (the wide kernel's row-block group) > 1
 // divides the unit count.

@@ -23,6 +23,9 @@ int check_layout(const df11_layout &L, uint64_t n);
 // A chunk's code count is stored in a byte: chunk bits / shortest code <= 255.
 int check_counts_fit(const df11_layout &L, const df11_codebook *cb);
 
+// Compute units of the current device (queried once per device).
+int cu_count();
+
 }  // namespace df11
 
 struct df11_encoded {
