@@ -223,6 +223,31 @@ def test_up_proj_full_size(B):
     assert np.array_equal(got16, orc.round_bf16(y.cpu().numpy()))
 
 
+@pytest.mark.parametrize("B", [1, 40, 64, 256])
+def test_down_proj_full_size(B):
+    """Wdown 4096 x 14336 (28 tiles per 32-row block, 128 row blocks, so the
+    work of a row block is split across workgroups and y is accumulated):
+    decoded weights compared in full, y against the oracle on 48 sampled
+    output features and against torch's float32 matmul of the BF16 values."""
+    N, K = 4096, 14336
+    _say("case gemm down_proj B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=0, index=6, count=7).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=2)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y = api.decode_gemm(dt, _x_to_gpu(X))
+    yd = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg)
+    torch.cuda.synchronize()
+    wt = torch.from_numpy(W.view(np.int16)).cuda()
+    assert torch.equal(wdbg.view(torch.int16), wt), "decoded weights differ"
+    cols = np.random.default_rng(B + 7).choice(N, size=48, replace=False)
+    ref = orc.gemm_f64(X, W[cols])
+    yt = (_x_to_gpu(X).float() @ wt.view(torch.bfloat16).float().T)
+    for out in (y, yd):
+        assert _rel(out.cpu().numpy()[:, cols], ref) < TOL
+        assert float((out - yt).norm() / yt.norm()) < TOL
+
+
 @pytest.mark.parametrize("B", [1, 8, 32, 64, 256])
 def test_bf16_output_within_one_step_of_oracle(B):
     """y as BF16 (one rounding of the float32 sum) against the oracle's
