@@ -17,14 +17,22 @@
 // l / 32) .. + 7, i.e. 8 consecutive stream elements, so operand reads are
 // contiguous across lanes.
 //
-// A workgroup owns a block of 32 weight rows (32 output features) and walks
-// its K / 512 tiles with two LDS buffers, each an exponent plane (filled by
-// the wavefront decode, one wave per segment) and a sign+mantissa plane
-// (copied from HBM).  While the waves run the matrix cores on tile t from
-// one buffer, tile t + 1's sign+mantissa bytes and stream words are already
-// in flight and its segments are decoded into the other buffer.  B operands
-// are assembled in registers (two bit-selects and two byte permutes per four
-// weights) from the two planes; A operands (x, the batch) come from L2.
+// Three kernels, chosen by the rows of x (B):
+//   decode_gemm_seg_kernel   (B <= 40, the product path for small batches):
+//       every wave walks its own segments of a 32-row block, decodes each
+//       into its staging and feeds the matrix cores in rounds of 512
+//       elements, with no barrier until the row block's partial sums are
+//       reduced; one or two 32-row batch tiles.
+//   decode_gemm_wide_kernel  (B > 40, and w_debug calls above 32 rows): a
+//       workgroup decodes the next weight tile of one or two row blocks
+//       into exponent planes while its matrix cores run on the current
+//       tile, which was merged once into a BF16 plane in LDS shared by all
+//       batch tiles.
+//   decode_gemm_kernel       (w_debug calls up to 32 rows; DF11_GEMM_NARROW):
+//       tile-synchronous, two exponent planes, every wave assembling its
+//       own B operands from a plane and sign+mantissa bytes read from HBM.
+// B operands are assembled with two bit-selects and two byte permutes per
+// four weights; A operands (x, the batch) come from L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
