@@ -3,7 +3,7 @@
  *
  * A plain, serial, deliberately slow implementation of what the DFloat11
  * (Dynamic-length Float) codec computes, used only by the tests, the smoke
- * check and the CPU-baseline leg of the benchmark to judge the HIP library.
+ * check and the CPU-baseline leg of the benchmark, to check the HIP library.
  * It shares no source with the library (no headers, tables or helpers) and
  * the library never calls it.
  *
