@@ -26,8 +26,10 @@
  *   - BF16 tensors are passed as their uint16 bit patterns.
  *   - "host" pointers are CPU memory; "device" pointers are GPU memory of the
  *     current HIP device.  Device work is asynchronous on `stream` (a
- *     hipStream_t passed as void*, NULL = the null stream).  The library
- *     allocates no device memory in any call and keeps no per-call state.
+ *     hipStream_t passed as void*, NULL = the null stream).  The decode,
+ *     row-gather and fused-product calls allocate no device memory and keep
+ *     no per-call state; only df11_encode_device allocates, the device arrays
+ *     it returns (freed with df11_device_encoded_free).
  *
  * Stream format (what df11_encode writes and the kernels read)
  *   exp_words  The exponent codes of all elements in stream order, each code
