@@ -91,7 +91,7 @@ extern "C" {
 #define DF11_E_CODE_LEN (-3)  /* max_len outside 1..32, or more than DF11_MAX_TABLES tables */
 #define DF11_E_FORMAT (-4)    /* df11_validate found an inconsistent stream or codebook */
 #define DF11_E_DEVICE (-5)    /* a HIP call failed; detail in df11_last_error() */
-#define DF11_E_ALLOC (-6)     /* host allocation failed */
+#define DF11_E_ALLOC (-6)     /* an allocation failed */
 #define DF11_E_UNSUPPORTED (-7) /* a valid request this build does not handle */
 
 #define DF11_MAX_LEN 32
@@ -250,7 +250,9 @@ int df11_device_encoded_to_host(const df11_device_encoded *enc, df11_encoded **o
  * including zeros, subnormals, Inf and NaN payloads, comes back unchanged.
  * Writes stay inside out[0..n) even for a corrupt stream (then the values are
  * unspecified).  n = 0 is a no-op.  Errors: E_ARG (null, misaligned, view
- * inconsistent), E_UNSUPPORTED (tables too large for the kernel), E_DEVICE. */
+ * inconsistent), E_UNSUPPORTED (tables too large for the kernel, or a
+ * layout other than 16-byte chunks: the encoders write other chunk sizes,
+ * the decode kernels are built for 16), E_DEVICE. */
 int df11_decode(const df11_view *device_view, uint16_t *out, void *stream);
 
 /* Decode several device views in one launch: view i into outs[i] (device,
