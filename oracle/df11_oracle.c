@@ -302,15 +302,21 @@ void orc_metadata(const uint64_t *start, const uint16_t *u, uint64_t n,
 /* ---- per-lane code counts: counts[c] = the number of codes whose first bit
  * lies in chunk c, i.e. in [c * chunk_bits, (c + 1) * chunk_bits), for the
  * nchunks chunks of the stream.  (The lane that owns chunk c decodes exactly
- * these codes; storing the count spares the decoder a counting pass.) */
-void orc_chunk_counts(const uint64_t *start, uint64_t n, uint64_t chunk_bits, uint64_t nchunks,
-                      uint8_t *counts)
+ * these codes; storing the count spares the decoder a counting pass.)  A
+ * count is stored in one byte: if any chunk holds more than 255 codes the
+ * layout cannot carry its counts, and the function returns -1 (counts then
+ * hold nothing meaningful) instead of storing a wrapped value; else 0. */
+int orc_chunk_counts(const uint64_t *start, uint64_t n, uint64_t chunk_bits, uint64_t nchunks,
+                     uint8_t *counts)
 {
     for (uint64_t c = 0; c < nchunks; c++) counts[c] = 0;
     for (uint64_t i = 0; i < n; i++) {
         uint64_t c = start[i] / chunk_bits;
-        if (c < nchunks) counts[c] = (uint8_t)(counts[c] + 1);
+        if (c >= nchunks) continue;
+        if (counts[c] == 255) return -1;
+        counts[c] = (uint8_t)(counts[c] + 1);
     }
+    return 0;
 }
 
 /* ---- matrix product that consumes the decoded weights ([P1] 2.2 item 3:

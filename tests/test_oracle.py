@@ -297,6 +297,37 @@ def test_chunk_counts_add_up_per_segment(name):
     assert np.array_equal(brute, enc.counts.astype(np.int64))
 
 
+def _chunks_of_255(k):
+    """k runs of 255 elements: a 2-bit code (exponents 0x80 and 0x81 in
+    turn) followed by 254 elements of exponent 0x7F, which gets the 1-bit
+    code (254k against k of the other two).  Each run fills 256 bits."""
+    runs = []
+    for i in range(k):
+        head = (0x80 + (i & 1)) << 7
+        runs.append(np.array([head] + [0x7F << 7] * 254, np.uint16))
+    return np.concatenate(runs) | (np.arange(255 * k, dtype=np.uint16) & 0x807F)
+
+
+def test_chunk_counts_refuse_more_than_255_codes():
+    """A chunk count is one byte.  With 32-byte chunks, runs of one 2-bit
+    and 254 1-bit codes put exactly 255 code starts in every chunk: stored
+    as 255 and decoded back.  One more 1-bit code in a chunk (all 1-bit
+    codes) would make 256: the oracle refuses that layout rather than
+    storing a wrapped count."""
+    u = _chunks_of_255(70)
+    enc = orc.encode(u, chunk_bytes=32)
+    assert list(enc.lengths[[0x7F, 0x80, 0x81]]) == [1, 2, 2]
+    full = enc.counts[:enc.total_bits // 256]
+    assert full.size == 70 and (full == 255).all()
+    assert np.array_equal(orc.decode(enc.E, enc.total_bits, enc.sm, enc.n, enc.lengths), u)
+    # 16-byte chunks: 128 bits hold at most 128 codes
+    assert int(orc.encode(u, chunk_bytes=16).counts.max()) <= 128
+    one = (np.full(4096, 0x3F80, np.uint16) | (np.arange(4096, dtype=np.uint16) & 0x807F))
+    with pytest.raises(ValueError, match="255"):
+        orc.encode(one, chunk_bytes=32)
+    assert int(orc.encode(one, chunk_bytes=16).counts.max()) == 128
+
+
 @pytest.mark.parametrize("name", ["normal", "adversarial", "exhaustive", "fibonacci", "tiny"])
 def test_round_trip_identity(name):
     if name == "normal":
