@@ -5,7 +5,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_build", "libdf11.so")
+# DF11_LIBRARY names another build of the same library (the sanitizer build
+# of `python -m huffman_decode_df11_amd.build --sanitize`)
+LIB_PATH = os.environ.get("DF11_LIBRARY") or os.path.join(_PKG, "_build", "libdf11.so")
 
 DF11_OK = 0
 DF11_MAX_TABLES = 64
@@ -13,6 +15,8 @@ DF11_FAST_BITS_MAX = 12
 DF11_FAST_BITS_DEFAULT = 11
 DF11_Y_F32 = 0
 DF11_Y_BF16 = 1
+DF11_STORES_AUTO, DF11_STORES_CACHED, DF11_STORES_STREAMING = 0, 1, 2
+DF11_GEMM_AUTO, DF11_GEMM_SEGMENT, DF11_GEMM_WIDE, DF11_GEMM_TILED = 0, 1, 2, 3
 
 u32, u64 = ctypes.c_uint32, ctypes.c_uint64
 
@@ -61,6 +65,14 @@ class View(ctypes.Structure):
     ]
 
 
+class DecodeTuning(ctypes.Structure):
+    _fields_ = [("waves", u32), ("stores", u32), ("reserved", u32 * 6)]
+
+
+class GemmTuning(ctypes.Structure):
+    _fields_ = [("kernel", u32), ("row_blocks", u32), ("parts", u32), ("split", u32), ("reserved", u32 * 4)]
+
+
 # (field, element ctype) of every array in a view
 VIEW_ARRAYS = (
     ("exp_words", ctypes.c_uint32),
@@ -76,8 +88,8 @@ VIEW_ARRAYS = (
 EXPORTS = (
     "df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_free",
     "df11_encoded_view", "df11_gemm_layout", "df11_gemm_tile_rows", "df11_gemm_tile_cols",
-    "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_rows", "df11_decode_gemm",
-    "df11_decode_gemm_out", "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
+    "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_batch_tuned", "df11_decode_rows",
+    "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_tuned", "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
     "df11_device_encoded_to_host",
     "df11_status_string", "df11_last_error", "df11_version",
 )
@@ -117,9 +129,13 @@ def lib():
     L.df11_validate.argtypes = [ctypes.POINTER(View), ctypes.POINTER(Codebook)]
     L.df11_decode.argtypes = [ctypes.POINTER(View), vp, vp]
     L.df11_decode_batch.argtypes = [ctypes.POINTER(View), ctypes.POINTER(vp), u32, vp]
+    L.df11_decode_batch_tuned.argtypes = [ctypes.POINTER(View), ctypes.POINTER(vp), u32,
+                                          ctypes.POINTER(DecodeTuning), vp]
     L.df11_decode_rows.argtypes = [ctypes.POINTER(View), vp, u64, vp, vp]
     L.df11_decode_gemm.argtypes = [ctypes.POINTER(View), vp, u32, vp, vp, vp]
     L.df11_decode_gemm_out.argtypes = [ctypes.POINTER(View), vp, u32, vp, ctypes.c_int, vp, vp]
+    L.df11_decode_gemm_tuned.argtypes = [ctypes.POINTER(View), vp, u32, vp, ctypes.c_int, vp,
+                                         ctypes.POINTER(GemmTuning), vp]
     L.df11_hist_device.argtypes = [vp, u64, vp, vp]
     L.df11_encode_device.argtypes = [vp, u64, ctypes.POINTER(Codebook), ctypes.POINTER(Layout), vp,
                                      ctypes.POINTER(vp)]
@@ -132,8 +148,9 @@ def lib():
     L.df11_last_error.restype = ctypes.c_char_p
     L.df11_version.restype = ctypes.c_char_p
     for name in ("df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_view",
-                 "df11_gemm_layout", "df11_validate", "df11_decode", "df11_decode_batch",
-                 "df11_decode_rows", "df11_decode_gemm", "df11_decode_gemm_out", "df11_hist_device", "df11_encode_device",
+                 "df11_gemm_layout", "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_batch_tuned",
+                 "df11_decode_rows", "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_tuned",
+                 "df11_hist_device", "df11_encode_device",
                  "df11_device_encoded_view", "df11_device_encoded_to_host"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L

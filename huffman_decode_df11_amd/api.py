@@ -13,7 +13,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _lib
-from ._lib import DF11_Y_BF16, DF11_Y_F32, Codebook, Layout, View, check, lib
+from ._lib import DF11_Y_BF16, DF11_Y_F32, Codebook, DecodeTuning, GemmTuning, Layout, View, check, lib
 
 DEFAULT_MAX_LEN = 32
 DEFAULT_FAST_BITS = _lib.DF11_FAST_BITS_DEFAULT
@@ -317,7 +317,17 @@ def decode(t: DF11Tensor, out=None, stream=None):
     return out
 
 
-def decode_batch(tensors: Sequence[DF11Tensor], outs=None, stream=None):
+def decode_tuning(waves: int = 0, stores: int = 0) -> DecodeTuning:
+    """Explicit launch choices for decode_batch (0 = the library's choice)."""
+    return DecodeTuning(waves=waves, stores=stores)
+
+
+def gemm_tuning(kernel: int = 0, row_blocks: int = 0, parts: int = 0, split: int = 0) -> GemmTuning:
+    """Explicit kernel choices for decode_gemm (0 = the library's choice)."""
+    return GemmTuning(kernel=kernel, row_blocks=row_blocks, parts=parts, split=split)
+
+
+def decode_batch(tensors: Sequence[DF11Tensor], outs=None, stream=None, tuning: Optional[DecodeTuning] = None):
     """Decode several tensors that share a codebook in one launch.  Returns
     the list of outputs (new torch.bfloat16 tensors where outs is None)."""
     import torch
@@ -332,7 +342,11 @@ def decode_batch(tensors: Sequence[DF11Tensor], outs=None, stream=None):
         assert o.is_cuda and o.is_contiguous() and o.numel() >= t.n and o.element_size() == 2
         ctypes.memmove(ctypes.byref(views, i * ctypes.sizeof(View)), ctypes.byref(t.view), ctypes.sizeof(View))
         ptrs[i] = o.data_ptr()
-    check(lib().df11_decode_batch(views, ptrs, len(tensors), _stream_handle(stream)), "df11_decode_batch")
+    if tuning is None:
+        check(lib().df11_decode_batch(views, ptrs, len(tensors), _stream_handle(stream)), "df11_decode_batch")
+    else:
+        check(lib().df11_decode_batch_tuned(views, ptrs, len(tensors), ctypes.byref(tuning), _stream_handle(stream)),
+              "df11_decode_batch_tuned")
     return outs
 
 
@@ -352,11 +366,12 @@ def decode_rows(t: DF11Tensor, rows, out=None, stream=None):
     return out
 
 
-def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None, out_dtype=None):
+def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None, out_dtype=None,
+                tuning: Optional[GemmTuning] = None):
     """y = x @ W^T with W decoded tile by tile inside the kernel.  x: [B, K]
     bf16 on the GPU; returns y [B, N], float32 (default) or bfloat16
     (out_dtype=torch.bfloat16, or an `out` of that type: the float32 sum
-    rounded once, ties to even)."""
+    rounded once, ties to even).  tuning: explicit kernel choices."""
     import torch
     N, K = int(w.host_view.rows), int(w.host_view.cols)
     assert x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[1] == K
@@ -373,6 +388,10 @@ def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None, out_dtype
         assert w_debug.is_contiguous() and w_debug.numel() == N * K and w_debug.element_size() == 2
         wd = w_debug.data_ptr()
     y_dtype = DF11_Y_BF16 if out_dtype == torch.bfloat16 else DF11_Y_F32
-    check(lib().df11_decode_gemm_out(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), y_dtype, wd,
-                                     _stream_handle(stream)), "df11_decode_gemm_out")
+    if tuning is None:
+        check(lib().df11_decode_gemm_out(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), y_dtype, wd,
+                                         _stream_handle(stream)), "df11_decode_gemm_out")
+    else:
+        check(lib().df11_decode_gemm_tuned(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), y_dtype, wd,
+                                           ctypes.byref(tuning), _stream_handle(stream)), "df11_decode_gemm_tuned")
     return out

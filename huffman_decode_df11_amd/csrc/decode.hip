@@ -35,14 +35,23 @@
 
 #include "df11_device.h"
 #include "df11_internal.h"
+#define DF11_HD __host__ __device__ __forceinline__
+#include "segment_plan.h"
 
 using namespace df11dev;
+using df11plan::RaggedLane;
+using df11plan::SegPlan;
+using df11plan::TileSeg;
 
 namespace {
 
-constexpr uint32_t kChunkBytes = 16;
-constexpr uint32_t kChunkBits = 8 * kChunkBytes;
-constexpr uint32_t kSegWords = 64 * kChunkBytes / 4;
+// A lane's chunk of the stream: CB = 16 or 8 bytes, loaded as CB / 4 words
+// (the window adds the next chunk's first word).
+template <int CB> struct Chunk;
+template <> struct Chunk<16> { typedef uint4 words_t; };
+template <> struct Chunk<8> { typedef uint2 words_t; };
+template <int CB> constexpr uint32_t chunk_bits() { return 8u * CB; }
+template <int CB> constexpr uint32_t seg_words() { return 64u * CB / 4u; }
 constexpr int kPrefetchRounds = 5;   // 8-element units per lane prefetched before the decode
 
 struct ViewArgs {
@@ -165,8 +174,9 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T *as_const(c
 // vector part (stream words, gap, stored count) is always loaded from valid
 // addresses, so the loads carry no condition and are first waited for where
 // the decode uses them.
+template <int CB>
 struct SegLoad {
-    uint4 own;          // this lane's 4 stream words
+    typename Chunk<CB>::words_t own;   // this lane's stream words
     uint32_t next;      // the following word (look-ahead)
     uint32_t gap;
     uint32_t count;     // codes that start in this lane's chunk (meaningful when the view stores counts)
@@ -174,12 +184,14 @@ struct SegLoad {
     uint64_t g0, g1;
 };
 
-__device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, uint32_t lane)
+template <int CB>
+__device__ __forceinline__ SegLoad<CB> load_segment(const ViewArgs &v, uint64_t s, uint32_t lane)
 {
-    SegLoad L;
-    const uint32_t *w = v.words + s * kSegWords + lane * 4;
-    L.own = *reinterpret_cast<const uint4 *>(w);
-    L.next = w[4];
+    typedef typename Chunk<CB>::words_t words_t;
+    SegLoad<CB> L;
+    const uint32_t *w = v.words + s * seg_words<CB>() + lane * (CB / 4);
+    L.own = *reinterpret_cast<const words_t *>(w);
+    L.next = w[CB / 4];
     L.gap = v.gaps[s * 64 + lane];
     const uint8_t *cp = v.counts ? v.counts : v.gaps;
     L.count = cp[s * 64 + lane];
@@ -191,22 +203,11 @@ __device__ __forceinline__ SegLoad load_segment(const ViewArgs &v, uint64_t s, u
 }
 
 // ------------------------------------------------------------ one segment
-struct SegPlan {
-    uint64_t g0, g1, gbase;   // elements [g0, g1); 8-element units from gbase
-    uint32_t head, nunits;
-    bool valid;               // records consistent and the segment fits the staging
-};
-
-__device__ __forceinline__ SegPlan plan_segment(const SegLoad &cur, uint64_t n, uint32_t stg_bytes)
+// (plan_segment, ragged_lane and the tile placement: segment_plan.h)
+template <int CB>
+__device__ __forceinline__ SegPlan plan_segment(const SegLoad<CB> &cur, uint64_t n, uint32_t stg_bytes)
 {
-    SegPlan p;
-    p.g0 = cur.g0;
-    p.g1 = cur.g1;
-    p.gbase = p.g0 & ~7ull;
-    p.head = (uint32_t)(p.g0 & 7);
-    p.valid = p.g1 <= n && p.g1 >= p.g0 && (uint64_t)p.head + (p.g1 - p.g0) + 32 <= stg_bytes;
-    p.nunits = p.valid ? (uint32_t)((((p.g1 + 7) & ~7ull) - p.gbase) >> 3) : 0u;
-    return p;
+    return df11plan::plan_segment(cur.g0, cur.g1, n, stg_bytes);
 }
 
 // the segment's sign+mantissa bytes for the first kPrefetchRounds rounds of
@@ -228,15 +229,15 @@ __device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm,
 // when the view carries counts, else the locate pass walks the chunk.
 // False when the counts disagree with the segment's records (then nothing
 // is staged).
-template <int K>
-__device__ __forceinline__ bool stage_segment(const SegLoad &cur, const SegPlan &p, bool stored, uint32_t stg,
+template <int K, int CB>
+__device__ __forceinline__ bool stage_segment(const SegLoad<CB> &cur, const SegPlan &p, bool stored, uint32_t stg,
                                               uint32_t fast, uint32_t chain, uint32_t lane)
 {
-    const Window win = make_window(cur.own, cur.next, cur.gap);
+    const auto win = make_window(cur.own, cur.next, cur.gap);
     uint32_t cnt = cur.count;
     if (!stored) {
-        const uint32_t c0 = lane * kChunkBits;
-        const uint32_t end = cur.nbits > c0 ? min(kChunkBits, cur.nbits - c0) : 0u;
+        const uint32_t c0 = lane * chunk_bits<CB>();
+        const uint32_t end = cur.nbits > c0 ? min(chunk_bits<CB>(), cur.nbits - c0) : 0u;
         cnt = cur.gap < end ? count_codes<K>(win, fast, chain, cur.gap, end) : 0u;
     }
     uint32_t total;
@@ -270,30 +271,17 @@ template <class Out>
 __device__ __forceinline__ void merge_unit(const SegPlan &p, uint64_t lo, uint64_t hi, uint32_t ui, uint2 smv,
                                            const Out &out, uint32_t stg, bool stream)
 {
-    const uint64_t gs = p.gbase + 8ull * ui;
-    if (ui < p.nunits && gs >= lo && gs + 8 <= hi) {
+    if (df11plan::unit_inside(p, lo, hi, ui)) {
+        const uint64_t gs = p.gbase + 8ull * ui;
         const uint2 rx = ld64(stg + 8 * ui);
         const uint2 a = assemble4(smv.x, rx.x), b = assemble4(smv.y, rx.y);
         store_bf16x8(out.at(gs), make_uint4(a.x, a.y, b.x, b.y), stream);
     }
 }
 
-// The ragged ends of [lo, hi): the elements before the first and after the
-// last whole 8-element unit, one per lane (lanes 0..7 the head, lanes
-// 8..15 the tail).
-struct RaggedLane {
-    uint64_t g;
-    bool act;
-};
-
 __device__ __forceinline__ RaggedLane ragged_lane(uint64_t lo, uint64_t hi, uint32_t lane)
 {
-    const uint64_t hend = min((lo + 7) & ~7ull, hi);
-    const uint64_t tstart = max(hi & ~7ull, hend);
-    RaggedLane r;
-    r.g = lane < 8 ? lo + lane : tstart + (lane - 8);
-    r.act = lane < 8 ? r.g < hend : (lane < 16 && r.g < hi);
-    return r;
+    return df11plan::ragged_lane(lo, hi, lane);
 }
 
 // Merge the staged exponents of elements [lo, hi) (inside the segment) with
@@ -332,44 +320,18 @@ __device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint6
 // segment at up to ~4K elements) go out before the decode, like the
 // row-major prefetch; later batches load after it.  Ragged ends as in
 // merge_range.
-struct TileSeg {
-    const uint8_t *smt;        // sign+mantissa bytes of the tile
-    uint16_t *obase;           // output of the tile's first element
-    uint32_t lo, hi;           // the segment's elements within the tile
-    uint32_t grp_a, grp_b;     // first and last column group touched
-    uint32_t stg_t;            // staging byte of tile element 0 (modulo 2^32)
-};
-
 __device__ __forceinline__ TileSeg tile_seg(const SegPlan &p, const ViewArgs &v, uint32_t stg)
 {
-    const uint32_t tcs = (v.pow2 >> 5) & 31u, ts = 5 + tcs;
-    const uint64_t tile = p.g0 >> ts, tile_start = tile << ts;
-    TileSeg q;
-    q.lo = (uint32_t)(p.g0 - tile_start);
-    q.hi = (uint32_t)(p.g1 - tile_start);
-    q.grp_a = q.lo >> 8;
-    q.grp_b = (q.hi - 1) >> 8;
-    const uint32_t t32 = (uint32_t)tile, rb = t32 / v.tiles_per_row, cb = t32 - rb * v.tiles_per_row;
-    q.obase = v.out + ((uint64_t)rb << 5) * v.cols + ((uint64_t)cb << tcs);
-    q.smt = v.sm + tile_start;
-    q.stg_t = stg + (uint32_t)(tile_start - p.gbase);
-    return q;
+    return df11plan::tile_seg(p, (v.pow2 >> 5) & 31u, v.tiles_per_row, v.cols, stg);
 }
 
-// element offset (in the tile) of lane's unit in pass k of group batch gb
-__device__ __forceinline__ uint32_t tile_unit(uint32_t gb, uint32_t k, uint32_t lane)
-{
-    return ((gb + (lane & 7u)) << 8) + ((8u * k + (lane >> 3)) << 3);
-}
-
-__device__ __forceinline__ bool tile_unit_in(const TileSeg &q, uint32_t gb, uint32_t e0, uint32_t lane)
-{
-    return gb + (lane & 7u) <= q.grp_b && e0 >= q.lo && e0 + 8 <= q.hi;
-}
+using df11plan::tile_unit;
+using df11plan::tile_unit_in;
 
 // sign+mantissa bytes of the lane's units in the first two group batches,
 // loaded before the decode (units outside the segment reload its first unit)
-__device__ __forceinline__ void prefetch_tile8(const TileSeg &q, uint32_t lane, bool stream, uint2 (&tsv)[8])
+__device__ __forceinline__ void prefetch_tile8(const TileSeg &q, const ViewArgs &v, uint32_t lane, bool stream,
+                                               uint2 (&tsv)[8])
 {
 #pragma unroll
     for (int bb = 0; bb < 2; bb++)
@@ -377,7 +339,7 @@ __device__ __forceinline__ void prefetch_tile8(const TileSeg &q, uint32_t lane, 
         for (int k = 0; k < 4; k++) {
             const uint32_t gb = q.grp_a + 8u * bb;
             const uint32_t e0 = tile_unit(gb, k, lane);
-            tsv[4 * bb + k] = load_sm8(q.smt + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)), stream);
+            tsv[4 * bb + k] = load_sm8(v.sm + q.sm_off + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)), stream);
         }
 }
 
@@ -395,8 +357,8 @@ __device__ __forceinline__ void merge_tile_groups8(const SegPlan &p, const ViewA
         if (tile_unit_in(q, gb, e0, lane)) {
             const uint2 rx = ld64(q.stg_t + e0);
             const uint2 a = assemble4(sv.x, rx.x), b = assemble4(sv.y, rx.y);
-            const uint32_t r = 8u * k + (lane >> 3), grp = gb + (lane & 7u);
-            store_bf16x8(q.obase + (uint64_t)r * v.cols + (grp << 3), make_uint4(a.x, a.y, b.x, b.y), stream);
+            store_bf16x8(v.out + q.out_off + df11plan::tile_unit_out(gb, k, lane, v.cols), make_uint4(a.x, a.y, b.x, b.y),
+                         stream);
         }
     };
 #pragma unroll
@@ -409,7 +371,7 @@ __device__ __forceinline__ void merge_tile_groups8(const SegPlan &p, const ViewA
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             const uint32_t e0 = tile_unit(gb, k, lane);
-            sv[k] = load_sm8(q.smt + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)), stream);
+            sv[k] = load_sm8(v.sm + q.sm_off + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)), stream);
         }
 #pragma unroll
         for (int k = 0; k < 4; k++) unit(gb, k, sv[k]);
@@ -417,7 +379,7 @@ __device__ __forceinline__ void merge_tile_groups8(const SegPlan &p, const ViewA
 }
 
 // ------------------------------------------------------------ kernels
-template <int K, int WAVES, bool TILE8>
+template <int K, int WAVES, bool TILE8, int CB>
 __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs &t)
 {
     extern __shared__ __align__(16) uint8_t lds_raw[];
@@ -434,10 +396,10 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
     const uint64_t stride = (uint64_t)gridDim.x * WAVES;
     const bool stream = b.stream != 0;
     uint32_t vi = 0;
-    SegLoad nx{};
+    SegLoad<CB> nx{};
     if (s < n_total) {
         vi = view_of(b, s);
-        nx = load_segment(b.v[vi], s - b.seg_begin[vi], lane0);
+        nx = load_segment<CB>(b.v[vi], s - b.seg_begin[vi], lane0);
     }
     stage_tables<K, WAVES * 64>(fast, chain, t.fast, t.chain, t.n_chain);
     __syncthreads();
@@ -449,7 +411,7 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
         // prefetch below).  The row-major kernel is faster as it is.
         uint32_t lane = lane0;
         if constexpr (TILE8) asm volatile("" : "+v"(lane));
-        const SegLoad cur = nx;
+        const SegLoad<CB> cur = nx;
         const ViewArgs &v = b.v[vi];
         const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
         // The next segment's words and records first (the last segment
@@ -459,7 +421,7 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
         const uint64_t s_next = s + stride;
         const bool more = s_next < n_total;
         const uint32_t vi_next = more ? view_of(b, s_next, vi) : vi;
-        nx = load_segment(b.v[vi_next], (more ? s_next : s) - b.seg_begin[vi_next], lane);
+        nx = load_segment<CB>(b.v[vi_next], (more ? s_next : s) - b.seg_begin[vi_next], lane);
         uint2 smp[kPrefetchRounds];
         uint2 tsv[TILE8 ? 8 : 1];
         TileSeg q{};
@@ -469,7 +431,7 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
             tiled = p.valid && v.kc == 8 && v.pow2 && v.tr == 32 && p.g1 > p.g0 && (p.g0 >> ts) == ((p.g1 - 1) >> ts);
             if (tiled) {
                 q = tile_seg(p, v, stg);
-                prefetch_tile8(q, lane, stream, tsv);
+                prefetch_tile8(q, v, lane, stream, tsv);
             }
         }
         if (!tiled) prefetch_sm(p, v.sm, lane, stream, smp);
@@ -497,18 +459,20 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
 // such a view (its prefetch and bookkeeping spill a few registers, which
 // costs less than fewer waves: 55 us against 61 us at 7 waves per SIMD on
 // up_proj), so that the row-major kernel stays free of spills.
-template <int K, int WAVES>
+template <int K, int WAVES, int CB>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
 decode_kernel(BatchArgs b, TableArgs t)
 {
-    decode_body<K, WAVES, false>(b, t);
+    decode_body<K, WAVES, false, CB>(b, t);
 }
 
-template <int K, int WAVES>
+// (the fused kernel's layout always has 16-byte chunks)
+template <int K, int WAVES, int CB>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
 decode_kernel_t8(BatchArgs b, TableArgs t)
 {
-    decode_body<K, WAVES, true>(b, t);
+    static_assert(CB == 16, "tile-order views are encoded with 16-byte chunks");
+    decode_body<K, WAVES, true, CB>(b, t);
 }
 
 // Row gather: up to four waves per requested row (about as many as the
@@ -562,7 +526,7 @@ __device__ __forceinline__ uint64_t segment_of(const ViewArgs &v, uint64_t e, ui
 
 // (6 waves per SIMD by registers: the staging in LDS allows no more for
 // the usual tables, and at 8 the segment search spills)
-template <int K, int WAVES>
+template <int K, int WAVES, int CB>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(6, 8)))
 decode_rows_kernel(RowArgs a, TableArgs t)
 {
@@ -587,7 +551,7 @@ decode_rows_kernel(RowArgs a, TableArgs t)
         const uint64_t s0 = segment_of(v, lo, lane);
         const RowOut out{a.out + i * v.cols, lo};
         for (uint64_t s = s0 + j; s < v.n_segments; s += a.split) {
-            const SegLoad cur = load_segment(v, s, lane);
+            const SegLoad<CB> cur = load_segment<CB>(v, s, lane);
             if (cur.g0 >= hi) break;
             const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
             uint2 smp[kPrefetchRounds];
@@ -605,20 +569,30 @@ decode_rows_kernel(RowArgs a, TableArgs t)
 int check_view(const df11_view *v)
 {
     if (!v) return df11::fail(DF11_E_ARG, "null view");
-    if (v->seg_lanes != 64 || v->chunk_bytes != kChunkBytes)
-        return df11::fail(DF11_E_UNSUPPORTED, "decode kernels are built for 16-byte chunks and 64-lane segments (got %u, %u)",
+    if (v->seg_lanes != 64 || (v->chunk_bytes != 16 && v->chunk_bytes != 8))
+        return df11::fail(DF11_E_ARG, "view: chunk_bytes %u and seg_lanes %u (need 8 or 16, and 64)",
                           v->chunk_bytes, v->seg_lanes);
     if (v->fast_bits < DF11_FAST_BITS_MIN || v->fast_bits > DF11_FAST_BITS_MAX)
         return df11::fail(DF11_E_ARG, "fast_bits %u out of range", v->fast_bits);
     if (v->n_tables < 1 || v->n_tables > DF11_MAX_TABLES || v->n_chain != (uint64_t)v->n_tables * 256 ||
         v->n_fast != (2ull << v->fast_bits))
         return df11::fail(DF11_E_ARG, "table sizes inconsistent");
+    const uint64_t seg_words = 64ull * v->chunk_bytes / 4;
     if (v->n_segs != v->n_segments + 1 || v->n_gaps != v->n_segments * 64 ||
         (v->n_counts && (v->n_counts != v->n_segments * 64 || !v->counts)) ||
-        v->n_exp_words < v->n_segments * kSegWords + 2 || v->n_sm < (v->n + 15) / 16 * 16)
+        v->n_exp_words < v->n_segments * seg_words + 2 || v->n_sm < (v->n + 15) / 16 * 16)
         return df11::fail(DF11_E_ARG, "view array sizes inconsistent with n / n_segments");
-    if (v->n && (!v->exp_words || !v->sm || !v->gaps || !v->segs || !v->chain || !v->fast))
-        return df11::fail(DF11_E_ARG, "null array in view");
+    if (v->n) {
+        if (!v->exp_words || !v->sm || !v->gaps || !v->segs || !v->chain || !v->fast)
+            return df11::fail(DF11_E_ARG, "null array in view");
+        // the staging is sized from max_seg_elems: it must be set, and no
+        // segment can hold more codes than its bits at the shortest length
+        const uint64_t seg_bits = 8ull * seg_words * 4;
+        if (v->min_len < 1 || v->min_len > v->max_len || v->max_len > DF11_MAX_LEN || !v->max_seg_elems ||
+            v->max_seg_elems > (seg_bits + v->min_len - 1) / v->min_len)
+            return df11::fail(DF11_E_ARG, "view: code lengths %u..%u or max_seg_elems %u out of range", v->min_len,
+                              v->max_len, v->max_seg_elems);
+    }
     if (((uintptr_t)v->sm & 15) || ((uintptr_t)v->exp_words & 15) || ((uintptr_t)v->fast & 15) ||
         ((uintptr_t)v->chain & 15) || ((uintptr_t)v->segs & 7))
         return df11::fail(DF11_E_ARG, "view arrays must be 16-byte aligned (sm, exp_words, fast, chain)");
@@ -636,7 +610,7 @@ int check_view(const df11_view *v)
 // code), an 8-element head offset and a tail unit.
 uint32_t staging_bytes(const df11_view *v)
 {
-    const uint32_t seg_bits = 64u * kChunkBits;
+    const uint32_t seg_bits = 64u * 8u * v->chunk_bytes;
     const uint32_t minlen = std::max(1u, v->min_len);
     const uint32_t tmax = std::min(seg_bits / minlen + 1, std::max(1u, v->max_seg_elems));
     return (16 + tmax + 32 + 15) & ~15u;
@@ -681,44 +655,38 @@ uint32_t lds_bytes(int waves, uint32_t stg, uint32_t fast_bits, uint32_t n_table
     return 16 + (uint32_t)waves * stg + (8u << fast_bits) + n_tables * 512u;
 }
 
-template <int K, int W, bool T8>
-int try_launch(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
-               hipStream_t st, int *resident)
+// The kernel of a launch: KIND 0 row-major decode, 1 its tile-order form,
+// 2 the row gather.
+template <int K, int W, int CB, int KIND>
+constexpr auto kernel_of()
 {
-    if (waves != W) return 1;
-    // *resident > 0: the resident waves per CU are already known
-    int per_cu = *resident > 0 ? *resident / W : 0;
-    if (per_cu < 1 &&
-        (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, T8 ? decode_kernel_t8<K, W> : decode_kernel<K, W>, W * 64, lds) !=
-             hipSuccess || per_cu < 1))
-        per_cu = 1;
-    *resident = per_cu * W;
-    if (!nseg) return 0;   // query only
-    // every resident slot busy: the decode is latency-bound per wave, so
-    // more waves in flight beat an evenly split last round
-    const uint64_t groups = std::min<uint64_t>((nseg + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
-    if (groups) {
-        if constexpr (T8)
-            hipLaunchKernelGGL((decode_kernel_t8<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
-        else
-            hipLaunchKernelGGL((decode_kernel<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
-    }
-    return 0;
+    if constexpr (KIND == 0) return decode_kernel<K, W, CB>;
+    else if constexpr (KIND == 1) return decode_kernel_t8<K, W, CB>;
+    else return decode_rows_kernel<K, W, CB>;
 }
 
 constexpr int kWaveChoices[] = {4, 6, 8, 10, 12, 14, 16};
+constexpr int kNumChoices = sizeof(kWaveChoices) / sizeof(kWaveChoices[0]);
 
-template <int K, bool T8>
-int run_shape(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, uint64_t nseg,
-              hipStream_t st, int *resident)
+// Resident workgroups per CU of kernel_of<K, W, CB, KIND> with `lds` bytes
+// of LDS, or 0 when the query fails.
+template <int K, int CB, int KIND>
+int occupancy(int waves, uint32_t lds)
 {
-    return try_launch<K, 4, T8>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 6, T8>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 8, T8>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 10, T8>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 12, T8>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 14, T8>(waves, a, t, lds, nseg, st, resident) &&
-           try_launch<K, 16, T8>(waves, a, t, lds, nseg, st, resident);
+    int per_cu = 0;
+    auto q = [&](auto kern, int w) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, w * 64, lds) != hipSuccess) per_cu = 0;
+    };
+    switch (waves) {
+    case 4: q(kernel_of<K, 4, CB, KIND>(), 4); break;
+    case 6: q(kernel_of<K, 6, CB, KIND>(), 6); break;
+    case 8: q(kernel_of<K, 8, CB, KIND>(), 8); break;
+    case 10: q(kernel_of<K, 10, CB, KIND>(), 10); break;
+    case 12: q(kernel_of<K, 12, CB, KIND>(), 12); break;
+    case 14: q(kernel_of<K, 14, CB, KIND>(), 14); break;
+    default: q(kernel_of<K, 16, CB, KIND>(), 16); break;
+    }
+    return per_cu;
 }
 
 // Waves per workgroup.  Occupancy (LDS and registers) gives, for every
@@ -729,18 +697,16 @@ int run_shape(int waves, const BatchArgs &a, const TableArgs &t, uint32_t lds, u
 // none reaches 24); a smaller one takes the choice that
 // puts the fewest waves on the busiest CU (ties: larger workgroups, fewer
 // table copies), since each wave's segment is then latency-bound.
-// DF11_DECODE_WAVES overrides the choice for tuning.  Occupancy answers
-// depend only on (device, K, staging bytes, table count) and the last few
-// are kept so that a sequence of launches does not repeat the queries.
-constexpr int kNumChoices = sizeof(kWaveChoices) / sizeof(kWaveChoices[0]);
+// Occupancy answers depend only on (device, kernel, staging bytes, table
+// count) and the last few are kept so that a sequence of launches does not
+// repeat the queries.
 constexpr int kSaturatedWaves = 24;
 struct ShapeKey {
-    int dev, k;
+    int dev, k, cb, kind;
     uint32_t stg, n_tables;
-    bool t8;
     bool operator==(const ShapeKey &o) const
     {
-        return dev == o.dev && k == o.k && stg == o.stg && n_tables == o.n_tables && t8 == o.t8;
+        return dev == o.dev && k == o.k && cb == o.cb && kind == o.kind && stg == o.stg && n_tables == o.n_tables;
     }
 };
 std::mutex g_shape_mu;
@@ -749,12 +715,12 @@ int g_shape_res[8][kNumChoices];
 uint32_t g_shape_n = 0;
 
 // res[i]: resident waves per CU with kWaveChoices[i] waves per workgroup (0: does not fit)
-template <int K, bool T8>
-void resident_waves(const TableArgs &t, const df11_view *v, hipStream_t st, int res[kNumChoices])
+template <int K, int CB, int KIND>
+void resident_waves(uint32_t stg_bytes, uint32_t fast_bits, uint32_t n_tables, int res[kNumChoices])
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-    const ShapeKey key{dev, K, t.stg_bytes, v->n_tables, T8};
+    const ShapeKey key{dev, K, CB, KIND, stg_bytes, n_tables};
     {
         std::lock_guard<std::mutex> g(g_shape_mu);
         for (uint32_t i = 0; i < std::min(g_shape_n, 8u); i++)
@@ -763,13 +729,12 @@ void resident_waves(const TableArgs &t, const df11_view *v, hipStream_t st, int 
                 return;
             }
     }
-    BatchArgs probe{};
     for (int i = 0; i < kNumChoices; i++) {
         const int w = kWaveChoices[i];
-        const uint32_t lds = lds_bytes(w, t.stg_bytes, v->fast_bits, v->n_tables);
+        const uint32_t lds = lds_bytes(w, stg_bytes, fast_bits, n_tables);
         res[i] = 0;
-        if (16 + (uint32_t)w * t.stg_bytes > 65520 || lds > 160u * 1024u) continue;
-        run_shape<K, T8>(w, probe, t, lds, 0, st, &res[i]);
+        if (16 + (uint32_t)w * stg_bytes > 65520 || lds > 160u * 1024u) continue;
+        res[i] = std::max(1, occupancy<K, CB, KIND>(w, lds)) * w;
     }
     std::lock_guard<std::mutex> g(g_shape_mu);
     g_shape_key[g_shape_n % 8] = key;
@@ -777,22 +742,21 @@ void resident_waves(const TableArgs &t, const df11_view *v, hipStream_t st, int 
     g_shape_n++;
 }
 
-// The choice index for nseg segments, or -1 when nothing fits.
-int pick_waves(const int res[kNumChoices], uint64_t nseg, uint64_t cus)
+// The choice index for `items` wave tasks (segments or row pieces), or -1
+// when nothing fits; `forced` (nonzero) takes that many waves per workgroup.
+int pick_waves(const int res[kNumChoices], uint64_t items, uint64_t cus, uint32_t forced)
 {
-    const char *env = getenv("DF11_DECODE_WAVES");
-    const int forced = env ? atoi(env) : 0;
     int best = -1;
     for (int i = 0; i < kNumChoices; i++) {
         if (!res[i]) continue;
         if (forced) {
-            if (kWaveChoices[i] == forced) return i;
+            if ((uint32_t)kWaveChoices[i] == forced) return i;
             continue;
         }
         if (best < 0 || res[i] > res[best]) best = i;
     }
     if (forced || best < 0) return best;
-    if (nseg >= cus * (uint64_t)res[best]) {
+    if (items >= cus * (uint64_t)res[best]) {
         // several rounds: 24 resident waves per CU already keep HBM busy
         // (more waves measured slower on a whole layer in one launch, with
         // more requests contending); take the shape closest above that,
@@ -806,7 +770,7 @@ int pick_waves(const int res[kNumChoices], uint64_t nseg, uint64_t cus)
     uint64_t best_load = ~0ull;
     for (int i = 0; i < kNumChoices; i++) {
         if (!res[i]) continue;
-        const uint64_t w = kWaveChoices[i], groups = (nseg + w - 1) / w;
+        const uint64_t w = kWaveChoices[i], groups = (items + w - 1) / w;
         if (groups > cus * (uint64_t)(res[i] / w)) continue;   // would not be resident at once
         const uint64_t load = (groups + cus - 1) / cus * w;    // waves on the busiest CU
         if (load <= best_load) { best_load = load; best = i; }
@@ -814,39 +778,70 @@ int pick_waves(const int res[kNumChoices], uint64_t nseg, uint64_t cus)
     return best;
 }
 
-template <int K, bool T8>
-int launch_decode_t(const BatchArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
+// One launch of kernel_of<K, W, CB, KIND> with every resident slot busy:
+// the decode is latency-bound per wave, so more waves in flight beat an
+// evenly split last round.
+template <int K, int CB, int KIND, class Args>
+int launch_waves(int choice, int resident, const Args &a, const TableArgs &t, uint32_t lds, uint64_t items,
+                 hipStream_t st)
 {
-    int res[kNumChoices];
-    resident_waves<K, T8>(t, v, st, res);
-    const int i = pick_waves(res, a.seg_begin[a.count], (uint64_t)device_cu_count());
-    if (i < 0) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
-    int r = res[i];
-    run_shape<K, T8>(kWaveChoices[i], a, t, lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables),
-                     a.seg_begin[a.count], st, &r);
+    const int w = kWaveChoices[choice];
+    const uint64_t per_cu = std::max(1, resident / w);
+    const uint64_t groups = std::min<uint64_t>((items + w - 1) / w, (uint64_t)device_cu_count() * per_cu);
+    if (!groups) return DF11_OK;
+    const dim3 grid((uint32_t)groups), block(w * 64);
+    switch (w) {
+    case 4: hipLaunchKernelGGL((kernel_of<K, 4, CB, KIND>()), grid, block, lds, st, a, t); break;
+    case 6: hipLaunchKernelGGL((kernel_of<K, 6, CB, KIND>()), grid, block, lds, st, a, t); break;
+    case 8: hipLaunchKernelGGL((kernel_of<K, 8, CB, KIND>()), grid, block, lds, st, a, t); break;
+    case 10: hipLaunchKernelGGL((kernel_of<K, 10, CB, KIND>()), grid, block, lds, st, a, t); break;
+    case 12: hipLaunchKernelGGL((kernel_of<K, 12, CB, KIND>()), grid, block, lds, st, a, t); break;
+    case 14: hipLaunchKernelGGL((kernel_of<K, 14, CB, KIND>()), grid, block, lds, st, a, t); break;
+    default: hipLaunchKernelGGL((kernel_of<K, 16, CB, KIND>()), grid, block, lds, st, a, t); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode launch: %s", hipGetErrorString(e));
     return DF11_OK;
 }
 
+template <int K, int CB, int KIND, class Args>
+int launch_kind(const Args &a, const TableArgs &t, const df11_view *v, uint64_t items, uint32_t forced_waves,
+                hipStream_t st)
+{
+    int res[kNumChoices];
+    resident_waves<K, CB, KIND>(t.stg_bytes, v->fast_bits, v->n_tables, res);
+    const int i = pick_waves(res, items, (uint64_t)device_cu_count(), forced_waves);
+    if (i < 0)
+        return df11::fail(forced_waves ? DF11_E_ARG : DF11_E_UNSUPPORTED,
+                          forced_waves ? "%u waves per workgroup do not fit this tensor's staging and tables"
+                                       : "tables and staging do not fit in LDS",
+                          forced_waves);
+    return launch_waves<K, CB, KIND>(i, res[i], a, t, lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables),
+                                     items, st);
+}
 
-// Views in 8-column-group tile order take a kernel with the row-wise merge
-// for them (merge_tile_groups8); all other launches a kernel without it.
-template <int K>
-int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
+// Views in 8-column-group tile order (16-byte chunks) take a kernel with the
+// row-wise merge for them (merge_tile_groups8); all other launches a kernel
+// without it.
+template <int K, int CB>
+int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, uint32_t waves, hipStream_t st)
 {
     bool t8 = false;
     for (uint32_t i = 0; i < a.count; i++)
         t8 = t8 || (a.v[i].kc == 8 && a.v[i].pow2 && a.v[i].tr == 32);
-    return t8 ? launch_decode_t<K, true>(a, t, v, st) : launch_decode_t<K, false>(a, t, v, st);
+    const uint64_t nseg = a.seg_begin[a.count];
+    if constexpr (CB == 16)
+        if (t8) return launch_kind<K, CB, 1>(a, t, v, nseg, waves, st);
+    return launch_kind<K, CB, 0>(a, t, v, nseg, waves, st);
 }
 
 }  // namespace
 
 namespace {
 
-// One launch over up to kMaxBatch views that share their tables.
-int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, hipStream_t st)
+// One launch over up to kMaxBatch views that share their tables and chunk size.
+int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, const df11_decode_tuning &tune,
+                 hipStream_t st)
 {
     BatchArgs b{};
     uint32_t stg = 0;
@@ -860,6 +855,8 @@ int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, 
         if (v0 && (v->fast != v0->fast || v->chain != v0->chain || v->fast_bits != v0->fast_bits ||
                    v->n_tables != v0->n_tables))
             return df11::fail(DF11_E_ARG, "views of one batch must share their device tables (view %u differs)", i);
+        if (v0 && v->chunk_bytes != v0->chunk_bytes)
+            return df11::fail(DF11_E_ARG, "views of one batch must share their chunk size (view %u differs)", i);
         if (!v0) v0 = v;
         b.v[b.count] = make_args(v, outs[i]);
         b.seg_begin[b.count + 1] = b.seg_begin[b.count] + v->n_segments;
@@ -868,45 +865,45 @@ int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, 
         stg = std::max(stg, staging_bytes(v));
     }
     if (!b.count || !b.seg_begin[b.count]) return DF11_OK;
-    b.stream = out_bytes > kStreamOutBytes;
+    b.stream = tune.stores == DF11_STORES_AUTO ? out_bytes > kStreamOutBytes : tune.stores == DF11_STORES_STREAMING;
     TableArgs t{v0->chain, v0->fast, (uint32_t)v0->n_chain, stg};
+    const uint32_t w = tune.waves;
+    if (v0->chunk_bytes == 8) {
+        switch (v0->fast_bits) {
+        case 8: return launch_decode<8, 8>(b, t, v0, w, st);
+        case 9: return launch_decode<9, 8>(b, t, v0, w, st);
+        case 10: return launch_decode<10, 8>(b, t, v0, w, st);
+        case 11: return launch_decode<11, 8>(b, t, v0, w, st);
+        default: return launch_decode<12, 8>(b, t, v0, w, st);
+        }
+    }
     switch (v0->fast_bits) {
-    case 8: return launch_decode<8>(b, t, v0, st);
-    case 9: return launch_decode<9>(b, t, v0, st);
-    case 10: return launch_decode<10>(b, t, v0, st);
-    case 11: return launch_decode<11>(b, t, v0, st);
-    default: return launch_decode<12>(b, t, v0, st);
+    case 8: return launch_decode<8, 16>(b, t, v0, w, st);
+    case 9: return launch_decode<9, 16>(b, t, v0, w, st);
+    case 10: return launch_decode<10, 16>(b, t, v0, w, st);
+    case 11: return launch_decode<11, 16>(b, t, v0, w, st);
+    default: return launch_decode<12, 16>(b, t, v0, w, st);
     }
 }
 
-template <int K, int W>
-int launch_rows_w(const RowArgs &a, const TableArgs &t, uint32_t lds, int resident, hipStream_t st)
-{
-    const uint64_t per_cu = std::max(1, resident / W);
-    const uint64_t groups = std::min<uint64_t>((a.n_rows * a.split + W - 1) / W, (uint64_t)device_cu_count() * per_cu);
-    hipLaunchKernelGGL((decode_rows_kernel<K, W>), dim3((uint32_t)groups), dim3(W * 64), lds, st, a, t);
-    return DF11_OK;
-}
-
-template <int K>
+template <int CB>
 int launch_rows(const RowArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
 {
-    int res[kNumChoices];
-    resident_waves<K, false>(t, v, st, res);
-    const int i = pick_waves(res, a.n_rows * a.split, (uint64_t)device_cu_count());
-    if (i < 0) return df11::fail(DF11_E_UNSUPPORTED, "tables and staging do not fit in LDS");
-    const uint32_t lds = lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables);
-    switch (kWaveChoices[i]) {
-    case 4: launch_rows_w<K, 4>(a, t, lds, res[i], st); break;
-    case 6: launch_rows_w<K, 6>(a, t, lds, res[i], st); break;
-    case 8: launch_rows_w<K, 8>(a, t, lds, res[i], st); break;
-    case 10: launch_rows_w<K, 10>(a, t, lds, res[i], st); break;
-    case 12: launch_rows_w<K, 12>(a, t, lds, res[i], st); break;
-    case 14: launch_rows_w<K, 14>(a, t, lds, res[i], st); break;
-    default: launch_rows_w<K, 16>(a, t, lds, res[i], st); break;
+    const uint64_t items = a.n_rows * a.split;
+    switch (v->fast_bits) {
+    case 8: return launch_kind<8, CB, 2>(a, t, v, items, 0, st);
+    case 9: return launch_kind<9, CB, 2>(a, t, v, items, 0, st);
+    case 10: return launch_kind<10, CB, 2>(a, t, v, items, 0, st);
+    case 11: return launch_kind<11, CB, 2>(a, t, v, items, 0, st);
+    default: return launch_kind<12, CB, 2>(a, t, v, items, 0, st);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_rows launch: %s", hipGetErrorString(e));
+}
+
+int check_tuning(const df11_decode_tuning &t)
+{
+    if (t.waves && std::find(std::begin(kWaveChoices), std::end(kWaveChoices), (int)t.waves) == std::end(kWaveChoices))
+        return df11::fail(DF11_E_ARG, "tuning: %u waves per workgroup (need 0 or one of 4, 6, ..., 16)", t.waves);
+    if (t.stores > DF11_STORES_STREAMING) return df11::fail(DF11_E_ARG, "tuning: stores = %u", t.stores);
     return DF11_OK;
 }
 
@@ -938,13 +935,7 @@ extern "C" int df11_decode_rows(const df11_view *v, const int64_t *rows, uint64_
     if (n_rows > (UINT64_MAX >> 3)) return df11::fail(DF11_E_ARG, "df11_decode_rows: too many rows");
     TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, staging_bytes(v)};
     hipStream_t st = (hipStream_t)stream;
-    switch (v->fast_bits) {
-    case 8: return launch_rows<8>(a, t, v, st);
-    case 9: return launch_rows<9>(a, t, v, st);
-    case 10: return launch_rows<10>(a, t, v, st);
-    case 11: return launch_rows<11>(a, t, v, st);
-    default: return launch_rows<12>(a, t, v, st);
-    }
+    return v->chunk_bytes == 8 ? launch_rows<8>(a, t, v, st) : launch_rows<16>(a, t, v, st);
 }
 
 extern "C" int df11_decode(const df11_view *v, uint16_t *out, void *stream)
@@ -954,21 +945,30 @@ extern "C" int df11_decode(const df11_view *v, uint16_t *out, void *stream)
     if (!v->n) return DF11_OK;
     if (!out || ((uintptr_t)out & 15)) return df11::fail(DF11_E_ARG, "out must be a 16-byte aligned device pointer");
     uint16_t *outs[1] = {out};
-    return decode_views(v, outs, 1, (hipStream_t)stream);
+    return decode_views(v, outs, 1, df11_decode_tuning{}, (hipStream_t)stream);
+}
+
+extern "C" int df11_decode_batch_tuned(const df11_view *views, uint16_t *const *outs, uint32_t count,
+                                       const df11_decode_tuning *tuning, void *stream)
+{
+    if (count && (!views || !outs)) return df11::fail(DF11_E_ARG, "df11_decode_batch: null pointer");
+    const df11_decode_tuning tune = tuning ? *tuning : df11_decode_tuning{};
+    int rc = check_tuning(tune);
+    if (rc) return rc;
+    for (uint32_t i = 0; i < count; i++) {
+        rc = check_view(&views[i]);
+        if (rc) return rc;
+    }
+    for (uint32_t i = 0; i < count; i += kMaxBatch) {
+        rc = decode_views(views + i, outs + i, std::min(kMaxBatch, count - i), tune, (hipStream_t)stream);
+        if (rc) return rc;
+    }
+    return DF11_OK;
 }
 
 extern "C" int df11_decode_batch(const df11_view *views, uint16_t *const *outs, uint32_t count, void *stream)
 {
-    if (count && (!views || !outs)) return df11::fail(DF11_E_ARG, "df11_decode_batch: null pointer");
-    for (uint32_t i = 0; i < count; i++) {
-        int rc = check_view(&views[i]);
-        if (rc) return rc;
-    }
-    for (uint32_t i = 0; i < count; i += kMaxBatch) {
-        int rc = decode_views(views + i, outs + i, std::min(kMaxBatch, count - i), (hipStream_t)stream);
-        if (rc) return rc;
-    }
-    return DF11_OK;
+    return df11_decode_batch_tuned(views, outs, count, nullptr, stream);
 }
 
 namespace df11 {

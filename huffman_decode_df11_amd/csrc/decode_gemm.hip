@@ -145,7 +145,7 @@ __device__ __forceinline__ void decode_into_plane(const SegLoad &L, uint64_t til
                                                   uint32_t fast, uint32_t chain, uint32_t lane)
 {
     if (L.g0 >= tile_start && L.g1 >= L.g0 && L.g1 <= tile_start + kTile) {
-        const Window win = make_window(L.own, L.next, L.gap);
+        const auto win = make_window(L.own, L.next, L.gap);
         uint32_t cnt = L.count;
         if (!stored) {   // no stored counts: the locate pass walks the chunk
             const uint32_t c0 = lane * kChunkBits;
@@ -356,7 +356,7 @@ template <int K>
 __device__ __forceinline__ bool stage_seg(const SegLoad &L, bool stored, uint32_t dst, uint32_t fast,
                                           uint32_t chain, uint32_t lane)
 {
-    const Window win = make_window(L.own, L.next, L.gap);
+    const auto win = make_window(L.own, L.next, L.gap);
     uint32_t cnt = L.count;
     if (!stored) {
         const uint32_t c0 = lane * kChunkBits;
@@ -749,7 +749,7 @@ int cu_count() { return df11::cu_count(); }
 // Row blocks per unit of work: RB (the wide kernel's row-block group) > 1
 // divides the unit count.
 template <int K, int MT, int W, bool WIDE, int RB = 1>
-int launch(GemmArgs a, uint32_t lds, hipStream_t st)
+int launch(GemmArgs a, uint32_t lds, uint32_t forced_split, hipStream_t st)
 {
     void (*kern)(GemmArgs) = nullptr;
     if constexpr (WIDE) kern = decode_gemm_wide_kernel<K, MT, RB>;
@@ -777,10 +777,10 @@ int launch(GemmArgs a, uint32_t lds, hipStream_t st)
     const uint32_t slots = (uint32_t)(cu_count() * per_cu);
     // split K when there are too few row blocks to fill every slot
     uint32_t split = 1;
-    if (const char *e = getenv("DF11_GEMM_SPLIT")) split = (uint32_t)atoi(e);
+    if (forced_split) split = forced_split;
     else if (2 * n_groups <= slots) split = (slots + n_groups - 1) / n_groups;
     split = std::max(1u, std::min(split, a.tiles_per_row));
-    if (a.y_bf16) split = 1;   // one writer per BF16 element
+    if (a.y_bf16) split = 1;   // one writer per BF16 element (a request for more is refused before)
     a.tiles_per_split = (a.tiles_per_row + split - 1) / split;
     a.split = (a.tiles_per_row + a.tiles_per_split - 1) / a.tiles_per_split;
     if (a.split > 1) clear_y(a, st);
@@ -794,12 +794,30 @@ int launch(GemmArgs a, uint32_t lds, hipStream_t st)
 
 // Segment-parallel launch (B <= 32 * MT): row blocks split into `parts`
 // segment ranges so that every resident workgroup slot has work.
-template <int K, int W, int MT>
-int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_t st)
+// Per-wave staging of the segment-parallel kernel: a segment's elements, its
+// offset inside its first 512-element round and a round of slack.
+uint32_t seg_staging_bytes(uint32_t max_seg_elems)
 {
-    a.stg_bytes = std::max(4096u, (max_seg_elems + 1024u + 16u + 15u) & ~15u);
+    return std::max(4096u, (max_seg_elems + 1024u + 16u + 15u) & ~15u);
+}
+
+// The segment-parallel kernel's 8 waves keep their staging in the first
+// 64 KB of LDS (the emit loop holds byte addresses in 16 bits) and the
+// tables after it within the 160 KB of a CU.
+bool seg_kernel_fits(uint32_t fast_bits, uint32_t n_tables, uint32_t max_seg_elems)
+{
+    const uint32_t stg = seg_staging_bytes(max_seg_elems);
+    return 16 + 8 * stg <= 65520 && 16 + 8 * stg + (8u << fast_bits) + n_tables * 512u <= 160u * 1024u;
+}
+
+template <int K, int W, int MT>
+int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, uint32_t forced_parts, hipStream_t st)
+{
+    static_assert(W == 8, "staging limit computed for 8 waves");
+    a.stg_bytes = seg_staging_bytes(max_seg_elems);
     const uint32_t lds = 16 + W * a.stg_bytes + (8u << K) + n_tables * 512u;
-    if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm staging and tables do not fit in LDS");
+    if (!seg_kernel_fits(K, n_tables, max_seg_elems))
+        return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: segment staging and tables do not fit in LDS");
     static std::mutex mu;
     static int q_dev = -1, q_per_cu = 0;
     static uint32_t q_lds = 0;
@@ -824,10 +842,13 @@ int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_
     // wave of workgroups costs more than idle slots: up_proj, 448 row blocks
     // on 512 slots, 44 us in one part, 47 us in two)
     uint32_t parts = 1;
-    if (const char *e = getenv("DF11_GEMM_PARTS")) parts = (uint32_t)atoi(e);
-    else parts = std::max(1u, slots / a.n_rowblocks);
-    // at least one segment per wave
-    parts = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(parts, segs_per_rb / W));
+    if (forced_parts) {
+        parts = forced_parts;
+    } else {
+        parts = std::max(1u, slots / a.n_rowblocks);
+        // at least one segment per wave
+        parts = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(parts, segs_per_rb / W));
+    }
     if (a.y_bf16) parts = 1;   // one writer per BF16 element
     a.parts = parts;
     if (parts > 1) clear_y(a, st);
@@ -840,39 +861,73 @@ int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_
 }
 
 template <int K>
-int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, hipStream_t st)
+int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, const df11_gemm_tuning &tune,
+              hipStream_t st)
 {
-    // the tile-synchronous kernel also serves the w_debug output
-    // segment-parallel up to 40 rows of x (one batch tile to 32, two above);
-    // from 41 rows the wide kernel is faster (up_proj: 58.5 against 60.7 us
-    // at 33 rows, 66.8 against 64.9 at 48, 76.4 against 67.7 at 64)
-    if (a.B <= 40 && !a.w_debug && !getenv("DF11_GEMM_TILED")) {
-        if (a.B <= 32) return launch_seg<K, 8, 1>(a, n_tables, max_seg_elems, st);
-        return launch_seg<K, 8, 2>(a, n_tables, max_seg_elems, st);
+    // Automatic choice: segment-parallel up to 40 rows of x (one batch tile
+    // to 32, two above) when its staging fits; from 41 rows the wide kernel
+    // is faster (up_proj: 58.5 against 60.7 us at 33 rows, 66.8 against
+    // 64.9 at 48, 76.4 against 67.7 at 64).  w_debug calls take the
+    // tile-synchronous kernel up to 32 rows, the wide one above.
+    const uint32_t mt = (a.B + 31) / 32;
+    uint32_t kernel = tune.kernel;
+    if (kernel == DF11_GEMM_AUTO) {
+        if (a.B <= 40 && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems)) kernel = DF11_GEMM_SEGMENT;
+        else kernel = mt <= 1 ? DF11_GEMM_TILED : DF11_GEMM_WIDE;
+    }
+    if (kernel == DF11_GEMM_SEGMENT) {
+        if (a.w_debug || mt > 2)
+            return df11::fail(DF11_E_ARG, "tuning: the segment-parallel kernel takes up to 64 rows of x and no w_debug");
+        if (mt <= 1) return launch_seg<K, 8, 1>(a, n_tables, max_seg_elems, tune.parts, st);
+        return launch_seg<K, 8, 2>(a, n_tables, max_seg_elems, tune.parts, st);
     }
     constexpr int W = 8;
     const uint32_t lds = gemm_lds_bytes(K, n_tables);
     if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm tables do not fit in LDS");
-    const uint32_t mt = (a.B + 31) / 32;
-    if (mt <= 1) return launch<K, 1, W, false>(a, lds, st);
-    // two or more batch tiles: the kernel with the shared BF16 plane (which
-    // takes the place of the second exponent plane and 16 KB more);
-    // DF11_GEMM_NARROW selects the tile-synchronous kernel instead
-    const uint32_t lds_wide = lds + kTile;
-    const bool wide = lds_wide <= 160u * 1024u && !getenv("DF11_GEMM_NARROW");
-    // above 112 rows of x two row blocks share each x operand (a second
-    // exponent plane and BF16 plane; up_proj at 128 / 192 / 256 rows: 88.1 /
-    // 95.5 / 104.5 us against 92.6 / 113.7 / 141.0 with one, even at 96);
-    // DF11_GEMM_RB = 1 or 2 overrides
-    const uint32_t lds_wide2 = lds_wide + 3 * kTile;
-    const char *rbe = getenv("DF11_GEMM_RB");
-    const bool two = wide && lds_wide2 <= 160u * 1024u && (rbe ? atoi(rbe) == 2 : a.B > 112);
-    if (mt <= 2) return two ? launch<K, 2, 16, true, 2>(a, lds_wide2, st)
-                            : wide ? launch<K, 2, W, true>(a, lds_wide, st) : launch<K, 2, W, false>(a, lds, st);
-    if (mt <= 4) return two ? launch<K, 4, 16, true, 2>(a, lds_wide2, st)
-                            : wide ? launch<K, 4, W, true>(a, lds_wide, st) : launch<K, 4, W, false>(a, lds, st);
-    return two ? launch<K, 8, 16, true, 2>(a, lds_wide2, st)
-               : wide ? launch<K, 8, W, true>(a, lds_wide, st) : launch<K, 8, W, false>(a, lds, st);
+    if (kernel == DF11_GEMM_TILED) {
+        if (mt <= 1) return launch<K, 1, W, false>(a, lds, tune.split, st);
+        if (mt <= 2) return launch<K, 2, W, false>(a, lds, tune.split, st);
+        if (mt <= 4) return launch<K, 4, W, false>(a, lds, tune.split, st);
+        return launch<K, 8, W, false>(a, lds, tune.split, st);
+    }
+    // the wide kernel: a BF16 plane takes the place of the second exponent
+    // plane and 16 KB more; above 112 rows of x two row blocks share each x
+    // operand (a second exponent plane and BF16 plane; up_proj at 128 / 192
+    // / 256 rows: 88.1 / 95.5 / 104.5 us against 92.6 / 113.7 / 141.0 with
+    // one, even at 96)
+    if (mt < 2) return df11::fail(DF11_E_ARG, "tuning: the wide kernel takes more than 32 rows of x");
+    const uint32_t lds_wide = lds + kTile, lds_wide2 = lds_wide + 3 * kTile;
+    if (lds_wide > 160u * 1024u) {
+        if (tune.kernel == DF11_GEMM_WIDE) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: wide kernel planes do not fit in LDS");
+        if (mt <= 2) return launch<K, 2, W, false>(a, lds, tune.split, st);
+        if (mt <= 4) return launch<K, 4, W, false>(a, lds, tune.split, st);
+        return launch<K, 8, W, false>(a, lds, tune.split, st);
+    }
+    const bool fits2 = lds_wide2 <= 160u * 1024u;
+    if (tune.row_blocks == 2 && !fits2)
+        return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: two row blocks' planes do not fit in LDS");
+    const bool two = tune.row_blocks ? tune.row_blocks == 2 : fits2 && a.B > 112;
+    if (mt <= 2) return two ? launch<K, 2, 16, true, 2>(a, lds_wide2, tune.split, st)
+                            : launch<K, 2, W, true>(a, lds_wide, tune.split, st);
+    if (mt <= 4) return two ? launch<K, 4, 16, true, 2>(a, lds_wide2, tune.split, st)
+                            : launch<K, 4, W, true>(a, lds_wide, tune.split, st);
+    return two ? launch<K, 8, 16, true, 2>(a, lds_wide2, tune.split, st)
+               : launch<K, 8, W, true>(a, lds_wide, tune.split, st);
+}
+
+int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
+{
+    if (t.kernel > DF11_GEMM_TILED) return df11::fail(DF11_E_ARG, "tuning: kernel %u", t.kernel);
+    if (t.row_blocks > 2 || (t.row_blocks && t.kernel != DF11_GEMM_WIDE))
+        return df11::fail(DF11_E_ARG, "tuning: row_blocks %u (0, or 1 or 2 with the wide kernel)", t.row_blocks);
+    if (t.parts && t.kernel != DF11_GEMM_SEGMENT)
+        return df11::fail(DF11_E_ARG, "tuning: parts applies to the segment-parallel kernel");
+    if (t.split && t.kernel != DF11_GEMM_WIDE && t.kernel != DF11_GEMM_TILED)
+        return df11::fail(DF11_E_ARG, "tuning: split applies to the wide and tile-synchronous kernels");
+    if (bf16_y && (t.parts > 1 || t.split > 1))
+        return df11::fail(DF11_E_ARG, "tuning: a BF16 y has one writer per element (parts and split 1)");
+    if (t.parts > (1u << 16) || t.split > (1u << 16)) return df11::fail(DF11_E_ARG, "tuning: parts or split too large");
+    return DF11_OK;
 }
 
 }  // namespace
@@ -886,8 +941,17 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
 extern "C" int df11_decode_gemm_out(const df11_view *w, const uint16_t *x, uint32_t B, void *y, int y_dtype,
                                     uint16_t *w_debug, void *stream)
 {
+    return df11_decode_gemm_tuned(w, x, B, y, y_dtype, w_debug, nullptr, stream);
+}
+
+extern "C" int df11_decode_gemm_tuned(const df11_view *w, const uint16_t *x, uint32_t B, void *y, int y_dtype,
+                                      uint16_t *w_debug, const df11_gemm_tuning *tuning, void *stream)
+{
     if (y_dtype != DF11_Y_F32 && y_dtype != DF11_Y_BF16)
         return df11::fail(DF11_E_ARG, "df11_decode_gemm_out: unknown y_dtype %d", y_dtype);
+    const df11_gemm_tuning tune = tuning ? *tuning : df11_gemm_tuning{};
+    int rc = check_gemm_tuning(tune, y_dtype == DF11_Y_BF16);
+    if (rc) return rc;
     if (!w || !x || !y) return df11::fail(DF11_E_ARG, "df11_decode_gemm: null pointer");
     if (B < 1 || B > 256) return df11::fail(DF11_E_ARG, "B = %u outside 1..256", B);
     if (w->tile_rows != kTR || w->tile_cols != kTC || w->tile_kchunk != kKC || w->align_elems != kTile ||
@@ -903,6 +967,14 @@ extern "C" int df11_decode_gemm_out(const df11_view *w, const uint16_t *x, uint3
     if (w->fast_bits < DF11_FAST_BITS_MIN || w->fast_bits > DF11_FAST_BITS_MAX || w->n_tables < 1 ||
         w->n_tables > DF11_MAX_TABLES || w->n_chain != (uint64_t)w->n_tables * 256 || w->n_fast != (2ull << w->fast_bits))
         return df11::fail(DF11_E_ARG, "table sizes inconsistent");
+    // staging is sized from max_seg_elems; a segment of 64 16-byte chunks
+    // holds at most 8192 / min_len codes
+    if (w->min_len < 1 || w->min_len > w->max_len || w->max_len > DF11_MAX_LEN || !w->max_seg_elems ||
+        w->max_seg_elems > (8192u + w->min_len - 1) / w->min_len)
+        return df11::fail(DF11_E_ARG, "view: code lengths %u..%u or max_seg_elems %u out of range", w->min_len, w->max_len,
+                          w->max_seg_elems);
+    if (!w->exp_words || !w->sm || !w->gaps || !w->segs || !w->chain || !w->fast)
+        return df11::fail(DF11_E_ARG, "null array in view");
     if (((uintptr_t)x & 15) || ((uintptr_t)y & 15) || ((uintptr_t)w_debug & 15) || ((uintptr_t)w->sm & 15) ||
         ((uintptr_t)w->exp_words & 15) || ((uintptr_t)w->fast & 15) || ((uintptr_t)w->chain & 15))
         return df11::fail(DF11_E_ARG, "x, y, w_debug and the view arrays must be 16-byte aligned");
@@ -928,10 +1000,10 @@ extern "C" int df11_decode_gemm_out(const df11_view *w, const uint16_t *x, uint3
     a.n_segments = w->n_segments;
     hipStream_t st = (hipStream_t)stream;
     switch (w->fast_bits) {
-    case 8: return launch_mt<8>(a, w->n_tables, w->max_seg_elems, st);
-    case 9: return launch_mt<9>(a, w->n_tables, w->max_seg_elems, st);
-    case 10: return launch_mt<10>(a, w->n_tables, w->max_seg_elems, st);
-    case 11: return launch_mt<11>(a, w->n_tables, w->max_seg_elems, st);
-    default: return launch_mt<12>(a, w->n_tables, w->max_seg_elems, st);
+    case 8: return launch_mt<8>(a, w->n_tables, w->max_seg_elems, tune, st);
+    case 9: return launch_mt<9>(a, w->n_tables, w->max_seg_elems, tune, st);
+    case 10: return launch_mt<10>(a, w->n_tables, w->max_seg_elems, tune, st);
+    case 11: return launch_mt<11>(a, w->n_tables, w->max_seg_elems, tune, st);
+    default: return launch_mt<12>(a, w->n_tables, w->max_seg_elems, tune, st);
     }
 }

@@ -17,8 +17,9 @@
 // bytes ([P1] "DFloat11无损压缩技术：基于哈夫曼编码的BFloat16大模型显存优化方案"
 // 2.2 item 2) into BF16.
 //
-// Bit window.  The 160 bits live in five registers, most significant first;
-// consuming b bits shifts all five left with v_alignbit_b32 by (32 - b) mod 32,
+// Bit window.  The chunk plus one look-ahead word live in registers, most
+// significant first (160 bits in five registers for 16-byte chunks);
+// consuming b bits shifts them all left with v_alignbit_b32 by (32 - b) mod 32,
 // which is exactly the low five bits of the table word meta = (codes << 16) - b,
 // so a lookup costs one LDS read and no address arithmetic on the stream.
 // Cursor.  A lane keeps one 32-bit state word: bits 0..15 hold kM0 - p for
@@ -79,23 +80,31 @@ __device__ __forceinline__ uint32_t lshl_add_s(uint32_t a, uint32_t b)
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
-// A lane's 160-bit stream window, first stream bit in bit 31 of w0.
+// A lane's stream window of 32 * NW bits, first stream bit in bit 31 of
+// w[0]: its chunk's NW - 1 words and the next chunk's first word (five
+// registers for 16-byte chunks, three for 8-byte chunks).
+template <int NW>
 struct Window {
-    uint32_t w0, w1, w2, w3, w4;
+    uint32_t w[NW];
     // consume b bits (1 <= b <= 32) where sh holds (32 - b) mod 32 in its low five bits
     __device__ __forceinline__ void consume(uint32_t sh)
     {
-        w0 = __builtin_amdgcn_alignbit(w0, w1, sh);
-        w1 = __builtin_amdgcn_alignbit(w1, w2, sh);
-        w2 = __builtin_amdgcn_alignbit(w2, w3, sh);
-        w3 = __builtin_amdgcn_alignbit(w3, w4, sh);
-        w4 = __builtin_amdgcn_alignbit(w4, 0u, sh);
+#pragma unroll
+        for (int i = 0; i + 1 < NW; i++) w[i] = __builtin_amdgcn_alignbit(w[i], w[i + 1], sh);
+        w[NW - 1] = __builtin_amdgcn_alignbit(w[NW - 1], 0u, sh);
     }
 };
 
-__device__ __forceinline__ Window make_window(uint4 own, uint32_t next, uint32_t gap)
+__device__ __forceinline__ Window<5> make_window(uint4 own, uint32_t next, uint32_t gap)
 {
-    Window w{own.x, own.y, own.z, own.w, next};
+    Window<5> w{{own.x, own.y, own.z, own.w, next}};
+    if (gap) w.consume(0u - gap);
+    return w;
+}
+
+__device__ __forceinline__ Window<3> make_window(uint2 own, uint32_t next, uint32_t gap)
+{
+    Window<3> w{{own.x, own.y, next}};
     if (gap) w.consume(0u - gap);
     return w;
 }
@@ -134,21 +143,21 @@ __device__ __forceinline__ void wave_lds_sync()
 // the window at p0.  Multi-code lookups run while a whole table window
 // (K bits) lies before `end`, so every code they count starts inside the
 // chunk; the last bits are then walked one code at a time.
-template <int K>
-__device__ __forceinline__ uint32_t count_codes(Window w, uint32_t fast, uint32_t chain, uint32_t p0,
+template <int K, int NW>
+__device__ __forceinline__ uint32_t count_codes(Window<NW> w, uint32_t fast, uint32_t chain, uint32_t p0,
                                                 uint32_t end)
 {
     uint32_t st = kM0 - p0;
     const uint32_t lim = kM0 - end;            // p < end      <=>  (st & 0xFFFF) > lim
     const uint32_t limk = lim + K;             // p + K <= end <=>  (st & 0xFFFF) >= limk
     while ((st & 0xFFFFu) >= limk) {
-        uint32_t meta = ld32(lshl_add_s<3>(w.w0 >> (32 - K), fast) + 4);
-        if (meta == 0) meta = (1u << 16) - ((chain_decode(chain, w.w0) >> 8) & 0x3Fu);
+        uint32_t meta = ld32(lshl_add_s<3>(w.w[0] >> (32 - K), fast) + 4);
+        if (meta == 0) meta = (1u << 16) - ((chain_decode(chain, w.w[0]) >> 8) & 0x3Fu);
         w.consume(meta);
         st += meta;
     }
     while ((st & 0xFFFFu) > lim) {
-        const uint32_t step = (1u << 16) - ((chain_decode(chain, w.w0) >> 8) & 0x3Fu);
+        const uint32_t step = (1u << 16) - ((chain_decode(chain, w.w[0]) >> 8) & 0x3Fu);
         w.consume(step);
         st += step;
     }
@@ -157,17 +166,17 @@ __device__ __forceinline__ uint32_t count_codes(Window w, uint32_t fast, uint32_
 
 // Emit: decode `cnt` codes from the window w and write their rotated
 // exponents to LDS bytes [wpos, wpos + cnt).  wpos + cnt must be below 65536.
-template <int K>
-__device__ __forceinline__ void emit_codes(Window w, uint32_t fast, uint32_t chain, uint32_t wpos,
+template <int K, int NW>
+__device__ __forceinline__ void emit_codes(Window<NW> w, uint32_t fast, uint32_t chain, uint32_t wpos,
                                            uint32_t cnt)
 {
     uint32_t st = (wpos << 16) | kM0;   // the low half only has to keep borrowing
     const uint32_t bound = (wpos + cnt - 3u) << 16;   // st < bound <=> at least 4 codes left
     while (st < bound) {
-        const uint2 f = ld64(lshl_add_s<3>(w.w0 >> (32 - K), fast));
+        const uint2 f = ld64(lshl_add_s<3>(w.w[0] >> (32 - K), fast));
         uint32_t syms = f.x, meta = f.y;
         if (meta == 0) {
-            const uint32_t e = chain_decode(chain, w.w0);
+            const uint32_t e = chain_decode(chain, w.w[0]);
             syms = rot_exp(e & 0xFFu);
             meta = (1u << 16) - ((e >> 8) & 0x3Fu);
         }
@@ -185,7 +194,7 @@ __device__ __forceinline__ void emit_codes(Window w, uint32_t fast, uint32_t cha
     }
     const uint32_t lend = wpos + cnt;
     while ((st >> 16) < lend) {
-        const uint32_t e = chain_decode(chain, w.w0);
+        const uint32_t e = chain_decode(chain, w.w[0]);
         const uint32_t step = (1u << 16) - ((e >> 8) & 0x3Fu);
         st8(st >> 16, rot_exp(e & 0xFFu));
         w.consume(step);

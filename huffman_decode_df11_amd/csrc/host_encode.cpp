@@ -65,8 +65,9 @@ namespace df11 {
 
 int check_layout(const df11_layout &L, uint64_t n)
 {
-    if (L.chunk_bytes < 4 || L.chunk_bytes > 32 || L.chunk_bytes % 4)
-        return fail(DF11_E_ARG, "chunk_bytes %u: need a multiple of 4 in 4..32", L.chunk_bytes);
+    // the decode kernels read 16- and 8-byte chunks: no other layout is written
+    if (L.chunk_bytes != 16 && L.chunk_bytes != 8)
+        return fail(DF11_E_ARG, "chunk_bytes %u: the decoders read 8- or 16-byte chunks", L.chunk_bytes);
     if (L.seg_lanes != DF11_SEG_LANES)
         return fail(DF11_E_ARG, "seg_lanes %u: this build decodes one segment per 64-lane wavefront", L.seg_lanes);
     if (L.align_elems % 16)

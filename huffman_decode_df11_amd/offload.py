@@ -32,6 +32,19 @@ def _round(n: int) -> int:
     return (n + _ALIGN - 1) // _ALIGN * _ALIGN
 
 
+def _same_tables(a, b) -> bool:
+    """Two codebooks decode alike: the same object, or equal code lengths and
+    lookup tables."""
+    if a is b:
+        return True
+    if (a.n_tables, a.fast_bits, a.min_len, a.max_len) != (b.n_tables, b.fast_bits, b.min_len, b.max_len):
+        return False
+    nt, nf = a.n_tables * 256, 2 << a.fast_bits
+    return (bytes(a.len) == bytes(b.len) and
+            np.array_equal(np.ctypeslib.as_array(a.chain)[:nt], np.ctypeslib.as_array(b.chain)[:nt]) and
+            np.array_equal(np.ctypeslib.as_array(a.fast)[:nf], np.ctypeslib.as_array(b.fast)[:nf]))
+
+
 class OffloadedModel:
     """Groups [(name, [(matrix, Encoded)])] held in pinned host memory."""
 
@@ -42,6 +55,12 @@ class OffloadedModel:
         max_blob = 0
         self.n_elements = 0
         for gname, mats in groups:
+            # the group's matrices decode through the first one's device tables
+            cb0 = mats[0][1].codebook
+            for name, enc in mats[1:]:
+                if not _same_tables(enc.codebook, cb0):
+                    raise ValueError("group %s: %s has another codebook than %s; a group shares one"
+                                     % (gname, name, mats[0][0]))
             layout, off = [], 0
             for name, enc in mats:
                 offs = {}

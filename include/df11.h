@@ -119,7 +119,8 @@ typedef struct df11_codebook {
 /* How the stream is laid out.  Zero-initialise and set what you need:
  * chunk_bytes 0 means 16; seg_lanes 0 means 64. */
 typedef struct df11_layout {
-    uint32_t chunk_bytes;   /* stream bytes per lane: multiple of 4 in 4..32 */
+    uint32_t chunk_bytes;   /* stream bytes per lane: 16, or 8 (twice the segments, for
+                               small tensors that would leave most of the GPU idle) */
     uint32_t seg_lanes;     /* lanes per segment: must be 64 */
     uint64_t align_elems;   /* 0, or begin a new segment every align_elems elements */
     uint64_t rows, cols;    /* matrix shape; cols = 0 means a flat tensor of rows = n */
@@ -184,9 +185,10 @@ int df11_codebook_build(const uint64_t hist[256], uint32_t max_len, uint32_t fas
  * encoding ([P1] 2.2 item 2; [P3] 4.2): exponent stream, sign+mantissa
  * bytes, per-lane gaps and per-segment records, laid out by `layout` (NULL
  * = defaults).  *out receives the encoding; free it with df11_encoded_free.
- * Errors: E_ARG (null pointers, layout out of range, rows*cols != n, tile
- * shape not dividing the matrix or tile_cols not a multiple of 16),
- * E_UNCODED (an exponent without a code), E_ALLOC. */
+ * Every layout it accepts is one the decode calls read.
+ * Errors: E_ARG (null pointers, chunk_bytes other than 8 or 16, layout out
+ * of range, rows*cols != n, tile shape not dividing the matrix or tile_cols
+ * not a multiple of 16), E_UNCODED (an exponent without a code), E_ALLOC. */
 int df11_encode(const uint16_t *bf16_bits, uint64_t n, const df11_codebook *cb,
                 const df11_layout *layout, df11_encoded **out);
 
@@ -248,11 +250,14 @@ int df11_device_encoded_to_host(const df11_device_encoded *enc, df11_encoded **o
  * ([P1] 2.2 item 3; [P3] 2.2 locate/reconstruct with a prefix sum).
  * out: device, 16-byte aligned, n elements.  Bit-exact: every input pattern,
  * including zeros, subnormals, Inf and NaN payloads, comes back unchanged.
- * Writes stay inside out[0..n) even for a corrupt stream (then the values are
- * unspecified).  n = 0 is a no-op.  Errors: E_ARG (null, misaligned, view
- * inconsistent), E_UNSUPPORTED (tables too large for the kernel, or a
- * layout other than 16-byte chunks: the encoders write other chunk sizes,
- * the decode kernels are built for 16), E_DEVICE. */
+ * Writes stay inside out[0..n) even for a corrupt stream (the exponent
+ * words, gaps or counts; then the values are unspecified): every write
+ * address comes from the segment records, which are checked against n.
+ * The view's max_seg_elems (set by the encoders) sizes the staging: a
+ * hand-built view that understates it leaves the larger segments' outputs
+ * unwritten.  n = 0 is a no-op.  Errors: E_ARG (null, misaligned, view
+ * inconsistent, max_seg_elems 0 or above segment bits / shortest code),
+ * E_UNSUPPORTED (tables too large for the kernel), E_DEVICE. */
 int df11_decode(const df11_view *device_view, uint16_t *out, void *stream);
 
 /* Decode several device views in one launch: view i into outs[i] (device,
@@ -264,6 +269,24 @@ int df11_decode(const df11_view *device_view, uint16_t *out, void *stream);
  * launches of 16. */
 int df11_decode_batch(const df11_view *device_views, uint16_t *const *outs, uint32_t count,
                       void *stream);
+
+/* Explicit launch choices of a decode, for measurements and tests.  A zeroed
+ * struct, or NULL, is the library's own choice. */
+#define DF11_STORES_AUTO 0       /* streaming when the launch writes more than the 256 MB last-level cache */
+#define DF11_STORES_CACHED 1     /* normal loads and stores: the output stays cache-resident for its consumer */
+#define DF11_STORES_STREAMING 2  /* nontemporal sign+mantissa loads and BF16 stores */
+typedef struct df11_decode_tuning {
+    uint32_t waves;        /* waves per workgroup: 0 = from occupancy and size, else 4, 6, ..., 16 */
+    uint32_t stores;       /* DF11_STORES_* */
+    uint32_t reserved[6];  /* zero */
+} df11_decode_tuning;
+
+/* df11_decode_batch with explicit launch choices ([P3] 5.2: occupancy is
+ * the tuning lever).  The output is the same for every choice.  Errors: as
+ * df11_decode_batch, and E_ARG for a choice out of range or a wave count
+ * whose staging and tables do not fit in LDS. */
+int df11_decode_batch_tuned(const df11_view *device_views, uint16_t *const *outs, uint32_t count,
+                            const df11_decode_tuning *tuning, void *stream);
 
 /* Row gather: decode rows rows[0..n_rows) of a row-major [rows, cols] view
  * into out[i][0..cols) (device, 16-byte aligned, n_rows x cols BF16), for
@@ -293,11 +316,15 @@ int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t
  * The kernel is chosen by B: up to 40 rows a segment-parallel kernel, above
  * that one that merges each decoded tile once into a BF16 tile in LDS shared
  * by all batch tiles (two row blocks per workgroup above 112 rows); w_debug
- * calls up to 32 rows take a tile-synchronous kernel.  The environment
- * variables DF11_GEMM_TILED, DF11_GEMM_NARROW, DF11_GEMM_RB (1 or 2),
- * DF11_GEMM_PARTS and DF11_GEMM_SPLIT override these choices for
- * measurements.  Errors: E_ARG (null, misaligned, layout not from
- * df11_gemm_layout, B out of range), E_UNSUPPORTED, E_DEVICE. */
+ * calls up to 32 rows, and weights whose segments are too large for the
+ * segment-parallel kernel's staging, take a tile-synchronous kernel
+ * (df11_decode_gemm_tuned makes the choice explicit).
+ * Non-finite x: a row of x holding Inf or NaN gives a non-finite row of y;
+ * where a plain product would give +-Inf, y may hold NaN instead (the
+ * segment-parallel kernel multiplies the weights of a neighbouring segment,
+ * masked to +0, by the same x).  Rows of x without them are unaffected.
+ * Errors: E_ARG (null, misaligned, layout not from df11_gemm_layout, B out
+ * of range), E_UNSUPPORTED, E_DEVICE. */
 int df11_decode_gemm(const df11_view *device_view, const uint16_t *x, uint32_t B,
                      float *y, uint16_t *w_debug, void *stream);
 
@@ -313,6 +340,32 @@ int df11_decode_gemm(const df11_view *device_view, const uint16_t *x, uint32_t B
  * Errors: as df11_decode_gemm, and E_ARG for an unknown y_dtype. */
 int df11_decode_gemm_out(const df11_view *device_view, const uint16_t *x, uint32_t B,
                          void *y, int y_dtype, uint16_t *w_debug, void *stream);
+
+/* Explicit kernel choices of a fused product, for measurements and tests.
+ * A zeroed struct, or NULL, is the library's own choice. */
+#define DF11_GEMM_AUTO 0
+#define DF11_GEMM_SEGMENT 1   /* segment-parallel: up to 64 rows of x, no w_debug */
+#define DF11_GEMM_WIDE 2      /* one BF16 tile in LDS shared by the batch tiles: 33 rows of x or more */
+#define DF11_GEMM_TILED 3     /* tile-synchronous, any rows of x */
+typedef struct df11_gemm_tuning {
+    uint32_t kernel;       /* DF11_GEMM_* */
+    uint32_t row_blocks;   /* wide kernel: 0 = by B, else 1 or 2 row blocks per workgroup */
+    uint32_t parts;        /* segment-parallel kernel: 0 = enough runs of a row block's segments to
+                              fill the device, else that many (float32 y) */
+    uint32_t split;        /* wide and tile-synchronous kernels: 0 = by occupancy, else that many K
+                              ranges per row block (float32 y) */
+    uint32_t reserved[4];  /* zero */
+} df11_gemm_tuning;
+
+/* df11_decode_gemm_out with explicit kernel choices ([P3] 5.2: the kernel
+ * shape is tuned to the hardware).  y agrees with every choice within the
+ * float32 summation order.  Errors: as df11_decode_gemm_out, E_ARG for a
+ * choice that does not apply (w_debug or more than 64 rows of x on the
+ * segment-parallel kernel, 32 rows or fewer on the wide one, parts or split
+ * above 1 with a BF16 y), E_UNSUPPORTED when the chosen kernel's LDS does
+ * not fit this weight. */
+int df11_decode_gemm_tuned(const df11_view *device_view, const uint16_t *x, uint32_t B, void *y,
+                           int y_dtype, uint16_t *w_debug, const df11_gemm_tuning *tuning, void *stream);
 
 /* ---------------------------------------------------------------- utilities */
 const char *df11_status_string(int status);

@@ -42,10 +42,23 @@ def build(force: bool = False) -> str:
     return _SO
 
 
+def build_sanitized() -> str:
+    """The oracle with AddressSanitizer and UndefinedBehaviorSanitizer
+    (clang, shared sanitizer runtime) into oracle/_build_san, for the CPU
+    tests run under the sanitizers (DF11_ORACLE_LIBRARY points at it)."""
+    so = os.path.join(os.path.dirname(os.path.dirname(_SO)), "_build_san", "liborc.so")
+    os.makedirs(os.path.dirname(so), exist_ok=True)
+    subprocess.check_call(["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c99", "-Wall", "-shared", "-fPIC",
+                           "-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+                           "-shared-libsan", "-fno-omit-frame-pointer", "-o", so, _SRC])
+    return so
+
+
 def lib():
     global _lib
     if _lib is None:
-        L = ctypes.CDLL(build())
+        path = os.environ.get("DF11_ORACLE_LIBRARY") or build()
+        L = ctypes.CDLL(path)
         L.orc_histogram.argtypes = [_u16p, _u64, _u64p]
         L.orc_huffman_lengths.argtypes = [_u64p, _u8p]
         L.orc_huffman_lengths.restype = ctypes.c_int

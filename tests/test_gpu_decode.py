@@ -48,15 +48,18 @@ def _decode_checked(dt, n, margin=64):
 
 def _check(u, layout=None, fast_bits=11, max_len=32, oracle=True, tag=""):
     u = np.ascontiguousarray(u).reshape(-1)
-    _say("case", tag, "n=%d fast_bits=%d" % (u.size, fast_bits))
+    cb_bytes = layout.chunk_bytes if layout is not None and layout.chunk_bytes else 16
+    _say("case", tag, "n=%d fast_bits=%d chunk=%d" % (u.size, fast_bits, cb_bytes))
     enc = api.encode(u, layout=layout, fast_bits=fast_bits, max_len=max_len)
     dt = enc.to("cuda")
     got = _decode_checked(dt, u.size)
     if oracle:
         ln = api.codebook_lengths(enc.codebook)
-        ref = orc.encode(u, lengths=ln, chunk_bytes=16, align_elems=layout.align_elems if layout else 0)
+        ref = orc.encode(u, lengths=ln, chunk_bytes=cb_bytes, align_elems=layout.align_elems if layout else 0)
+        assert np.array_equal(enc.stream_bytes_msb_first(), ref.E)
+        assert np.array_equal(enc.counts, ref.counts) and np.array_equal(enc.gaps, ref.gaps)
         want = orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln,
-                          seg_bits=16 * 8 * 64, align_elems=layout.align_elems if layout else 0)
+                          seg_bits=cb_bytes * 8 * 64, align_elems=layout.align_elems if layout else 0)
     else:
         want = u
     bad = np.nonzero(got != want)[0]
@@ -347,3 +350,145 @@ def test_batch_mixed_layouts():
         got = _to_bits(o)
         assert np.array_equal(got[:t.size], t.reshape(-1))
         assert (got[t.size:] == 0x5555).all()
+
+
+# ------------------------------------------------------------ 8-byte chunks
+
+C8 = dict(chunk_bytes=8)
+
+
+@pytest.mark.parametrize("fast_bits", [8, 11, 12])
+def test_chunk8_tensor_1024x1024(fast_bits):
+    _check(synth.tensor_1024(seed=0), layout=api.make_layout(**C8), fast_bits=fast_bits, tag="chunk8 1024x1024")
+
+
+@pytest.mark.parametrize("n", [1, 17, 1000, 65537, 1_000_003])
+def test_chunk8_ragged_sizes(n):
+    _check(synth.normal_bf16(n, 0.02, seed=n + 1), layout=api.make_layout(**C8), tag="chunk8 ragged")
+
+
+@pytest.mark.parametrize("name", ["exhaustive", "adversarial", "fibonacci", "one", "aligned"])
+def test_chunk8_workloads(name):
+    u = {"exhaustive": synth.exhaustive_bf16,
+         "adversarial": lambda: synth.adversarial_bf16(1 << 20, seed=6),
+         "fibonacci": lambda: synth.fibonacci_bf16(seed=7),
+         "one": lambda: (np.full(70_001, 0x3F80, np.uint16) | (np.arange(70_001) % 256)).astype(np.uint16),
+         "aligned": lambda: synth.normal_bf16(300_000, 0.02, seed=8)}[name]()
+    lay = api.make_layout(chunk_bytes=8, align_elems=2048 if name == "aligned" else 0)
+    _check(u, layout=lay, tag="chunk8 " + name)
+
+
+@pytest.mark.parametrize("kc", [0, 8])
+def test_chunk8_tile_order_decodes_row_major(kc):
+    rows, cols = 128, 2048
+    u = synth.normal_bf16(rows * cols, 0.02, seed=9).reshape(rows, cols)
+    lay = api.make_layout(chunk_bytes=8, rows=rows, cols=cols, tile_rows=32, tile_cols=512, align_elems=32 * 512,
+                          tile_kchunk=kc)
+    _say("case chunk8 tile order kc=%d" % kc)
+    got = _decode_checked(api.encode(u, layout=lay).to("cuda"), u.size)
+    assert np.array_equal(got, u.reshape(-1))
+
+
+@pytest.mark.parametrize("name", ["normal", "fibonacci"])
+def test_chunk8_locate_pass(name):
+    u = {"normal": lambda: synth.normal_bf16(1_000_003, 0.02, seed=10),
+         "fibonacci": lambda: synth.fibonacci_bf16(seed=11)}[name]()
+    _say("case chunk8 locate pass", name)
+    dt = api.encode(u, layout=api.make_layout(**C8)).to("cuda")
+    dt.view.counts = None
+    dt.view.n_counts = 0
+    assert np.array_equal(_decode_checked(dt, u.size), u)
+
+
+def test_chunk8_batch_and_mixed_chunk_sizes_refused():
+    """A launch of 8-byte-chunk views decodes them all; views of different
+    chunk sizes cannot share a launch."""
+    from huffman_decode_df11_amd import _lib
+    ts = [synth.normal_bf16(n, 0.02, seed=12 + n) for n in (5, 4_194_304, 77_777)]
+    hist = None
+    for t in ts:
+        hist = api.hist_accumulate(t, hist)
+    cb = api.build_codebook(hist)
+    dts = [api.encode(t, codebook=cb, layout=api.make_layout(**C8)).to("cuda") for t in ts]
+    _say("case chunk8 batch")
+    outs = [torch.full((t.size + 16,), 0x5555, dtype=torch.int16, device="cuda") for t in ts]
+    api.decode_batch(dts, outs=[o.view(torch.bfloat16) for o in outs])
+    torch.cuda.synchronize()
+    for t, o in zip(ts, outs):
+        got = _to_bits(o)
+        assert np.array_equal(got[:t.size], t) and (got[t.size:] == 0x5555).all()
+    d16 = api.encode(ts[0], codebook=cb).to("cuda")
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.decode_batch([dts[1], d16])
+    assert ei.value.status == -1
+
+
+# ------------------------------------------------------------ launch choices
+
+@pytest.mark.parametrize("chunk", [16, 8])
+def test_every_launch_choice_gives_the_same_output(chunk):
+    """Explicit waves per workgroup and store kinds (tuning) on a Llama-sized
+    k_proj and a ragged tensor in one launch: every choice bit-exact."""
+    from huffman_decode_df11_amd import _lib
+    ts = [synth.normal_bf16(1024 * 4096, 0.02, seed=20), synth.normal_bf16(300_001, 0.02, seed=21)]
+    hist = api.hist_accumulate(ts[1], api.hist_accumulate(ts[0]))
+    cb = api.build_codebook(hist)
+    dts = [api.encode(t, codebook=cb, layout=api.make_layout(chunk_bytes=chunk)).to("cuda") for t in ts]
+    for waves in (0, 4, 6, 8, 10, 12, 14, 16):
+        for stores in (_lib.DF11_STORES_AUTO, _lib.DF11_STORES_CACHED, _lib.DF11_STORES_STREAMING):
+            _say("case tuning chunk=%d waves=%d stores=%d" % (chunk, waves, stores))
+            outs = [torch.full((t.size + 16,), 0x5555, dtype=torch.int16, device="cuda") for t in ts]
+            api.decode_batch(dts, outs=[o.view(torch.bfloat16) for o in outs],
+                             tuning=api.decode_tuning(waves=waves, stores=stores))
+            torch.cuda.synchronize()
+            for t, o in zip(ts, outs):
+                got = _to_bits(o)
+                assert np.array_equal(got[:t.size], t) and (got[t.size:] == 0x5555).all()
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.decode_batch(dts, tuning=api.decode_tuning(waves=5))
+    assert ei.value.status == -1
+
+
+# ------------------------------------------------------------ corrupt streams
+
+GUARD = 1024   # elements of guard band on either side of the output (16-byte aligned)
+
+
+def _guarded_decode(dt, n, fill):
+    buf = torch.full((n + 2 * GUARD,), fill, dtype=torch.int16, device="cuda")
+    api.decode(dt, out=buf[GUARD:GUARD + n].view(torch.bfloat16))
+    torch.cuda.synchronize()
+    b = _to_bits(buf)
+    return b[:GUARD], b[GUARD:GUARD + n], b[GUARD + n:]
+
+
+@pytest.mark.parametrize("layout", ["row-major", "chunk8", "tile-order", "aligned", "no-counts"])
+def test_corrupt_exponent_words_write_only_inside_the_output(layout):
+    """Random bits flipped in the exponent words of the device copy (the
+    other metadata intact): the decoded values are garbage, but every write
+    stays inside out[0, n) -- the guard bands on both sides keep their
+    sentinels -- and the call completes.  Without stored counts the locate
+    pass reads the corrupt stream too (segments whose counts no longer add
+    up to their records are skipped)."""
+    rows, cols = 300, 2048
+    u = synth.normal_bf16(rows * cols, 0.02, seed=90).reshape(rows, cols)
+    lay = {"row-major": None, "chunk8": api.make_layout(chunk_bytes=8), "tile-order": api.gemm_layout(rows - 12, cols),
+           "aligned": api.make_layout(align_elems=4096), "no-counts": None}[layout]
+    if layout == "tile-order":
+        u = u[:rows - 12]
+    n = u.size
+    dt = api.encode(u, layout=lay).to("cuda")
+    if layout == "no-counts":
+        dt.view.counts = None
+        dt.view.n_counts = 0
+    words = dt.tensors["exp_words"].view(torch.int32)
+    gen = torch.Generator(device="cuda").manual_seed(91)
+    for density in (0.01, 0.5):
+        _say("case corrupt %s density %.2f" % (layout, density))
+        flips = torch.randint(-2 ** 31, 2 ** 31 - 1, words.shape, generator=gen, device="cuda", dtype=torch.int32)
+        keep = torch.rand(words.shape, generator=gen, device="cuda") >= density
+        words ^= torch.where(keep, torch.zeros_like(flips), flips)
+        for fill in (0x5555, -0x5556):
+            lo, _, hi = _guarded_decode(dt, n, fill)
+            s = fill & 0xFFFF
+            assert (lo == s).all() and (hi == s).all(), "a write left out[0, n)"

@@ -54,8 +54,8 @@ def test_device_encoder_matches_host(name, lay):
     layout = {"default": None, "chunk8": api.make_layout(chunk_bytes=8),
               "chunk32": api.make_layout(chunk_bytes=32), "aligned": api.make_layout(align_elems=4112)}[lay]
     cb = api.build_codebook(api.hist_accumulate(u))
-    if lay == "chunk32" and cb.min_len == 1:
-        # 256-bit chunks of 1-bit codes overflow the count byte: both encoders refuse
+    if lay == "chunk32":
+        # the decoders read 8- and 16-byte chunks only: both encoders refuse others
         for f in (lambda: api.encode(u, codebook=cb, layout=layout),
                   lambda: api.encode_device(_dev(u), codebook=cb, layout=layout)):
             with pytest.raises(_lib.DF11Error) as ei:
@@ -116,3 +116,32 @@ def test_device_encode_errors():
     assert ei.value.status == -1
     e = api.encode_device(_dev(np.zeros(0, np.uint16)), codebook=cb)
     assert e.n == 0 and e.n_segments == 0
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("lay", ["default", "chunk8", "aligned"])
+def test_device_encoder_matches_oracle(name, lay):
+    """The GPU encoder against the oracle directly (not through the host
+    encoder): stream bytes, sign+mantissa bytes, gaps, code counts and
+    segment records on the same inputs and code lengths, including the
+    exhaustive 65,536-pattern tensor and the Fibonacci histogram whose
+    32-bit length limit binds."""
+    u = WORKLOADS[name]()
+    _say("case encode_device vs oracle %s %s n=%d" % (name, lay, u.size))
+    kw = {"default": {}, "chunk8": dict(chunk_bytes=8), "aligned": dict(align_elems=4112)}[lay]
+    d = api.encode_device(_dev(u), layout=api.make_layout(**kw)).to_host()
+    ln = api.codebook_lengths(d.codebook)
+    ref = orc.encode(u, lengths=ln, chunk_bytes=kw.get("chunk_bytes", 16), seg_lanes=64,
+                     align_elems=kw.get("align_elems", 0))
+    assert d.total_bits == ref.total_bits
+    assert np.array_equal(d.stream_bytes_msb_first(), ref.E)
+    assert np.array_equal(d.sm[:d.n], ref.sm)
+    assert d.n_segments == ref.n_segments
+    assert np.array_equal(d.gaps, ref.gaps)
+    assert np.array_equal(d.counts, ref.counts)
+    assert np.array_equal(d.seg_elem, ref.seg_elem)
+    assert np.array_equal(d.seg_nbits[:-1], ref.seg_nbits)
+    # and the code itself is optimal for the tensor's histogram (oracle cost)
+    hist = orc.histogram(u)
+    cost = lambda lens: int(sum(int(h) * int(l) for h, l in zip(hist, lens)))
+    assert cost(ln) == cost(orc.code_lengths(hist, 32))

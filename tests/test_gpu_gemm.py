@@ -7,7 +7,7 @@ tile of 32 rows up to 32, two above), which has no w_debug output: its
 decode is checked bit-exactly through y with x = rows of the identity.
 Above 40 rows (and for w_debug calls above 32) the wide kernel merges each
 tile once into a BF16 plane in LDS, one row block per unit up to 112 rows
-and two above (DF11_GEMM_RB forces either); up to 32 rows w_debug calls
+and two above (tuning.row_blocks forces either); up to 32 rows w_debug calls
 take the tile-synchronous kernel.  Every case checks y of the call without w_debug
 (the product path) as well as of the call with it."""
 import ctypes
@@ -16,7 +16,7 @@ import sys
 import numpy as np
 import pytest
 
-from huffman_decode_df11_amd import api, synth
+from huffman_decode_df11_amd import _lib, api, synth
 from oracle import oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +37,7 @@ def _x_to_gpu(X):
     return torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def _run(W, X, with_debug=True):
+def _run(W, X, with_debug=True, tuning=None):
     """y of the product call (no w_debug); with_debug: also the decoded
     weights and y of a second call that writes them.  Returns (y, wd, y_dbg)."""
     N, K = W.shape
@@ -46,12 +46,12 @@ def _run(W, X, with_debug=True):
     dt = enc.to("cuda")
     x = _x_to_gpu(X)
     y = torch.full((X.shape[0], N), float("nan"), dtype=torch.float32, device="cuda")
-    api.decode_gemm(dt, x, out=y)
+    api.decode_gemm(dt, x, out=y, tuning=tuning)
     wd = y_dbg = None
     if with_debug:
         wdbg = torch.full((N, K), 0x5555, dtype=torch.int16, device="cuda")
         yd = torch.full((X.shape[0], N), float("nan"), dtype=torch.float32, device="cuda")
-        api.decode_gemm(dt, x, out=yd, w_debug=wdbg.view(torch.bfloat16))
+        api.decode_gemm(dt, x, out=yd, w_debug=wdbg.view(torch.bfloat16), tuning=tuning)
         torch.cuda.synchronize()
         wd = wdbg.cpu().numpy().view(np.uint16)
         y_dbg = yd.cpu().numpy()
@@ -127,19 +127,19 @@ def test_k_split_shapes(N, K, B):
     assert _rel(yd, orc.gemm_f64(X, W)) < TOL
 
 
-@pytest.mark.parametrize("rb", ["1", "2"])
+@pytest.mark.parametrize("rb", [1, 2])
 @pytest.mark.parametrize("B", [64, 100, 256])
-def test_wide_kernel_row_block_modes(B, rb, monkeypatch):
+def test_wide_kernel_row_block_modes(B, rb):
     """The wide kernel with one and with two row blocks per unit, each
-    forced (DF11_GEMM_RB) on a weight of three row blocks (so the last pair
-    has one) and a weight split along K: decoded weights bit-exact, y
+    forced (tuning.row_blocks) on a weight of three row blocks (so the last
+    pair has one) and a weight split along K: decoded weights bit-exact, y
     within tolerance."""
-    monkeypatch.setenv("DF11_GEMM_RB", rb)
+    tune = api.gemm_tuning(kernel=_lib.DF11_GEMM_WIDE, row_blocks=rb)
     for N, K, seed in ((96, 1536, 41), (64, 4096, 42)):
         _say("case gemm wide rb=%s B=%d N=%d K=%d" % (rb, B, N, K))
         W = synth.normal_bf16(N * K, 0.02, seed=seed).reshape(N, K)
         X = synth.activations_bf16(B, K, seed=seed + 1)
-        y, wd, yd = _run(W, X)
+        y, wd, yd = _run(W, X, tuning=tune)
         assert np.array_equal(wd, W), "decoded weights differ"
         ref = orc.gemm_f64(X, W)
         assert _rel(y, ref) < TOL and _rel(yd, ref) < TOL
@@ -349,3 +349,108 @@ def test_graph_replays_match_eager():
         assert torch.allclose(y, ref32, rtol=1e-5, atol=1e-6), i
         assert torch.equal(y16.view(torch.int16), ref16.view(torch.int16)), i
         del junk
+
+
+def _identity_recover_on_gpu(dt, N, K, rows, tuning=None):
+    """W [N, K] as float32 through y alone, on the GPU: x = `rows` rows of
+    the identity placed at columns k0 .. k0 + rows - 1, for every k0, gives
+    y[b, n] = W[n, k0 + b] exactly (one nonzero product per output)."""
+    got = torch.empty((K, N), dtype=torch.float32, device="cuda")
+    for k0 in range(0, K, rows):
+        b = min(rows, K - k0)
+        X = torch.zeros((b, K), dtype=torch.int16, device="cuda")
+        X[torch.arange(b), k0 + torch.arange(b)] = 0x3F80
+        got[k0:k0 + b] = api.decode_gemm(dt, X.view(torch.bfloat16), tuning=tuning)
+    torch.cuda.synchronize()
+    return got.T
+
+
+@pytest.mark.parametrize("rows", [32, 40])
+def test_identity_x_recovers_up_proj_on_product_path(rows):
+    """Wup 14336 x 4096 through the call the product path makes at up to 40
+    rows of x (no tuning: the segment-parallel kernel; its 448 row blocks
+    fill the device's workgroup slots once, so each row block is one run and
+    every wave walks about five segments, its accumulator carried from one
+    to the next).  x = 32 identity rows per call (one batch tile), or 40
+    (two batch tiles; the last call 16 rows, one tile): every one of the
+    58,720,256 weights comes back through y and is compared bit for bit."""
+    N, K = 14336, 4096
+    _say("case gemm identity up_proj product path rows=%d" % rows)
+    W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
+    assert ((W & 0x7FFF) != 0).all()    # no zeros: 1 * w + 0 keeps every bit
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    got = _identity_recover_on_gpu(dt, N, K, rows)
+    want = (torch.from_numpy(W.view(np.int16)).cuda().to(torch.int32) << 16)
+    bad = int((got.contiguous().view(torch.int32) != want).sum())
+    assert bad == 0, "%d of %d weights differ" % (bad, N * K)
+
+
+@pytest.mark.parametrize("B", [1, 33])
+@pytest.mark.parametrize("kind", ["zero", "sparse95"])
+def test_sparse_weights_take_a_kernel_whose_staging_fits(kind, B):
+    """An all-zero weight (one exponent, 1-bit codes: 8,192 per segment) and
+    a 95%-zero one (~7,300 per segment) make segments too large for the
+    segment-parallel kernel's staging, whose LDS byte addresses must stay
+    below 64 KB.  The call takes another kernel: decoded weights bit-exact,
+    y equal to the oracle's (exactly zero for the all-zero weight)."""
+    N, K = 64, 4096
+    _say("case gemm sparse %s B=%d" % (kind, B))
+    if kind == "zero":
+        W = np.zeros((N, K), np.uint16)
+    else:
+        rng = np.random.default_rng(77)
+        W = synth.normal_bf16(N * K, 0.02, seed=78).reshape(N, K)
+        W[rng.random((N, K)) < 0.95] = 0
+    enc = api.encode(W, layout=api.gemm_layout(N, K))
+    assert enc.view.max_seg_elems > 7000
+    X = synth.activations_bf16(B, K, seed=79)
+    y, wd, yd = _run(W, X)
+    assert np.array_equal(wd, W)
+    ref = orc.gemm_f64(X, W)
+    for got in (y, yd):
+        if kind == "zero":
+            assert (got == 0).all()
+        else:
+            assert _rel(got, ref) < TOL
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.decode_gemm(enc.to("cuda"), _x_to_gpu(X), tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_SEGMENT))
+    assert ei.value.status == -7
+
+
+@pytest.mark.parametrize("kernel", ["auto", "tiled"])
+def test_nonfinite_x_row(kernel):
+    """A row of x holding +Inf: the other rows of y are as the oracle's
+    product; that row of y is non-finite everywhere, as the oracle's is
+    (+-Inf there: no weight in the Inf's column is zero), where the
+    segment-parallel kernel may give NaN in place of +-Inf (it also
+    multiplies neighbouring segments' weights, masked to +0, by that x)."""
+    N, K, B = 96, 1536, 8
+    _say("case gemm nonfinite x %s" % kernel)
+    W = synth.normal_bf16(N * K, 0.02, seed=80).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=81)
+    X[2, 700] = 0x7F80
+    ref = orc.gemm_f64(X, W)
+    assert np.isinf(ref[2]).all() and np.isfinite(np.delete(ref, 2, axis=0)).all()
+    tune = None if kernel == "auto" else api.gemm_tuning(kernel=_lib.DF11_GEMM_TILED)
+    y, _, _ = _run(W, X, with_debug=False, tuning=tune)
+    assert not np.isfinite(y[2]).any()
+    assert _rel(np.delete(y, 2, axis=0), np.delete(ref, 2, axis=0)) < TOL
+    if kernel == "tiled":   # no masked neighbours: the signs of the plain product
+        assert np.array_equal(y[2], ref[2])
+
+
+@pytest.mark.parametrize("kernel,B,extra", [("segment", 8, dict(parts=2)), ("segment", 40, dict()),
+                                            ("tiled", 8, dict(split=3)), ("wide", 64, dict(split=2)),
+                                            ("wide", 100, dict(row_blocks=2))])
+def test_explicit_kernel_choices_agree(kernel, B, extra):
+    """Every explicit kernel choice (tuning) gives the oracle's product."""
+    N, K = 256, 4096
+    _say("case gemm tuning %s B=%d %s" % (kernel, B, extra))
+    W = synth.normal_bf16(N * K, 0.02, seed=82).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=83)
+    code = {"segment": _lib.DF11_GEMM_SEGMENT, "tiled": _lib.DF11_GEMM_TILED, "wide": _lib.DF11_GEMM_WIDE}[kernel]
+    y, wd, yd = _run(W, X, with_debug=kernel != "segment", tuning=api.gemm_tuning(kernel=code, **extra))
+    ref = orc.gemm_f64(X, W)
+    assert _rel(y, ref) < TOL
+    if wd is not None:
+        assert np.array_equal(wd, W) and _rel(yd, ref) < TOL

@@ -28,15 +28,16 @@ def _i16(u):
     return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).cuda()
 
 
+@pytest.mark.parametrize("chunk", [16, 8])
 @pytest.mark.parametrize("rows,cols", [(1000, 4096), (333, 24), (64, 40000), (4096, 4096)])
-def test_decode_rows_matches_input(rows, cols):
+def test_decode_rows_matches_input(rows, cols, chunk):
     """Random ids with repeats, the first and last rows; rows spanning one,
     several and a fraction of a segment (one, two and four waves per row),
     and a table of ~5300 segments (three steps of the 64-way segment
-    search)."""
-    _say("case decode_rows %dx%d" % (rows, cols))
+    search); 16- and 8-byte chunks."""
+    _say("case decode_rows %dx%d chunk %d" % (rows, cols, chunk))
     W = synth.normal_bf16(rows * cols, 0.02, seed=30).reshape(rows, cols)
-    dt = api.encode(W, layout=api.make_layout(rows=rows, cols=cols)).to("cuda")
+    dt = api.encode(W, layout=api.make_layout(rows=rows, cols=cols, chunk_bytes=chunk)).to("cuda")
     ids = np.concatenate([[0, rows - 1, rows - 1], np.random.default_rng(31).integers(0, rows, 200)])
     out = api.decode_rows(dt, torch.from_numpy(ids).cuda())
     torch.cuda.synchronize()

@@ -31,12 +31,13 @@ def _bits(t):
 
 @SETTINGS
 @given(kind=st.sampled_from(["normal", "specials", "few", "one", "uniform"]),
-       n=st.integers(1, 200000), seed=st.integers(0, 2 ** 31 - 1), align=st.sampled_from([0, 512, 16384]))
-def test_decode_random_tensors(kind, n, seed, align):
-    print("case decode", kind, n, seed, align, flush=True)
+       n=st.integers(1, 200000), seed=st.integers(0, 2 ** 31 - 1), align=st.sampled_from([0, 512, 16384]),
+       chunk=st.sampled_from([16, 8]))
+def test_decode_random_tensors(kind, n, seed, align, chunk):
+    print("case decode", kind, n, seed, align, chunk, flush=True)
     sys.stdout.flush()
     u = _values(kind, n, seed)
-    dt = api.encode(u, layout=api.make_layout(align_elems=align)).to("cuda")
+    dt = api.encode(u, layout=api.make_layout(align_elems=align, chunk_bytes=chunk)).to("cuda")
     out = torch.full((n + 8,), 0x5555, dtype=torch.int16, device="cuda")
     api.decode(dt, out=out.view(torch.bfloat16))
     torch.cuda.synchronize()
@@ -47,13 +48,14 @@ def test_decode_random_tensors(kind, n, seed, align):
 
 @SETTINGS
 @given(kind=st.sampled_from(["normal", "specials", "few", "uniform"]),
-       rows=st.integers(1, 300), cols8=st.integers(1, 1200), seed=st.integers(0, 2 ** 31 - 1))
-def test_decode_rows_random_shapes(kind, rows, cols8, seed):
+       rows=st.integers(1, 300), cols8=st.integers(1, 1200), seed=st.integers(0, 2 ** 31 - 1),
+       chunk=st.sampled_from([16, 8]))
+def test_decode_rows_random_shapes(kind, rows, cols8, seed, chunk):
     cols = 8 * cols8
-    print("case rows", kind, rows, cols, seed, flush=True)
+    print("case rows", kind, rows, cols, seed, chunk, flush=True)
     sys.stdout.flush()
     u = _values(kind, rows * cols, seed).reshape(rows, cols)
-    dt = api.encode(u, layout=api.make_layout(rows=rows, cols=cols)).to("cuda")
+    dt = api.encode(u, layout=api.make_layout(rows=rows, cols=cols, chunk_bytes=chunk)).to("cuda")
     ids = np.random.default_rng(seed).integers(0, rows, 50)
     ids[0], ids[-1] = 0, rows - 1
     out = api.decode_rows(dt, torch.from_numpy(ids).cuda())

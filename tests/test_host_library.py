@@ -125,8 +125,8 @@ def test_lookup_tables_against_oracle_codes(name):
 LAYOUTS = {
     "default": dict(),
     "chunk8": dict(chunk_bytes=8),
-    "chunk32": dict(chunk_bytes=32),
     "aligned": dict(align_elems=4096),
+    "chunk8_aligned": dict(chunk_bytes=8, align_elems=2048),
 }
 
 
@@ -226,7 +226,8 @@ def test_max_len_too_small_rejected():
     assert ei.value.status == -3
 
 
-@pytest.mark.parametrize("kw", [dict(chunk_bytes=6), dict(chunk_bytes=64), dict(align_elems=10),
+@pytest.mark.parametrize("kw", [dict(chunk_bytes=6), dict(chunk_bytes=64), dict(chunk_bytes=4), dict(chunk_bytes=12),
+                                dict(chunk_bytes=32), dict(align_elems=10),
                                 dict(rows=3, cols=5), dict(rows=100, cols=100, tile_rows=3, tile_cols=16),
                                 dict(tile_kchunk=8),
                                 dict(rows=64, cols=160, tile_rows=32, tile_cols=32, tile_kchunk=12),

@@ -46,7 +46,7 @@ def _values(kind: str, n: int, seed: int) -> np.ndarray:
 @given(kind=st.sampled_from(["normal", "specials", "few", "one", "uniform"]),
        n=st.integers(1, 3000),
        seed=st.integers(0, 2 ** 31 - 1),
-       chunk_bytes=st.sampled_from([8, 16, 32]),
+       chunk_bytes=st.sampled_from([8, 16]),
        align=st.sampled_from([0, 0, 512, 4096]),
        lmax_slack=st.integers(0, 24))
 def test_encoder_matches_oracle_on_random_tensors(kind, n, seed, chunk_bytes, align, lmax_slack):
