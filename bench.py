@@ -1,26 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the DF11 decode hot path on one MI355X.
 
-Default workload: one Llama-3-8B-shaped decoder layer of synthetic
-N(0, 0.02) BF16 weights (q, k, v, o, gate, up, down: 218,103,808 elements)
-with one codebook for the layer, compressed and resident in HBM.  One step
-decodes all seven matrices in one launch (df11_decode_batch), each into its
-slice of one reused layer-sized BF16 buffer.
+The step: one pass over an 8B-parameter model of synthetic N(0, 0.02) BF16
+weights shaped like Llama-3-8B (embedding 128256 x 4096, 32 decoder layers
+of q, k, v, o, gate, up, down, LM head: 8,029,995,008 elements in 226
+matrices), compressed with one codebook per layer and resident in HBM.  A
+pass decodes each layer (and the embedding, and the head) in one
+df11_decode_batch launch into one reused buffer: 34 launches.  Every
+element is checked against its generator through those launches before
+timing.
 
-Also reported: the seven matrices one launch each into one reused
-matrix-sized buffer (eager, and replayed as one HIP graph), the whole
-8B-parameter model (226 matrices) per pass, compressed CPU offload, the GPU
-encoder, and the fused decode+GEMM on up_proj at B in {1, 8, 64, 256}.
+Also reported: the same pass as 226 per-matrix launches (eager and as one
+HIP graph), one decoder layer on its own, the 1024 x 1024 tensor and the
+16M adversarial mix, compressed CPU offload, the GPU encoder, the embedding
+row gather, the fused decode+GEMM on up_proj at B in {1, 8, 64, 256}, and
+one GPU's share of an 8-way row split.
 
 Prints one JSON line:
-  value     decoded BF16 GB/s (2 bytes per element / step time)
+  value     decoded BF16 GB/s (2 bytes per element / pass time)
   roofline  the decode kernel's algorithmic HBM bytes per launch / its
-            average launch time (HIP events on the launch stream; one launch
-            per step), against the 8 TB/s HBM peak
-  cpu_baseline  the CPU oracle's bit-serial decode of the same layer, timed
-            on this host's allowed cores (one thread each; also on one core)
+            average launch duration (HIP events around every launch on the
+            launch stream), against the 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle's bit-serial decode on this host's allowed
+            cores over a bounded sample of the model (one layer and 8,192
+            embedding rows), extrapolated to the pass; cpu_baseline_legs
+            holds the other oracle timings (one core)
 
-    python bench.py [--steps K] [--warmup W] [--no-model] [--no-fused] [--no-shard] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--headline-only] [--no-extras] [--no-fused] [--no-shard]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -193,19 +200,91 @@ def time_graph(dts, outbuf, steps: int, warmup: int):
     return a.elapsed_time(b) / steps
 
 
-def model_pass(steps: int, warmup: int, seed: int = 0):
-    """The 8B-parameter model (32 layers, embedding, LM head; 226 matrices,
-    8,029,995,008 elements, one codebook per layer): every matrix decoded
-    into one reused buffer, as eager launches, as one HIP graph, and as one
-    batched launch per layer."""
+def model_headline(steps: int, warmup: int, seed: int = 0):
+    """The step: one pass over the 8B-parameter model (embedding, 32 decoder
+    layers, LM head: 226 matrices, 8,029,995,008 elements, one codebook per
+    layer, compressed and resident in HBM), each group of matrices (a layer,
+    the embedding, the head) decoded in one df11_decode_batch launch into one
+    reused group-sized buffer, 34 launches per pass.  Every element of every
+    matrix is checked against its generator through those launches first.
+
+    Timed twice, each time `steps` passes back to back behind a short spin
+    kernel on the launch stream: between two events (ms per pass, the
+    step), and again with an event pair around every launch (the decode
+    kernel's own duration per launch; the pairs add a few microseconds of
+    gap between launches, so the step is not taken from this run).
+    Returns (model, record)."""
     import torch
     from huffman_decode_df11_amd import model as mdl
     t0 = time.time()
     m = mdl.synthetic_llama3_8b(seed=seed, device="cuda")
     t_build = time.time() - t0
-    checked = mdl.verify_pass(m, seed)
-    log("8B model built in %.1f s; all %d elements decoded and verified" % (t_build, checked))
-    alg = sum((t.total_bits + 7) // 8 + t.n + t.n_segments * 144 + 16 + 2 * t.n for _, _, t in m.matrices)
+    checked = mdl.verify_pass_batched(m, seed)
+    log("8B model built in %.1f s; all %d elements decoded through the batched launches and verified"
+        % (t_build, checked))
+    alg_launch = [sum(algorithmic_bytes(t) for _, t in mats) for _, mats in m.groups]
+    alg = sum(alg_launch)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        m.decode_pass_batched(stream)
+    torch.cuda.synchronize()
+    ng = len(m.groups)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a, b = ev(), ev()
+    _hold_queue(5.0)
+    a.record(stream)
+    for s in range(steps):
+        for i in range(ng):
+            m.decode_group(i, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_pass = a.elapsed_time(b) / steps
+    evs = [[(ev(), ev()) for _ in range(ng)] for _ in range(steps)]
+    _hold_queue(5.0)
+    for s in range(steps):
+        for i in range(ng):
+            evs[s][i][0].record(stream)
+            m.decode_group(i, stream)
+            evs[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = np.array([[e0.elapsed_time(e1) for e0, e1 in row] for row in evs])
+    kernel_ms = float(launch_ms.sum(axis=1).mean())
+    # the buffers hold the last pass's head: check it again after the timing
+    from huffman_decode_df11_amd import synth
+    spec = synth.llama3_8b_tensors(len(m.groups) - 2)[-1]
+    want = synth.normal_bf16_torch(spec[2], spec[3], seed, len(m.matrices) - 1, "cuda").view(torch.int16)
+    if not torch.equal(m._layer_outs[ng - 1][0].view(torch.int16), want.reshape(-1)):
+        raise SystemExit("model pass parity check after timing failed")
+    n = m.n_elements
+    layer_ms = launch_ms[:, 1:ng - 1].mean()
+    rec = {
+        "elements": n,
+        "matrices": len(m.matrices),
+        "launches_per_step": ng,
+        "compressed_bytes": m.compressed_nbytes(),
+        "bits_per_weight": round(8.0 * m.compressed_nbytes() / n, 4),
+        "exponent_bits_per_weight": round(m.stream_bits() / n, 4),
+        "build_s": round(t_build, 1),
+        "verified_elements": checked,
+        "ms_per_step": ms_pass,
+        "kernel_ms_per_step": kernel_ms,
+        "algorithmic_bytes_per_step": int(alg),
+        "launch_us": {"embedding": round(float(launch_ms[:, 0].mean()) * 1e3, 2),
+                      "decoder_layer_mean": round(float(layer_ms) * 1e3, 2),
+                      "decoder_layer_min": round(float(launch_ms[:, 1:ng - 1].min()) * 1e3, 2),
+                      "decoder_layer_max": round(float(launch_ms[:, 1:ng - 1].max()) * 1e3, 2),
+                      "lm_head": round(float(launch_ms[:, ng - 1].mean()) * 1e3, 2)},
+        "layer_launch_hbm_frac": round(float(np.mean(alg_launch[1:ng - 1])) / (layer_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    return m, rec
+
+
+def model_other_modes(m, steps: int, warmup: int):
+    """The same model pass as 226 eager launches (one per matrix into one
+    reused matrix-sized buffer) and as those launches captured once in a HIP
+    graph and replayed."""
+    import torch
+    alg = sum(algorithmic_bytes(t) for _, _, t in m.matrices)
 
     def timeit(f, n):
         for _ in range(warmup):
@@ -220,28 +299,12 @@ def model_pass(steps: int, warmup: int, seed: int = 0):
         return a.elapsed_time(b) / n
 
     n = max(3, steps // 4)
-    t_eager = timeit(m.decode_pass, n)
-    t_graph = timeit(m.capture(), n)
-    t_batched = timeit(m.decode_pass_batched, n)
-    out = {
-        "workload": "llama3-8b model: embedding, 32 layers, LM head, bf16 N(0,0.02), "
-                    "%d elements in %d matrices, one codebook per layer, one reused buffer" % (
-                        m.n_elements, len(m.matrices)),
-        "elements": m.n_elements,
-        "compressed_bytes": m.compressed_nbytes(),
-        "bf16_bytes": 2 * m.n_elements,
-        "bits_per_weight": round(8.0 * m.compressed_nbytes() / m.n_elements, 4),
-        "build_s": round(t_build, 1),
-        "verified_elements": checked,
-        "passes_timed": n,
-    }
-    for name, t, launches in (("graph", t_graph, len(m.matrices)), ("eager", t_eager, len(m.matrices)),
-                              ("batched_per_layer", t_batched, len(m.groups))):
-        out[name] = {"ms_per_pass": round(t, 3), "launches": launches,
+    out = {"passes_timed": n}
+    for name, f in (("eager", m.decode_pass), ("graph", m.capture())):
+        t = timeit(f, n)
+        out[name] = {"ms_per_pass": round(t, 3), "launches": len(m.matrices),
                      "decoded_gbs": round(2.0 * m.n_elements / (t * 1e-3) / 1e9, 1),
                      "hbm_frac": round(alg / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del m
-    torch.cuda.empty_cache()
     return out
 
 
@@ -565,49 +628,81 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline_layer(mats, one_core_s: float = 12.0, all_cores_s: float = 10.0):
-    """The oracle's serial decode on the host over the layer's matrices:
-    first on one core (the loop pinned to the first CPU this process may
-    use), then on every allowed core, one thread per core, each thread
-    decoding whole matrices in turn (independent tensors; the oracle's C
-    decode runs without the interpreter lock).  Returns (all cores, one
-    core) baseline records."""
-    from concurrent.futures import ThreadPoolExecutor
-    import itertools
-    from oracle import oracle as orc
-    hist = None
-    for m in mats:
-        hist = orc.histogram(m) if hist is None else hist + orc.histogram(m)
-    ln = orc.code_lengths(hist, 32)
-    refs = [orc.encode(m, lengths=ln) for m in mats]
+def _pinned_one_core(f):
+    """Run f() with this process pinned to the first CPU it may use."""
     allowed = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
-    cpu = _cpu_model()
-
-    # one core
     if allowed:
         os.sched_setaffinity(0, {allowed[0]})
-    elems, secs, passes = 0, 0.0, 0
     try:
-        while passes == 0 or secs < one_core_s:
-            for m, ref in zip(mats, refs):
-                t0 = time.perf_counter()
-                out = orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln)
-                secs += time.perf_counter() - t0
-                elems += m.size
-                if passes == 0 and not np.array_equal(out, m.reshape(-1)):
-                    raise SystemExit("oracle round trip failed")
-                del out
-            passes += 1
+        return f()
     finally:
         if allowed:
             os.sched_setaffinity(0, set(allowed))
-    one = {"value": round(2.0 * elems / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": "bit-serial oracle decode of the layer's 7 matrices, %d passes (%d elements, %.1f s), "
-                     "one host thread pinned to CPU %s of %d allowed (%s)" % (
-                         passes, elems, secs, allowed[0] if allowed else "?", len(allowed), cpu)}
 
-    # every allowed core: threads take matrices in turn until the budget is used
+
+def _repeat(f, min_s: float):
+    """Call f() until min_s seconds have passed (at least once); returns
+    (calls, seconds)."""
+    calls, secs = 0, 0.0
+    while calls == 0 or secs < min_s:
+        t0 = time.perf_counter()
+        f()
+        secs += time.perf_counter() - t0
+        calls += 1
+    return calls, secs
+
+
+def cpu_baselines(seed: int = 0, all_cores_s: float = 10.0):
+    """The oracle as written (plain serial C: bit-serial decode, serial
+    encode, scalar float32 GEMM) timed on this host.  Returns (headline,
+    legs).
+
+    Headline: the 8B model pass extrapolated from a bounded sample -- layer
+    0's seven matrices (218,103,808 elements) and the first 8,192 rows of the
+    embedding (33,554,432 elements), generated exactly as the model's -- the
+    oracle decoding whole tensors in turn on every allowed CPU (one thread
+    each; its C decode runs outside the interpreter lock) for about
+    all_cores_s seconds.  Decoded GB/s over that mix = 2 x elements / wall;
+    the pass would take 8,029,995,008 / (elements/s).
+
+    Legs, on one core pinned: the 1024 x 1024 tensor, the 16M adversarial
+    mix, the layer's matrices, the oracle encoder on up_proj, and the scalar
+    GEMM on up_proj at each B (a sample of W's rows, extrapolated by flops)."""
+    import itertools
+    from concurrent.futures import ThreadPoolExecutor
+    import torch
+    from oracle import oracle as orc
+    from huffman_decode_df11_amd import synth
+    cpu = _cpu_model()
+    allowed = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else [0]
     threads = max(1, len(allowed))
+    specs = synth.llama3_8b_tensors()
+    t_setup = time.perf_counter()
+
+    def host(idx, rows=None):
+        g, name, r, c = specs[idx]
+        t = synth.normal_bf16_torch(r, c, seed, idx, "cuda")
+        if rows is not None:
+            t = t[:rows]
+        return name, t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+
+    layer = [host(i) for i in range(1, 8)]
+    emb = host(0, rows=8192)
+    torch.cuda.empty_cache()
+    hist = None
+    for _, u in layer:
+        hist = orc.histogram(u) if hist is None else hist + orc.histogram(u)
+    ln_layer = orc.code_lengths(hist, 32)
+    ln_emb = orc.code_lengths(orc.histogram(emb[1]), 32)
+    jobs = [(name, u, ln_layer) for name, u in layer] + [("embed_tokens[:8192]", emb[1], ln_emb)]
+    with ThreadPoolExecutor(max_workers=min(threads, len(jobs))) as ex:
+        refs = list(ex.map(lambda j: orc.encode(j[1], lengths=j[2]), jobs))
+    for (name, u, ln), ref in zip(jobs, refs):
+        if not np.array_equal(orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln), u):
+            raise SystemExit("oracle round trip failed on " + name)
+    t_setup = time.perf_counter() - t_setup
+
+    # headline: every allowed core, whole tensors in turn until the budget is used
     order = itertools.count()
     t_start = time.perf_counter()
     deadline = t_start + all_cores_s
@@ -618,16 +713,59 @@ def cpu_baseline_layer(mats, one_core_s: float = 12.0, all_cores_s: float = 10.0
             i = next(order)
             if i >= threads and time.perf_counter() >= deadline:
                 return done
-            ref = refs[i % len(refs)]
+            (name, u, ln), ref = jobs[i % len(jobs)], refs[i % len(jobs)]
             orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln)
             done += ref.n
     with ThreadPoolExecutor(max_workers=threads) as ex:
         total = sum(ex.map(worker, range(threads)))
     wall = time.perf_counter() - t_start
-    allc = {"value": round(2.0 * total / wall / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "bit-serial oracle decode of the layer's 7 matrices (whole matrices, in turn) on %d host "
-                      "threads, one per allowed CPU, %.1f s wall, %d elements (%s)" % (threads, wall, total, cpu)}
-    return allc, one
+    model_n = sum(r * c for _, _, r, c in specs)
+    rate = total / wall
+    headline = {"value": round(2.0 * rate / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": "bit-serial oracle decode, whole tensors in turn on %d host threads (one per allowed CPU, "
+                          "%s) for %.1f s wall, %d elements: layer 0's 7 matrices and embedding rows 0..8191 of the "
+                          "8B model (same generator); the model pass (%d elements) extrapolates to %.1f s"
+                          % (threads, cpu, wall, total, model_n, model_n / rate)}
+
+    legs = {"host_cpu": cpu, "allowed_cpus": threads, "setup_s": round(t_setup, 1)}
+
+    def one_core_decode(u, ln, ref, min_s):
+        calls, secs = _pinned_one_core(lambda: _repeat(lambda: orc.decode(ref.E, ref.total_bits, ref.sm, ref.n, ln),
+                                                          min_s))
+        return {"value": round(2.0 * ref.n * calls / secs / 1e9, 4), "unit": "GB/s decoded", "cores": 1,
+                "elements": int(ref.n), "calls": calls, "seconds": round(secs, 2)}
+
+    u0 = synth.tensor_1024(seed=seed).reshape(-1)
+    ln0 = orc.code_lengths(orc.histogram(u0), 32)
+    legs["decode_1024x1024"] = one_core_decode(u0, ln0, orc.encode(u0, lengths=ln0), 1.0)
+    u2 = synth.adversarial_bf16(1 << 24, seed=seed)
+    ln2 = orc.code_lengths(orc.histogram(u2), 32)
+    legs["decode_adversarial_16m"] = one_core_decode(u2, ln2, orc.encode(u2, lengths=ln2), 1.5)
+    calls, secs = _pinned_one_core(lambda: _repeat(
+        lambda: [orc.decode(r.E, r.total_bits, r.sm, r.n, j[2]) for j, r in zip(jobs[:7], refs[:7])], 2.0))
+    n_layer = sum(r.n for r in refs[:7])
+    legs["decode_llama3_8b_layer"] = {"value": round(2.0 * n_layer * calls / secs / 1e9, 4), "unit": "GB/s decoded",
+                                      "cores": 1, "elements": n_layer, "passes": calls, "seconds": round(secs, 2)}
+    legs["decode_model_pass_one_core_extrapolated_s"] = round(model_n * secs / (n_layer * calls), 1)
+    up = dict(layer)["up_proj"]
+    t0 = time.perf_counter()
+    _pinned_one_core(lambda: orc.encode(up, lengths=ln_layer))
+    te = time.perf_counter() - t0
+    legs["encode_up_proj"] = {"value": round(2.0 * up.size / te / 1e9, 4), "unit": "GB/s of BF16 input", "cores": 1,
+                              "elements": int(up.size), "seconds": round(te, 2)}
+    W = up.reshape(14336, 4096)
+    X = synth.activations_bf16(256, 4096, seed=1)
+    gemm = {}
+    for B in (1, 8, 64, 256):
+        rows = int(min(14336, max(16, (1e9 / (2 * B * 4096)) // 16 * 16)))
+        t0 = time.perf_counter()
+        _pinned_one_core(lambda: orc.gemm_f32(X[:B], W[:rows]))
+        tg = time.perf_counter() - t0
+        flops = 2.0 * B * rows * 4096
+        gemm[str(B)] = {"tflops": round(flops / tg / 1e12, 6), "rows_sampled": rows,
+                        "seconds": round(tg, 3), "full_up_proj_s_extrapolated": round(tg * 14336 / rows, 2)}
+    legs["gemm_up_proj_scalar_f32"] = {"unit": "TFLOP/s", "cores": 1, "by_batch": gemm}
+    return headline, legs
 
 
 def main():
@@ -635,118 +773,94 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="layer", choices=["layer"])
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the model pass (build, verify, warm-up, timed passes): the profiled command")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-shard", action="store_true")
-    ap.add_argument("--no-model", action="store_true", help="skip the 8B-parameter model pass")
+    ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the decode path has no cross-GPU step; "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the decode path has no cross-GPU step (the row-split shard of one "
+              "GPU is reported as shard_8way); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
-    from huffman_decode_df11_amd import api
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
 
-    encs = build_layer(args.seed)
-    mats = [m for _, m, _ in encs]
-    dts = [e.to("cuda") for _, _, e in encs]
-    n_total = sum(e.n for _, _, e in encs)
-    biggest = max(e.n for _, _, e in encs)
-    outbuf = torch.empty(biggest, dtype=torch.bfloat16, device="cuda")
-    verify(dts, mats, outbuf)
-    log("parity verified on all %d matrices" % len(dts))
-
-    alg = [algorithmic_bytes(e) for _, _, e in encs]
-    compressed = sum(e.compressed_nbytes() for _, _, e in encs)
-    stream_bits = sum(e.total_bits for _, _, e in encs)
-
-    # the step: the layer's seven matrices in one launch, each into its own
-    # slice of one reused layer-sized buffer
-    ms_per_step, outs = time_batched(dts, args.steps, args.warmup)
-    for o, m in zip(outs, mats):
-        if not np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), m.reshape(-1)):
-            raise SystemExit("batched parity check failed")
-    del outs
-    achieved = sum(alg) / (ms_per_step * 1e-3) / 1e9
-
+    m, rec = model_headline(args.steps, args.warmup, args.seed)
+    n = rec["elements"]
+    ms = rec["ms_per_step"]
+    kernel_ms = rec["kernel_ms_per_step"]
+    alg = rec["algorithmic_bytes_per_step"]
+    ng = rec["launches_per_step"]
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
     result = {
-        "metric": "decoded BF16 GB/s (df11_decode, Llama-3-8B layer)",
-        "value": round(2.0 * n_total / (ms_per_step * 1e-3) / 1e9, 2),
+        "metric": "decoded BF16 GB/s (df11_decode_batch, 8B-parameter model pass)",
+        "value": round(2.0 * n / (ms * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u32",
         "data": "synthetic",
         "config": {
-            "workload": "llama3-8b-layer: q,k,v,o,gate,up,down bf16 N(0,0.02), 218,103,808 elements, "
-                        "one codebook, the seven matrices decoded in one launch (df11_decode_batch), each "
-                        "into its slice of one reused layer-sized buffer",
-            "elements": n_total,
-            "launches_per_step": 1,
-            "bits_per_weight": round(8.0 * compressed / n_total, 4),
-            "exponent_bits_per_weight": round(stream_bits / n_total, 4),
+            "workload": "llama3-8b-sized model pass: embedding 128256x4096, 32 decoder layers (q,k,v,o,gate,up,down), "
+                        "LM head; bf16 N(0,0.02), %d elements in %d matrices, one codebook per layer; each layer "
+                        "(and the embedding, the head) decoded in one launch into one reused buffer" % (n, rec["matrices"]),
+            "elements": n,
+            "launches_per_step": ng,
+            "bits_per_weight": rec["bits_per_weight"],
+            "exponent_bits_per_weight": rec["exponent_bits_per_weight"],
             "parallelism": "1 GPU",
         },
-        "elements_per_s": round(n_total / (ms_per_step * 1e-3), 1),
+        "elements_per_s": round(n / (ms * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("decode_kernel_llama3_8b_layer.md", DECODE_SOURCES),
+            "traffic": measured_traffic("decode_kernel_llama3_8b_model_pass.md", DECODE_SOURCES),
             "kernel": "decode_kernel",
-            "algorithmic_bytes_per_launch": int(sum(alg)),
-            "algorithmic_bytes_per_element": round(sum(alg) / n_total, 4),
-            "timing": "events around the timed back-to-back launches on the launch stream, enqueued "
-                      "behind a short spin kernel; one launch per step, so the average launch duration "
-                      "is the step time",
+            "launches_per_step": ng,
+            "avg_launch_us": round(kernel_ms / ng * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(alg / ng),
+            "algorithmic_bytes_per_element": round(alg / n, 4),
+            "timing": "HIP events around every decode launch on the launch stream over `steps` timed passes "
+                      "(queued behind a short spin kernel); achieved = algorithmic bytes per launch / average "
+                      "launch duration; ms_per_step from `steps` passes without the per-launch events",
         },
+        "model_pass": {k: rec[k] for k in ("verified_elements", "build_s", "compressed_bytes", "launch_us",
+                                           "layer_launch_hbm_frac")},
     }
-    copy_gbs = copy_peak()
-    result["roofline"]["copy_peak_gbs"] = round(copy_gbs, 1)
-    result["roofline"]["frac_of_copy_peak"] = round(achieved / copy_gbs, 4)
-    # the same matrices one launch each into one matrix-sized reused buffer
-    launch_ms, eager_ms = time_decode(dts, outbuf, args.steps, args.warmup)
-    graph_ms = time_graph(dts, outbuf, args.steps, args.warmup)
-    # after the replays the buffer holds the last matrix of the layer
-    last = outbuf.view(torch.int16)[:mats[-1].size].cpu().numpy().view(np.uint16)
-    if not np.array_equal(last, mats[-1].reshape(-1)):
-        raise SystemExit("graph replay parity check failed")
-    result["per_matrix_layer"] = {
-        "buffer": "one reused buffer of the largest matrix",
-        "graph": {"launches_per_step": len(dts), "ms_per_step": round(graph_ms, 4),
-                  "decoded_gbs": round(2.0 * n_total / (graph_ms * 1e-3) / 1e9, 2),
-                  "hbm_frac": round(sum(alg) / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "eager": {"launches_per_step": len(dts), "ms_per_step": round(eager_ms, 4),
-                  "decoded_gbs": round(2.0 * n_total / (eager_ms * 1e-3) / 1e9, 2)},
-        "repeated_launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
-        "repeated_launch_note": "each matrix decoded again and again into the same buffer; its 100-200 MB "
-                                "of traffic partly stays in the 256 MB Infinity Cache, so these are warm-cache "
-                                "kernel times",
-    }
-    if not args.no_model:
-        result["model_pass"] = model_pass(args.steps, args.warmup, args.seed)
+    result["model_pass"]["kernel_ms_per_pass"] = round(kernel_ms, 4)
+    headline_only = args.headline_only
+    if not headline_only:
+        copy_gbs = copy_peak()
+        result["roofline"]["copy_peak_gbs"] = round(copy_gbs, 1)
+        result["roofline"]["frac_of_copy_peak"] = round(achieved / copy_gbs, 4)
+        if not args.no_extras:
+            result["model_pass"].update(model_other_modes(m, args.steps, args.warmup))
+    del m
+    torch.cuda.empty_cache()
+    if not headline_only and not args.no_extras:
+        result["llama3_8b_layer"] = layer_workload(args.steps, args.warmup, args.seed)
         result["offload_pass"] = offload_pass(args.steps, args.warmup, args.seed)
         result["encode"] = encode_rate(args.seed)
-    if not args.no_fused:
-        result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
-    if not args.no_model:
         result["other_configs"] = other_configs(args.steps, args.warmup, args.seed)
         result["embedding_lookup"] = embedding_lookup(args.steps, args.warmup, args.seed)
-    if not args.no_shard:
+    if not headline_only and not args.no_fused:
+        result["fused_up_proj"] = fused_up_proj(args.steps, args.warmup, args.seed)
+    if not headline_only and not args.no_shard and not args.no_extras:
         # what one GPU does under an 8-way row split of each matrix (no collective)
         result["shard_8way"] = {
             "layer_decode": shard_layer_decode(args.steps, args.warmup, ways=8, seed=args.seed),
@@ -759,9 +873,46 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 256 << 20
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"], result["cpu_baseline_one_core"] = cpu_baseline_layer(mats)
+    if not headline_only and not args.no_cpu_baseline:
+        result["cpu_baseline"], result["cpu_baseline_legs"] = cpu_baselines(args.seed)
     print(json.dumps(result), flush=True)
+
+
+def layer_workload(steps: int, warmup: int, seed: int = 0):
+    """One Llama-3-8B-shaped decoder layer (218,103,808 elements, one
+    codebook): the seven matrices in one batched launch into a layer-sized
+    buffer, and one launch each into one reused matrix-sized buffer (eager,
+    and as one HIP graph).  Parity checked in full first."""
+    import torch
+    encs = build_layer(seed)
+    mats = [m for _, m, _ in encs]
+    dts = [e.to("cuda") for _, _, e in encs]
+    n_total = sum(e.n for _, _, e in encs)
+    outbuf = torch.empty(max(e.n for _, _, e in encs), dtype=torch.bfloat16, device="cuda")
+    verify(dts, mats, outbuf)
+    alg = [algorithmic_bytes(e) for _, _, e in encs]
+    ms, outs = time_batched(dts, steps, warmup)
+    for o, m in zip(outs, mats):
+        if not np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), m.reshape(-1)):
+            raise SystemExit("batched parity check failed")
+    del outs
+    launch_ms, eager_ms = time_decode(dts, outbuf, steps, warmup)
+    graph_ms = time_graph(dts, outbuf, steps, warmup)
+    last = outbuf.view(torch.int16)[:mats[-1].size].cpu().numpy().view(np.uint16)
+    if not np.array_equal(last, mats[-1].reshape(-1)):
+        raise SystemExit("graph replay parity check failed")
+    per = lambda t: {"ms_per_step": round(t, 4), "decoded_gbs": round(2.0 * n_total / (t * 1e-3) / 1e9, 2),
+                     "hbm_frac": round(sum(alg) / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return {
+        "workload": "llama3-8b layer: q,k,v,o,gate,up,down bf16 N(0,0.02), %d elements, one codebook" % n_total,
+        "batched_one_launch": per(ms),
+        "per_matrix_graph": dict(per(graph_ms), launches_per_step=len(dts)),
+        "per_matrix_eager": dict(per(eager_ms), launches_per_step=len(dts)),
+        "repeated_launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
+        "repeated_launch_note": "each matrix decoded again and again into the same buffer; its 100-200 MB "
+                                "of traffic partly stays in the 256 MB Infinity Cache, so these are warm-cache "
+                                "kernel times",
+    }
 
 
 if __name__ == "__main__":

@@ -199,3 +199,27 @@ def verify_pass(model: CompressedModel, seed: int, stream=None) -> int:
             raise RuntimeError("model pass: %s %s differs at element %d" % (g, name, bad))
         checked += t.n
     return checked
+
+
+def verify_pass_batched(model: CompressedModel, seed: int, stream=None) -> int:
+    """Decode every group in one launch each (decode_group, the launches of
+    decode_pass_batched) and compare every output, on the device, with the
+    same matrix generated again from its seed.  Returns the number of
+    elements checked; raises on the first mismatch."""
+    import torch
+    specs = synth.llama3_8b_tensors(len(model.groups) - 2)
+    assert len(specs) == len(model.matrices)
+    checked, idx = 0, 0
+    for i, (g, mats) in enumerate(model.groups):
+        outs = model.decode_group(i, stream)
+        for (name, t), out in zip(mats, outs):
+            sg, sname, r, c = specs[idx]
+            assert (sg, sname) == (g, name)
+            want = synth.normal_bf16_torch(r, c, seed, idx, model.device).view(torch.int16).reshape(-1)
+            got = out.view(torch.int16)
+            if not torch.equal(got, want):
+                bad = int((got != want).nonzero()[0])
+                raise RuntimeError("model pass: %s %s differs at element %d" % (g, name, bad))
+            checked += t.n
+            idx += 1
+    return checked
