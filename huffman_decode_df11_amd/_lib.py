@@ -66,7 +66,7 @@ class View(ctypes.Structure):
 
 
 class DecodeTuning(ctypes.Structure):
-    _fields_ = [("waves", u32), ("stores", u32), ("reserved", u32 * 6)]
+    _fields_ = [("waves", u32), ("stores", u32), ("groups", u32), ("reserved", u32 * 5)]
 
 
 class GemmTuning(ctypes.Structure):
@@ -89,7 +89,7 @@ EXPORTS = (
     "df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_free",
     "df11_encoded_view", "df11_gemm_layout", "df11_gemm_tile_rows", "df11_gemm_tile_cols",
     "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_batch_tuned", "df11_decode_rows",
-    "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_tuned", "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
+    "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_ex", "df11_decode_gemm_workspace_bytes", "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
     "df11_device_encoded_to_host",
     "df11_status_string", "df11_last_error", "df11_version",
 )
@@ -134,8 +134,10 @@ def lib():
     L.df11_decode_rows.argtypes = [ctypes.POINTER(View), vp, u64, vp, vp]
     L.df11_decode_gemm.argtypes = [ctypes.POINTER(View), vp, u32, vp, vp, vp]
     L.df11_decode_gemm_out.argtypes = [ctypes.POINTER(View), vp, u32, vp, ctypes.c_int, vp, vp]
-    L.df11_decode_gemm_tuned.argtypes = [ctypes.POINTER(View), vp, u32, vp, ctypes.c_int, vp,
-                                         ctypes.POINTER(GemmTuning), vp]
+    L.df11_decode_gemm_ex.argtypes = [ctypes.POINTER(View), vp, u32, vp, ctypes.c_int, vp,
+                                      ctypes.POINTER(GemmTuning), vp, u64, vp]
+    L.df11_decode_gemm_workspace_bytes.argtypes = [ctypes.POINTER(View), u32]
+    L.df11_decode_gemm_workspace_bytes.restype = u64
     L.df11_hist_device.argtypes = [vp, u64, vp, vp]
     L.df11_encode_device.argtypes = [vp, u64, ctypes.POINTER(Codebook), ctypes.POINTER(Layout), vp,
                                      ctypes.POINTER(vp)]
@@ -149,7 +151,7 @@ def lib():
     L.df11_version.restype = ctypes.c_char_p
     for name in ("df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_view",
                  "df11_gemm_layout", "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_batch_tuned",
-                 "df11_decode_rows", "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_tuned",
+                 "df11_decode_rows", "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_ex",
                  "df11_hist_device", "df11_encode_device",
                  "df11_device_encoded_view", "df11_device_encoded_to_host"):
         getattr(L, name).restype = ctypes.c_int

@@ -317,9 +317,9 @@ def decode(t: DF11Tensor, out=None, stream=None):
     return out
 
 
-def decode_tuning(waves: int = 0, stores: int = 0) -> DecodeTuning:
+def decode_tuning(waves: int = 0, stores: int = 0, groups: int = 0) -> DecodeTuning:
     """Explicit launch choices for decode_batch (0 = the library's choice)."""
-    return DecodeTuning(waves=waves, stores=stores)
+    return DecodeTuning(waves=waves, stores=stores, groups=groups)
 
 
 def gemm_tuning(kernel: int = 0, row_blocks: int = 0, parts: int = 0, split: int = 0) -> GemmTuning:
@@ -366,12 +366,20 @@ def decode_rows(t: DF11Tensor, rows, out=None, stream=None):
     return out
 
 
+def gemm_workspace_bytes(w: DF11Tensor, B: int) -> int:
+    """Bytes of the packed-x workspace decode_gemm uses for B rows of x."""
+    return int(lib().df11_decode_gemm_workspace_bytes(ctypes.byref(w.view), B))
+
+
 def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None, out_dtype=None,
-                tuning: Optional[GemmTuning] = None):
+                tuning: Optional[GemmTuning] = None, workspace="auto"):
     """y = x @ W^T with W decoded tile by tile inside the kernel.  x: [B, K]
     bf16 on the GPU; returns y [B, N], float32 (default) or bfloat16
     (out_dtype=torch.bfloat16, or an `out` of that type: the float32 sum
-    rounded once, ties to even).  tuning: explicit kernel choices."""
+    rounded once, ties to even).  tuning: explicit kernel choices.
+    workspace: "auto" (above 32 rows of x, a device buffer from torch's
+    allocator for x in operand order), None (x read in place), or a uint8
+    device tensor of at least gemm_workspace_bytes(w, B) bytes."""
     import torch
     N, K = int(w.host_view.rows), int(w.host_view.cols)
     assert x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[1] == K
@@ -388,10 +396,17 @@ def decode_gemm(w: DF11Tensor, x, out=None, w_debug=None, stream=None, out_dtype
         assert w_debug.is_contiguous() and w_debug.numel() == N * K and w_debug.element_size() == 2
         wd = w_debug.data_ptr()
     y_dtype = DF11_Y_BF16 if out_dtype == torch.bfloat16 else DF11_Y_F32
-    if tuning is None:
-        check(lib().df11_decode_gemm_out(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), y_dtype, wd,
-                                         _stream_handle(stream)), "df11_decode_gemm_out")
-    else:
-        check(lib().df11_decode_gemm_tuned(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), y_dtype, wd,
-                                           ctypes.byref(tuning), _stream_handle(stream)), "df11_decode_gemm_tuned")
+    ws_ptr, ws_bytes = None, 0
+    if isinstance(workspace, str):
+        assert workspace == "auto"
+        ws_bytes = gemm_workspace_bytes(w, B)
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+            ws_ptr = workspace.data_ptr()
+    elif workspace is not None:
+        assert workspace.is_cuda and workspace.is_contiguous()
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().df11_decode_gemm_ex(ctypes.byref(w.view), x.data_ptr(), B, out.data_ptr(), y_dtype, wd,
+                                    ctypes.byref(tuning) if tuning is not None else None, ws_ptr, ws_bytes,
+                                    _stream_handle(stream)), "df11_decode_gemm_ex")
     return out

@@ -783,11 +783,12 @@ int pick_waves(const int res[kNumChoices], uint64_t items, uint64_t cus, uint32_
 // evenly split last round.
 template <int K, int CB, int KIND, class Args>
 int launch_waves(int choice, int resident, const Args &a, const TableArgs &t, uint32_t lds, uint64_t items,
-                 hipStream_t st)
+                 uint32_t forced_groups, hipStream_t st)
 {
     const int w = kWaveChoices[choice];
     const uint64_t per_cu = std::max(1, resident / w);
-    const uint64_t groups = std::min<uint64_t>((items + w - 1) / w, (uint64_t)device_cu_count() * per_cu);
+    const uint64_t groups = std::min<uint64_t>((items + w - 1) / w,
+                                               forced_groups ? forced_groups : (uint64_t)device_cu_count() * per_cu);
     if (!groups) return DF11_OK;
     const dim3 grid((uint32_t)groups), block(w * 64);
     switch (w) {
@@ -806,7 +807,7 @@ int launch_waves(int choice, int resident, const Args &a, const TableArgs &t, ui
 
 template <int K, int CB, int KIND, class Args>
 int launch_kind(const Args &a, const TableArgs &t, const df11_view *v, uint64_t items, uint32_t forced_waves,
-                hipStream_t st)
+                uint32_t forced_groups, hipStream_t st)
 {
     int res[kNumChoices];
     resident_waves<K, CB, KIND>(t.stg_bytes, v->fast_bits, v->n_tables, res);
@@ -817,22 +818,23 @@ int launch_kind(const Args &a, const TableArgs &t, const df11_view *v, uint64_t 
                                        : "tables and staging do not fit in LDS",
                           forced_waves);
     return launch_waves<K, CB, KIND>(i, res[i], a, t, lds_bytes(kWaveChoices[i], t.stg_bytes, v->fast_bits, v->n_tables),
-                                     items, st);
+                                     items, forced_groups, st);
 }
 
 // Views in 8-column-group tile order (16-byte chunks) take a kernel with the
 // row-wise merge for them (merge_tile_groups8); all other launches a kernel
 // without it.
 template <int K, int CB>
-int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, uint32_t waves, hipStream_t st)
+int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, const df11_decode_tuning &tune,
+                  hipStream_t st)
 {
     bool t8 = false;
     for (uint32_t i = 0; i < a.count; i++)
         t8 = t8 || (a.v[i].kc == 8 && a.v[i].pow2 && a.v[i].tr == 32);
     const uint64_t nseg = a.seg_begin[a.count];
     if constexpr (CB == 16)
-        if (t8) return launch_kind<K, CB, 1>(a, t, v, nseg, waves, st);
-    return launch_kind<K, CB, 0>(a, t, v, nseg, waves, st);
+        if (t8) return launch_kind<K, CB, 1>(a, t, v, nseg, tune.waves, tune.groups, st);
+    return launch_kind<K, CB, 0>(a, t, v, nseg, tune.waves, tune.groups, st);
 }
 
 }  // namespace
@@ -867,22 +869,21 @@ int decode_views(const df11_view *views, uint16_t *const *outs, uint32_t count, 
     if (!b.count || !b.seg_begin[b.count]) return DF11_OK;
     b.stream = tune.stores == DF11_STORES_AUTO ? out_bytes > kStreamOutBytes : tune.stores == DF11_STORES_STREAMING;
     TableArgs t{v0->chain, v0->fast, (uint32_t)v0->n_chain, stg};
-    const uint32_t w = tune.waves;
     if (v0->chunk_bytes == 8) {
         switch (v0->fast_bits) {
-        case 8: return launch_decode<8, 8>(b, t, v0, w, st);
-        case 9: return launch_decode<9, 8>(b, t, v0, w, st);
-        case 10: return launch_decode<10, 8>(b, t, v0, w, st);
-        case 11: return launch_decode<11, 8>(b, t, v0, w, st);
-        default: return launch_decode<12, 8>(b, t, v0, w, st);
+        case 8: return launch_decode<8, 8>(b, t, v0, tune, st);
+        case 9: return launch_decode<9, 8>(b, t, v0, tune, st);
+        case 10: return launch_decode<10, 8>(b, t, v0, tune, st);
+        case 11: return launch_decode<11, 8>(b, t, v0, tune, st);
+        default: return launch_decode<12, 8>(b, t, v0, tune, st);
         }
     }
     switch (v0->fast_bits) {
-    case 8: return launch_decode<8, 16>(b, t, v0, w, st);
-    case 9: return launch_decode<9, 16>(b, t, v0, w, st);
-    case 10: return launch_decode<10, 16>(b, t, v0, w, st);
-    case 11: return launch_decode<11, 16>(b, t, v0, w, st);
-    default: return launch_decode<12, 16>(b, t, v0, w, st);
+    case 8: return launch_decode<8, 16>(b, t, v0, tune, st);
+    case 9: return launch_decode<9, 16>(b, t, v0, tune, st);
+    case 10: return launch_decode<10, 16>(b, t, v0, tune, st);
+    case 11: return launch_decode<11, 16>(b, t, v0, tune, st);
+    default: return launch_decode<12, 16>(b, t, v0, tune, st);
     }
 }
 
@@ -891,11 +892,11 @@ int launch_rows(const RowArgs &a, const TableArgs &t, const df11_view *v, hipStr
 {
     const uint64_t items = a.n_rows * a.split;
     switch (v->fast_bits) {
-    case 8: return launch_kind<8, CB, 2>(a, t, v, items, 0, st);
-    case 9: return launch_kind<9, CB, 2>(a, t, v, items, 0, st);
-    case 10: return launch_kind<10, CB, 2>(a, t, v, items, 0, st);
-    case 11: return launch_kind<11, CB, 2>(a, t, v, items, 0, st);
-    default: return launch_kind<12, CB, 2>(a, t, v, items, 0, st);
+    case 8: return launch_kind<8, CB, 2>(a, t, v, items, 0, 0, st);
+    case 9: return launch_kind<9, CB, 2>(a, t, v, items, 0, 0, st);
+    case 10: return launch_kind<10, CB, 2>(a, t, v, items, 0, 0, st);
+    case 11: return launch_kind<11, CB, 2>(a, t, v, items, 0, 0, st);
+    default: return launch_kind<12, CB, 2>(a, t, v, items, 0, 0, st);
     }
 }
 
@@ -904,6 +905,7 @@ int check_tuning(const df11_decode_tuning &t)
     if (t.waves && std::find(std::begin(kWaveChoices), std::end(kWaveChoices), (int)t.waves) == std::end(kWaveChoices))
         return df11::fail(DF11_E_ARG, "tuning: %u waves per workgroup (need 0 or one of 4, 6, ..., 16)", t.waves);
     if (t.stores > DF11_STORES_STREAMING) return df11::fail(DF11_E_ARG, "tuning: stores = %u", t.stores);
+    if (t.groups > 0x7FFFFFFFu) return df11::fail(DF11_E_ARG, "tuning: groups = %u", t.groups);
     return DF11_OK;
 }
 

@@ -77,6 +77,8 @@ struct GemmArgs {
     uint32_t parts;          // segment-parallel form: segment ranges per row block (> 1: y accumulated atomically)
     uint32_t stg_bytes;      // segment-parallel form: exponent staging per wave
     uint64_t n_segments;
+    const uint4 *xo;         // x packed in operand order (x_pack_kernel), or null: x read in place
+    uint32_t xo_tiles;       // batch tiles of the packing
 };
 
 struct SegLoad {
@@ -434,6 +436,7 @@ decode_gemm_seg_kernel(GemmArgs g)
             const uint16_t *xr = g.x + (uint64_t)n_l * g.K + kt * kTC + khalf * 8;
             // x operand of batch tile m in round r (rows past B are zero)
             auto x_op = [&](int m, uint32_t r) {
+                if (g.xo) return g.xo[((uint64_t)(kt * 32u + u0 / 64 + r) * g.xo_tiles + m) * 64 + lane];
                 return n_l + 32u * m < g.B
                            ? *reinterpret_cast<const uint4 *>(xr + (uint64_t)(32u * m) * g.K + (u0 / 64 + r) * 16)
                            : make_uint4(0, 0, 0, 0);
@@ -615,6 +618,7 @@ decode_gemm_wide_kernel(GemmArgs g)
         }
     };
     auto x_op = [&](uint32_t tid, uint32_t kt, uint32_t ks) {
+        if (g.xo) return g.xo[((uint64_t)(kt * 32u + ks) * MT + m) * 64 + (tid & 63u)];
         const uint32_t brow = m * 32 + (tid & 31u), khalf = (tid >> 5) & 1u;
         return brow < g.B ? *reinterpret_cast<const uint4 *>(g.x + (uint64_t)brow * g.K + kt * kTC + ks * 16 + khalf * 8)
                           : make_uint4(0, 0, 0, 0);
@@ -715,6 +719,27 @@ decode_gemm_wide_kernel(GemmArgs g)
         __syncthreads();   // the planes are reused by the next unit
     }
 }
+
+// x [B, K] in the matrix cores' A-operand order: piece (s, m, l) holds the 8
+// BF16 of row 32 m + l % 32, columns 16 s + 8 (l / 32) .. + 7 (zero past row
+// B), at index (s * tiles + m) * 64 + l, so that the operand of k-step s and
+// batch tile m is one contiguous kilobyte.
+__global__ void x_pack_kernel(const uint16_t *x, uint32_t B, uint32_t K, uint32_t tiles, uint4 *xo)
+{
+    const uint64_t n = (uint64_t)(K / 16) * tiles * 64;
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t l = (uint32_t)(i & 63), m = (uint32_t)((i >> 6) % tiles);
+        const uint64_t ks = (i >> 6) / tiles;
+        const uint32_t row = m * 32 + (l & 31);
+        xo[i] = row < B ? *reinterpret_cast<const uint4 *>(x + (uint64_t)row * K + ks * 16 + (l >> 5) * 8)
+                        : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// batch tiles of the packed x for B rows: the wide kernel's 2, 4 or 8
+uint32_t packed_tiles(uint32_t B) { return B <= 64 ? 2 : B <= 128 ? 4 : 8; }
+
+uint64_t packed_bytes(uint32_t K, uint32_t B) { return B <= 32 ? 0 : (uint64_t)(K / 16) * packed_tiles(B) * 64 * 16; }
 
 __global__ void zero_kernel(float4 *p, uint64_t n4)
 {
@@ -861,19 +886,32 @@ int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, uint32_t f
 }
 
 template <int K>
-int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, const df11_gemm_tuning &tune,
+int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_gemm_tuning &tune, void *ws,
               hipStream_t st)
 {
     // Automatic choice: segment-parallel up to 40 rows of x (one batch tile
     // to 32, two above) when its staging fits; from 41 rows the wide kernel
     // is faster (up_proj: 58.5 against 60.7 us at 33 rows, 66.8 against
-    // 64.9 at 48, 76.4 against 67.7 at 64).  w_debug calls take the
-    // tile-synchronous kernel up to 32 rows, the wide one above.
+    // 64.9 at 48, 76.4 against 67.7 at 64).  With x packed in a workspace
+    // the wide kernel is the faster one from 33 rows (up_proj, packed: 56.6
+    // against 58.1 us at 33 rows, 56.5 against 58.3 at 40).  w_debug calls
+    // take the tile-synchronous kernel up to 32 rows, the wide one above.
     const uint32_t mt = (a.B + 31) / 32;
     uint32_t kernel = tune.kernel;
     if (kernel == DF11_GEMM_AUTO) {
-        if (a.B <= 40 && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems)) kernel = DF11_GEMM_SEGMENT;
+        if (a.B <= (ws ? 32u : 40u) && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems))
+            kernel = DF11_GEMM_SEGMENT;
         else kernel = mt <= 1 ? DF11_GEMM_TILED : DF11_GEMM_WIDE;
+    }
+    // the segment-parallel kernel with two batch tiles and the wide kernel
+    // read x from the packed copy
+    if (ws && mt >= 2 && kernel != DF11_GEMM_TILED) {
+        const uint32_t tiles = packed_tiles(a.B);
+        const uint64_t n = (uint64_t)(a.K / 16) * tiles * 64;
+        hipLaunchKernelGGL(x_pack_kernel, dim3((uint32_t)std::min<uint64_t>((n + 255) / 256, 4096)), dim3(256), 0, st,
+                           a.x, a.B, a.K, tiles, reinterpret_cast<uint4 *>(ws));
+        a.xo = reinterpret_cast<const uint4 *>(ws);
+        a.xo_tiles = tiles;
     }
     if (kernel == DF11_GEMM_SEGMENT) {
         if (a.w_debug || mt > 2)
@@ -894,7 +932,8 @@ int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, cons
     // plane and 16 KB more; above 112 rows of x two row blocks share each x
     // operand (a second exponent plane and BF16 plane; up_proj at 128 / 192
     // / 256 rows: 88.1 / 95.5 / 104.5 us against 92.6 / 113.7 / 141.0 with
-    // one, even at 96)
+    // one, even at 96); with x packed, above 128 rows (packed: 70.6 / 105.8 /
+    // 107.3 us with one row block against 69.8 / 95.1 / 95.9 with two)
     if (mt < 2) return df11::fail(DF11_E_ARG, "tuning: the wide kernel takes more than 32 rows of x");
     const uint32_t lds_wide = lds + kTile, lds_wide2 = lds_wide + 3 * kTile;
     if (lds_wide > 160u * 1024u) {
@@ -906,7 +945,7 @@ int launch_mt(const GemmArgs &a, uint32_t n_tables, uint32_t max_seg_elems, cons
     const bool fits2 = lds_wide2 <= 160u * 1024u;
     if (tune.row_blocks == 2 && !fits2)
         return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: two row blocks' planes do not fit in LDS");
-    const bool two = tune.row_blocks ? tune.row_blocks == 2 : fits2 && a.B > 112;
+    const bool two = tune.row_blocks ? tune.row_blocks == 2 : fits2 && a.B > (a.xo ? 128u : 112u);
     if (mt <= 2) return two ? launch<K, 2, 16, true, 2>(a, lds_wide2, tune.split, st)
                             : launch<K, 2, W, true>(a, lds_wide, tune.split, st);
     if (mt <= 4) return two ? launch<K, 4, 16, true, 2>(a, lds_wide2, tune.split, st)
@@ -941,11 +980,20 @@ extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t 
 extern "C" int df11_decode_gemm_out(const df11_view *w, const uint16_t *x, uint32_t B, void *y, int y_dtype,
                                     uint16_t *w_debug, void *stream)
 {
-    return df11_decode_gemm_tuned(w, x, B, y, y_dtype, w_debug, nullptr, stream);
+    return df11_decode_gemm_ex(w, x, B, y, y_dtype, w_debug, nullptr, nullptr, 0, stream);
 }
 
-extern "C" int df11_decode_gemm_tuned(const df11_view *w, const uint16_t *x, uint32_t B, void *y, int y_dtype,
-                                      uint16_t *w_debug, const df11_gemm_tuning *tuning, void *stream)
+extern "C" uint64_t df11_decode_gemm_workspace_bytes(const df11_view *w, uint32_t B)
+{
+    if (!w || w->tile_rows != kTR || w->tile_cols != kTC || w->tile_kchunk != kKC || !w->cols || w->cols % kTC ||
+        w->cols > 0xFFFFFFFFull || B > 256)
+        return 0;
+    return packed_bytes((uint32_t)w->cols, B);
+}
+
+extern "C" int df11_decode_gemm_ex(const df11_view *w, const uint16_t *x, uint32_t B, void *y, int y_dtype,
+                                   uint16_t *w_debug, const df11_gemm_tuning *tuning, void *workspace,
+                                   uint64_t workspace_bytes, void *stream)
 {
     if (y_dtype != DF11_Y_F32 && y_dtype != DF11_Y_BF16)
         return df11::fail(DF11_E_ARG, "df11_decode_gemm_out: unknown y_dtype %d", y_dtype);
@@ -978,6 +1026,10 @@ extern "C" int df11_decode_gemm_tuned(const df11_view *w, const uint16_t *x, uin
     if (((uintptr_t)x & 15) || ((uintptr_t)y & 15) || ((uintptr_t)w_debug & 15) || ((uintptr_t)w->sm & 15) ||
         ((uintptr_t)w->exp_words & 15) || ((uintptr_t)w->fast & 15) || ((uintptr_t)w->chain & 15))
         return df11::fail(DF11_E_ARG, "x, y, w_debug and the view arrays must be 16-byte aligned");
+    if (workspace && (((uintptr_t)workspace & 255) || workspace_bytes < packed_bytes((uint32_t)w->cols, B)))
+        return df11::fail(DF11_E_ARG, "workspace: %llu bytes at %p; need %llu, 256-byte aligned",
+                          (unsigned long long)workspace_bytes, workspace,
+                          (unsigned long long)packed_bytes((uint32_t)w->cols, B));
     GemmArgs a{};
     a.words = w->exp_words;
     a.sm = w->sm;
@@ -1000,10 +1052,10 @@ extern "C" int df11_decode_gemm_tuned(const df11_view *w, const uint16_t *x, uin
     a.n_segments = w->n_segments;
     hipStream_t st = (hipStream_t)stream;
     switch (w->fast_bits) {
-    case 8: return launch_mt<8>(a, w->n_tables, w->max_seg_elems, tune, st);
-    case 9: return launch_mt<9>(a, w->n_tables, w->max_seg_elems, tune, st);
-    case 10: return launch_mt<10>(a, w->n_tables, w->max_seg_elems, tune, st);
-    case 11: return launch_mt<11>(a, w->n_tables, w->max_seg_elems, tune, st);
-    default: return launch_mt<12>(a, w->n_tables, w->max_seg_elems, tune, st);
+    case 8: return launch_mt<8>(a, w->n_tables, w->max_seg_elems, tune, workspace, st);
+    case 9: return launch_mt<9>(a, w->n_tables, w->max_seg_elems, tune, workspace, st);
+    case 10: return launch_mt<10>(a, w->n_tables, w->max_seg_elems, tune, workspace, st);
+    case 11: return launch_mt<11>(a, w->n_tables, w->max_seg_elems, tune, workspace, st);
+    default: return launch_mt<12>(a, w->n_tables, w->max_seg_elems, tune, workspace, st);
     }
 }

@@ -278,7 +278,9 @@ int df11_decode_batch(const df11_view *device_views, uint16_t *const *outs, uint
 typedef struct df11_decode_tuning {
     uint32_t waves;        /* waves per workgroup: 0 = from occupancy and size, else 4, 6, ..., 16 */
     uint32_t stores;       /* DF11_STORES_* */
-    uint32_t reserved[6];  /* zero */
+    uint32_t groups;       /* workgroups per launch: 0 = as many as are resident at once (each wave
+                              then walks several segments), else that many, at most 2^31 - 1 */
+    uint32_t reserved[5];  /* zero */
 } df11_decode_tuning;
 
 /* df11_decode_batch with explicit launch choices ([P3] 5.2: occupancy is
@@ -318,7 +320,7 @@ int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t
  * by all batch tiles (two row blocks per workgroup above 112 rows); w_debug
  * calls up to 32 rows, and weights whose segments are too large for the
  * segment-parallel kernel's staging, take a tile-synchronous kernel
- * (df11_decode_gemm_tuned makes the choice explicit).
+ * (df11_decode_gemm_ex makes the choice explicit).
  * Non-finite x: a row of x holding Inf or NaN gives a non-finite row of y;
  * where a plain product would give +-Inf, y may hold NaN instead (the
  * segment-parallel kernel multiplies the weights of a neighbouring segment,
@@ -357,15 +359,33 @@ typedef struct df11_gemm_tuning {
     uint32_t reserved[4];  /* zero */
 } df11_gemm_tuning;
 
-/* df11_decode_gemm_out with explicit kernel choices ([P3] 5.2: the kernel
- * shape is tuned to the hardware).  y agrees with every choice within the
- * float32 summation order.  Errors: as df11_decode_gemm_out, E_ARG for a
- * choice that does not apply (w_debug or more than 64 rows of x on the
- * segment-parallel kernel, 32 rows or fewer on the wide one, parts or split
- * above 1 with a BF16 y), E_UNSUPPORTED when the chosen kernel's LDS does
- * not fit this weight. */
-int df11_decode_gemm_tuned(const df11_view *device_view, const uint16_t *x, uint32_t B, void *y,
-                           int y_dtype, uint16_t *w_debug, const df11_gemm_tuning *tuning, void *stream);
+/* Bytes of the workspace df11_decode_gemm_ex can use for B rows of x with
+ * this weight: x repacked in the matrix cores' operand order (16 bytes per
+ * lane and k-step, one contiguous kilobyte per wavefront load, rows past B
+ * zero): 32 T rows of x, (K / 16) * T * 1024 bytes, for T = 2, 4 or 8
+ * batch tiles of 32 rows (B up to 64, 128, 256).  0 when B <= 32, where x
+ * is read in place, and for a view not in the fused layout. */
+uint64_t df11_decode_gemm_workspace_bytes(const df11_view *device_view, uint32_t B);
+
+/* df11_decode_gemm_out with explicit kernel choices and a workspace
+ * ([P1] 2.2 item 3: decoded weights feed the matmul; [P3] 5.2: the kernel
+ * shape is tuned to the hardware).  tuning: NULL or zeroed = the library's
+ * choice.  workspace: NULL, or device memory of workspace_bytes >=
+ * df11_decode_gemm_workspace_bytes(w, B), 256-byte aligned, owned by the
+ * caller and not used by any other work on the GPU until this call's work on
+ * `stream` has finished: above 32 rows of x a packing kernel first writes x
+ * into it in operand order (overwriting all of the bytes it needs, so its
+ * contents need no clearing), and the product reads x from there (up_proj at
+ * 64 / 128 / 256 rows: 68 / 91 / 117 us in place, 57 / 70 / 96 us packed).
+ * y agrees with every choice within the float32 summation order.  Errors:
+ * as df11_decode_gemm_out, E_ARG for a choice that does not apply (w_debug
+ * or more than 64 rows of x on the segment-parallel kernel, 32 rows or fewer
+ * on the wide one, parts or split above 1 with a BF16 y) or a workspace too
+ * small or misaligned, E_UNSUPPORTED when the chosen kernel's LDS does not
+ * fit this weight. */
+int df11_decode_gemm_ex(const df11_view *device_view, const uint16_t *x, uint32_t B, void *y, int y_dtype,
+                        uint16_t *w_debug, const df11_gemm_tuning *tuning, void *workspace,
+                        uint64_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------- utilities */
 const char *df11_status_string(int status);

@@ -454,3 +454,48 @@ def test_explicit_kernel_choices_agree(kernel, B, extra):
     assert _rel(y, ref) < TOL
     if wd is not None:
         assert np.array_equal(wd, W) and _rel(yd, ref) < TOL
+
+
+@pytest.mark.parametrize("B", [33, 40, 64, 65, 100, 128, 129, 200, 256])
+def test_packed_x_workspace_and_in_place_x_agree(B):
+    """Above 32 rows of x the product can read x packed in operand order
+    from a workspace (filled first by a packing kernel; here a caller-owned
+    buffer full of garbage, since every byte the product reads is written
+    by the packing) or in place: both within tolerance of the oracle, the
+    decoded weights bit-exact either way, on a weight split along K."""
+    N, K = 96, 3072
+    _say("case gemm packed x B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=84).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=85)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    x = _x_to_gpu(X)
+    nb = api.gemm_workspace_bytes(dt, B)
+    assert nb == K // 16 * (2 if B <= 64 else 4 if B <= 128 else 8) * 1024
+    ws = torch.randint(0, 255, (nb + 256,), dtype=torch.uint8, device="cuda")
+    ref = orc.gemm_f64(X, W)
+    outs = []
+    for workspace in (None, ws, "auto"):
+        wd = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+        y = api.decode_gemm(dt, x, workspace=workspace)
+        yd = api.decode_gemm(dt, x, workspace=workspace, w_debug=wd)
+        torch.cuda.synchronize()
+        assert np.array_equal(wd.view(torch.int16).cpu().numpy().view(np.uint16), W)
+        for got in (y, yd):
+            assert _rel(got.cpu().numpy(), ref) < TOL
+        outs.append(y.cpu().numpy())
+    assert _rel(outs[1], outs[0].astype(np.float64)) < 1e-5
+
+
+@pytest.mark.parametrize("rows", [40, 64])
+def test_identity_x_recovers_up_proj_packed_x(rows):
+    """Wup through y with x packed (the default above 32 rows): 40 rows of
+    the identity per call (the wide kernel, two batch tiles) and 64 (two
+    full batch tiles), every weight bit for bit."""
+    N, K = 14336, 4096
+    _say("case gemm identity up_proj packed rows=%d" % rows)
+    W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    got = _identity_recover_on_gpu(dt, N, K, rows)
+    want = (torch.from_numpy(W.view(np.int16)).cuda().to(torch.int32) << 16)
+    bad = int((got.contiguous().view(torch.int32) != want).sum())
+    assert bad == 0, "%d of %d weights differ" % (bad, N * K)

@@ -74,8 +74,8 @@ def _gemm_call(view, B, tune, y_dtype=_lib.DF11_Y_F32, w_debug=False):
     _x, x = _aligned(2 * B * K)
     _y, y = _aligned(4 * B * N)
     _w, w = _aligned(2 * N * K)
-    rc = _lib.lib().df11_decode_gemm_tuned(ctypes.byref(view), x, B, y, y_dtype, w if w_debug else None,
-                                           ctypes.byref(tune), None)
+    rc = _lib.lib().df11_decode_gemm_ex(ctypes.byref(view), x, B, y, y_dtype, w if w_debug else None,
+                                        ctypes.byref(tune), None, 0, None)
     return rc, _lib.lib().df11_last_error().decode()
 
 
@@ -140,3 +140,22 @@ def test_offload_group_refuses_mixed_codebooks():
         OffloadedModel([("layer0", [("a", ea), ("b", eb)])], device="cpu")
     assert _same_tables(ea.codebook, api.encode(a).codebook)     # rebuilt from the same histogram
     assert not _same_tables(ea.codebook, eb.codebook)
+
+
+def test_fused_workspace_size_and_refusals():
+    """The packed-x workspace: none up to 32 rows of x, 32 T rows of x
+    ((K / 16) x T kilobytes) for T = 2, 4, 8 batch tiles above; a call with a workspace that is
+    too small or not 256-byte aligned is refused before any GPU work."""
+    N, K = 64, 1024
+    e = api.encode(synth.normal_bf16(N * K, 0.02, seed=5).reshape(N, K), layout=api.gemm_layout(N, K))
+    L = _lib.lib()
+    size = lambda B: int(L.df11_decode_gemm_workspace_bytes(ctypes.byref(e.view), B))
+    assert [size(B) for B in (1, 32, 33, 64, 65, 128, 129, 256)] == \
+        [0, 0] + [K // 16 * T * 1024 for T in (2, 2, 4, 4, 8, 8)]
+    assert int(L.df11_decode_gemm_workspace_bytes(ctypes.byref(api.encode(synth.normal_bf16(1000, 0.02)).view), 64)) == 0
+    _x, x = _aligned(2 * 64 * K)
+    _y, y = _aligned(4 * 64 * N)
+    _w, w = _aligned(size(64) + 512)
+    for ptr, nbytes in ((w, size(64) - 16), (w + 16, size(64))):
+        rc = L.df11_decode_gemm_ex(ctypes.byref(e.view), x, 64, y, _lib.DF11_Y_F32, None, None, ptr, nbytes, None)
+        assert rc == -1, L.df11_last_error()
