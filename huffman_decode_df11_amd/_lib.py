@@ -89,7 +89,7 @@ EXPORTS = (
     "df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_free",
     "df11_encoded_view", "df11_gemm_layout", "df11_gemm_tile_rows", "df11_gemm_tile_cols",
     "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_batch_tuned", "df11_decode_rows",
-    "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_ex", "df11_decode_gemm_workspace_bytes", "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
+    "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_ex", "df11_decode_gemm_noalloc", "df11_decode_gemm_workspace_bytes", "df11_decode_gemm_noalloc", "df11_hist_device", "df11_encode_device", "df11_device_encoded_free", "df11_device_encoded_view",
     "df11_device_encoded_to_host",
     "df11_status_string", "df11_last_error", "df11_version",
 )
@@ -137,6 +137,8 @@ def lib():
     L.df11_decode_gemm_ex.argtypes = [ctypes.POINTER(View), vp, u32, vp, ctypes.c_int, vp,
                                       ctypes.POINTER(GemmTuning), vp, u64, vp]
     L.df11_decode_gemm_workspace_bytes.argtypes = [ctypes.POINTER(View), u32]
+    L.df11_decode_gemm_noalloc.argtypes = [ctypes.POINTER(View), vp, u32, vp, ctypes.c_int, vp,
+                                           ctypes.POINTER(GemmTuning), vp]
     L.df11_decode_gemm_workspace_bytes.restype = u64
     L.df11_hist_device.argtypes = [vp, u64, vp, vp]
     L.df11_encode_device.argtypes = [vp, u64, ctypes.POINTER(Codebook), ctypes.POINTER(Layout), vp,
@@ -151,7 +153,7 @@ def lib():
     L.df11_version.restype = ctypes.c_char_p
     for name in ("df11_hist_accumulate", "df11_codebook_build", "df11_encode", "df11_encoded_view",
                  "df11_gemm_layout", "df11_validate", "df11_decode", "df11_decode_batch", "df11_decode_batch_tuned",
-                 "df11_decode_rows", "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_ex",
+                 "df11_decode_rows", "df11_decode_gemm", "df11_decode_gemm_out", "df11_decode_gemm_ex", "df11_decode_gemm_noalloc",
                  "df11_hist_device", "df11_encode_device",
                  "df11_device_encoded_view", "df11_device_encoded_to_host"):
         getattr(L, name).restype = ctypes.c_int

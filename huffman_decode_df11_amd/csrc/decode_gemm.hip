@@ -969,6 +969,37 @@ int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
     return DF11_OK;
 }
 
+// Scratch of df11_decode_gemm_noalloc: the packed x of callers that cannot
+// allocate, one copy per device (each device that loads the library holds it
+// until the process ends), shared by every such call on that device.
+constexpr uint64_t kScratchBytes = 16ull << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with the device current.  The array's name in host code is only a
+// stand-in for the symbol; kernels get this address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return df11::fail(DF11_E_UNSUPPORTED, "device %d: scratch kept for %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return df11::fail(DF11_E_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DF11_OK;
+}
+
 }  // namespace
 
 extern "C" int df11_decode_gemm(const df11_view *w, const uint16_t *x, uint32_t B, float *y,
@@ -1058,4 +1089,21 @@ extern "C" int df11_decode_gemm_ex(const df11_view *w, const uint16_t *x, uint32
     case 11: return launch_mt<11>(a, w->n_tables, w->max_seg_elems, tune, workspace, st);
     default: return launch_mt<12>(a, w->n_tables, w->max_seg_elems, tune, workspace, st);
     }
+}
+
+extern "C" int df11_decode_gemm_noalloc(const df11_view *w, const uint16_t *x, uint32_t B, void *y, int y_dtype,
+                                        uint16_t *w_debug, const df11_gemm_tuning *tuning, void *stream)
+{
+    const uint64_t need = df11_decode_gemm_workspace_bytes(w, B);
+    if (need > kScratchBytes)
+        return df11::fail(DF11_E_UNSUPPORTED,
+                          "df11_decode_gemm_noalloc: %llu bytes of packed x for B = %u and K = %llu; the library's "
+                          "scratch holds %llu",
+                          (unsigned long long)need, B, (unsigned long long)w->cols, (unsigned long long)kScratchBytes);
+    void *ws = nullptr;
+    if (need) {
+        int rc = scratch_address(&ws);
+        if (rc) return rc;
+    }
+    return df11_decode_gemm_ex(w, x, B, y, y_dtype, w_debug, tuning, ws, ws ? kScratchBytes : 0, stream);
 }

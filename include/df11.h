@@ -387,6 +387,21 @@ int df11_decode_gemm_ex(const df11_view *device_view, const uint16_t *x, uint32_
                         uint16_t *w_debug, const df11_gemm_tuning *tuning, void *workspace,
                         uint64_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * df11_decode_gemm_ex with the packed x kept in the library's own scratch,
+ * a 16 MiB array in device memory that every device the library runs on
+ * holds until the process ends; no allocation happens in the call.  The
+ * scratch covers df11_decode_gemm_workspace_bytes(w, B) <= 16 MiB, that is
+ * K * T <= 262144 (T = 2, 4, 8 batch tiles for B up to 64, 128, 256; K up to
+ * 32768 at 256 rows of x).  All such calls on one GPU share its scratch:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it; calls ordered on one stream do not (each packs x afresh, nothing
+ * has to start at zero).  Errors: as df11_decode_gemm_ex, and E_UNSUPPORTED
+ * when the packed x would not fit the scratch. */
+int df11_decode_gemm_noalloc(const df11_view *device_view, const uint16_t *x, uint32_t B, void *y,
+                             int y_dtype, uint16_t *w_debug, const df11_gemm_tuning *tuning, void *stream);
+
 /* ---------------------------------------------------------------- utilities */
 const char *df11_status_string(int status);
 const char *df11_last_error(void);
