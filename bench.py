@@ -424,7 +424,7 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8, rows:
         return a.elapsed_time(b) / steps
 
     by_b = {}
-    for B in (1, 8, 64, 256):
+    for B in (1, 8, 32, 64, 128, 256):
         X = synth.activations_bf16(B, K, seed=1)
         x = torch.from_numpy(X.view(np.int16)).cuda().view(torch.bfloat16)
         y = torch.empty(B, N, dtype=torch.float32, device="cuda")
@@ -465,13 +465,18 @@ def other_configs(steps: int, warmup: int, seed: int = 0):
     1024 x 1024 N(0, 0.02) tensor (launch-bound; the same tensor again and
     again) and 16,777,216 elements of 99% Student-t(3) x 0.02 plus 1% random
     16-bit patterns (every exponent, the longest codes; 12 copies cycled so
-    the compressed data comes from HBM).  Parity is checked in full first."""
+    the compressed data comes from HBM), each in the default 16-byte chunks
+    and in 8-byte chunks (twice the segments: shorter per-wave work for
+    tensors too small to fill the GPU many times over).  Parity is checked
+    in full first."""
     import torch
     from huffman_decode_df11_amd import api, synth
     out = {}
-    for name, u, copies in (("tensor_1024x1024", synth.tensor_1024(seed=seed).reshape(-1), 1),
-                            ("adversarial_16m", synth.adversarial_bf16(1 << 24, seed=seed), 12)):
-        enc = api.encode(u)
+    for name, u, copies, chunk in (("tensor_1024x1024", synth.tensor_1024(seed=seed).reshape(-1), 1, 16),
+                                   ("tensor_1024x1024_chunk8", synth.tensor_1024(seed=seed).reshape(-1), 1, 8),
+                                   ("adversarial_16m", synth.adversarial_bf16(1 << 24, seed=seed), 12, 16),
+                                   ("adversarial_16m_chunk8", synth.adversarial_bf16(1 << 24, seed=seed), 12, 8)):
+        enc = api.encode(u, layout=api.make_layout(chunk_bytes=chunk))
         dts = [enc.to("cuda") for _ in range(copies)]
         buf = torch.empty(u.size, dtype=torch.bfloat16, device="cuda")
         api.decode(dts[0], out=buf)
@@ -495,7 +500,7 @@ def other_configs(steps: int, warmup: int, seed: int = 0):
                      "decoded_gbs": round(2.0 * u.size / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "bits_per_weight": round(enc.compressed_nbytes() * 8.0 / u.size, 3),
-                     "copies_cycled": copies}
+                     "chunk_bytes": chunk, "copies_cycled": copies}
     return out
 
 
@@ -509,8 +514,6 @@ def embedding_lookup(steps: int, warmup: int, seed: int = 0, vocab: int = 128256
     import torch
     from huffman_decode_df11_amd import api, synth
     W = synth.normal_bf16_torch(vocab, dim, seed=seed, index=900, device="cuda")
-    dt = api.encode_device(W, layout=api.make_layout(rows=vocab, cols=dim))
-    row_alg = dim * (dt.total_bits / dt.n / 8.0 + 1.0) + 2.0 * dim
     rng = np.random.default_rng(seed + 77)
 
     def timeit(f, n):
@@ -526,23 +529,29 @@ def embedding_lookup(steps: int, warmup: int, seed: int = 0, vocab: int = 128256
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n * 1e3
 
-    out = {"workload": "embedding table %dx%d bf16 N(0,0.02), row-major layout, B random token ids per call"
-                       % (vocab, dim),
-           "bits_per_weight": round(dt.compressed_nbytes() * 8.0 / dt.n, 4), "by_tokens": {}}
-    for B in (1, 32, 2048):
-        ids = torch.from_numpy(rng.integers(0, vocab, B)).cuda()
-        buf = torch.empty(B, dim, dtype=torch.bfloat16, device="cuda")
-        api.decode_rows(dt, ids, out=buf)
-        torch.cuda.synchronize()
-        if not torch.equal(buf.view(torch.int16), W[ids].view(torch.int16)):
-            raise SystemExit("embedding lookup parity failed at B=%d" % B)
-        n = max(steps, 50)
-        us = timeit(lambda: api.decode_rows(dt, ids, out=buf), n)
-        us_t = timeit(lambda: torch.nn.functional.embedding(ids, W), n)
-        out["by_tokens"][str(B)] = {"us_per_call": round(us, 2), "torch_bf16_gather_us": round(us_t, 2),
-                                    "rows_per_s": round(B / (us * 1e-6), 1),
-                                    "hbm_frac": round(B * row_alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    del W, dt
+    out = {"workload": "embedding table %dx%d bf16 N(0,0.02), row-major layout (8-byte chunks, the DF11Embedding "
+                       "default; and 16-byte chunks), B random token ids per call" % (vocab, dim), "by_tokens": {}}
+    ids_by_b = {B: torch.from_numpy(rng.integers(0, vocab, B)).cuda() for B in (1, 32, 2048)}
+    for chunk in (8, 16):
+        dt = api.encode_device(W, layout=api.make_layout(rows=vocab, cols=dim, chunk_bytes=chunk))
+        row_alg = dim * (dt.total_bits / dt.n / 8.0 + 1.0) + 2.0 * dim
+        out["bits_per_weight_chunk%d" % chunk] = round(dt.compressed_nbytes() * 8.0 / dt.n, 4)
+        for B, ids in ids_by_b.items():
+            buf = torch.empty(B, dim, dtype=torch.bfloat16, device="cuda")
+            api.decode_rows(dt, ids, out=buf)
+            torch.cuda.synchronize()
+            if not torch.equal(buf.view(torch.int16), W[ids].view(torch.int16)):
+                raise SystemExit("embedding lookup parity failed at B=%d" % B)
+            n = max(steps, 50)
+            us = timeit(lambda: api.decode_rows(dt, ids, out=buf), n)
+            rec = out["by_tokens"].setdefault(str(B), {})
+            if chunk == 8:
+                rec["torch_bf16_gather_us"] = round(timeit(lambda: torch.nn.functional.embedding(ids, W), n), 2)
+            rec["us_per_call_chunk%d" % chunk] = round(us, 2)
+            rec["rows_per_s_chunk%d" % chunk] = round(B / (us * 1e-6), 1)
+            rec["hbm_frac_chunk%d" % chunk] = round(B * row_alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        del dt
+    del W
     torch.cuda.empty_cache()
     return out
 
@@ -884,6 +893,7 @@ def layer_workload(steps: int, warmup: int, seed: int = 0):
     buffer, and one launch each into one reused matrix-sized buffer (eager,
     and as one HIP graph).  Parity checked in full first."""
     import torch
+    from huffman_decode_df11_amd import api
     encs = build_layer(seed)
     mats = [m for _, m, _ in encs]
     dts = [e.to("cuda") for _, _, e in encs]
@@ -903,11 +913,26 @@ def layer_workload(steps: int, warmup: int, seed: int = 0):
         raise SystemExit("graph replay parity check failed")
     per = lambda t: {"ms_per_step": round(t, 4), "decoded_gbs": round(2.0 * n_total / (t * 1e-3) / 1e9, 2),
                      "hbm_frac": round(sum(alg) / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # the four smaller matrices (q, k, v, o: 1,328-5,306 segments, too few to
+    # fill the GPU many times over) in 8-byte chunks, the others in 16
+    cb = encs[0][2].codebook
+    small = {"q_proj", "k_proj", "v_proj", "o_proj"}
+    encs8 = [api.encode(m, codebook=cb, layout=api.make_layout(chunk_bytes=8 if name in small else 16))
+             for name, m, _ in encs]
+    dts8 = [e.to("cuda") for e in encs8]
+    verify(dts8, mats, outbuf)
+    _, eager8_ms = time_decode(dts8, outbuf, steps, warmup)
+    alg8 = sum(algorithmic_bytes(e) for e in encs8)
     return {
         "workload": "llama3-8b layer: q,k,v,o,gate,up,down bf16 N(0,0.02), %d elements, one codebook" % n_total,
         "batched_one_launch": per(ms),
         "per_matrix_graph": dict(per(graph_ms), launches_per_step=len(dts)),
         "per_matrix_eager": dict(per(eager_ms), launches_per_step=len(dts)),
+        "per_matrix_eager_small_chunk8": {
+            "ms_per_step": round(eager8_ms, 4), "decoded_gbs": round(2.0 * n_total / (eager8_ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(alg8 / (eager8_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bits_per_weight": round(8.0 * sum(e.compressed_nbytes() for e in encs8) / n_total, 4),
+            "note": "q, k, v, o encoded with 8-byte chunks, gate, up, down with 16"},
         "repeated_launch_ms": {name: round(float(t), 4) for (name, _, _), t in zip(encs, launch_ms)},
         "repeated_launch_note": "each matrix decoded again and again into the same buffer; its 100-200 MB "
                                 "of traffic partly stays in the 256 MB Infinity Cache, so these are warm-cache "

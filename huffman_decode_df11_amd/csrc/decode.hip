@@ -475,11 +475,10 @@ decode_kernel_t8(BatchArgs b, TableArgs t)
     decode_body<K, WAVES, true, CB>(b, t);
 }
 
-// Row gather: up to four waves per requested row (about as many as the
-// segments a row overlaps); the row's first segment is found by segment_of,
-// wave j of the row decodes the overlapping
-// segments j, j + split, ... whole into its staging, and only the row's
-// elements are written.
+// Row gather: up to eight waves per requested row (as many as the segments
+// a row can overlap); the row's first segment is found by segment_of, wave
+// j of the row decodes the overlapping segments j, j + split, ... whole
+// into its staging, and only the row's elements are written.
 struct RowArgs {
     ViewArgs v;               // row-major view (out unused)
     const int64_t *rows;      // requested row ids
@@ -537,21 +536,45 @@ decode_rows_kernel(RowArgs a, TableArgs t)
     const uint32_t stg = lds0 + 16 + wave * t.stg_bytes;
     const uint32_t fast = lds0 + 16 + WAVES * t.stg_bytes;
     const uint32_t chain = fast + (8u << K);
+    const ViewArgs &v = a.v;
+    const uint64_t items = a.n_rows * a.split;
+    // A work item w is piece j of requested row i.  The first item's
+    // segment search and first segment load go out before the tables are
+    // staged, so that their latency overlaps the staging.
+    struct Item {
+        uint64_t i, lo, hi, s;   // s: the item's first segment (n_segments: nothing to do)
+        uint32_t j;
+    };
+    auto item = [&](uint64_t w) {
+        Item it;
+        it.i = w / a.split;
+        it.j = (uint32_t)(w - it.i * a.split);
+        const int64_t r = a.rows[it.i];
+        it.s = v.n_segments;
+        it.lo = it.hi = 0;
+        if (r >= 0 && (uint64_t)r < a.n_view_rows) {   // an out-of-range id leaves its row as it is
+            it.lo = (uint64_t)r * v.cols;
+            it.hi = it.lo + v.cols;
+            it.s = min(segment_of(v, it.lo, lane) + it.j, v.n_segments);
+        }
+        return it;
+    };
+    uint64_t w = (uint64_t)blockIdx.x * WAVES + wave;
+    Item it{};
+    SegLoad<CB> first{};
+    if (w < items) {
+        it = item(w);
+        if (it.s < v.n_segments) first = load_segment<CB>(v, it.s, lane);
+    }
     stage_tables<K, WAVES * 64>(fast, chain, t.fast, t.chain, t.n_chain);
     __syncthreads();
 
-    const ViewArgs &v = a.v;
-    const uint64_t items = a.n_rows * a.split;
-    for (uint64_t w = (uint64_t)blockIdx.x * WAVES + wave; w < items; w += (uint64_t)gridDim.x * WAVES) {
-        const uint64_t i = w / a.split;
-        const uint32_t j = (uint32_t)(w - i * a.split);
-        const int64_t r = a.rows[i];
-        if (r < 0 || (uint64_t)r >= a.n_view_rows) continue;   // out-of-range id: row left as it is
-        const uint64_t lo = (uint64_t)r * v.cols, hi = lo + v.cols;
-        const uint64_t s0 = segment_of(v, lo, lane);
-        const RowOut out{a.out + i * v.cols, lo};
-        for (uint64_t s = s0 + j; s < v.n_segments; s += a.split) {
-            const SegLoad<CB> cur = load_segment<CB>(v, s, lane);
+    for (bool head = true; w < items; w += (uint64_t)gridDim.x * WAVES, head = false) {
+        if (!head) it = item(w);
+        const uint64_t lo = it.lo, hi = it.hi;
+        const RowOut out{a.out + it.i * v.cols, lo};
+        for (uint64_t s = it.s; s < v.n_segments; s += a.split) {
+            const SegLoad<CB> cur = head && s == it.s ? first : load_segment<CB>(v, s, lane);
             if (cur.g0 >= hi) break;
             const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
             uint2 smp[kPrefetchRounds];
@@ -756,6 +779,10 @@ int pick_waves(const int res[kNumChoices], uint64_t items, uint64_t cus, uint32_
         if (best < 0 || res[i] > res[best]) best = i;
     }
     if (forced || best < 0) return best;
+    // fewer than two rounds at the most resident waves: take them all (a
+    // 16M-element tensor in 8-byte chunks, 10.6K segments: 15.4 us at 32
+    // resident waves per CU against 17.1 us at 24)
+    if (items >= cus * (uint64_t)res[best] && items < 2 * cus * (uint64_t)res[best]) return best;
     if (items >= cus * (uint64_t)res[best]) {
         // several rounds: 24 resident waves per CU already keep HBM busy
         // (more waves measured slower on a whole layer in one launch, with
@@ -927,12 +954,18 @@ extern "C" int df11_decode_rows(const df11_view *v, const int64_t *rows, uint64_
     a.out = out;
     a.n_rows = n_rows;
     a.n_view_rows = v->rows;
-    // a row spans about cols / (elements per segment) + 1 segments: that
-    // many waves per row (at most 4) decode them side by side
+    // A row overlaps at most cols / (elements per segment) + 2 segments.  A
+    // few rows take that many waves each (at most 8), so that no wave
+    // decodes two of a row's segments in turn; many rows take one wave
+    // fewer, since every wave decodes a whole segment of which the row uses
+    // a part (128256 x 4096 table, 8-byte chunks: 4.9 / 5.4 us for 1 / 32
+    // ids at four waves per row; 2048 ids: 17.7 us at four, 12.7 at three).
     a.split = 1;
     if (v->n_segments) {
         const uint64_t per_seg = std::max<uint64_t>(1, v->n / v->n_segments);
-        a.split = (uint32_t)std::min<uint64_t>(4, v->cols / per_seg + 1);
+        const uint64_t wide = std::min<uint64_t>(8, v->cols / per_seg + 2);
+        a.split = (uint32_t)(n_rows * wide <= 16ull * (uint64_t)device_cu_count() ? wide
+                                                                                 : std::max<uint64_t>(1, wide - 1));
     }
     if (n_rows > (UINT64_MAX >> 3)) return df11::fail(DF11_E_ARG, "df11_decode_rows: too many rows");
     TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, staging_bytes(v)};

@@ -46,15 +46,15 @@ def _bits(weight) -> np.ndarray:
 class DF11Linear(torch.nn.Module):
     """A linear layer y = x W^T + b with W [out_features, in_features] held
     compressed.  mode "fused" (needs out % 32 == 0 and in % 512 == 0) runs
-    df11_decode_gemm for up to fused_max_rows rows of x and decode + matmul
-    above (default 88: on an up_proj-shaped weight, 14336 x 4096, the fused
-    call measured 72 us at 64 rows and 78 us at 88 rows against 80 us for
-    decoding the tile-ordered weight and calling torch.matmul, and 82 us
-    against 79 us at 96 rows, since the fused kernel re-reads x for every
-    32-row block of W); mode "decode" always decodes into the shared buffer
-    and calls torch.matmul.  "auto" picks "fused" when the shape allows it."""
+    the fused product (x packed in operand order above 32 rows) for up to
+    fused_max_rows rows of x and decode + matmul above (default 128: on an
+    up_proj-shaped weight, 14336 x 4096, the fused call measured 58.6 us at
+    64 rows and 73.4 us at 128 against about 79 and 82 us for decoding the
+    tile-ordered weight and calling torch.matmul; at 192 rows 95-98 against
+    91 us); mode "decode" always decodes into the shared buffer and calls
+    torch.matmul.  "auto" picks "fused" when the shape allows it."""
 
-    fused_max_rows = 88
+    fused_max_rows = 128
 
     def __init__(self, weight, bias: Optional[torch.Tensor] = None, mode: str = "auto", device="cuda",
                  codebook=None):
@@ -113,16 +113,19 @@ class DF11Linear(torch.nn.Module):
 class DF11Embedding(torch.nn.Module):
     """An embedding table [num_embeddings, embedding_dim] held compressed;
     a lookup decodes only the rows it returns.  Ids must lie in
-    [0, num_embeddings) (an id outside leaves its output row unwritten)."""
+    [0, num_embeddings) (an id outside leaves its output row unwritten).
+    chunk_bytes 8 (the default) halves the segments a looked-up row decodes
+    (128256 x 4096 table: 6.7 against 8.7 us for one id, 7.2 against 9.3 us
+    for 32) for 0.37 more bits per weight; 16 is the smaller encoding."""
 
-    def __init__(self, weight, device="cuda", codebook=None):
+    def __init__(self, weight, device="cuda", codebook=None, chunk_bytes: int = 8):
         super().__init__()
         w = _bits(weight)
         assert w.ndim == 2
         self.num_embeddings, self.embedding_dim = (int(v) for v in w.shape)
         if self.embedding_dim % 8:
             raise ValueError("embedding_dim must be a multiple of 8")
-        layout = api.make_layout(rows=self.num_embeddings, cols=self.embedding_dim)
+        layout = api.make_layout(rows=self.num_embeddings, cols=self.embedding_dim, chunk_bytes=chunk_bytes)
         self.weight_df11 = api.encode(w, codebook=codebook, layout=layout).to(device)
         self.device = self.weight_df11.device
 

@@ -296,9 +296,10 @@ int df11_decode_batch_tuned(const df11_view *device_views, uint16_t *const *outs
  * item 3: weights are restored right before use).  rows: device int64 ids,
  * 8-byte aligned.  The segments that overlap each requested row are found
  * from an interpolated guess, checked against the 64 segment records around
- * it, else by a 64-way search, and decoded whole (up to four waves per row,
- * one segment each); only the row's elements are written.  An id outside [0, rows) leaves its output row
- * unwritten.  Bit-exact like df11_decode.  Errors: E_ARG (null, misaligned,
+ * it, else by a 64-way search, and decoded whole (up to eight waves per
+ * row, one segment each; 8-byte chunks halve the segments and with them the
+ * latency of a lookup); only the row's elements are written.  An id outside
+ * [0, rows) leaves its output row unwritten.  Bit-exact like df11_decode.  Errors: E_ARG (null, misaligned,
  * tile-ordered view, cols not a multiple of 8), E_UNSUPPORTED, E_DEVICE. */
 int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t n_rows, uint16_t *out,
                      void *stream);
