@@ -789,6 +789,9 @@ def main():
     ap.add_argument("--no-shard", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--only", default="",
+                    help="comma-separated sections to run instead of the step (for profiling): fused, other_configs, "
+                         "embedding_lookup, encode, llama3_8b_layer")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -800,6 +803,20 @@ def main():
     import torch
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.only:
+        sections = {"fused": lambda: fused_up_proj(args.steps, args.warmup, args.seed),
+                    "other_configs": lambda: other_configs(args.steps, args.warmup, args.seed),
+                    "embedding_lookup": lambda: embedding_lookup(args.steps, args.warmup, args.seed),
+                    "encode": lambda: encode_rate(args.seed),
+                    "llama3_8b_layer": lambda: layer_workload(args.steps, args.warmup, args.seed)}
+        out = {}
+        for name in args.only.split(","):
+            log("section", name)
+            out[name] = sections[name]()
+        if args.calibrate_copy:
+            out["calibration_copy_bytes"] = calibration_copy()
+        print(json.dumps(out), flush=True)
+        return
 
     m, rec = model_headline(args.steps, args.warmup, args.seed)
     n = rec["elements"]
@@ -876,15 +893,22 @@ def main():
             "fused_up_proj": fused_up_proj(args.steps, args.warmup, args.seed, copies=32, rows=14336 // 8),
         }
     if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = 256 << 20
+        result["calibration_copy_bytes"] = calibration_copy()
     if not headline_only and not args.no_cpu_baseline:
         result["cpu_baseline"], result["cpu_baseline_legs"] = cpu_baselines(args.seed)
     print(json.dumps(result), flush=True)
+
+
+def calibration_copy(nbytes: int = 256 << 20) -> int:
+    """Three plain device-to-device copies of nbytes, whose HBM counters
+    calibrate FETCH_SIZE and WRITE_SIZE in the profiles."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return nbytes
 
 
 def layer_workload(steps: int, warmup: int, seed: int = 0):
