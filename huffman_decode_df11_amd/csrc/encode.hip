@@ -45,6 +45,7 @@ struct df11_device_encoded {
     uint64_t *block_seg = nullptr;
     uint8_t *counts = nullptr;
     uint64_t n_exp_words = 0, n_sm = 0, n_gaps = 0, n_segs = 0, n_chain = 0, n_fast = 0, n_block_seg = 0, n_counts = 0;
+    void *blob = nullptr;   // one device allocation holding every array above
 };
 
 namespace {
@@ -56,9 +57,24 @@ constexpr uint32_t kMaxBlock = 4096;   // elements per scan block
 // column groups inside tiles), as the layout defines it.
 struct DevOrder {
     uint64_t cols, tr, tc, kc, tile, tiles_per_row;
+    uint32_t pow2, trs, tcs, kcs;   // pow2: tr, tc (and kc when set) are powers of two with these shifts
     __device__ __forceinline__ uint64_t operator()(uint64_t g) const
     {
         if (!tr) return g;
+        if (pow2) {
+            const uint64_t t = g >> (trs + tcs), w = g & ((1ull << (trs + tcs)) - 1);
+            uint64_t r, c;
+            if (kc) {
+                const uint64_t in = w & ((1ull << (trs + kcs)) - 1);
+                r = in >> kcs;
+                c = ((w >> (trs + kcs)) << kcs) | (in & ((1ull << kcs) - 1));
+            } else {
+                r = w >> tcs;
+                c = w & ((1ull << tcs) - 1);
+            }
+            const uint64_t rb = t / tiles_per_row, cb = t - rb * tiles_per_row;
+            return ((rb << trs) + r) * cols + (cb << tcs) + c;
+        }
         const uint64_t t = g / tile, w = g - t * tile;
         uint64_t r, c;
         if (kc) {
@@ -84,6 +100,19 @@ DevOrder make_order(const df11_layout &L)
         o.kc = L.tile_kchunk;
         o.tile = o.tr * o.tc;
         o.tiles_per_row = L.cols / L.tile_cols;
+        auto lg = [](uint64_t x) -> int {
+            if (!x || (x & (x - 1))) return -1;
+            int k = 0;
+            while ((1ull << k) != x) k++;
+            return k;
+        };
+        const int a = lg(o.tr), b = lg(o.tc), c = o.kc ? lg(o.kc) : 0;
+        if (a >= 0 && b >= 0 && c >= 0) {
+            o.pow2 = 1;
+            o.trs = (uint32_t)a;
+            o.tcs = (uint32_t)b;
+            o.kcs = (uint32_t)c;
+        }
     }
     return o;
 }
@@ -93,18 +122,40 @@ struct CodeTable {
     uint32_t code[256];
 };
 
+// Exponent histogram.  Gaussian-like weights put most exponents in a handful
+// of bins, so 64 lanes adding into one histogram collide on the same LDS
+// words; each wave keeps kSub copies (lane l adds into copy l % kSub), which
+// are summed per bin at the end.  Eight elements per lane per load.
+constexpr uint32_t kSub = 16;
+
 __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *bits, uint64_t n, unsigned long long *hist)
 {
-    __shared__ uint32_t h[kThreads / 64][256];
-    const uint32_t wave = threadIdx.x >> 6;
-    for (uint32_t i = threadIdx.x; i < 256 * (kThreads / 64); i += kThreads) h[i / 256][i % 256] = 0;
+    __shared__ uint32_t h[kThreads / 64 * kSub][256];
+    uint32_t *hf = &h[0][0];
+    for (uint32_t i = threadIdx.x; i < kThreads / 64 * kSub * 256; i += kThreads) hf[i] = 0;
     __syncthreads();
-    for (uint64_t i = blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n; i += (uint64_t)gridDim.x * kThreads)
-        atomicAdd(&h[wave][(bits[i] >> 7) & 0xFF], 1u);
+    uint32_t *mine = h[(threadIdx.x >> 6) * kSub + (threadIdx.x & (kSub - 1))];
+    const uint64_t n8 = n / 8;
+    const uint4 *b8 = reinterpret_cast<const uint4 *>(bits);
+    const bool aligned = ((uintptr_t)bits & 15) == 0;
+    if (aligned) {
+        for (uint64_t i = blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n8; i += (uint64_t)gridDim.x * kThreads) {
+            const uint4 v = b8[i];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                atomicAdd(&mine[(w[k] >> 7) & 0xFFu], 1u);
+                atomicAdd(&mine[(w[k] >> 23) & 0xFFu], 1u);
+            }
+        }
+    }
+    for (uint64_t i = (aligned ? n8 * 8 : 0) + blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n;
+         i += (uint64_t)gridDim.x * kThreads)
+        atomicAdd(&mine[(bits[i] >> 7) & 0xFF], 1u);
     __syncthreads();
     for (uint32_t e = threadIdx.x; e < 256; e += kThreads) {
         uint64_t c = 0;
-        for (uint32_t w = 0; w < kThreads / 64; w++) c += h[w][e];
+        for (uint32_t k = 0; k < kThreads / 64 * kSub; k++) c += h[k][e];
         if (c) atomicAdd(&hist[e], (unsigned long long)c);
     }
 }
@@ -139,6 +190,7 @@ __global__ void __launch_bounds__(kThreads) bits_kernel(const uint16_t *bits, ui
 struct EmitArgs {
     const uint16_t *bits;
     uint64_t n, nseg, seg_bits, chunk_bits;
+    uint32_t sb_shift, cb_shift;   // seg_bits = 1 << sb_shift, chunk_bits = 1 << cb_shift
     uint32_t E;
     DevOrder order;
     const uint64_t *base;   // [nblocks + 1]: first bit of each block; base[nblocks] = ~0
@@ -150,23 +202,49 @@ struct EmitArgs {
     uint32_t *counts32;     // codes starting in each chunk (accumulated)
 };
 
+// One block of E elements per workgroup: each thread takes consecutive
+// elements (their codes' bit positions from a workgroup scan of the lengths),
+// ORs its codes into the block's stream words and counts code starts per
+// chunk in LDS, and stages the sign+mantissa bytes there; the words, bytes
+// and counts then go out with plain coalesced stores, except the block's
+// first and last word and chunk, which it may share with its neighbours
+// (atomic OR / add into memory cleared beforehand).
+constexpr uint32_t kPer = kMaxBlock / kThreads;   // elements per thread at most
+constexpr uint32_t kMaxWords = kMaxBlock + 2;       // stream words of a block of codes of at most 32 bits
+constexpr uint32_t kMaxChunks = kMaxBlock * 32 / 64 + 2;   // chunks of at least 8 bytes
+
 __global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct)
 {
     __shared__ uint8_t len[256];
     __shared__ uint32_t code[256];
     __shared__ uint32_t scan[kThreads];
+    __shared__ uint32_t words[kMaxWords];
+    __shared__ uint32_t ccount[kMaxChunks];
+    __shared__ __align__(16) uint8_t smb[kMaxBlock];
+    const uint64_t b = blockIdx.x;
+    const uint64_t g0 = b * a.E;
+    const uint32_t cnt = (uint32_t)min<uint64_t>(a.E, a.n - g0);
+    const uint64_t bbase = a.base[b], bend = a.end[b];
+    const uint32_t cbs = a.cb_shift, sbs = a.sb_shift;
+    const uint64_t wlo = bbase >> 5, clo = bbase >> cbs;
+    const uint32_t nw = (uint32_t)(((bend - 1) >> 5) - wlo + 1);
+    const uint32_t nc = (uint32_t)(((bend - 1) >> cbs) - clo + 1);
     for (uint32_t i = threadIdx.x; i < 256; i += kThreads) {
         len[i] = ct.len[i];
         code[i] = ct.code[i];
     }
-    const uint64_t b = blockIdx.x;
-    const uint64_t g0 = b * a.E;
-    const uint32_t cnt = (uint32_t)min<uint64_t>(a.E, a.n - g0);
+    for (uint32_t i = threadIdx.x; i < nw; i += kThreads) words[i] = 0;
+    for (uint32_t i = threadIdx.x; i < nc; i += kThreads) ccount[i] = 0;
     const uint32_t per = (cnt + kThreads - 1) / kThreads;       // consecutive elements per thread
     const uint32_t i0 = min(cnt, threadIdx.x * per), i1 = min(cnt, i0 + per);
     __syncthreads();
+    uint16_t uu[kPer];
     uint32_t mine = 0;
-    for (uint32_t i = i0; i < i1; i++) mine += len[(a.bits[a.order(g0 + i)] >> 7) & 0xFF];
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; k++) {
+        uu[k] = i0 + k < i1 ? a.bits[a.order(g0 + i0 + k)] : 0;
+        if (i0 + k < i1) mine += len[(uu[k] >> 7) & 0xFF];
+    }
     scan[threadIdx.x] = mine;
     __syncthreads();
     for (uint32_t off = 1; off < kThreads; off <<= 1) {   // inclusive Hillis-Steele scan
@@ -175,7 +253,7 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct
         scan[threadIdx.x] += v;
         __syncthreads();
     }
-    uint64_t pos = a.base[b] + (scan[threadIdx.x] - mine);
+    uint64_t pos = bbase + (scan[threadIdx.x] - mine);
     // start of the element before i0
     uint64_t prev;
     bool has_prev = g0 + i0 > 0;
@@ -188,38 +266,41 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct
     const uint64_t SB = a.seg_bits, CB = a.chunk_bits;
     uint64_t run_chunk = ~0ull;   // chunk of the codes counted in run_n, not yet added
     uint32_t run_n = 0;
-    for (uint32_t i = i0; i < i1; i++) {
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; k++) {
+        if (i0 + k >= i1) break;
+        const uint32_t i = i0 + k;
         const uint64_t g = g0 + i;
-        const uint16_t u = a.bits[a.order(g)];
+        const uint16_t u = uu[k];
         const uint32_t e = (u >> 7) & 0xFF;
         const uint32_t L = len[e];
         // the code, first bit at bit (31 - pos % 32) of word pos / 32
-        const uint64_t w = pos >> 5, off = pos & 31;
+        const uint32_t w = (uint32_t)((pos >> 5) - wlo), off = (uint32_t)(pos & 31);
         const uint64_t wide = (uint64_t)code[e] << (64 - off - L);
         const uint32_t hi = (uint32_t)(wide >> 32), lo = (uint32_t)wide;
-        if (hi) atomicOr(&a.words[w], hi);
-        if (lo) atomicOr(&a.words[w + 1], lo);
-        a.sm[g] = (uint8_t)(((u >> 8) & 0x80) | (u & 0x7F));
-        if (pos / CB != run_chunk) {
-            if (run_n) atomicAdd(&a.counts32[run_chunk], run_n);
-            run_chunk = pos / CB;
+        if (hi) atomicOr(&words[w], hi);
+        if (lo) atomicOr(&words[w + 1], lo);
+        smb[i] = (uint8_t)(((u >> 8) & 0x80) | (u & 0x7F));
+        if ((pos >> cbs) != run_chunk) {
+            if (run_n) atomicAdd(&ccount[run_chunk - clo], run_n);
+            run_chunk = pos >> cbs;
             run_n = 0;
         }
         run_n++;
-        const uint64_t s = pos / SB;
+        const uint64_t s = pos >> sbs;
         // gap of the chunk holding this code's first bit, when no earlier code starts in it
-        const uint64_t c0 = pos - pos % CB;
-        if (!has_prev || prev < c0) a.gaps[c0 / CB] = (uint8_t)(pos - c0);
+        const uint64_t c0 = pos & ~(CB - 1);
+        if (!has_prev || prev < c0) a.gaps[c0 >> cbs] = (uint8_t)(pos - c0);
         // this element opens segments (previous segment, s]
-        const uint64_t sp = has_prev ? prev / SB : ~0ull;
+        const uint64_t sp = has_prev ? prev >> sbs : ~0ull;
         for (uint64_t t = sp + 1; t <= s; t++) a.segs[t].elem_off = g;
         // last code of its segment: segment length in bits and the gap of a chunk it runs into
         const uint64_t vend = pos + L;
         const uint64_t next = i + 1 < cnt ? vend : a.base[b + 1];
-        if (next == ~0ull || next / SB > s) {
-            a.segs[s].nbits = (uint32_t)min<uint64_t>(SB, vend - s * SB);
+        if (next == ~0ull || (next >> sbs) > s) {
+            a.segs[s].nbits = (uint32_t)min<uint64_t>(SB, vend - (s << sbs));
             const uint64_t c1 = c0 + CB;
-            if (c1 < vend && c1 < (s + 1) * SB) a.gaps[c1 / CB] = (uint8_t)(vend - c1);
+            if (c1 < vend && c1 < ((s + 1) << sbs)) a.gaps[c1 >> cbs] = (uint8_t)(vend - c1);
         }
         if (g + 1 == a.n)   // trailing segments without a code start, and the closing record
             for (uint64_t t = s + 1; t <= a.nseg; t++) a.segs[t].elem_off = a.n;
@@ -227,7 +308,39 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(EmitArgs a, CodeTable ct
         has_prev = true;
         pos = vend;
     }
-    if (run_n) atomicAdd(&a.counts32[run_chunk], run_n);
+    if (run_n) atomicAdd(&ccount[run_chunk - clo], run_n);
+    __syncthreads();
+    // words and chunks strictly inside the block's bits belong to it alone
+    for (uint32_t i = threadIdx.x; i < nw; i += kThreads) {
+        const uint32_t v = words[i];
+        if (i == 0 || i + 1 == nw) {
+            if (v) atomicOr(&a.words[wlo + i], v);
+        } else {
+            a.words[wlo + i] = v;
+        }
+    }
+    for (uint32_t i = threadIdx.x; i < nc; i += kThreads) {
+        const uint32_t v = ccount[i];
+        if (i == 0 || i + 1 == nc) {
+            if (v) atomicAdd(&a.counts32[clo + i], v);
+        } else {
+            a.counts32[clo + i] = v;
+        }
+    }
+    // sign+mantissa bytes [g0, g0 + cnt): 16-byte stores where they align
+    uint8_t *smo = a.sm + g0;
+    const uint32_t head = (uint32_t)((16 - ((uintptr_t)smo & 15)) & 15);
+    const uint32_t h = min(head, cnt);
+    for (uint32_t i = threadIdx.x; i < h; i += kThreads) smo[i] = smb[i];
+    const uint32_t body = (cnt - h) / 16;
+    for (uint32_t q = threadIdx.x; q < body; q += kThreads) {
+        uint4 v;
+        uint8_t *vb = reinterpret_cast<uint8_t *>(&v);
+#pragma unroll
+        for (int k = 0; k < 16; k++) vb[k] = smb[h + 16 * q + k];
+        *reinterpret_cast<uint4 *>(smo + h + 16 * q) = v;
+    }
+    for (uint32_t i = h + 16 * body + threadIdx.x; i < cnt; i += kThreads) smo[i] = smb[i];
 }
 
 __global__ void narrow_counts_kernel(const uint32_t *c32, uint8_t *c8, uint64_t n)
@@ -264,11 +377,20 @@ uint32_t grid_for(uint64_t items, uint32_t per_group)
 void free_device(df11_device_encoded *d)
 {
     if (!d) return;
-    void *ps[] = {d->exp_words, d->sm, d->gaps, d->segs, d->chain, d->fast, d->block_seg, d->counts};
-    for (void *p : ps)
-        if (p) (void)hipFree(p);
+    if (d->blob) (void)hipFree(d->blob);
     delete d;
 }
+
+// Byte offsets of consecutive 256-byte aligned parts of one allocation.
+struct Carve {
+    uint64_t total = 0;
+    uint64_t take(uint64_t bytes)
+    {
+        const uint64_t off = total;
+        total += (std::max<uint64_t>(bytes, 16) + 255) / 256 * 256;
+        return off;
+    }
+};
 
 // Device scratch freed on every return path.
 struct Scratch {
@@ -298,7 +420,8 @@ extern "C" int df11_hist_device(const uint16_t *bits, uint64_t n, uint64_t hist[
     unsigned long long *dh;
     HIP_TRY(s.alloc(&dh, 256), "hist buffer");
     HIP_TRY(hipMemsetAsync(dh, 0, 256 * sizeof(unsigned long long), st), "hist clear");
-    hipLaunchKernelGGL(hist_kernel, dim3(grid_for(n, kThreads * 64)), dim3(kThreads), 0, st, bits, n, dh);
+    hipLaunchKernelGGL(hist_kernel, dim3(std::min<uint32_t>(grid_for(n, kThreads * 64), 2048)), dim3(kThreads), 0, st,
+                       bits, n, dh);
     HIP_TRY(hipGetLastError(), "hist launch");
     unsigned long long h[256];
     HIP_TRY(hipMemcpyAsync(h, dh, sizeof h, hipMemcpyDeviceToHost, st), "hist copy");
@@ -337,8 +460,8 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
     uint64_t total = 0;
     if (n) {
         uint32_t *dbits, *dflag;
-        HIP_TRY(s.alloc(&dbits, nb), "block sums");
-        HIP_TRY(s.alloc(&dflag, 1), "flag");
+        HIP_TRY(s.alloc(&dbits, nb + 1), "block sums");
+        dflag = dbits + nb;
         HIP_TRY(hipMemsetAsync(dflag, 0, sizeof(uint32_t), st), "flag clear");
         hipLaunchKernelGGL(bits_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, st, bits, n, E, order, ct, dbits, dflag);
         HIP_TRY(hipGetLastError(), "block sum launch");
@@ -381,19 +504,26 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
     d->n_chain = (uint64_t)cb->n_tables * 256;
     d->n_fast = 2ull << cb->fast_bits;
     d->n_block_seg = L.align_elems ? (n + L.align_elems - 1) / L.align_elems + 1 : 0;
-    HIP_TRY(hipMalloc((void **)&d->exp_words, d->n_exp_words * 4), "stream words");
-    HIP_TRY(hipMalloc((void **)&d->sm, std::max<uint64_t>(d->n_sm, 16)), "sign+mantissa");
-    HIP_TRY(hipMalloc((void **)&d->gaps, std::max<uint64_t>(d->n_gaps, 16)), "gaps");
-    HIP_TRY(hipMalloc((void **)&d->counts, std::max<uint64_t>(d->n_counts, 16)), "counts");
-    HIP_TRY(hipMalloc((void **)&d->segs, d->n_segs * sizeof(df11_segment)), "segment records");
-    HIP_TRY(hipMalloc((void **)&d->chain, d->n_chain * 2), "tables");
-    HIP_TRY(hipMalloc((void **)&d->fast, d->n_fast * 4), "tables");
-    if (d->n_block_seg) HIP_TRY(hipMalloc((void **)&d->block_seg, d->n_block_seg * 8), "block index");
-    HIP_TRY(hipMemsetAsync(d->exp_words, 0, d->n_exp_words * 4, st), "clear");
-    HIP_TRY(hipMemsetAsync(d->sm, 0, std::max<uint64_t>(d->n_sm, 16), st), "clear");
-    HIP_TRY(hipMemsetAsync(d->gaps, 0, std::max<uint64_t>(d->n_gaps, 16), st), "clear");
-    HIP_TRY(hipMemsetAsync(d->counts, 0, std::max<uint64_t>(d->n_counts, 16), st), "clear");
-    HIP_TRY(hipMemsetAsync(d->segs, 0, d->n_segs * sizeof(df11_segment), st), "clear");
+    // every array in one allocation (one hipMalloc and one hipFree per
+    // encoding); the parts the emit kernel fills only in part are cleared
+    // in one fill: stream words, sign+mantissa bytes, gaps, counts, records
+    Carve cv;
+    const uint64_t o_words = cv.take(d->n_exp_words * 4), o_sm = cv.take(d->n_sm), o_gaps = cv.take(d->n_gaps),
+                   o_counts = cv.take(d->n_counts), o_segs = cv.take(d->n_segs * sizeof(df11_segment));
+    const uint64_t cleared = cv.total;
+    const uint64_t o_chain = cv.take(d->n_chain * 2), o_fast = cv.take(d->n_fast * 4),
+                   o_bseg = cv.take(d->n_block_seg * 8);
+    HIP_TRY(hipMalloc(&d->blob, cv.total), "encoded arrays");
+    uint8_t *blob = static_cast<uint8_t *>(d->blob);
+    d->exp_words = reinterpret_cast<uint32_t *>(blob + o_words);
+    d->sm = blob + o_sm;
+    d->gaps = blob + o_gaps;
+    d->counts = blob + o_counts;
+    d->segs = reinterpret_cast<df11_segment *>(blob + o_segs);
+    d->chain = reinterpret_cast<uint16_t *>(blob + o_chain);
+    d->fast = reinterpret_cast<uint32_t *>(blob + o_fast);
+    d->block_seg = d->n_block_seg ? reinterpret_cast<uint64_t *>(blob + o_bseg) : nullptr;
+    HIP_TRY(hipMemsetAsync(blob, 0, cleared, st), "clear");
     HIP_TRY(hipMemcpyAsync(d->chain, cb->chain, d->n_chain * 2, hipMemcpyHostToDevice, st), "tables");
     HIP_TRY(hipMemcpyAsync(d->fast, cb->fast, d->n_fast * 4, hipMemcpyHostToDevice, st), "tables");
     std::vector<uint64_t> bseg(d->n_block_seg);
@@ -403,18 +533,21 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
         HIP_TRY(hipMemcpyAsync(d->block_seg, bseg.data(), d->n_block_seg * 8, hipMemcpyHostToDevice, st), "block index");
     }
     if (n) {
+        // block starts and ends, then the segment maximum and the 32-bit
+        // chunk counts (cleared), in one scratch allocation
         uint64_t *dbase, *dend;
-        uint32_t *dmax;
-        HIP_TRY(s.alloc(&dbase, nb + 1), "block starts");
-        HIP_TRY(s.alloc(&dend, nb), "block ends");
-        HIP_TRY(s.alloc(&dmax, 1), "max");
+        uint32_t *dmax, *dcnt;
+        HIP_TRY(s.alloc(&dbase, (nb + 1) + nb + 1 + (d->n_counts + 2) / 2), "encode scratch");
+        dend = dbase + nb + 1;
+        dmax = reinterpret_cast<uint32_t *>(dend + nb);
+        dcnt = dmax + 2;
         HIP_TRY(hipMemcpyAsync(dbase, base.data(), (nb + 1) * 8, hipMemcpyHostToDevice, st), "block starts");
         HIP_TRY(hipMemcpyAsync(dend, end.data(), nb * 8, hipMemcpyHostToDevice, st), "block ends");
-        HIP_TRY(hipMemsetAsync(dmax, 0, 4, st), "clear");
-        uint32_t *dcnt;
-        HIP_TRY(s.alloc(&dcnt, d->n_counts), "chunk counts");
-        HIP_TRY(hipMemsetAsync(dcnt, 0, std::max<uint64_t>(d->n_counts, 1) * 4, st), "clear");
-        EmitArgs a{bits, n, nseg, seg_bits, chunk_bits, E, order, dbase, dend, d->exp_words, d->sm, d->gaps, d->segs, dcnt};
+        HIP_TRY(hipMemsetAsync(dmax, 0, 8 + std::max<uint64_t>(d->n_counts, 1) * 4, st), "clear");
+        // chunk and segment sizes are powers of two (8 or 16 bytes, 64 lanes)
+        const uint32_t cbs = L.chunk_bytes == 8 ? 6u : 7u, sbs = cbs + 6u;
+        EmitArgs a{bits, n, nseg, seg_bits, chunk_bits, sbs, cbs, E, order, dbase, dend, d->exp_words, d->sm,
+                   d->gaps, d->segs, dcnt};
         hipLaunchKernelGGL(emit_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, st, a, ct);
         HIP_TRY(hipGetLastError(), "emit launch");
         if (d->n_counts)
