@@ -17,7 +17,10 @@
 // l / 32) .. + 7, i.e. 8 consecutive stream elements, so operand reads are
 // contiguous across lanes.
 //
-// Three kernels, chosen by the rows of x (B):
+// Four kernels, chosen by the rows of x (B):
+//   decode_gemm_vec_kernel   (B <= 2): the segment-parallel walk below with
+//       the products formed as dot products on the vector ALU, one float32
+//       partial sum per row of x and lane, at 6 waves per SIMD.
 //   decode_gemm_seg_kernel   (B <= 40, the product path for small batches):
 //       every wave walks its own segments of a 32-row block, decodes each
 //       into its staging and feeds the matrix cores in rounds of 512
@@ -518,6 +521,161 @@ decode_gemm_seg_kernel(GemmArgs g)
     }
 }
 
+// ---------------------------------------------------------------- B <= 2
+// Vector form for one or two rows of x.  A matrix-core product spends its
+// 16-register accumulator and 16-byte operands on 32 batch rows of which
+// one or two are used; here the products are dot products on the vector
+// ALU (v_dot2c_f32_bf16, two BF16 products and a float32 add per
+// instruction), so a wave holds one float32 partial sum per row of x and
+// the kernel fits 6 waves per SIMD (80 VGPRs) against the segment-parallel
+// kernel's 4, which is what the latency-bound decode chain needs.  The walk
+// over a row block's segments, the staging and the 512-element rounds are
+// those of the segment-parallel kernel: unit u0 + 64 r + lane of a round is
+// row lane % 32 of the row block and columns 16 (u0 / 64 + r) + 8 (lane /
+// 32) .. + 7 of the tile, so a lane's row is fixed for the whole row block
+// and it needs the 16 bytes of x at those columns.  At the end of a row
+// block lanes l and l + 32 (the two column halves) are added, then the
+// waves through LDS, and one wave writes the 32 sums per row of x.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t x, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), acc, false);
+}
+
+template <int K, int WAVES, int NB>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(6, 8)))
+decode_gemm_vec_kernel(GemmArgs g)
+{
+    constexpr int kXAhead = 4 / NB;   // rounds whose x slices are loaded before the decode
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = lane_id();
+    // [guard][staging: WAVES x stg_bytes, also the reduction buffer][tables]
+    const uint32_t area = lds0 + 16;
+    const uint32_t stg = area + wave * g.stg_bytes;
+    const uint32_t fast = area + WAVES * g.stg_bytes;
+    const uint32_t chain = fast + (8u << K);
+    stage_tables<K, WAVES * 64>(fast, chain, g.fast, g.chain, g.n_chain);
+    __syncthreads();
+
+    const uint32_t khalf = lane >> 5;
+    const bool stored = g.counts != nullptr;
+    const uint64_t n_elems = (uint64_t)g.N * g.K;
+    const uint32_t n_units = g.n_rowblocks * g.parts;
+    for (uint32_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+        const uint32_t rb = unit / g.parts, part = unit - rb * g.parts;
+        const auto *bs = as_const(g.block_seg);
+        const uint64_t S0 = min(bs[(uint64_t)rb * g.tiles_per_row], g.n_segments);
+        const uint64_t S1 = min(bs[(uint64_t)(rb + 1) * g.tiles_per_row], g.n_segments);
+        const uint64_t len = S1 > S0 ? (S1 - S0 + g.parts - 1) / g.parts : 0;
+        const uint64_t s_begin = S0 + part * len, s_end = min(S1, s_begin + len);
+        float acc[NB];
+#pragma unroll
+        for (int b = 0; b < NB; b++) acc[b] = 0.0f;
+
+        uint64_t s = s_begin + wave;
+        SegLoad nx{};
+        if (s < s_end) nx = load_segment(g, s, lane);
+        while (s < s_end) {
+            const SegLoad cur = nx;
+            const uint64_t s_next = s + WAVES;
+            const bool more = s_next < s_end;
+            nx = load_segment(g, more ? s_next : s, lane);
+
+            // the segment inside its tile: elements [lo, hi), rounds from unit u0
+            const uint64_t t = cur.g0 >> 14;
+            bool valid = cur.g0 < n_elems && cur.g1 >= cur.g0 && cur.g1 <= min((t + 1) << 14, n_elems) &&
+                         t / g.tiles_per_row == rb;
+            const uint64_t tile_start = valid ? t << 14 : 0ull;
+            const uint32_t lo = valid ? (uint32_t)(cur.g0 - tile_start) : 0u;
+            const uint32_t hi = valid ? (uint32_t)(cur.g1 - tile_start) : 0u;
+            const uint32_t u0 = (lo >> 9) << 6, head = lo & 511u;
+            valid = valid && head + (hi - lo) + 512 <= g.stg_bytes;
+            const uint32_t nrounds = valid ? (hi - u0 * 8 + 511) >> 9 : 0u;
+            const uint32_t kt = valid ? (uint32_t)(t - (uint64_t)rb * g.tiles_per_row) : 0u;
+            const uint8_t *smt = g.sm + tile_start;
+            const uint16_t *xr = g.x + kt * kTC + (u0 / 64) * 16 + khalf * 8;
+            // the 8 x values of round r for row b of x (b < B)
+            auto x_at = [&](int b, uint32_t r) {
+                return *reinterpret_cast<const uint4 *>(xr + (uint64_t)min((uint32_t)b, g.B - 1) * g.K + r * 16);
+            };
+
+            // operands of the first rounds (rounds past the segment reload its last round)
+            uint2 smp[kSegRounds];
+            uint4 xp[kXAhead][NB];
+            const uint32_t last_round = nrounds ? nrounds - 1 : 0u;
+#pragma unroll
+            for (int r = 0; r < kSegRounds; r++) {
+                const uint32_t rr = min((uint32_t)r, last_round);
+                smp[r] = *reinterpret_cast<const uint2 *>(smt + 8 * (u0 + 64 * rr + lane));
+                if (r < kXAhead)
+#pragma unroll
+                    for (int b = 0; b < NB; b++) xp[r < kXAhead ? r : 0][b] = x_at(b, rr);
+            }
+
+            if (valid && stage_seg<K>(cur, stored, stg + head, fast, chain, lane)) {
+                auto round = [&](uint32_t r, uint2 sv, const uint4 *xv) {
+                    const uint32_t u = u0 + 64 * r + lane;
+                    const uint2 mk = unit_mask((int)lo - (int)(8 * u), (int)hi - (int)(8 * u));
+                    const uint2 rx = ld64(stg + 8 * (64 * r + lane));
+                    const uint2 a = assemble4(sv.x & mk.x, rx.x & mk.x), c = assemble4(sv.y & mk.y, rx.y & mk.y);
+#pragma unroll
+                    for (int b = 0; b < NB; b++) {
+                        float v = dot2_bf16(a.x, xv[b].x, acc[b]);
+                        v = dot2_bf16(a.y, xv[b].y, v);
+                        v = dot2_bf16(c.x, xv[b].z, v);
+                        acc[b] = dot2_bf16(c.y, xv[b].w, v);
+                    }
+                };
+#pragma unroll
+                for (int r = 0; r < kSegRounds; r++)
+                    if ((uint32_t)r < nrounds) {
+                        if (r < kXAhead) {
+                            round(r, smp[r], xp[r < kXAhead ? r : 0]);
+                        } else {
+                            uint4 xv[NB];
+#pragma unroll
+                            for (int b = 0; b < NB; b++) xv[b] = x_at(b, r);
+                            round(r, smp[r], xv);
+                        }
+                    }
+                for (uint32_t r = kSegRounds; r < nrounds; r++) {
+                    const uint2 sv = *reinterpret_cast<const uint2 *>(smt + 8 * (u0 + 64 * r + lane));
+                    uint4 xv[NB];
+#pragma unroll
+                    for (int b = 0; b < NB; b++) xv[b] = x_at(b, r);
+                    round(r, sv, xv);
+                }
+            }
+            wave_lds_sync();   // the staging is reused by the next segment
+            s = s_next;
+        }
+
+        // the two column halves, then the waves through LDS (the staging is
+        // free after the barrier); wave 0 sums them in wave order
+        lds_f32 *red = (lds_f32 *)(size_t)area;
+#pragma unroll
+        for (int b = 0; b < NB; b++) acc[b] += __shfl_xor(acc[b], 32);
+        __syncthreads();
+        if (lane < 32)
+#pragma unroll
+            for (int b = 0; b < NB; b++) red[(wave * NB + b) * 32 + lane] = acc[b];
+        __syncthreads();
+        if (wave == 0 && lane < 32) {
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                float v = 0.0f;
+#pragma unroll 1
+                for (uint32_t w = 0; w < (uint32_t)WAVES; w++) v += red[(w * NB + b) * 32 + lane];
+                if ((uint32_t)b < g.B) store_y_at(g, (uint64_t)b * g.N + rb * kTR + lane, v, g.parts > 1);
+            }
+        }
+        __syncthreads();   // the staging is reused by the next unit
+    }
+}
+
 // ---------------------------------------------------------------- B > 40
 // Wide batches.  In the tile-synchronous kernel every wave builds the B
 // operand of every k-step (exponent plane + sign+mantissa bytes, two
@@ -885,6 +1043,75 @@ int launch_seg(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, uint32_t f
     return DF11_OK;
 }
 
+// Resident workgroups per CU of `kern` with `lds` bytes of LDS; the last
+// answers per (kernel, device, LDS size) are kept so that a sequence of
+// calls does not repeat the query.
+int resident_groups(const void *kern, uint32_t threads, uint32_t lds)
+{
+    struct Answer {
+        const void *kern;
+        int dev;
+        uint32_t lds;
+        int per_cu;
+    };
+    static std::mutex mu;
+    static Answer kept[16];
+    static uint32_t n_kept = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        for (uint32_t i = 0; i < std::min(n_kept, 16u); i++)
+            if (kept[i].kern == kern && kept[i].dev == dev && kept[i].lds == lds) return kept[i].per_cu;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, (int)threads, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    std::lock_guard<std::mutex> lk(mu);
+    kept[n_kept % 16] = Answer{kern, dev, lds, per_cu};
+    n_kept++;
+    return per_cu;
+}
+
+// Waves per workgroup of the vector kernel for this weight: 12 when their
+// staging stays in the first 64 KB of LDS (the emit loop keeps byte
+// addresses in 16 bits), else 8; 0 when neither fits (up_proj at 1 row of
+// x: 38.3 us with 12-wave groups, two per CU, 43.0 with 8-wave groups,
+// three per CU).
+uint32_t vec_kernel_waves(uint32_t fast_bits, uint32_t n_tables, uint32_t max_seg_elems)
+{
+    const uint32_t stg = seg_staging_bytes(max_seg_elems);
+    for (uint32_t w : {12u, 8u})
+        if (16 + w * stg <= 65520 && 16 + w * stg + (8u << fast_bits) + n_tables * 512u <= 160u * 1024u) return w;
+    return 0;
+}
+
+template <int K, int W, int NB>
+int launch_vec(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, uint32_t forced_parts, hipStream_t st)
+{
+    a.stg_bytes = seg_staging_bytes(max_seg_elems);
+    const uint32_t lds = 16 + W * a.stg_bytes + (8u << K) + n_tables * 512u;
+    const uint32_t slots =
+        (uint32_t)(cu_count() * resident_groups((const void *)decode_gemm_vec_kernel<K, W, NB>, W * 64, lds));
+    const uint64_t segs_per_rb = (a.n_segments + a.n_rowblocks - 1) / a.n_rowblocks;
+    // as many runs per row block as fit whole into the resident slots, at
+    // least one segment per wave (as for the segment-parallel kernel)
+    uint32_t parts = forced_parts;
+    if (!parts) {
+        parts = std::max(1u, slots / a.n_rowblocks);
+        parts = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(parts, segs_per_rb / W));
+    }
+    if (a.y_bf16) parts = 1;   // one writer per BF16 element
+    a.parts = parts;
+    if (parts > 1) clear_y(a, st);
+    const uint64_t units = (uint64_t)a.n_rowblocks * parts;
+    const uint32_t groups = (uint32_t)std::min<uint64_t>(units, 1u << 20);
+    hipLaunchKernelGGL((decode_gemm_vec_kernel<K, W, NB>), dim3(groups), dim3(W * 64), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
+    return DF11_OK;
+}
+
 template <int K>
 int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_gemm_tuning &tune, void *ws,
               hipStream_t st)
@@ -897,11 +1124,27 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
     // against 58.1 us at 33 rows, 56.5 against 58.3 at 40).  w_debug calls
     // take the tile-synchronous kernel up to 32 rows, the wide one above.
     const uint32_t mt = (a.B + 31) / 32;
+    const uint32_t vec_waves = vec_kernel_waves(K, n_tables, max_seg_elems);
     uint32_t kernel = tune.kernel;
     if (kernel == DF11_GEMM_AUTO) {
-        if (a.B <= (ws ? 32u : 40u) && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems))
+        // one or two rows of x: the vector kernel (up_proj: 38.3 / 42.0 us
+        // against 45.1 / 45.3 on the segment-parallel one; at 3 and 4 rows
+        // it is slower, 53 us)
+        if (a.B <= 2 && !a.w_debug && vec_waves) kernel = DF11_GEMM_VECTOR;
+        else if (a.B <= (ws ? 32u : 40u) && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems))
             kernel = DF11_GEMM_SEGMENT;
         else kernel = mt <= 1 ? DF11_GEMM_TILED : DF11_GEMM_WIDE;
+    }
+    if (kernel == DF11_GEMM_VECTOR) {
+        if (a.w_debug || a.B > 2)
+            return df11::fail(DF11_E_ARG, "tuning: the vector kernel takes one or two rows of x and no w_debug");
+        if (!vec_waves)
+            return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: vector kernel staging and tables do not fit in LDS");
+        if (vec_waves == 12)
+            return a.B == 1 ? launch_vec<K, 12, 1>(a, n_tables, max_seg_elems, tune.parts, st)
+                            : launch_vec<K, 12, 2>(a, n_tables, max_seg_elems, tune.parts, st);
+        return a.B == 1 ? launch_vec<K, 8, 1>(a, n_tables, max_seg_elems, tune.parts, st)
+                        : launch_vec<K, 8, 2>(a, n_tables, max_seg_elems, tune.parts, st);
     }
     // the segment-parallel kernel with two batch tiles and the wide kernel
     // read x from the packed copy
@@ -956,11 +1199,11 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
 
 int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
 {
-    if (t.kernel > DF11_GEMM_TILED) return df11::fail(DF11_E_ARG, "tuning: kernel %u", t.kernel);
+    if (t.kernel > DF11_GEMM_VECTOR) return df11::fail(DF11_E_ARG, "tuning: kernel %u", t.kernel);
     if (t.row_blocks > 2 || (t.row_blocks && t.kernel != DF11_GEMM_WIDE))
         return df11::fail(DF11_E_ARG, "tuning: row_blocks %u (0, or 1 or 2 with the wide kernel)", t.row_blocks);
-    if (t.parts && t.kernel != DF11_GEMM_SEGMENT)
-        return df11::fail(DF11_E_ARG, "tuning: parts applies to the segment-parallel kernel");
+    if (t.parts && t.kernel != DF11_GEMM_SEGMENT && t.kernel != DF11_GEMM_VECTOR)
+        return df11::fail(DF11_E_ARG, "tuning: parts applies to the segment-parallel and vector kernels");
     if (t.split && t.kernel != DF11_GEMM_WIDE && t.kernel != DF11_GEMM_TILED)
         return df11::fail(DF11_E_ARG, "tuning: split applies to the wide and tile-synchronous kernels");
     if (bf16_y && (t.parts > 1 || t.split > 1))

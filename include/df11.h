@@ -316,16 +316,19 @@ int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t
  * runs of its segments) and the partial sums are added into y (cleared
  * first, on the same stream) with float atomics, so the order of those few
  * additions, and with it the last bits of y, can differ from run to run.
- * The kernel is chosen by B: up to 40 rows a segment-parallel kernel, above
- * that one that merges each decoded tile once into a BF16 tile in LDS shared
- * by all batch tiles (two row blocks per workgroup above 112 rows); w_debug
- * calls up to 32 rows, and weights whose segments are too large for the
- * segment-parallel kernel's staging, take a tile-synchronous kernel
- * (df11_decode_gemm_ex makes the choice explicit).
+ * The kernel is chosen by B: one or two rows a kernel that forms the
+ * products as dot products on the vector ALU, up to 40 rows a
+ * segment-parallel kernel on the matrix cores, above that one that merges
+ * each decoded tile once into a BF16 tile in LDS shared by all batch tiles
+ * (two row blocks per workgroup above 112 rows); w_debug calls up to 32
+ * rows, and weights whose segments are too large for the segment-parallel
+ * kernel's staging, take a tile-synchronous kernel (df11_decode_gemm_ex
+ * makes the choice explicit).
  * Non-finite x: a row of x holding Inf or NaN gives a non-finite row of y;
  * where a plain product would give +-Inf, y may hold NaN instead (the
- * segment-parallel kernel multiplies the weights of a neighbouring segment,
- * masked to +0, by the same x).  Rows of x without them are unaffected.
+ * segment-parallel and vector kernels multiply the weights of a
+ * neighbouring segment, masked to +0, by the same x).  Rows of x without
+ * them are unaffected.
  * Errors: E_ARG (null, misaligned, layout not from df11_gemm_layout, B out
  * of range), E_UNSUPPORTED, E_DEVICE. */
 int df11_decode_gemm(const df11_view *device_view, const uint16_t *x, uint32_t B,
@@ -350,11 +353,12 @@ int df11_decode_gemm_out(const df11_view *device_view, const uint16_t *x, uint32
 #define DF11_GEMM_SEGMENT 1   /* segment-parallel: up to 64 rows of x, no w_debug */
 #define DF11_GEMM_WIDE 2      /* one BF16 tile in LDS shared by the batch tiles: 33 rows of x or more */
 #define DF11_GEMM_TILED 3     /* tile-synchronous, any rows of x */
+#define DF11_GEMM_VECTOR 4    /* dot products on the vector ALU: one or two rows of x, no w_debug */
 typedef struct df11_gemm_tuning {
     uint32_t kernel;       /* DF11_GEMM_* */
     uint32_t row_blocks;   /* wide kernel: 0 = by B, else 1 or 2 row blocks per workgroup */
-    uint32_t parts;        /* segment-parallel kernel: 0 = enough runs of a row block's segments to
-                              fill the device, else that many (float32 y) */
+    uint32_t parts;        /* segment-parallel and vector kernels: 0 = enough runs of a row block's
+                              segments to fill the device, else that many (float32 y) */
     uint32_t split;        /* wide and tile-synchronous kernels: 0 = by occupancy, else that many K
                               ranges per row block (float32 y) */
     uint32_t reserved[4];  /* zero */
@@ -380,8 +384,9 @@ uint64_t df11_decode_gemm_workspace_bytes(const df11_view *device_view, uint32_t
  * 64 / 128 / 256 rows: 68 / 91 / 117 us in place, 57 / 70 / 96 us packed).
  * y agrees with every choice within the float32 summation order.  Errors:
  * as df11_decode_gemm_out, E_ARG for a choice that does not apply (w_debug
- * or more than 64 rows of x on the segment-parallel kernel, 32 rows or fewer
- * on the wide one, parts or split above 1 with a BF16 y) or a workspace too
+ * or more than 64 rows of x on the segment-parallel kernel, w_debug or more
+ * than 2 rows on the vector one, 32 rows or fewer on the wide one, parts or
+ * split above 1 with a BF16 y) or a workspace too
  * small or misaligned, E_UNSUPPORTED when the chosen kernel's LDS does not
  * fit this weight. */
 int df11_decode_gemm_ex(const df11_view *device_view, const uint16_t *x, uint32_t B, void *y, int y_dtype,

@@ -2,7 +2,9 @@
 the C ABI: the decoded weights are bit-exact against the input (w_debug), and
 y matches the oracle's float32 product within 2e-3 relative Frobenius error
 (float32 accumulation differs only in summation order; BF16 products are
-exact).  Up to 40 rows of x take the segment-parallel kernel (one batch
+exact).  One or two rows of x take the vector kernel (dot products on the
+vector ALU, no w_debug: its decode is checked through y with identity rows
+of x, at full up_proj size).  Up to 40 rows of x take the segment-parallel kernel (one batch
 tile of 32 rows up to 32, two above), which has no w_debug output: its
 decode is checked bit-exactly through y with x = rows of the identity.
 Above 40 rows (and for w_debug calls above 32) the wide kernel merges each
@@ -412,9 +414,12 @@ def test_sparse_weights_take_a_kernel_whose_staging_fits(kind, B):
             assert (got == 0).all()
         else:
             assert _rel(got, ref) < TOL
-    with pytest.raises(_lib.DF11Error) as ei:
-        api.decode_gemm(enc.to("cuda"), _x_to_gpu(X), tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_SEGMENT))
-    assert ei.value.status == -7
+    for code in (_lib.DF11_GEMM_SEGMENT, _lib.DF11_GEMM_VECTOR):
+        if code == _lib.DF11_GEMM_VECTOR and B > 2:
+            continue
+        with pytest.raises(_lib.DF11Error) as ei:
+            api.decode_gemm(enc.to("cuda"), _x_to_gpu(X), tuning=api.gemm_tuning(kernel=code))
+        assert ei.value.status == -7
 
 
 @pytest.mark.parametrize("kernel", ["auto", "tiled"])
@@ -441,15 +446,17 @@ def test_nonfinite_x_row(kernel):
 
 @pytest.mark.parametrize("kernel,B,extra", [("segment", 8, dict(parts=2)), ("segment", 40, dict()),
                                             ("tiled", 8, dict(split=3)), ("wide", 64, dict(split=2)),
-                                            ("wide", 100, dict(row_blocks=2))])
+                                            ("wide", 100, dict(row_blocks=2)), ("vector", 1, dict()),
+                                            ("vector", 2, dict()), ("vector", 2, dict(parts=3))])
 def test_explicit_kernel_choices_agree(kernel, B, extra):
     """Every explicit kernel choice (tuning) gives the oracle's product."""
     N, K = 256, 4096
     _say("case gemm tuning %s B=%d %s" % (kernel, B, extra))
     W = synth.normal_bf16(N * K, 0.02, seed=82).reshape(N, K)
     X = synth.activations_bf16(B, K, seed=83)
-    code = {"segment": _lib.DF11_GEMM_SEGMENT, "tiled": _lib.DF11_GEMM_TILED, "wide": _lib.DF11_GEMM_WIDE}[kernel]
-    y, wd, yd = _run(W, X, with_debug=kernel != "segment", tuning=api.gemm_tuning(kernel=code, **extra))
+    code = {"segment": _lib.DF11_GEMM_SEGMENT, "tiled": _lib.DF11_GEMM_TILED, "wide": _lib.DF11_GEMM_WIDE,
+            "vector": _lib.DF11_GEMM_VECTOR}[kernel]
+    y, wd, yd = _run(W, X, with_debug=kernel not in ("segment", "vector"), tuning=api.gemm_tuning(kernel=code, **extra))
     ref = orc.gemm_f64(X, W)
     assert _rel(y, ref) < TOL
     if wd is not None:
@@ -499,3 +506,52 @@ def test_identity_x_recovers_up_proj_packed_x(rows):
     want = (torch.from_numpy(W.view(np.int16)).cuda().to(torch.int32) << 16)
     bad = int((got.contiguous().view(torch.int32) != want).sum())
     assert bad == 0, "%d of %d weights differ" % (bad, N * K)
+
+
+@pytest.mark.parametrize("rows", [1, 2])
+def test_identity_x_recovers_up_proj_vector_kernel(rows):
+    """Wup 14336 x 4096 through the vector kernel, the product path at one
+    and two rows of x (no tuning): x = identity rows, 4096 / rows calls, and
+    every one of the 58,720,256 weights comes back through y bit for bit
+    (one nonzero dot-product term per output, masked neighbours +0)."""
+    N, K = 14336, 4096
+    _say("case gemm identity up_proj vector kernel rows=%d" % rows)
+    W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
+    assert ((W & 0x7FFF) != 0).all()
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    got = _identity_recover_on_gpu(dt, N, K, rows)
+    want = (torch.from_numpy(W.view(np.int16)).cuda().to(torch.int32) << 16)
+    bad = int((got.contiguous().view(torch.int32) != want).sum())
+    assert bad == 0, "%d of %d weights differ" % (bad, N * K)
+
+
+def test_vector_kernel_refuses_what_it_does_not_take():
+    """The vector kernel takes one or two rows of x and no w_debug: an
+    explicit request for more rows, or with w_debug, is an argument error."""
+    N, K = 64, 1024
+    W = synth.normal_bf16(N * K, 0.02, seed=84).reshape(N, K)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    tune = api.gemm_tuning(kernel=_lib.DF11_GEMM_VECTOR)
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.decode_gemm(dt, _x_to_gpu(synth.activations_bf16(3, K, seed=85)), tuning=tune)
+    assert ei.value.status == -1
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(_lib.DF11Error) as ei:
+        api.decode_gemm(dt, _x_to_gpu(synth.activations_bf16(1, K, seed=85)), w_debug=wdbg, tuning=tune)
+    assert ei.value.status == -1
+    torch.cuda.synchronize()
+
+
+def test_vector_kernel_nonfinite_x_row():
+    """Two rows of x, the second holding +Inf: the first row of y is as the
+    oracle's, the second non-finite everywhere (NaN where masked neighbours
+    meet the Inf, as with the segment-parallel kernel)."""
+    N, K = 96, 1536
+    _say("case gemm vector nonfinite x")
+    W = synth.normal_bf16(N * K, 0.02, seed=86).reshape(N, K)
+    X = synth.activations_bf16(2, K, seed=87)
+    X[1, 700] = 0x7F80
+    ref = orc.gemm_f64(X, W)
+    y, _, _ = _run(W, X, with_debug=False)
+    assert not np.isfinite(y[1]).any()
+    assert _rel(y[:1], ref[:1]) < TOL

@@ -97,6 +97,9 @@ def test_fused_segment_kernel_refused_when_staging_exceeds_64k(kind):
     for B in (1, 33):
         rc, msg = _gemm_call(e.view, B, api.gemm_tuning(kernel=_lib.DF11_GEMM_SEGMENT))
         assert rc == -7 and "staging" in msg, msg
+    # the vector kernel (one or two rows of x) keeps the same staging, 8 or 12 waves
+    rc, msg = _gemm_call(e.view, 1, api.gemm_tuning(kernel=_lib.DF11_GEMM_VECTOR))
+    assert rc == -7 and "staging" in msg, msg
 
 
 @pytest.mark.parametrize("B,tune,bf16,wd", [
@@ -107,7 +110,10 @@ def test_fused_segment_kernel_refused_when_staging_exceeds_64k(kind):
     (8, dict(parts=2), False, False),                               # parts without the segment kernel
     (8, dict(kernel=_lib.DF11_GEMM_SEGMENT, parts=2), True, False), # BF16 y: one writer per element
     (64, dict(kernel=_lib.DF11_GEMM_WIDE, split=2), True, False),
-    (8, dict(kernel=4), False, False),
+    (3, dict(kernel=_lib.DF11_GEMM_VECTOR), False, False),          # the vector kernel takes 1 or 2 rows
+    (1, dict(kernel=_lib.DF11_GEMM_VECTOR), False, True),           # and no w_debug
+    (2, dict(kernel=_lib.DF11_GEMM_VECTOR, parts=2), True, False),  # BF16 y: one writer per element
+    (8, dict(kernel=5), False, False),                              # no such kernel
 ])
 def test_fused_refuses_choices_that_do_not_apply(B, tune, bf16, wd):
     N, K = 64, 1024
