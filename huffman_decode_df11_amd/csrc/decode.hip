@@ -52,7 +52,19 @@ template <> struct Chunk<16> { typedef uint4 words_t; };
 template <> struct Chunk<8> { typedef uint2 words_t; };
 template <int CB> constexpr uint32_t chunk_bits() { return 8u * CB; }
 template <int CB> constexpr uint32_t seg_words() { return 64u * CB / 4u; }
-constexpr int kPrefetchRounds = 5;   // 8-element units per lane prefetched before the decode
+// Rounds of 8-element units per lane whose sign+mantissa bytes are loaded
+// before the decode.  A 16-byte-chunk segment of Gaussian-like weights holds
+// ~2,800-3,200 elements, 6-7 rounds: the rounds after the prefetched ones
+// are loaded after the decode, one exposed round trip, which costs most
+// where each wave takes a single segment (a 16M-element tensor: 17.2 us
+// with 5, 15.6 with 6; 7 spills registers at 8 waves per SIMD, 16.9).  An
+// 8-byte-chunk segment holds ~1,400 elements, 3 rounds (5 kept: 3 measured
+// no faster).
+template <int CB>
+constexpr int prefetch_rounds()
+{
+    return CB == 16 ? 6 : 5;
+}
 
 struct ViewArgs {
     const uint32_t *words;
@@ -210,17 +222,18 @@ __device__ __forceinline__ SegPlan plan_segment(const SegLoad<CB> &cur, uint64_t
     return df11plan::plan_segment(cur.g0, cur.g1, n, stg_bytes);
 }
 
-// the segment's sign+mantissa bytes for the first kPrefetchRounds rounds of
+// the segment's sign+mantissa bytes for the first PR rounds of
 // units.  Lanes past the last unit load the last unit again (an address
 // that is always inside the array), so no value has to be selected and the
 // loads stay in flight during the decode.
+template <int PR>
 __device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm, uint32_t lane, bool stream,
-                                            uint2 (&smp)[kPrefetchRounds])
+                                            uint2 (&smp)[PR])
 {
     const uint32_t last = p.nunits ? p.nunits - 1 : 0u;
     const uint64_t base = p.nunits ? p.gbase : 0ull;
 #pragma unroll
-    for (int r = 0; r < kPrefetchRounds; r++)
+    for (int r = 0; r < PR; r++)
         smp[r] = load_sm8(sm + base + 8ull * min(lane + 64u * r, last), stream);
 }
 
@@ -289,8 +302,8 @@ __device__ __forceinline__ RaggedLane ragged_lane(uint64_t lo, uint64_t hi, uint
 // 16-byte stores (the first rounds from the prefetched bytes), the ragged
 // ends one element per lane from rag_sm, the lane's ragged element's
 // sign+mantissa byte (loaded by the caller).
-template <class Out>
-__device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint64_t hi, const uint2 (&smp)[kPrefetchRounds],
+template <class Out, int PR>
+__device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint64_t hi, const uint2 (&smp)[PR],
                                             uint32_t rag_sm, const uint8_t *sm, const Out &out, uint32_t stg, uint32_t lane,
                                             bool stream)
 {
@@ -302,8 +315,8 @@ __device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint6
         *out.at(rg.g) = assemble1(rag_sm, rx);
     }
 #pragma unroll
-    for (int r = 0; r < kPrefetchRounds; r++) merge_unit(p, lo, hi, lane + 64u * r, smp[r], out, stg, stream);
-    for (uint32_t r = kPrefetchRounds; 64u * r < p.nunits; r++) {
+    for (int r = 0; r < PR; r++) merge_unit(p, lo, hi, lane + 64u * r, smp[r], out, stg, stream);
+    for (uint32_t r = PR; 64u * r < p.nunits; r++) {
         const uint32_t ui = lane + 64u * r;
         const uint2 smv = ui < p.nunits ? load_sm8(sm + p.gbase + 8ull * ui, stream) : make_uint2(0, 0);
         merge_unit(p, lo, hi, ui, smv, out, stg, stream);
@@ -422,7 +435,7 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
         const bool more = s_next < n_total;
         const uint32_t vi_next = more ? view_of(b, s_next, vi) : vi;
         nx = load_segment<CB>(b.v[vi_next], (more ? s_next : s) - b.seg_begin[vi_next], lane);
-        uint2 smp[kPrefetchRounds];
+        uint2 smp[prefetch_rounds<CB>()];
         uint2 tsv[TILE8 ? 8 : 1];
         TileSeg q{};
         bool tiled = false;
@@ -577,7 +590,7 @@ decode_rows_kernel(RowArgs a, TableArgs t)
             const SegLoad<CB> cur = head && s == it.s ? first : load_segment<CB>(v, s, lane);
             if (cur.g0 >= hi) break;
             const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
-            uint2 smp[kPrefetchRounds];
+            uint2 smp[prefetch_rounds<CB>()];
             prefetch_sm(p, v.sm, lane, false, smp);
             const uint64_t mlo = max(lo, p.g0), mhi = min(hi, p.g1);
             const RaggedLane rg = ragged_lane(mlo, mhi, lane);
