@@ -394,7 +394,8 @@ def encode_rate(seed: int = 0):
 
 def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8, rows: int = 14336):
     """df11_decode_gemm on the up_proj weight (14336 x 4096; or its first
-    `rows` rows, one GPU's share of a row split) for B in {1, 8, 64, 256},
+    `rows` rows, one GPU's share of a row split) for B in {1, 8, 64, 256}
+    (and 2, 32, 128),
     next to torch.matmul on the BF16 weight and to the unfused path
     (df11_decode of a row-major encoding, then torch.matmul).  Every variant
     cycles through `copies` copies of its weight (> 256 MB in all), so
@@ -426,7 +427,7 @@ def fused_up_proj(steps: int, warmup: int, seed: int = 0, copies: int = 8, rows:
         return a.elapsed_time(b) / steps
 
     by_b = {}
-    for B in (1, 8, 32, 64, 128, 256):
+    for B in (1, 2, 8, 32, 64, 128, 256):
         X = synth.activations_bf16(B, K, seed=1)
         x = torch.from_numpy(X.view(np.int16)).cuda().view(torch.bfloat16)
         y = torch.empty(B, N, dtype=torch.float32, device="cuda")
@@ -498,12 +499,37 @@ def other_configs(steps: int, warmup: int, seed: int = 0):
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / n_launch
         alg = algorithmic_bytes(dts[0])
+        copy_us = _copy_same_traffic_us(alg, copies, n_launch)
         out[name] = {"elements": int(u.size), "us_per_launch": round(ms * 1e3, 2),
                      "decoded_gbs": round(2.0 * u.size / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "copy_same_traffic_us": round(copy_us, 2),
+                     "copy_same_traffic_hbm_frac": round(alg / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "bits_per_weight": round(enc.compressed_nbytes() * 8.0 / u.size, 3),
                      "chunk_bytes": chunk, "copies_cycled": copies}
     return out
+
+
+def _copy_same_traffic_us(alg_bytes: int, copies: int, n: int) -> float:
+    """A plain device copy moving the same bytes as one decode launch (reads
+    alg/2, writes alg/2), timed the same way (back-to-back calls behind a
+    spin kernel, `copies` sources cycled): what HBM gives a kernel of this
+    size with no decoding at all."""
+    import torch
+    nb = max(16, int(alg_bytes // 2) // 16 * 16)
+    srcs = [torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(i) for i in range(copies)]
+    dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for i in range(copies):
+        dst.copy_(srcs[i])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _hold_queue(2.0 + 0.05 * n)
+    a.record()
+    for i in range(n):
+        dst.copy_(srcs[i % copies])
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n * 1e3
 
 
 def embedding_lookup(steps: int, warmup: int, seed: int = 0, vocab: int = 128256, dim: int = 4096):

@@ -57,13 +57,15 @@ template <int CB> constexpr uint32_t seg_words() { return 64u * CB / 4u; }
 // ~2,800-3,200 elements, 6-7 rounds: the rounds after the prefetched ones
 // are loaded after the decode, one exposed round trip, which costs most
 // where each wave takes a single segment (a 16M-element tensor: 17.2 us
-// with 5, 15.6 with 6; 7 spills registers at 8 waves per SIMD, 16.9).  An
-// 8-byte-chunk segment holds ~1,400 elements, 3 rounds (5 kept: 3 measured
-// no faster).
-template <int CB>
+// with 5, 15.6 with 6; 7 spills registers at 8 waves per SIMD, 16.9).  The
+// sixth round costs one spilled register, which a launch that streams more
+// output than the Infinity Cache holds pays for (the 8B model pass: 5.52 ms
+// with 5 rounds, 5.80 with 6), so those launches keep 5.  An 8-byte-chunk
+// segment holds ~1,400 elements, 3 rounds (5 kept: 3 measured no faster).
+template <int CB, bool STREAM = false>
 constexpr int prefetch_rounds()
 {
-    return CB == 16 ? 6 : 5;
+    return CB == 16 && !STREAM ? 6 : 5;
 }
 
 struct ViewArgs {
@@ -392,7 +394,7 @@ __device__ __forceinline__ void merge_tile_groups8(const SegPlan &p, const ViewA
 }
 
 // ------------------------------------------------------------ kernels
-template <int K, int WAVES, bool TILE8, int CB>
+template <int K, int WAVES, bool TILE8, int CB, int PR>
 __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs &t)
 {
     extern __shared__ __align__(16) uint8_t lds_raw[];
@@ -435,7 +437,7 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
         const bool more = s_next < n_total;
         const uint32_t vi_next = more ? view_of(b, s_next, vi) : vi;
         nx = load_segment<CB>(b.v[vi_next], (more ? s_next : s) - b.seg_begin[vi_next], lane);
-        uint2 smp[prefetch_rounds<CB>()];
+        uint2 smp[PR];
         uint2 tsv[TILE8 ? 8 : 1];
         TileSeg q{};
         bool tiled = false;
@@ -467,16 +469,17 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
     }
 }
 
-// Two kernels from one body, both at 8 waves per SIMD (64 VGPRs): the
-// row-major one, and one with the tile-order merge for launches that hold
-// such a view (its prefetch and bookkeeping spill a few registers, which
-// costs less than fewer waves: 55 us against 61 us at 7 waves per SIMD on
-// up_proj), so that the row-major kernel stays free of spills.
-template <int K, int WAVES, int CB>
+// Kernels from one body, all at 8 waves per SIMD (64 VGPRs): the row-major
+// one (PR prefetched rounds: 6 for 16-byte chunks, 5 in the form for
+// streaming launches and for 8-byte chunks), and one with the tile-order
+// merge for launches that hold such a view (its prefetch and bookkeeping
+// spill a few registers, which costs less than fewer waves: 55 us against
+// 61 us at 7 waves per SIMD on up_proj).
+template <int K, int WAVES, int CB, int PR>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
 decode_kernel(BatchArgs b, TableArgs t)
 {
-    decode_body<K, WAVES, false, CB>(b, t);
+    decode_body<K, WAVES, false, CB, PR>(b, t);
 }
 
 // (the fused kernel's layout always has 16-byte chunks)
@@ -485,7 +488,7 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
 decode_kernel_t8(BatchArgs b, TableArgs t)
 {
     static_assert(CB == 16, "tile-order views are encoded with 16-byte chunks");
-    decode_body<K, WAVES, true, CB>(b, t);
+    decode_body<K, WAVES, true, CB, prefetch_rounds<CB, true>()>(b, t);
 }
 
 // Row gather: up to eight waves per requested row (as many as the segments
@@ -692,13 +695,14 @@ uint32_t lds_bytes(int waves, uint32_t stg, uint32_t fast_bits, uint32_t n_table
 }
 
 // The kernel of a launch: KIND 0 row-major decode, 1 its tile-order form,
-// 2 the row gather.
+// 2 the row gather, 3 the row-major decode of a streaming launch.
 template <int K, int W, int CB, int KIND>
 constexpr auto kernel_of()
 {
-    if constexpr (KIND == 0) return decode_kernel<K, W, CB>;
+    if constexpr (KIND == 0) return decode_kernel<K, W, CB, prefetch_rounds<CB>()>;
     else if constexpr (KIND == 1) return decode_kernel_t8<K, W, CB>;
-    else return decode_rows_kernel<K, W, CB>;
+    else if constexpr (KIND == 2) return decode_rows_kernel<K, W, CB>;
+    else return decode_kernel<K, W, CB, prefetch_rounds<CB, true>()>;
 }
 
 constexpr int kWaveChoices[] = {4, 6, 8, 10, 12, 14, 16};
@@ -874,6 +878,8 @@ int launch_decode(const BatchArgs &a, const TableArgs &t, const df11_view *v, co
     const uint64_t nseg = a.seg_begin[a.count];
     if constexpr (CB == 16)
         if (t8) return launch_kind<K, CB, 1>(a, t, v, nseg, tune.waves, tune.groups, st);
+    if constexpr (CB == 16)
+        if (a.stream) return launch_kind<K, CB, 3>(a, t, v, nseg, tune.waves, tune.groups, st);
     return launch_kind<K, CB, 0>(a, t, v, nseg, tune.waves, tune.groups, st);
 }
 
