@@ -50,10 +50,10 @@ class View(ctypes.Structure):
         ("chunk_bytes", u32), ("seg_lanes", u32),
         ("rows", u64), ("cols", u64),
         ("tile_rows", u32), ("tile_cols", u32),
-        ("tile_kchunk", u32), ("reserved0", u32),
+        ("tile_kchunk", u32), ("row_win_lo", ctypes.c_int32),
         ("align_elems", u64),
         ("min_len", u32), ("max_len", u32), ("n_tables", u32), ("fast_bits", u32),
-        ("max_seg_elems", u32), ("reserved", u32),
+        ("max_seg_elems", u32), ("row_win_span", u32),
         ("exp_words", ctypes.c_void_p), ("n_exp_words", u64),
         ("sm", ctypes.c_void_p), ("n_sm", u64),
         ("gaps", ctypes.c_void_p), ("n_gaps", u64),

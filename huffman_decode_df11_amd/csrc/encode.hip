@@ -36,6 +36,8 @@ struct df11_device_encoded {
     uint64_t n = 0, total_bits = 0, n_segments = 0;
     df11_layout layout{};
     uint32_t min_len = 0, max_len = 0, n_tables = 0, fast_bits = 0, max_seg_elems = 0;
+    int32_t row_win_lo = 0;
+    uint32_t row_win_span = 0;
     uint32_t *exp_words = nullptr;
     uint8_t *sm = nullptr;
     uint8_t *gaps = nullptr;
@@ -558,6 +560,19 @@ extern "C" int df11_encode_device(const uint16_t *bits, uint64_t n, const df11_c
         HIP_TRY(hipGetLastError(), "segment max launch");
         HIP_TRY(hipMemcpyAsync(&d->max_seg_elems, dmax, 4, hipMemcpyDeviceToHost, st), "max copy");
         HIP_TRY(hipStreamSynchronize(st), "encode sync");
+        if (L.rows && L.cols && !L.tile_rows) {
+            // the row window from the records, computed as the host encoder does
+            std::vector<df11_segment> hs;
+            try {
+                hs.resize(d->n_segs);
+            } catch (...) {
+                return df11::fail(DF11_E_ALLOC, "out of host memory");
+            }
+            HIP_TRY(hipMemcpyAsync(hs.data(), d->segs, d->n_segs * sizeof(df11_segment), hipMemcpyDeviceToHost, st),
+                    "segment records");
+            HIP_TRY(hipStreamSynchronize(st), "encode sync");
+            df11::row_window(hs.data(), nseg, n, L, &d->row_win_lo, &d->row_win_span);
+        }
     } else {
         HIP_TRY(hipStreamSynchronize(st), "encode sync");
     }
@@ -588,6 +603,8 @@ extern "C" int df11_device_encoded_view(const df11_device_encoded *d, df11_view 
     v->n_tables = d->n_tables;
     v->fast_bits = d->fast_bits;
     v->max_seg_elems = d->max_seg_elems;
+    v->row_win_lo = d->row_win_lo;
+    v->row_win_span = d->row_win_span;
     v->exp_words = d->exp_words;  v->n_exp_words = d->n_exp_words;
     v->sm = d->sm;                v->n_sm = d->n_sm;
     v->gaps = d->gaps;            v->n_gaps = d->n_gaps;
@@ -627,6 +644,8 @@ extern "C" int df11_device_encoded_to_host(const df11_device_encoded *d, df11_en
     h->n_tables = d->n_tables;
     h->fast_bits = d->fast_bits;
     h->max_seg_elems = d->max_seg_elems;
+    h->row_win_lo = d->row_win_lo;
+    h->row_win_span = d->row_win_span;
     struct { void *dst; const void *src; uint64_t bytes; } parts[] = {
         {h->exp_words.data(), d->exp_words, d->n_exp_words * 4}, {h->sm.data(), d->sm, d->n_sm},
         {h->gaps.data(), d->gaps, d->n_gaps}, {h->segs.data(), d->segs, d->n_segs * sizeof(df11_segment)},

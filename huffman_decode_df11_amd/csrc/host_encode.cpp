@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <new>
 #include <string>
@@ -261,8 +262,33 @@ extern "C" int df11_encode(const uint16_t *bits, uint64_t n, const df11_codebook
         const uint64_t c = segs[s + 1].elem_off - segs[s].elem_off;
         if (c > enc->max_seg_elems) enc->max_seg_elems = (uint32_t)c;
     }
+    df11::row_window(segs, nseg, n, enc->layout, &enc->row_win_lo, &enc->row_win_span);
     *out = enc;
     return DF11_OK;
+}
+
+void df11::row_window(const df11_segment *segs, uint64_t n_segments, uint64_t n, const df11_layout &L, int32_t *lo,
+                      uint32_t *span)
+{
+    *lo = 0;
+    *span = 0;
+    if (!n || !n_segments || !L.rows || !L.cols || L.tile_rows || L.rows * L.cols != n) return;
+    const double ratio = (double)n_segments / (double)n;
+    int64_t lo_min = INT64_MAX, hi_max = INT64_MIN;
+    uint64_t s0 = 0, s1 = 0;   // last segment starting at or before the row's first / last element
+    for (uint64_t r = 0; r < L.rows; r++) {
+        const uint64_t e0 = r * L.cols, e1 = e0 + L.cols - 1;
+        while (s0 + 1 < n_segments && segs[s0 + 1].elem_off <= e0) s0++;
+        if (s1 < s0) s1 = s0;
+        while (s1 + 1 < n_segments && segs[s1 + 1].elem_off <= e1) s1++;
+        const int64_t g = (int64_t)std::floor((double)e0 * ratio);
+        lo_min = std::min(lo_min, (int64_t)s0 - g);
+        hi_max = std::max(hi_max, (int64_t)s1 - g);
+    }
+    const int64_t w = hi_max - lo_min + 1;
+    if (lo_min < INT32_MIN || lo_min > INT32_MAX || w < 1 || w > (int64_t)UINT32_MAX) return;
+    *lo = (int32_t)lo_min;
+    *span = (uint32_t)w;
 }
 
 extern "C" void df11_encoded_free(df11_encoded *enc) { delete enc; }
@@ -287,6 +313,8 @@ extern "C" int df11_encoded_view(const df11_encoded *enc, df11_view *v)
     v->n_tables = enc->n_tables;
     v->fast_bits = enc->fast_bits;
     v->max_seg_elems = enc->max_seg_elems;
+    v->row_win_lo = enc->row_win_lo;
+    v->row_win_span = enc->row_win_span;
     v->exp_words = enc->exp_words.data();  v->n_exp_words = enc->exp_words.size();
     v->sm = enc->sm.data();                v->n_sm = enc->sm.size();
     v->gaps = enc->gaps.data();            v->n_gaps = enc->gaps.size();

@@ -145,11 +145,18 @@ typedef struct df11_view {
     uint32_t chunk_bytes, seg_lanes;
     uint64_t rows, cols;
     uint32_t tile_rows, tile_cols;
-    uint32_t tile_kchunk, reserved0;
+    uint32_t tile_kchunk;
+    int32_t row_win_lo;         /* row window (see below) */
     uint64_t align_elems;
     uint32_t min_len, max_len, n_tables, fast_bits;
     uint32_t max_seg_elems;     /* most codes starting in any one segment */
-    uint32_t reserved;
+    uint32_t row_win_span;      /* row window: 0 = none.  For a row-major view with rows and
+                                   cols set, both encoders record the window that holds every
+                                   segment overlapping any row r: with g(r) = floor(r * cols *
+                                   (n_segments / n)), the segment indices in IEEE double
+                                   arithmetic (the quotient first), row r's segments lie in
+                                   [g(r) + row_win_lo, g(r) + row_win_lo + row_win_span).
+                                   df11_decode_rows relies on it as written by the encoder. */
     const uint32_t *exp_words;  uint64_t n_exp_words;  /* n_segments*seg_words + 2 */
     const uint8_t *sm;          uint64_t n_sm;         /* n rounded up to 16 */
     const uint8_t *gaps;        uint64_t n_gaps;       /* n_segments * seg_lanes */
@@ -294,11 +301,14 @@ int df11_decode_batch_tuned(const df11_view *device_views, uint16_t *const *outs
  * into out[i][0..cols) (device, 16-byte aligned, n_rows x cols BF16), for
  * an embedding lookup that restores only the rows a batch uses ([P1] 2.2
  * item 3: weights are restored right before use).  rows: device int64 ids,
- * 8-byte aligned.  The segments that overlap each requested row are found
- * from an interpolated guess, checked against the 64 segment records around
- * it, else by a 64-way search, and decoded whole (up to eight waves per
- * row, one segment each; 8-byte chunks halve the segments and with them the
- * latency of a lookup); only the row's elements are written.  An id outside
+ * 8-byte aligned.  For a few rows whose view records a row window of at
+ * most 16 segments (row_win_span), every segment of the window gets its own
+ * wave, so no search precedes the segment loads; otherwise the segments that
+ * overlap each requested row are found from an interpolated guess, checked
+ * against the 64 segment records around it, else by a 64-way search (up to
+ * eight waves per row, one segment each).  Segments are decoded whole
+ * (8-byte chunks halve the segments and with them the latency of a lookup);
+ * only the row's elements are written.  An id outside
  * [0, rows) leaves its output row unwritten.  Bit-exact like df11_decode.  Errors: E_ARG (null, misaligned,
  * tile-ordered view, cols not a multiple of 8), E_UNSUPPORTED, E_DEVICE. */
 int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t n_rows, uint16_t *out,

@@ -32,7 +32,8 @@ def _same(h, d):
         assert a.size == b.size, name
         bad = np.nonzero(a != b)[0]
         assert bad.size == 0, "%s differs at byte %d" % (name, bad[0])
-    for f in ("n", "total_bits", "n_segments", "max_seg_elems", "min_len", "max_len", "n_tables", "fast_bits"):
+    for f in ("n", "total_bits", "n_segments", "max_seg_elems", "min_len", "max_len", "n_tables", "fast_bits",
+              "row_win_lo", "row_win_span"):
         assert getattr(h.view, f) == getattr(d.view, f), f
 
 
@@ -145,3 +146,20 @@ def test_device_encoder_matches_oracle(name, lay):
     hist = orc.histogram(u)
     cost = lambda lens: int(sum(int(h) * int(l) for h, l in zip(hist, lens)))
     assert cost(ln) == cost(orc.code_lengths(hist, 32))
+
+
+@pytest.mark.parametrize("chunk", [8, 16])
+def test_device_encoder_row_window(chunk):
+    """A row-major table with rows and cols set: the GPU encoder records the
+    same row window (row_win_lo, row_win_span) as the host encoder, with
+    every other array byte-identical."""
+    rows, cols = 4096, 4096
+    _say("case encode_device row window chunk %d" % chunk)
+    u = synth.normal_bf16(rows * cols, 0.02, seed=57).reshape(rows, cols)
+    layout = api.make_layout(rows=rows, cols=cols, chunk_bytes=chunk)
+    cb = api.build_codebook(api.hist_accumulate(u))
+    h = api.encode(u, codebook=cb, layout=layout)
+    d = api.encode_device(_dev(u.reshape(-1)), codebook=cb, layout=layout)
+    assert h.view.row_win_span > 0
+    _same(h, d.to_host())
+    assert (d.view.row_win_lo, d.view.row_win_span) == (h.view.row_win_lo, h.view.row_win_span)

@@ -78,6 +78,31 @@ def test_decode_rows_adversarial_and_bad_ids():
         assert (o[k] == 0x5555).all()
 
 
+@pytest.mark.parametrize("chunk", [8, 16])
+def test_decode_rows_window_and_search_agree(chunk):
+    """A few ids take the window mode (every segment of the row's recorded
+    window loaded with no search before it); the same view with its window
+    field cleared takes the segment search.  Both give the rows bit for bit,
+    including the first and last rows of the table."""
+    rows, cols = 4096, 4096
+    _say("case decode_rows window/search chunk %d" % chunk)
+    W = synth.normal_bf16(rows * cols, 0.02, seed=41).reshape(rows, cols)
+    dt = api.encode(W, layout=api.make_layout(rows=rows, cols=cols, chunk_bytes=chunk)).to("cuda")
+    assert 0 < dt.view.row_win_span <= 16
+    ids = torch.from_numpy(np.array([0, rows - 1, 1, 2047, 3000, 17, 17], np.int64)).cuda()
+    got_win = api.decode_rows(dt, ids)
+    span = dt.view.row_win_span
+    dt.view.row_win_span = 0
+    try:
+        got_search = api.decode_rows(dt, ids)
+    finally:
+        dt.view.row_win_span = span
+    torch.cuda.synchronize()
+    want = _i16(W[ids.cpu().numpy()])
+    assert torch.equal(got_win.view(torch.int16), want)
+    assert torch.equal(got_search.view(torch.int16), want)
+
+
 def test_decode_rows_rejects_tile_order():
     from huffman_decode_df11_amd import _lib
     W = synth.normal_bf16(64 * 512, 0.02, seed=33).reshape(64, 512)

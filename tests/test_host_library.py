@@ -313,3 +313,42 @@ def test_c_api_program_host_half():
     r = subprocess.run([b.C_API_CHECK, "--host-only"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("c-api ok (host only)")
+
+
+@pytest.mark.parametrize("chunk,rows,cols,kind", [(8, 600, 512, "normal"), (16, 600, 512, "normal"),
+                                                   (8, 97, 1032, "skewed"), (16, 1, 4096, "normal"),
+                                                   (16, 3000, 8, "normal")])
+def test_row_window_matches_oracle_segments(chunk, rows, cols, kind):
+    """The row window of a row-major encoding (df11_view row_win_lo and
+    row_win_span) against the oracle's segment offsets on the same code:
+    with g(r) = floor(r * cols * (segments / n)) in float64, every segment
+    that overlaps row r (from the one holding the row's first element to the
+    one holding its last) lies in [g + lo, g + lo + span), and the window is
+    the tightest such (both ends reached by some row).  "skewed" rows differ
+    tenfold in scale, so segments hold very different element counts."""
+    n = rows * cols
+    if kind == "normal":
+        u = synth.normal_bf16(n, 0.02, seed=60).reshape(rows, cols)
+    else:
+        u = synth.normal_bf16(n, 0.02, seed=61).reshape(rows, cols)
+        u[: rows // 2] = synth.adversarial_bf16(cols * (rows // 2), seed=62).reshape(rows // 2, cols)
+    enc = api.encode(u, layout=api.make_layout(rows=rows, cols=cols, chunk_bytes=chunk))
+    ref = orc.encode(u, lengths=api.codebook_lengths(enc.codebook), chunk_bytes=chunk, seg_lanes=64)
+    nseg = ref.n_segments
+    assert enc.n_segments == nseg
+    starts = np.asarray(ref.seg_elem[:nseg], np.int64)
+    e0 = np.arange(rows, dtype=np.int64) * cols
+    first = np.searchsorted(starts, e0, side="right") - 1
+    last = np.searchsorted(starts, e0 + cols - 1, side="right") - 1
+    g = np.floor(e0.astype(np.float64) * (float(nseg) / float(n))).astype(np.int64)
+    lo, span = int(enc.view.row_win_lo), int(enc.view.row_win_span)
+    assert lo == int((first - g).min())
+    assert span == int((last - g).max()) - lo + 1
+    assert (first >= g + lo).all() and (last < g + lo + span).all()
+
+
+def test_row_window_absent_without_rows_or_in_tile_order():
+    u = synth.normal_bf16(96 * 1536, 0.02, seed=63)
+    for layout in (api.make_layout(), api.gemm_layout(96, 1536)):
+        e = api.encode(u.reshape(96, 1536), layout=layout)
+        assert e.view.row_win_lo == 0 and e.view.row_win_span == 0
