@@ -1113,9 +1113,12 @@ int launch_vec(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, uint32_t f
 }
 
 template <int K>
-int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_gemm_tuning &tune, void *ws,
+int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_gemm_tuning &tune_in, void *ws,
               hipStream_t st)
 {
+    // one writer per element of y: no segment runs and no K ranges
+    df11_gemm_tuning tune = tune_in;
+    if (tune.one_writer) tune.parts = tune.split = 1;
     // Automatic choice: segment-parallel up to 40 rows of x (one batch tile
     // to 32, two above) when its staging fits; from 41 rows the wide kernel
     // is faster (up_proj: 58.5 against 60.7 us at 33 rows, 66.8 against
@@ -1208,6 +1211,8 @@ int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
         return df11::fail(DF11_E_ARG, "tuning: split applies to the wide and tile-synchronous kernels");
     if (bf16_y && (t.parts > 1 || t.split > 1))
         return df11::fail(DF11_E_ARG, "tuning: a BF16 y has one writer per element (parts and split 1)");
+    if (t.one_writer && (t.parts > 1 || t.split > 1))
+        return df11::fail(DF11_E_ARG, "tuning: one_writer takes parts and split 1");
     if (t.parts > (1u << 16) || t.split > (1u << 16)) return df11::fail(DF11_E_ARG, "tuning: parts or split too large");
     return DF11_OK;
 }

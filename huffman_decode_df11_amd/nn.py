@@ -52,13 +52,18 @@ class DF11Linear(torch.nn.Module):
     64 rows and 73.4 us at 128 against about 79 and 82 us for decoding the
     tile-ordered weight and calling torch.matmul; at 192 rows 95-98 against
     91 us); mode "decode" always decodes into the shared buffer and calls
-    torch.matmul.  "auto" picks "fused" when the shape allows it."""
+    torch.matmul.  "auto" picks "fused" when the shape allows it.
+    deterministic=True asks the fused kernels for one writer per element of
+    y (df11_gemm_tuning one_writer): the same output on every run, where
+    weights with few 32-row blocks (4096 x 4096, 4096 x 14336) otherwise
+    split a row block's work and add float32 partial sums atomically."""
 
     fused_max_rows = 128
 
     def __init__(self, weight, bias: Optional[torch.Tensor] = None, mode: str = "auto", device="cuda",
-                 codebook=None):
+                 codebook=None, deterministic: bool = False):
         super().__init__()
+        self.deterministic = bool(deterministic)
         w = _bits(weight)
         assert w.ndim == 2
         self.out_features, self.in_features = (int(v) for v in w.shape)
@@ -78,8 +83,10 @@ class DF11Linear(torch.nn.Module):
                      if bias is not None else None)
 
     @classmethod
-    def from_linear(cls, lin: torch.nn.Linear, mode: str = "auto", device="cuda") -> "DF11Linear":
-        return cls(lin.weight.detach().to(torch.bfloat16), lin.bias, mode=mode, device=device)
+    def from_linear(cls, lin: torch.nn.Linear, mode: str = "auto", device="cuda",
+                    deterministic: bool = False) -> "DF11Linear":
+        return cls(lin.weight.detach().to(torch.bfloat16), lin.bias, mode=mode, device=device,
+                   deterministic=deterministic)
 
     def decoded_weight(self) -> torch.Tensor:
         """W restored into the shared buffer (valid until the next decode on
@@ -94,7 +101,8 @@ class DF11Linear(torch.nn.Module):
         x2 = x.reshape(-1, self.in_features).to(torch.bfloat16).contiguous()
         B = x2.shape[0]
         if self.mode == "fused" and 1 <= B <= min(256, self.fused_max_rows):
-            y = api.decode_gemm(self.weight_df11, x2)
+            y = api.decode_gemm(self.weight_df11, x2,
+                                tuning=api.gemm_tuning(one_writer=1) if self.deterministic else None)
             if self.bias is not None:
                 y = y + self.bias.float()
             y = y.to(torch.bfloat16)

@@ -371,7 +371,11 @@ typedef struct df11_gemm_tuning {
                               segments to fill the device, else that many (float32 y) */
     uint32_t split;        /* wide and tile-synchronous kernels: 0 = by occupancy, else that many K
                               ranges per row block (float32 y) */
-    uint32_t reserved[4];  /* zero */
+    uint32_t one_writer;   /* nonzero: every element of y is summed by one workgroup in a fixed
+                              order (no K ranges, no segment runs: parts and split 1), so a
+                              float32 y is the same on every run; slower for weights with too few
+                              row blocks to fill the device */
+    uint32_t reserved[3];  /* zero */
 } df11_gemm_tuning;
 
 /* Bytes of the workspace df11_decode_gemm_ex can use for B rows of x with
@@ -396,7 +400,7 @@ uint64_t df11_decode_gemm_workspace_bytes(const df11_view *device_view, uint32_t
  * as df11_decode_gemm_out, E_ARG for a choice that does not apply (w_debug
  * or more than 64 rows of x on the segment-parallel kernel, w_debug or more
  * than 2 rows on the vector one, 32 rows or fewer on the wide one, parts or
- * split above 1 with a BF16 y) or a workspace too
+ * split above 1 with a BF16 y or with one_writer) or a workspace too
  * small or misaligned, E_UNSUPPORTED when the chosen kernel's LDS does not
  * fit this weight. */
 int df11_decode_gemm_ex(const df11_view *device_view, const uint16_t *x, uint32_t B, void *y, int y_dtype,

@@ -555,3 +555,24 @@ def test_vector_kernel_nonfinite_x_row():
     y, _, _ = _run(W, X, with_debug=False)
     assert not np.isfinite(y[1]).any()
     assert _rel(y[:1], ref[:1]) < TOL
+
+
+@pytest.mark.parametrize("B", [1, 8, 64, 200])
+def test_one_writer_is_the_same_on_every_run(B):
+    """A 4096 x 4096 weight has 128 row blocks, too few to fill the device:
+    by default a row block's work is split (segment runs or K ranges) and
+    float32 partial sums are added atomically.  With one_writer every
+    element of y is summed by one workgroup in a fixed order: three calls
+    give the same bits, within the oracle's tolerance."""
+    N, K = 4096, 4096
+    _say("case gemm one_writer B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=88).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=89)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    x = _x_to_gpu(X)
+    tune = api.gemm_tuning(one_writer=1)
+    ys = [api.decode_gemm(dt, x, tuning=tune) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int32), ys[0].view(torch.int32))
+    assert _rel(ys[0].cpu().numpy(), orc.gemm_f64(X, W)) < TOL

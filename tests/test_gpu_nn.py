@@ -137,6 +137,25 @@ def test_linear_fused_and_decode_modes(B):
         assert float(np.linalg.norm(y32.cpu().numpy() - r64) / np.linalg.norm(r64)) < 2e-3
 
 
+@pytest.mark.parametrize("B", [1, 16, 100])
+def test_linear_deterministic_mode(B):
+    """DF11Linear(deterministic=True) on a q_proj-shaped weight (4096 x 4096,
+    whose row blocks are otherwise split): the same output bits on every
+    call, equal to torch's product of the same BF16 values within BF16
+    output rounding."""
+    N = K = 4096
+    _say("case DF11Linear deterministic B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=37).reshape(N, K)
+    x = _i16(synth.activations_bf16(B, K, seed=38)).view(torch.bfloat16).reshape(B, K)
+    lin = dnn.DF11Linear(W, mode="fused", deterministic=True)
+    ys = [lin(x) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    ref = x.float() @ _i16(W).view(torch.bfloat16).float().t()
+    assert float((ys[0].float() - ref).norm() / ref.norm()) < 8e-3
+
+
 @torch.no_grad()
 def test_linear_from_torch_and_3d_input():
     lin_t = torch.nn.Linear(512, 96, bias=True).to(torch.bfloat16).cuda()

@@ -114,6 +114,8 @@ def test_fused_segment_kernel_refused_when_staging_exceeds_64k(kind):
     (1, dict(kernel=_lib.DF11_GEMM_VECTOR), False, True),           # and no w_debug
     (2, dict(kernel=_lib.DF11_GEMM_VECTOR, parts=2), True, False),  # BF16 y: one writer per element
     (8, dict(kernel=5), False, False),                              # no such kernel
+    (8, dict(kernel=_lib.DF11_GEMM_SEGMENT, parts=2, one_writer=1), False, False),  # one writer: parts 1
+    (64, dict(kernel=_lib.DF11_GEMM_WIDE, split=2, one_writer=1), False, False),    # and split 1
 ])
 def test_fused_refuses_choices_that_do_not_apply(B, tune, bf16, wd):
     N, K = 64, 1024
