@@ -617,6 +617,100 @@ decode_rows_kernel(RowArgs a, TableArgs t)
     }
 }
 
+// Row gather in window mode, one workgroup per requested row (WAVES >= the
+// view's row window): wave j loads segment g(r) + win_lo + j of the window
+// right after the row id, while the whole workgroup copies the row's
+// sign+mantissa bytes into LDS next to the tables, so the merge waits on
+// no global load after the decode.  LDS: [guard][WAVES x staging][the row's
+// sign+mantissa bytes][tables].
+template <int K, int WAVES, int CB>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+decode_row_window_kernel(RowArgs a, TableArgs t, uint32_t row_sm_bytes)
+{
+    constexpr uint32_t kThreads = WAVES * 64;
+    constexpr uint32_t kPieces = 4;   // 8-byte pieces of the row's bytes per thread (cols <= 32 * kThreads)
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = lane_id();
+    const uint32_t stg = lds0 + 16 + wave * t.stg_bytes;
+    const uint32_t row_sm = lds0 + 16 + WAVES * t.stg_bytes;
+    const uint32_t fast = row_sm + row_sm_bytes;
+    const uint32_t chain = fast + (8u << K);
+    const ViewArgs &v = a.v;
+    const uint64_t i = blockIdx.x;
+    const int64_t r = a.rows[i];
+    const bool in_range = r >= 0 && (uint64_t)r < a.n_view_rows;   // an out-of-range id leaves its row as it is
+    const uint64_t lo = in_range ? (uint64_t)r * v.cols : 0, hi = in_range ? lo + v.cols : 0;
+    uint64_t s = v.n_segments;
+    if (in_range && wave < a.win) {
+        const int64_t sg = (int64_t)floor((double)lo * a.seg_per_elem) + a.win_lo + (int64_t)wave;
+        if (sg >= 0 && (uint64_t)sg < v.n_segments) s = (uint64_t)sg;
+    }
+    SegLoad<CB> cur{};
+    if (s < v.n_segments) cur = load_segment<CB>(v, s, lane);
+    // the row's sign+mantissa bytes (8-byte pieces; cols is a multiple of 8)
+    const uint32_t n8 = in_range ? (uint32_t)(v.cols / 8) : 0u;
+    uint2 piece[kPieces];
+#pragma unroll
+    for (uint32_t k = 0; k < kPieces; k++) {
+        const uint32_t idx = threadIdx.x + k * kThreads;
+        piece[k] = idx < n8 ? *reinterpret_cast<const uint2 *>(v.sm + lo + 8ull * idx) : make_uint2(0, 0);
+    }
+    stage_tables<K, kThreads>(fast, chain, t.fast, t.chain, t.n_chain);
+#pragma unroll
+    for (uint32_t k = 0; k < kPieces; k++) {
+        const uint32_t idx = threadIdx.x + k * kThreads;
+        if (idx < n8) *(lds_u2 *)(size_t)(row_sm + 8 * idx) = v2u32{piece[k].x, piece[k].y};
+    }
+    __syncthreads();
+    if (s >= v.n_segments || cur.g0 >= hi || cur.g1 <= lo) return;
+    const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
+    if (!p.valid || !stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane)) return;
+    const uint64_t mlo = max(lo, p.g0), mhi = min(hi, p.g1);
+    uint16_t *out = a.out + i * v.cols;
+    const RaggedLane rg = ragged_lane(mlo, mhi, lane);
+    if (rg.act) {
+        const uint32_t rx = *(const lds_u8 *)(size_t)(stg + (uint32_t)(rg.g - p.gbase));
+        const uint32_t sm = *(const lds_u8 *)(size_t)(row_sm + (uint32_t)(rg.g - lo));
+        out[rg.g - lo] = assemble1(sm, rx);
+    }
+    for (uint32_t ui = lane; ui < p.nunits; ui += 64) {
+        if (!df11plan::unit_inside(p, mlo, mhi, ui)) continue;
+        const uint64_t gs = p.gbase + 8ull * ui;
+        const uint2 rx = ld64(stg + 8 * ui);
+        const uint2 sv = ld64(row_sm + (uint32_t)(gs - lo));
+        const uint2 x = assemble4(sv.x, rx.x), y = assemble4(sv.y, rx.y);
+        *reinterpret_cast<uint4 *>(out + (gs - lo)) = make_uint4(x.x, x.y, y.x, y.y);
+    }
+}
+
+template <int K, int CB>
+int launch_row_window(const RowArgs &a, const TableArgs &t, const df11_view *v, hipStream_t st)
+{
+    const uint32_t w = a.win <= 8 ? 8u : a.win <= 12 ? 12u : 16u;
+    const uint32_t row_bytes = (uint32_t)((v->cols + 15) & ~15ull);
+    const uint32_t lds = 16 + w * t.stg_bytes + row_bytes + (8u << K) + v->n_tables * 512u;
+    const dim3 grid((uint32_t)a.n_rows), block(w * 64);
+    if (w == 8) hipLaunchKernelGGL((decode_row_window_kernel<K, 8, CB>), grid, block, lds, st, a, t, row_bytes);
+    else if (w == 12) hipLaunchKernelGGL((decode_row_window_kernel<K, 12, CB>), grid, block, lds, st, a, t, row_bytes);
+    else hipLaunchKernelGGL((decode_row_window_kernel<K, 16, CB>), grid, block, lds, st, a, t, row_bytes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "row gather launch: %s", hipGetErrorString(e));
+    return DF11_OK;
+}
+
+// The window kernel's LDS for this view and window (0 when it does not fit:
+// the staging within the first 64 KB, the row's bytes at most 32 pieces of
+// 8 bytes per thread, everything within a CU's 160 KB).
+uint32_t row_window_lds(const df11_view *v, uint32_t win, uint32_t stg)
+{
+    const uint32_t w = win <= 8 ? 8u : win <= 12 ? 12u : 16u;
+    if (v->cols > 32ull * w * 64 || 16 + w * stg > 65520) return 0;
+    const uint64_t lds = 16 + (uint64_t)w * stg + ((v->cols + 15) & ~15ull) + (8u << v->fast_bits) + v->n_tables * 512u;
+    return lds <= 160u * 1024u ? (uint32_t)lds : 0u;
+}
+
 int check_view(const df11_view *v)
 {
     if (!v) return df11::fail(DF11_E_ARG, "null view");
@@ -1001,7 +1095,8 @@ extern "C" int df11_decode_rows(const df11_view *v, const int64_t *rows, uint64_
         // before the segment loads (128256 x 4096 table, 8-byte chunks, an
         // 11-segment window: 1 / 32 ids in 4.6 / 5.0 us against 4.9 / 5.4
         // us with the search; 16-byte chunks, 7 segments: 5.5 / 6.1 against
-        // 6.0 / 6.7)
+        // 6.0 / 6.7); with a workgroup per row and the row's bytes in LDS
+        // (decode_row_window_kernel) 4.4 / 4.8 and 5.4 / 5.8 us
         a.win = a.split = v->row_win_span;
         a.win_lo = v->row_win_lo;
         a.seg_per_elem = (double)v->n_segments / (double)v->n;
@@ -1013,6 +1108,17 @@ extern "C" int df11_decode_rows(const df11_view *v, const int64_t *rows, uint64_
     if (n_rows > (UINT64_MAX >> 3)) return df11::fail(DF11_E_ARG, "df11_decode_rows: too many rows");
     TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, staging_bytes(v)};
     hipStream_t st = (hipStream_t)stream;
+    if (a.win && n_rows <= (1u << 20) && row_window_lds(v, a.win, t.stg_bytes)) {
+        // one workgroup per row, the row's sign+mantissa bytes in LDS
+        const bool c8 = v->chunk_bytes == 8;
+        switch (v->fast_bits) {
+        case 8: return c8 ? launch_row_window<8, 8>(a, t, v, st) : launch_row_window<8, 16>(a, t, v, st);
+        case 9: return c8 ? launch_row_window<9, 8>(a, t, v, st) : launch_row_window<9, 16>(a, t, v, st);
+        case 10: return c8 ? launch_row_window<10, 8>(a, t, v, st) : launch_row_window<10, 16>(a, t, v, st);
+        case 11: return c8 ? launch_row_window<11, 8>(a, t, v, st) : launch_row_window<11, 16>(a, t, v, st);
+        default: return c8 ? launch_row_window<12, 8>(a, t, v, st) : launch_row_window<12, 16>(a, t, v, st);
+        }
+    }
     return v->chunk_bytes == 8 ? launch_rows<8>(a, t, v, st) : launch_rows<16>(a, t, v, st);
 }
 

@@ -302,8 +302,10 @@ int df11_decode_batch_tuned(const df11_view *device_views, uint16_t *const *outs
  * an embedding lookup that restores only the rows a batch uses ([P1] 2.2
  * item 3: weights are restored right before use).  rows: device int64 ids,
  * 8-byte aligned.  For a few rows whose view records a row window of at
- * most 16 segments (row_win_span), every segment of the window gets its own
- * wave, so no search precedes the segment loads; otherwise the segments that
+ * most 16 segments (row_win_span), each row gets a workgroup in which every
+ * segment of the window has its own wave, so no search precedes the segment
+ * loads, and the row's sign+mantissa bytes are copied into LDS beside them;
+ * otherwise the segments that
  * overlap each requested row are found from an interpolated guess, checked
  * against the 64 segment records around it, else by a 64-way search (up to
  * eight waves per row, one segment each).  Segments are decoded whole
