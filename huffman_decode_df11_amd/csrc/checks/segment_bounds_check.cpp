@@ -44,7 +44,9 @@ void expect(bool ok, const char *what, uint64_t a, uint64_t b, uint64_t c)
                                           (unsigned long long)c);
 }
 
-constexpr int kPrefetch = 5;   // rounds of units whose sign+mantissa bytes are loaded before the decode
+// rounds of units whose sign+mantissa bytes are loaded before the decode:
+// 6 or 5 by chunk size and store mode, both checked
+int g_prefetch = 5;
 
 // Row-major merge of elements [lo, hi) of a plan (merge_range): unit
 // stores, ragged stores, staging reads, sign+mantissa loads.  cover[g - lo]
@@ -56,7 +58,7 @@ void check_range(const SegPlan &p, uint64_t lo, uint64_t hi, uint64_t n, uint64_
     const uint32_t last = p.nunits ? p.nunits - 1 : 0u;
     const uint64_t base = p.nunits ? p.gbase : 0ull;
     for (uint32_t lane = 0; lane < 64; lane++)
-        for (int r = 0; r < kPrefetch; r++) {
+        for (int r = 0; r < g_prefetch; r++) {
             const uint64_t u = std::min<uint64_t>(lane + 64u * r, last);
             expect(base + 8 * u + 8 <= n_sm, "prefetch load inside sm", base, u, n_sm);
         }
@@ -137,6 +139,47 @@ void row_gather_cases(long iters)
     }
 }
 
+// the row gather's window kernel: the row's sign+mantissa bytes in LDS
+// (row_bytes = cols rounded up to 16), read at g - lo for every element the
+// merge writes, and the output row written at g - lo; a window segment is
+// merged only when it overlaps the row and its plan is valid
+void row_window_cases(long iters)
+{
+    for (long it = 0; it < iters; it++) {
+        const uint64_t cols = 8 * (rnd_below(4096) + 1), nrows = rnd_below(300) + 1, n = cols * nrows;
+        const uint64_t row_bytes = (cols + 15) & ~15ull;
+        const uint32_t stg = (uint32_t)((rnd_below(65520 - 64) + 64) & ~15u);
+        uint64_t g0, g1;
+        switch (rnd_below(4)) {
+        case 0: g0 = rnd(); g1 = rnd(); break;                                 // garbage
+        case 1: g0 = rnd_below(n + 1); g1 = g0 - rnd_below(9000) - 1; break;   // reversed
+        default: g0 = rnd_below(n + 1); g1 = std::min(n, g0 + rnd_below(12000)); break;
+        }
+        const uint64_t r = rnd_below(nrows), lo = r * cols, hi = lo + cols;
+        if (g0 >= hi || g1 <= lo) continue;   // not merged
+        const SegPlan p = plan_segment(g0, g1, n, stg);
+        if (!p.valid) continue;
+        const uint64_t mlo = std::max(lo, p.g0), mhi = std::min(hi, p.g1);
+        std::vector<uint8_t> cover(mhi > mlo ? mhi - mlo : 0, 0);
+        for (uint32_t ui = 0; ui < p.nunits; ui++) {
+            if (!unit_inside(p, mlo, mhi, ui)) continue;
+            const uint64_t gs = p.gbase + 8ull * ui;
+            expect(gs >= lo && gs - lo + 8 <= cols, "window unit inside the output row", gs, lo, cols);
+            expect(gs - lo + 8 <= row_bytes, "window unit's bytes inside the LDS row copy", gs, lo, row_bytes);
+            expect(8ull * ui + 8 <= stg, "window unit staging read inside staging", ui, stg, 0);
+            for (int e = 0; e < 8; e++) cover[gs + e - mlo]++;
+        }
+        for (uint32_t lane = 0; lane < 64; lane++) {
+            const RaggedLane rg = ragged_lane(mlo, mhi, lane);
+            if (!rg.act) continue;
+            expect(rg.g >= lo && rg.g - lo < cols, "window ragged store inside the output row", rg.g, lo, cols);
+            expect(rg.g - p.gbase < stg, "window ragged staging read inside staging", rg.g, p.gbase, stg);
+            cover[rg.g - mlo]++;
+        }
+        check_cover(cover, "window stores cover the row's part of the segment once", mlo, mhi);
+    }
+}
+
 // the fused kernel's order: 32-row tiles of 2^tcs columns in 8-column groups,
 // a segment inside one tile written row-major (merge_tile_groups8)
 void tile_cases(long iters)
@@ -194,6 +237,9 @@ int main(int argc, char **argv)
     if (argc > 2) g_state ^= (uint64_t)std::atoll(argv[2]) * 0x2545F4914F6CDD1Dull;
     row_major_cases(iters);
     row_gather_cases(iters / 4);
+    row_window_cases(iters / 4);
+    g_prefetch = 6;
+    row_major_cases(iters / 4);
     tile_cases(iters / 4);
     std::printf("%s: %ld checks, %ld failed\n", g_fail ? "FAILED" : "ok", g_checks, g_fail);
     return g_fail ? 1 : 0;
