@@ -494,17 +494,17 @@ decode_kernel_t8(BatchArgs b, TableArgs t)
 // Row gather: up to eight waves per requested row (as many as the segments
 // a row can overlap); the row's first segment is found by segment_of, wave
 // j of the row decodes the overlapping segments j, j + split, ... whole
-// into its staging, and only the row's elements are written.  In window
-// mode (win > 0, the view's row window) wave j of a row takes segment
-// g(r) + win_lo + j of the window, which holds every segment the row
-// overlaps, with no search before its loads.
+// into its staging, and only the row's elements are written.  The window
+// kernel below (win > 0, the view's row window) gives wave j of a row
+// segment g(r) + win_lo + j of the window, which holds every segment the
+// row overlaps, with no search before its loads.
 struct RowArgs {
     ViewArgs v;               // row-major view (out unused)
     const int64_t *rows;      // requested row ids
     uint16_t *out;            // [n_rows, cols]
     uint64_t n_rows, n_view_rows;
     uint32_t split;           // waves per row: wave j of a row takes its overlapping segments j, j + split, ...
-    uint32_t win;             // window mode: the window's segments (= split), else 0
+    uint32_t win;             // window kernel: the window's segments
     int32_t win_lo;
     double seg_per_elem;      // n_segments / n, as the encoder computed it
 };
@@ -577,12 +577,7 @@ decode_rows_kernel(RowArgs a, TableArgs t)
         if (r >= 0 && (uint64_t)r < a.n_view_rows) {   // an out-of-range id leaves its row as it is
             it.lo = (uint64_t)r * v.cols;
             it.hi = it.lo + v.cols;
-            if (a.win) {
-                const int64_t s = (int64_t)floor((double)it.lo * a.seg_per_elem) + a.win_lo + (int64_t)it.j;
-                it.s = s >= 0 && (uint64_t)s < v.n_segments ? (uint64_t)s : v.n_segments;
-            } else {
-                it.s = min(segment_of(v, it.lo, lane) + it.j, v.n_segments);
-            }
+            it.s = min(segment_of(v, it.lo, lane) + it.j, v.n_segments);
         }
         return it;
     };
@@ -612,7 +607,6 @@ decode_rows_kernel(RowArgs a, TableArgs t)
             if (p.valid && cur.g1 > lo && stage_segment<K>(cur, p, v.counts != nullptr, stg, fast, chain, lane))
                 merge_range(p, mlo, mhi, smp, rag_sm, v.sm, out, stg, lane, false);
             wave_lds_sync();
-            if (a.win) break;   // one segment of the window per wave
         }
     }
 }
@@ -1090,14 +1084,15 @@ extern "C" int df11_decode_rows(const df11_view *v, const int64_t *rows, uint64_
     // ids at four waves per row; 2048 ids: 17.7 us at four, 12.7 at three).
     a.split = 1;
     const uint64_t slots = 16ull * (uint64_t)device_cu_count();
-    if (v->n_segments && v->row_win_span && v->row_win_span <= kRowWindowMax && n_rows * v->row_win_span <= slots) {
-        // window mode: one wave per segment of the row's window, no search
-        // before the segment loads (128256 x 4096 table, 8-byte chunks, an
-        // 11-segment window: 1 / 32 ids in 4.6 / 5.0 us against 4.9 / 5.4
-        // us with the search; 16-byte chunks, 7 segments: 5.5 / 6.1 against
-        // 6.0 / 6.7); with a workgroup per row and the row's bytes in LDS
-        // (decode_row_window_kernel) 4.4 / 4.8 and 5.4 / 5.8 us
-        a.win = a.split = v->row_win_span;
+    const TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, staging_bytes(v)};
+    if (v->n_segments && v->row_win_span && v->row_win_span <= kRowWindowMax && n_rows * v->row_win_span <= slots &&
+        row_window_lds(v, v->row_win_span, t.stg_bytes)) {
+        // window kernel: a workgroup per row, one wave per segment of the
+        // row's window, no search before the segment loads, the row's bytes
+        // in LDS (128256 x 4096 table, 8-byte chunks, an 11-segment window:
+        // 1 / 32 ids in 4.4 / 4.8 us against 4.9 / 5.4 us with the search;
+        // 16-byte chunks, 7 segments: 5.4 / 5.8 against 6.0 / 6.7)
+        a.win = v->row_win_span;
         a.win_lo = v->row_win_lo;
         a.seg_per_elem = (double)v->n_segments / (double)v->n;
     } else if (v->n_segments) {
@@ -1106,9 +1101,8 @@ extern "C" int df11_decode_rows(const df11_view *v, const int64_t *rows, uint64_
         a.split = (uint32_t)(n_rows * wide <= slots ? wide : std::max<uint64_t>(1, wide - 1));
     }
     if (n_rows > (UINT64_MAX >> 3)) return df11::fail(DF11_E_ARG, "df11_decode_rows: too many rows");
-    TableArgs t{v->chain, v->fast, (uint32_t)v->n_chain, staging_bytes(v)};
     hipStream_t st = (hipStream_t)stream;
-    if (a.win && n_rows <= (1u << 20) && row_window_lds(v, a.win, t.stg_bytes)) {
+    if (a.win) {
         // one workgroup per row, the row's sign+mantissa bytes in LDS
         const bool c8 = v->chunk_bytes == 8;
         switch (v->fast_bits) {
