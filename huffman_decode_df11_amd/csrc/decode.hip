@@ -94,26 +94,26 @@ struct BatchArgs {
     ViewArgs v[kMaxBatch];
     uint64_t seg_begin[kMaxBatch + 1];
     uint32_t count;
-    uint32_t stream;          // nonzero: streaming (nontemporal) sign+mantissa loads and BF16 stores
+    uint32_t stream;          // nonzero: streaming (nontemporal) BF16 stores
 };
 
 // A launch whose BF16 output is larger than the last-level cache (the
 // 256 MB Infinity Cache) cannot leave it there for the matmul that follows,
-// so it streams: sign+mantissa bytes are read and BF16 written with
-// nontemporal accesses, which keeps the write-allocate and eviction of data
-// used once out of the cache.  Smaller outputs are written normally and are
-// still cache-resident when the consumer reads them.
+// so it streams: BF16 is written with nontemporal stores, which keeps the
+// write-allocate and eviction of data used once out of the cache.  Smaller
+// outputs are written normally and are still cache-resident when the
+// consumer reads them.  Sign+mantissa bytes are always read with normal
+// loads: the 128-byte line at each segment boundary is read by two waves,
+// usually of one workgroup, and a cached line serves the second (the 8B
+// model pass: 5.53 ms with nontemporal loads, 5.49 with normal ones; its
+// reads were 7.3% above the algorithmic bytes).
 constexpr uint64_t kStreamOutBytes = 256ull << 20;
 
 typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u32g __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint2 load_sm8(const uint8_t *p, bool stream)
+__device__ __forceinline__ uint2 load_sm8(const uint8_t *p)
 {
-    if (stream) {
-        const v2u32 t = __builtin_nontemporal_load(reinterpret_cast<const v2u32 *>(p));
-        return make_uint2(t.x, t.y);
-    }
     return *reinterpret_cast<const uint2 *>(p);
 }
 
@@ -229,14 +229,14 @@ __device__ __forceinline__ SegPlan plan_segment(const SegLoad<CB> &cur, uint64_t
 // that is always inside the array), so no value has to be selected and the
 // loads stay in flight during the decode.
 template <int PR>
-__device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm, uint32_t lane, bool stream,
+__device__ __forceinline__ void prefetch_sm(const SegPlan &p, const uint8_t *sm, uint32_t lane,
                                             uint2 (&smp)[PR])
 {
     const uint32_t last = p.nunits ? p.nunits - 1 : 0u;
     const uint64_t base = p.nunits ? p.gbase : 0ull;
 #pragma unroll
     for (int r = 0; r < PR; r++)
-        smp[r] = load_sm8(sm + base + 8ull * min(lane + 64u * r, last), stream);
+        smp[r] = load_sm8(sm + base + 8ull * min(lane + 64u * r, last));
 }
 
 // Locate, scan and emit one segment into the wave's staging (exponent of
@@ -320,7 +320,7 @@ __device__ __forceinline__ void merge_range(const SegPlan &p, uint64_t lo, uint6
     for (int r = 0; r < PR; r++) merge_unit(p, lo, hi, lane + 64u * r, smp[r], out, stg, stream);
     for (uint32_t r = PR; 64u * r < p.nunits; r++) {
         const uint32_t ui = lane + 64u * r;
-        const uint2 smv = ui < p.nunits ? load_sm8(sm + p.gbase + 8ull * ui, stream) : make_uint2(0, 0);
+        const uint2 smv = ui < p.nunits ? load_sm8(sm + p.gbase + 8ull * ui) : make_uint2(0, 0);
         merge_unit(p, lo, hi, ui, smv, out, stg, stream);
     }
 }
@@ -345,7 +345,7 @@ using df11plan::tile_unit_in;
 
 // sign+mantissa bytes of the lane's units in the first two group batches,
 // loaded before the decode (units outside the segment reload its first unit)
-__device__ __forceinline__ void prefetch_tile8(const TileSeg &q, const ViewArgs &v, uint32_t lane, bool stream,
+__device__ __forceinline__ void prefetch_tile8(const TileSeg &q, const ViewArgs &v, uint32_t lane,
                                                uint2 (&tsv)[8])
 {
 #pragma unroll
@@ -354,7 +354,7 @@ __device__ __forceinline__ void prefetch_tile8(const TileSeg &q, const ViewArgs 
         for (int k = 0; k < 4; k++) {
             const uint32_t gb = q.grp_a + 8u * bb;
             const uint32_t e0 = tile_unit(gb, k, lane);
-            tsv[4 * bb + k] = load_sm8(v.sm + q.sm_off + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)), stream);
+            tsv[4 * bb + k] = load_sm8(v.sm + q.sm_off + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)));
         }
 }
 
@@ -386,7 +386,7 @@ __device__ __forceinline__ void merge_tile_groups8(const SegPlan &p, const ViewA
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             const uint32_t e0 = tile_unit(gb, k, lane);
-            sv[k] = load_sm8(v.sm + q.sm_off + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)), stream);
+            sv[k] = load_sm8(v.sm + q.sm_off + (tile_unit_in(q, gb, e0, lane) ? e0 : (q.lo & ~7u)));
         }
 #pragma unroll
         for (int k = 0; k < 4; k++) unit(gb, k, sv[k]);
@@ -446,10 +446,10 @@ __device__ __forceinline__ void decode_body(const BatchArgs &b, const TableArgs 
             tiled = p.valid && v.kc == 8 && v.pow2 && v.tr == 32 && p.g1 > p.g0 && (p.g0 >> ts) == ((p.g1 - 1) >> ts);
             if (tiled) {
                 q = tile_seg(p, v, stg);
-                prefetch_tile8(q, v, lane, stream, tsv);
+                prefetch_tile8(q, v, lane, tsv);
             }
         }
-        if (!tiled) prefetch_sm(p, v.sm, lane, stream, smp);
+        if (!tiled) prefetch_sm(p, v.sm, lane, smp);
         const RaggedLane rg = ragged_lane(p.g0, p.g1, lane);
         const uint32_t rag_sm = v.sm[p.valid && rg.act ? rg.g : 0];
 
@@ -600,7 +600,7 @@ decode_rows_kernel(RowArgs a, TableArgs t)
             if (cur.g0 >= hi) break;
             const SegPlan p = plan_segment(cur, v.n, t.stg_bytes);
             uint2 smp[prefetch_rounds<CB>()];
-            prefetch_sm(p, v.sm, lane, false, smp);
+            prefetch_sm(p, v.sm, lane, smp);
             const uint64_t mlo = max(lo, p.g0), mhi = min(hi, p.g1);
             const RaggedLane rg = ragged_lane(mlo, mhi, lane);
             const uint32_t rag_sm = v.sm[p.valid && mlo < mhi && rg.act ? rg.g : 0];

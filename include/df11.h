@@ -281,7 +281,7 @@ int df11_decode_batch(const df11_view *device_views, uint16_t *const *outs, uint
  * struct, or NULL, is the library's own choice. */
 #define DF11_STORES_AUTO 0       /* streaming when the launch writes more than the 256 MB last-level cache */
 #define DF11_STORES_CACHED 1     /* normal loads and stores: the output stays cache-resident for its consumer */
-#define DF11_STORES_STREAMING 2  /* nontemporal sign+mantissa loads and BF16 stores */
+#define DF11_STORES_STREAMING 2  /* nontemporal BF16 stores */
 typedef struct df11_decode_tuning {
     uint32_t waves;        /* waves per workgroup: 0 = from occupancy and size, else 4, 6, ..., 16 */
     uint32_t stores;       /* DF11_STORES_* */
