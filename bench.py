@@ -624,23 +624,29 @@ def shard_layer_decode(steps: int, warmup: int, ways: int = 8, copies: int = 4, 
             "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def copy_peak(nbytes: int = 512 << 20, reps: int = 10):
+def copy_peak(nbytes: int = 512 << 20, reps: int = 5, groups: int = 3):
     """Device-to-device copy rate (read + write bytes per second) of a
-    buffer larger than the Infinity Cache: the practical HBM ceiling."""
+    buffer larger than the Infinity Cache: the practical HBM ceiling.  The
+    best of `groups` timed groups of `reps` copies (a single group has read
+    low now and then, which would overstate the fraction of it reached)."""
     import torch
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
+    for _ in range(2):
         dst.copy_(src)
-    b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    best = 0.0
+    for _ in range(groups):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        best = max(best, 2.0 * nbytes / (ms * 1e-3) / 1e9)
     del src, dst
-    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+    return best
 
 
 def verify(dts, mats, outbuf):
