@@ -42,6 +42,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 
 #include "df11_device.h"
 #include "df11_internal.h"
@@ -878,6 +879,378 @@ decode_gemm_wide_kernel(GemmArgs g)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined kernel: decoder waves and matrix-core waves of one workgroup work
+// on different tiles at once, handing tiles over through a ring of BF16 tile
+// planes in LDS and two counters per ring slot, with no workgroup barrier
+// after the table staging.
+//
+//   decoder waves (all but the first nm): take the segments of the
+//     workgroup's tile sequence in turn (running segment index = wave
+//     number mod the decoder count), wait until the tile's slot has been
+//     released by every matrix-core wave, write each code's rotated
+//     exponent into the high byte of its BF16 slot, merge the segment's
+//     sign+mantissa bytes in place (whole 8-element units with one 16-byte
+//     store, the units shared with a neighbouring segment element by
+//     element), then add one to the slot's ready counter.  The next
+//     segment's stream words and sign+mantissa bytes are loaded before the
+//     current one is decoded.
+//   matrix-core waves (waves 0 .. nm - 1, nm = ceil(B / 32)): wave m owns
+//     the 32-row batch tile m and one 32 x 32 float32 accumulator; per tile
+//     it waits for the slot's ready counter to reach the segments decoded
+//     into that slot so far, runs the tile's 32 k-steps of
+//     v_mfma_f32_32x32x16_bf16 from the plane, and adds one to the slot's
+//     release counter.  Each y element has one writer (unless K is split).
+//
+// Waits are bounded spins on LDS (s_sleep between reads); a wait that runs
+// out (not reachable with well-formed arguments: every counter is advanced
+// by a wave that only waits on earlier tiles) lets the wave continue and
+// makes the matrix-core wave store NaN.
+constexpr uint32_t kPipePlane = 2 * kTile;         // bytes of one BF16 tile plane
+constexpr uint32_t kPipeGuard = 16;                // LDS bytes before the first plane
+constexpr uint32_t kPipeMaxSlots = 3;
+// The emit cursor's high half holds plane / 2 + element index and must stay
+// within 16 bits up to one past a tile's last element (the emit loops'
+// end); the guard keeps the lowest position above 3 (its 4-code bound).
+static_assert((kPipeGuard + kPipeMaxSlots * kPipePlane) / 2 <= 65535, "pipelined planes beyond the emit cursor");
+static_assert(kPipeGuard / 2 >= 3, "pipelined emit bound");
+constexpr uint32_t kPipePieces = 8;                // 8-element units per lane loaded ahead
+constexpr uint32_t kPipeSpin = 1u << 22;
+
+__device__ __forceinline__ bool lds_wait_geq(uint32_t addr, uint32_t target)
+{
+    bool ok = false;
+    for (uint32_t i = 0; i < kPipeSpin; i++) {
+        const uint32_t v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load((lds_u32 *)(size_t)addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if ((int32_t)(v - target) >= 0) {
+            ok = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    return ok;
+}
+
+// all LDS accesses of this wave done, then one lane adds 1 to the counter
+__device__ __forceinline__ void lds_signal(uint32_t addr, uint32_t lane)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) __hip_atomic_fetch_add((lds_u32 *)(size_t)addr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// emit_codes with each rotated exponent written to the high byte of a
+// 16-bit slot: the cursor's high half holds (plane byte address / 2 +
+// element index) and, its low half never dropping below 32768, st >> 15 is
+// the byte address of that high byte.  wpos >= 3 and wpos + cnt <= 65535.
+template <int K, int NW>
+__device__ __forceinline__ void emit_codes_hi(Window<NW> w, uint32_t fast, uint32_t chain, uint32_t wpos, uint32_t cnt)
+{
+    uint32_t st = (wpos << 16) | kM0;
+    const uint32_t bound = (wpos + cnt - 3u) << 16;   // st < bound <=> at least 4 codes left
+    while (st < bound) {
+        const uint2 f = ld64(lshl_add_s<3>(w.w[0] >> (32 - K), fast));
+        uint32_t syms = f.x, meta = f.y;
+        if (meta == 0) {
+            const uint32_t e = chain_decode(chain, w.w[0]);
+            syms = rot_exp(e & 0xFFu);
+            meta = (1u << 16) - ((e >> 8) & 0x3Fu);
+        }
+        const uint32_t a = st >> 15;
+        uint32_t t = syms >> 8;
+        asm("" : "+v"(t));
+        st8(a, syms);
+        st8(a + 2, t);
+        st8(a + 4, syms >> 16);
+        st8(a + 6, t >> 16);
+        w.consume(meta);
+        st += meta;
+    }
+    const uint32_t lend = wpos + cnt;
+    while ((st >> 16) < lend) {
+        const uint32_t e = chain_decode(chain, w.w[0]);
+        const uint32_t step = (1u << 16) - ((e >> 8) & 0x3Fu);
+        st8(st >> 15, rot_exp(e & 0xFFu));
+        w.consume(step);
+        st += step;
+    }
+}
+
+// 8 BF16 slots holding rotated exponents in their high bytes + 8
+// sign+mantissa bytes -> 8 BF16 words
+__device__ __forceinline__ uint4 merge_hi(uint4 v, uint2 sm)
+{
+    const uint32_t rlo = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
+    const uint32_t rhi = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
+    const uint2 a = assemble4(sm.x, rlo), b = assemble4(sm.y, rhi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// One segment job of a decoder wave, loaded ahead of its decode.
+struct PipeJob {
+    SegLoad L;
+    uint2 sv[kPipePieces];
+    uint64_t ts;          // first element of the segment's tile
+    uint32_t a, b;        // the segment's elements inside its tile, [a, b); a = b when out of range
+    uint32_t q;           // ring slot of the tile | its earlier uses of that slot << 2
+};
+
+// Walks the workgroup's tile sequence: units blockIdx.x, + gridDim.x, ...;
+// unit = (row block, K range); tiles kt0 .. kt1 - 1 of the row block.
+struct PipeSeq {
+    uint32_t unit, kt, kt1, q;
+    uint32_t t, first, nseg;   // tile, its first segment and segment count (n_segments < 2^32)
+};
+
+// block_seg[i] clamped to n_segments in 32-bit scalar arithmetic (64-bit
+// ordered compares would run on the vector ALU)
+__device__ __forceinline__ uint32_t pipe_seg(const GemmArgs &g, uint32_t i)
+{
+    const uint64_t v = as_const(g.block_seg)[i];
+    const uint32_t n = (uint32_t)g.n_segments;
+    return (uint32_t)(v >> 32) ? n : min((uint32_t)v, n);
+}
+
+__device__ __forceinline__ void pipe_tile(const GemmArgs &g, PipeSeq &p)
+{
+    p.first = pipe_seg(g, p.t);
+    const uint32_t end = pipe_seg(g, p.t + 1);
+    p.nseg = end > p.first ? end - p.first : 0;
+}
+
+__device__ __forceinline__ bool pipe_unit(const GemmArgs &g, PipeSeq &p, uint32_t n_units)
+{
+    if (p.unit >= n_units) return false;
+    const uint32_t rb = p.unit / g.split, sp = p.unit - rb * g.split;
+    p.kt = sp * g.tiles_per_split;
+    p.kt1 = min(p.kt + g.tiles_per_split, g.tiles_per_row);
+    p.t = rb * g.tiles_per_row + p.kt;
+    pipe_tile(g, p);
+    return true;
+}
+
+// next tile of the sequence; false past the last
+__device__ __forceinline__ bool pipe_next(const GemmArgs &g, PipeSeq &p, uint32_t n_units)
+{
+    p.q++;
+    if (p.kt + 1 < p.kt1) {
+        p.kt++;
+        p.t++;
+        pipe_tile(g, p);
+        return true;
+    }
+    p.unit += gridDim.x;
+    return pipe_unit(g, p, n_units);
+}
+
+template <int K, int MT, int W>
+__global__ void __launch_bounds__(W * 64) decode_gemm_pipe_kernel(GemmArgs g, uint32_t nslot)
+{
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = lane_id();
+    // [guard][nslot BF16 planes][ready[4], release[4]][tables]
+    const uint32_t planes = lds0 + kPipeGuard;
+    const uint32_t ctr = planes + nslot * kPipePlane;
+    const uint32_t fast = ctr + 64;
+    const uint32_t chain = fast + (8u << K);
+    if (threadIdx.x < 8) st32(ctr + 4 * threadIdx.x, 0u);
+    stage_tables<K, W * 64>(fast, chain, g.fast, g.chain, g.n_chain);
+    __syncthreads();
+
+    const uint32_t nm = (g.B + 31) / 32;   // matrix-core waves, one per batch tile
+    const uint32_t n_units = g.n_rowblocks * g.split;
+    const bool stored = g.counts != nullptr;
+
+    if (wave < nm) {
+        // ---- matrix-core wave: batch tile m = wave
+        const uint32_t m = wave;
+        const bool writes_w = g.w_debug && m == 0;
+        uint32_t cum[kPipeMaxSlots] = {};
+        bool ok = true;
+        f32x16 acc;
+#pragma unroll
+        for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+        // one tile from ring slot `sl`: x operands of k-step ks at xb + ks *
+        // xs bytes (packed: the operand kilobyte of batch tile m; in place:
+        // row m * 32 + n_l, clamped to row B - 1, whose products only reach
+        // rows of y that are not stored), issued before the wait; no branch
+        // inside the k-loop (w_debug calls run their own copy of it)
+        auto run_tile = [&](auto wd_tag, const PipeSeq &p, uint32_t sl, uint32_t target) {
+            constexpr bool kWD = decltype(wd_tag)::value;
+            uint32_t ln = lane;
+            asm volatile("" : "+v"(ln));
+            const uint32_t brow = min(m * 32 + (ln & 31u), g.B - 1);
+            const uint8_t *xb = g.xo ? reinterpret_cast<const uint8_t *>(g.xo + ((uint64_t)p.kt * 32u * MT + m) * 64 + ln)
+                                     : reinterpret_cast<const uint8_t *>(g.x + (uint64_t)brow * g.K + p.kt * kTC + (ln >> 5) * 8);
+            const uint32_t xs = g.xo ? MT * 64u * 16u : 32u;
+            constexpr int kAhead = 8;
+            uint4 xa[kAhead];
+#pragma unroll
+            for (int i = 0; i < kAhead; i++) xa[i] = *reinterpret_cast<const uint4 *>(xb + i * xs);
+            ok &= lds_wait_geq(ctr + 4 * sl, target);
+            const uint32_t rb = p.unit / g.split;
+            const uint32_t pl = planes + sl * kPipePlane + 16u * ((ln >> 5) * kTR + (ln & 31u));
+            uint16_t *wd = nullptr;
+            if constexpr (kWD) wd = g.w_debug + (uint64_t)(rb * kTR + (ln & 31u)) * g.K + p.kt * kTC + (ln >> 5) * kKC;
+            // k-step i: groups c = 2 i + lane / 32, row n_l; the plane's
+            // operands are read kWAhead k-steps before their product
+            constexpr int kWAhead = 4;
+            v4u32 wq[kWAhead];
+#pragma unroll
+            for (int i = 0; i < kWAhead; i++) wq[i] = *(const lds_u4 *)(size_t)(pl + 16u * (2 * i * kTR));
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                const v4u32 wb = wq[i % kWAhead];
+                if (i + kWAhead < 32) wq[i % kWAhead] = *(const lds_u4 *)(size_t)(pl + 16u * (2 * (i + kWAhead) * kTR));
+                if constexpr (kWD) *reinterpret_cast<uint4 *>(wd + 2 * i * kKC) = make_uint4(wb.x, wb.y, wb.z, wb.w);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[i % kAhead]),
+                                                              __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
+                if (i + kAhead < 32) xa[i % kAhead] = *reinterpret_cast<const uint4 *>(xb + (i + kAhead) * xs);
+                __builtin_amdgcn_sched_barrier(0);   // keeps the loads ahead of their products as written
+            }
+        };
+        PipeSeq p{blockIdx.x, 0, 0, 0, 0, 0, 0};
+        uint32_t slot = 0;
+        for (bool more = pipe_unit(g, p, n_units); more;) {
+#pragma unroll
+            for (uint32_t i = 0; i < kPipeMaxSlots; i++)
+                if (i == slot) cum[i] += p.nseg;
+            uint32_t target = cum[0];
+#pragma unroll
+            for (uint32_t i = 1; i < kPipeMaxSlots; i++)
+                if (i == slot) target = cum[i];
+            if (writes_w) run_tile(std::true_type{}, p, slot, target);
+            else run_tile(std::false_type{}, p, slot, target);
+            const uint32_t rb = p.unit / g.split;
+            lds_signal(ctr + 16 + 4 * slot, lane);
+            slot = slot + 1 == nslot ? 0 : slot + 1;
+            const bool last = p.kt + 1 == p.kt1;
+            if (last) {
+                // lane holds n = rb*32 + lane%32, b = 32*m + 8*blk + 4*(lane/32) + e
+                // (addresses formed here, not kept across the tile loop)
+                uint32_t ln = lane, nB = g.B, nN = g.N;
+                asm volatile("" : "+v"(ln), "+s"(nB), "+s"(nN));
+#pragma unroll
+                for (int blk = 0; blk < 4; blk++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const uint32_t b = m * 32 + 8 * blk + 4 * (ln >> 5) + e;
+                        if (b < nB)
+                            store_y_at(g, (uint64_t)b * nN + rb * kTR + (ln & 31u),
+                                       ok ? acc[4 * blk + e] : __builtin_nanf(""), g.split > 1);
+                    }
+#pragma unroll
+                for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+            }
+            more = pipe_next(g, p, n_units);
+        }
+        return;
+    }
+
+    // ---- decoder wave d of nd
+    const uint32_t nd = W - nm, d = wave - nm;
+    PipeSeq p{blockIdx.x, 0, 0, 0, 0, 0, 0};
+    bool more = pipe_unit(g, p, n_units);
+    uint32_t c = 0;        // segments of the sequence before tile p.q
+    uint32_t r = d;        // running index of this wave's next segment
+    uint32_t slot = 0, use = 0;   // ring slot of tile p.q and its earlier uses
+    // Load the next job; false past the sequence.  The loads are issued on
+    // every path (a job past the end loads segment 0 and is not decoded) and
+    // at clamped addresses, so the number of loads in flight is the same on
+    // every path and the decode of the current job waits only for its own.
+    auto next_job = [&](PipeJob &j) {
+        while (more && r >= c + p.nseg) {
+            c += p.nseg;
+            more = pipe_next(g, p, n_units);
+            if (++slot == nslot) {
+                slot = 0;
+                use++;
+            }
+        }
+        const bool has = more;
+        const uint32_t s = has ? p.first + (r - c) : 0;
+        if (has) r += nd;
+        j.L = load_segment(g, s, lane);
+        j.ts = has ? (uint64_t)p.t * kTile : 0;
+        j.q = slot | use << 2;
+        const bool valid = has && j.L.g0 >= j.ts && j.L.g1 >= j.L.g0 && j.L.g1 <= j.ts + kTile;
+        j.a = valid ? (uint32_t)(j.L.g0 - j.ts) : 0u;
+        j.b = valid ? (uint32_t)(j.L.g1 - j.ts) : 0u;
+        const uint8_t *smt = g.sm + j.ts;
+#pragma unroll
+        for (uint32_t k = 0; k < kPipePieces; k++) {
+            const uint32_t u = min((j.a >> 3) + lane + 64 * k, kTile / 8 - 1);
+            j.sv[k] = *reinterpret_cast<const uint2 *>(smt + 8 * u);
+        }
+        return has;
+    };
+    // one merge unit: the high bytes of slots 8u .. 8u + 7 with their
+    // sign+mantissa bytes; units shared with a neighbouring segment are
+    // written element by element
+    auto merge_unit_hi = [&](uint32_t plane, uint32_t u, uint2 sv, uint32_t a, uint32_t b) {
+        const uint4 v = merge_hi(ld128(plane + 16 * u), sv);
+        if (8 * u >= a && 8 * u + 8 <= b) {
+            *(lds_u4 *)(size_t)(plane + 16 * u) = v4u32{v.x, v.y, v.z, v.w};
+        } else {
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (uint32_t e = 0; e < 8; e++) {
+                const uint32_t idx = 8 * u + e;
+                if (idx >= a && idx < b) *(lds_u16 *)(size_t)(plane + 2 * idx) = (uint16_t)(wv[e / 2] >> (16 * (e & 1)));
+            }
+        }
+    };
+    auto process = [&](const PipeJob &j) {
+        // every load of this job is waited for here, so that refilling its
+        // buffer afterwards waits for none of the other buffer's loads
+#pragma unroll
+        for (uint32_t k = 0; k < kPipePieces; k++) asm volatile("" ::"v"(j.sv[k].x), "v"(j.sv[k].y));
+        asm volatile("" ::"v"(j.L.own.x), "v"(j.L.own.y), "v"(j.L.own.z), "v"(j.L.own.w), "v"(j.L.next), "v"(j.L.gap),
+                     "v"(j.L.count));
+        const uint32_t jslot = j.q & 3u, juse = j.q >> 2;
+        lds_wait_geq(ctr + 16 + 4 * jslot, juse * nm);
+        const uint32_t plane = planes + jslot * kPipePlane;
+        // decode: counts, positions, exponents into the high bytes
+        const auto win = make_window(j.L.own, j.L.next, j.L.gap);
+        uint32_t cnt = j.L.count;
+        if (!stored) {
+            const uint32_t c0 = lane * kChunkBits;
+            const uint32_t end = j.L.nbits > c0 ? min(kChunkBits, j.L.nbits - c0) : 0u;
+            cnt = j.L.gap < end ? count_codes<K>(win, fast, chain, j.L.gap, end) : 0u;
+        }
+        uint32_t total;
+        const uint32_t excl = wave_exclusive_scan(cnt, &total);
+        if (j.b > j.a && total == j.b - j.a) emit_codes_hi<K>(win, fast, chain, plane / 2 + j.a + excl, cnt);
+        wave_lds_sync();
+        // merge the segment's units in place: the first 64 * kPipePieces
+        // from the bytes loaded ahead, any further ones (segments of more
+        // than 4088 elements) loaded here
+        const uint32_t u0 = j.a >> 3, u_end = (j.b + 7) >> 3;
+#pragma unroll
+        for (uint32_t k = 0; k < kPipePieces; k++) {
+            const uint32_t u = u0 + lane + 64 * k;
+            if (u < u_end) merge_unit_hi(plane, u, j.sv[k], j.a, j.b);
+        }
+        const uint8_t *smt = g.sm + j.ts;
+        for (uint32_t u = u0 + 64 * kPipePieces + lane; u < u_end; u += 64)
+            merge_unit_hi(plane, u, *reinterpret_cast<const uint2 *>(smt + 8 * u), j.a, j.b);
+        lds_signal(ctr + 4 * jslot, lane);
+    };
+    // two job buffers in turn: one decoded while the other's loads land
+    PipeJob ja, jb;
+    bool ha = next_job(ja);
+    while (ha) {
+        const bool hb = next_job(jb);
+        process(ja);
+        if (!hb) break;
+        ha = next_job(ja);
+        process(jb);
+    }
+}
+
 // x [B, K] in the matrix cores' A-operand order: piece (s, m, l) holds the 8
 // BF16 of row 32 m + l % 32, columns 16 s + 8 (l / 32) .. + 7 (zero past row
 // B), at index (s * tiles + m) * 64 + l, so that the operand of k-step s and
@@ -1112,6 +1485,43 @@ int launch_vec(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, uint32_t f
     return DF11_OK;
 }
 
+// LDS of the pipelined kernel with nslot tile planes
+uint32_t pipe_lds_bytes(uint32_t nslot, uint32_t fast_bits, uint32_t n_tables)
+{
+    return kPipeGuard + nslot * kPipePlane + 64 + (8u << fast_bits) + n_tables * 512u;
+}
+
+// Pipelined launch: as many ring slots (up to 3) as fit beside the tables;
+// K split when there are too few row blocks to fill every resident slot.
+template <int K, int MT>
+int launch_pipe(GemmArgs a, uint32_t n_tables, uint32_t forced_split, hipStream_t st)
+{
+    constexpr int W = 16;   // 1024 threads: the most a workgroup holds
+    uint32_t nslot = kPipeMaxSlots;
+    while (nslot >= 2 && pipe_lds_bytes(nslot, K, n_tables) > 160u * 1024u) nslot--;
+    if (nslot < 2) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: pipelined kernel planes and tables do not fit in LDS");
+    if (a.xo && a.xo_tiles != (uint32_t)MT) return df11::fail(DF11_E_ARG, "decode_gemm: packed x tiles");
+    if (a.n_segments >= (1ull << 32) || (uint64_t)a.n_rowblocks * a.tiles_per_row >= (1ull << 32))
+        return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: the pipelined kernel takes fewer than 2^32 segments and tiles");
+    const uint32_t lds = pipe_lds_bytes(nslot, K, n_tables);
+    const void *kern = (const void *)decode_gemm_pipe_kernel<K, MT, W>;
+    const uint32_t slots = (uint32_t)(cu_count() * resident_groups(kern, W * 64, lds));
+    uint32_t split = 1;
+    if (forced_split) split = forced_split;
+    else if (2 * a.n_rowblocks <= slots) split = (slots + a.n_rowblocks - 1) / a.n_rowblocks;
+    split = std::max(1u, std::min(split, a.tiles_per_row));
+    if (a.y_bf16) split = 1;
+    a.tiles_per_split = (a.tiles_per_row + split - 1) / split;
+    a.split = (a.tiles_per_row + a.tiles_per_split - 1) / a.tiles_per_split;
+    if (a.split > 1) clear_y(a, st);
+    const uint32_t units = a.n_rowblocks * a.split;
+    const uint32_t groups = std::min<uint32_t>(units, slots);
+    hipLaunchKernelGGL((decode_gemm_pipe_kernel<K, MT, W>), dim3(groups), dim3(W * 64), lds, st, a, nslot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
+    return DF11_OK;
+}
+
 template <int K>
 int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_gemm_tuning &tune_in, void *ws,
               hipStream_t st)
@@ -1159,6 +1569,12 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
         a.xo = reinterpret_cast<const uint4 *>(ws);
         a.xo_tiles = tiles;
     }
+    if (kernel == DF11_GEMM_PIPE) {
+        if (mt <= 1) return launch_pipe<K, 1>(a, n_tables, tune.split, st);
+        if (mt <= 2) return launch_pipe<K, 2>(a, n_tables, tune.split, st);
+        if (mt <= 4) return launch_pipe<K, 4>(a, n_tables, tune.split, st);
+        return launch_pipe<K, 8>(a, n_tables, tune.split, st);
+    }
     if (kernel == DF11_GEMM_SEGMENT) {
         if (a.w_debug || mt > 2)
             return df11::fail(DF11_E_ARG, "tuning: the segment-parallel kernel takes up to 64 rows of x and no w_debug");
@@ -1202,13 +1618,13 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
 
 int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
 {
-    if (t.kernel > DF11_GEMM_VECTOR) return df11::fail(DF11_E_ARG, "tuning: kernel %u", t.kernel);
+    if (t.kernel > DF11_GEMM_PIPE) return df11::fail(DF11_E_ARG, "tuning: kernel %u", t.kernel);
     if (t.row_blocks > 2 || (t.row_blocks && t.kernel != DF11_GEMM_WIDE))
         return df11::fail(DF11_E_ARG, "tuning: row_blocks %u (0, or 1 or 2 with the wide kernel)", t.row_blocks);
     if (t.parts && t.kernel != DF11_GEMM_SEGMENT && t.kernel != DF11_GEMM_VECTOR)
         return df11::fail(DF11_E_ARG, "tuning: parts applies to the segment-parallel and vector kernels");
-    if (t.split && t.kernel != DF11_GEMM_WIDE && t.kernel != DF11_GEMM_TILED)
-        return df11::fail(DF11_E_ARG, "tuning: split applies to the wide and tile-synchronous kernels");
+    if (t.split && t.kernel != DF11_GEMM_WIDE && t.kernel != DF11_GEMM_TILED && t.kernel != DF11_GEMM_PIPE)
+        return df11::fail(DF11_E_ARG, "tuning: split applies to the wide, tile-synchronous and pipelined kernels");
     if (bf16_y && (t.parts > 1 || t.split > 1))
         return df11::fail(DF11_E_ARG, "tuning: a BF16 y has one writer per element (parts and split 1)");
     if (t.one_writer && (t.parts > 1 || t.split > 1))

@@ -366,6 +366,7 @@ int df11_decode_gemm_out(const df11_view *device_view, const uint16_t *x, uint32
 #define DF11_GEMM_WIDE 2      /* one BF16 tile in LDS shared by the batch tiles: 33 rows of x or more */
 #define DF11_GEMM_TILED 3     /* tile-synchronous, any rows of x */
 #define DF11_GEMM_VECTOR 4    /* dot products on the vector ALU: one or two rows of x, no w_debug */
+#define DF11_GEMM_PIPE 5      /* decoder and matrix-core waves on a ring of BF16 tiles in LDS: any rows of x */
 typedef struct df11_gemm_tuning {
     uint32_t kernel;       /* DF11_GEMM_* */
     uint32_t row_blocks;   /* wide kernel: 0 = by B, else 1 or 2 row blocks per workgroup */

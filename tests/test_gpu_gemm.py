@@ -576,3 +576,115 @@ def test_one_writer_is_the_same_on_every_run(B):
     for y in ys[1:]:
         assert torch.equal(y.view(torch.int32), ys[0].view(torch.int32))
     assert _rel(ys[0].cpu().numpy(), orc.gemm_f64(X, W)) < TOL
+
+
+# ---- pipelined kernel (DF11_GEMM_PIPE): decoder waves and matrix-core waves
+# of one workgroup handing tiles over through a ring of BF16 planes in LDS
+
+@pytest.mark.parametrize("N,K,B,extra", [(256, 4096, 1, dict()), (256, 4096, 8, dict()), (256, 4096, 33, dict()),
+                                         (256, 4096, 64, dict(split=3)), (256, 4096, 100, dict(one_writer=1)),
+                                         (256, 4096, 200, dict()), (256, 4096, 256, dict(one_writer=1)),
+                                         (96, 1536, 17, dict()), (96, 1536, 250, dict(split=1))])
+def test_pipelined_kernel_matches_oracle(N, K, B, extra):
+    """Few row blocks (the K range of a row block split across workgroups,
+    y added atomically, unless one_writer or split=1): decoded weights
+    bit-exact through w_debug, y of both calls within the oracle's
+    tolerance, and a BF16 y one rounding of the float32 one-writer sums."""
+    _say("case gemm pipelined N=%d K=%d B=%d %s" % (N, K, B, extra))
+    W = synth.normal_bf16(N * K, 0.02, seed=90).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=91)
+    tune = api.gemm_tuning(kernel=_lib.DF11_GEMM_PIPE, **extra)
+    y, wd, yd = _run(W, X, tuning=tune)
+    ref = orc.gemm_f64(X, W)
+    assert np.array_equal(wd, W)
+    assert _rel(y, ref) < TOL and _rel(yd, ref) < TOL
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    one = api.gemm_tuning(kernel=_lib.DF11_GEMM_PIPE, one_writer=1)
+    y32 = api.decode_gemm(dt, _x_to_gpu(X), tuning=one)
+    y16 = api.decode_gemm(dt, _x_to_gpu(X), out_dtype=torch.bfloat16, tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_PIPE))
+    torch.cuda.synchronize()
+    got16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got16, orc.round_bf16(y32.cpu().numpy()))
+
+
+@pytest.mark.parametrize("B", [1, 64, 256])
+def test_pipelined_kernel_up_proj_full_size(B):
+    """Wup 14336 x 4096 (448 row blocks: one workgroup sums each element of
+    y): the decoded weights compared in full, y against the oracle on 48
+    sampled output features and against torch's float32 matmul of the same
+    BF16 values, and the same bits from a second call."""
+    N, K = 14336, 4096
+    _say("case gemm pipelined up_proj B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=1)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    tune = api.gemm_tuning(kernel=_lib.DF11_GEMM_PIPE)
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y = api.decode_gemm(dt, _x_to_gpu(X), tuning=tune)
+    y2 = api.decode_gemm(dt, _x_to_gpu(X), tuning=tune)
+    yd = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg, tuning=tune)
+    torch.cuda.synchronize()
+    wt = torch.from_numpy(W.view(np.int16)).cuda()
+    assert torch.equal(wdbg.view(torch.int16), wt), "decoded weights differ"
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    cols = np.random.default_rng(B + 3).choice(N, size=48, replace=False)
+    ref = orc.gemm_f64(X, W[cols])
+    yt = (_x_to_gpu(X).float() @ wt.view(torch.bfloat16).float().T)
+    for out in (y, yd):
+        assert _rel(out.cpu().numpy()[:, cols], ref) < TOL
+        assert float((out - yt).norm() / yt.norm()) < TOL
+
+
+@pytest.mark.parametrize("B", [1, 64])
+@pytest.mark.parametrize("kind", ["zero", "sparse95"])
+def test_pipelined_kernel_long_segments(kind, B):
+    """All-zero and 95%-zero weights: segments of 7,000-8,192 elements, more
+    than the units a decoder wave loads ahead, so the rest of each segment
+    is merged from bytes loaded during the merge.  Bit-exact weights, y as
+    the oracle's (exactly zero for the all-zero weight)."""
+    N, K = 64, 4096
+    _say("case gemm pipelined long segments %s B=%d" % (kind, B))
+    if kind == "zero":
+        W = np.zeros((N, K), np.uint16)
+    else:
+        rng = np.random.default_rng(77)
+        W = synth.normal_bf16(N * K, 0.02, seed=78).reshape(N, K)
+        W[rng.random((N, K)) < 0.95] = 0
+    assert api.encode(W, layout=api.gemm_layout(N, K)).view.max_seg_elems > 7000
+    X = synth.activations_bf16(B, K, seed=79)
+    y, wd, yd = _run(W, X, tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_PIPE))
+    assert np.array_equal(wd, W)
+    ref = orc.gemm_f64(X, W)
+    for got in (y, yd):
+        if kind == "zero":
+            assert (got == 0).all()
+        else:
+            assert _rel(got, ref) < TOL
+
+
+def test_pipelined_kernel_locate_pass_without_stored_counts():
+    """No stored code counts: the decoder waves walk each chunk to count its
+    codes first.  Adversarial weights (long codes through the hierarchical
+    tables): decoded weights bit-exact, y as the oracle's."""
+    N, K, B = 96, 1536, 40
+    _say("case gemm pipelined locate pass")
+    W = synth.adversarial_bf16(N * K, seed=66).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=67)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    dt.view.counts = None
+    dt.view.n_counts = 0
+    tune = api.gemm_tuning(kernel=_lib.DF11_GEMM_PIPE)
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg, tuning=tune)
+    torch.cuda.synchronize()
+    assert np.array_equal(wdbg.view(torch.int16).cpu().numpy().view(np.uint16), W)
+    ref = orc.gemm_f64(X, W)
+    got = y.cpu().numpy()
+    # output features with no Inf or NaN weight; of those, the ones whose
+    # float32 sums stay finite (exponents up to 254 can overflow float32
+    # partial sums where the float64 sum is finite)
+    fin = np.isfinite(ref).all(axis=0)
+    ok = fin & np.isfinite(got).all(axis=0)
+    assert 0 < fin.sum() < N and ok.sum() >= fin.sum() - 8
+    assert _rel(got[:, ok], ref[:, ok]) < TOL
+    assert not np.isfinite(got[:, ~fin]).all(axis=0).any()
