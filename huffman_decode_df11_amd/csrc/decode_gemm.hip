@@ -895,12 +895,16 @@ decode_gemm_wide_kernel(GemmArgs g)
 //     element), then add one to the slot's ready counter.  The next
 //     segment's stream words and sign+mantissa bytes are loaded before the
 //     current one is decoded.
-//   matrix-core waves (waves 0 .. nm - 1, nm = ceil(B / 32)): wave m owns
-//     the 32-row batch tile m and one 32 x 32 float32 accumulator; per tile
-//     it waits for the slot's ready counter to reach the segments decoded
-//     into that slot so far, runs the tile's 32 k-steps of
-//     v_mfma_f32_32x32x16_bf16 from the plane, and adds one to the slot's
-//     release counter.  Each y element has one writer (unless K is split).
+//   matrix-core waves (waves 0 .. nm - 1, nm = ceil(ceil(B / 32) / TPW)):
+//     wave m owns the TPW 32-row batch tiles m TPW .. m TPW + TPW - 1 and a
+//     32 x 32 float32 accumulator for each; per tile it waits for the slot's
+//     ready counter to reach the segments decoded into that slot so far,
+//     runs the tile's 32 k-steps of v_mfma_f32_32x32x16_bf16 from the plane
+//     (each B operand read once from LDS and used by TPW products), and
+//     adds one to the slot's release counter.  Each y element has one writer
+//     (unless K is split).  The decode bounds the kernel, so every wave the
+//     products do not need decodes: two batch tiles per matrix-core wave
+//     leave more decoder waves at large B.
 //
 // Waits are bounded spins on LDS (s_sleep between reads); a wait that runs
 // out (not reachable with well-formed arguments: every counter is advanced
@@ -987,6 +991,14 @@ __device__ __forceinline__ uint4 merge_hi(uint4 v, uint2 sm)
     return make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// 16 bytes from a pointer known to be global memory (a global, not a flat,
+// load: it does not count against the LDS wait counter)
+__device__ __forceinline__ uint4 ld_global128(const __attribute__((address_space(1))) uint8_t *p)
+{
+    const v4u32 v = *(const __attribute__((address_space(1))) v4u32 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // One segment job of a decoder wave, loaded ahead of its decode.
 struct PipeJob {
     SegLoad L;
@@ -1044,9 +1056,10 @@ __device__ __forceinline__ bool pipe_next(const GemmArgs &g, PipeSeq &p, uint32_
     return pipe_unit(g, p, n_units);
 }
 
-template <int K, int MT, int W>
+template <int K, int MT, int W, int TPW>
 __global__ void __launch_bounds__(W * 64) decode_gemm_pipe_kernel(GemmArgs g, uint32_t nslot)
 {
+    static_assert((TPW == 1 || TPW == 2) && TPW <= MT, "batch tiles per matrix-core wave");
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1060,44 +1073,63 @@ __global__ void __launch_bounds__(W * 64) decode_gemm_pipe_kernel(GemmArgs g, ui
     stage_tables<K, W * 64>(fast, chain, g.fast, g.chain, g.n_chain);
     __syncthreads();
 
-    const uint32_t nm = (g.B + 31) / 32;   // matrix-core waves, one per batch tile
+    // matrix-core waves, TPW batch tiles each (with two, a tile past the
+    // rows of x reads zero rows of the packed x, or row B - 1 in place, and
+    // its sums are not stored)
+    const uint32_t nm = ((g.B + 31) / 32 + TPW - 1) / TPW;
     const uint32_t n_units = g.n_rowblocks * g.split;
     const bool stored = g.counts != nullptr;
 
     if (wave < nm) {
-        // ---- matrix-core wave: batch tile m = wave
-        const uint32_t m = wave;
-        const bool writes_w = g.w_debug && m == 0;
+        // ---- matrix-core wave: batch tiles m0 .. m0 + TPW - 1
+        const uint32_t m0 = wave * TPW;
+        const bool writes_w = g.w_debug && m0 == 0;
         uint32_t cum[kPipeMaxSlots] = {};
         bool ok = true;
-        f32x16 acc;
+        f32x16 acc[TPW];
 #pragma unroll
-        for (int j = 0; j < 16; j++) acc[j] = 0.0f;
-        // one tile from ring slot `sl`: x operands of k-step ks at xb + ks *
-        // xs bytes (packed: the operand kilobyte of batch tile m; in place:
-        // row m * 32 + n_l, clamped to row B - 1, whose products only reach
-        // rows of y that are not stored), issued before the wait; no branch
-        // inside the k-loop (w_debug calls run their own copy of it)
+        for (int t = 0; t < TPW; t++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc[t][j] = 0.0f;
+        // one tile from ring slot `sl`: x operands of k-step ks and batch
+        // tile m0 + t at xb[t] + ks * xs bytes (packed: the operand kilobyte
+        // of that tile; in place: row (m0 + t) * 32 + n_l, clamped to row
+        // B - 1, whose products only reach rows of y that are not stored),
+        // issued before the wait; no branch inside the k-loop (w_debug calls
+        // run their own copy of it)
         auto run_tile = [&](auto wd_tag, const PipeSeq &p, uint32_t sl, uint32_t target) {
             constexpr bool kWD = decltype(wd_tag)::value;
             uint32_t ln = lane;
             asm volatile("" : "+v"(ln));
-            const uint32_t brow = min(m * 32 + (ln & 31u), g.B - 1);
-            const uint8_t *xb = g.xo ? reinterpret_cast<const uint8_t *>(g.xo + ((uint64_t)p.kt * 32u * MT + m) * 64 + ln)
-                                     : reinterpret_cast<const uint8_t *>(g.x + (uint64_t)brow * g.K + p.kt * kTC + (ln >> 5) * 8);
-            const uint32_t xs = g.xo ? MT * 64u * 16u : 32u;
-            constexpr int kAhead = 8;
-            uint4 xa[kAhead];
+            constexpr int kAhead = 8 / TPW;   // k-steps of x operands in flight per batch tile
+            // global address space named explicitly: a generic (flat) load
+            // would also count against the LDS wait counter, and every wait
+            // for a plane read would then wait for the x loads in flight
+            const __attribute__((address_space(1))) uint8_t *xb[TPW];
 #pragma unroll
-            for (int i = 0; i < kAhead; i++) xa[i] = *reinterpret_cast<const uint4 *>(xb + i * xs);
+            for (int t = 0; t < TPW; t++) {
+                const uint32_t brow = min((m0 + t) * 32 + (ln & 31u), g.B - 1);
+                const uint8_t *gp = g.xo ? reinterpret_cast<const uint8_t *>(g.xo + ((uint64_t)p.kt * 32u * MT + m0 + t) * 64 + ln)
+                                         : reinterpret_cast<const uint8_t *>(g.x + (uint64_t)brow * g.K + p.kt * kTC + (ln >> 5) * 8);
+                xb[t] = (const __attribute__((address_space(1))) uint8_t *)gp;
+            }
+            const uint32_t xs = g.xo ? MT * 64u * 16u : 32u;
+            uint4 xa[kAhead][TPW];
+#pragma unroll
+            for (int i = 0; i < kAhead; i++)
+#pragma unroll
+                for (int t = 0; t < TPW; t++) {
+                    xa[i][t] = ld_global128(xb[t]);
+                    xb[t] += xs;
+                }
             ok &= lds_wait_geq(ctr + 4 * sl, target);
             const uint32_t rb = p.unit / g.split;
             const uint32_t pl = planes + sl * kPipePlane + 16u * ((ln >> 5) * kTR + (ln & 31u));
             uint16_t *wd = nullptr;
             if constexpr (kWD) wd = g.w_debug + (uint64_t)(rb * kTR + (ln & 31u)) * g.K + p.kt * kTC + (ln >> 5) * kKC;
             // k-step i: groups c = 2 i + lane / 32, row n_l; the plane's
-            // operands are read kWAhead k-steps before their product
-            constexpr int kWAhead = 4;
+            // operands are read kWAhead k-steps before their products
+            constexpr int kWAhead = 4 / TPW;
             v4u32 wq[kWAhead];
 #pragma unroll
             for (int i = 0; i < kWAhead; i++) wq[i] = *(const lds_u4 *)(size_t)(pl + 16u * (2 * i * kTR));
@@ -1106,9 +1138,15 @@ __global__ void __launch_bounds__(W * 64) decode_gemm_pipe_kernel(GemmArgs g, ui
                 const v4u32 wb = wq[i % kWAhead];
                 if (i + kWAhead < 32) wq[i % kWAhead] = *(const lds_u4 *)(size_t)(pl + 16u * (2 * (i + kWAhead) * kTR));
                 if constexpr (kWD) *reinterpret_cast<uint4 *>(wd + 2 * i * kKC) = make_uint4(wb.x, wb.y, wb.z, wb.w);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[i % kAhead]),
-                                                              __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
-                if (i + kAhead < 32) xa[i % kAhead] = *reinterpret_cast<const uint4 *>(xb + (i + kAhead) * xs);
+#pragma unroll
+                for (int t = 0; t < TPW; t++) {
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[i % kAhead][t]),
+                                                                     __builtin_bit_cast(bf16x8, wb), acc[t], 0, 0, 0);
+                    if (i + kAhead < 32) {
+                        xa[i % kAhead][t] = ld_global128(xb[t]);
+                        xb[t] += xs;
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);   // keeps the loads ahead of their products as written
             }
         };
@@ -1129,21 +1167,25 @@ __global__ void __launch_bounds__(W * 64) decode_gemm_pipe_kernel(GemmArgs g, ui
             slot = slot + 1 == nslot ? 0 : slot + 1;
             const bool last = p.kt + 1 == p.kt1;
             if (last) {
-                // lane holds n = rb*32 + lane%32, b = 32*m + 8*blk + 4*(lane/32) + e
+                // lane holds n = rb*32 + lane%32, b = 32*(m0+t) + 8*blk + 4*(lane/32) + e
                 // (addresses formed here, not kept across the tile loop)
                 uint32_t ln = lane, nB = g.B, nN = g.N;
                 asm volatile("" : "+v"(ln), "+s"(nB), "+s"(nN));
 #pragma unroll
-                for (int blk = 0; blk < 4; blk++)
+                for (int t = 0; t < TPW; t++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const uint32_t b = m * 32 + 8 * blk + 4 * (ln >> 5) + e;
-                        if (b < nB)
-                            store_y_at(g, (uint64_t)b * nN + rb * kTR + (ln & 31u),
-                                       ok ? acc[4 * blk + e] : __builtin_nanf(""), g.split > 1);
-                    }
+                    for (int blk = 0; blk < 4; blk++)
 #pragma unroll
-                for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+                        for (int e = 0; e < 4; e++) {
+                            const uint32_t b = (m0 + t) * 32 + 8 * blk + 4 * (ln >> 5) + e;
+                            if (b < nB)
+                                store_y_at(g, (uint64_t)b * nN + rb * kTR + (ln & 31u),
+                                           ok ? acc[t][4 * blk + e] : __builtin_nanf(""), g.split > 1);
+                        }
+#pragma unroll
+                for (int t = 0; t < TPW; t++)
+#pragma unroll
+                    for (int j = 0; j < 16; j++) acc[t][j] = 0.0f;
             }
             more = pipe_next(g, p, n_units);
         }
@@ -1493,7 +1535,7 @@ uint32_t pipe_lds_bytes(uint32_t nslot, uint32_t fast_bits, uint32_t n_tables)
 
 // Pipelined launch: as many ring slots (up to 3) as fit beside the tables;
 // K split when there are too few row blocks to fill every resident slot.
-template <int K, int MT>
+template <int K, int MT, int TPW>
 int launch_pipe(GemmArgs a, uint32_t n_tables, uint32_t forced_split, hipStream_t st)
 {
     constexpr int W = 16;   // 1024 threads: the most a workgroup holds
@@ -1504,7 +1546,7 @@ int launch_pipe(GemmArgs a, uint32_t n_tables, uint32_t forced_split, hipStream_
     if (a.n_segments >= (1ull << 32) || (uint64_t)a.n_rowblocks * a.tiles_per_row >= (1ull << 32))
         return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: the pipelined kernel takes fewer than 2^32 segments and tiles");
     const uint32_t lds = pipe_lds_bytes(nslot, K, n_tables);
-    const void *kern = (const void *)decode_gemm_pipe_kernel<K, MT, W>;
+    const void *kern = (const void *)decode_gemm_pipe_kernel<K, MT, W, TPW>;
     const uint32_t slots = (uint32_t)(cu_count() * resident_groups(kern, W * 64, lds));
     uint32_t split = 1;
     if (forced_split) split = forced_split;
@@ -1516,10 +1558,28 @@ int launch_pipe(GemmArgs a, uint32_t n_tables, uint32_t forced_split, hipStream_
     if (a.split > 1) clear_y(a, st);
     const uint32_t units = a.n_rowblocks * a.split;
     const uint32_t groups = std::min<uint32_t>(units, slots);
-    hipLaunchKernelGGL((decode_gemm_pipe_kernel<K, MT, W>), dim3(groups), dim3(W * 64), lds, st, a, nslot);
+    hipLaunchKernelGGL((decode_gemm_pipe_kernel<K, MT, W, TPW>), dim3(groups), dim3(W * 64), lds, st, a, nslot);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
     return DF11_OK;
+}
+
+// batch tiles per matrix-core wave of the pipelined kernel: the tuning's
+// choice, else by the batch tiles of x
+uint32_t pipe_tiles_per_wave(uint32_t B, uint32_t forced)
+{
+    // up_proj, x packed: one tile per wave 63.1 / 69.3 / 75.0 / 95.2 us at
+    // 128 / 160 / 192 / 256 rows, two 65.7 / 69.0 / 70.0 / 77.6
+    if (forced) return forced;
+    return B <= 128 ? 1u : 2u;
+}
+
+template <int K, int MT>
+int launch_pipe_mt(GemmArgs a, uint32_t n_tables, uint32_t forced_split, uint32_t tpw, hipStream_t st)
+{
+    if constexpr (MT >= 2)
+        if (tpw == 2) return launch_pipe<K, MT, 2>(a, n_tables, forced_split, st);
+    return launch_pipe<K, MT, 1>(a, n_tables, forced_split, st);
 }
 
 template <int K>
@@ -1546,6 +1606,14 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
         if (a.B <= 2 && !a.w_debug && vec_waves) kernel = DF11_GEMM_VECTOR;
         else if (a.B <= (ws ? 32u : 40u) && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems))
             kernel = DF11_GEMM_SEGMENT;
+        // above 32 rows with x packed, the pipelined kernel (up_proj, 8
+        // weight copies cycled: 54.9 / 55.3 / 57.2 / 63.1 / 69.0 / 70.0 /
+        // 77.6 us at 33 / 64 / 96 / 128 / 160 / 192 / 256 rows against 55.6
+        // / 56.1 / 70.1 / 69.5 / 94.5 / 95.7 / 96.6 on the wide kernel); with
+        // x read in place it is slower than the wide kernel (145 against
+        // 97 us at 256 rows)
+        else if (ws && mt >= 2 && !a.w_debug && pipe_lds_bytes(2, K, n_tables) <= 160u * 1024u)
+            kernel = DF11_GEMM_PIPE;
         else kernel = mt <= 1 ? DF11_GEMM_TILED : DF11_GEMM_WIDE;
     }
     if (kernel == DF11_GEMM_VECTOR) {
@@ -1570,10 +1638,11 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
         a.xo_tiles = tiles;
     }
     if (kernel == DF11_GEMM_PIPE) {
-        if (mt <= 1) return launch_pipe<K, 1>(a, n_tables, tune.split, st);
-        if (mt <= 2) return launch_pipe<K, 2>(a, n_tables, tune.split, st);
-        if (mt <= 4) return launch_pipe<K, 4>(a, n_tables, tune.split, st);
-        return launch_pipe<K, 8>(a, n_tables, tune.split, st);
+        const uint32_t tpw = pipe_tiles_per_wave(a.B, tune.tiles_per_wave);
+        if (mt <= 1) return launch_pipe_mt<K, 1>(a, n_tables, tune.split, tpw, st);
+        if (mt <= 2) return launch_pipe_mt<K, 2>(a, n_tables, tune.split, tpw, st);
+        if (mt <= 4) return launch_pipe_mt<K, 4>(a, n_tables, tune.split, tpw, st);
+        return launch_pipe_mt<K, 8>(a, n_tables, tune.split, tpw, st);
     }
     if (kernel == DF11_GEMM_SEGMENT) {
         if (a.w_debug || mt > 2)
@@ -1630,6 +1699,8 @@ int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
     if (t.one_writer && (t.parts > 1 || t.split > 1))
         return df11::fail(DF11_E_ARG, "tuning: one_writer takes parts and split 1");
     if (t.parts > (1u << 16) || t.split > (1u << 16)) return df11::fail(DF11_E_ARG, "tuning: parts or split too large");
+    if (t.tiles_per_wave && (t.kernel != DF11_GEMM_PIPE || t.tiles_per_wave > 2))
+        return df11::fail(DF11_E_ARG, "tuning: tiles_per_wave %u (0, or 1 or 2 with the pipelined kernel)", t.tiles_per_wave);
     return DF11_OK;
 }
 

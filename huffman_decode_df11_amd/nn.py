@@ -47,18 +47,18 @@ class DF11Linear(torch.nn.Module):
     """A linear layer y = x W^T + b with W [out_features, in_features] held
     compressed.  mode "fused" (needs out % 32 == 0 and in % 512 == 0) runs
     the fused product (x packed in operand order above 32 rows) for up to
-    fused_max_rows rows of x and decode + matmul above (default 128: on an
-    up_proj-shaped weight, 14336 x 4096, the fused call measured 58.6 us at
-    64 rows and 73.4 us at 128 against about 79 and 82 us for decoding the
-    tile-ordered weight and calling torch.matmul; at 192 rows 95-98 against
-    91 us); mode "decode" always decodes into the shared buffer and calls
-    torch.matmul.  "auto" picks "fused" when the shape allows it.
+    fused_max_rows rows of x and decode + matmul above (default 256, the
+    fused kernels' limit: on an up_proj-shaped weight, 14336 x 4096, the
+    fused call measured 55 / 63 / 78 us at 64 / 128 / 256 rows against about
+    79 / 82 / 105 us for decoding the tile-ordered weight and calling
+    torch.matmul); mode "decode" always decodes into the shared buffer and
+    calls torch.matmul.  "auto" picks "fused" when the shape allows it.
     deterministic=True asks the fused kernels for one writer per element of
     y (df11_gemm_tuning one_writer): the same output on every run, where
     weights with few 32-row blocks (4096 x 4096, 4096 x 14336) otherwise
     split a row block's work and add float32 partial sums atomically."""
 
-    fused_max_rows = 128
+    fused_max_rows = 256
 
     def __init__(self, weight, bias: Optional[torch.Tensor] = None, mode: str = "auto", device="cuda",
                  codebook=None, deterministic: bool = False):

@@ -378,7 +378,9 @@ typedef struct df11_gemm_tuning {
                               order (no K ranges, no segment runs: parts and split 1), so a
                               float32 y is the same on every run; slower for weights with too few
                               row blocks to fill the device */
-    uint32_t reserved[3];  /* zero */
+    uint32_t tiles_per_wave; /* pipelined kernel: 0 = by B, else 1 or 2 batch tiles of 32 rows of x
+                              per matrix-core wave */
+    uint32_t reserved[2];  /* zero */
 } df11_gemm_tuning;
 
 /* Bytes of the workspace df11_decode_gemm_ex can use for B rows of x with

@@ -584,6 +584,8 @@ def test_one_writer_is_the_same_on_every_run(B):
 @pytest.mark.parametrize("N,K,B,extra", [(256, 4096, 1, dict()), (256, 4096, 8, dict()), (256, 4096, 33, dict()),
                                          (256, 4096, 64, dict(split=3)), (256, 4096, 100, dict(one_writer=1)),
                                          (256, 4096, 200, dict()), (256, 4096, 256, dict(one_writer=1)),
+                                         (256, 4096, 160, dict(tiles_per_wave=1)),
+                                         (256, 4096, 64, dict(tiles_per_wave=2)),
                                          (96, 1536, 17, dict()), (96, 1536, 250, dict(split=1))])
 def test_pipelined_kernel_matches_oracle(N, K, B, extra):
     """Few row blocks (the K range of a row block split across workgroups,
@@ -605,6 +607,26 @@ def test_pipelined_kernel_matches_oracle(N, K, B, extra):
     torch.cuda.synchronize()
     got16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got16, orc.round_bf16(y32.cpu().numpy()))
+
+
+@pytest.mark.parametrize("B,tpw", [(33, 2), (96, 2), (160, 2), (230, 1), (256, 2)])
+def test_pipelined_kernel_x_in_place(B, tpw):
+    """x read in place (no workspace): rows past B, in the last batch tile
+    and in a matrix-core wave's second tile beyond the rows of x, are
+    clamped to row B - 1, and their sums are not stored.  y against the
+    oracle; every element of a y prefilled with NaN written."""
+    N, K = 128, 2048
+    _say("case gemm pipelined x in place B=%d tiles_per_wave=%d" % (B, tpw))
+    W = synth.normal_bf16(N * K, 0.02, seed=92).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=93)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    api.decode_gemm(dt, _x_to_gpu(X), out=y, workspace=None,
+                    tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_PIPE, tiles_per_wave=tpw, one_writer=1))
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert _rel(got, orc.gemm_f64(X, W)) < TOL
 
 
 @pytest.mark.parametrize("B", [1, 64, 256])

@@ -117,6 +117,9 @@ def test_fused_segment_kernel_refused_when_staging_exceeds_64k(kind):
     (8, dict(kernel=_lib.DF11_GEMM_PIPE, parts=2), False, False),   # parts without the segment kernels
     (64, dict(kernel=_lib.DF11_GEMM_PIPE, split=2), True, False),   # BF16 y: one writer per element
     (64, dict(kernel=_lib.DF11_GEMM_PIPE, split=2, one_writer=1), False, False),
+    (64, dict(kernel=_lib.DF11_GEMM_PIPE, tiles_per_wave=3), False, False),   # 1 or 2 batch tiles per wave
+    (64, dict(kernel=_lib.DF11_GEMM_WIDE, tiles_per_wave=2), False, False),   # only on the pipelined kernel
+    (64, dict(tiles_per_wave=1), False, False),
     (8, dict(kernel=_lib.DF11_GEMM_SEGMENT, parts=2, one_writer=1), False, False),  # one writer: parts 1
     (64, dict(kernel=_lib.DF11_GEMM_WIDE, split=2, one_writer=1), False, False),    # and split 1
 ])
