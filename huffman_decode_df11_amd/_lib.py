@@ -16,7 +16,8 @@ DF11_FAST_BITS_DEFAULT = 11
 DF11_Y_F32 = 0
 DF11_Y_BF16 = 1
 DF11_STORES_AUTO, DF11_STORES_CACHED, DF11_STORES_STREAMING = 0, 1, 2
-DF11_GEMM_AUTO, DF11_GEMM_SEGMENT, DF11_GEMM_WIDE, DF11_GEMM_TILED, DF11_GEMM_VECTOR, DF11_GEMM_PIPE = 0, 1, 2, 3, 4, 5
+DF11_GEMM_AUTO, DF11_GEMM_SEGMENT, DF11_GEMM_WIDE, DF11_GEMM_TILED, DF11_GEMM_VECTOR, DF11_GEMM_PIPE, DF11_GEMM_RING = \
+    0, 1, 2, 3, 4, 5, 6
 
 u32, u64 = ctypes.c_uint32, ctypes.c_uint64
 

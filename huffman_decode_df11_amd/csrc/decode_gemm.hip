@@ -999,6 +999,12 @@ __device__ __forceinline__ uint4 ld_global128(const __attribute__((address_space
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ uint2 ld_global64(const __attribute__((address_space(1))) uint8_t *p)
+{
+    const v2u32 v = *(const __attribute__((address_space(1))) v2u32 *)p;
+    return make_uint2(v.x, v.y);
+}
+
 // One segment job of a decoder wave, loaded ahead of its decode.
 struct PipeJob {
     SegLoad L;
@@ -1283,6 +1289,197 @@ __global__ void __launch_bounds__(W * 64) decode_gemm_pipe_kernel(GemmArgs g, ui
     };
     // two job buffers in turn: one decoded while the other's loads land
     PipeJob ja, jb;
+    bool ha = next_job(ja);
+    while (ha) {
+        const bool hb = next_job(jb);
+        process(ja);
+        if (!hb) break;
+        ha = next_job(ja);
+        process(jb);
+    }
+}
+
+// Exponent-ring kernel: the pipelined kernel's hand-over with planes that
+// hold only the rotated exponents (16 KB per tile instead of a 32 KB BF16
+// plane), so that three ring slots and the tables fit in 80 KB and two
+// 12-wave workgroups share a CU: 22 decoder waves per CU at one batch tile
+// instead of 15.
+//   decoder waves: decode each segment of the tile sequence into its slot's
+//     exponent plane (count, scan, emit; no sign+mantissa bytes and no
+//     merge), then add one to the slot's ready counter.
+//   matrix-core wave m (batch tile m): per k-step, 8 exponent bytes from the
+//     plane and the same 8 sign+mantissa bytes, loaded from global memory
+//     kAhead k-steps ahead with x, give the B operand of
+//     v_mfma_f32_32x32x16_bf16 (two bit-selects and two byte permutes per 4
+//     weights).
+// Waits and counters as in the pipelined kernel above.
+constexpr uint32_t kRingSlots = 3;
+constexpr uint32_t kRingGuard = 16;   // emit_codes writes from position >= 3
+
+uint32_t ring_lds_bytes(uint32_t fast_bits, uint32_t n_tables)
+{
+    return kRingGuard + kRingSlots * kTile + 64 + (8u << fast_bits) + n_tables * 512u;
+}
+static_assert(kRingGuard + kRingSlots * kTile < 65536, "ring planes beyond the emit cursor");
+
+template <int K, int MT, int W>
+__global__ void __launch_bounds__(W * 64, 6) decode_gemm_ring_kernel(GemmArgs g)
+{
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = lane_id();
+    // [guard][3 exponent planes][ready[4], release[4]][tables]
+    const uint32_t planes = lds0 + kRingGuard;
+    const uint32_t ctr = planes + kRingSlots * kTile;
+    const uint32_t fast = ctr + 64;
+    const uint32_t chain = fast + (8u << K);
+    if (threadIdx.x < 8) st32(ctr + 4 * threadIdx.x, 0u);
+    stage_tables<K, W * 64>(fast, chain, g.fast, g.chain, g.n_chain);
+    __syncthreads();
+
+    const uint32_t nm = (g.B + 31) / 32;
+    const uint32_t n_units = g.n_rowblocks * g.split;
+    const bool stored = g.counts != nullptr;
+
+    if (wave < nm) {
+        // ---- matrix-core wave: batch tile m = wave
+        const uint32_t m = wave;
+        const bool writes_w = g.w_debug && m == 0;
+        uint32_t cum[kRingSlots] = {};
+        bool ok = true;
+        f32x16 acc;
+#pragma unroll
+        for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+        // k-step i of a tile: column group c = 2 i + lane / 32, row n_l; its
+        // 8 weights sit at tile-order bytes c * 256 + n_l * 8 of the
+        // exponent plane and of the tile's sign+mantissa bytes
+        auto run_tile = [&](auto wd_tag, const PipeSeq &p, uint32_t sl, uint32_t target) {
+            constexpr bool kWD = decltype(wd_tag)::value;
+            uint32_t ln = lane;
+            asm volatile("" : "+v"(ln));
+            constexpr int kAhead = 4;
+            const uint32_t brow = min(m * 32 + (ln & 31u), g.B - 1);
+            const uint8_t *gx = g.xo ? reinterpret_cast<const uint8_t *>(g.xo + ((uint64_t)p.kt * 32u * MT + m) * 64 + ln)
+                                     : reinterpret_cast<const uint8_t *>(g.x + (uint64_t)brow * g.K + p.kt * kTC + (ln >> 5) * 8);
+            const __attribute__((address_space(1))) uint8_t *xb = (const __attribute__((address_space(1))) uint8_t *)gx;
+            const uint32_t xs = g.xo ? MT * 64u * 16u : 32u;
+            const uint32_t lo_off = (ln >> 5) * (kTR * kKC) + (ln & 31u) * kKC;
+            const __attribute__((address_space(1))) uint8_t *sb =
+                (const __attribute__((address_space(1))) uint8_t *)(g.sm + (uint64_t)p.t * kTile + lo_off);
+            uint4 xa[kAhead];
+            uint2 sv[kAhead];
+#pragma unroll
+            for (int i = 0; i < kAhead; i++) {
+                xa[i] = ld_global128(xb);
+                xb += xs;
+                sv[i] = ld_global64(sb);
+                sb += 2 * kTR * kKC;
+            }
+            ok &= lds_wait_geq(ctr + 4 * sl, target);
+            const uint32_t rb = p.unit / g.split;
+            const uint32_t ep = planes + sl * kTile + lo_off;
+            uint16_t *wd = nullptr;
+            if constexpr (kWD) wd = g.w_debug + (uint64_t)(rb * kTR + (ln & 31u)) * g.K + p.kt * kTC + (ln >> 5) * kKC;
+            constexpr int kEAhead = 2;
+            uint2 rq[kEAhead];
+#pragma unroll
+            for (int i = 0; i < kEAhead; i++) rq[i] = ld64(ep + i * 2 * kTR * kKC);
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                const uint2 rx = rq[i % kEAhead];
+                if (i + kEAhead < 32) rq[i % kEAhead] = ld64(ep + (i + kEAhead) * 2 * kTR * kKC);
+                const uint2 svi = sv[i % kAhead];
+                const uint2 lo = assemble4(svi.x, rx.x), hi = assemble4(svi.y, rx.y);
+                if constexpr (kWD) *reinterpret_cast<uint4 *>(wd + 2 * i * kKC) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[i % kAhead]),
+                                                              __builtin_bit_cast(bf16x8, v4u32{lo.x, lo.y, hi.x, hi.y}),
+                                                              acc, 0, 0, 0);
+                if (i + kAhead < 32) {
+                    xa[i % kAhead] = ld_global128(xb);
+                    xb += xs;
+                    sv[i % kAhead] = ld_global64(sb);
+                    sb += 2 * kTR * kKC;
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keeps the loads ahead of their products as written
+            }
+        };
+        PipeSeq p{blockIdx.x, 0, 0, 0, 0, 0, 0};
+        uint32_t slot = 0;
+        for (bool more = pipe_unit(g, p, n_units); more;) {
+#pragma unroll
+            for (uint32_t i = 0; i < kRingSlots; i++)
+                if (i == slot) cum[i] += p.nseg;
+            uint32_t target = cum[0];
+#pragma unroll
+            for (uint32_t i = 1; i < kRingSlots; i++)
+                if (i == slot) target = cum[i];
+            if (writes_w) run_tile(std::true_type{}, p, slot, target);
+            else run_tile(std::false_type{}, p, slot, target);
+            const uint32_t rb = p.unit / g.split;
+            lds_signal(ctr + 16 + 4 * slot, lane);
+            slot = slot + 1 == kRingSlots ? 0 : slot + 1;
+            if (p.kt + 1 == p.kt1) {
+                // lane holds n = rb*32 + lane%32, b = 32*m + 8*blk + 4*(lane/32) + e
+                uint32_t ln = lane, nB = g.B, nN = g.N;
+                asm volatile("" : "+v"(ln), "+s"(nB), "+s"(nN));
+#pragma unroll
+                for (int blk = 0; blk < 4; blk++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const uint32_t b = m * 32 + 8 * blk + 4 * (ln >> 5) + e;
+                        if (b < nB)
+                            store_y_at(g, (uint64_t)b * nN + rb * kTR + (ln & 31u),
+                                       ok ? acc[4 * blk + e] : __builtin_nanf(""), g.split > 1);
+                    }
+#pragma unroll
+                for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+            }
+            more = pipe_next(g, p, n_units);
+        }
+        return;
+    }
+
+    // ---- decoder wave d of nd: segments d, d + nd, ... of the sequence
+    const uint32_t nd = W - nm, d = wave - nm;
+    PipeSeq p{blockIdx.x, 0, 0, 0, 0, 0, 0};
+    bool more = pipe_unit(g, p, n_units);
+    uint32_t c = 0;               // segments of the sequence before tile p
+    uint32_t r = d;               // running index of this wave's next segment
+    uint32_t slot = 0, use = 0;   // ring slot of tile p and its earlier uses
+    struct RingJob {
+        SegLoad L;
+        uint64_t ts;
+        uint32_t q;
+    };
+    // the next job's records and words are loaded before the current job
+    // is decoded; a job past the sequence loads segment 0 and is not decoded
+    auto next_job = [&](RingJob &j) {
+        while (more && r >= c + p.nseg) {
+            c += p.nseg;
+            more = pipe_next(g, p, n_units);
+            if (++slot == kRingSlots) {
+                slot = 0;
+                use++;
+            }
+        }
+        const bool has = more;
+        const uint32_t s = has ? p.first + (r - c) : 0;
+        if (has) r += nd;
+        j.L = load_segment(g, s, lane);
+        j.ts = has ? (uint64_t)p.t * kTile : 0;
+        j.q = slot | use << 2;
+        return has;
+    };
+    auto process = [&](const RingJob &j) {
+        asm volatile("" ::"v"(j.L.own.x), "v"(j.L.own.y), "v"(j.L.own.z), "v"(j.L.own.w), "v"(j.L.next), "v"(j.L.gap),
+                     "v"(j.L.count));
+        const uint32_t jslot = j.q & 3u, juse = j.q >> 2;
+        lds_wait_geq(ctr + 16 + 4 * jslot, juse * nm);
+        decode_into_plane<K>(j.L, j.ts, planes + jslot * kTile, stored, fast, chain, lane);
+        lds_signal(ctr + 4 * jslot, lane);
+    };
+    RingJob ja, jb;
     bool ha = next_job(ja);
     while (ha) {
         const bool hb = next_job(jb);
@@ -1582,6 +1779,35 @@ int launch_pipe_mt(GemmArgs a, uint32_t n_tables, uint32_t forced_split, uint32_
     return launch_pipe<K, MT, 1>(a, n_tables, forced_split, st);
 }
 
+// Exponent-ring launch: 12-wave workgroups, two per CU where the planes
+// and tables fit in 80 KB; K split as for the pipelined kernel.
+template <int K, int MT>
+int launch_ring(GemmArgs a, uint32_t n_tables, uint32_t forced_split, hipStream_t st)
+{
+    constexpr int W = 12;
+    const uint32_t lds = ring_lds_bytes(K, n_tables);
+    if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: exponent-ring planes and tables do not fit in LDS");
+    if (a.xo && a.xo_tiles != (uint32_t)MT) return df11::fail(DF11_E_ARG, "decode_gemm: packed x tiles");
+    if (a.n_segments >= (1ull << 32) || (uint64_t)a.n_rowblocks * a.tiles_per_row >= (1ull << 32))
+        return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: the exponent-ring kernel takes fewer than 2^32 segments and tiles");
+    const void *kern = (const void *)decode_gemm_ring_kernel<K, MT, W>;
+    const uint32_t slots = (uint32_t)(cu_count() * resident_groups(kern, W * 64, lds));
+    uint32_t split = 1;
+    if (forced_split) split = forced_split;
+    else if (2 * a.n_rowblocks <= slots) split = (slots + a.n_rowblocks - 1) / a.n_rowblocks;
+    split = std::max(1u, std::min(split, a.tiles_per_row));
+    if (a.y_bf16) split = 1;
+    a.tiles_per_split = (a.tiles_per_row + split - 1) / split;
+    a.split = (a.tiles_per_row + a.tiles_per_split - 1) / a.tiles_per_split;
+    if (a.split > 1) clear_y(a, st);
+    const uint32_t units = a.n_rowblocks * a.split;
+    const uint32_t groups = std::min<uint32_t>(units, slots);
+    hipLaunchKernelGGL((decode_gemm_ring_kernel<K, MT, W>), dim3(groups), dim3(W * 64), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
+    return DF11_OK;
+}
+
 template <int K>
 int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_gemm_tuning &tune_in, void *ws,
               hipStream_t st)
@@ -1589,12 +1815,10 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
     // one writer per element of y: no segment runs and no K ranges
     df11_gemm_tuning tune = tune_in;
     if (tune.one_writer) tune.parts = tune.split = 1;
-    // Automatic choice: segment-parallel up to 40 rows of x (one batch tile
-    // to 32, two above) when its staging fits; from 41 rows the wide kernel
-    // is faster (up_proj: 58.5 against 60.7 us at 33 rows, 66.8 against
-    // 64.9 at 48, 76.4 against 67.7 at 64).  With x packed in a workspace
-    // the wide kernel is the faster one from 33 rows (up_proj, packed: 56.6
-    // against 58.1 us at 33 rows, 56.5 against 58.3 at 40).  w_debug calls
+    // Automatic choice: one or two rows of x the vector kernel, up to 32 the
+    // segment-parallel one when its staging fits (up_proj: 42.6 / 48.3 us
+    // at 8 / 32 rows against 46.4 / 47.7 on the exponent-ring kernel), above
+    // that the exponent-ring and pipelined kernels (below).  w_debug calls
     // take the tile-synchronous kernel up to 32 rows, the wide one above.
     const uint32_t mt = (a.B + 31) / 32;
     const uint32_t vec_waves = vec_kernel_waves(K, n_tables, max_seg_elems);
@@ -1604,14 +1828,20 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
         // against 45.1 / 45.3 on the segment-parallel one; at 3 and 4 rows
         // it is slower, 53 us)
         if (a.B <= 2 && !a.w_debug && vec_waves) kernel = DF11_GEMM_VECTOR;
-        else if (a.B <= (ws ? 32u : 40u) && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems))
+        else if (a.B <= 32u && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems))
             kernel = DF11_GEMM_SEGMENT;
-        // above 32 rows with x packed, the pipelined kernel (up_proj, 8
-        // weight copies cycled: 54.9 / 55.3 / 57.2 / 63.1 / 69.0 / 70.0 /
-        // 77.6 us at 33 / 64 / 96 / 128 / 160 / 192 / 256 rows against 55.6
-        // / 56.1 / 70.1 / 69.5 / 94.5 / 95.7 / 96.6 on the wide kernel); with
-        // x read in place it is slower than the wide kernel (145 against
-        // 97 us at 256 rows)
+        // 33 to 128 rows: the exponent-ring kernel, x packed (up_proj, 8
+        // weight copies cycled: 50.1 / 50.3 / 52.7 / 59.2 us at 33 / 64 / 96
+        // / 128 rows against 55.6 / 56.2 / 70.1 / 69.7 on the wide kernel
+        // and 54.9 / 55.3 / 57.2 / 63.1 on the pipelined one), or x read in
+        // place up to 64 rows (48.7 / 57.8 us at 33 / 64 rows; 78 at 96)
+        else if (mt >= 2 && mt <= 4 && !a.w_debug && (ws || mt <= 2) && ring_lds_bytes(K, n_tables) <= 160u * 1024u)
+            kernel = DF11_GEMM_RING;
+        // above 128 rows with x packed, the pipelined kernel with two batch
+        // tiles per matrix-core wave (69.0 / 70.0 / 77.6 us at 160 / 192 /
+        // 256 rows against 94.5 / 95.7 / 96.6 on the wide kernel); with x
+        // read in place it is slower than the wide kernel (145 against 97
+        // us at 256 rows)
         else if (ws && mt >= 2 && !a.w_debug && pipe_lds_bytes(2, K, n_tables) <= 160u * 1024u)
             kernel = DF11_GEMM_PIPE;
         else kernel = mt <= 1 ? DF11_GEMM_TILED : DF11_GEMM_WIDE;
@@ -1636,6 +1866,12 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
                            a.x, a.B, a.K, tiles, reinterpret_cast<uint4 *>(ws));
         a.xo = reinterpret_cast<const uint4 *>(ws);
         a.xo_tiles = tiles;
+    }
+    if (kernel == DF11_GEMM_RING) {
+        if (mt <= 1) return launch_ring<K, 1>(a, n_tables, tune.split, st);
+        if (mt <= 2) return launch_ring<K, 2>(a, n_tables, tune.split, st);
+        if (mt <= 4) return launch_ring<K, 4>(a, n_tables, tune.split, st);
+        return df11::fail(DF11_E_ARG, "tuning: the exponent-ring kernel takes up to 128 rows of x");
     }
     if (kernel == DF11_GEMM_PIPE) {
         const uint32_t tpw = pipe_tiles_per_wave(a.B, tune.tiles_per_wave);
@@ -1687,12 +1923,13 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
 
 int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
 {
-    if (t.kernel > DF11_GEMM_PIPE) return df11::fail(DF11_E_ARG, "tuning: kernel %u", t.kernel);
+    if (t.kernel > DF11_GEMM_RING) return df11::fail(DF11_E_ARG, "tuning: kernel %u", t.kernel);
     if (t.row_blocks > 2 || (t.row_blocks && t.kernel != DF11_GEMM_WIDE))
         return df11::fail(DF11_E_ARG, "tuning: row_blocks %u (0, or 1 or 2 with the wide kernel)", t.row_blocks);
     if (t.parts && t.kernel != DF11_GEMM_SEGMENT && t.kernel != DF11_GEMM_VECTOR)
         return df11::fail(DF11_E_ARG, "tuning: parts applies to the segment-parallel and vector kernels");
-    if (t.split && t.kernel != DF11_GEMM_WIDE && t.kernel != DF11_GEMM_TILED && t.kernel != DF11_GEMM_PIPE)
+    if (t.split && t.kernel != DF11_GEMM_WIDE && t.kernel != DF11_GEMM_TILED && t.kernel != DF11_GEMM_PIPE &&
+        t.kernel != DF11_GEMM_RING)
         return df11::fail(DF11_E_ARG, "tuning: split applies to the wide, tile-synchronous and pipelined kernels");
     if (bf16_y && (t.parts > 1 || t.split > 1))
         return df11::fail(DF11_E_ARG, "tuning: a BF16 y has one writer per element (parts and split 1)");
@@ -1768,6 +2005,8 @@ extern "C" int df11_decode_gemm_ex(const df11_view *w, const uint16_t *x, uint32
     if (rc) return rc;
     if (!w || !x || !y) return df11::fail(DF11_E_ARG, "df11_decode_gemm: null pointer");
     if (B < 1 || B > 256) return df11::fail(DF11_E_ARG, "B = %u outside 1..256", B);
+    if (tune.kernel == DF11_GEMM_RING && B > 128)
+        return df11::fail(DF11_E_ARG, "tuning: the exponent-ring kernel takes up to 128 rows of x");
     if (w->tile_rows != kTR || w->tile_cols != kTC || w->tile_kchunk != kKC || w->align_elems != kTile ||
         w->chunk_bytes != 16 || w->seg_lanes != 64 || !w->rows || !w->cols || w->rows % kTR ||
         w->cols % kTC || w->rows * w->cols != w->n)

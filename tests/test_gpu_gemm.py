@@ -710,3 +710,117 @@ def test_pipelined_kernel_locate_pass_without_stored_counts():
     assert 0 < fin.sum() < N and ok.sum() >= fin.sum() - 8
     assert _rel(got[:, ok], ref[:, ok]) < TOL
     assert not np.isfinite(got[:, ~fin]).all(axis=0).any()
+
+
+# ---- exponent-ring kernel (DF11_GEMM_RING): the pipelined hand-over with
+# exponent-only planes, the sign+mantissa bytes merged by the matrix-core waves
+
+@pytest.mark.parametrize("N,K,B,extra", [(256, 4096, 1, dict()), (256, 4096, 8, dict()), (256, 4096, 33, dict()),
+                                         (256, 4096, 64, dict(split=3)), (256, 4096, 100, dict(one_writer=1)),
+                                         (256, 4096, 128, dict()), (96, 1536, 17, dict()),
+                                         (96, 1536, 120, dict(split=1))])
+def test_ring_kernel_matches_oracle(N, K, B, extra):
+    """Decoded weights bit-exact through w_debug, y of both calls within the
+    oracle's tolerance, and a BF16 y one rounding of the float32 one-writer
+    sums."""
+    _say("case gemm ring N=%d K=%d B=%d %s" % (N, K, B, extra))
+    W = synth.normal_bf16(N * K, 0.02, seed=94).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=95)
+    y, wd, yd = _run(W, X, tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_RING, **extra))
+    ref = orc.gemm_f64(X, W)
+    assert np.array_equal(wd, W)
+    assert _rel(y, ref) < TOL and _rel(yd, ref) < TOL
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    y32 = api.decode_gemm(dt, _x_to_gpu(X), tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_RING, one_writer=1))
+    y16 = api.decode_gemm(dt, _x_to_gpu(X), out_dtype=torch.bfloat16, tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_RING))
+    torch.cuda.synchronize()
+    got16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got16, orc.round_bf16(y32.cpu().numpy()))
+
+
+@pytest.mark.parametrize("B", [8, 64, 128])
+def test_ring_kernel_up_proj_full_size(B):
+    """Wup 14336 x 4096: the decoded weights compared in full, y against the
+    oracle on 48 sampled output features and against torch's float32 matmul
+    of the same BF16 values, and the same bits from a second call."""
+    N, K = 14336, 4096
+    _say("case gemm ring up_proj B=%d" % B)
+    W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=1)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    tune = api.gemm_tuning(kernel=_lib.DF11_GEMM_RING)
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y = api.decode_gemm(dt, _x_to_gpu(X), tuning=tune)
+    y2 = api.decode_gemm(dt, _x_to_gpu(X), tuning=tune)
+    yd = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg, tuning=tune)
+    torch.cuda.synchronize()
+    wt = torch.from_numpy(W.view(np.int16)).cuda()
+    assert torch.equal(wdbg.view(torch.int16), wt), "decoded weights differ"
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    cols = np.random.default_rng(B + 5).choice(N, size=48, replace=False)
+    ref = orc.gemm_f64(X, W[cols])
+    yt = (_x_to_gpu(X).float() @ wt.view(torch.bfloat16).float().T)
+    for out in (y, yd):
+        assert _rel(out.cpu().numpy()[:, cols], ref) < TOL
+        assert float((out - yt).norm() / yt.norm()) < TOL
+
+
+@pytest.mark.parametrize("B", [1, 64])
+@pytest.mark.parametrize("kind", ["zero", "sparse95"])
+def test_ring_kernel_long_segments(kind, B):
+    """All-zero and 95%-zero weights (segments of 7,000-8,192 elements):
+    bit-exact weights, y as the oracle's (exactly zero for the all-zero
+    weight)."""
+    N, K = 64, 4096
+    _say("case gemm ring long segments %s B=%d" % (kind, B))
+    if kind == "zero":
+        W = np.zeros((N, K), np.uint16)
+    else:
+        rng = np.random.default_rng(97)
+        W = synth.normal_bf16(N * K, 0.02, seed=98).reshape(N, K)
+        W[rng.random((N, K)) < 0.95] = 0
+    assert api.encode(W, layout=api.gemm_layout(N, K)).view.max_seg_elems > 7000
+    X = synth.activations_bf16(B, K, seed=99)
+    y, wd, yd = _run(W, X, tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_RING))
+    assert np.array_equal(wd, W)
+    ref = orc.gemm_f64(X, W)
+    for got in (y, yd):
+        if kind == "zero":
+            assert (got == 0).all()
+        else:
+            assert _rel(got, ref) < TOL
+
+
+@pytest.mark.parametrize("B", [5, 40])
+def test_ring_kernel_locate_pass_and_x_in_place(B):
+    """No stored code counts (the decoder waves walk each chunk first) on
+    adversarial weights, and x read in place without a workspace: decoded
+    weights bit-exact; y as the oracle's on the output features whose
+    largest finite weight is below 2^100 (float32 sums of K products with
+    |x| < 2^8 cannot overflow there), non-finite where the oracle's is."""
+    N, K = 96, 1536
+    _say("case gemm ring locate pass B=%d" % B)
+    W = synth.adversarial_bf16(N * K, seed=68).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=69)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    dt.view.counts = None
+    dt.view.n_counts = 0
+    tune = api.gemm_tuning(kernel=_lib.DF11_GEMM_RING)
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg, tuning=tune, workspace=None)
+    torch.cuda.synchronize()
+    assert np.array_equal(wdbg.view(torch.int16).cpu().numpy().view(np.uint16), W)
+    ref = orc.gemm_f64(X, W)
+    got = y.cpu().numpy()
+    fin = np.isfinite(ref).all(axis=0)
+    def as_f32(u):   # BF16 bits -> value (signalling NaN patterns become quiet NaN)
+        with np.errstate(invalid="ignore"):
+            return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wf = as_f32(W)
+    wmax = np.where(np.isfinite(wf), np.abs(wf), 0.0).max(axis=1)
+    safe = fin & (wmax < 2.0 ** 100)
+    assert np.abs(as_f32(X)).max() < 2.0 ** 8
+    assert 0 < safe.sum() < N
+    assert np.isfinite(got[:, safe]).all()
+    assert _rel(got[:, safe], ref[:, safe]) < TOL
+    assert not np.isfinite(got[:, ~fin]).all(axis=0).any()

@@ -113,7 +113,8 @@ def test_fused_segment_kernel_refused_when_staging_exceeds_64k(kind):
     (3, dict(kernel=_lib.DF11_GEMM_VECTOR), False, False),          # the vector kernel takes 1 or 2 rows
     (1, dict(kernel=_lib.DF11_GEMM_VECTOR), False, True),           # and no w_debug
     (2, dict(kernel=_lib.DF11_GEMM_VECTOR, parts=2), True, False),  # BF16 y: one writer per element
-    (8, dict(kernel=6), False, False),                              # no such kernel
+    (8, dict(kernel=7), False, False),                              # no such kernel
+    (129, dict(kernel=_lib.DF11_GEMM_RING), False, False),          # the exponent ring takes up to 128 rows
     (8, dict(kernel=_lib.DF11_GEMM_PIPE, parts=2), False, False),   # parts without the segment kernels
     (64, dict(kernel=_lib.DF11_GEMM_PIPE, split=2), True, False),   # BF16 y: one writer per element
     (64, dict(kernel=_lib.DF11_GEMM_PIPE, split=2, one_writer=1), False, False),
