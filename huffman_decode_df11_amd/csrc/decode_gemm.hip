@@ -1493,16 +1493,32 @@ __global__ void __launch_bounds__(W * 64, 6) decode_gemm_ring_kernel(GemmArgs g)
 // x [B, K] in the matrix cores' A-operand order: piece (s, m, l) holds the 8
 // BF16 of row 32 m + l % 32, columns 16 s + 8 (l / 32) .. + 7 (zero past row
 // B), at index (s * tiles + m) * 64 + l, so that the operand of k-step s and
-// batch tile m is one contiguous kilobyte.
-__global__ void x_pack_kernel(const uint16_t *x, uint32_t B, uint32_t K, uint32_t tiles, uint4 *xo)
+// batch tile m is one contiguous kilobyte.  A workgroup of 256 threads takes
+// batch tile m = blockIdx.y and the kXPackSteps k-steps from blockIdx.x *
+// kXPackSteps: it reads the 32 rows' pieces of those columns whole (256
+// contiguous bytes per row) into LDS, then writes the kXPackSteps packed
+// kilobytes.  K is a multiple of 16 * kXPackSteps (the fused layout's
+// 512-column tiles).
+constexpr uint32_t kXPackSteps = 8;
+__global__ void __launch_bounds__(256) x_pack_kernel(const uint16_t *x, uint32_t B, uint32_t K, uint32_t tiles, uint4 *xo)
 {
-    const uint64_t n = (uint64_t)(K / 16) * tiles * 64;
-    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
-        const uint32_t l = (uint32_t)(i & 63), m = (uint32_t)((i >> 6) % tiles);
-        const uint64_t ks = (i >> 6) / tiles;
-        const uint32_t row = m * 32 + (l & 31);
-        xo[i] = row < B ? *reinterpret_cast<const uint4 *>(x + (uint64_t)row * K + ks * 16 + (l >> 5) * 8)
-                        : make_uint4(0, 0, 0, 0);
+    constexpr uint32_t kPieces = 2 * kXPackSteps;   // 16-byte pieces per row in the block's columns
+    __shared__ uint4 buf[32][kPieces + 1];
+    const uint32_t m = blockIdx.y, s0 = blockIdx.x * kXPackSteps;
+    const uint32_t c0 = s0 * 16;
+#pragma unroll
+    for (uint32_t j = 0; j < 32 * kPieces / 256; j++) {
+        const uint32_t p = threadIdx.x + 256 * j;
+        const uint32_t r = p / kPieces, q = p % kPieces;
+        const uint32_t row = m * 32 + r;
+        buf[r][q] = row < B ? *reinterpret_cast<const uint4 *>(x + (uint64_t)row * K + c0 + q * 8) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t j = 0; j < kXPackSteps * 64 / 256; j++) {
+        const uint32_t o = threadIdx.x + 256 * j;
+        const uint32_t sl = o / 64, l = o % 64;
+        xo[((uint64_t)(s0 + sl) * tiles + m) * 64 + l] = buf[l & 31][2 * sl + (l >> 5)];
     }
 }
 
@@ -1857,12 +1873,12 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
         return a.B == 1 ? launch_vec<K, 8, 1>(a, n_tables, max_seg_elems, tune.parts, st)
                         : launch_vec<K, 8, 2>(a, n_tables, max_seg_elems, tune.parts, st);
     }
-    // the segment-parallel kernel with two batch tiles and the wide kernel
-    // read x from the packed copy
+    // every kernel but the tile-synchronous one reads x from the packed copy
+    // when there is one
     if (ws && mt >= 2 && kernel != DF11_GEMM_TILED) {
         const uint32_t tiles = packed_tiles(a.B);
-        const uint64_t n = (uint64_t)(a.K / 16) * tiles * 64;
-        hipLaunchKernelGGL(x_pack_kernel, dim3((uint32_t)std::min<uint64_t>((n + 255) / 256, 4096)), dim3(256), 0, st,
+        if (a.K % (16 * kXPackSteps)) return df11::fail(DF11_E_ARG, "decode_gemm: K %u not a multiple of %u", a.K, 16 * kXPackSteps);
+        hipLaunchKernelGGL(x_pack_kernel, dim3(a.K / (16 * kXPackSteps), tiles), dim3(256), 0, st,
                            a.x, a.B, a.K, tiles, reinterpret_cast<uint4 *>(ws));
         a.xo = reinterpret_cast<const uint4 *>(ws);
         a.xo_tiles = tiles;
