@@ -72,7 +72,7 @@ class DecodeTuning(ctypes.Structure):
 
 class GemmTuning(ctypes.Structure):
     _fields_ = [("kernel", u32), ("row_blocks", u32), ("parts", u32), ("split", u32), ("one_writer", u32),
-                ("tiles_per_wave", u32), ("reserved", u32 * 2)]
+                ("tiles_per_wave", u32), ("k_slices", u32), ("reserved", u32)]
 
 
 # (field, element ctype) of every array in a view

@@ -323,12 +323,13 @@ def decode_tuning(waves: int = 0, stores: int = 0, groups: int = 0) -> DecodeTun
 
 
 def gemm_tuning(kernel: int = 0, row_blocks: int = 0, parts: int = 0, split: int = 0,
-                one_writer: int = 0, tiles_per_wave: int = 0) -> GemmTuning:
+                one_writer: int = 0, tiles_per_wave: int = 0, k_slices: int = 0) -> GemmTuning:
     """Explicit kernel choices for decode_gemm (0 = the library's choice);
     one_writer=1: y summed in a fixed order, the same on every run;
-    tiles_per_wave: batch tiles per matrix-core wave of the pipelined kernel."""
+    tiles_per_wave: batch tiles per matrix-core wave of the pipelined kernel;
+    k_slices: matrix-core waves per batch tile of the exponent-ring kernel."""
     return GemmTuning(kernel=kernel, row_blocks=row_blocks, parts=parts, split=split, one_writer=one_writer,
-                      tiles_per_wave=tiles_per_wave)
+                      tiles_per_wave=tiles_per_wave, k_slices=k_slices)
 
 
 def decode_batch(tensors: Sequence[DF11Tensor], outs=None, stream=None, tuning: Optional[DecodeTuning] = None):

@@ -1307,46 +1307,60 @@ __global__ void __launch_bounds__(W * 64) decode_gemm_pipe_kernel(GemmArgs g, ui
 //   decoder waves: decode each segment of the tile sequence into its slot's
 //     exponent plane (count, scan, emit; no sign+mantissa bytes and no
 //     merge), then add one to the slot's ready counter.
-//   matrix-core wave m (batch tile m): per k-step, 8 exponent bytes from the
-//     plane and the same 8 sign+mantissa bytes, loaded from global memory
-//     kAhead k-steps ahead with x, give the B operand of
-//     v_mfma_f32_32x32x16_bf16 (two bit-selects and two byte permutes per 4
-//     weights).
+//   matrix-core waves: KS per batch tile, wave (m, ks) taking k-steps
+//     ks * 32 / KS .. (ks + 1) * 32 / KS - 1 of every tile for batch tile m;
+//     per k-step, 8 exponent bytes from the plane and the same 8
+//     sign+mantissa bytes, loaded from global memory kAhead k-steps ahead
+//     with x, give the B operand of v_mfma_f32_32x32x16_bf16 (two
+//     bit-selects and two byte permutes per 4 weights).  A wave's loads of
+//     a tile form a chain of 32 / KS / kAhead round trips to memory (the
+//     sign+mantissa bytes come from HBM), which is what bounds one wave per
+//     batch tile; with KS = 2 the second wave of a batch tile hands its
+//     partial sums to the first through LDS at the end of each row block
+//     (two more counters per batch tile: sums written, sums read), and the
+//     first adds them in a fixed order and writes y.
 // Waits and counters as in the pipelined kernel above.
 constexpr uint32_t kRingSlots = 3;
 constexpr uint32_t kRingGuard = 16;   // emit_codes writes from position >= 3
 
-uint32_t ring_lds_bytes(uint32_t fast_bits, uint32_t n_tables)
+constexpr uint32_t kRingRed = 32 * 32 * 4;   // one batch tile's partial sums (KS = 2)
+
+uint32_t ring_lds_bytes(uint32_t fast_bits, uint32_t n_tables, uint32_t ks)
 {
-    return kRingGuard + kRingSlots * kTile + 64 + (8u << fast_bits) + n_tables * 512u;
+    return kRingGuard + kRingSlots * kTile + 64 + (ks == 2 ? 2 * kRingRed : 0) + (8u << fast_bits) + n_tables * 512u;
 }
 static_assert(kRingGuard + kRingSlots * kTile < 65536, "ring planes beyond the emit cursor");
 
-template <int K, int MT, int W>
+template <int K, int MT, int W, int KS>
 __global__ void __launch_bounds__(W * 64, 6) decode_gemm_ring_kernel(GemmArgs g)
 {
+    static_assert(KS == 1 || (KS == 2 && MT <= 2), "k-slices per batch tile");
     extern __shared__ __align__(16) uint8_t lds_raw[];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8 *)lds_raw;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = lane_id();
-    // [guard][3 exponent planes][ready[4], release[4]][tables]
+    // [guard][3 exponent planes][ready[4], release[4], sums written[2], sums
+    // read[2], unused[4]][KS = 2: two batch tiles' partial sums][tables]
     const uint32_t planes = lds0 + kRingGuard;
     const uint32_t ctr = planes + kRingSlots * kTile;
-    const uint32_t fast = ctr + 64;
+    const uint32_t red = ctr + 64;
+    const uint32_t fast = red + (KS == 2 ? 2 * kRingRed : 0);
     const uint32_t chain = fast + (8u << K);
-    if (threadIdx.x < 8) st32(ctr + 4 * threadIdx.x, 0u);
+    if (threadIdx.x < 16) st32(ctr + 4 * threadIdx.x, 0u);
     stage_tables<K, W * 64>(fast, chain, g.fast, g.chain, g.n_chain);
     __syncthreads();
 
-    const uint32_t nm = (g.B + 31) / 32;
+    const uint32_t nm = (g.B + 31) / 32 * KS;
     const uint32_t n_units = g.n_rowblocks * g.split;
     const bool stored = g.counts != nullptr;
 
     if (wave < nm) {
-        // ---- matrix-core wave: batch tile m = wave
-        const uint32_t m = wave;
+        // ---- matrix-core wave: batch tile m, k-slice ks
+        const uint32_t m = wave / KS, ks = wave % KS;
+        constexpr int kSteps = 32 / KS;   // k-steps of a tile per wave
         const bool writes_w = g.w_debug && m == 0;
         uint32_t cum[kRingSlots] = {};
+        uint32_t nred = 0;   // row blocks whose partial sums were handed over
         bool ok = true;
         f32x16 acc;
 #pragma unroll
@@ -1359,12 +1373,13 @@ __global__ void __launch_bounds__(W * 64, 6) decode_gemm_ring_kernel(GemmArgs g)
             uint32_t ln = lane;
             asm volatile("" : "+v"(ln));
             constexpr int kAhead = 4;
+            const uint32_t kb = ks * kSteps;   // first k-step of this wave in the tile
             const uint32_t brow = min(m * 32 + (ln & 31u), g.B - 1);
-            const uint8_t *gx = g.xo ? reinterpret_cast<const uint8_t *>(g.xo + ((uint64_t)p.kt * 32u * MT + m) * 64 + ln)
-                                     : reinterpret_cast<const uint8_t *>(g.x + (uint64_t)brow * g.K + p.kt * kTC + (ln >> 5) * 8);
+            const uint8_t *gx = g.xo ? reinterpret_cast<const uint8_t *>(g.xo + ((uint64_t)(p.kt * 32u + kb) * MT + m) * 64 + ln)
+                                     : reinterpret_cast<const uint8_t *>(g.x + (uint64_t)brow * g.K + p.kt * kTC + kb * 16 + (ln >> 5) * 8);
             const __attribute__((address_space(1))) uint8_t *xb = (const __attribute__((address_space(1))) uint8_t *)gx;
             const uint32_t xs = g.xo ? MT * 64u * 16u : 32u;
-            const uint32_t lo_off = (ln >> 5) * (kTR * kKC) + (ln & 31u) * kKC;
+            const uint32_t lo_off = (ln >> 5) * (kTR * kKC) + (ln & 31u) * kKC + kb * 2 * kTR * kKC;
             const __attribute__((address_space(1))) uint8_t *sb =
                 (const __attribute__((address_space(1))) uint8_t *)(g.sm + (uint64_t)p.t * kTile + lo_off);
             uint4 xa[kAhead];
@@ -1380,22 +1395,23 @@ __global__ void __launch_bounds__(W * 64, 6) decode_gemm_ring_kernel(GemmArgs g)
             const uint32_t rb = p.unit / g.split;
             const uint32_t ep = planes + sl * kTile + lo_off;
             uint16_t *wd = nullptr;
-            if constexpr (kWD) wd = g.w_debug + (uint64_t)(rb * kTR + (ln & 31u)) * g.K + p.kt * kTC + (ln >> 5) * kKC;
+            if constexpr (kWD)
+                wd = g.w_debug + (uint64_t)(rb * kTR + (ln & 31u)) * g.K + p.kt * kTC + kb * 16 + (ln >> 5) * kKC;
             constexpr int kEAhead = 2;
             uint2 rq[kEAhead];
 #pragma unroll
             for (int i = 0; i < kEAhead; i++) rq[i] = ld64(ep + i * 2 * kTR * kKC);
 #pragma unroll
-            for (int i = 0; i < 32; i++) {
+            for (int i = 0; i < kSteps; i++) {
                 const uint2 rx = rq[i % kEAhead];
-                if (i + kEAhead < 32) rq[i % kEAhead] = ld64(ep + (i + kEAhead) * 2 * kTR * kKC);
+                if (i + kEAhead < kSteps) rq[i % kEAhead] = ld64(ep + (i + kEAhead) * 2 * kTR * kKC);
                 const uint2 svi = sv[i % kAhead];
                 const uint2 lo = assemble4(svi.x, rx.x), hi = assemble4(svi.y, rx.y);
                 if constexpr (kWD) *reinterpret_cast<uint4 *>(wd + 2 * i * kKC) = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[i % kAhead]),
                                                               __builtin_bit_cast(bf16x8, v4u32{lo.x, lo.y, hi.x, hi.y}),
                                                               acc, 0, 0, 0);
-                if (i + kAhead < 32) {
+                if (i + kAhead < kSteps) {
                     xa[i % kAhead] = ld_global128(xb);
                     xb += xs;
                     sv[i % kAhead] = ld_global64(sb);
@@ -1419,7 +1435,31 @@ __global__ void __launch_bounds__(W * 64, 6) decode_gemm_ring_kernel(GemmArgs g)
             const uint32_t rb = p.unit / g.split;
             lds_signal(ctr + 16 + 4 * slot, lane);
             slot = slot + 1 == kRingSlots ? 0 : slot + 1;
-            if (p.kt + 1 == p.kt1) {
+            bool store = p.kt + 1 == p.kt1;
+            if constexpr (KS == 2) {
+                if (store) {
+                    // k-slice 1 hands its sums to k-slice 0 (element j of
+                    // lane l at float j * 64 + l of the batch tile's area)
+                    const uint32_t area = red + m * kRingRed;
+                    if (ks == 1) {
+                        ok &= lds_wait_geq(ctr + 40 + 4 * m, nred);   // the previous sums were read
+#pragma unroll
+                        for (int j = 0; j < 16; j++)
+                            *(lds_f32 *)(size_t)(area + 4 * (j * 64 + lane)) = ok ? acc[j] : __builtin_nanf("");
+                        lds_signal(ctr + 32 + 4 * m, lane);
+#pragma unroll
+                        for (int j = 0; j < 16; j++) acc[j] = 0.0f;
+                        store = false;
+                    } else {
+                        ok &= lds_wait_geq(ctr + 32 + 4 * m, nred + 1);
+#pragma unroll
+                        for (int j = 0; j < 16; j++) acc[j] += *(const lds_f32 *)(size_t)(area + 4 * (j * 64 + lane));
+                        lds_signal(ctr + 40 + 4 * m, lane);
+                    }
+                    nred++;
+                }
+            }
+            if (store) {
                 // lane holds n = rb*32 + lane%32, b = 32*m + 8*blk + 4*(lane/32) + e
                 uint32_t ln = lane, nB = g.B, nN = g.N;
                 asm volatile("" : "+v"(ln), "+s"(nB), "+s"(nN));
@@ -1777,6 +1817,17 @@ int launch_pipe(GemmArgs a, uint32_t n_tables, uint32_t forced_split, hipStream_
     return DF11_OK;
 }
 
+// matrix-core waves per batch tile of the exponent-ring kernel: the
+// tuning's choice, else by the batch tiles of x
+uint32_t ring_k_slices(uint32_t B, uint32_t forced)
+{
+    // up_proj: 36.5 / 40.9 / 44.8 us at 8 / 32 / 64 rows with two, 56.9 /
+    // 59.6 / 50.3 with one (one wave's chain of sign+mantissa and x loads
+    // per tile bounds it)
+    if (forced) return forced;
+    return B <= 64 ? 2u : 1u;
+}
+
 // batch tiles per matrix-core wave of the pipelined kernel: the tuning's
 // choice, else by the batch tiles of x
 uint32_t pipe_tiles_per_wave(uint32_t B, uint32_t forced)
@@ -1797,16 +1848,16 @@ int launch_pipe_mt(GemmArgs a, uint32_t n_tables, uint32_t forced_split, uint32_
 
 // Exponent-ring launch: 12-wave workgroups, two per CU where the planes
 // and tables fit in 80 KB; K split as for the pipelined kernel.
-template <int K, int MT>
+template <int K, int MT, int KS>
 int launch_ring(GemmArgs a, uint32_t n_tables, uint32_t forced_split, hipStream_t st)
 {
     constexpr int W = 12;
-    const uint32_t lds = ring_lds_bytes(K, n_tables);
+    const uint32_t lds = ring_lds_bytes(K, n_tables, KS);
     if (lds > 160u * 1024u) return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: exponent-ring planes and tables do not fit in LDS");
     if (a.xo && a.xo_tiles != (uint32_t)MT) return df11::fail(DF11_E_ARG, "decode_gemm: packed x tiles");
     if (a.n_segments >= (1ull << 32) || (uint64_t)a.n_rowblocks * a.tiles_per_row >= (1ull << 32))
         return df11::fail(DF11_E_UNSUPPORTED, "decode_gemm: the exponent-ring kernel takes fewer than 2^32 segments and tiles");
-    const void *kern = (const void *)decode_gemm_ring_kernel<K, MT, W>;
+    const void *kern = (const void *)decode_gemm_ring_kernel<K, MT, W, KS>;
     const uint32_t slots = (uint32_t)(cu_count() * resident_groups(kern, W * 64, lds));
     uint32_t split = 1;
     if (forced_split) split = forced_split;
@@ -1818,7 +1869,7 @@ int launch_ring(GemmArgs a, uint32_t n_tables, uint32_t forced_split, hipStream_
     if (a.split > 1) clear_y(a, st);
     const uint32_t units = a.n_rowblocks * a.split;
     const uint32_t groups = std::min<uint32_t>(units, slots);
-    hipLaunchKernelGGL((decode_gemm_ring_kernel<K, MT, W>), dim3(groups), dim3(W * 64), lds, st, a);
+    hipLaunchKernelGGL((decode_gemm_ring_kernel<K, MT, W, KS>), dim3(groups), dim3(W * 64), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return df11::fail(DF11_E_DEVICE, "decode_gemm launch: %s", hipGetErrorString(e));
     return DF11_OK;
@@ -1831,27 +1882,22 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
     // one writer per element of y: no segment runs and no K ranges
     df11_gemm_tuning tune = tune_in;
     if (tune.one_writer) tune.parts = tune.split = 1;
-    // Automatic choice: one or two rows of x the vector kernel, up to 32 the
-    // segment-parallel one when its staging fits (up_proj: 42.6 / 48.3 us
-    // at 8 / 32 rows against 46.4 / 47.7 on the exponent-ring kernel), above
-    // that the exponent-ring and pipelined kernels (below).  w_debug calls
-    // take the tile-synchronous kernel up to 32 rows, the wide one above.
+    // Automatic choice: up to 128 rows of x the exponent-ring kernel (two
+    // matrix-core waves per batch tile up to 64 rows, one above), above
+    // that the pipelined kernel (below).  w_debug calls take the
+    // tile-synchronous kernel up to 32 rows, the wide one above.
     const uint32_t mt = (a.B + 31) / 32;
     const uint32_t vec_waves = vec_kernel_waves(K, n_tables, max_seg_elems);
     uint32_t kernel = tune.kernel;
     if (kernel == DF11_GEMM_AUTO) {
-        // one or two rows of x: the vector kernel (up_proj: 38.3 / 42.0 us
-        // against 45.1 / 45.3 on the segment-parallel one; at 3 and 4 rows
-        // it is slower, 53 us)
-        if (a.B <= 2 && !a.w_debug && vec_waves) kernel = DF11_GEMM_VECTOR;
-        else if (a.B <= 32u && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems))
-            kernel = DF11_GEMM_SEGMENT;
-        // 33 to 128 rows: the exponent-ring kernel, x packed (up_proj, 8
-        // weight copies cycled: 50.1 / 50.3 / 52.7 / 59.2 us at 33 / 64 / 96
-        // / 128 rows against 55.6 / 56.2 / 70.1 / 69.7 on the wide kernel
-        // and 54.9 / 55.3 / 57.2 / 63.1 on the pipelined one), or x read in
-        // place up to 64 rows (48.7 / 57.8 us at 33 / 64 rows; 78 at 96)
-        else if (mt >= 2 && mt <= 4 && !a.w_debug && (ws || mt <= 2) && ring_lds_bytes(K, n_tables) <= 160u * 1024u)
+        // 1 to 128 rows: the exponent-ring kernel (up_proj, 8 weight copies
+        // cycled, two k-slices: 36.0 / 36.4 / 36.5 / 40.9 / 44.5 / 44.8 us
+        // at 1 / 2 / 8 / 32 / 33 / 64 rows against 36.3 / 39.3 on the vector
+        // kernel at 1 / 2, 42.4 / 48.5 on the segment-parallel one at 8 /
+        // 32, 55.8 / 55.6 on the wide one at 33 / 64; one k-slice: 53.1 /
+        // 60.3 us at 96 / 128 against 68.6 / 69.4 on the wide kernel), x
+        // packed above 32 rows, or read in place up to 64
+        if (!a.w_debug && (ws || mt <= 2) && mt <= 4 && ring_lds_bytes(K, n_tables, 2) <= 160u * 1024u)
             kernel = DF11_GEMM_RING;
         // above 128 rows with x packed, the pipelined kernel with two batch
         // tiles per matrix-core wave (69.0 / 70.0 / 77.6 us at 160 / 192 /
@@ -1860,6 +1906,12 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
         // us at 256 rows)
         else if (ws && mt >= 2 && !a.w_debug && pipe_lds_bytes(2, K, n_tables) <= 160u * 1024u)
             kernel = DF11_GEMM_PIPE;
+        // where the ring's planes and tables would not fit in LDS: the
+        // vector kernel at one or two rows, the segment-parallel one up to
+        // 32, the wide one above
+        else if (a.B <= 2 && !a.w_debug && vec_waves) kernel = DF11_GEMM_VECTOR;
+        else if (a.B <= 32u && !a.w_debug && seg_kernel_fits(K, n_tables, max_seg_elems))
+            kernel = DF11_GEMM_SEGMENT;
         else kernel = mt <= 1 ? DF11_GEMM_TILED : DF11_GEMM_WIDE;
     }
     if (kernel == DF11_GEMM_VECTOR) {
@@ -1884,9 +1936,13 @@ int launch_mt(GemmArgs a, uint32_t n_tables, uint32_t max_seg_elems, const df11_
         a.xo_tiles = tiles;
     }
     if (kernel == DF11_GEMM_RING) {
-        if (mt <= 1) return launch_ring<K, 1>(a, n_tables, tune.split, st);
-        if (mt <= 2) return launch_ring<K, 2>(a, n_tables, tune.split, st);
-        if (mt <= 4) return launch_ring<K, 4>(a, n_tables, tune.split, st);
+        const uint32_t kslices = ring_k_slices(a.B, tune.k_slices);
+        if (mt <= 1) return kslices == 2 ? launch_ring<K, 1, 2>(a, n_tables, tune.split, st)
+                                         : launch_ring<K, 1, 1>(a, n_tables, tune.split, st);
+        if (mt <= 2) return kslices == 2 ? launch_ring<K, 2, 2>(a, n_tables, tune.split, st)
+                                         : launch_ring<K, 2, 1>(a, n_tables, tune.split, st);
+        if (kslices == 2) return df11::fail(DF11_E_ARG, "tuning: two k-slices per batch tile take up to 64 rows of x");
+        if (mt <= 4) return launch_ring<K, 4, 1>(a, n_tables, tune.split, st);
         return df11::fail(DF11_E_ARG, "tuning: the exponent-ring kernel takes up to 128 rows of x");
     }
     if (kernel == DF11_GEMM_PIPE) {
@@ -1952,6 +2008,8 @@ int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
     if (t.one_writer && (t.parts > 1 || t.split > 1))
         return df11::fail(DF11_E_ARG, "tuning: one_writer takes parts and split 1");
     if (t.parts > (1u << 16) || t.split > (1u << 16)) return df11::fail(DF11_E_ARG, "tuning: parts or split too large");
+    if (t.k_slices && (t.kernel != DF11_GEMM_RING || t.k_slices > 2))
+        return df11::fail(DF11_E_ARG, "tuning: k_slices %u (0, or 1 or 2 with the exponent-ring kernel)", t.k_slices);
     if (t.tiles_per_wave && (t.kernel != DF11_GEMM_PIPE || t.tiles_per_wave > 2))
         return df11::fail(DF11_E_ARG, "tuning: tiles_per_wave %u (0, or 1 or 2 with the pipelined kernel)", t.tiles_per_wave);
     return DF11_OK;
@@ -2023,6 +2081,8 @@ extern "C" int df11_decode_gemm_ex(const df11_view *w, const uint16_t *x, uint32
     if (B < 1 || B > 256) return df11::fail(DF11_E_ARG, "B = %u outside 1..256", B);
     if (tune.kernel == DF11_GEMM_RING && B > 128)
         return df11::fail(DF11_E_ARG, "tuning: the exponent-ring kernel takes up to 128 rows of x");
+    if (tune.kernel == DF11_GEMM_RING && tune.k_slices == 2 && B > 64)
+        return df11::fail(DF11_E_ARG, "tuning: two k-slices per batch tile take up to 64 rows of x");
     if (w->tile_rows != kTR || w->tile_cols != kTC || w->tile_kchunk != kKC || w->align_elems != kTile ||
         w->chunk_bytes != 16 || w->seg_lanes != 64 || !w->rows || !w->cols || w->rows % kTR ||
         w->cols % kTC || w->rows * w->cols != w->n)

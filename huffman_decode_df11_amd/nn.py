@@ -49,10 +49,10 @@ class DF11Linear(torch.nn.Module):
     the fused product (x packed in operand order above 32 rows) for up to
     fused_max_rows rows of x and decode + matmul above (default 256, the
     fused kernels' limit: on an up_proj-shaped weight, 14336 x 4096, the
-    fused call measured 55 / 63 / 78 us at 64 / 128 / 256 rows against about
-    79 / 82 / 105 us for decoding the tile-ordered weight and calling
-    torch.matmul); mode "decode" always decodes into the shared buffer and
-    calls torch.matmul.  "auto" picks "fused" when the shape allows it.
+    fused call measured about 37 / 45 / 62 / 85 us at 1 / 64 / 128 / 256
+    rows against about 60 / 79 / 82 / 105 us for decoding the tile-ordered
+    weight and calling torch.matmul); mode "decode" always decodes into the
+    shared buffer and calls torch.matmul.  "auto" picks "fused" when the shape allows it.
     deterministic=True asks the fused kernels for one writer per element of
     y (df11_gemm_tuning one_writer): the same output on every run, where
     weights with few 32-row blocks (4096 x 4096, 4096 x 14336) otherwise

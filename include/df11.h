@@ -328,21 +328,19 @@ int df11_decode_rows(const df11_view *device_view, const int64_t *rows, uint64_t
  * runs of its segments) and the partial sums are added into y (cleared
  * first, on the same stream) with float atomics, so the order of those few
  * additions, and with it the last bits of y, can differ from run to run.
- * The kernel is chosen by B: one or two rows a kernel that forms the
- * products as dot products on the vector ALU, up to 32 rows a
- * segment-parallel kernel on the matrix cores, up to 64 rows (128 with the
- * workspace of df11_decode_gemm_ex) one whose decoder waves hand tiles of
- * exponents to matrix-core waves through a ring in LDS, above that (with
- * the workspace) one whose ring holds whole BF16 tiles, else one that
- * merges each decoded tile once into a BF16 tile in LDS shared by all batch
- * tiles (two row blocks per workgroup above 112 rows); w_debug calls up to
- * 32 rows, and weights whose segments are too large for the
- * segment-parallel kernel's staging, take a tile-synchronous kernel, and
- * w_debug calls above 32 rows the shared-tile one (df11_decode_gemm_ex
- * makes the choice explicit).
+ * The kernel is chosen by B: up to 64 rows (128 with the workspace of
+ * df11_decode_gemm_ex) one whose decoder waves hand tiles of exponents to
+ * matrix-core waves through a ring in LDS, above that (with the workspace)
+ * one whose ring holds whole BF16 tiles, else one that merges each decoded
+ * tile once into a BF16 tile in LDS shared by all batch tiles (two row
+ * blocks per workgroup above 112 rows); w_debug calls take a
+ * tile-synchronous kernel up to 32 rows and the shared-tile one above.  A
+ * kernel that forms the products on the vector ALU (one or two rows) and a
+ * segment-parallel one (up to 64 rows) are explicit choices
+ * (df11_decode_gemm_ex makes every choice explicit).
  * Non-finite x: a row of x holding Inf or NaN gives a non-finite row of y;
- * where a plain product would give +-Inf, y may hold NaN instead (the
- * segment-parallel and vector kernels multiply the weights of a
+ * where a plain product would give +-Inf, the segment-parallel and vector
+ * kernels may give NaN instead (they multiply the weights of a
  * neighbouring segment, masked to +0, by the same x).  Rows of x without
  * them are unaffected.
  * Errors: E_ARG (null, misaligned, layout not from df11_gemm_layout, B out
@@ -371,7 +369,8 @@ int df11_decode_gemm_out(const df11_view *device_view, const uint16_t *x, uint32
 #define DF11_GEMM_TILED 3     /* tile-synchronous, any rows of x */
 #define DF11_GEMM_VECTOR 4    /* dot products on the vector ALU: one or two rows of x, no w_debug */
 #define DF11_GEMM_PIPE 5      /* decoder and matrix-core waves on a ring of BF16 tiles in LDS: any rows of x */
-#define DF11_GEMM_RING 6      /* as DF11_GEMM_PIPE with exponent-only planes, two workgroups per CU: up to 128 rows of x */
+#define DF11_GEMM_RING 6      /* as DF11_GEMM_PIPE with exponent-only planes, two workgroups per CU: up to 128 rows of x
+                                 (two matrix-core waves per batch tile, k_slices, up to 64) */
 typedef struct df11_gemm_tuning {
     uint32_t kernel;       /* DF11_GEMM_* */
     uint32_t row_blocks;   /* wide kernel: 0 = by B, else 1 or 2 row blocks per workgroup */
@@ -385,7 +384,9 @@ typedef struct df11_gemm_tuning {
                               row blocks to fill the device */
     uint32_t tiles_per_wave; /* pipelined kernel: 0 = by B, else 1 or 2 batch tiles of 32 rows of x
                               per matrix-core wave */
-    uint32_t reserved[2];  /* zero */
+    uint32_t k_slices;     /* exponent-ring kernel: 0 = by B, else 1 or 2 matrix-core waves per batch
+                              tile of x, each taking that share of a tile's k-steps (2: up to 64 rows) */
+    uint32_t reserved[1];  /* zero */
 } df11_gemm_tuning;
 
 /* Bytes of the workspace df11_decode_gemm_ex can use for B rows of x with

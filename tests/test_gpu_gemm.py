@@ -61,11 +61,13 @@ def _run(W, X, with_debug=True, tuning=None):
     return y.cpu().numpy(), wd, y_dbg
 
 
-def _recover_by_identity(W, rows=32, counts=True):
+def _recover_by_identity(W, rows=32, counts=True, tuning=None):
     """W through y alone: x = rows of the identity placed at columns k0 ..
     k0 + rows - 1, for every k0, gives y[b, n] = W[n, k0 + b] exactly (one
     nonzero product per output).  counts=False drops the stored code counts
-    (the kernel then runs the locate pass).  Returns the recovered float32 W."""
+    (the kernel then runs the locate pass).  tuning: None, a tuning, or a
+    function of the call's rows of x giving one.  Returns the recovered
+    float32 W."""
     N, K = W.shape
     dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
     if not counts:
@@ -76,9 +78,15 @@ def _recover_by_identity(W, rows=32, counts=True):
         b = min(rows, K - k0)
         X = np.zeros((b, K), np.uint16)
         X[np.arange(b), k0 + np.arange(b)] = 0x3F80
-        y = api.decode_gemm(dt, _x_to_gpu(X))
+        y = api.decode_gemm(dt, _x_to_gpu(X), tuning=tuning(b) if callable(tuning) else tuning)
         got[:, k0:k0 + b] = y.cpu().numpy().T
     return got
+
+
+def _legacy_tuning(rows):
+    """The kernels that were the automatic choice before the ring kernels:
+    segment-parallel up to 40 rows of x, wide above."""
+    return api.gemm_tuning(kernel=_lib.DF11_GEMM_SEGMENT if rows <= 40 else _lib.DF11_GEMM_WIDE)
 
 
 def _as_f32(W):
@@ -117,16 +125,20 @@ def test_small_weight_all_batch_shapes(B):
 def test_k_split_shapes(N, K, B):
     """Few 32-row blocks: the K range is split across workgroups and the
     partial sums meet in y (28 tiles per row in 7 ranges of 4; 8 tiles in 8
-    ranges; a single tile), through the segment-parallel kernel (5 and 40
-    rows of x) and the wide one with 8, 4 and 2 batch tiles (256, 72 and 48
-    rows)."""
+    ranges; a single tile), through the automatic choice (the exponent ring
+    up to 128 rows, the BF16 ring at 256) and, forced, the segment-parallel
+    kernel (5 and 40 rows of x) and the wide one with 8, 4 and 2 batch tiles
+    (256, 72 and 48 rows)."""
     _say("case gemm split N=%d K=%d B=%d" % (N, K, B))
     W = synth.normal_bf16(N * K, 0.02, seed=26).reshape(N, K)
     X = synth.activations_bf16(B, K, seed=27)
-    y, wd, yd = _run(W, X)
-    assert np.array_equal(wd, W), "decoded weights differ"
-    assert _rel(y, orc.gemm_f64(X, W)) < TOL
-    assert _rel(yd, orc.gemm_f64(X, W)) < TOL
+    ref = orc.gemm_f64(X, W)
+    for tune in (None, _legacy_tuning(B)):   # the segment-parallel kernel writes no w_debug
+        y, wd, yd = _run(W, X, with_debug=tune is None or B > 40, tuning=tune)
+        assert _rel(y, ref) < TOL
+        if wd is not None:
+            assert np.array_equal(wd, W), "decoded weights differ"
+            assert _rel(yd, ref) < TOL
 
 
 @pytest.mark.parametrize("rb", [1, 2])
@@ -158,30 +170,34 @@ def test_identity_x_recovers_weights_exactly():
     assert np.array_equal(y, _as_f32(W)[:, :B].T)
 
 
+@pytest.mark.parametrize("kernel", ["auto", "legacy"])
 @pytest.mark.parametrize("rows", [32, 40, 48, 64])
 @pytest.mark.parametrize("N,K,seed", [(96, 1536, 28), (256, 4096, 29)])
-def test_identity_x_recovers_weights_segment_parallel(N, K, seed, rows):
-    """Every weight through y alone, compared exactly: the segment-parallel
-    kernel at 32 and 40 rows of x (one batch tile, then two with the second
-    a quarter full: masks at segment edges, rounds, the row block reduction
-    per batch tile, the K split of y for the 8-row-block weight) and the
-    wide kernel at 48 and 64 rows (the merged BF16 plane, k-slice
-    reduction)."""
-    _say("case gemm identity segment-parallel N=%d K=%d rows=%d" % (N, K, rows))
+def test_identity_x_recovers_weights_segment_parallel(N, K, seed, rows, kernel):
+    """Every weight through y alone, compared exactly: the automatic choice
+    (the exponent ring, two k-slices per batch tile: their hand-over of
+    partial sums) and, forced, the segment-parallel kernel at 32 and 40 rows
+    of x (one batch tile, then two with the second a quarter full: masks at
+    segment edges, rounds, the row block reduction per batch tile, the K
+    split of y for the 8-row-block weight) and the wide kernel at 48 and 64
+    rows (the merged BF16 plane, k-slice reduction)."""
+    _say("case gemm identity %s N=%d K=%d rows=%d" % (kernel, N, K, rows))
     W = synth.normal_bf16(N * K, 0.02, seed=seed).reshape(N, K)
-    assert np.array_equal(_recover_by_identity(W, rows=rows), _as_f32(W))
+    tune = None if kernel == "auto" else _legacy_tuning   # per call: its rows of x
+    assert np.array_equal(_recover_by_identity(W, rows=rows, tuning=tune), _as_f32(W))
 
 
 def test_identity_x_recovers_long_code_weights():
     """Adversarial exponent mix (long codes, short segments) without the
     non-finite exponent 255, so that 0 * w stays 0: recovered exactly
-    through y of the segment-parallel kernel."""
+    through y of the automatic choice and of the segment-parallel kernel."""
     N, K = 64, 1024
     _say("case gemm identity adversarial")
     W = synth.adversarial_bf16(N * K, seed=30).reshape(N, K)
     W = np.where((W >> 7) & 0xFF == 0xFF, W & 0x807F, W).astype(np.uint16)
     assert np.array_equal(_recover_by_identity(W), _as_f32(W))
     assert np.array_equal(_recover_by_identity(W, rows=64), _as_f32(W))
+    assert np.array_equal(_recover_by_identity(W, tuning=_legacy_tuning), _as_f32(W))
 
 
 def test_adversarial_weights_decode_exactly():
@@ -367,21 +383,24 @@ def _identity_recover_on_gpu(dt, N, K, rows, tuning=None):
     return got.T
 
 
+@pytest.mark.parametrize("kernel", ["auto", "segment"])
 @pytest.mark.parametrize("rows", [32, 40])
-def test_identity_x_recovers_up_proj_on_product_path(rows):
-    """Wup 14336 x 4096 through the call the product path makes at up to 40
-    rows of x (no tuning: the segment-parallel kernel; its 448 row blocks
-    fill the device's workgroup slots once, so each row block is one run and
-    every wave walks about five segments, its accumulator carried from one
-    to the next).  x = 32 identity rows per call (one batch tile), or 40
-    (two batch tiles; the last call 16 rows, one tile): every one of the
-    58,720,256 weights comes back through y and is compared bit for bit."""
+def test_identity_x_recovers_up_proj_on_product_path(rows, kernel):
+    """Wup 14336 x 4096 through the call the product path makes (no tuning:
+    the exponent ring with two k-slices per batch tile), and through the
+    segment-parallel kernel forced (its 448 row blocks fill the device's
+    workgroup slots once, so each row block is one run and every wave walks
+    about five segments, its accumulator carried from one to the next).
+    x = 32 identity rows per call (one batch tile), or 40 (two batch tiles;
+    the last call 16 rows, one tile): every one of the 58,720,256 weights
+    comes back through y and is compared bit for bit."""
     N, K = 14336, 4096
-    _say("case gemm identity up_proj product path rows=%d" % rows)
+    _say("case gemm identity up_proj product path rows=%d %s" % (rows, kernel))
     W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
     assert ((W & 0x7FFF) != 0).all()    # no zeros: 1 * w + 0 keeps every bit
     dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
-    got = _identity_recover_on_gpu(dt, N, K, rows)
+    got = _identity_recover_on_gpu(dt, N, K, rows,
+                                   tuning=None if kernel == "auto" else api.gemm_tuning(kernel=_lib.DF11_GEMM_SEGMENT))
     want = (torch.from_numpy(W.view(np.int16)).cuda().to(torch.int32) << 16)
     bad = int((got.contiguous().view(torch.int32) != want).sum())
     assert bad == 0, "%d of %d weights differ" % (bad, N * K)
@@ -422,13 +441,15 @@ def test_sparse_weights_take_a_kernel_whose_staging_fits(kind, B):
         assert ei.value.status == -7
 
 
-@pytest.mark.parametrize("kernel", ["auto", "tiled"])
+@pytest.mark.parametrize("kernel", ["auto", "tiled", "segment"])
 def test_nonfinite_x_row(kernel):
     """A row of x holding +Inf: the other rows of y are as the oracle's
     product; that row of y is non-finite everywhere, as the oracle's is
     (+-Inf there: no weight in the Inf's column is zero), where the
     segment-parallel kernel may give NaN in place of +-Inf (it also
-    multiplies neighbouring segments' weights, masked to +0, by that x)."""
+    multiplies neighbouring segments' weights, masked to +0, by that x).
+    The automatic choice (the exponent ring) and the tile-synchronous kernel
+    multiply whole decoded tiles: the signs of the plain product."""
     N, K, B = 96, 1536, 8
     _say("case gemm nonfinite x %s" % kernel)
     W = synth.normal_bf16(N * K, 0.02, seed=80).reshape(N, K)
@@ -436,11 +457,12 @@ def test_nonfinite_x_row(kernel):
     X[2, 700] = 0x7F80
     ref = orc.gemm_f64(X, W)
     assert np.isinf(ref[2]).all() and np.isfinite(np.delete(ref, 2, axis=0)).all()
-    tune = None if kernel == "auto" else api.gemm_tuning(kernel=_lib.DF11_GEMM_TILED)
+    tune = {"auto": None, "tiled": api.gemm_tuning(kernel=_lib.DF11_GEMM_TILED),
+            "segment": api.gemm_tuning(kernel=_lib.DF11_GEMM_SEGMENT)}[kernel]
     y, _, _ = _run(W, X, with_debug=False, tuning=tune)
     assert not np.isfinite(y[2]).any()
     assert _rel(np.delete(y, 2, axis=0), np.delete(ref, 2, axis=0)) < TOL
-    if kernel == "tiled":   # no masked neighbours: the signs of the plain product
+    if kernel != "segment":   # no masked neighbours: the signs of the plain product
         assert np.array_equal(y[2], ref[2])
 
 
@@ -493,11 +515,12 @@ def test_packed_x_workspace_and_in_place_x_agree(B):
     assert _rel(outs[1], outs[0].astype(np.float64)) < 1e-5
 
 
-@pytest.mark.parametrize("rows", [40, 64])
+@pytest.mark.parametrize("rows", [40, 64, 96])
 def test_identity_x_recovers_up_proj_packed_x(rows):
     """Wup through y with x packed (the default above 32 rows): 40 rows of
-    the identity per call (the wide kernel, two batch tiles) and 64 (two
-    full batch tiles), every weight bit for bit."""
+    the identity per call (the exponent ring, two batch tiles of two
+    k-slices each), 64 (two full batch tiles) and 96 (three batch tiles of
+    one k-slice), every weight bit for bit."""
     N, K = 14336, 4096
     _say("case gemm identity up_proj packed rows=%d" % rows)
     W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
@@ -510,16 +533,17 @@ def test_identity_x_recovers_up_proj_packed_x(rows):
 
 @pytest.mark.parametrize("rows", [1, 2])
 def test_identity_x_recovers_up_proj_vector_kernel(rows):
-    """Wup 14336 x 4096 through the vector kernel, the product path at one
-    and two rows of x (no tuning): x = identity rows, 4096 / rows calls, and
-    every one of the 58,720,256 weights comes back through y bit for bit
-    (one nonzero dot-product term per output, masked neighbours +0)."""
+    """Wup 14336 x 4096 through the vector kernel (forced; the product path
+    takes the exponent ring, covered at 32 and 40 rows above): x = identity
+    rows, 4096 / rows calls, and every one of the 58,720,256 weights comes
+    back through y bit for bit (one nonzero dot-product term per output,
+    masked neighbours +0)."""
     N, K = 14336, 4096
     _say("case gemm identity up_proj vector kernel rows=%d" % rows)
     W = synth.normal_bf16(N * K, 0.02, seed=0, index=5, count=7).reshape(N, K)
     assert ((W & 0x7FFF) != 0).all()
     dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
-    got = _identity_recover_on_gpu(dt, N, K, rows)
+    got = _identity_recover_on_gpu(dt, N, K, rows, tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_VECTOR))
     want = (torch.from_numpy(W.view(np.int16)).cuda().to(torch.int32) << 16)
     bad = int((got.contiguous().view(torch.int32) != want).sum())
     assert bad == 0, "%d of %d weights differ" % (bad, N * K)
@@ -552,7 +576,7 @@ def test_vector_kernel_nonfinite_x_row():
     X = synth.activations_bf16(2, K, seed=87)
     X[1, 700] = 0x7F80
     ref = orc.gemm_f64(X, W)
-    y, _, _ = _run(W, X, with_debug=False)
+    y, _, _ = _run(W, X, with_debug=False, tuning=api.gemm_tuning(kernel=_lib.DF11_GEMM_VECTOR))
     assert not np.isfinite(y[1]).any()
     assert _rel(y[:1], ref[:1]) < TOL
 
@@ -718,7 +742,9 @@ def test_pipelined_kernel_locate_pass_without_stored_counts():
 @pytest.mark.parametrize("N,K,B,extra", [(256, 4096, 1, dict()), (256, 4096, 8, dict()), (256, 4096, 33, dict()),
                                          (256, 4096, 64, dict(split=3)), (256, 4096, 100, dict(one_writer=1)),
                                          (256, 4096, 128, dict()), (96, 1536, 17, dict()),
-                                         (96, 1536, 120, dict(split=1))])
+                                         (96, 1536, 120, dict(split=1)), (256, 4096, 33, dict(k_slices=1)),
+                                         (256, 4096, 5, dict(k_slices=1, split=2)),
+                                         (96, 1536, 64, dict(k_slices=2, one_writer=1))])
 def test_ring_kernel_matches_oracle(N, K, B, extra):
     """Decoded weights bit-exact through w_debug, y of both calls within the
     oracle's tolerance, and a BF16 y one rounding of the float32 one-writer
@@ -824,3 +850,30 @@ def test_ring_kernel_locate_pass_and_x_in_place(B):
     assert np.isfinite(got[:, safe]).all()
     assert _rel(got[:, safe], ref[:, safe]) < TOL
     assert not np.isfinite(got[:, ~fin]).all(axis=0).any()
+
+
+@pytest.mark.parametrize("B,extra", [(8, dict(k_slices=2)), (64, dict(k_slices=2, one_writer=1)),
+                                     (40, dict(k_slices=1)), (100, dict())])
+def test_ring_kernel_many_row_blocks_per_workgroup(B, extra):
+    """640 row blocks of one tile each, more than the resident workgroups,
+    so each workgroup walks several row blocks and (two k-slices) hands
+    partial sums over through the same LDS area again and again: decoded
+    weights bit-exact, y against the oracle on 64 sampled output features,
+    and every element of a NaN-prefilled y written."""
+    N, K = 20480, 512
+    _say("case gemm ring many row blocks B=%d %s" % (B, extra))
+    W = synth.normal_bf16(N * K, 0.02, seed=101).reshape(N, K)
+    X = synth.activations_bf16(B, K, seed=102)
+    dt = api.encode(W, layout=api.gemm_layout(N, K)).to("cuda")
+    tune = api.gemm_tuning(kernel=_lib.DF11_GEMM_RING, **extra)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    api.decode_gemm(dt, _x_to_gpu(X), out=y, tuning=tune)
+    wdbg = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    yd = api.decode_gemm(dt, _x_to_gpu(X), w_debug=wdbg, tuning=tune)
+    torch.cuda.synchronize()
+    assert np.array_equal(wdbg.view(torch.int16).cpu().numpy().view(np.uint16), W)
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    cols = np.random.default_rng(B).choice(N, size=64, replace=False)
+    ref = orc.gemm_f64(X, W[cols])
+    assert _rel(got[:, cols], ref) < TOL and _rel(yd.cpu().numpy()[:, cols], ref) < TOL

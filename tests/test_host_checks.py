@@ -115,6 +115,9 @@ def test_fused_segment_kernel_refused_when_staging_exceeds_64k(kind):
     (2, dict(kernel=_lib.DF11_GEMM_VECTOR, parts=2), True, False),  # BF16 y: one writer per element
     (8, dict(kernel=7), False, False),                              # no such kernel
     (129, dict(kernel=_lib.DF11_GEMM_RING), False, False),          # the exponent ring takes up to 128 rows
+    (65, dict(kernel=_lib.DF11_GEMM_RING, k_slices=2), False, False),  # two k-slices up to 64 rows
+    (8, dict(kernel=_lib.DF11_GEMM_RING, k_slices=3), False, False),
+    (8, dict(kernel=_lib.DF11_GEMM_PIPE, k_slices=2), False, False),   # k_slices only on the exponent ring
     (8, dict(kernel=_lib.DF11_GEMM_PIPE, parts=2), False, False),   # parts without the segment kernels
     (64, dict(kernel=_lib.DF11_GEMM_PIPE, split=2), True, False),   # BF16 y: one writer per element
     (64, dict(kernel=_lib.DF11_GEMM_PIPE, split=2, one_writer=1), False, False),
