@@ -30,19 +30,23 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _call(fn, dt, x, B, N, K, workspace=None):
+def _call(fn, dt, x, B, N, K, workspace=None, debug=True):
+    """y (and the decoded weights when debug) of one call; debug=False is
+    the product path (the ring kernels, x packed above 32 rows), debug=True
+    a w_debug call (the wide kernel above 32 rows)."""
     y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
-    wd = torch.full((N, K), 0x5555, dtype=torch.int16, device="cuda")
+    wd = torch.full((N, K), 0x5555, dtype=torch.int16, device="cuda") if debug else None
+    wd_ptr = wd.data_ptr() if debug else None
     L = _lib.lib()
     if fn == "noalloc":
         rc = L.df11_decode_gemm_noalloc(ctypes.byref(dt.view), x.data_ptr(), B, y.data_ptr(), _lib.DF11_Y_F32,
-                                        wd.data_ptr(), None, _stream())
+                                        wd_ptr, None, _stream())
     else:
         rc = L.df11_decode_gemm_ex(ctypes.byref(dt.view), x.data_ptr(), B, y.data_ptr(), _lib.DF11_Y_F32,
-                                   wd.data_ptr(), None, workspace.data_ptr(), workspace.numel(), _stream())
+                                   wd_ptr, None, workspace.data_ptr(), workspace.numel(), _stream())
     assert rc == 0, L.df11_last_error()
     torch.cuda.synchronize()
-    return y.cpu().numpy(), wd.cpu().numpy().view(np.uint16)
+    return y.cpu().numpy(), (wd.cpu().numpy().view(np.uint16) if debug else None)
 
 
 def test_noalloc_matches_workspace_entry_point_twice():
@@ -60,6 +64,11 @@ def test_noalloc_matches_workspace_entry_point_twice():
         ref = orc.gemm_f64(X, W)
         assert _rel(y_na, ref) < TOL and _rel(y_ws, ref) < TOL
         assert _rel(y_na, y_ws.astype(np.float64)) < 1e-5
+        # the product path: the ring kernels read the packed x from the scratch
+        p_ws, _ = _call("ex", dt, x, B, N, K, ws, debug=False)
+        p_na, _ = _call("noalloc", dt, x, B, N, K, debug=False)
+        assert _rel(p_na, ref) < TOL and _rel(p_ws, ref) < TOL
+        assert _rel(p_na, p_ws.astype(np.float64)) < 1e-5
 
 
 def test_noalloc_refuses_packed_x_beyond_its_scratch():
