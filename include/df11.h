@@ -376,8 +376,9 @@ typedef struct df11_gemm_tuning {
     uint32_t row_blocks;   /* wide kernel: 0 = by B, else 1 or 2 row blocks per workgroup */
     uint32_t parts;        /* segment-parallel and vector kernels: 0 = enough runs of a row block's
                               segments to fill the device, else that many (float32 y) */
-    uint32_t split;        /* wide and tile-synchronous kernels: 0 = by occupancy, else that many K
-                              ranges per row block (float32 y) */
+    uint32_t split;        /* wide, tile-synchronous, pipelined and exponent-ring kernels (named in
+                              `kernel`): 0 = by occupancy, else that many K ranges per row block
+                              (float32 y) */
     uint32_t one_writer;   /* nonzero: every element of y is summed by one workgroup in a fixed
                               order (no K ranges, no segment runs: parts and split 1), so a
                               float32 y is the same on every run; slower for weights with too few
@@ -406,12 +407,14 @@ uint64_t df11_decode_gemm_workspace_bytes(const df11_view *device_view, uint32_t
  * `stream` has finished: above 32 rows of x a packing kernel first writes x
  * into it in operand order (overwriting all of the bytes it needs, so its
  * contents need no clearing), and the product reads x from there (up_proj at
- * 64 / 128 / 256 rows: 68 / 91 / 117 us in place, 57 / 70 / 96 us packed).
+ * 64 / 128 / 256 rows: 63 / 103 / 97 us with x read in place, 47 / 63 / 85
+ * us with x packed, the packing included).
  * y agrees with every choice within the float32 summation order.  Errors:
  * as df11_decode_gemm_out, E_ARG for a choice that does not apply (w_debug
  * or more than 64 rows of x on the segment-parallel kernel, w_debug or more
- * than 2 rows on the vector one, 32 rows or fewer on the wide one, parts or
- * split above 1 with a BF16 y or with one_writer) or a workspace too
+ * than 2 rows on the vector one, 32 rows or fewer on the wide one, split
+ * without a kernel that takes it, parts or split above 1 with a BF16 y or
+ * with one_writer) or a workspace too
  * small or misaligned, E_UNSUPPORTED when the chosen kernel's LDS does not
  * fit this weight. */
 int df11_decode_gemm_ex(const df11_view *device_view, const uint16_t *x, uint32_t B, void *y, int y_dtype,
