@@ -2002,7 +2002,7 @@ int check_gemm_tuning(const df11_gemm_tuning &t, bool bf16_y)
         return df11::fail(DF11_E_ARG, "tuning: parts applies to the segment-parallel and vector kernels");
     if (t.split && t.kernel != DF11_GEMM_WIDE && t.kernel != DF11_GEMM_TILED && t.kernel != DF11_GEMM_PIPE &&
         t.kernel != DF11_GEMM_RING)
-        return df11::fail(DF11_E_ARG, "tuning: split applies to the wide, tile-synchronous, pipelined and exponent-ring kernels, named in kernel");
+        return df11::fail(DF11_E_ARG, "tuning: split applies to the wide, tile-synchronous and pipelined kernels");
     if (bf16_y && (t.parts > 1 || t.split > 1))
         return df11::fail(DF11_E_ARG, "tuning: a BF16 y has one writer per element (parts and split 1)");
     if (t.one_writer && (t.parts > 1 || t.split > 1))
